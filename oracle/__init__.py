@@ -1,0 +1,29 @@
+"""CPU oracle for paged decode attention and its block manager.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product (the C ABI library under
+paged_kv_cache_162_amd/, its Python binding) may import, call or link this
+package. Only tests/, the smoke check in __graft_entry__.py and the CPU
+baseline leg of bench.py use it.
+
+The oracle is a plain, slow, obviously-correct restatement of what the pages
+define, in float64 numpy:
+  * attention.py     - slot formula, cache scatter, block copy, and decode
+                       attention (softmax(q K^T * scale) V) over a paged pool,
+                       plus a second loop order and the split/merge form used
+                       to pin the first;
+  * block_manager.py - the host block manager (free list, refcounts, lazy
+                       per-token growth, fork, copy-on-write, free);
+  * sizes.py         - the KV-cache size formula and block/waste counts.
+
+Every function is pinned by tests under tests/ against values the pages print,
+closed forms, invariants and brute force; none is "parity unpinned".
+"""
+from .attention import (  # noqa: F401
+    widen, slot_of, slot_mapping, gather_sequence, decode_attention,
+    decode_attention_blockwise, partial_attention, merge_partials,
+    decode_attention_split, reshape_and_cache, copy_blocks,
+)
+from .block_manager import BlockManager, KVError  # noqa: F401
+from .sizes import (  # noqa: F401
+    kv_cache_bytes, blocks_for_tokens, waste_slots, decode_call_bytes,
+)
