@@ -1,0 +1,214 @@
+"""Benchmark: one decode step of paged attention on one MI355X.
+
+A step is the whole hot path for one layer and one batch: slot mapping of
+every sequence's new token, the cache write of its K/V (reshape_and_cache),
+and paged decode attention over the whole cache (partition kernel plus, for
+sequences longer than one partition, the split-K merge). Inputs are resident
+in HBM before the timed region starts. The host block manager's bookkeeping
+for the step happens before timing.
+
+Default workload: the Llama-3-70B-shaped grouped-query decode layer, 128
+sequences, 64 query / 8 KV heads, head_dim 128, bf16, lognormal lengths
+(median 512) - synthetic, seeded data. To measure from HBM rather than the
+256 MB last-level cache, the step rotates over several replicas of the pools
+and queries (default: enough to exceed 1 GB).
+
+Prints ONE JSON line (see the keys below). `value` is KV GB/s over the step:
+the live K and V bytes of every sequence (exact lengths) divided by the step
+time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=3, help="workload number 1-6")
+    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
+    ap.add_argument("--replicas", type=int, default=0, help="pool replicas to rotate (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--pmc-traffic", default="", help="JSON file with measured HBM traffic per launch")
+    return ap.parse_args()
+
+
+def to_dev(a, dt):
+    import torch
+    a = np.ascontiguousarray(a)
+    if dt == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def kv_bytes(lens, Hkv, D, eb):
+    return int(np.sum(lens.astype(np.int64))) * Hkv * D * eb * 2
+
+
+def decode_alg_bytes(lens, S, Hq, Hkv, D, eb):
+    """Algorithmic bytes of one decode-attention call: live K/V, queries, fp32
+    outputs, live block-table entries, lengths."""
+    nb = int(np.sum((lens.astype(np.int64) + 15) // 16))
+    return kv_bytes(lens, Hkv, D, eb) + S * Hq * D * eb + S * Hq * D * 4 + nb * 4 + S * 4
+
+
+def cpu_baseline(w, seconds):
+    """The oracle, untouched, timed on this host on the same workload: the
+    whole decode (gather through the block table + fp64 attention) over all
+    sequences, repeated until `seconds` have elapsed (at most 5 passes)."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from oracle.block_manager import run_ops
+    bm = oracle.BlockManager(w.num_blocks, free_order=w.free_order)
+    h, _, _ = run_ops(bm, w.setup_ops + w.step_ops)
+    tables, lens = bm.packed_tables([h[i] for i in range(w.S)])
+    sp = w.spec
+    passes, t_total = 0, 0.0
+    with threadpool_limits(limits=1):
+        while passes < 5 and (passes == 0 or t_total < seconds):
+            t0 = time.perf_counter()
+            oracle.decode_attention(w.q, w.k_pool, w.v_pool, tables, lens, sp.scale, sp.dtype)
+            t_total += time.perf_counter() - t0
+            passes += 1
+    per = t_total / passes
+    kvb = kv_bytes(lens, sp.Hkv, sp.D, sp.elem_bytes)
+    return {"value": round(kvb / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seqs_per_s": round(sp.S / per, 2), "seconds_per_pass": round(per, 3),
+            "sample": f"the whole workload ({sp.S} sequences x {sp.Hq} query heads), {passes} "
+                      f"pass(es), BLAS limited to 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the design for sharding is described in DESIGN.md)"}))
+        sys.exit(2)
+    import torch
+    from workloads import make_workload
+    lib_path = os.path.join(ROOT, "paged_kv_cache_162_amd", "libpagedkv.so")
+    if not os.path.exists(lib_path):
+        from paged_kv_cache_162_amd import build as b
+        b.build()
+    import paged_kv_cache_162_amd as kv
+    from paged_kv_cache_162_amd.session import DecodeSession
+
+    w = make_workload(args.workload)
+    sp = w.spec
+    dt = sp.dtype
+    print(f"[bench] workload {sp.name}: S={sp.S} Hq={sp.Hq} Hkv={sp.Hkv} D={sp.D} {dt} "
+          f"blocks={w.num_blocks} sum_ctx={int(w.context_lens.sum())} max_ctx={int(w.context_lens.max())}",
+          file=sys.stderr, flush=True)
+    kp, vp = to_dev(w.k_pool, dt), to_dev(w.v_pool, dt)
+    sess = DecodeSession(k_pool=kp, v_pool=vp, num_q_heads=sp.Hq, free_order=w.free_order,
+                         partition_size=args.partition)
+    values = {}
+    if w.tail_k is not None:
+        values = {s: (to_dev(w.tail_k[s], dt), to_dev(w.tail_v[s], dt)) for s in range(sp.S)}
+    sess.run_ops(w.setup_ops, values)
+    sess.prepare_step(list(range(sp.S)))
+    lens = sess.host_lens
+    q, kn, vn = to_dev(w.q, dt), to_dev(w.k_new, dt), to_dev(w.v_new, dt)
+    out = torch.empty((sp.S, sp.Hq, sp.D), dtype=torch.float32, device="cuda")
+
+    pool_bytes = 2 * kp.numel() * kp.element_size()
+    R = args.replicas or max(1, int(np.ceil(1.0e9 / pool_bytes)))
+    reps = [(kp, vp, q, kn, vn)]
+    for _ in range(R - 1):
+        reps.append((kp.clone(), vp.clone(), q.clone(), kn.clone(), vn.clone()))
+    torch.cuda.synchronize()
+
+    def one(k, events=None):
+        a, b, qq, kk, vv = reps[k % R]
+        sess.step(qq, kk, vv, out, sp.scale, k_pool=a, v_pool=b, decode_events=events)
+
+    for k in range(args.warmup):
+        one(k)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for k in range(K):
+        one(k, ev[k])
+    t_end.record()
+    torch.cuda.synchronize()
+    step_ms = t_start.elapsed_time(t_end) / K
+    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    dec_avg = float(dec_ms.mean())
+
+    # warm number: same buffers every step
+    for k in range(10):
+        one(0)
+    torch.cuda.synchronize()
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record()
+    for k in range(K):
+        one(0)
+    w1.record()
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / K
+
+    kvb = kv_bytes(lens, sp.Hkv, sp.D, sp.elem_bytes)
+    alg = decode_alg_bytes(lens, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes)
+    value = kvb / (step_ms * 1e-3) / 1e9
+    achieved = alg / (dec_avg * 1e-3) / 1e9
+    traffic = None
+    if args.pmc_traffic and os.path.exists(args.pmc_traffic):
+        traffic = json.load(open(args.pmc_traffic)).get("bytes_per_launch")
+
+    res = {
+        "metric": "paged decode attention KV GB/s (% of HBM peak) and seqs/s per config, 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{sp.name}: {sp.description}",
+            "sequences": sp.S, "q_heads": sp.Hq, "kv_heads": sp.Hkv, "head_dim": sp.D,
+            "block_size": 16, "partition_tokens": args.partition or 512,
+            "sum_context": int(lens.sum()), "max_context": int(lens.max()),
+            "kv_bytes_per_step": kvb, "replicas_rotated": R, "parallelism": "single GPU",
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(sp.S / (step_ms * 1e-3), 1),
+        "decode_ms": round(dec_avg, 5),
+        "decode_kv_gbs": round(kvb / (dec_avg * 1e-3) / 1e9, 2),
+        "warm_ms_per_step": round(warm_ms, 5),
+        "warm_kv_gbs": round(kvb / (warm_ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "kv_paged_attention_decode (partition kernel + split-K merge)",
+                     "alg_bytes_per_launch": alg},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,250 @@
+/*
+ * pagedkv - paged KV cache and paged decode attention for AMD Instinct MI355X
+ * (gfx950). C ABI of libpagedkv.so.
+ *
+ * Pages cited in this header:
+ *   [1] "PagedAttention - how vLLM stopped wasting 80% of your GPU memory"
+ *       (shivam2003.com/posts/pagedattention.html)
+ *   [2] "PagedAttention: How vLLM Borrowed Virtual Memory to Unlock GPU
+ *       Serving at Scale" (fp4-site.pages.dev/system/pagedattention-vllm-deep-dive/)
+ *   [3] "PagedAttention and vLLM: Virtual Memory for the KV Cache"
+ *       (passgenai.com, NCA-GENL course lesson 12-07)
+ *   [4] "What is paged attention?" (netraruntime.com/learn/paged-attention)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every call returns kv_status (or a plain value where stated). On an error
+ *   kv_last_error() returns a message for the calling thread.
+ * - Host operations on a pool are all-or-nothing: on any error no block,
+ *   reference count, table or length changes ([3], "L3": preemption and
+ *   admission are all-or-nothing per sequence).
+ * - A kv_pool_t is host metadata only. It is not thread-safe: callers
+ *   serialise calls on one handle.
+ * - Device entry points take device pointers owned by the caller (PyTorch in
+ *   the bundled binding) and a hipStream_t. The library never allocates or
+ *   frees device memory and never synchronises; work is enqueued on the
+ *   given stream. Argument checks happen on the host before any launch; a
+ *   failed launch returns KV_ERR_HIP.
+ * - Cache layout, per layer ([2], "The Custom CUDA Kernel"): a K pool and a V
+ *   pool, each [num_blocks][num_kv_heads][block_size][head_dim], row-major,
+ *   elements of one kv_dtype; the leading index is the physical block ID.
+ * - Token position p of a sequence lives in slot
+ *   table[p / B] * B + p % B ([4], "How it works"); slot s is element
+ *   [s / B][h][s % B][:] of a pool.
+ * - Supported on the device: block_size 16, head_dim 64 or 128, num_q_heads
+ *   a multiple of num_kv_heads, dtypes f32/f16/bf16. Anything else returns
+ *   KV_ERR_UNSUPPORTED.
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+  KV_OK = 0,
+  KV_ERR_INVALID = -1,     /* bad argument (null pointer, size, out-of-range ID) */
+  KV_ERR_OOM = -2,         /* not enough free blocks; nothing changed */
+  KV_ERR_UNSUPPORTED = -3, /* shape or dtype the device kernels do not cover */
+  KV_ERR_HIP = -4,         /* the HIP runtime reported an error at launch */
+  KV_ERR_STATE = -5        /* wrong object state: unknown sequence, block not held */
+} kv_status;
+
+typedef enum { KV_F32 = 0, KV_F16 = 1, KV_BF16 = 2 } kv_dtype;
+
+typedef struct {
+  int32_t num_blocks;   /* physical blocks in the pool, > 0 */
+  int32_t block_size;   /* tokens per block, > 0 (the device path needs 16) */
+  int32_t num_layers;   /* layers sharing one block ID space, > 0 */
+  int32_t num_kv_heads; /* > 0 */
+  int32_t head_dim;     /* > 0 */
+  kv_dtype dtype;
+} kv_pool_config;
+
+typedef struct kv_pool kv_pool_t; /* opaque; host metadata only */
+
+/* ---------------------------------------------------------------------------
+ * Host: block pool ([3], "L2 - Mechanism", the block pool; [4], "How it
+ * works": allocation pops the free list and freeing pushes it, both O(1)).
+ * ------------------------------------------------------------------------- */
+
+/* Create the host metadata for a pool of uniform blocks, all free. The
+ * initial free order hands out block 0 first, then 1, 2, ... ([1], "A small
+ * worked example": the first free blocks are P0 and P1). *out receives the
+ * handle; release it with kv_pool_destroy. */
+kv_status kv_pool_create(const kv_pool_config* cfg, kv_pool_t** out);
+void kv_pool_destroy(kv_pool_t* pool);
+
+/* Replace the free order: afterwards blocks are handed out as order[0],
+ * order[1], ... `order` must be a permutation of [0, num_blocks) (n ==
+ * num_blocks). Only allowed while every block is free (KV_ERR_STATE
+ * otherwise). Used to place sequences in shuffled physical blocks. */
+kv_status kv_pool_set_free_order(kv_pool_t* pool, int32_t n, const int32_t* order);
+
+/* Bytes of ONE layer's K pool (equal to its V pool):
+ * num_blocks * num_kv_heads * block_size * head_dim * element size. */
+size_t kv_pool_layer_bytes(const kv_pool_t* pool);
+/* Resident-token capacity num_blocks * block_size ([3], "L2": the block
+ * count is the hard capacity, however tokens are spread). -1 on NULL. */
+int64_t kv_pool_capacity_tokens(const kv_pool_t* pool);
+int32_t kv_num_free_blocks(const kv_pool_t* pool);
+
+/* Pop n blocks (reference count 1 each) into ids_out[0..n). All or nothing:
+ * KV_ERR_OOM if fewer than n are free. */
+kv_status kv_block_alloc(kv_pool_t* pool, int32_t n, int32_t* ids_out);
+/* Add one reference per listed block ([1], "Memory sharing": a reference
+ * count per physical block). Every block must be held (KV_ERR_STATE). */
+kv_status kv_block_incref(kv_pool_t* pool, int32_t n, const int32_t* ids);
+/* Drop one reference per listed block; blocks reaching zero are pushed on the
+ * free list in reverse list order, so the next allocations return them in
+ * list order. KV_ERR_STATE if a block would drop below zero. */
+kv_status kv_block_free(kv_pool_t* pool, int32_t n, const int32_t* ids);
+/* Current reference count, 0 if free, -1 for an ID outside the pool. */
+int32_t kv_block_refcount(const kv_pool_t* pool, int32_t id);
+
+/* ---------------------------------------------------------------------------
+ * Host: sequences ([3], "The allocation lifecycle"; [2], "Walking Through the
+ * Lifecycle"; copy-on-write per [2], "Copy-on-Write for Beam Search and
+ * Parallel Sampling").
+ * ------------------------------------------------------------------------- */
+
+/* New empty sequence; handles are never reused within a pool. */
+kv_status kv_seq_create(kv_pool_t* pool, int64_t* seq_out);
+/* New sequence sharing every block of `parent` (each gains a reference). */
+kv_status kv_seq_fork(kv_pool_t* pool, int64_t parent, int64_t* child_out);
+/* Reserve n_tokens new positions at the end of `seq`.
+ * - Growth is lazy: a block is taken just before position p with
+ *   p % block_size == 0, so t tokens hold ceil(t / block_size) blocks
+ *   ([4], "How it works").
+ * - If the first new position falls inside the last block and that block's
+ *   reference count exceeds one, the block is copied: a new block is taken,
+ *   the old one loses a reference, the table entry is redirected, and the
+ *   pair is reported in (cow_src[0], cow_dst[0]) with *n_cow = 1. The caller
+ *   must run kv_copy_blocks on that pair before writing the new tokens.
+ *   Otherwise *n_cow = 0. Appending after a full shared block copies nothing
+ *   ([1], "A small worked example", step 3).
+ * - slots_out[i] receives the slot of position len + i (int64).
+ * - The copy block (if any) is taken before the new blocks.
+ * All or nothing (KV_ERR_OOM). slots_out may be NULL when n_tokens == 0;
+ * cow_src, cow_dst and n_cow must not be NULL. */
+kv_status kv_seq_append(kv_pool_t* pool, int64_t seq, int32_t n_tokens, int64_t* slots_out,
+                        int32_t* cow_src, int32_t* cow_dst, int32_t* n_cow);
+/* Return every block of the sequence ([2], "Sequence Completion"): one
+ * reference each, pushed in reverse logical order when it reaches zero. */
+kv_status kv_seq_free(kv_pool_t* pool, int64_t seq);
+/* Copy the block table into ids[0..*n). If cap < the table length, returns
+ * KV_ERR_INVALID with *n set to the length needed. */
+kv_status kv_seq_block_table(const kv_pool_t* pool, int64_t seq, int32_t cap, int32_t* ids,
+                             int32_t* n);
+/* Tokens held by the sequence, -1 if the handle is unknown. */
+int32_t kv_seq_len(const kv_pool_t* pool, int64_t seq);
+/* Pack the tables of n_seqs sequences into a row-major host array
+ * tables_out[n_seqs][max_blocks] (unused entries = -1) and their lengths into
+ * lens_out[n_seqs]. KV_ERR_INVALID if a table is wider than max_blocks. */
+kv_status kv_seq_pack_tables(const kv_pool_t* pool, int32_t n_seqs, const int64_t* seqs,
+                             int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
+
+/* ---------------------------------------------------------------------------
+ * Device: slot mapping and cache writes.
+ * ------------------------------------------------------------------------- */
+
+/* slots[i] = tables[seq_idx[i]][pos[i] / block_size] * block_size
+ *            + pos[i] % block_size, as int64 ([4], "How it works").
+ * Entries that cannot be mapped (seq_idx outside [0, num_rows), pos < 0,
+ * pos / block_size >= max_blocks, a negative table entry) give -1, which
+ * kv_reshape_and_cache skips. tables is [num_rows][max_blocks] int32; seq_idx
+ * and pos are int32 [n]; slots is int64 [n]; all device pointers. */
+kv_status kv_slot_mapping(const int32_t* tables, int32_t num_rows, int32_t max_blocks,
+                          const int32_t* seq_idx, const int32_t* pos, int32_t n,
+                          int32_t block_size, int64_t* slots, hipStream_t stream);
+
+/* Write each new token's K and V into its slot ([3], "The allocation
+ * lifecycle": each decode step writes the token's K,V into the last block).
+ * k_new, v_new: [n][num_kv_heads][head_dim] of `dtype`; k_pool, v_pool: one
+ * layer's pools with num_blocks blocks; slots: int64 [n]. The copy is bit
+ * exact. Slots < 0 or >= num_blocks * block_size are skipped. Slots must be
+ * distinct within a call (duplicates race). Pointers must be 16-byte
+ * aligned. */
+kv_status kv_reshape_and_cache(const void* k_new, const void* v_new, void* k_pool,
+                               void* v_pool, const int64_t* slots, int32_t n,
+                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, kv_dtype dtype, hipStream_t stream);
+
+/* Device half of copy-on-write ([2], "Copy-on-Write ...": copy the shared
+ * block's content into the new block): for every pair (pairs[2i] = src,
+ * pairs[2i+1] = dst) and every layer, copy block_bytes bytes of K and of V
+ * from block src to block dst. k_pools and v_pools are HOST arrays of
+ * num_layers device pointers (num_layers <= 256); pairs is a device int32
+ * array of 2n entries; every src and dst must be < num_blocks (checked on
+ * the device: out-of-range pairs are skipped). block_bytes must be a
+ * multiple of 16 and the pools 16-byte aligned. Pairs must not chain (a dst
+ * that is also a src in the same call). */
+kv_status kv_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,
+                         const int32_t* pairs, int32_t n, int32_t num_blocks,
+                         size_t block_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Device: paged decode attention ([1], "The PagedAttention kernel"; [2],
+ * "The Custom CUDA Kernel"; [3], "The kernel change").
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes kv_paged_attention_decode needs for these sizes: 0 when
+ * max_context_len <= the partition size (every sequence finishes in one
+ * partition), else S * num_q_heads * num_partitions * (head_dim + 2) * 4 for
+ * the per-partition partial outputs, maxima and sums. partition_size 0 picks
+ * the default (512). Returns 0 for invalid sizes. */
+size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_t head_dim,
+                                          int32_t max_context_len, int32_t partition_size);
+
+/* out[s][hq][:] = sum_j softmax_j(scale * <q[s][hq], K_s[j]>) V_s[j] over the
+ * first context_lens[s] positions of sequence s, where K_s[j] and V_s[j] are
+ * read from slot(j) of KV head hq / (num_q_heads / num_kv_heads) - exactly
+ * the attention of the contiguous cache ([1], "The PagedAttention kernel").
+ *
+ * out:          device float [S][num_q_heads][head_dim] (fp32 output)
+ * q:            device [S][num_q_heads][head_dim] of `dtype`
+ * k_pool/v_pool device, one layer's pools with num_blocks blocks
+ * block_tables: device int32 [S][max_blocks]
+ * context_lens: device int32 [S]
+ * max_context_len: host upper bound on every context_lens[s]; it sizes the
+ *               grid (number of partitions).
+ * partition_size: tokens per work item (multiple of 16, 16..8192); 0 = 512.
+ *               Sequences longer than one partition are split and merged
+ *               with a log-sum-exp reduction ([2], "The Custom CUDA Kernel":
+ *               per-piece partial outputs and denominators merged stably).
+ * workspace:    device scratch of at least
+ *               kv_paged_attention_workspace_bytes(...) bytes (may be NULL
+ *               when that is 0).
+ *
+ * Per-sequence device-side checks (no fault, no error code): a sequence with
+ * context_lens[s] == 0 gets an all-zero output. A sequence whose length is
+ * negative, exceeds max_blocks * block_size or max_context_len, or whose
+ * live table entries fall outside [0, num_blocks), gets NaN in every output
+ * element, and no out-of-range memory is read.
+ *
+ * Kernels: head groups of 2..16 query heads per KV head with f16/bf16 and
+ * head_dim 128 run on MFMA matrix cores; other cases run on the vector ALUs.
+ * One workgroup handles one (sequence, KV head, partition). */
+kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_pool,
+                                    const void* v_pool, const int32_t* block_tables,
+                                    int32_t max_blocks, const int32_t* context_lens, int32_t S,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t num_blocks, float scale,
+                                    kv_dtype dtype, int32_t partition_size,
+                                    int32_t max_context_len, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/* Message describing the calling thread's last error ("" if none). */
+const char* kv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */

@@ -1,0 +1,861 @@
+// Device side of pagedkv for AMD CDNA4 (gfx950): slot mapping, cache scatter,
+// copy-on-write block copy, paged decode attention and the split-K merge.
+//
+// Pages cited in this file:
+//   [1] "PagedAttention - how vLLM stopped wasting 80% of your GPU memory"
+//       (shivam2003.com/posts/pagedattention.html)
+//   [2] "PagedAttention: How vLLM Borrowed Virtual Memory to Unlock GPU
+//       Serving at Scale" (fp4-site.pages.dev/system/pagedattention-vllm-deep-dive/)
+//   [3] "PagedAttention and vLLM: Virtual Memory for the KV Cache" (passgenai.com)
+//   [4] "What is paged attention?" (netraruntime.com/learn/paged-attention)
+//
+// Pool layout per layer ([2], "The Custom CUDA Kernel"):
+// [num_blocks][num_kv_heads][16][head_dim]. One (block, KV head) is a
+// contiguous 16 x head_dim tile: 4 KB for 16-bit elements at head_dim 128.
+//
+// Decode attention computes, per sequence and query head, the softmax of the
+// scaled dot products with every live key and the weighted sum of the values
+// - exactly the contiguous-cache result ([1], "The PagedAttention kernel").
+// Work split: one workgroup (4 wave64s) per (sequence, KV head, context
+// partition). The partition's block-table entries are staged in LDS first, so
+// every K/V address is known before the first load. Each wave walks every
+// fourth 16-token block of the partition, keeps an online softmax (running
+// max and sum, [2] "The Custom CUDA Kernel"), and the four waves merge in
+// LDS. Sequences longer than one partition write unnormalised partial results
+// that a second kernel merges with the log-sum-exp rule.
+//
+// Softmax runs in base 2: scores are multiplied by scale*log2(e) and
+// exponentiated with v_exp_f32; the result is the same softmax.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/pagedkv.h"
+#include "status.h"
+
+using pagedkv::fail;
+
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+
+constexpr int kBlock = 16;          // tokens per KV block (device kernels)
+constexpr int kWaves = 4;           // wave64s per decode workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxPartition = 8192; // tokens
+constexpr int kMaxPartBlocks = kMaxPartition / kBlock;
+constexpr int kDefaultPartition = 512;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- element conversion -----------------------------------------------------
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+}
+
+// Unpack one 16-byte chunk into fp32 values (4 for fp32, 8 for 16-bit types).
+template <int DT>
+__device__ __forceinline__ void unpack16(const uint4& u, float* f) {
+  if constexpr (DT == KV_F32) {
+    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+  } else if constexpr (DT == KV_BF16) {
+    f[0] = bf16lo(u.x); f[1] = bf16hi(u.x); f[2] = bf16lo(u.y); f[3] = bf16hi(u.y);
+    f[4] = bf16lo(u.z); f[5] = bf16hi(u.z); f[6] = bf16lo(u.w); f[7] = bf16hi(u.w);
+  } else {
+    f[0] = f16lo(u.x); f[1] = f16hi(u.x); f[2] = f16lo(u.y); f[3] = f16hi(u.y);
+    f[4] = f16lo(u.z); f[5] = f16hi(u.z); f[6] = f16lo(u.w); f[7] = f16hi(u.w);
+  }
+}
+
+// ---- cross-lane reductions --------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over groups of LPR consecutive lanes (LPR = 8, 16 or 32). Within a
+// 16-lane DPP row: swap neighbours, swap pairs, mirror halves, mirror the row.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  if constexpr (LPR >= 16) x += dpp<0x140>(x);  // row_mirror
+  if constexpr (LPR >= 32) x += __shfl_xor(x, 16, 64);
+  return x;
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+// ---- shared decode parameters ----------------------------------------------
+struct DecodeParams {
+  float* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* tables;
+  const int32_t* lens;
+  float* ws_o;   // [S][Hq][nparts][D]
+  float* ws_ml;  // [S][Hq][nparts][2]
+  int32_t max_blocks, S, Hq, Hkv, G, num_blocks, part_tokens, nparts;
+  float scale_log2;
+};
+
+// Work-item decode: blockIdx.x enumerates (partition, KV head, sequence) with
+// the sequence fastest, so every first partition is dispatched before any
+// second one and long sequences' extra partitions come last.
+struct WorkItem {
+  int s, h, part;
+};
+__device__ __forceinline__ WorkItem work_item(const DecodeParams& p) {
+  const int L = blockIdx.x;
+  WorkItem w;
+  w.s = L % p.S;
+  w.h = (L / p.S) % p.Hkv;
+  w.part = L / (p.S * p.Hkv);
+  return w;
+}
+
+// Sequence-level checks shared by both decode kernels. Returns false when the
+// workgroup has nothing to do (its output, if any, is already written).
+template <int D>
+__device__ __forceinline__ bool sequence_prologue(const DecodeParams& p, const WorkItem& w,
+                                                  int ctx) {
+  const bool bad = ctx < 0 || (int64_t)ctx > (int64_t)p.max_blocks * kBlock ||
+                   (int64_t)ctx > (int64_t)p.nparts * p.part_tokens;
+  if (bad || ctx == 0) {
+    if (w.part == 0) {
+      const float v = bad ? __builtin_nanf("") : 0.0f;
+      for (int i = threadIdx.x; i < p.G * D; i += kThreads) {
+        const int g = i / D, d = i % D;
+        p.out[((size_t)w.s * p.Hq + (size_t)w.h * p.G + g) * D + d] = v;
+      }
+    }
+    return false;
+  }
+  const int nps = (ctx + p.part_tokens - 1) / p.part_tokens;
+  return w.part < nps;
+}
+
+// Stage the partition's physical block IDs in LDS. Out-of-range IDs are
+// replaced by 0 (a safe read) and flag the partition as invalid.
+__device__ __forceinline__ void stage_table(const DecodeParams& p, const WorkItem& w, int b0,
+                                            int nblk, int* s_tab, int* s_bad) {
+  if (threadIdx.x == 0) *s_bad = 0;
+  __syncthreads();
+  const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + b0;
+  for (int i = threadIdx.x; i < nblk; i += kThreads) {
+    int e = row[i];
+    if (e < 0 || e >= p.num_blocks) {
+      *s_bad = 1;
+      e = 0;
+    }
+    s_tab[i] = e;
+  }
+  __syncthreads();
+}
+
+// Merge the four waves' (m, l, o) held in LDS and write either the final
+// output (single partition) or the partition's partial result.
+template <int D, int GMAX>
+__device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, const WorkItem& w,
+                                                      int nps, bool part_bad,
+                                                      float (*s_m)[GMAX], float (*s_l)[GMAX],
+                                                      float (*s_o)[GMAX][D]) {
+  for (int i = threadIdx.x; i < p.G * D; i += kThreads) {
+    const int g = i / D, d = i % D;
+    float M = s_m[0][g];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, s_m[k][g]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      const float mk = s_m[k][g];
+      const float f = (mk == neg_inf()) ? 0.f : fast_exp2(mk - M);
+      L += s_l[k][g] * f;
+      O += s_o[k][g][d] * f;
+    }
+    if (part_bad) {
+      M = L = O = __builtin_nanf("");
+    }
+    const size_t hq = (size_t)w.h * p.G + g;
+    if (nps == 1) {
+      p.out[((size_t)w.s * p.Hq + hq) * D + d] = O / L;
+    } else {
+      const size_t slot = ((size_t)w.s * p.Hq + hq) * p.nparts + w.part;
+      p.ws_o[slot * D + d] = O;
+      if (d == 0) {
+        p.ws_ml[slot * 2 + 0] = M;
+        p.ws_ml[slot * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// ============================================================================
+// Decode on the vector ALUs: any dtype, head_dim 64/128, up to GMAX query
+// heads per KV head. Each token row of a block is spread over LPR lanes
+// (16 bytes per lane), so one dwordx4 load per lane reads TPI whole rows and a
+// 16-token block takes IPB loads. Dot products are finished with DPP row
+// reductions. Each group of LPR lanes keeps its own online softmax over the
+// tokens it reads; the groups and then the waves are merged at the end.
+// ============================================================================
+template <int DT, int D, int GMAX>
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
+  constexpr int EB = DT == KV_F32 ? 4 : 2;
+  constexpr int EPL = 16 / EB;           // elements per lane chunk
+  constexpr int LPR = D * EB / 16;       // lanes per token row
+  constexpr int TPI = 64 / LPR;          // rows per wave-wide load
+  constexpr int IPB = kBlock / TPI;      // loads per 16-token block
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "unsupported row width");
+
+  __shared__ int s_tab[kMaxPartBlocks];
+  __shared__ int s_bad;
+  __shared__ float s_m[kWaves][GMAX], s_l[kWaves][GMAX];
+  __shared__ float s_o[kWaves][GMAX][D];
+
+  const WorkItem w = work_item(p);
+  const int ctx = p.lens[w.s];
+  if (!sequence_prologue<D>(p, w, ctx)) return;
+  const int nps = (ctx + p.part_tokens - 1) / p.part_tokens;
+  const int t0 = w.part * p.part_tokens;
+  const int t1 = min(ctx, t0 + p.part_tokens);
+  const int b0 = t0 / kBlock;
+  const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
+  stage_table(p, w, b0, nblk, s_tab, &s_bad);
+  const bool part_bad = s_bad != 0;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane / LPR, c = lane % LPR;
+
+  // query chunk of every head in the group, pre-scaled into base-2 logits
+  float qf[GMAX][EPL];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    if (g < p.G) {
+      const uint4* qp = reinterpret_cast<const uint4*>(
+          static_cast<const char*>(p.q) + (((size_t)w.s * p.Hq + (size_t)w.h * p.G + g) * D) * EB);
+      unpack16<DT>(qp[c], qf[g]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[g][e] *= p.scale_log2;
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[g][e] = 0.f;
+    }
+  }
+
+  float m[GMAX], l[GMAX], acc[GMAX][EPL];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    m[g] = neg_inf();
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+  }
+
+  const size_t tile_u4 = (size_t)kBlock * LPR;  // uint4 per (block, head) tile
+  const uint4* kbase = static_cast<const uint4*>(p.k_pool);
+  const uint4* vbase = static_cast<const uint4*>(p.v_pool);
+
+  for (int jb = wave; jb < nblk; jb += kWaves) {
+    const size_t tile = ((size_t)s_tab[jb] * p.Hkv + w.h) * tile_u4;
+    uint4 ku[IPB], vu[IPB];
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) ku[i] = kbase[tile + (size_t)(r + TPI * i) * LPR + c];
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) vu[i] = vbase[tile + (size_t)(r + TPI * i) * LPR + c];
+    const int valid = t1 - (t0 + jb * kBlock);  // live tokens in this block (>= 1)
+    const bool full = valid >= kBlock;
+
+    float kf[IPB][EPL], vf[IPB][EPL];
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      unpack16<DT>(ku[i], kf[i]);
+      unpack16<DT>(vu[i], vf[i]);
+    }
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < IPB; ++i)
+        if (r + TPI * i >= valid) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) vf[i][e] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      float sc[IPB];
+#pragma unroll
+      for (int i = 0; i < IPB; ++i) {
+        float d0 = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) d0 = fmaf(qf[g][e], kf[i][e], d0);
+        sc[i] = row_sum<LPR>(d0);
+      }
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < IPB; ++i)
+          if (r + TPI * i >= valid) sc[i] = neg_inf();
+      }
+      float mb = sc[0];
+#pragma unroll
+      for (int i = 1; i < IPB; ++i) mb = fmaxf(mb, sc[i]);
+      const float mn = fmaxf(m[g], mb);
+      if (mn == neg_inf()) continue;  // this row has seen no live token yet
+      const float alpha = fast_exp2(m[g] - mn);  // 0 when m was -inf
+      l[g] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < IPB; ++i) {
+        const float pi = fast_exp2(sc[i] - mn);  // 0 for masked tokens
+        l[g] += pi;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pi, vf[i][e], acc[g][e]);
+      }
+      m[g] = mn;
+    }
+  }
+
+  // merge the row groups of the wave (lanes differing in the row bits)
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) {
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      const float mo = __shfl_xor(m[g], o, 64);
+      const float lo = __shfl_xor(l[g], o, 64);
+      const float M = fmaxf(m[g], mo);
+      const float a1 = (m[g] == neg_inf()) ? 0.f : fast_exp2(m[g] - M);
+      const float a2 = (mo == neg_inf()) ? 0.f : fast_exp2(mo - M);
+      l[g] = l[g] * a1 + lo * a2;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float ao = __shfl_xor(acc[g][e], o, 64);
+        acc[g][e] = acc[g][e] * a1 + ao * a2;
+      }
+      m[g] = M;
+    }
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_o[wave][g][c * EPL + e] = acc[g][e];
+      if (c == 0) {
+        s_m[wave][g] = m[g];
+        s_l[wave][g] = l[g];
+      }
+    }
+  }
+  __syncthreads();
+  merge_waves_and_store<D, GMAX>(p, w, nps, part_bad, s_m, s_l, s_o);
+}
+
+// ============================================================================
+// Decode on MFMA matrix cores for grouped-query attention: f16/bf16, head_dim
+// 128, 2..16 query heads sharing one KV head. Per 16-token block a wave forms
+//   S^T[token][head] = K[token][:] . Q[head][:]   (4 x mfma 16x16x32)
+//   O^T[d][head]   += V^T[d][token] . P^T[token][head]   (16 x mfma 16x16x16)
+// The group's heads are the 16 MFMA columns (unused columns are zero). K is
+// loaded straight into the A-operand layout (lane l: token l%16, 8 dims at
+// 32*kc + 8*(l/16)); V is loaded as whole 256-byte rows (lane l: dims
+// 8*(l%16)..+8 of token 4*(l/16)+jj) and regrouped in registers so that lane l
+// feeds d = 8*(l%16)+n of tile n - no LDS transpose. The S^T output layout
+// (lane l: head l%16, tokens 4*(l/16)+r) is exactly the B operand P^T needs.
+// P stays in fp32 precision: it is split into a 16-bit high part and a 16-bit
+// residual and both go through the PV MFMA, so the products are accumulated
+// in fp32 with no 16-bit rounding of the weights.
+// ============================================================================
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_qk(const uint4& a, const uint4& b, f32x4 c) {
+  if constexpr (DT == KV_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_pv(const uint2& a, const uint2& b, f32x4 c) {
+  if constexpr (DT == KV_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// Split an fp32 weight into a 16-bit high part and a 16-bit residual.
+template <int DT>
+__device__ __forceinline__ void split_weight(float x, uint32_t& hi, uint32_t& lo) {
+  if constexpr (DT == KV_BF16) {
+    const uint32_t xb = __float_as_uint(x);
+    hi = xb >> 16;  // truncation; the residual below is exact in fp32
+    const float rem = x - __uint_as_float(xb & 0xffff0000u);
+    const uint32_t rb = __float_as_uint(rem);
+    lo = (rb + 0x7fffu + ((rb >> 16) & 1u)) >> 16;  // round to nearest even
+  } else {
+    const _Float16 h = (_Float16)x;
+    const _Float16 r = (_Float16)(x - (float)h);
+    hi = __builtin_bit_cast(unsigned short, h);
+    lo = __builtin_bit_cast(unsigned short, r);
+  }
+}
+
+// 16-bit element n (0..7) of four 16-byte chunks, packed as the MFMA operand
+// (element of chunk 0 in the low half of the first dword).
+__device__ __forceinline__ uint2 gather_col(const uint4* v, int n) {
+  auto word = [](const uint4& u, int k) -> uint32_t {
+    return k == 0 ? u.x : (k == 1 ? u.y : (k == 2 ? u.z : u.w));
+  };
+  const uint32_t w0 = word(v[0], n >> 1), w1 = word(v[1], n >> 1);
+  const uint32_t w2 = word(v[2], n >> 1), w3 = word(v[3], n >> 1);
+  uint2 r;
+  if (n & 1) {
+    r.x = (w0 >> 16) | (w1 & 0xffff0000u);
+    r.y = (w2 >> 16) | (w3 & 0xffff0000u);
+  } else {
+    r.x = (w0 & 0xffffu) | (w1 << 16);
+    r.y = (w2 & 0xffffu) | (w3 << 16);
+  }
+  return r;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+  constexpr int D = 128;
+  constexpr int GMAX = 16;
+  __shared__ int s_tab[kMaxPartBlocks];
+  __shared__ int s_bad;
+  __shared__ float s_m[kWaves][GMAX], s_l[kWaves][GMAX];
+  __shared__ float s_o[kWaves][GMAX][D];
+
+  const WorkItem w = work_item(p);
+  const int ctx = p.lens[w.s];
+  if (!sequence_prologue<D>(p, w, ctx)) return;
+  const int nps = (ctx + p.part_tokens - 1) / p.part_tokens;
+  const int t0 = w.part * p.part_tokens;
+  const int t1 = min(ctx, t0 + p.part_tokens);
+  const int b0 = t0 / kBlock;
+  const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
+  stage_table(p, w, b0, nblk, s_tab, &s_bad);
+  const bool part_bad = s_bad != 0;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15;  // MFMA column: query head of the group / token row
+  const int grp = lane >> 4;  // k-slot group
+
+  // B operand of the score MFMA: Q^T, lane holds head `col`, dims 32kc+8grp..+8
+  uint4 qb[4];
+  {
+    const bool live = col < p.G;
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(p.q) +
+        (((size_t)w.s * p.Hq + (size_t)w.h * p.G + (live ? col : 0)) * D) * 2);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const uint4 v = qp[kc * 4 + grp];
+      qb[kc] = live ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  f32x4 o[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = neg_inf(), l = 0.f;
+
+  const char* kbase = static_cast<const char*>(p.k_pool);
+  const char* vbase = static_cast<const char*>(p.v_pool);
+  constexpr size_t kTileBytes = (size_t)kBlock * D * 2;  // 4 KB
+
+  for (int jb = wave; jb < nblk; jb += kWaves) {
+    const size_t tile = ((size_t)s_tab[jb] * p.Hkv + w.h) * kTileBytes;
+    const uint4* kt = reinterpret_cast<const uint4*>(kbase + tile);
+    const uint4* vt = reinterpret_cast<const uint4*>(vbase + tile);
+    uint4 ku[4], vu[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) ku[kc] = kt[col * 16 + kc * 4 + grp];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) vu[jj] = vt[(4 * grp + jj) * 16 + col];
+
+    f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) st = mfma_qk<DT>(ku[kc], qb[kc], st);
+
+    const int valid = t1 - (t0 + jb * kBlock);
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = st[r] * p.scale_log2;
+    if (valid < kBlock) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * grp + r >= valid) {
+          sc[r] = neg_inf();
+          vu[r] = make_uint4(0, 0, 0, 0);  // masked rows may hold NaN
+        }
+    }
+    float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float mn = fmaxf(m, mb);  // finite: every block has a live token
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    l *= alpha;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) o[n] *= alpha;
+
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pr = fast_exp2(sc[r] - mn);
+      l += pr;
+      split_weight<DT>(pr, hi[r], lo[r]);
+    }
+    const uint2 phi = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+    const uint2 plo = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const uint2 a = gather_col(vu, n);
+      o[n] = mfma_pv<DT>(a, phi, o[n]);
+      o[n] = mfma_pv<DT>(a, plo, o[n]);
+    }
+  }
+
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (grp == 0) {
+    s_m[wave][col] = m;
+    s_l[wave][col] = l;
+  }
+  if (col < p.G) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) s_o[wave][col][32 * grp + 8 * r + n] = o[n][r];
+  }
+  __syncthreads();
+  merge_waves_and_store<D, GMAX>(p, w, nps, part_bad, s_m, s_l, s_o);
+}
+
+// ============================================================================
+// Split-K merge ([2], "The Custom CUDA Kernel": partial outputs and softmax
+// denominators combined with a numerically stable merge): for every
+// (sequence, query head) with more than one partition,
+//   M = max_k m_k,  L = sum_k l_k 2^(m_k - M),  out = sum_k 2^(m_k - M) o_k / L.
+// A NaN denominator (invalid table entry) makes the whole output NaN.
+// ============================================================================
+template <int D>
+__global__ __launch_bounds__(D) void splitk_reduce_kernel(float* __restrict__ out,
+                                                          const float* __restrict__ ws_o,
+                                                          const float* __restrict__ ws_ml,
+                                                          const int32_t* __restrict__ lens,
+                                                          int32_t Hq, int32_t nparts,
+                                                          int32_t part_tokens,
+                                                          int32_t max_blocks) {
+  const int hq = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+  const int ctx = lens[s];
+  if (ctx <= 0 || (int64_t)ctx > (int64_t)max_blocks * kBlock ||
+      (int64_t)ctx > (int64_t)nparts * part_tokens)
+    return;  // handled by the partition kernel
+  const int nps = (ctx + part_tokens - 1) / part_tokens;
+  if (nps <= 1) return;
+  const size_t base = ((size_t)s * Hq + hq) * nparts;
+  float M = neg_inf();
+  bool bad = false;
+  for (int k = 0; k < nps; ++k) {
+    const float mk = ws_ml[(base + k) * 2];
+    const float lk = ws_ml[(base + k) * 2 + 1];
+    bad |= (lk != lk);
+    M = fmaxf(M, mk);
+  }
+  float L = 0.f, O = 0.f;
+  for (int k = 0; k < nps; ++k) {
+    const float f = fast_exp2(ws_ml[(base + k) * 2] - M);
+    L += ws_ml[(base + k) * 2 + 1] * f;
+    O += ws_o[(base + k) * D + d] * f;
+  }
+  out[((size_t)s * Hq + hq) * D + d] = bad ? __builtin_nanf("") : O / L;
+}
+
+// ============================================================================
+// Slot mapping ([4], "How it works"): slot = table[p / B] * B + p % B.
+// ============================================================================
+__global__ void slot_mapping_kernel(const int32_t* __restrict__ tables, int32_t num_rows,
+                                    int32_t max_blocks, const int32_t* __restrict__ seq_idx,
+                                    const int32_t* __restrict__ pos, int32_t n, int32_t B,
+                                    int64_t* __restrict__ slots) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t s = seq_idx[i], p = pos[i];
+  int64_t out = -1;
+  if (s >= 0 && s < num_rows && p >= 0 && p / B < max_blocks) {
+    const int32_t e = tables[(size_t)s * max_blocks + p / B];
+    if (e >= 0) out = (int64_t)e * B + p % B;
+  }
+  slots[i] = out;
+}
+
+// ============================================================================
+// reshape_and_cache ([3], "The allocation lifecycle"): copy each new token's
+// K and V rows (all KV heads) into its slot. One thread moves 16 bytes of K
+// and 16 bytes of V; consecutive threads cover consecutive bytes of a token,
+// so reads and writes are coalesced per head row.
+// ============================================================================
+__global__ void reshape_and_cache_kernel(const uint4* __restrict__ k_new,
+                                         const uint4* __restrict__ v_new,
+                                         uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+                                         const int64_t* __restrict__ slots, int32_t n,
+                                         int64_t num_slots, int32_t Hkv, int32_t row_u4,
+                                         int32_t B) {
+  const int64_t per_token = (int64_t)Hkv * row_u4;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)n * per_token) return;
+  const int64_t i = t / per_token;
+  const int64_t c = t % per_token;
+  const int64_t h = c / row_u4, cc = c % row_u4;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / B, off = slot % B;
+  const int64_t dst = ((blk * Hkv + h) * B + off) * row_u4 + cc;
+  k_pool[dst] = k_new[t];
+  v_pool[dst] = v_new[t];
+}
+
+// ============================================================================
+// Block copy for copy-on-write ([2], "Copy-on-Write ..."): blockIdx.x = pair,
+// blockIdx.y = layer within this launch's chunk, blockIdx.z = 0 (K) / 1 (V).
+// ============================================================================
+constexpr int kCopyLayers = 64;
+struct CopyPools {
+  uint4* k[kCopyLayers];
+  uint4* v[kCopyLayers];
+};
+
+__global__ void copy_blocks_kernel(CopyPools pools, const int32_t* __restrict__ pairs,
+                                   int32_t num_blocks, int64_t block_u4) {
+  const int32_t src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint4* base = blockIdx.z == 0 ? pools.k[blockIdx.y] : pools.v[blockIdx.y];
+  const uint4* s = base + (int64_t)src * block_u4;
+  uint4* d = base + (int64_t)dst * block_u4;
+  for (int64_t i = threadIdx.x; i < block_u4; i += blockDim.x) d[i] = s[i];
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kv_status launch_status(const char* who) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KV_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return KV_OK;
+}
+
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int32_t effective_partition(int32_t partition_size) {
+  return partition_size == 0 ? kDefaultPartition : partition_size;
+}
+
+template <int DT, int D>
+kv_status launch_valu(const DecodeParams& prm, int gmax, dim3 grid, hipStream_t st) {
+  switch (gmax) {
+    case 1: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 1>), grid, dim3(kThreads), 0, st, prm); break;
+    case 2: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 2>), grid, dim3(kThreads), 0, st, prm); break;
+    case 4: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 4>), grid, dim3(kThreads), 0, st, prm); break;
+    case 8: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 8>), grid, dim3(kThreads), 0, st, prm); break;
+    case 16: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 16>), grid, dim3(kThreads), 0, st, prm); break;
+    default: return fail(KV_ERR_UNSUPPORTED, "decode: group size");
+  }
+  return launch_status("kv_paged_attention_decode");
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status kv_slot_mapping(const int32_t* tables, int32_t num_rows, int32_t max_blocks,
+                          const int32_t* seq_idx, const int32_t* pos, int32_t n,
+                          int32_t block_size, int64_t* slots, hipStream_t stream) {
+  pagedkv::clear_error();
+  if (n < 0 || num_rows < 0 || max_blocks < 0 || block_size <= 0)
+    return fail(KV_ERR_INVALID, "kv_slot_mapping: negative or zero size");
+  if (n == 0) return KV_OK;
+  if (!tables || !seq_idx || !pos || !slots)
+    return fail(KV_ERR_INVALID, "kv_slot_mapping: null pointer");
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3((unsigned)ceil_div64(n, 256)), dim3(256), 0,
+                     stream, tables, num_rows, max_blocks, seq_idx, pos, n, block_size, slots);
+  return launch_status("kv_slot_mapping");
+}
+
+kv_status kv_reshape_and_cache(const void* k_new, const void* v_new, void* k_pool,
+                               void* v_pool, const int64_t* slots, int32_t n,
+                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, kv_dtype dtype, hipStream_t stream) {
+  pagedkv::clear_error();
+  const size_t eb = pagedkv::dtype_bytes(dtype);
+  if (eb == 0) return fail(KV_ERR_UNSUPPORTED, "kv_reshape_and_cache: unknown dtype");
+  if (n < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+    return fail(KV_ERR_INVALID, "kv_reshape_and_cache: bad sizes");
+  if ((head_dim * eb) % 16 != 0)
+    return fail(KV_ERR_UNSUPPORTED, "kv_reshape_and_cache: head_dim*elem must be a multiple of 16 bytes");
+  if (n == 0) return KV_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !slots)
+    return fail(KV_ERR_INVALID, "kv_reshape_and_cache: null pointer");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(KV_ERR_INVALID, "kv_reshape_and_cache: pointers must be 16-byte aligned");
+  const int32_t row_u4 = (int32_t)(head_dim * eb / 16);
+  const int64_t total = (int64_t)n * num_kv_heads * row_u4;
+  const int64_t blocks = ceil_div64(total, 256);
+  if (blocks > INT32_MAX) return fail(KV_ERR_INVALID, "kv_reshape_and_cache: too many tokens");
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                     static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), slots, n,
+                     (int64_t)num_blocks * block_size, num_kv_heads, row_u4, block_size);
+  return launch_status("kv_reshape_and_cache");
+}
+
+kv_status kv_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,
+                         const int32_t* pairs, int32_t n, int32_t num_blocks,
+                         size_t block_bytes, hipStream_t stream) {
+  pagedkv::clear_error();
+  if (n < 0 || num_layers < 0 || num_layers > 256 || num_blocks <= 0)
+    return fail(KV_ERR_INVALID, "kv_copy_blocks: bad sizes");
+  if (block_bytes == 0 || block_bytes % 16 != 0)
+    return fail(KV_ERR_INVALID, "kv_copy_blocks: block_bytes must be a positive multiple of 16");
+  if (n == 0 || num_layers == 0) return KV_OK;
+  if (!k_pools || !v_pools || !pairs) return fail(KV_ERR_INVALID, "kv_copy_blocks: null pointer");
+  for (int32_t i = 0; i < num_layers; ++i)
+    if (!k_pools[i] || !v_pools[i] || !aligned16(k_pools[i]) || !aligned16(v_pools[i]))
+      return fail(KV_ERR_INVALID, "kv_copy_blocks: layer %d pool null or misaligned", i);
+  for (int32_t l0 = 0; l0 < num_layers; l0 += kCopyLayers) {
+    CopyPools cp{};
+    const int32_t nl = num_layers - l0 < kCopyLayers ? num_layers - l0 : kCopyLayers;
+    for (int32_t i = 0; i < nl; ++i) {
+      cp.k[i] = static_cast<uint4*>(k_pools[l0 + i]);
+      cp.v[i] = static_cast<uint4*>(v_pools[l0 + i]);
+    }
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(n, nl, 2), dim3(256), 0, stream, cp, pairs,
+                       num_blocks, (int64_t)(block_bytes / 16));
+    kv_status st = launch_status("kv_copy_blocks");
+    if (st != KV_OK) return st;
+  }
+  return KV_OK;
+}
+
+size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_t head_dim,
+                                          int32_t max_context_len, int32_t partition_size) {
+  const int32_t P = effective_partition(partition_size);
+  if (S < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 || P <= 0) return 0;
+  const int64_t nparts = ceil_div64(max_context_len, P);
+  if (nparts <= 1) return 0;
+  return (size_t)S * num_q_heads * nparts * (head_dim + 2) * sizeof(float);
+}
+
+kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_pool,
+                                    const void* v_pool, const int32_t* block_tables,
+                                    int32_t max_blocks, const int32_t* context_lens, int32_t S,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t num_blocks, float scale,
+                                    kv_dtype dtype, int32_t partition_size,
+                                    int32_t max_context_len, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream) {
+  pagedkv::clear_error();
+  if (pagedkv::dtype_bytes(dtype) == 0)
+    return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: unknown dtype");
+  if (S < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks < 0 || num_blocks <= 0 ||
+      max_context_len < 0)
+    return fail(KV_ERR_INVALID, "kv_paged_attention_decode: bad sizes");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: query heads %d not a multiple of KV heads %d",
+                num_q_heads, num_kv_heads);
+  if (block_size != kBlock)
+    return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: block_size %d (only 16)", block_size);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: head_dim %d (64 or 128)", head_dim);
+  const int32_t G = num_q_heads / num_kv_heads;
+  if (G > 16) return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: group size %d > 16", G);
+  const int32_t P = effective_partition(partition_size);
+  if (P < kBlock || P > kMaxPartition || P % kBlock != 0)
+    return fail(KV_ERR_INVALID, "kv_paged_attention_decode: partition_size %d", partition_size);
+  if (S == 0) return KV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
+    return fail(KV_ERR_INVALID, "kv_paged_attention_decode: null pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(KV_ERR_INVALID, "kv_paged_attention_decode: out/q/pools must be 16-byte aligned");
+  const int64_t nparts = ceil_div64(max_context_len, P) < 1 ? 1 : ceil_div64(max_context_len, P);
+  const size_t need = kv_paged_attention_workspace_bytes(S, num_q_heads, head_dim,
+                                                         max_context_len, partition_size);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace)))
+    return fail(KV_ERR_INVALID, "kv_paged_attention_decode: workspace of %zu bytes needed (got %zu)",
+                need, ws_bytes);
+  const int64_t nwg = nparts * num_kv_heads * (int64_t)S;
+  if (nwg > INT32_MAX) return fail(KV_ERR_INVALID, "kv_paged_attention_decode: grid too large");
+
+  DecodeParams prm;
+  prm.out = out;
+  prm.q = q;
+  prm.k_pool = k_pool;
+  prm.v_pool = v_pool;
+  prm.tables = block_tables;
+  prm.lens = context_lens;
+  float* ws = static_cast<float*>(workspace);
+  const size_t o_elems = (size_t)S * num_q_heads * nparts * head_dim;
+  prm.ws_o = need ? ws : nullptr;
+  prm.ws_ml = need ? ws + o_elems : nullptr;
+  prm.max_blocks = max_blocks;
+  prm.S = S;
+  prm.Hq = num_q_heads;
+  prm.Hkv = num_kv_heads;
+  prm.G = G;
+  prm.num_blocks = num_blocks;
+  prm.part_tokens = P;
+  prm.nparts = (int32_t)nparts;
+  prm.scale_log2 = scale * 1.4426950408889634f;
+
+  const dim3 grid((unsigned)nwg);
+  kv_status st;
+  const bool mfma = (dtype == KV_F16 || dtype == KV_BF16) && head_dim == 128 && G >= 2;
+  if (mfma) {
+    if (dtype == KV_BF16)
+      hipLaunchKernelGGL(decode_mfma_kernel<KV_BF16>, grid, dim3(kThreads), 0, stream, prm);
+    else
+      hipLaunchKernelGGL(decode_mfma_kernel<KV_F16>, grid, dim3(kThreads), 0, stream, prm);
+    st = launch_status("kv_paged_attention_decode");
+  } else {
+    const int gmax = G == 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
+    if (dtype == KV_F32)
+      st = head_dim == 64 ? launch_valu<KV_F32, 64>(prm, gmax, grid, stream)
+                          : launch_valu<KV_F32, 128>(prm, gmax, grid, stream);
+    else if (dtype == KV_F16)
+      st = head_dim == 64 ? launch_valu<KV_F16, 64>(prm, gmax, grid, stream)
+                          : launch_valu<KV_F16, 128>(prm, 1, grid, stream);
+    else
+      st = head_dim == 64 ? launch_valu<KV_BF16, 64>(prm, gmax, grid, stream)
+                          : launch_valu<KV_BF16, 128>(prm, 1, grid, stream);
+  }
+  if (st != KV_OK) return st;
+  if (nparts > 1) {
+    const dim3 rgrid((unsigned)num_q_heads, (unsigned)S);
+    if (head_dim == 128)
+      hipLaunchKernelGGL(splitk_reduce_kernel<128>, rgrid, dim3(128), 0, stream, out, prm.ws_o,
+                         prm.ws_ml, context_lens, num_q_heads, prm.nparts, P, max_blocks);
+    else
+      hipLaunchKernelGGL(splitk_reduce_kernel<64>, rgrid, dim3(64), 0, stream, out, prm.ws_o,
+                         prm.ws_ml, context_lens, num_q_heads, prm.nparts, P, max_blocks);
+    st = launch_status("kv_paged_attention_decode (reduce)");
+  }
+  return st;
+}
+
+}  // extern "C"

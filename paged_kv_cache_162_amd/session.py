@@ -1,0 +1,132 @@
+"""One layer's paged KV cache on the GPU and the decode step over it.
+
+DecodeSession ties the host block manager (libpagedkv's kv_pool_* / kv_seq_*)
+to device buffers owned by torch, and runs the decode step as the pages'
+lifecycle describes it ("PagedAttention and vLLM: Virtual Memory for the KV
+Cache", passgenai.com, "The allocation lifecycle"): reserve a slot for each
+sequence's new token, write the token's K/V into it, then attend over the
+whole cache. The host part (`prepare_step`) and the device part (`step`) are
+separate so a benchmark can time the device part alone.
+
+Operation scripts are lists of tuples: ("create", s), ("fork", parent, child),
+("append", s, n) where s are caller-chosen sequence numbers.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import binding as kv
+
+
+class DecodeSession:
+    def __init__(self, *, k_pool, v_pool, num_q_heads: int, free_order: Optional[Sequence[int]] = None,
+                 partition_size: int = 0):
+        import torch
+        self.torch = torch
+        NB, Hkv, B, D = k_pool.shape
+        self.k_pool, self.v_pool = k_pool, v_pool
+        self.NB, self.Hkv, self.B, self.D, self.Hq = NB, Hkv, B, D, num_q_heads
+        self.dtype = kv.dtype_code(k_pool)
+        self.partition_size = partition_size
+        self.pool = kv.kv_pool_create(NB, B, 1, Hkv, D, self.dtype)
+        if free_order is not None:
+            kv.kv_pool_set_free_order(self.pool, free_order)
+        self.handles: Dict[int, int] = {}
+        self.block_bytes = Hkv * B * D * k_pool.element_size()
+        self.device = k_pool.device
+
+    def close(self) -> None:
+        if self.pool:
+            kv.kv_pool_destroy(self.pool)
+            self.pool = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- host operations (plus the device writes they imply) ----------------
+    def run_ops(self, ops, values: Optional[Dict[int, Tuple]] = None) -> List[Tuple[int, int]]:
+        """Apply an operation script. Copy-on-write pairs reported by an
+        append are copied on the device at once. An append tagged "values"
+        (4th element) then writes values[s] = (k, v), device tensors
+        [n, Hkv, D], into the new slots. Returns the copy-on-write pairs."""
+        torch = self.torch
+        cows: List[Tuple[int, int]] = []
+        for op in ops:
+            if op[0] == "create":
+                self.handles[op[1]] = kv.kv_seq_create(self.pool)
+            elif op[0] == "fork":
+                self.handles[op[2]] = kv.kv_seq_fork(self.pool, self.handles[op[1]])
+            elif op[0] == "append":
+                s, n = op[1], op[2]
+                slots, pair = kv.kv_seq_append(self.pool, self.handles[s], n)
+                if pair is not None:
+                    cows.append(pair)
+                    p = torch.tensor([pair], dtype=torch.int32, device=self.device)
+                    kv.kv_copy_blocks([self.k_pool], [self.v_pool], p, self.NB, self.block_bytes)
+                if len(op) > 3 and op[3] == "values":
+                    k, v = values[s]
+                    d_slots = torch.from_numpy(slots).to(self.device)
+                    kv.kv_reshape_and_cache(k, v, self.k_pool, self.v_pool, d_slots)
+            else:
+                raise ValueError(op)
+        return cows
+
+    def tables(self, seqs: Sequence[int], max_blocks: Optional[int] = None):
+        ids = [self.handles[s] for s in seqs]
+        if max_blocks is None:
+            max_blocks = max(1, max(-(-kv.kv_seq_len(self.pool, h) // self.B) for h in ids))
+        return kv.kv_seq_pack_tables(self.pool, ids, max_blocks)
+
+    # -- the decode step ----------------------------------------------------
+    def prepare_step(self, seqs: Sequence[int]):
+        """Host half of a decode step: reserve one new slot per sequence and
+        upload tables, lengths and the (sequence, position) list. Returns the
+        host-side slots the allocator chose and any copy-on-write pairs."""
+        torch = self.torch
+        host_slots = np.zeros(len(seqs), dtype=np.int64)
+        pairs = []
+        for i, s in enumerate(seqs):
+            sl, pair = kv.kv_seq_append(self.pool, self.handles[s], 1)
+            host_slots[i] = sl[0]
+            if pair is not None:
+                pairs.append(pair)
+        tables, lens = self.tables(seqs)
+        dev = self.device
+        self.seqs = list(seqs)
+        self.d_tables = torch.from_numpy(tables).to(dev)
+        self.d_lens = torch.from_numpy(lens).to(dev)
+        self.d_seq_idx = torch.arange(len(seqs), dtype=torch.int32, device=dev)
+        self.d_pos = (self.d_lens - 1).contiguous()
+        self.d_slots = torch.empty(len(seqs), dtype=torch.int64, device=dev)
+        self.d_pairs = torch.tensor(pairs, dtype=torch.int32, device=dev).reshape(-1, 2)
+        self.max_context_len = int(lens.max()) if len(lens) else 0
+        S = len(seqs)
+        ws = kv.kv_paged_attention_workspace_bytes(S, self.Hq, self.D, self.max_context_len,
+                                                   self.partition_size)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev) if ws else None
+        self.host_tables, self.host_lens = tables, lens
+        return host_slots, pairs
+
+    def step(self, q, k_new, v_new, out, scale: float, k_pool=None, v_pool=None,
+             decode_events=None) -> None:
+        """Device half of a decode step, all on the current stream: slot
+        mapping, copy-on-write copies, cache write, decode attention.
+        `decode_events` = (start, end) torch events recorded around the
+        decode-attention call."""
+        kp = self.k_pool if k_pool is None else k_pool
+        vp_ = self.v_pool if v_pool is None else v_pool
+        kv.kv_slot_mapping(self.d_tables, self.d_seq_idx, self.d_pos, self.d_slots, self.B)
+        if self.d_pairs.shape[0]:
+            kv.kv_copy_blocks([kp], [vp_], self.d_pairs, self.NB, self.block_bytes)
+        kv.kv_reshape_and_cache(k_new, v_new, kp, vp_, self.d_slots)
+        if decode_events is not None:
+            decode_events[0].record()
+        kv.kv_paged_attention_decode(out, q, kp, vp_, self.d_tables, self.d_lens, scale,
+                                     self.max_context_len, self.workspace, self.partition_size)
+        if decode_events is not None:
+            decode_events[1].record()

@@ -1,0 +1,317 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact for slot mapping, the cache scatter and block copies; attention
+within max |err| <= 1e-5 (fp32 inputs) or max |err| / RMS(oracle) <= 2e-3
+(fp16/bf16 inputs). Every workload runs through the same session code the
+benchmark times.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as oa
+from workloads import round_to_dtype
+from gpu_common import (Case, check_attention, log, to_dev, to_host, bits, POISON)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_162_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+
+
+def kvlib():
+    import paged_kv_cache_162_amd as kv
+    return kv
+
+
+# ---------------------------------------------------------------------------
+# integer and byte work: bit exact
+# ---------------------------------------------------------------------------
+def test_slot_mapping_bit_exact():
+    kv = kvlib()
+    rng = np.random.default_rng(7)
+    rows, maxb = 37, 9
+    tables = rng.integers(-1, 5000, size=(rows, maxb)).astype(np.int32)
+    n = 4099
+    seq = rng.integers(-2, rows + 2, size=n).astype(np.int32)
+    pos = rng.integers(-3, maxb * 16 + 5, size=n).astype(np.int32)
+    log("[gpu] slot mapping n=%d" % n)
+    d_slots = torch.empty(n, dtype=torch.int64, device="cuda")
+    kv.kv_slot_mapping(torch.from_numpy(tables).cuda(), torch.from_numpy(seq).cuda(),
+                       torch.from_numpy(pos).cuda(), d_slots)
+    got = d_slots.cpu().numpy()
+    ok = (seq >= 0) & (seq < rows)
+    ref = np.full(n, -1, np.int64)
+    ref[ok] = oa.slot_mapping(tables, seq[ok], pos[ok])
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("dt,D", [("f32", 64), ("f16", 128), ("bf16", 128), ("bf16", 64), ("f32", 128)])
+def test_reshape_and_cache_bit_exact(dt, D):
+    kv = kvlib()
+    rng = np.random.default_rng(11)
+    NB, Hkv, n = 50, 3, 123
+    store = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16}[dt]
+    nb = np.dtype(store).itemsize
+    kp = rng.integers(0, 2 ** (8 * nb), size=(NB, Hkv, 16, D), dtype=np.uint64).astype(store)
+    vp = rng.integers(0, 2 ** (8 * nb), size=(NB, Hkv, 16, D), dtype=np.uint64).astype(store)
+    kn = rng.integers(0, 2 ** (8 * nb), size=(n, Hkv, D), dtype=np.uint64).astype(store)
+    vn = rng.integers(0, 2 ** (8 * nb), size=(n, Hkv, D), dtype=np.uint64).astype(store)
+    slots = rng.choice(NB * 16, size=n, replace=False).astype(np.int64)
+    slots[::17] = -1
+    slots[5] = NB * 16 + 3  # out of range: skipped
+    view = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dt]
+    log(f"[gpu] reshape_and_cache {dt} D={D} n={n}")
+    dk, dv = to_dev(kp.view(view), dt), to_dev(vp.view(view), dt)
+    kv.kv_reshape_and_cache(to_dev(kn.view(view), dt), to_dev(vn.view(view), dt), dk, dv,
+                            torch.from_numpy(slots).cuda())
+    ok = (slots >= 0) & (slots < NB * 16)
+    rk, rv = kp.copy().view(view), vp.copy().view(view)
+    oa.reshape_and_cache(kn.view(view)[ok], vn.view(view)[ok], rk, rv, slots[ok])
+    assert np.array_equal(bits(to_host(dk, dt)), bits(rk))
+    assert np.array_equal(bits(to_host(dv, dt)), bits(rv))
+
+
+def test_copy_blocks_bit_exact():
+    kv = kvlib()
+    rng = np.random.default_rng(12)
+    L, NB, Hkv, D = 3, 40, 2, 128
+    pools = [rng.integers(0, 2 ** 16, size=(NB, Hkv, 16, D), dtype=np.uint64).astype(np.uint16)
+             for _ in range(2 * L)]
+    perm = rng.permutation(NB)
+    pairs = np.stack([perm[:10], perm[10:20]], axis=1).astype(np.int32)  # no chaining
+    bad = np.array([[NB + 1, 3], [2, -1]], dtype=np.int32)               # skipped on device
+    dev = [to_dev(p, "bf16") for p in pools]
+    log("[gpu] copy_blocks")
+    kv.kv_copy_blocks(dev[:L], dev[L:], torch.from_numpy(np.concatenate([pairs, bad])).cuda(),
+                      NB, Hkv * 16 * D * 2)
+    oa.copy_blocks(pools, [tuple(p) for p in pairs])
+    for d, p in zip(dev, pools):
+        assert np.array_equal(to_host(d, "bf16"), p)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads (+ the copy-on-write variant), end to end
+# ---------------------------------------------------------------------------
+def sample_pairs(case, n, rng):
+    S, Hq = case.sp.S, case.sp.Hq
+    pairs = {(int(rng.integers(S)), int(rng.integers(Hq))) for _ in range(n)}
+    longest = int(np.argmax(case.lens))
+    pairs |= {(longest, 0), (longest, Hq - 1), (0, 0), (S - 1, Hq - 1)}
+    return sorted(pairs)
+
+
+def run_workload(cfg, S=None, full_pool_compare=True, n_sample=None, partition_size=0):
+    case = Case(cfg, S=S, partition_size=partition_size)
+    cows, host_slots, step_pairs = case.device_run()
+    sp = case.sp
+    # allocator parity (C++ vs oracle model)
+    assert len(cows) == len(case.setup_pairs) and [tuple(c) for c in cows] == case.setup_pairs
+    assert np.array_equal(host_slots, case.step_slots) and not step_pairs
+    assert np.array_equal(case.sess.host_tables[:, :case.tables.shape[1]], case.tables)
+    assert np.array_equal(case.sess.host_lens, case.lens)
+    # slot mapping kernel and scatter: bit exact
+    assert np.array_equal(case.sess.d_slots.cpu().numpy(), case.step_slots)
+    if full_pool_compare:
+        assert np.array_equal(bits(to_host(case.k_dev, case.dt)), bits(case.k_ref))
+        assert np.array_equal(bits(to_host(case.v_dev, case.dt)), bits(case.v_ref))
+    else:
+        blocks = np.unique(np.concatenate([case.step_slots // 16,
+                                           np.random.default_rng(3).integers(0, case.w.num_blocks, 64)]))
+        idx = torch.from_numpy(blocks).cuda()
+        assert np.array_equal(bits(to_host(case.k_dev[idx], case.dt)), bits(case.k_ref[blocks]))
+        assert np.array_equal(bits(to_host(case.v_dev[idx], case.dt)), bits(case.v_ref[blocks]))
+    got = case.out_dev.cpu().numpy()
+    if n_sample is None:
+        ref = case.oracle_out()
+        stats = check_attention(got.reshape(-1, sp.D), ref.reshape(-1, sp.D), case.dt, sp.name)
+    else:
+        pairs = sample_pairs(case, n_sample, np.random.default_rng(cfg))
+        ref = case.oracle_out(pairs)
+        g = np.stack([got[s, h] for s, h in pairs])
+        r = np.stack([ref[s, h] for s, h in pairs])
+        stats = check_attention(g, r, case.dt, sp.name)
+        assert np.isfinite(got).all()
+    log(f"[ok] {sp.name}: {stats}")
+    return case
+
+
+def test_workload_tiny_fp32():
+    run_workload(1)
+
+
+def test_workload_tiny_fp32_every_partition_size():
+    for ps in (16, 32, 48):
+        run_workload(1, partition_size=ps)
+
+
+def test_workload_llama13b_mha_fp16():
+    run_workload(2, full_pool_compare=False, n_sample=48)
+
+
+def test_workload_llama70b_gqa_bf16():
+    run_workload(3, n_sample=96)
+
+
+def test_workload_longctx_splitk_bf16():
+    run_workload(4, full_pool_compare=False, n_sample=24)
+
+
+def test_workload_prefix_share_bf16():
+    case = run_workload(5, n_sample=64)
+    # 128 shared prefix blocks with reference count 32
+    t0 = case.tables[0][:128]
+    assert all((case.tables[s][:128] == t0).all() for s in range(case.sp.S))
+
+
+def test_workload_prefix_cow_bf16():
+    case = run_workload(6, n_sample=64)
+    assert len(case.setup_pairs) == 31
+
+
+def test_truncated_workloads_full_output():
+    # complete outputs (no sampling) at sizes the oracle finishes quickly
+    run_workload(3, S=12)
+    run_workload(2, S=3, full_pool_compare=False)
+
+
+# ---------------------------------------------------------------------------
+# kernel coverage on random ragged shapes (every dtype / head_dim / group)
+# ---------------------------------------------------------------------------
+def random_case(rng, lens, Hq, Hkv, D, dt, num_blocks=None, poison=True):
+    nbs = [-(-t // 16) for t in lens]
+    NB = num_blocks or (sum(nbs) + 5)
+    perm = rng.permutation(NB)
+    tab = np.full((len(lens), max(nbs + [1])), -1, np.int32)
+    off = 0
+    for s, nb in enumerate(nbs):
+        tab[s, :nb] = perm[off:off + nb]
+        off += nb
+    kp = round_to_dtype(rng.standard_normal((NB, Hkv, 16, D)).astype(np.float32), dt)
+    vp = round_to_dtype(rng.standard_normal((NB, Hkv, 16, D)).astype(np.float32), dt)
+    if poison:
+        live = np.zeros((NB, 16), bool)
+        for s, t in enumerate(lens):
+            for p in range(t):
+                live[tab[s, p // 16], p % 16] = True
+        for pool in (kp, vp):
+            b = bits(pool)
+            dead = np.argwhere(~live)
+            b[dead[:, 0], :, dead[:, 1], :] = POISON[dt]
+    q = round_to_dtype(rng.standard_normal((len(lens), Hq, D)).astype(np.float32), dt)
+    return q, kp, vp, tab, np.array(lens, np.int32)
+
+
+def gpu_decode(q, kp, vp, tab, lens, scale, dt, partition_size=0, max_ctx=None):
+    kv = kvlib()
+    S, Hq, D = q.shape
+    out = torch.full((S, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    mc = int(lens.max()) if max_ctx is None else max_ctx
+    wsb = kv.kv_paged_attention_workspace_bytes(S, Hq, D, mc, partition_size)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
+    kv.kv_paged_attention_decode(out, to_dev(q, dt), to_dev(kp, dt), to_dev(vp, dt),
+                                 torch.from_numpy(tab).cuda(), torch.from_numpy(lens).cuda(),
+                                 scale, mc, ws, partition_size)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+SHAPES = [(dt, D, G) for dt in ("f32", "f16", "bf16") for D in (64, 128) for G in (1, 2, 4, 8, 16)]
+
+
+@pytest.mark.parametrize("dt,D,G", SHAPES)
+def test_decode_shapes_against_oracle(dt, D, G):
+    rng = np.random.default_rng(hash((dt, D, G)) % 2 ** 32)
+    lens = [1, 15, 16, 17, 33, 100, 511, 512, 513, 700]
+    Hkv = 2
+    q, kp, vp, tab, cl = random_case(rng, lens, G * Hkv, Hkv, D, dt)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    ref = oracle.decode_attention(q, kp, vp, tab, cl, scale, dt)
+    for ps in (0, 64, 16):
+        log(f"[gpu] decode {dt} D={D} G={G} partition={ps}")
+        got = gpu_decode(q, kp, vp, tab, cl, scale, dt, ps)
+        check_attention(got.reshape(-1, D), ref.reshape(-1, D), dt, f"{dt}/{D}/{G}/{ps}")
+
+
+def test_zero_length_and_invalid_sequences():
+    rng = np.random.default_rng(21)
+    dt, D, Hkv, G = "bf16", 128, 2, 4
+    lens = [40, 0, 33, 20]
+    q, kp, vp, tab, cl = random_case(rng, lens, G * Hkv, Hkv, D, dt)
+    tab[2, 1] = 10_000          # live entry outside the pool -> that sequence is NaN
+    cl2 = cl.copy()
+    cl2[3] = tab.shape[1] * 16 + 1  # longer than its table -> NaN
+    log("[gpu] invalid sequences")
+    got = gpu_decode(q, kp, vp, tab, cl2, 0.1, dt, 16)
+    assert np.all(got[1] == 0.0)
+    assert np.isnan(got[2]).all() and np.isnan(got[3]).all()
+    ref = oracle.decode_attention(q, kp, vp, tab, cl, 0.1, dt, pairs=[(0, h) for h in range(8)])
+    check_attention(got[0], ref[0], dt, "valid neighbour")
+    # a length beyond max_context_len is caught too
+    got = gpu_decode(q, kp, vp, tab, cl, 0.1, dt, 16, max_ctx=32)
+    assert np.isnan(got[0]).all() and np.isnan(got[2]).all() and np.isfinite(got[3]).all()
+
+
+def test_placement_invariance_bitwise():
+    """Same logical cache in two different physical placements: identical bits."""
+    rng = np.random.default_rng(31)
+    dt, D, Hkv, G = "bf16", 128, 4, 8
+    lens = [5, 300, 1030, 77]
+    q, kp, vp, tab, cl = random_case(rng, lens, G * Hkv, Hkv, D, dt, poison=False)
+    NB = kp.shape[0]
+    perm = rng.permutation(NB)            # move physical block b to perm[b]
+    kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+    kp2[perm], vp2[perm] = kp, vp
+    tab2 = np.where(tab >= 0, perm[np.maximum(tab, 0)], -1).astype(np.int32)
+    for ps in (0, 128):
+        a = gpu_decode(q, kp, vp, tab, cl, 0.09, dt, ps)
+        b = gpu_decode(q, kp2, vp2, tab2, cl, 0.09, dt, ps)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_shared_prefix_bitwise_equals_duplicated():
+    rng = np.random.default_rng(32)
+    dt, D, Hkv, G = "bf16", 128, 2, 4
+    pre_blocks, tails = 6, [3, 17, 40]
+    nb_t = [-(-t // 16) for t in tails]
+    NB = pre_blocks + sum(nb_t)
+    kp = round_to_dtype(rng.standard_normal((NB, Hkv, 16, D)).astype(np.float32), dt)
+    vp = round_to_dtype(rng.standard_normal((NB, Hkv, 16, D)).astype(np.float32), dt)
+    lens = np.array([pre_blocks * 16 + t for t in tails], np.int32)
+    shared = np.full((3, pre_blocks + max(nb_t)), -1, np.int32)
+    off = pre_blocks
+    for s, nb in enumerate(nb_t):
+        shared[s, :pre_blocks] = np.arange(pre_blocks)
+        shared[s, pre_blocks:pre_blocks + nb] = np.arange(off, off + nb)
+        off += nb
+    # duplicated: every sequence gets a private copy of the prefix blocks
+    kd = np.concatenate([kp] + [kp[:pre_blocks]] * 3)
+    vd = np.concatenate([vp] + [vp[:pre_blocks]] * 3)
+    dup = shared.copy()
+    for s in range(3):
+        dup[s, :pre_blocks] = NB + s * pre_blocks + np.arange(pre_blocks)
+    q = round_to_dtype(rng.standard_normal((3, G * Hkv, D)).astype(np.float32), dt)
+    a = gpu_decode(q, kp, vp, shared, lens, 0.1, dt)
+    b = gpu_decode(q, kd, vd, dup, lens, 0.1, dt)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_split_and_unsplit_agree_and_runs_are_deterministic():
+    rng = np.random.default_rng(33)
+    dt, D, Hkv, G = "bf16", 128, 2, 4
+    lens = [4097, 2000, 16, 9000]
+    q, kp, vp, tab, cl = random_case(rng, lens, G * Hkv, Hkv, D, dt)
+    ref = oracle.decode_attention(q, kp, vp, tab, cl, 0.088, dt)
+    outs = {}
+    for ps in (256, 512, 8192):
+        outs[ps] = gpu_decode(q, kp, vp, tab, cl, 0.088, dt, ps)
+        check_attention(outs[ps].reshape(-1, D), ref.reshape(-1, D), dt, f"partition {ps}")
+    again = gpu_decode(q, kp, vp, tab, cl, 0.088, dt, 512)
+    assert np.array_equal(again.view(np.uint32), outs[512].view(np.uint32))

@@ -138,8 +138,11 @@ def spec(cfg: int) -> WorkloadSpec:
 
 
 # Operation script entries: ("create", seq) | ("append", seq, n) |
-# ("fork", parent, child). Sequence handles are small integers local to the
-# script; each side maps them to its own handles.
+# ("append", seq, n, "values") | ("fork", parent, child). Sequence handles are
+# small integers local to the script; each side maps them to its own handles.
+# An append tagged "values" writes the sequence's next rows of tail_k/tail_v
+# into the new slots; untagged appends reserve slots whose content is the
+# pool's synthetic fill.
 Op = Tuple
 
 
@@ -240,7 +243,8 @@ def make_workload(cfg: int, seed: Optional[int] = None, *, with_values: bool = T
         for c in range(1, sp.S):
             setup.append(("fork", 0, c))
         for s_ in range(sp.S):
-            setup.append(("append", s_, sp.tail))
+            # tagged: these tokens' K/V are written from tail_k / tail_v
+            setup.append(("append", s_, sp.tail, "values"))
     else:
         for s_ in range(sp.S):
             setup.append(("create", s_))
