@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--workload", type=int, default=3, help="workload number 1-6")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas to rotate (0 = auto)")
+    ap.add_argument("--no-plan", action="store_true", help="padded grid instead of the host work plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--pmc-traffic", default="", help="JSON file with measured HBM traffic per launch")
@@ -70,7 +71,7 @@ def decode_alg_bytes(lens, S, Hq, Hkv, D, eb):
 def cpu_baseline(w, seconds):
     """The oracle, untouched, timed on this host on the same workload: the
     whole decode (gather through the block table + fp64 attention) over all
-    sequences, repeated until `seconds` have elapsed (at most 5 passes)."""
+    sequences, repeated until `seconds` have elapsed (at most 50 passes)."""
     from threadpoolctl import threadpool_limits
     import oracle
     from oracle.block_manager import run_ops
@@ -80,7 +81,7 @@ def cpu_baseline(w, seconds):
     sp = w.spec
     passes, t_total = 0, 0.0
     with threadpool_limits(limits=1):
-        while passes < 5 and (passes == 0 or t_total < seconds):
+        while passes < 50 and (passes == 0 or t_total < seconds):
             t0 = time.perf_counter()
             oracle.decode_attention(w.q, w.k_pool, w.v_pool, tables, lens, sp.scale, sp.dtype)
             t_total += time.perf_counter() - t0
@@ -116,7 +117,7 @@ def main():
           file=sys.stderr, flush=True)
     kp, vp = to_dev(w.k_pool, dt), to_dev(w.v_pool, dt)
     sess = DecodeSession(k_pool=kp, v_pool=vp, num_q_heads=sp.Hq, free_order=w.free_order,
-                         partition_size=args.partition)
+                         partition_size=args.partition, use_plan=not args.no_plan)
     values = {}
     if w.tail_k is not None:
         values = {s: (to_dev(w.tail_k[s], dt), to_dev(w.tail_v[s], dt)) for s in range(sp.S)}

@@ -194,6 +194,21 @@ kv_status kv_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num
  * "The Custom CUDA Kernel"; [3], "The kernel change").
  * ------------------------------------------------------------------------- */
 
+/* Work plan for kv_paged_attention_decode, built on the host from the host
+ * copy of the context lengths (the block manager has them): the list of
+ * (sequence, partition) items that hold tokens, longest first - every full
+ * partition, then partial last partitions by decreasing length, then one
+ * item for each sequence of length <= 0 (so its output is still written).
+ * items_out: host int32 [cap][2] receiving (sequence, partition) pairs;
+ * *n_items receives the item count, which is at most
+ * S * ceil(max_len / partition) (KV_ERR_INVALID with *n_items set if cap is
+ * smaller). partition_size as for the decode (0 = 512). The caller copies
+ * the items to the device and passes them to the decode with the same
+ * lengths and partition size. */
+kv_status kv_paged_attention_plan(const int32_t* context_lens_host, int32_t S,
+                                  int32_t partition_size, int32_t* items_out, int32_t cap,
+                                  int32_t* n_items);
+
 /* Workspace bytes kv_paged_attention_decode needs for these sizes: 0 when
  * max_context_len <= the partition size (every sequence finishes in one
  * partition), else S * num_q_heads * num_partitions * (head_dim + 2) * 4 for
@@ -218,6 +233,12 @@ size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_
  *               Sequences longer than one partition are split and merged
  *               with a log-sum-exp reduction ([2], "The Custom CUDA Kernel":
  *               per-piece partial outputs and denominators merged stably).
+ * work_items:   optional device int32 [n_items][2] from
+ *               kv_paged_attention_plan; the grid is then exactly n_items *
+ *               num_kv_heads workgroups. NULL: the grid covers every possible
+ *               partition, S * num_kv_heads * ceil(max_context_len /
+ *               partition), and workgroups past a sequence's end exit at once.
+ *               Items whose sequence or partition is out of range are skipped.
  * workspace:    device scratch of at least
  *               kv_paged_attention_workspace_bytes(...) bytes (may be NULL
  *               when that is 0).
@@ -237,7 +258,8 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t block_size, int32_t num_blocks, float scale,
                                     kv_dtype dtype, int32_t partition_size,
-                                    int32_t max_context_len, void* workspace, size_t ws_bytes,
+                                    int32_t max_context_len, const int32_t* work_items,
+                                    int32_t n_items, void* workspace, size_t ws_bytes,
                                     hipStream_t stream);
 
 /* Message describing the calling thread's last error ("" if none). */

@@ -71,9 +71,11 @@ _SIGS = {
     "kv_slot_mapping": (C.c_int, [vp, i32, i32, vp, vp, i32, i32, vp, vp]),
     "kv_reshape_and_cache": (C.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, C.c_int, vp]),
     "kv_copy_blocks": (C.c_int, [C.POINTER(vp), C.POINTER(vp), i32, vp, i32, i32, C.c_size_t, vp]),
+    "kv_paged_attention_plan": (C.c_int, [P_i32, i32, i32, P_i32, i32, P_i32]),
     "kv_paged_attention_workspace_bytes": (C.c_size_t, [i32, i32, i32, i32, i32]),
     "kv_paged_attention_decode": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
-                                            i32, f32, C.c_int, i32, i32, vp, C.c_size_t, vp]),
+                                            i32, f32, C.c_int, i32, i32, vp, i32, vp, C.c_size_t,
+                                            vp]),
     "kv_last_error": (C.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -263,6 +265,19 @@ def kv_copy_blocks(k_pools: List, v_pools: List, pairs, num_blocks: int, block_b
                               num_blocks, block_bytes, _stream(stream)), "kv_copy_blocks")
 
 
+def kv_paged_attention_plan(context_lens_host, partition_size: int = 0) -> np.ndarray:
+    """Host work plan: int32 [n_items, 2] (sequence, partition), longest first."""
+    lens = _i32_array(context_lens_host)
+    n = i32()
+    st = lib.kv_paged_attention_plan(_p32(lens), len(lens), partition_size, None, 0, C.byref(n))
+    if st != KV_OK and n.value == 0:
+        _check(st, "kv_paged_attention_plan")
+    out = np.zeros((max(n.value, 1), 2), dtype=np.int32)
+    _check(lib.kv_paged_attention_plan(_p32(lens), len(lens), partition_size, _p32(out),
+                                       out.shape[0], C.byref(n)), "kv_paged_attention_plan")
+    return out[:n.value]
+
+
 def kv_paged_attention_workspace_bytes(S: int, num_q_heads: int, head_dim: int,
                                        max_context_len: int, partition_size: int = 0) -> int:
     return int(lib.kv_paged_attention_workspace_bytes(S, num_q_heads, head_dim,
@@ -271,9 +286,10 @@ def kv_paged_attention_workspace_bytes(S: int, num_q_heads: int, head_dim: int,
 
 def kv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale: float,
                               max_context_len: int, workspace=None, partition_size: int = 0,
-                              stream=None) -> None:
+                              work_items=None, stream=None) -> None:
     """out fp32 [S, Hq, D]; q [S, Hq, D]; pools [NB, Hkv, B, D]; tables int32 [S, max_blocks];
-    context_lens int32 [S]; workspace: uint8/any device tensor or None."""
+    context_lens int32 [S]; workspace: uint8/any device tensor or None; work_items: device
+    int32 [n, 2] from kv_paged_attention_plan or None."""
     torch = _torch()
     S, Hq, D = q.shape
     NB, Hkv, B, D2 = k_pool.shape
@@ -286,5 +302,7 @@ def kv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens
         _dev(out, "out", torch.float32), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, B, NB, float(scale),
-        dtype_code(q), partition_size, max_context_len, ws_ptr or None, ws_bytes, _stream(stream)),
+        dtype_code(q), partition_size, max_context_len,
+        None if work_items is None else _dev(work_items, "work_items", torch.int32),
+        0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes, _stream(stream)),
         "kv_paged_attention_decode")

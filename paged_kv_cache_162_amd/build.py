@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedkv.so")
-SOURCES = [os.path.join(CSRC, "host_pool.cpp"), os.path.join(CSRC, "kernels.hip")]
+SOURCES = [os.path.join(CSRC, "host_pool.cpp"), os.path.join(CSRC, "plan.cpp"),
+           os.path.join(CSRC, "kernels.hip")]
 ARCH = os.environ.get("PAGEDKV_ARCH", "gfx950")
 
 

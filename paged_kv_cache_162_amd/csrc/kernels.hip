@@ -49,7 +49,6 @@ constexpr int kBlock = 16;          // tokens per KV block (device kernels)
 constexpr int kWaves = 4;           // wave64s per decode workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxPartition = 8192; // tokens
-constexpr int kMaxPartBlocks = kMaxPartition / kBlock;
 constexpr int kDefaultPartition = 512;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -107,24 +106,39 @@ struct DecodeParams {
   const void* v_pool;
   const int32_t* tables;
   const int32_t* lens;
+  const int32_t* items;  // optional work plan: [n_items][2] = (sequence, partition)
   float* ws_o;   // [S][Hq][nparts][D]
   float* ws_ml;  // [S][Hq][nparts][2]
-  int32_t max_blocks, S, Hq, Hkv, G, num_blocks, part_tokens, nparts;
+  int32_t max_blocks, S, Hq, Hkv, G, num_blocks, part_tokens, nparts, n_items;
   float scale_log2;
 };
 
-// Work-item decode: blockIdx.x enumerates (partition, KV head, sequence) with
-// the sequence fastest, so every first partition is dispatched before any
-// second one and long sequences' extra partitions come last.
+// Work item of this workgroup. With a plan, blockIdx.x = item * Hkv + head:
+// consecutive workgroups take the KV heads of one item, so with the
+// round-robin workgroup-to-XCD dispatch a given head of every sequence lands
+// on the same XCD whenever Hkv is a multiple or divisor of the XCD count
+// (shared prefix blocks of one head then hit in that XCD's L2). Without a
+// plan, blockIdx.x enumerates (partition, head, sequence) over every possible
+// partition and the workgroups past a sequence's end exit at once.
 struct WorkItem {
   int s, h, part;
+  bool ok;
 };
 __device__ __forceinline__ WorkItem work_item(const DecodeParams& p) {
-  const int L = blockIdx.x;
   WorkItem w;
-  w.s = L % p.S;
-  w.h = (L / p.S) % p.Hkv;
-  w.part = L / (p.S * p.Hkv);
+  const int L = blockIdx.x;
+  if (p.items) {
+    const int it = L / p.Hkv;
+    w.h = L % p.Hkv;
+    w.s = p.items[2 * it];
+    w.part = p.items[2 * it + 1];
+    w.ok = w.s >= 0 && w.s < p.S && w.part >= 0 && w.part < p.nparts;
+  } else {
+    w.s = L % p.S;
+    w.h = (L / p.S) % p.Hkv;
+    w.part = L / (p.S * p.Hkv);
+    w.ok = true;
+  }
   return w;
 }
 
@@ -149,48 +163,71 @@ __device__ __forceinline__ bool sequence_prologue(const DecodeParams& p, const W
   return w.part < nps;
 }
 
+// Dynamic LDS of a decode workgroup: the partition's block-table entries,
+// an invalid-entry flag, and each wave's (m, l, o) for the G heads.
+struct DecodeSmem {
+  int* tab;
+  int* bad;
+  float* m;  // [kWaves][G]
+  float* l;  // [kWaves][G]
+  float* o;  // [kWaves][G][D]
+};
+__host__ __device__ inline size_t decode_smem_bytes(int part_tokens, int G, int D) {
+  return (size_t)(part_tokens / kBlock) * 4 + 16 + (size_t)2 * kWaves * G * 4 +
+         (size_t)kWaves * G * D * 4;
+}
+__device__ __forceinline__ DecodeSmem decode_smem(unsigned char* base, int part_tokens, int G) {
+  DecodeSmem sm;
+  sm.tab = reinterpret_cast<int*>(base);
+  sm.bad = sm.tab + part_tokens / kBlock;
+  sm.m = reinterpret_cast<float*>(sm.bad + 4);
+  sm.l = sm.m + kWaves * G;
+  sm.o = sm.l + kWaves * G;
+  return sm;
+}
+
 // Stage the partition's physical block IDs in LDS. Out-of-range IDs are
 // replaced by 0 (a safe read) and flag the partition as invalid.
 __device__ __forceinline__ void stage_table(const DecodeParams& p, const WorkItem& w, int b0,
-                                            int nblk, int* s_tab, int* s_bad) {
-  if (threadIdx.x == 0) *s_bad = 0;
+                                            int nblk, const DecodeSmem& sm) {
+  if (threadIdx.x == 0) *sm.bad = 0;
   __syncthreads();
   const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + b0;
   for (int i = threadIdx.x; i < nblk; i += kThreads) {
     int e = row[i];
     if (e < 0 || e >= p.num_blocks) {
-      *s_bad = 1;
+      *sm.bad = 1;
       e = 0;
     }
-    s_tab[i] = e;
+    sm.tab[i] = e;
   }
   __syncthreads();
 }
 
 // Merge the four waves' (m, l, o) held in LDS and write either the final
 // output (single partition) or the partition's partial result.
-template <int D, int GMAX>
+template <int D>
 __device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, const WorkItem& w,
                                                       int nps, bool part_bad,
-                                                      float (*s_m)[GMAX], float (*s_l)[GMAX],
-                                                      float (*s_o)[GMAX][D]) {
-  for (int i = threadIdx.x; i < p.G * D; i += kThreads) {
+                                                      const DecodeSmem& sm) {
+  const int G = p.G;
+  for (int i = threadIdx.x; i < G * D; i += kThreads) {
     const int g = i / D, d = i % D;
-    float M = s_m[0][g];
+    float M = sm.m[g];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, s_m[k][g]);
+    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, sm.m[k * G + g]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int k = 0; k < kWaves; ++k) {
-      const float mk = s_m[k][g];
+      const float mk = sm.m[k * G + g];
       const float f = (mk == neg_inf()) ? 0.f : fast_exp2(mk - M);
-      L += s_l[k][g] * f;
-      O += s_o[k][g][d] * f;
+      L += sm.l[k * G + g] * f;
+      O += sm.o[(k * G + g) * D + d] * f;
     }
     if (part_bad) {
       M = L = O = __builtin_nanf("");
     }
-    const size_t hq = (size_t)w.h * p.G + g;
+    const size_t hq = (size_t)w.h * G + g;
     if (nps == 1) {
       p.out[((size_t)w.s * p.Hq + hq) * D + d] = O / L;
     } else {
@@ -211,6 +248,7 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, con
 // 16-token block takes IPB loads. Dot products are finished with DPP row
 // reductions. Each group of LPR lanes keeps its own online softmax over the
 // tokens it reads; the groups and then the waves are merged at the end.
+// A wave issues the loads of its next block before computing the current one.
 // ============================================================================
 template <int DT, int D, int GMAX>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
@@ -221,21 +259,19 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
   constexpr int IPB = kBlock / TPI;      // loads per 16-token block
   static_assert(LPR == 8 || LPR == 16 || LPR == 32, "unsupported row width");
 
-  __shared__ int s_tab[kMaxPartBlocks];
-  __shared__ int s_bad;
-  __shared__ float s_m[kWaves][GMAX], s_l[kWaves][GMAX];
-  __shared__ float s_o[kWaves][GMAX][D];
-
+  extern __shared__ __align__(16) unsigned char smem_raw[];
   const WorkItem w = work_item(p);
+  if (!w.ok) return;
   const int ctx = p.lens[w.s];
   if (!sequence_prologue<D>(p, w, ctx)) return;
+  const DecodeSmem sm = decode_smem(smem_raw, p.part_tokens, p.G);
   const int nps = (ctx + p.part_tokens - 1) / p.part_tokens;
   const int t0 = w.part * p.part_tokens;
   const int t1 = min(ctx, t0 + p.part_tokens);
   const int b0 = t0 / kBlock;
   const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
-  stage_table(p, w, b0, nblk, s_tab, &s_bad);
-  const bool part_bad = s_bad != 0;
+  stage_table(p, w, b0, nblk, sm);
+  const bool part_bad = *sm.bad != 0;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane / LPR, c = lane % LPR;
@@ -269,16 +305,17 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
   const uint4* kbase = static_cast<const uint4*>(p.k_pool);
   const uint4* vbase = static_cast<const uint4*>(p.v_pool);
 
-  for (int jb = wave; jb < nblk; jb += kWaves) {
-    const size_t tile = ((size_t)s_tab[jb] * p.Hkv + w.h) * tile_u4;
-    uint4 ku[IPB], vu[IPB];
+  auto load = [&](int jb, uint4* ku, uint4* vu) {
+    const size_t tile = ((size_t)sm.tab[jb] * p.Hkv + w.h) * tile_u4;
 #pragma unroll
     for (int i = 0; i < IPB; ++i) ku[i] = kbase[tile + (size_t)(r + TPI * i) * LPR + c];
 #pragma unroll
     for (int i = 0; i < IPB; ++i) vu[i] = vbase[tile + (size_t)(r + TPI * i) * LPR + c];
+  };
+
+  auto compute = [&](int jb, const uint4* ku, const uint4* vu) {
     const int valid = t1 - (t0 + jb * kBlock);  // live tokens in this block (>= 1)
     const bool full = valid >= kBlock;
-
     float kf[IPB][EPL], vf[IPB][EPL];
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
@@ -326,6 +363,20 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
       }
       m[g] = mn;
     }
+  };
+
+  // this wave's blocks: wave, wave + 4, ...; two register sets alternate so
+  // the next block's loads are in flight while the current one is computed
+  const int nmine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
+  uint4 ka[IPB], va[IPB], kb[IPB], vb[IPB];
+  if (nmine > 0) load(wave, ka, va);
+  for (int i = 0; i < nmine; i += 2) {
+    const int jb = wave + i * kWaves;
+    if (i + 1 < nmine) load(jb + kWaves, kb, vb);
+    compute(jb, ka, va);
+    if (i + 1 >= nmine) break;
+    if (i + 2 < nmine) load(jb + 2 * kWaves, ka, va);
+    compute(jb + kWaves, kb, vb);
   }
 
   // merge the row groups of the wave (lanes differing in the row bits)
@@ -350,16 +401,18 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
   if (r == 0) {
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
+      if (g < p.G) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_o[wave][g][c * EPL + e] = acc[g][e];
-      if (c == 0) {
-        s_m[wave][g] = m[g];
-        s_l[wave][g] = l[g];
+        for (int e = 0; e < EPL; ++e) sm.o[(wave * p.G + g) * D + c * EPL + e] = acc[g][e];
+        if (c == 0) {
+          sm.m[wave * p.G + g] = m[g];
+          sm.l[wave * p.G + g] = l[g];
+        }
       }
     }
   }
   __syncthreads();
-  merge_waves_and_store<D, GMAX>(p, w, nps, part_bad, s_m, s_l, s_o);
+  merge_waves_and_store<D>(p, w, nps, part_bad, sm);
 }
 
 // ============================================================================
@@ -436,22 +489,19 @@ __device__ __forceinline__ uint2 gather_col(const uint4* v, int n) {
 template <int DT>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   constexpr int D = 128;
-  constexpr int GMAX = 16;
-  __shared__ int s_tab[kMaxPartBlocks];
-  __shared__ int s_bad;
-  __shared__ float s_m[kWaves][GMAX], s_l[kWaves][GMAX];
-  __shared__ float s_o[kWaves][GMAX][D];
-
+  extern __shared__ __align__(16) unsigned char smem_raw[];
   const WorkItem w = work_item(p);
+  if (!w.ok) return;
   const int ctx = p.lens[w.s];
   if (!sequence_prologue<D>(p, w, ctx)) return;
+  const DecodeSmem sm = decode_smem(smem_raw, p.part_tokens, p.G);
   const int nps = (ctx + p.part_tokens - 1) / p.part_tokens;
   const int t0 = w.part * p.part_tokens;
   const int t1 = min(ctx, t0 + p.part_tokens);
   const int b0 = t0 / kBlock;
   const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
-  stage_table(p, w, b0, nblk, s_tab, &s_bad);
-  const bool part_bad = s_bad != 0;
+  stage_table(p, w, b0, nblk, sm);
+  const bool part_bad = *sm.bad != 0;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15;  // MFMA column: query head of the group / token row
@@ -480,16 +530,17 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const char* vbase = static_cast<const char*>(p.v_pool);
   constexpr size_t kTileBytes = (size_t)kBlock * D * 2;  // 4 KB
 
-  for (int jb = wave; jb < nblk; jb += kWaves) {
-    const size_t tile = ((size_t)s_tab[jb] * p.Hkv + w.h) * kTileBytes;
+  auto load = [&](int jb, uint4* ku, uint4* vu) {
+    const size_t tile = ((size_t)sm.tab[jb] * p.Hkv + w.h) * kTileBytes;
     const uint4* kt = reinterpret_cast<const uint4*>(kbase + tile);
     const uint4* vt = reinterpret_cast<const uint4*>(vbase + tile);
-    uint4 ku[4], vu[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) ku[kc] = kt[col * 16 + kc * 4 + grp];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) vu[jj] = vt[(4 * grp + jj) * 16 + col];
+  };
 
+  auto compute = [&](int jb, const uint4* ku, uint4* vu) {
     f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) st = mfma_qk<DT>(ku[kc], qb[kc], st);
@@ -531,24 +582,37 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       o[n] = mfma_pv<DT>(a, phi, o[n]);
       o[n] = mfma_pv<DT>(a, plo, o[n]);
     }
+  };
+
+  // this wave's blocks: wave, wave + 4, ...; two register sets alternate so
+  // the next block's loads are in flight while the current one is computed
+  const int nmine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
+  uint4 ka[4], va[4], kb[4], vb[4];
+  if (nmine > 0) load(wave, ka, va);
+  for (int i = 0; i < nmine; i += 2) {
+    const int jb = wave + i * kWaves;
+    if (i + 1 < nmine) load(jb + kWaves, kb, vb);
+    compute(jb, ka, va);
+    if (i + 1 >= nmine) break;
+    if (i + 2 < nmine) load(jb + 2 * kWaves, ka, va);
+    compute(jb + kWaves, kb, vb);
   }
 
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (grp == 0) {
-    s_m[wave][col] = m;
-    s_l[wave][col] = l;
-  }
   if (col < p.G) {
+    if (grp == 0) {
+      sm.m[wave * p.G + col] = m;
+      sm.l[wave * p.G + col] = l;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int n = 0; n < 8; ++n) s_o[wave][col][32 * grp + 8 * r + n] = o[n][r];
+      for (int n = 0; n < 8; ++n) sm.o[(wave * p.G + col) * D + 32 * grp + 8 * r + n] = o[n][r];
   }
   __syncthreads();
-  merge_waves_and_store<D, GMAX>(p, w, nps, part_bad, s_m, s_l, s_o);
+  merge_waves_and_store<D>(p, w, nps, part_bad, sm);
 }
-
 // ============================================================================
 // Split-K merge ([2], "The Custom CUDA Kernel": partial outputs and softmax
 // denominators combined with a numerically stable merge): for every
@@ -668,13 +732,13 @@ int32_t effective_partition(int32_t partition_size) {
 }
 
 template <int DT, int D>
-kv_status launch_valu(const DecodeParams& prm, int gmax, dim3 grid, hipStream_t st) {
+kv_status launch_valu(const DecodeParams& prm, int gmax, dim3 grid, size_t lds, hipStream_t st) {
   switch (gmax) {
-    case 1: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 1>), grid, dim3(kThreads), 0, st, prm); break;
-    case 2: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 2>), grid, dim3(kThreads), 0, st, prm); break;
-    case 4: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 4>), grid, dim3(kThreads), 0, st, prm); break;
-    case 8: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 8>), grid, dim3(kThreads), 0, st, prm); break;
-    case 16: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 16>), grid, dim3(kThreads), 0, st, prm); break;
+    case 1: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 1>), grid, dim3(kThreads), lds, st, prm); break;
+    case 2: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 2>), grid, dim3(kThreads), lds, st, prm); break;
+    case 4: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 4>), grid, dim3(kThreads), lds, st, prm); break;
+    case 8: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 8>), grid, dim3(kThreads), lds, st, prm); break;
+    case 16: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 16>), grid, dim3(kThreads), lds, st, prm); break;
     default: return fail(KV_ERR_UNSUPPORTED, "decode: group size");
   }
   return launch_status("kv_paged_attention_decode");
@@ -768,7 +832,8 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t block_size, int32_t num_blocks, float scale,
                                     kv_dtype dtype, int32_t partition_size,
-                                    int32_t max_context_len, void* workspace, size_t ws_bytes,
+                                    int32_t max_context_len, const int32_t* work_items,
+                                    int32_t n_items, void* workspace, size_t ws_bytes,
                                     hipStream_t stream) {
   pagedkv::clear_error();
   if (pagedkv::dtype_bytes(dtype) == 0)
@@ -799,7 +864,10 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
   if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace)))
     return fail(KV_ERR_INVALID, "kv_paged_attention_decode: workspace of %zu bytes needed (got %zu)",
                 need, ws_bytes);
-  const int64_t nwg = nparts * num_kv_heads * (int64_t)S;
+  if (work_items && n_items <= 0)
+    return fail(KV_ERR_INVALID, "kv_paged_attention_decode: work plan with %d items", n_items);
+  const int64_t nwg = work_items ? (int64_t)n_items * num_kv_heads
+                                 : nparts * num_kv_heads * (int64_t)S;
   if (nwg > INT32_MAX) return fail(KV_ERR_INVALID, "kv_paged_attention_decode: grid too large");
 
   DecodeParams prm;
@@ -809,6 +877,8 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
   prm.v_pool = v_pool;
   prm.tables = block_tables;
   prm.lens = context_lens;
+  prm.items = work_items;
+  prm.n_items = work_items ? n_items : 0;
   float* ws = static_cast<float*>(workspace);
   const size_t o_elems = (size_t)S * num_q_heads * nparts * head_dim;
   prm.ws_o = need ? ws : nullptr;
@@ -824,25 +894,26 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
   prm.scale_log2 = scale * 1.4426950408889634f;
 
   const dim3 grid((unsigned)nwg);
+  const size_t lds = decode_smem_bytes(P, G, head_dim);
   kv_status st;
   const bool mfma = (dtype == KV_F16 || dtype == KV_BF16) && head_dim == 128 && G >= 2;
   if (mfma) {
     if (dtype == KV_BF16)
-      hipLaunchKernelGGL(decode_mfma_kernel<KV_BF16>, grid, dim3(kThreads), 0, stream, prm);
+      hipLaunchKernelGGL(decode_mfma_kernel<KV_BF16>, grid, dim3(kThreads), lds, stream, prm);
     else
-      hipLaunchKernelGGL(decode_mfma_kernel<KV_F16>, grid, dim3(kThreads), 0, stream, prm);
+      hipLaunchKernelGGL(decode_mfma_kernel<KV_F16>, grid, dim3(kThreads), lds, stream, prm);
     st = launch_status("kv_paged_attention_decode");
   } else {
     const int gmax = G == 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
     if (dtype == KV_F32)
-      st = head_dim == 64 ? launch_valu<KV_F32, 64>(prm, gmax, grid, stream)
-                          : launch_valu<KV_F32, 128>(prm, gmax, grid, stream);
+      st = head_dim == 64 ? launch_valu<KV_F32, 64>(prm, gmax, grid, lds, stream)
+                          : launch_valu<KV_F32, 128>(prm, gmax, grid, lds, stream);
     else if (dtype == KV_F16)
-      st = head_dim == 64 ? launch_valu<KV_F16, 64>(prm, gmax, grid, stream)
-                          : launch_valu<KV_F16, 128>(prm, 1, grid, stream);
+      st = head_dim == 64 ? launch_valu<KV_F16, 64>(prm, gmax, grid, lds, stream)
+                          : launch_valu<KV_F16, 128>(prm, 1, grid, lds, stream);
     else
-      st = head_dim == 64 ? launch_valu<KV_BF16, 64>(prm, gmax, grid, stream)
-                          : launch_valu<KV_BF16, 128>(prm, 1, grid, stream);
+      st = head_dim == 64 ? launch_valu<KV_BF16, 64>(prm, gmax, grid, lds, stream)
+                          : launch_valu<KV_BF16, 128>(prm, 1, grid, lds, stream);
   }
   if (st != KV_OK) return st;
   if (nparts > 1) {

@@ -1,0 +1,55 @@
+// Host-side work plan for paged decode attention.
+//
+// The decode kernel runs one workgroup per (sequence, KV head, context
+// partition). Built from the host's copy of the context lengths, the plan
+// lists exactly the (sequence, partition) pairs that hold tokens, so the grid
+// has no idle workgroups, and orders them longest first: every full partition,
+// then the partial last partitions by decreasing length, then one item per
+// empty (or invalid) sequence so its output still gets written. Longest-first
+// order lets the hardware dispatcher balance the tail.
+
+#include <algorithm>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/pagedkv.h"
+#include "status.h"
+
+using pagedkv::fail;
+
+extern "C" kv_status kv_paged_attention_plan(const int32_t* context_lens_host, int32_t S,
+                                             int32_t partition_size, int32_t* items_out,
+                                             int32_t cap, int32_t* n_items) {
+  pagedkv::clear_error();
+  const int32_t P = partition_size == 0 ? 512 : partition_size;
+  if (!n_items || S < 0 || (S > 0 && !context_lens_host))
+    return fail(KV_ERR_INVALID, "kv_paged_attention_plan: null argument or negative S");
+  if (P < 16 || P > 8192 || P % 16 != 0)
+    return fail(KV_ERR_INVALID, "kv_paged_attention_plan: partition_size %d", partition_size);
+  struct Item {
+    int32_t s, p, len;
+  };
+  std::vector<Item> items;
+  items.reserve((size_t)S * 2);
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t ctx = context_lens_host[s];
+    if (ctx <= 0) {
+      items.push_back({s, 0, -1});
+      continue;
+    }
+    const int32_t np = (int32_t)(((int64_t)ctx + P - 1) / P);
+    for (int32_t p = 0; p < np; ++p)
+      items.push_back({s, p, std::min<int32_t>(P, ctx - p * P)});
+  }
+  std::stable_sort(items.begin(), items.end(),
+                   [](const Item& a, const Item& b) { return a.len > b.len; });
+  *n_items = (int32_t)items.size();
+  if ((size_t)cap < items.size() || (!items_out && !items.empty()))
+    return fail(KV_ERR_INVALID, "kv_paged_attention_plan: capacity %d < %zu items", cap,
+                items.size());
+  for (size_t i = 0; i < items.size(); ++i) {
+    items_out[2 * i] = items[i].s;
+    items_out[2 * i + 1] = items[i].p;
+  }
+  return KV_OK;
+}

@@ -22,7 +22,7 @@ from . import binding as kv
 
 class DecodeSession:
     def __init__(self, *, k_pool, v_pool, num_q_heads: int, free_order: Optional[Sequence[int]] = None,
-                 partition_size: int = 0):
+                 partition_size: int = 0, use_plan: bool = True):
         import torch
         self.torch = torch
         NB, Hkv, B, D = k_pool.shape
@@ -30,6 +30,7 @@ class DecodeSession:
         self.NB, self.Hkv, self.B, self.D, self.Hq = NB, Hkv, B, D, num_q_heads
         self.dtype = kv.dtype_code(k_pool)
         self.partition_size = partition_size
+        self.use_plan = use_plan
         self.pool = kv.kv_pool_create(NB, B, 1, Hkv, D, self.dtype)
         if free_order is not None:
             kv.kv_pool_set_free_order(self.pool, free_order)
@@ -110,6 +111,10 @@ class DecodeSession:
                                                    self.partition_size)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev) if ws else None
         self.host_tables, self.host_lens = tables, lens
+        self.d_items = None
+        if self.use_plan:
+            items = kv.kv_paged_attention_plan(lens, self.partition_size)
+            self.d_items = torch.from_numpy(items).to(dev)
         return host_slots, pairs
 
     def step(self, q, k_new, v_new, out, scale: float, k_pool=None, v_pool=None,
@@ -127,6 +132,7 @@ class DecodeSession:
         if decode_events is not None:
             decode_events[0].record()
         kv.kv_paged_attention_decode(out, q, kp, vp_, self.d_tables, self.d_lens, scale,
-                                     self.max_context_len, self.workspace, self.partition_size)
+                                     self.max_context_len, self.workspace, self.partition_size,
+                                     self.d_items)
         if decode_events is not None:
             decode_events[1].record()

@@ -38,7 +38,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(kv):
     names = header_functions()
-    assert len(names) >= 23, names
+    assert len(names) >= 24, names
     for n in names:
         assert hasattr(kv.lib, n), f"{n} declared but not exported"
     assert set(names) == set(kv.EXPORTED), set(names) ^ set(kv.EXPORTED)
@@ -79,7 +79,7 @@ def test_device_entry_points_validate_on_the_host(kv):
         a = dict(args, **kw)
         return lib.kv_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["t"], a["mb"], a["lens"],
                                              a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"], a["scale"],
-                                             a["dt"], a["P"], a["mc"], a["ws"], a["wsb"], a["st"])
+                                             a["dt"], a["P"], a["mc"], None, 0, a["ws"], a["wsb"], a["st"])
     assert call(B=8) == kv.KV_ERR_UNSUPPORTED
     assert call(D=96) == kv.KV_ERR_UNSUPPORTED
     assert call(Hq=7) == kv.KV_ERR_UNSUPPORTED
@@ -246,3 +246,18 @@ def test_worked_trace_through_the_c_abi(kv):
                 assert kv.kv_block_refcount(p, int(blk)) == rc
     finally:
         kv.kv_pool_destroy(p)
+
+
+def test_work_plan_lists_every_partition_longest_first(kv):
+    lens = [0, 40, 1030, 512, 513, -3, 16]
+    items = kv.kv_paged_attention_plan(lens, 512)
+    got = sorted(map(tuple, items))
+    want = sorted([(0, 0), (1, 0), (2, 0), (2, 1), (2, 2), (3, 0), (4, 0), (4, 1), (5, 0), (6, 0)])
+    assert got == want
+    sizes = []
+    for s, p in items:
+        t = lens[s]
+        sizes.append(-1 if t <= 0 else min(512, t - 512 * p))
+    assert sizes == sorted(sizes, reverse=True)
+    with pytest.raises(kv.KVError):
+        kv.kv_paged_attention_plan(lens, 24)

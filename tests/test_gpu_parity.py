@@ -209,16 +209,19 @@ def random_case(rng, lens, Hq, Hkv, D, dt, num_blocks=None, poison=True):
     return q, kp, vp, tab, np.array(lens, np.int32)
 
 
-def gpu_decode(q, kp, vp, tab, lens, scale, dt, partition_size=0, max_ctx=None):
+def gpu_decode(q, kp, vp, tab, lens, scale, dt, partition_size=0, max_ctx=None, plan=False):
     kv = kvlib()
     S, Hq, D = q.shape
     out = torch.full((S, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
     mc = int(lens.max()) if max_ctx is None else max_ctx
     wsb = kv.kv_paged_attention_workspace_bytes(S, Hq, D, mc, partition_size)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
+    items = None
+    if plan:
+        items = torch.from_numpy(kv.kv_paged_attention_plan(lens, partition_size)).cuda()
     kv.kv_paged_attention_decode(out, to_dev(q, dt), to_dev(kp, dt), to_dev(vp, dt),
                                  torch.from_numpy(tab).cuda(), torch.from_numpy(lens).cuda(),
-                                 scale, mc, ws, partition_size)
+                                 scale, mc, ws, partition_size, items)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -228,16 +231,28 @@ SHAPES = [(dt, D, G) for dt in ("f32", "f16", "bf16") for D in (64, 128) for G i
 
 @pytest.mark.parametrize("dt,D,G", SHAPES)
 def test_decode_shapes_against_oracle(dt, D, G):
-    rng = np.random.default_rng(hash((dt, D, G)) % 2 ** 32)
+    rng = np.random.default_rng(1000 + SHAPES.index((dt, D, G)))
     lens = [1, 15, 16, 17, 33, 100, 511, 512, 513, 700]
     Hkv = 2
     q, kp, vp, tab, cl = random_case(rng, lens, G * Hkv, Hkv, D, dt)
     scale = float(np.float32(1 / np.sqrt(D)))
     ref = oracle.decode_attention(q, kp, vp, tab, cl, scale, dt)
-    for ps in (0, 64, 16):
-        log(f"[gpu] decode {dt} D={D} G={G} partition={ps}")
-        got = gpu_decode(q, kp, vp, tab, cl, scale, dt, ps)
-        check_attention(got.reshape(-1, D), ref.reshape(-1, D), dt, f"{dt}/{D}/{G}/{ps}")
+    for ps, plan in ((0, True), (0, False), (64, True), (16, False)):
+        log(f"[gpu] decode {dt} D={D} G={G} partition={ps} plan={plan}")
+        got = gpu_decode(q, kp, vp, tab, cl, scale, dt, ps, plan=plan)
+        check_attention(got.reshape(-1, D), ref.reshape(-1, D), dt, f"{dt}/{D}/{G}/{ps}/{plan}")
+
+
+def test_plan_and_padded_grid_are_bitwise_identical():
+    rng = np.random.default_rng(40)
+    dt, D, Hkv, G = "bf16", 128, 8, 8
+    lens = [0, 1, 700, 4097, 512, 33, 1500]
+    q, kp, vp, tab, cl = random_case(rng, lens, G * Hkv, Hkv, D, dt)
+    for ps in (128, 512):
+        a = gpu_decode(q, kp, vp, tab, cl, 0.088, dt, ps, plan=True)
+        b = gpu_decode(q, kp, vp, tab, cl, 0.088, dt, ps, plan=False)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        assert np.all(a[0] == 0.0)
 
 
 def test_zero_length_and_invalid_sequences():
