@@ -212,10 +212,14 @@ kv_status kv_paged_attention_plan(const int32_t* context_lens_host, int32_t S,
 /* Workspace bytes kv_paged_attention_decode needs for these sizes: 0 when
  * max_context_len <= the partition size (every sequence finishes in one
  * partition), else S * num_q_heads * num_partitions * (head_dim + 2) * 4 for
- * the per-partition partial outputs, maxima and sums. partition_size 0 picks
- * the default (512). Returns 0 for invalid sizes. */
-size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_t head_dim,
-                                          int32_t max_context_len, int32_t partition_size);
+ * the per-partition partial outputs, maxima and sums. num_kv_heads is
+ * accepted for forward compatibility and does not change the size.
+ * partition_size 0 picks the default (512). Returns 0 for invalid sizes.
+ * The workspace needs no initialisation; calls that run concurrently need
+ * separate workspaces. */
+size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t max_context_len,
+                                          int32_t partition_size);
 
 /* out[s][hq][:] = sum_j softmax_j(scale * <q[s][hq], K_s[j]>) V_s[j] over the
  * first context_lens[s] positions of sequence s, where K_s[j] and V_s[j] are

@@ -72,7 +72,7 @@ _SIGS = {
     "kv_reshape_and_cache": (C.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, C.c_int, vp]),
     "kv_copy_blocks": (C.c_int, [C.POINTER(vp), C.POINTER(vp), i32, vp, i32, i32, C.c_size_t, vp]),
     "kv_paged_attention_plan": (C.c_int, [P_i32, i32, i32, P_i32, i32, P_i32]),
-    "kv_paged_attention_workspace_bytes": (C.c_size_t, [i32, i32, i32, i32, i32]),
+    "kv_paged_attention_workspace_bytes": (C.c_size_t, [i32, i32, i32, i32, i32, i32]),
     "kv_paged_attention_decode": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                             i32, f32, C.c_int, i32, i32, vp, i32, vp, C.c_size_t,
                                             vp]),
@@ -278,9 +278,9 @@ def kv_paged_attention_plan(context_lens_host, partition_size: int = 0) -> np.nd
     return out[:n.value]
 
 
-def kv_paged_attention_workspace_bytes(S: int, num_q_heads: int, head_dim: int,
+def kv_paged_attention_workspace_bytes(S: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                                        max_context_len: int, partition_size: int = 0) -> int:
-    return int(lib.kv_paged_attention_workspace_bytes(S, num_q_heads, head_dim,
+    return int(lib.kv_paged_attention_workspace_bytes(S, num_q_heads, num_kv_heads, head_dim,
                                                        max_context_len, partition_size))
 
 

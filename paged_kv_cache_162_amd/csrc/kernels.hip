@@ -107,137 +107,103 @@ struct DecodeParams {
   const int32_t* tables;
   const int32_t* lens;
   const int32_t* items;  // optional work plan: [n_items][2] = (sequence, partition)
-  float* ws_o;   // [S][Hq][nparts][D]
-  float* ws_ml;  // [S][Hq][nparts][2]
-  int32_t max_blocks, S, Hq, Hkv, G, num_blocks, part_tokens, nparts, n_items;
+  float* ws_o;           // [S][Hq][nparts][D]   partial outputs (unnormalised)
+  float* ws_ml;          // [S][Hq][nparts][2]   partial (max, sum) in base-2 units
+  int32_t max_blocks, S, Hq, Hkv, G, num_blocks, part_tokens, nparts, n_units;
   float scale_log2;
 };
 
-// Work item of this workgroup. With a plan, blockIdx.x = item * Hkv + head:
-// consecutive workgroups take the KV heads of one item, so with the
-// round-robin workgroup-to-XCD dispatch a given head of every sequence lands
-// on the same XCD whenever Hkv is a multiple or divisor of the XCD count
-// (shared prefix blocks of one head then hit in that XCD's L2). Without a
-// plan, blockIdx.x enumerates (partition, head, sequence) over every possible
-// partition and the workgroups past a sequence's end exit at once.
+// Every wave64 is an independent worker: wave `u` of the grid processes work
+// unit u, one (sequence, KV head, context partition), from its first block
+// to its last, and writes its result itself - the normalised output when the
+// sequence has a single partition, else an unnormalised partial result for
+// the split-K merge. There is no cross-wave merge, no LDS and no barrier, so
+// nothing stalls one wave on another. With a plan, u = item * Hkv + head and
+// the items are sorted longest first: the four waves of a workgroup get
+// units of similar size and finish together, and the hardware dispatcher
+// balances the tail. Without a plan, u enumerates (partition, head,
+// sequence) over every possible partition and units past a sequence's end
+// return at once.
 struct WorkItem {
   int s, h, part;
   bool ok;
 };
-__device__ __forceinline__ WorkItem work_item(const DecodeParams& p) {
+__device__ __forceinline__ WorkItem unit_item(const DecodeParams& p, int u) {
   WorkItem w;
-  const int L = blockIdx.x;
   if (p.items) {
-    const int it = L / p.Hkv;
-    w.h = L % p.Hkv;
+    const int it = u / p.Hkv;
+    w.h = u % p.Hkv;
     w.s = p.items[2 * it];
     w.part = p.items[2 * it + 1];
     w.ok = w.s >= 0 && w.s < p.S && w.part >= 0 && w.part < p.nparts;
   } else {
-    w.s = L % p.S;
-    w.h = (L / p.S) % p.Hkv;
-    w.part = L / (p.S * p.Hkv);
+    w.s = u % p.S;
+    w.h = (u / p.S) % p.Hkv;
+    w.part = u / (p.S * p.Hkv);
     w.ok = true;
   }
   return w;
 }
 
-// Sequence-level checks shared by both decode kernels. Returns false when the
-// workgroup has nothing to do (its output, if any, is already written).
+// Sequence-level checks shared by both decode kernels (one wave). Returns the
+// number of partitions of the sequence when this unit has tokens to process,
+// else 0 (the output of an empty or invalid sequence is written by its
+// partition-0 unit: zeros, or NaN for a length that is negative or exceeds
+// the table or max_context_len).
 template <int D>
-__device__ __forceinline__ bool sequence_prologue(const DecodeParams& p, const WorkItem& w,
-                                                  int ctx) {
+__device__ __forceinline__ int unit_prologue(const DecodeParams& p, const WorkItem& w, int ctx,
+                                             int lane) {
   const bool bad = ctx < 0 || (int64_t)ctx > (int64_t)p.max_blocks * kBlock ||
                    (int64_t)ctx > (int64_t)p.nparts * p.part_tokens;
   if (bad || ctx == 0) {
     if (w.part == 0) {
       const float v = bad ? __builtin_nanf("") : 0.0f;
-      for (int i = threadIdx.x; i < p.G * D; i += kThreads) {
-        const int g = i / D, d = i % D;
-        p.out[((size_t)w.s * p.Hq + (size_t)w.h * p.G + g) * D + d] = v;
-      }
+      float* dst = p.out + ((size_t)w.s * p.Hq + (size_t)w.h * p.G) * D;
+      for (int i = lane; i < p.G * D; i += 64) dst[i] = v;
     }
-    return false;
+    return 0;
   }
   const int nps = (ctx + p.part_tokens - 1) / p.part_tokens;
-  return w.part < nps;
+  return w.part < nps ? nps : 0;
 }
 
-// Dynamic LDS of a decode workgroup: the partition's block-table entries,
-// an invalid-entry flag, and each wave's (m, l, o) for the G heads.
-struct DecodeSmem {
-  int* tab;
-  int* bad;
-  float* m;  // [kWaves][G]
-  float* l;  // [kWaves][G]
-  float* o;  // [kWaves][G][D]
-};
-__host__ __device__ inline size_t decode_smem_bytes(int part_tokens, int G, int D) {
-  return (size_t)(part_tokens / kBlock) * 4 + 16 + (size_t)2 * kWaves * G * 4 +
-         (size_t)kWaves * G * D * 4;
-}
-__device__ __forceinline__ DecodeSmem decode_smem(unsigned char* base, int part_tokens, int G) {
-  DecodeSmem sm;
-  sm.tab = reinterpret_cast<int*>(base);
-  sm.bad = sm.tab + part_tokens / kBlock;
-  sm.m = reinterpret_cast<float*>(sm.bad + 4);
-  sm.l = sm.m + kWaves * G;
-  sm.o = sm.l + kWaves * G;
-  return sm;
-}
-
-// Stage the partition's physical block IDs in LDS. Out-of-range IDs are
-// replaced by 0 (a safe read) and flag the partition as invalid.
-__device__ __forceinline__ void stage_table(const DecodeParams& p, const WorkItem& w, int b0,
-                                            int nblk, const DecodeSmem& sm) {
-  if (threadIdx.x == 0) *sm.bad = 0;
-  __syncthreads();
-  const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + b0;
-  for (int i = threadIdx.x; i < nblk; i += kThreads) {
-    int e = row[i];
-    if (e < 0 || e >= p.num_blocks) {
-      *sm.bad = 1;
-      e = 0;
-    }
-    sm.tab[i] = e;
+// Physical block of logical block `jb` of the unit's partition, read through
+// the scalar cache (the index is wave-uniform). An ID outside the pool marks
+// the unit invalid and is read as block 0, so no load leaves the pool.
+__device__ __forceinline__ int block_id(const DecodeParams& p, const int32_t* row, int jb,
+                                        bool& bad) {
+  int e = row[jb];
+  if (e < 0 || e >= p.num_blocks) {
+    bad = true;
+    e = 0;
   }
-  __syncthreads();
+  return e;
 }
 
-// Merge the four waves' (m, l, o) held in LDS and write either the final
-// output (single partition) or the partition's partial result.
-template <int D>
-__device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, const WorkItem& w,
-                                                      int nps, bool part_bad,
-                                                      const DecodeSmem& sm) {
-  const int G = p.G;
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int g = i / D, d = i % D;
-    float M = sm.m[g];
-#pragma unroll
-    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, sm.m[k * G + g]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int k = 0; k < kWaves; ++k) {
-      const float mk = sm.m[k * G + g];
-      const float f = (mk == neg_inf()) ? 0.f : fast_exp2(mk - M);
-      L += sm.l[k * G + g] * f;
-      O += sm.o[(k * G + g) * D + d] * f;
+// Store `n` consecutive floats of head `hq` starting at dimension d0: the
+// final output o / l for a single-partition sequence, else the partial
+// result o (and, from the lane with `write_ml`, the pair (m, l)). An invalid
+// unit stores NaN.
+__device__ __forceinline__ void store_result(const DecodeParams& p, const WorkItem& w, int nps,
+                                             int hq, int d0, const float* o, int n, float m,
+                                             float l, bool write_ml, bool bad, int D) {
+  const float nan = __builtin_nanf("");
+  if (nps == 1) {
+    float* dst = p.out + ((size_t)w.s * p.Hq + hq) * D + d0;
+    const float inv = 1.0f / l;
+    for (int i = 0; i < n; i += 4) {
+      float4 v = make_float4(o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv);
+      if (bad) v = make_float4(nan, nan, nan, nan);
+      *reinterpret_cast<float4*>(dst + i) = v;
     }
-    if (part_bad) {
-      M = L = O = __builtin_nanf("");
-    }
-    const size_t hq = (size_t)w.h * G + g;
-    if (nps == 1) {
-      p.out[((size_t)w.s * p.Hq + hq) * D + d] = O / L;
-    } else {
-      const size_t slot = ((size_t)w.s * p.Hq + hq) * p.nparts + w.part;
-      p.ws_o[slot * D + d] = O;
-      if (d == 0) {
-        p.ws_ml[slot * 2 + 0] = M;
-        p.ws_ml[slot * 2 + 1] = L;
-      }
-    }
+  } else {
+    const size_t slot = ((size_t)w.s * p.Hq + hq) * p.nparts + w.part;
+    float* dst = p.ws_o + slot * D + d0;
+    for (int i = 0; i < n; i += 4)
+      *reinterpret_cast<float4*>(dst + i) = make_float4(o[i], o[i + 1], o[i + 2], o[i + 3]);
+    if (write_ml)
+      *reinterpret_cast<float2*>(p.ws_ml + slot * 2) = bad ? make_float2(nan, nan)
+                                                            : make_float2(m, l);
   }
 }
 
@@ -247,8 +213,7 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, con
 // (16 bytes per lane), so one dwordx4 load per lane reads TPI whole rows and a
 // 16-token block takes IPB loads. Dot products are finished with DPP row
 // reductions. Each group of LPR lanes keeps its own online softmax over the
-// tokens it reads; the groups and then the waves are merged at the end.
-// A wave issues the loads of its next block before computing the current one.
+// tokens it reads; the groups are merged with cross-lane shuffles at the end.
 // ============================================================================
 template <int DT, int D, int GMAX>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
@@ -259,22 +224,20 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
   constexpr int IPB = kBlock / TPI;      // loads per 16-token block
   static_assert(LPR == 8 || LPR == 16 || LPR == 32, "unsupported row width");
 
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  const WorkItem w = work_item(p);
+  const int lane = threadIdx.x & 63;
+  const int u = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (u >= p.n_units) return;
+  const int r = lane / LPR, c = lane % LPR;
+  const WorkItem w = unit_item(p, u);
   if (!w.ok) return;
   const int ctx = p.lens[w.s];
-  if (!sequence_prologue<D>(p, w, ctx)) return;
-  const DecodeSmem sm = decode_smem(smem_raw, p.part_tokens, p.G);
-  const int nps = (ctx + p.part_tokens - 1) / p.part_tokens;
+  const int nps = unit_prologue<D>(p, w, ctx, lane);
+  if (nps == 0) return;
   const int t0 = w.part * p.part_tokens;
   const int t1 = min(ctx, t0 + p.part_tokens);
-  const int b0 = t0 / kBlock;
   const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
-  stage_table(p, w, b0, nblk, sm);
-  const bool part_bad = *sm.bad != 0;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane / LPR, c = lane % LPR;
+  const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + t0 / kBlock;
+  bool bad = false;
 
   // query chunk of every head in the group, pre-scaled into base-2 logits
   float qf[GMAX][EPL];
@@ -305,8 +268,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
   const uint4* kbase = static_cast<const uint4*>(p.k_pool);
   const uint4* vbase = static_cast<const uint4*>(p.v_pool);
 
-  auto load = [&](int jb, uint4* ku, uint4* vu) {
-    const size_t tile = ((size_t)sm.tab[jb] * p.Hkv + w.h) * tile_u4;
+  auto load = [&](int e, uint4* ku, uint4* vu) {
+    const size_t tile = ((size_t)e * p.Hkv + w.h) * tile_u4;
 #pragma unroll
     for (int i = 0; i < IPB; ++i) ku[i] = kbase[tile + (size_t)(r + TPI * i) * LPR + c];
 #pragma unroll
@@ -327,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
       for (int i = 0; i < IPB; ++i)
         if (r + TPI * i >= valid) {
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) vf[i][e] = 0.f;
+          for (int e = 0; e < EPL; ++e) vf[i][e] = 0.f;  // masked rows may hold NaN
         }
     }
 #pragma unroll
@@ -365,18 +328,31 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     }
   };
 
-  // this wave's blocks: wave, wave + 4, ...; two register sets alternate so
-  // the next block's loads are in flight while the current one is computed
-  const int nmine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
-  uint4 ka[IPB], va[IPB], kb[IPB], vb[IPB];
-  if (nmine > 0) load(wave, ka, va);
-  for (int i = 0; i < nmine; i += 2) {
-    const int jb = wave + i * kWaves;
-    if (i + 1 < nmine) load(jb + kWaves, kb, vb);
-    compute(jb, ka, va);
-    if (i + 1 >= nmine) break;
-    if (i + 2 < nmine) load(jb + 2 * kWaves, ka, va);
-    compute(jb + kWaves, kb, vb);
+  // Two register sets alternate so the next block's loads are in flight
+  // while the current one is computed. The steady-state loop issues its loads
+  // unconditionally (a load under a branch would force a wait for every
+  // outstanding load at the join); the last one or two blocks are peeled.
+  {
+    uint4 ka[IPB], va[IPB], kb[IPB], vb[IPB];
+    const int last = nblk - 1;
+    int eb = block_id(p, row, min(1, last), bad);
+    load(block_id(p, row, 0, bad), ka, va);
+    int jb = 0;
+    for (; jb + 2 < nblk; jb += 2) {
+      const int ea2 = block_id(p, row, jb + 2, bad);
+      load(eb, kb, vb);
+      compute(jb, ka, va);
+      eb = block_id(p, row, min(jb + 3, last), bad);
+      load(ea2, ka, va);
+      compute(jb + 1, kb, vb);
+    }
+    if (jb + 1 < nblk) {
+      load(eb, kb, vb);
+      compute(jb, ka, va);
+      compute(jb + 1, kb, vb);
+    } else {
+      compute(jb, ka, va);
+    }
   }
 
   // merge the row groups of the wave (lanes differing in the row bits)
@@ -398,21 +374,13 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
       m[g] = M;
     }
   }
+  // lanes of row 0 hold the whole result: head g, dims c*EPL .. c*EPL+EPL-1
   if (r == 0) {
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-      if (g < p.G) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) sm.o[(wave * p.G + g) * D + c * EPL + e] = acc[g][e];
-        if (c == 0) {
-          sm.m[wave * p.G + g] = m[g];
-          sm.l[wave * p.G + g] = l[g];
-        }
-      }
-    }
+    for (int g = 0; g < GMAX; ++g)
+      if (g < p.G)
+        store_result(p, w, nps, w.h * p.G + g, c * EPL, acc[g], EPL, m[g], l[g], c == 0, bad, D);
   }
-  __syncthreads();
-  merge_waves_and_store<D>(p, w, nps, part_bad, sm);
 }
 
 // ============================================================================
@@ -425,7 +393,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 // 32*kc + 8*(l/16)); V is loaded as whole 256-byte rows (lane l: dims
 // 8*(l%16)..+8 of token 4*(l/16)+jj) and regrouped in registers so that lane l
 // feeds d = 8*(l%16)+n of tile n - no LDS transpose. The S^T output layout
-// (lane l: head l%16, tokens 4*(l/16)+r) is exactly the B operand P^T needs.
+// (lane l: head l%16, tokens 4*(l/16)+r) is exactly the B operand P^T needs,
+// and the O^T accumulator leaves lane l with head l%16, dims 32*(l/16)..+32.
 // P stays in fp32 precision: it is split into a 16-bit high part and a 16-bit
 // residual and both go through the PV MFMA, so the products are accumulated
 // in fp32 with no 16-bit rounding of the weights.
@@ -489,23 +458,22 @@ __device__ __forceinline__ uint2 gather_col(const uint4* v, int n) {
 template <int DT>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   constexpr int D = 128;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  const WorkItem w = work_item(p);
-  if (!w.ok) return;
-  const int ctx = p.lens[w.s];
-  if (!sequence_prologue<D>(p, w, ctx)) return;
-  const DecodeSmem sm = decode_smem(smem_raw, p.part_tokens, p.G);
-  const int nps = (ctx + p.part_tokens - 1) / p.part_tokens;
-  const int t0 = w.part * p.part_tokens;
-  const int t1 = min(ctx, t0 + p.part_tokens);
-  const int b0 = t0 / kBlock;
-  const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
-  stage_table(p, w, b0, nblk, sm);
-  const bool part_bad = *sm.bad != 0;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr size_t kTileBytes = (size_t)kBlock * D * 2;  // 4 KB
+  const int lane = threadIdx.x & 63;
+  const int u = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (u >= p.n_units) return;
   const int col = lane & 15;  // MFMA column: query head of the group / token row
   const int grp = lane >> 4;  // k-slot group
+  const WorkItem w = unit_item(p, u);
+  if (!w.ok) return;
+  const int ctx = p.lens[w.s];
+  const int nps = unit_prologue<D>(p, w, ctx, lane);
+  if (nps == 0) return;
+  const int t0 = w.part * p.part_tokens;
+  const int t1 = min(ctx, t0 + p.part_tokens);
+  const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
+  const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + t0 / kBlock;
+  bool bad = false;
 
   // B operand of the score MFMA: Q^T, lane holds head `col`, dims 32kc+8grp..+8
   uint4 qb[4];
@@ -528,10 +496,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 
   const char* kbase = static_cast<const char*>(p.k_pool);
   const char* vbase = static_cast<const char*>(p.v_pool);
-  constexpr size_t kTileBytes = (size_t)kBlock * D * 2;  // 4 KB
 
-  auto load = [&](int jb, uint4* ku, uint4* vu) {
-    const size_t tile = ((size_t)sm.tab[jb] * p.Hkv + w.h) * kTileBytes;
+  auto load = [&](int e, uint4* ku, uint4* vu) {
+    const size_t tile = ((size_t)e * p.Hkv + w.h) * kTileBytes;
     const uint4* kt = reinterpret_cast<const uint4*>(kbase + tile);
     const uint4* vt = reinterpret_cast<const uint4*>(vbase + tile);
 #pragma unroll
@@ -584,70 +551,84 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     }
   };
 
-  // this wave's blocks: wave, wave + 4, ...; two register sets alternate so
-  // the next block's loads are in flight while the current one is computed
-  const int nmine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
-  uint4 ka[4], va[4], kb[4], vb[4];
-  if (nmine > 0) load(wave, ka, va);
-  for (int i = 0; i < nmine; i += 2) {
-    const int jb = wave + i * kWaves;
-    if (i + 1 < nmine) load(jb + kWaves, kb, vb);
-    compute(jb, ka, va);
-    if (i + 1 >= nmine) break;
-    if (i + 2 < nmine) load(jb + 2 * kWaves, ka, va);
-    compute(jb + kWaves, kb, vb);
+  // Two register sets alternate so the next block's loads are in flight
+  // while the current block is computed. The steady-state loop issues its
+  // loads unconditionally (a load under a branch would force a wait for every
+  // outstanding load at the join); the last one or two blocks are peeled.
+  {
+    uint4 ka[4], va[4], kb[4], vb[4];
+    const int last = nblk - 1;
+    int eb = block_id(p, row, min(1, last), bad);
+    load(block_id(p, row, 0, bad), ka, va);
+    int jb = 0;
+    for (; jb + 2 < nblk; jb += 2) {
+      const int ea2 = block_id(p, row, jb + 2, bad);
+      load(eb, kb, vb);
+      compute(jb, ka, va);
+      eb = block_id(p, row, min(jb + 3, last), bad);
+      load(ea2, ka, va);
+      compute(jb + 1, kb, vb);
+    }
+    if (jb + 1 < nblk) {
+      load(eb, kb, vb);
+      compute(jb, ka, va);
+      compute(jb + 1, kb, vb);
+    } else {
+      compute(jb, ka, va);
+    }
   }
 
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
   if (col < p.G) {
-    if (grp == 0) {
-      sm.m[wave * p.G + col] = m;
-      sm.l[wave * p.G + col] = l;
-    }
+    // lane holds head `col`, dims 32*grp + 8*r + n for r < 4, n < 8
+    float res[32];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int n = 0; n < 8; ++n) sm.o[(wave * p.G + col) * D + 32 * grp + 8 * r + n] = o[n][r];
+      for (int n = 0; n < 8; ++n) res[8 * r + n] = o[n][r];
+    store_result(p, w, nps, w.h * p.G + col, 32 * grp, res, 32, m, l, grp == 0, bad, D);
   }
-  __syncthreads();
-  merge_waves_and_store<D>(p, w, nps, part_bad, sm);
 }
+
 // ============================================================================
 // Split-K merge ([2], "The Custom CUDA Kernel": partial outputs and softmax
-// denominators combined with a numerically stable merge): for every
-// (sequence, query head) with more than one partition,
+// denominators computed per piece, then merged with a numerically stable
+// rule). One workgroup per (sequence, query head) whose sequence has more
+// than one partition; thread d merges dimension d in partition order:
 //   M = max_k m_k,  L = sum_k l_k 2^(m_k - M),  out = sum_k 2^(m_k - M) o_k / L.
-// A NaN denominator (invalid table entry) makes the whole output NaN.
+// A NaN denominator (invalid table entry) makes the output NaN. All partial
+// (max, sum) pairs of the sequence are read by independent loads before use.
 // ============================================================================
 template <int D>
-__global__ __launch_bounds__(D) void splitk_reduce_kernel(float* __restrict__ out,
-                                                          const float* __restrict__ ws_o,
-                                                          const float* __restrict__ ws_ml,
-                                                          const int32_t* __restrict__ lens,
-                                                          int32_t Hq, int32_t nparts,
-                                                          int32_t part_tokens,
-                                                          int32_t max_blocks) {
+__global__ __launch_bounds__(D) void splitk_merge_kernel(float* __restrict__ out,
+                                                         const float* __restrict__ ws_o,
+                                                         const float* __restrict__ ws_ml,
+                                                         const int32_t* __restrict__ lens,
+                                                         int32_t Hq, int32_t nparts,
+                                                         int32_t part_tokens,
+                                                         int32_t max_blocks) {
   const int hq = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
   const int ctx = lens[s];
   if (ctx <= 0 || (int64_t)ctx > (int64_t)max_blocks * kBlock ||
       (int64_t)ctx > (int64_t)nparts * part_tokens)
-    return;  // handled by the partition kernel
+    return;  // written by the decode kernel
   const int nps = (ctx + part_tokens - 1) / part_tokens;
   if (nps <= 1) return;
   const size_t base = ((size_t)s * Hq + hq) * nparts;
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml) + base;
   float M = neg_inf();
   bool bad = false;
   for (int k = 0; k < nps; ++k) {
-    const float mk = ws_ml[(base + k) * 2];
-    const float lk = ws_ml[(base + k) * 2 + 1];
-    bad |= (lk != lk);
-    M = fmaxf(M, mk);
+    const float2 v = ml[k];
+    bad |= (v.y != v.y);
+    M = fmaxf(M, v.x);
   }
   float L = 0.f, O = 0.f;
   for (int k = 0; k < nps; ++k) {
-    const float f = fast_exp2(ws_ml[(base + k) * 2] - M);
-    L += ws_ml[(base + k) * 2 + 1] * f;
+    const float2 v = ml[k];
+    const float f = fast_exp2(v.x - M);
+    L += v.y * f;
     O += ws_o[(base + k) * D + d] * f;
   }
   out[((size_t)s * Hq + hq) * D + d] = bad ? __builtin_nanf("") : O / L;
@@ -731,17 +712,24 @@ int32_t effective_partition(int32_t partition_size) {
   return partition_size == 0 ? kDefaultPartition : partition_size;
 }
 
+// One wave per work unit, four waves per workgroup.
+template <typename Kernel>
+kv_status launch_decode(Kernel kernel, const DecodeParams& prm, hipStream_t st) {
+  const int64_t grid = ((int64_t)prm.n_units + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, prm);
+  return launch_status("kv_paged_attention_decode");
+}
+
 template <int DT, int D>
-kv_status launch_valu(const DecodeParams& prm, int gmax, dim3 grid, size_t lds, hipStream_t st) {
+kv_status launch_valu(const DecodeParams& prm, int gmax, hipStream_t st) {
   switch (gmax) {
-    case 1: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 1>), grid, dim3(kThreads), lds, st, prm); break;
-    case 2: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 2>), grid, dim3(kThreads), lds, st, prm); break;
-    case 4: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 4>), grid, dim3(kThreads), lds, st, prm); break;
-    case 8: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 8>), grid, dim3(kThreads), lds, st, prm); break;
-    case 16: hipLaunchKernelGGL((decode_valu_kernel<DT, D, 16>), grid, dim3(kThreads), lds, st, prm); break;
+    case 1: return launch_decode(decode_valu_kernel<DT, D, 1>, prm, st);
+    case 2: return launch_decode(decode_valu_kernel<DT, D, 2>, prm, st);
+    case 4: return launch_decode(decode_valu_kernel<DT, D, 4>, prm, st);
+    case 8: return launch_decode(decode_valu_kernel<DT, D, 8>, prm, st);
+    case 16: return launch_decode(decode_valu_kernel<DT, D, 16>, prm, st);
     default: return fail(KV_ERR_UNSUPPORTED, "decode: group size");
   }
-  return launch_status("kv_paged_attention_decode");
 }
 
 }  // namespace
@@ -817,12 +805,16 @@ kv_status kv_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num
   return KV_OK;
 }
 
-size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_t head_dim,
-                                          int32_t max_context_len, int32_t partition_size) {
+size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t max_context_len,
+                                          int32_t partition_size) {
   const int32_t P = effective_partition(partition_size);
-  if (S < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 || P <= 0) return 0;
+  if (S < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+      P <= 0)
+    return 0;
   const int64_t nparts = ceil_div64(max_context_len, P);
   if (nparts <= 1) return 0;
+  // partial outputs, then (max, sum) pairs
   return (size_t)S * num_q_heads * nparts * (head_dim + 2) * sizeof(float);
 }
 
@@ -859,16 +851,17 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(KV_ERR_INVALID, "kv_paged_attention_decode: out/q/pools must be 16-byte aligned");
   const int64_t nparts = ceil_div64(max_context_len, P) < 1 ? 1 : ceil_div64(max_context_len, P);
-  const size_t need = kv_paged_attention_workspace_bytes(S, num_q_heads, head_dim,
+  const size_t need = kv_paged_attention_workspace_bytes(S, num_q_heads, num_kv_heads, head_dim,
                                                          max_context_len, partition_size);
   if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace)))
     return fail(KV_ERR_INVALID, "kv_paged_attention_decode: workspace of %zu bytes needed (got %zu)",
                 need, ws_bytes);
   if (work_items && n_items <= 0)
     return fail(KV_ERR_INVALID, "kv_paged_attention_decode: work plan with %d items", n_items);
-  const int64_t nwg = work_items ? (int64_t)n_items * num_kv_heads
-                                 : nparts * num_kv_heads * (int64_t)S;
-  if (nwg > INT32_MAX) return fail(KV_ERR_INVALID, "kv_paged_attention_decode: grid too large");
+  const int64_t n_units = work_items ? (int64_t)n_items * num_kv_heads
+                                     : nparts * num_kv_heads * (int64_t)S;
+  if (n_units > INT32_MAX)
+    return fail(KV_ERR_INVALID, "kv_paged_attention_decode: too many work units");
 
   DecodeParams prm;
   prm.out = out;
@@ -878,7 +871,7 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
   prm.tables = block_tables;
   prm.lens = context_lens;
   prm.items = work_items;
-  prm.n_items = work_items ? n_items : 0;
+  prm.n_units = (int32_t)n_units;
   float* ws = static_cast<float*>(workspace);
   const size_t o_elems = (size_t)S * num_q_heads * nparts * head_dim;
   prm.ws_o = need ? ws : nullptr;
@@ -893,40 +886,32 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
   prm.nparts = (int32_t)nparts;
   prm.scale_log2 = scale * 1.4426950408889634f;
 
-  const dim3 grid((unsigned)nwg);
-  const size_t lds = decode_smem_bytes(P, G, head_dim);
   kv_status st;
   const bool mfma = (dtype == KV_F16 || dtype == KV_BF16) && head_dim == 128 && G >= 2;
   if (mfma) {
-    if (dtype == KV_BF16)
-      hipLaunchKernelGGL(decode_mfma_kernel<KV_BF16>, grid, dim3(kThreads), lds, stream, prm);
-    else
-      hipLaunchKernelGGL(decode_mfma_kernel<KV_F16>, grid, dim3(kThreads), lds, stream, prm);
-    st = launch_status("kv_paged_attention_decode");
+    st = dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16>, prm, stream)
+                          : launch_decode(decode_mfma_kernel<KV_F16>, prm, stream);
   } else {
     const int gmax = G == 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
     if (dtype == KV_F32)
-      st = head_dim == 64 ? launch_valu<KV_F32, 64>(prm, gmax, grid, lds, stream)
-                          : launch_valu<KV_F32, 128>(prm, gmax, grid, lds, stream);
+      st = head_dim == 64 ? launch_valu<KV_F32, 64>(prm, gmax, stream)
+                          : launch_valu<KV_F32, 128>(prm, gmax, stream);
     else if (dtype == KV_F16)
-      st = head_dim == 64 ? launch_valu<KV_F16, 64>(prm, gmax, grid, lds, stream)
-                          : launch_valu<KV_F16, 128>(prm, 1, grid, lds, stream);
+      st = head_dim == 64 ? launch_valu<KV_F16, 64>(prm, gmax, stream)
+                          : launch_valu<KV_F16, 128>(prm, 1, stream);
     else
-      st = head_dim == 64 ? launch_valu<KV_BF16, 64>(prm, gmax, grid, lds, stream)
-                          : launch_valu<KV_BF16, 128>(prm, 1, grid, lds, stream);
+      st = head_dim == 64 ? launch_valu<KV_BF16, 64>(prm, gmax, stream)
+                          : launch_valu<KV_BF16, 128>(prm, 1, stream);
   }
-  if (st != KV_OK) return st;
-  if (nparts > 1) {
-    const dim3 rgrid((unsigned)num_q_heads, (unsigned)S);
-    if (head_dim == 128)
-      hipLaunchKernelGGL(splitk_reduce_kernel<128>, rgrid, dim3(128), 0, stream, out, prm.ws_o,
-                         prm.ws_ml, context_lens, num_q_heads, prm.nparts, P, max_blocks);
-    else
-      hipLaunchKernelGGL(splitk_reduce_kernel<64>, rgrid, dim3(64), 0, stream, out, prm.ws_o,
-                         prm.ws_ml, context_lens, num_q_heads, prm.nparts, P, max_blocks);
-    st = launch_status("kv_paged_attention_decode (reduce)");
-  }
-  return st;
+  if (st != KV_OK || nparts <= 1) return st;
+  const dim3 rgrid((unsigned)num_q_heads, (unsigned)S);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(splitk_merge_kernel<128>, rgrid, dim3(128), 0, stream, out, prm.ws_o,
+                       prm.ws_ml, context_lens, num_q_heads, prm.nparts, P, max_blocks);
+  else
+    hipLaunchKernelGGL(splitk_merge_kernel<64>, rgrid, dim3(64), 0, stream, out, prm.ws_o,
+                       prm.ws_ml, context_lens, num_q_heads, prm.nparts, P, max_blocks);
+  return launch_status("kv_paged_attention_decode (split-K merge)");
 }
 
 }  // extern "C"

@@ -107,8 +107,8 @@ class DecodeSession:
         self.d_pairs = torch.tensor(pairs, dtype=torch.int32, device=dev).reshape(-1, 2)
         self.max_context_len = int(lens.max()) if len(lens) else 0
         S = len(seqs)
-        ws = kv.kv_paged_attention_workspace_bytes(S, self.Hq, self.D, self.max_context_len,
-                                                   self.partition_size)
+        ws = kv.kv_paged_attention_workspace_bytes(S, self.Hq, self.Hkv, self.D,
+                                                   self.max_context_len, self.partition_size)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev) if ws else None
         self.host_tables, self.host_lens = tables, lens
         self.d_items = None

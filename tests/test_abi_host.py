@@ -95,9 +95,9 @@ def test_device_entry_points_validate_on_the_host(kv):
 
 
 def test_workspace_size_formula(kv):
-    assert kv.kv_paged_attention_workspace_bytes(8, 32, 128, 512, 0) == 0
-    assert kv.kv_paged_attention_workspace_bytes(8, 32, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
-    assert kv.kv_paged_attention_workspace_bytes(4, 4, 64, 40, 16) == 4 * 4 * 3 * 66 * 4
+    assert kv.kv_paged_attention_workspace_bytes(8, 32, 8, 128, 512, 0) == 0
+    assert kv.kv_paged_attention_workspace_bytes(8, 32, 8, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
+    assert kv.kv_paged_attention_workspace_bytes(4, 4, 2, 64, 40, 16) == 4 * 4 * 3 * 66 * 4
 
 
 # ---------------------------------------------------------------------------

@@ -214,8 +214,8 @@ def gpu_decode(q, kp, vp, tab, lens, scale, dt, partition_size=0, max_ctx=None, 
     S, Hq, D = q.shape
     out = torch.full((S, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
     mc = int(lens.max()) if max_ctx is None else max_ctx
-    wsb = kv.kv_paged_attention_workspace_bytes(S, Hq, D, mc, partition_size)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
+    wsb = kv.kv_paged_attention_workspace_bytes(S, Hq, kp.shape[1], D, mc, partition_size)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
     items = None
     if plan:
         items = torch.from_numpy(kv.kv_paged_attention_plan(lens, partition_size)).cuda()
@@ -330,3 +330,30 @@ def test_split_and_unsplit_agree_and_runs_are_deterministic():
         check_attention(outs[ps].reshape(-1, D), ref.reshape(-1, D), dt, f"partition {ps}")
     again = gpu_decode(q, kp, vp, tab, cl, 0.088, dt, 512)
     assert np.array_equal(again.view(np.uint32), outs[512].view(np.uint32))
+
+
+def test_workspace_reuse_gives_identical_results():
+    """Repeated calls on one workspace (with and without a plan) give
+    bit-identical results: nothing from a previous call leaks into the next."""
+    kv = kvlib()
+    rng = np.random.default_rng(41)
+    dt, D, Hkv, G = "bf16", 128, 4, 4
+    lens = np.array([3000, 1, 513, 1024, 777], np.int32)
+    q, kp, vp, tab, cl = random_case(rng, list(lens), G * Hkv, Hkv, D, dt)
+    S, Hq = len(lens), G * Hkv
+    P = 256
+    mc = int(lens.max())
+    wsb = kv.kv_paged_attention_workspace_bytes(S, Hq, Hkv, D, mc, P)
+    ws = torch.full((wsb // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    args = (to_dev(q, dt), to_dev(kp, dt), to_dev(vp, dt), torch.from_numpy(tab).cuda(),
+            torch.from_numpy(cl).cuda())
+    items = torch.from_numpy(kv.kv_paged_attention_plan(cl, P)).cuda()
+    outs = []
+    for rep in range(3):
+        out = torch.full((S, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+        kv.kv_paged_attention_decode(out, *args, 0.088, mc, ws, P, items if rep != 1 else None)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert all(np.array_equal(outs[0].view(np.uint32), o.view(np.uint32)) for o in outs[1:])
+    ref = oracle.decode_attention(q, kp, vp, tab, cl, 0.088, dt)
+    check_attention(outs[0].reshape(-1, D), ref.reshape(-1, D), dt, "workspace reuse")
