@@ -45,8 +45,98 @@ def parse():
     ap.add_argument("--no-plan", action="store_true", help="padded grid instead of the host work plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--pmc-traffic", default="", help="JSON file with measured HBM traffic per launch")
+    ap.add_argument("--pmc-traffic", default="",
+                    help="JSON file with the measured HBM traffic per decode call "
+                         "(default: profiles/decode_traffic_<workload>.json when it matches the kernels)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before the timed steps, run kv_copy_blocks over a buffer of known size "
+                         "(reference dispatches for scaling the HBM byte counters)")
+    ap.add_argument("--pmc-parse", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --copy-calibration` into the traffic JSON and exit")
+    ap.add_argument("--pmc-out", default="", help="where --pmc-parse writes its JSON")
     return ap.parse_args()
+
+
+CAL_PAIRS = 4096            # block pairs copied by the calibration dispatch
+CAL_BLOCK_BYTES = 32768     # bytes per block and pool (K and V each)
+
+
+def kernel_source_digest():
+    """Digest of the device sources: measured traffic is only reported while
+    the kernels it was taken on are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_162_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith(".hip"):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration(kv, torch):
+    """A plain copy of known size through kv_copy_blocks: CAL_PAIRS blocks of
+    CAL_BLOCK_BYTES in each of two pools, i.e. 2*CAL_PAIRS*CAL_BLOCK_BYTES bytes
+    read and the same written per dispatch."""
+    nb = 2 * CAL_PAIRS
+    k = torch.zeros(nb * CAL_BLOCK_BYTES, dtype=torch.uint8, device="cuda")
+    v = torch.zeros_like(k)
+    pairs = torch.stack([torch.arange(CAL_PAIRS, dtype=torch.int32),
+                         torch.arange(CAL_PAIRS, 2 * CAL_PAIRS, dtype=torch.int32)], 1).cuda()
+    for _ in range(5):
+        kv.kv_copy_blocks([k], [v], pairs, nb, CAL_BLOCK_BYTES)
+    torch.cuda.synchronize()
+    del k, v
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def _mean_counter(rows, kernel_substr, counter):
+    """Mean over dispatches of one counter for kernels whose name contains
+    kernel_substr (values summed per dispatch first)."""
+    per = {}
+    for r in rows:
+        if kernel_substr in r["Kernel_Name"] and r["Counter_Name"].startswith(counter):
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return (sum(per.values()) / len(per), len(per)) if per else (0.0, 0)
+
+
+def pmc_parse(fetch_dir, write_dir, out_path, workload, partition):
+    """HBM bytes per decode call from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the calibration
+    copy, whose true byte count is known."""
+    cal_bytes = 2 * CAL_PAIRS * CAL_BLOCK_BYTES
+    res = {"workload": workload, "partition": partition,
+           "kernel_source_digest": kernel_source_digest(), "calibration_bytes": cal_bytes}
+    total = 0.0
+    for tag, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(d)
+        cal, ncal = _mean_counter(rows, "copy_blocks_kernel", counter)
+        dec, ndec = _mean_counter(rows, "decode_", counter)
+        mrg, nmrg = _mean_counter(rows, "splitk_merge", counter)
+        if ncal == 0 or ndec == 0:
+            raise SystemExit(f"{d}: calibration or decode dispatches missing")
+        factor = cal_bytes / (cal * 1024.0)
+        per_call = (dec + (mrg if nmrg else 0.0)) * 1024.0 * factor
+        res[tag] = {"counter": counter, "calibration_kib": cal, "factor": factor,
+                    "decode_kib": dec, "merge_kib": mrg if nmrg else None,
+                    "decode_dispatches": ndec, "bytes_per_call": per_call}
+        total += per_call
+    res["bytes_per_launch"] = total
+    with open(out_path, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res))
 
 
 def to_dev(a, dt):
@@ -96,6 +186,10 @@ def cpu_baseline(w, seconds):
 
 def main():
     args = parse()
+    if args.pmc_parse:
+        out = args.pmc_out or os.path.join(ROOT, "profiles", f"decode_traffic_w{args.workload}.json")
+        pmc_parse(args.pmc_parse[0], args.pmc_parse[1], out, args.workload, args.partition or 512)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the design for sharding is described in DESIGN.md)"}))
@@ -133,6 +227,8 @@ def main():
     for _ in range(R - 1):
         reps.append((kp.clone(), vp.clone(), q.clone(), kn.clone(), vn.clone()))
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration(kv, torch)
 
     def one(k, events=None):
         a, b, qq, kk, vv = reps[k % R]
@@ -171,8 +267,12 @@ def main():
     value = kvb / (step_ms * 1e-3) / 1e9
     achieved = alg / (dec_avg * 1e-3) / 1e9
     traffic = None
-    if args.pmc_traffic and os.path.exists(args.pmc_traffic):
-        traffic = json.load(open(args.pmc_traffic)).get("bytes_per_launch")
+    tpath = args.pmc_traffic or os.path.join(ROOT, "profiles", f"decode_traffic_w{args.workload}.json")
+    if os.path.exists(tpath):
+        t = json.load(open(tpath))
+        if t.get("kernel_source_digest") == kernel_source_digest() and \
+                t.get("workload") == args.workload and (args.partition or 512) == t.get("partition", 512):
+            traffic = round(float(t["bytes_per_launch"]))
 
     res = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) and seqs/s per config, 1 GPU",
