@@ -176,6 +176,23 @@ kv_status kv_reshape_and_cache(const void* k_new, const void* v_new, void* k_poo
                                int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                                int32_t block_size, kv_dtype dtype, hipStream_t stream);
 
+/* Slot mapping and cache write of a batch of new tokens in one launch: token
+ * i (i < n) goes to position pos[i] of sequence seq_idx[i]; its slot is
+ * computed as kv_slot_mapping does ([4], "How it works"), stored in slots[i],
+ * and its K and V rows are copied there as kv_reshape_and_cache does ([3],
+ * "The allocation lifecycle": each decode step writes the new token's K,V
+ * into the last block). Arguments as for those two calls: tables
+ * [num_rows][max_blocks] int32, seq_idx and pos int32 [n], k_new and v_new
+ * [n][num_kv_heads][head_dim] of `dtype`, slots int64 [n]; all device
+ * pointers. Unmappable tokens get slot -1 and are not written. The copy is
+ * bit exact; slots must be distinct within a call. */
+kv_status kv_append_tokens(const int32_t* tables, int32_t num_rows, int32_t max_blocks,
+                           const int32_t* seq_idx, const int32_t* pos, int32_t n,
+                           const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                           int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, kv_dtype dtype, int64_t* slots,
+                           hipStream_t stream);
+
 /* Device half of copy-on-write ([2], "Copy-on-Write ...": copy the shared
  * block's content into the new block): for every pair (pairs[2i] = src,
  * pairs[2i+1] = dst) and every layer, copy block_bytes bytes of K and of V
@@ -211,12 +228,13 @@ kv_status kv_paged_attention_plan(const int32_t* context_lens_host, int32_t S,
 
 /* Workspace bytes kv_paged_attention_decode needs for these sizes: 0 when
  * max_context_len <= the partition size (every sequence finishes in one
- * partition), else S * num_q_heads * num_partitions * (head_dim + 2) * 4 for
- * the per-partition partial outputs, maxima and sums. num_kv_heads is
- * accepted for forward compatibility and does not change the size.
- * partition_size 0 picks the default (512). Returns 0 for invalid sizes.
- * The workspace needs no initialisation; calls that run concurrently need
- * separate workspaces. */
+ * partition), else S * num_q_heads * num_partitions * (head_dim + 2) * 4.
+ * Layout (fp32): partial outputs [S][num_kv_heads][num_partitions][G][head_dim]
+ * then partial (max, sum) pairs [S][num_kv_heads][num_partitions][G][2],
+ * G = num_q_heads / num_kv_heads, so one work unit's partials are
+ * contiguous. partition_size 0 picks the default (512). Returns 0 for
+ * invalid sizes. The workspace needs no initialisation; calls that run
+ * concurrently need separate workspaces. */
 size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
                                           int32_t head_dim, int32_t max_context_len,
                                           int32_t partition_size);
@@ -233,10 +251,12 @@ size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_
  * context_lens: device int32 [S]
  * max_context_len: host upper bound on every context_lens[s]; it sizes the
  *               grid (number of partitions).
- * partition_size: tokens per work item (multiple of 16, 16..8192); 0 = 512.
- *               Sequences longer than one partition are split and merged
- *               with a log-sum-exp reduction ([2], "The Custom CUDA Kernel":
- *               per-piece partial outputs and denominators merged stably).
+ * partition_size: tokens per work item (multiple of 16, 16..1024); 0 = 512.
+ *               Sequences longer than one partition are split and a second
+ *               kernel merges the partial results with a log-sum-exp
+ *               reduction ([2], "The Custom CUDA Kernel": per-piece partial
+ *               outputs and denominators merged stably), in partition
+ *               order, so results do not depend on scheduling.
  * work_items:   optional device int32 [n_items][2] from
  *               kv_paged_attention_plan; the grid is then exactly n_items *
  *               num_kv_heads workgroups. NULL: the grid covers every possible
@@ -255,7 +275,9 @@ size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_
  *
  * Kernels: head groups of 2..16 query heads per KV head with f16/bf16 and
  * head_dim 128 run on MFMA matrix cores; other cases run on the vector ALUs.
- * One workgroup handles one (sequence, KV head, partition). */
+ * One workgroup (a single wave64) handles one (sequence, KV head,
+ * partition). A call is one kernel launch, plus the merge launch when
+ * max_context_len exceeds the partition size. */
 kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_pool,
                                     const void* v_pool, const int32_t* block_tables,
                                     int32_t max_blocks, const int32_t* context_lens, int32_t S,

@@ -70,6 +70,8 @@ _SIGS = {
     "kv_seq_pack_tables": (C.c_int, [vp, i32, P_i64, i32, P_i32, P_i32]),
     "kv_slot_mapping": (C.c_int, [vp, i32, i32, vp, vp, i32, i32, vp, vp]),
     "kv_reshape_and_cache": (C.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, C.c_int, vp]),
+    "kv_append_tokens": (C.c_int, [vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32,
+                                   C.c_int, vp, vp]),
     "kv_copy_blocks": (C.c_int, [C.POINTER(vp), C.POINTER(vp), i32, vp, i32, i32, C.c_size_t, vp]),
     "kv_paged_attention_plan": (C.c_int, [P_i32, i32, i32, P_i32, i32, P_i32]),
     "kv_paged_attention_workspace_bytes": (C.c_size_t, [i32, i32, i32, i32, i32, i32]),
@@ -250,6 +252,25 @@ def kv_reshape_and_cache(k_new, v_new, k_pool, v_pool, slots, stream=None) -> No
                                     _dev(v_pool, "v_pool"), _dev(slots, "slots", torch.int64),
                                     k_new.shape[0], NB, Hkv, D, B, dtype_code(k_pool), _stream(stream)),
            "kv_reshape_and_cache")
+
+
+def kv_append_tokens(tables, seq_idx, pos, k_new, v_new, k_pool, v_pool, slots, stream=None) -> None:
+    """Slot mapping + cache write in one launch. tables int32 [rows, max_blocks];
+    seq_idx/pos int32 [n]; k_new/v_new [n, Hkv, D]; pools [NB, Hkv, B, D];
+    slots int64 [n] (output)."""
+    torch = _torch()
+    NB, Hkv, B, D = k_pool.shape
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or k_new.shape != v_new.shape \
+            or k_new.shape[1:] != (Hkv, D) or k_new.dtype != k_pool.dtype \
+            or seq_idx.numel() != k_new.shape[0] or pos.numel() != k_new.shape[0] \
+            or slots.numel() != k_new.shape[0]:
+        raise KVError(KV_ERR_INVALID, "kv_append_tokens", "shape/dtype mismatch")
+    _check(lib.kv_append_tokens(_dev(tables, "tables", torch.int32), tables.shape[0], tables.shape[1],
+                                _dev(seq_idx, "seq_idx", torch.int32), _dev(pos, "pos", torch.int32),
+                                k_new.shape[0], _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), NB, Hkv, D, B,
+                                dtype_code(k_pool), _dev(slots, "slots", torch.int64), _stream(stream)),
+           "kv_append_tokens")
 
 
 def kv_copy_blocks(k_pools: List, v_pools: List, pairs, num_blocks: int, block_bytes: int,

@@ -1,5 +1,5 @@
 // Device side of pagedkv for AMD CDNA4 (gfx950): slot mapping, cache scatter,
-// copy-on-write block copy, paged decode attention and the split-K merge.
+// copy-on-write block copy and paged decode attention with its split-K merge.
 //
 // Pages cited in this file:
 //   [1] "PagedAttention - how vLLM stopped wasting 80% of your GPU memory"
@@ -16,13 +16,13 @@
 // Decode attention computes, per sequence and query head, the softmax of the
 // scaled dot products with every live key and the weighted sum of the values
 // - exactly the contiguous-cache result ([1], "The PagedAttention kernel").
-// Work split: one workgroup (4 wave64s) per (sequence, KV head, context
-// partition). The partition's block-table entries are staged in LDS first, so
-// every K/V address is known before the first load. Each wave walks every
-// fourth 16-token block of the partition, keeps an online softmax (running
-// max and sum, [2] "The Custom CUDA Kernel"), and the four waves merge in
-// LDS. Sequences longer than one partition write unnormalised partial results
-// that a second kernel merges with the log-sum-exp rule.
+// Work split: one workgroup of one wave64 per (sequence, KV head, context
+// partition). The partition's block-table entries are read once, one per
+// lane, and broadcast from registers, so every K/V address is known before
+// the first load. The wave keeps an online softmax (running max and sum, [2]
+// "The Custom CUDA Kernel") over its partition. Sequences longer than one
+// partition write unnormalised partial results, which a second kernel
+// merges with the log-sum-exp rule.
 //
 // Softmax runs in base 2: scores are multiplied by scale*log2(e) and
 // exponentiated with v_exp_f32; the result is the same softmax.
@@ -40,18 +40,23 @@ using pagedkv::fail;
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 
-constexpr int kBlock = 16;          // tokens per KV block (device kernels)
-constexpr int kWaves = 4;           // wave64s per decode workgroup
-constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxPartition = 8192; // tokens
+constexpr int kBlock = 16;           // tokens per KV block (device kernels)
+constexpr int kMaxPartition = 1024;  // tokens: at most 64 blocks, one table entry per lane
 constexpr int kDefaultPartition = 512;
+constexpr int kStageStride = 132;  // floats per head row in LDS (128 + 4 against bank conflicts)
+#ifndef PAGEDKV_DECODE_RING
+#define PAGEDKV_DECODE_RING 3
+#endif
+constexpr int kDecodeRing = PAGEDKV_DECODE_RING;  // K/V blocks in flight per wave (MFMA decode)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
 // ---- element conversion -----------------------------------------------------
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -78,7 +83,7 @@ __device__ __forceinline__ void unpack16(const uint4& u, float* f) {
   }
 }
 
-// ---- cross-lane reductions --------------------------------------------------
+// ---- cross-lane operations ---------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -96,8 +101,6 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
-
 // ---- shared decode parameters ----------------------------------------------
 struct DecodeParams {
   float* out;
@@ -107,21 +110,17 @@ struct DecodeParams {
   const int32_t* tables;
   const int32_t* lens;
   const int32_t* items;  // optional work plan: [n_items][2] = (sequence, partition)
-  float* ws_o;           // [S][Hq][nparts][D]   partial outputs (unnormalised)
-  float* ws_ml;          // [S][Hq][nparts][2]   partial (max, sum) in base-2 units
+  float* ws_o;           // [S][Hkv][nparts][G][D]  partial outputs (unnormalised)
+  float* ws_ml;          // [S][Hkv][nparts][G][2]  partial (max, sum) in base-2 units
   int32_t max_blocks, S, Hq, Hkv, G, num_blocks, part_tokens, nparts, n_units;
   float scale_log2;
 };
 
-// Every wave64 is an independent worker: wave `u` of the grid processes work
-// unit u, one (sequence, KV head, context partition), from its first block
-// to its last, and writes its result itself - the normalised output when the
-// sequence has a single partition, else an unnormalised partial result for
-// the split-K merge. There is no cross-wave merge, no LDS and no barrier, so
-// nothing stalls one wave on another. With a plan, u = item * Hkv + head and
-// the items are sorted longest first: the four waves of a workgroup get
-// units of similar size and finish together, and the hardware dispatcher
-// balances the tail. Without a plan, u enumerates (partition, head,
+// Wave u of the grid (one wave per workgroup) processes work unit u: one
+// (sequence, KV head, partition). With a plan, u = item * Hkv + head and the
+// items are sorted longest first; since workgroups go to the eight XCDs in
+// turn, a head count that is a multiple of 8 keeps every unit of one KV head
+// on one XCD (and its L2). Without a plan, u enumerates (partition, head,
 // sequence) over every possible partition and units past a sequence's end
 // return at once.
 struct WorkItem {
@@ -145,11 +144,11 @@ __device__ __forceinline__ WorkItem unit_item(const DecodeParams& p, int u) {
   return w;
 }
 
-// Sequence-level checks shared by both decode kernels (one wave). Returns the
-// number of partitions of the sequence when this unit has tokens to process,
-// else 0 (the output of an empty or invalid sequence is written by its
-// partition-0 unit: zeros, or NaN for a length that is negative or exceeds
-// the table or max_context_len).
+// Sequence-level checks (one wave). Returns the number of partitions of the
+// sequence when this unit has tokens to process, else 0. The output of an
+// empty or invalid sequence is written here by its partition-0 unit: zeros,
+// or NaN for a length that is negative or exceeds the table or
+// max_context_len.
 template <int D>
 __device__ __forceinline__ int unit_prologue(const DecodeParams& p, const WorkItem& w, int ctx,
                                              int lane) {
@@ -167,29 +166,41 @@ __device__ __forceinline__ int unit_prologue(const DecodeParams& p, const WorkIt
   return w.part < nps ? nps : 0;
 }
 
-// Physical block of logical block `jb` of the unit's partition, read through
-// the scalar cache (the index is wave-uniform). An ID outside the pool marks
-// the unit invalid and is read as block 0, so no load leaves the pool.
-__device__ __forceinline__ int block_id(const DecodeParams& p, const int32_t* row, int jb,
-                                        bool& bad) {
-  int e = row[jb];
-  if (e < 0 || e >= p.num_blocks) {
-    bad = true;
-    e = 0;
-  }
+// Stage the unit's table entries ([2], "The Custom CUDA Kernel": the kernel
+// resolves logical blocks through the block table): lane i receives the
+// physical ID of the partition's block i (i < nblk <= 64). An ID outside the
+// pool marks the unit invalid and is replaced by block 0, so no load leaves
+// the pool. Entry j is later read by every lane with readlane.
+__device__ __forceinline__ int stage_entries(const DecodeParams& p, const int32_t* row, int nblk,
+                                             int lane, bool& bad) {
+  int e = 0;
+  if (lane < nblk) e = row[lane];
+  const bool out_of_pool = lane < nblk && (e < 0 || e >= p.num_blocks);
+  if (out_of_pool) e = 0;
+  bad = __builtin_amdgcn_ballot_w64(out_of_pool) != 0;
   return e;
 }
 
-// Store `n` consecutive floats of head `hq` starting at dimension d0: the
-// final output o / l for a single-partition sequence, else the partial
-// result o (and, from the lane with `write_ml`, the pair (m, l)). An invalid
+__device__ __forceinline__ int entry_of(int staged, int j) {
+  return __builtin_amdgcn_readlane(staged, j);
+}
+
+// Start of the unit's partial results: the G heads of (sequence, KV head,
+// partition) are contiguous, G x D outputs then G (max, sum) pairs.
+__device__ __forceinline__ size_t partial_group(const DecodeParams& p, const WorkItem& w) {
+  return ((size_t)w.s * p.Hkv + w.h) * p.nparts + w.part;
+}
+
+// Store n (multiple of 4) consecutive floats of group head g from dimension
+// d0: the final output o / l for a single-partition sequence, else the
+// partial o and, from the lane with write_ml, the pair (m, l). An invalid
 // unit stores NaN.
 __device__ __forceinline__ void store_result(const DecodeParams& p, const WorkItem& w, int nps,
-                                             int hq, int d0, const float* o, int n, float m,
+                                             int g, int d0, const float* o, int n, float m,
                                              float l, bool write_ml, bool bad, int D) {
   const float nan = __builtin_nanf("");
   if (nps == 1) {
-    float* dst = p.out + ((size_t)w.s * p.Hq + hq) * D + d0;
+    float* dst = p.out + ((size_t)w.s * p.Hq + (size_t)w.h * p.G + g) * D + d0;
     const float inv = 1.0f / l;
     for (int i = 0; i < n; i += 4) {
       float4 v = make_float4(o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv);
@@ -197,13 +208,69 @@ __device__ __forceinline__ void store_result(const DecodeParams& p, const WorkIt
       *reinterpret_cast<float4*>(dst + i) = v;
     }
   } else {
-    const size_t slot = ((size_t)w.s * p.Hq + hq) * p.nparts + w.part;
-    float* dst = p.ws_o + slot * D + d0;
+    const size_t grp = partial_group(p, w);
+    float* dst = p.ws_o + (grp * p.G + g) * D + d0;
     for (int i = 0; i < n; i += 4)
       *reinterpret_cast<float4*>(dst + i) = make_float4(o[i], o[i + 1], o[i + 2], o[i + 3]);
     if (write_ml)
-      *reinterpret_cast<float2*>(p.ws_ml + slot * 2) = bad ? make_float2(nan, nan)
-                                                            : make_float2(m, l);
+      *reinterpret_cast<float2*>(p.ws_ml + (grp * p.G + g) * 2) =
+          bad ? make_float2(nan, nan) : make_float2(m, l);
+  }
+}
+
+// ============================================================================
+// Split-K merge ([2], "The Custom CUDA Kernel": per-piece partial outputs and
+// softmax denominators, merged with a numerically stable rule):
+//   M = max_k m_k,  L = sum_k l_k 2^(m_k - M),  out = sum_k 2^(m_k - M) o_k / L.
+// One workgroup per (sequence, KV head); sequences with one partition were
+// finished by the decode kernel and return at once. Thread t merges float4
+// chunk t of the group's G x D outputs, in partition order, so for each
+// partition the workgroup reads that partition's G x D partials as one
+// contiguous span and writes the group's outputs as one contiguous span. A
+// NaN partial sum (invalid table entry) makes the output NaN.
+// ============================================================================
+constexpr int kMergeThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void splitk_merge_kernel(DecodeParams p) {
+  const int s = blockIdx.x / p.Hkv, h = blockIdx.x % p.Hkv;
+  const int ctx = p.lens[s];
+  if (ctx <= 0 || (int64_t)ctx > (int64_t)p.max_blocks * kBlock ||
+      (int64_t)ctx > (int64_t)p.nparts * p.part_tokens)
+    return;  // written by the decode kernel
+  const int nps = (ctx + p.part_tokens - 1) / p.part_tokens;
+  if (nps <= 1) return;
+  const size_t grp0 = ((size_t)s * p.Hkv + h) * p.nparts;  // partition 0 of the group
+  const int n_chunks = p.G * (D / 4);
+  for (int c = threadIdx.x; c < n_chunks; c += kMergeThreads) {
+    const int g = c / (D / 4);
+    const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + grp0 * p.G + g;
+    float M = neg_inf();
+    bool bad = false;
+    for (int k = 0; k < nps; ++k) {
+      const float2 v = ml[(size_t)k * p.G];
+      bad |= (v.y != v.y);
+      M = fmaxf(M, v.x);
+    }
+    float L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* po = p.ws_o + grp0 * p.G * D + (size_t)c * 4;
+#pragma unroll 8
+    for (int k = 0; k < nps; ++k) {
+      const float2 v = ml[(size_t)k * p.G];
+      const float f = fast_exp2(v.x - M);
+      const float4 o = *reinterpret_cast<const float4*>(po + (size_t)k * p.G * D);
+      L += v.y * f;
+      O.x += o.x * f;
+      O.y += o.y * f;
+      O.z += o.z * f;
+      O.w += o.w * f;
+    }
+    const float inv = 1.0f / L;
+    float4 r = make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
+    if (bad) r = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                             __builtin_nanf(""));
+    *reinterpret_cast<float4*>(p.out + ((size_t)s * p.Hq + (size_t)h * p.G) * D + (size_t)c * 4) = r;
   }
 }
 
@@ -216,7 +283,7 @@ __device__ __forceinline__ void store_result(const DecodeParams& p, const WorkIt
 // tokens it reads; the groups are merged with cross-lane shuffles at the end.
 // ============================================================================
 template <int DT, int D, int GMAX>
-__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   constexpr int EB = DT == KV_F32 ? 4 : 2;
   constexpr int EPL = 16 / EB;           // elements per lane chunk
   constexpr int LPR = D * EB / 16;       // lanes per token row
@@ -224,8 +291,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
   constexpr int IPB = kBlock / TPI;      // loads per 16-token block
   static_assert(LPR == 8 || LPR == 16 || LPR == 32, "unsupported row width");
 
-  const int lane = threadIdx.x & 63;
-  const int u = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x;
+  const int u = blockIdx.x;
   if (u >= p.n_units) return;
   const int r = lane / LPR, c = lane % LPR;
   const WorkItem w = unit_item(p, u);
@@ -238,6 +305,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
   const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
   const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + t0 / kBlock;
   bool bad = false;
+  const int staged = stage_entries(p, row, nblk, lane, bad);
 
   // query chunk of every head in the group, pre-scaled into base-2 logits
   float qf[GMAX][EPL];
@@ -330,24 +398,21 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 
   // Two register sets alternate so the next block's loads are in flight
   // while the current one is computed. The steady-state loop issues its loads
-  // unconditionally (a load under a branch would force a wait for every
+  // unconditionally (a load under a branch makes the compiler wait for every
   // outstanding load at the join); the last one or two blocks are peeled.
   {
     uint4 ka[IPB], va[IPB], kb[IPB], vb[IPB];
     const int last = nblk - 1;
-    int eb = block_id(p, row, min(1, last), bad);
-    load(block_id(p, row, 0, bad), ka, va);
+    load(entry_of(staged, 0), ka, va);
     int jb = 0;
     for (; jb + 2 < nblk; jb += 2) {
-      const int ea2 = block_id(p, row, jb + 2, bad);
-      load(eb, kb, vb);
+      load(entry_of(staged, jb + 1), kb, vb);
       compute(jb, ka, va);
-      eb = block_id(p, row, min(jb + 3, last), bad);
-      load(ea2, ka, va);
+      load(entry_of(staged, jb + 2), ka, va);
       compute(jb + 1, kb, vb);
     }
     if (jb + 1 < nblk) {
-      load(eb, kb, vb);
+      load(entry_of(staged, min(jb + 1, last)), kb, vb);
       compute(jb, ka, va);
       compute(jb + 1, kb, vb);
     } else {
@@ -379,26 +444,43 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 #pragma unroll
     for (int g = 0; g < GMAX; ++g)
       if (g < p.G)
-        store_result(p, w, nps, w.h * p.G + g, c * EPL, acc[g], EPL, m[g], l[g], c == 0, bad, D);
+        store_result(p, w, nps, g, c * EPL, acc[g], EPL, m[g], l[g], c == 0, bad, D);
   }
 }
 
 // ============================================================================
 // Decode on MFMA matrix cores for grouped-query attention: f16/bf16, head_dim
 // 128, 2..16 query heads sharing one KV head. Per 16-token block a wave forms
-//   S^T[token][head] = K[token][:] . Q[head][:]   (4 x mfma 16x16x32)
-//   O^T[d][head]   += V^T[d][token] . P^T[token][head]   (16 x mfma 16x16x16)
-// The group's heads are the 16 MFMA columns (unused columns are zero). K is
-// loaded straight into the A-operand layout (lane l: token l%16, 8 dims at
-// 32*kc + 8*(l/16)); V is loaded as whole 256-byte rows (lane l: dims
-// 8*(l%16)..+8 of token 4*(l/16)+jj) and regrouped in registers so that lane l
-// feeds d = 8*(l%16)+n of tile n - no LDS transpose. The S^T output layout
-// (lane l: head l%16, tokens 4*(l/16)+r) is exactly the B operand P^T needs,
-// and the O^T accumulator leaves lane l with head l%16, dims 32*(l/16)..+32.
-// P stays in fp32 precision: it is split into a 16-bit high part and a 16-bit
-// residual and both go through the PV MFMA, so the products are accumulated
-// in fp32 with no 16-bit rounding of the weights.
+//   S^T[token][col] = K[token][:] . Q[col][:]       (4 x mfma 16x16x32)
+//   O^T[d][col]   += V^T[d][token] . P^T[token][col]  (8 x mfma 16x16x16)
+// The 16 MFMA columns are query heads. P stays in fp32 precision: each weight
+// is split into a 16-bit high part and a 16-bit residual. With at most 8
+// heads (SPLITCOL) the group's queries are placed twice, in columns 0..7 and
+// 8..15; columns 0..7 carry the high parts and 8..15 the residuals through
+// the same PV MFMA, and the two halves are added at the end. With 9..16 heads
+// each tile takes two PV MFMAs, one per part.
+//
+// Register layouts (lane l, c = l % 16, g = l / 16):
+//   16x16x32: A row c, k = 8g..8g+7;  B k = 8g..8g+7, column c;
+//   16x16x16: A row c, k = 4g..4g+3;  B k = 4g..4g+3, column c;
+//   C (both): rows 4g..4g+3, column c.
+// K is loaded straight into the A layout of the score MFMA (lane: token c,
+// dims 32kc+8g..+8). The score tile leaves lane l with column c, tokens
+// 4g..4g+3 - exactly the lane's B operand of the PV product. V is loaded as
+// whole 256-byte rows (lane: dims 8c..8c+7 of tokens 4g..4g+3) and regrouped
+// with v_perm so that tile n holds dimension d = 8c + n in row c - no LDS
+// transpose. The O^T accumulator then leaves lane l with column c, dims
+// 32g..32g+31.
+//
+// The running max is updated lazily: a block's weights are taken against the
+// current max unless some score exceeds it by more than kRescaleSlack
+// (base-2 units), so most blocks skip the cross-lane max and the rescale of
+// the accumulators; weights stay below 2^kRescaleSlack, far from overflow.
 // ============================================================================
+constexpr float kRescaleSlack = 8.0f;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+
 template <int DT>
 __device__ __forceinline__ f32x4 mfma_qk(const uint4& a, const uint4& b, f32x4 c) {
   if constexpr (DT == KV_BF16)
@@ -419,50 +501,83 @@ __device__ __forceinline__ f32x4 mfma_pv(const uint2& a, const uint2& b, f32x4 c
                                                  __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
-// Split an fp32 weight into a 16-bit high part and a 16-bit residual.
+// Two fp32 values rounded (to nearest even) into one packed 16-bit pair, and
+// the two rounded values back as fp32.
 template <int DT>
-__device__ __forceinline__ void split_weight(float x, uint32_t& hi, uint32_t& lo) {
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (DT == KV_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+template <int DT>
+__device__ __forceinline__ void unpack2(uint32_t w, float& a, float& b) {
   if constexpr (DT == KV_BF16) {
-    const uint32_t xb = __float_as_uint(x);
-    hi = xb >> 16;  // truncation; the residual below is exact in fp32
-    const float rem = x - __uint_as_float(xb & 0xffff0000u);
-    const uint32_t rb = __float_as_uint(rem);
-    lo = (rb + 0x7fffu + ((rb >> 16) & 1u)) >> 16;  // round to nearest even
+    a = bf16lo(w);
+    b = bf16hi(w);
   } else {
-    const _Float16 h = (_Float16)x;
-    const _Float16 r = (_Float16)(x - (float)h);
-    hi = __builtin_bit_cast(unsigned short, h);
-    lo = __builtin_bit_cast(unsigned short, r);
+    a = f16lo(w);
+    b = f16hi(w);
   }
 }
 
-// 16-bit element n (0..7) of four 16-byte chunks, packed as the MFMA operand
-// (element of chunk 0 in the low half of the first dword).
-__device__ __forceinline__ uint2 gather_col(const uint4* v, int n) {
+// Weights of 4 tokens as a B operand: the 16-bit high parts when
+// residual == 0, the 16-bit residuals x - high(x) when residual == 1.
+template <int DT>
+__device__ __forceinline__ uint2 weight_part(const float* x, float residual) {
+  uint32_t o[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t h = pack2<DT>(x[2 * i], x[2 * i + 1]);
+    float h0, h1;
+    unpack2<DT>(h, h0, h1);
+    o[i] = pack2<DT>(fmaf(-residual, h0, x[2 * i]), fmaf(-residual, h1, x[2 * i + 1]));
+  }
+  return make_uint2(o[0], o[1]);
+}
+
+// 16-bit element n (0..7) of the four V rows a lane holds, packed as an A
+// operand (row of token 4g in the low half of the first dword).
+__device__ __forceinline__ uint2 v_column(const uint4* v, int n) {
   auto word = [](const uint4& u, int k) -> uint32_t {
     return k == 0 ? u.x : (k == 1 ? u.y : (k == 2 ? u.z : u.w));
   };
-  const uint32_t w0 = word(v[0], n >> 1), w1 = word(v[1], n >> 1);
-  const uint32_t w2 = word(v[2], n >> 1), w3 = word(v[3], n >> 1);
-  uint2 r;
-  if (n & 1) {
-    r.x = (w0 >> 16) | (w1 & 0xffff0000u);
-    r.y = (w2 >> 16) | (w3 & 0xffff0000u);
-  } else {
-    r.x = (w0 & 0xffffu) | (w1 << 16);
-    r.y = (w2 & 0xffffu) | (w3 << 16);
-  }
-  return r;
+  const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
+  const int k = n >> 1;
+  return make_uint2(__builtin_amdgcn_perm(word(v[1], k), word(v[0], k), sel),
+                    __builtin_amdgcn_perm(word(v[3], k), word(v[2], k), sel));
 }
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+// Maximum and sum over the four lanes of an MFMA column (lanes l, l^16,
+// l^32, l^48), with the gfx950 row-swap instructions: permlane16_swap of x
+// with itself yields the values of rows (0,0,2,2) and (1,1,3,3), so
+// combining the two results reduces over row pairs; permlane32_swap does the
+// same for the two halves. The combination is symmetric, so every lane gets
+// the same value in the same order.
+__device__ __forceinline__ float column_max(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  u = __float_as_uint(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+  auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float column_sum(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  u = __float_as_uint(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+  auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+template <int DT, bool SPLITCOL, int RING>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_mfma_kernel(DecodeParams p) {
   constexpr int D = 128;
   constexpr size_t kTileBytes = (size_t)kBlock * D * 2;  // 4 KB
-  const int lane = threadIdx.x & 63;
-  const int u = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x;
+  const int u = blockIdx.x;
   if (u >= p.n_units) return;
-  const int col = lane & 15;  // MFMA column: query head of the group / token row
+  const int col = lane & 15;  // MFMA column / token row of a K tile
   const int grp = lane >> 4;  // k-slot group
   const WorkItem w = unit_item(p, u);
   if (!w.ok) return;
@@ -472,22 +587,26 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const int t0 = w.part * p.part_tokens;
   const int t1 = min(ctx, t0 + p.part_tokens);
   const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
+  const int last = nblk - 1;
   const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + t0 / kBlock;
   bool bad = false;
+  const int staged = stage_entries(p, row, nblk, lane, bad);
 
-  // B operand of the score MFMA: Q^T, lane holds head `col`, dims 32kc+8grp..+8
+  // B operand of the score MFMA: Q^T, lane holds head `hd`, dims 32kc+8grp..+8
+  const int hd = SPLITCOL ? (col & 7) : col;
+  const bool live_head = hd < p.G;
   uint4 qb[4];
   {
-    const bool live = col < p.G;
     const uint4* qp = reinterpret_cast<const uint4*>(
         static_cast<const char*>(p.q) +
-        (((size_t)w.s * p.Hq + (size_t)w.h * p.G + (live ? col : 0)) * D) * 2);
+        (((size_t)w.s * p.Hq + (size_t)w.h * p.G + (live_head ? hd : 0)) * D) * 2);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const uint4 v = qp[kc * 4 + grp];
-      qb[kc] = live ? v : make_uint4(0, 0, 0, 0);
+      qb[kc] = live_head ? v : make_uint4(0, 0, 0, 0);
     }
   }
+  const bool residual_lane = SPLITCOL && col >= 8;
 
   f32x4 o[8];
 #pragma unroll
@@ -497,8 +616,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const char* kbase = static_cast<const char*>(p.k_pool);
   const char* vbase = static_cast<const char*>(p.v_pool);
 
-  auto load = [&](int e, uint4* ku, uint4* vu) {
-    const size_t tile = ((size_t)e * p.Hkv + w.h) * kTileBytes;
+  auto load = [&](int j, uint4* ku, uint4* vu) {
+    const size_t tile = ((size_t)entry_of(staged, j) * p.Hkv + w.h) * kTileBytes;
     const uint4* kt = reinterpret_cast<const uint4*>(kbase + tile);
     const uint4* vt = reinterpret_cast<const uint4*>(vbase + tile);
 #pragma unroll
@@ -511,145 +630,135 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) st = mfma_qk<DT>(ku[kc], qb[kc], st);
-
-    const int valid = t1 - (t0 + jb * kBlock);
-    float sc[4];
+    float x[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = st[r] * p.scale_log2;
+    for (int r = 0; r < 4; ++r) x[r] = st[r] * p.scale_log2;
+    const int valid = t1 - (t0 + jb * kBlock);  // live tokens of the block (>= 1)
     if (valid < kBlock) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (4 * grp + r >= valid) {
-          sc[r] = neg_inf();
+          x[r] = neg_inf();
           vu[r] = make_uint4(0, 0, 0, 0);  // masked rows may hold NaN
         }
     }
-    float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float mn = fmaxf(m, mb);  // finite: every block has a live token
-    const float alpha = fast_exp2(m - mn);
-    m = mn;
-    l *= alpha;
+    const float lm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__builtin_amdgcn_ballot_w64(lm > m + kRescaleSlack) != 0) {
+      const float mn = fmaxf(m, column_max(lm));
+      const float alpha = fast_exp2(m - mn);  // 0 while m is -inf
+      l *= alpha;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) o[n] *= alpha;
-
-    uint32_t hi[4], lo[4];
+      for (int n = 0; n < 8; ++n) o[n] *= alpha;
+      m = mn;
+    }
+    float pw[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float pr = fast_exp2(sc[r] - mn);
-      l += pr;
-      split_weight<DT>(pr, hi[r], lo[r]);
+      pw[r] = fast_exp2(x[r] - m);  // 0 for masked tokens
+      l += pw[r];
     }
-    const uint2 phi = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-    const uint2 plo = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+    if constexpr (SPLITCOL) {
+      const uint2 ph = weight_part<DT>(pw, 0.0f);
+      const uint2 pl = weight_part<DT>(pw, 1.0f);
+      const uint2 pb = residual_lane ? pl : ph;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const uint2 a = gather_col(vu, n);
-      o[n] = mfma_pv<DT>(a, phi, o[n]);
-      o[n] = mfma_pv<DT>(a, plo, o[n]);
+      for (int n = 0; n < 8; ++n) o[n] = mfma_pv<DT>(v_column(vu, n), pb, o[n]);
+    } else {
+      const uint2 ph = weight_part<DT>(pw, 0.0f);
+      const uint2 pl = weight_part<DT>(pw, 1.0f);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const uint2 a = v_column(vu, n);
+        o[n] = mfma_pv<DT>(a, ph, o[n]);
+        o[n] = mfma_pv<DT>(a, pl, o[n]);
+      }
     }
   };
 
-  // Two register sets alternate so the next block's loads are in flight
-  // while the current block is computed. The steady-state loop issues its
-  // loads unconditionally (a load under a branch would force a wait for every
-  // outstanding load at the join); the last one or two blocks are peeled.
+  // Ring of RING blocks: while one block is computed the next RING-1 are in
+  // flight. The prologue and the steady-state loop issue their loads
+  // unconditionally (a load under a branch makes the compiler wait for every
+  // outstanding load at the join); the last blocks are drained with guarded
+  // refills.
   {
-    uint4 ka[4], va[4], kb[4], vb[4];
-    const int last = nblk - 1;
-    int eb = block_id(p, row, min(1, last), bad);
-    load(block_id(p, row, 0, bad), ka, va);
-    int jb = 0;
-    for (; jb + 2 < nblk; jb += 2) {
-      const int ea2 = block_id(p, row, jb + 2, bad);
-      load(eb, kb, vb);
-      compute(jb, ka, va);
-      eb = block_id(p, row, min(jb + 3, last), bad);
-      load(ea2, ka, va);
-      compute(jb + 1, kb, vb);
+    uint4 kr[RING][4], vr[RING][4];
+#pragma unroll
+    for (int s = 0; s < RING; ++s) load(min(s, last), kr[s], vr[s]);
+    int j = 0;
+    for (; j + 2 * RING <= nblk; j += RING) {
+#pragma unroll
+      for (int s = 0; s < RING; ++s) {
+        compute(j + s, kr[s], vr[s]);
+        load(j + s + RING, kr[s], vr[s]);
+      }
     }
-    if (jb + 1 < nblk) {
-      load(eb, kb, vb);
-      compute(jb, ka, va);
-      compute(jb + 1, kb, vb);
-    } else {
-      compute(jb, ka, va);
+#pragma unroll
+    for (int s = 0; s < RING; ++s) {
+      if (j + s < nblk) compute(j + s, kr[s], vr[s]);
+      if (j + s + RING < nblk) load(j + s + RING, kr[s], vr[s]);
     }
+#pragma unroll
+    for (int s = 0; s < RING; ++s)
+      if (j + RING + s < nblk) compute(j + RING + s, kr[s], vr[s]);
   }
 
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (col < p.G) {
-    // lane holds head `col`, dims 32*grp + 8*r + n for r < 4, n < 8
-    float res[32];
+  l = column_sum(l);
+  if constexpr (SPLITCOL) {
+    // column c < 8 adds the residual half held by column c + 8
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[n][r] += dpp<0x128>(o[n][r]);  // row_ror:8
+  }
+  // Stage the group's G x D results in LDS and write them back as contiguous
+  // 1 KB spans: in the accumulator layout neighbouring lanes hold different
+  // heads, 512 bytes apart in memory.
+  __shared__ float stage[16 * kStageStride];
+  const bool writer = SPLITCOL ? (col < 8 && live_head) : live_head;
+  if (writer) {
+    // lane holds head hd, dims 32*grp + 8*r + n for r < 4, n < 8
+    const float inv = nps == 1 ? 1.0f / l : 1.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int n = 0; n < 8; ++n) res[8 * r + n] = o[n][r];
-    store_result(p, w, nps, w.h * p.G + col, 32 * grp, res, 32, m, l, grp == 0, bad, D);
+      for (int hh = 0; hh < 2; ++hh)
+        *reinterpret_cast<float4*>(&stage[hd * kStageStride + 32 * grp + 8 * r + 4 * hh]) =
+            make_float4(o[4 * hh][r] * inv, o[4 * hh + 1][r] * inv, o[4 * hh + 2][r] * inv,
+                        o[4 * hh + 3][r] * inv);
   }
-}
-
-// ============================================================================
-// Split-K merge ([2], "The Custom CUDA Kernel": partial outputs and softmax
-// denominators computed per piece, then merged with a numerically stable
-// rule). One workgroup per (sequence, query head) whose sequence has more
-// than one partition; thread d merges dimension d in partition order:
-//   M = max_k m_k,  L = sum_k l_k 2^(m_k - M),  out = sum_k 2^(m_k - M) o_k / L.
-// A NaN denominator (invalid table entry) makes the output NaN. All partial
-// (max, sum) pairs of the sequence are read by independent loads before use.
-// ============================================================================
-template <int D>
-__global__ __launch_bounds__(D) void splitk_merge_kernel(float* __restrict__ out,
-                                                         const float* __restrict__ ws_o,
-                                                         const float* __restrict__ ws_ml,
-                                                         const int32_t* __restrict__ lens,
-                                                         int32_t Hq, int32_t nparts,
-                                                         int32_t part_tokens,
-                                                         int32_t max_blocks) {
-  const int hq = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-  const int ctx = lens[s];
-  if (ctx <= 0 || (int64_t)ctx > (int64_t)max_blocks * kBlock ||
-      (int64_t)ctx > (int64_t)nparts * part_tokens)
-    return;  // written by the decode kernel
-  const int nps = (ctx + part_tokens - 1) / part_tokens;
-  if (nps <= 1) return;
-  const size_t base = ((size_t)s * Hq + hq) * nparts;
-  const float2* ml = reinterpret_cast<const float2*>(ws_ml) + base;
-  float M = neg_inf();
-  bool bad = false;
-  for (int k = 0; k < nps; ++k) {
-    const float2 v = ml[k];
-    bad |= (v.y != v.y);
-    M = fmaxf(M, v.x);
+  __syncthreads();
+  const size_t pg = partial_group(p, w);
+  float* dst = nps == 1 ? p.out + ((size_t)w.s * p.Hq + (size_t)w.h * p.G) * D
+                        : p.ws_o + pg * p.G * D;
+  const float nan = __builtin_nanf("");
+  for (int c = lane; c < p.G * (D / 4); c += 64) {
+    float4 v = *reinterpret_cast<const float4*>(&stage[(c >> 5) * kStageStride + 4 * (c & 31)]);
+    if (bad && nps == 1) v = make_float4(nan, nan, nan, nan);
+    *reinterpret_cast<float4*>(dst + (size_t)c * 4) = v;
   }
-  float L = 0.f, O = 0.f;
-  for (int k = 0; k < nps; ++k) {
-    const float2 v = ml[k];
-    const float f = fast_exp2(v.x - M);
-    L += v.y * f;
-    O += ws_o[(base + k) * D + d] * f;
-  }
-  out[((size_t)s * Hq + hq) * D + d] = bad ? __builtin_nanf("") : O / L;
+  if (nps > 1 && writer && grp == 0)
+    *reinterpret_cast<float2*>(p.ws_ml + (pg * p.G + hd) * 2) =
+        bad ? make_float2(nan, nan) : make_float2(m, l);
 }
 
 // ============================================================================
 // Slot mapping ([4], "How it works"): slot = table[p / B] * B + p % B.
+// Entries that cannot be mapped give -1.
 // ============================================================================
+__device__ __forceinline__ int64_t slot_of(const int32_t* __restrict__ tables, int32_t num_rows,
+                                           int32_t max_blocks, int32_t s, int32_t pos, int32_t B) {
+  if (s < 0 || s >= num_rows || pos < 0 || pos / B >= max_blocks) return -1;
+  const int32_t e = tables[(size_t)s * max_blocks + pos / B];
+  return e >= 0 ? (int64_t)e * B + pos % B : -1;
+}
+
 __global__ void slot_mapping_kernel(const int32_t* __restrict__ tables, int32_t num_rows,
                                     int32_t max_blocks, const int32_t* __restrict__ seq_idx,
                                     const int32_t* __restrict__ pos, int32_t n, int32_t B,
                                     int64_t* __restrict__ slots) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  const int32_t s = seq_idx[i], p = pos[i];
-  int64_t out = -1;
-  if (s >= 0 && s < num_rows && p >= 0 && p / B < max_blocks) {
-    const int32_t e = tables[(size_t)s * max_blocks + p / B];
-    if (e >= 0) out = (int64_t)e * B + p % B;
-  }
-  slots[i] = out;
+  slots[i] = slot_of(tables, num_rows, max_blocks, seq_idx[i], pos[i], B);
 }
 
 // ============================================================================
@@ -658,6 +767,21 @@ __global__ void slot_mapping_kernel(const int32_t* __restrict__ tables, int32_t 
 // and 16 bytes of V; consecutive threads cover consecutive bytes of a token,
 // so reads and writes are coalesced per head row.
 // ============================================================================
+__device__ __forceinline__ void copy_token_chunk(const uint4* __restrict__ k_new,
+                                                 const uint4* __restrict__ v_new,
+                                                 uint4* __restrict__ k_pool,
+                                                 uint4* __restrict__ v_pool, int64_t i,
+                                                 int64_t c, int64_t slot, int64_t num_slots,
+                                                 int32_t Hkv, int32_t row_u4, int32_t B) {
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t h = c / row_u4, cc = c % row_u4;
+  const int64_t blk = slot / B, off = slot % B;
+  const int64_t dst = ((blk * Hkv + h) * B + off) * row_u4 + cc;
+  const int64_t src = i * Hkv * row_u4 + c;
+  k_pool[dst] = k_new[src];
+  v_pool[dst] = v_new[src];
+}
+
 __global__ void reshape_and_cache_kernel(const uint4* __restrict__ k_new,
                                          const uint4* __restrict__ v_new,
                                          uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
@@ -668,14 +792,25 @@ __global__ void reshape_and_cache_kernel(const uint4* __restrict__ k_new,
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= (int64_t)n * per_token) return;
   const int64_t i = t / per_token;
-  const int64_t c = t % per_token;
-  const int64_t h = c / row_u4, cc = c % row_u4;
-  const int64_t slot = slots[i];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot / B, off = slot % B;
-  const int64_t dst = ((blk * Hkv + h) * B + off) * row_u4 + cc;
-  k_pool[dst] = k_new[t];
-  v_pool[dst] = v_new[t];
+  copy_token_chunk(k_new, v_new, k_pool, v_pool, i, t % per_token, slots[i], num_slots, Hkv,
+                   row_u4, B);
+}
+
+// Slot mapping and cache write in one launch: workgroup i handles new token
+// i, computes its slot (thread 0 also records it) and copies its K/V rows.
+__global__ void append_tokens_kernel(const int32_t* __restrict__ tables, int32_t num_rows,
+                                     int32_t max_blocks, const int32_t* __restrict__ seq_idx,
+                                     const int32_t* __restrict__ pos, int32_t B,
+                                     int64_t* __restrict__ slots, const uint4* __restrict__ k_new,
+                                     const uint4* __restrict__ v_new, uint4* __restrict__ k_pool,
+                                     uint4* __restrict__ v_pool, int64_t num_slots, int32_t Hkv,
+                                     int32_t row_u4) {
+  const int64_t i = blockIdx.x;
+  const int64_t slot = slot_of(tables, num_rows, max_blocks, seq_idx[i], pos[i], B);
+  if (threadIdx.x == 0) slots[i] = slot;
+  const int64_t per_token = (int64_t)Hkv * row_u4;
+  for (int64_t c = threadIdx.x; c < per_token; c += blockDim.x)
+    copy_token_chunk(k_new, v_new, k_pool, v_pool, i, c, slot, num_slots, Hkv, row_u4, B);
 }
 
 // ============================================================================
@@ -712,11 +847,10 @@ int32_t effective_partition(int32_t partition_size) {
   return partition_size == 0 ? kDefaultPartition : partition_size;
 }
 
-// One wave per work unit, four waves per workgroup.
+// One wave64 workgroup per work unit.
 template <typename Kernel>
 kv_status launch_decode(Kernel kernel, const DecodeParams& prm, hipStream_t st) {
-  const int64_t grid = ((int64_t)prm.n_units + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, prm);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)prm.n_units), dim3(64), 0, st, prm);
   return launch_status("kv_paged_attention_decode");
 }
 
@@ -730,6 +864,23 @@ kv_status launch_valu(const DecodeParams& prm, int gmax, hipStream_t st) {
     case 16: return launch_decode(decode_valu_kernel<DT, D, 16>, prm, st);
     default: return fail(KV_ERR_UNSUPPORTED, "decode: group size");
   }
+}
+
+kv_status check_cache_write(const char* who, const void* k_new, const void* v_new,
+                            const void* k_pool, const void* v_pool, int32_t n, int32_t num_blocks,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            kv_dtype dtype) {
+  const size_t eb = pagedkv::dtype_bytes(dtype);
+  if (eb == 0) return fail(KV_ERR_UNSUPPORTED, "%s: unknown dtype", who);
+  if (n < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+    return fail(KV_ERR_INVALID, "%s: bad sizes", who);
+  if ((head_dim * eb) % 16 != 0)
+    return fail(KV_ERR_UNSUPPORTED, "%s: head_dim*elem must be a multiple of 16 bytes", who);
+  if (n == 0) return KV_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool) return fail(KV_ERR_INVALID, "%s: null pointer", who);
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(KV_ERR_INVALID, "%s: pointers must be 16-byte aligned", who);
+  return KV_OK;
 }
 
 }  // namespace
@@ -755,18 +906,11 @@ kv_status kv_reshape_and_cache(const void* k_new, const void* v_new, void* k_poo
                                int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                                int32_t block_size, kv_dtype dtype, hipStream_t stream) {
   pagedkv::clear_error();
-  const size_t eb = pagedkv::dtype_bytes(dtype);
-  if (eb == 0) return fail(KV_ERR_UNSUPPORTED, "kv_reshape_and_cache: unknown dtype");
-  if (n < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
-    return fail(KV_ERR_INVALID, "kv_reshape_and_cache: bad sizes");
-  if ((head_dim * eb) % 16 != 0)
-    return fail(KV_ERR_UNSUPPORTED, "kv_reshape_and_cache: head_dim*elem must be a multiple of 16 bytes");
-  if (n == 0) return KV_OK;
-  if (!k_new || !v_new || !k_pool || !v_pool || !slots)
-    return fail(KV_ERR_INVALID, "kv_reshape_and_cache: null pointer");
-  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
-    return fail(KV_ERR_INVALID, "kv_reshape_and_cache: pointers must be 16-byte aligned");
-  const int32_t row_u4 = (int32_t)(head_dim * eb / 16);
+  kv_status st = check_cache_write("kv_reshape_and_cache", k_new, v_new, k_pool, v_pool, n,
+                                   num_blocks, num_kv_heads, head_dim, block_size, dtype);
+  if (st != KV_OK || n == 0) return st;
+  if (!slots) return fail(KV_ERR_INVALID, "kv_reshape_and_cache: null pointer");
+  const int32_t row_u4 = (int32_t)(head_dim * pagedkv::dtype_bytes(dtype) / 16);
   const int64_t total = (int64_t)n * num_kv_heads * row_u4;
   const int64_t blocks = ceil_div64(total, 256);
   if (blocks > INT32_MAX) return fail(KV_ERR_INVALID, "kv_reshape_and_cache: too many tokens");
@@ -775,6 +919,29 @@ kv_status kv_reshape_and_cache(const void* k_new, const void* v_new, void* k_poo
                      static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), slots, n,
                      (int64_t)num_blocks * block_size, num_kv_heads, row_u4, block_size);
   return launch_status("kv_reshape_and_cache");
+}
+
+kv_status kv_append_tokens(const int32_t* tables, int32_t num_rows, int32_t max_blocks,
+                           const int32_t* seq_idx, const int32_t* pos, int32_t n,
+                           const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                           int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, kv_dtype dtype, int64_t* slots,
+                           hipStream_t stream) {
+  pagedkv::clear_error();
+  if (num_rows < 0 || max_blocks < 0)
+    return fail(KV_ERR_INVALID, "kv_append_tokens: negative size");
+  kv_status st = check_cache_write("kv_append_tokens", k_new, v_new, k_pool, v_pool, n,
+                                   num_blocks, num_kv_heads, head_dim, block_size, dtype);
+  if (st != KV_OK || n == 0) return st;
+  if (!tables || !seq_idx || !pos || !slots)
+    return fail(KV_ERR_INVALID, "kv_append_tokens: null pointer");
+  const int32_t row_u4 = (int32_t)(head_dim * pagedkv::dtype_bytes(dtype) / 16);
+  hipLaunchKernelGGL(append_tokens_kernel, dim3((unsigned)n), dim3(64), 0, stream, tables,
+                     num_rows, max_blocks, seq_idx, pos, block_size, slots,
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                     static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool),
+                     (int64_t)num_blocks * block_size, num_kv_heads, row_u4);
+  return launch_status("kv_append_tokens");
 }
 
 kv_status kv_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,
@@ -889,8 +1056,13 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
   kv_status st;
   const bool mfma = (dtype == KV_F16 || dtype == KV_BF16) && head_dim == 128 && G >= 2;
   if (mfma) {
-    st = dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16>, prm, stream)
-                          : launch_decode(decode_mfma_kernel<KV_F16>, prm, stream);
+    constexpr int R = kDecodeRing;
+    if (G <= 8)
+      st = dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16, true, R>, prm, stream)
+                            : launch_decode(decode_mfma_kernel<KV_F16, true, R>, prm, stream);
+    else
+      st = dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16, false, R>, prm, stream)
+                            : launch_decode(decode_mfma_kernel<KV_F16, false, R>, prm, stream);
   } else {
     const int gmax = G == 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
     if (dtype == KV_F32)
@@ -904,13 +1076,11 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
                           : launch_valu<KV_BF16, 128>(prm, 1, stream);
   }
   if (st != KV_OK || nparts <= 1) return st;
-  const dim3 rgrid((unsigned)num_q_heads, (unsigned)S);
+  const dim3 mgrid((unsigned)((int64_t)S * num_kv_heads));
   if (head_dim == 128)
-    hipLaunchKernelGGL(splitk_merge_kernel<128>, rgrid, dim3(128), 0, stream, out, prm.ws_o,
-                       prm.ws_ml, context_lens, num_q_heads, prm.nparts, P, max_blocks);
+    hipLaunchKernelGGL(splitk_merge_kernel<128>, mgrid, dim3(kMergeThreads), 0, stream, prm);
   else
-    hipLaunchKernelGGL(splitk_merge_kernel<64>, rgrid, dim3(64), 0, stream, out, prm.ws_o,
-                       prm.ws_ml, context_lens, num_q_heads, prm.nparts, P, max_blocks);
+    hipLaunchKernelGGL(splitk_merge_kernel<64>, mgrid, dim3(kMergeThreads), 0, stream, prm);
   return launch_status("kv_paged_attention_decode (split-K merge)");
 }
 

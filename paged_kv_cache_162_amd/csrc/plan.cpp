@@ -24,7 +24,7 @@ extern "C" kv_status kv_paged_attention_plan(const int32_t* context_lens_host, i
   const int32_t P = partition_size == 0 ? 512 : partition_size;
   if (!n_items || S < 0 || (S > 0 && !context_lens_host))
     return fail(KV_ERR_INVALID, "kv_paged_attention_plan: null argument or negative S");
-  if (P < 16 || P > 8192 || P % 16 != 0)
+  if (P < 16 || P > 1024 || P % 16 != 0)
     return fail(KV_ERR_INVALID, "kv_paged_attention_plan: partition_size %d", partition_size);
   struct Item {
     int32_t s, p, len;

@@ -119,16 +119,17 @@ class DecodeSession:
 
     def step(self, q, k_new, v_new, out, scale: float, k_pool=None, v_pool=None,
              decode_events=None) -> None:
-        """Device half of a decode step, all on the current stream: slot
-        mapping, copy-on-write copies, cache write, decode attention.
+        """Device half of a decode step, all on the current stream:
+        copy-on-write copies, slot mapping + cache write (one launch), decode
+        attention (one launch).
         `decode_events` = (start, end) torch events recorded around the
         decode-attention call."""
         kp = self.k_pool if k_pool is None else k_pool
         vp_ = self.v_pool if v_pool is None else v_pool
-        kv.kv_slot_mapping(self.d_tables, self.d_seq_idx, self.d_pos, self.d_slots, self.B)
         if self.d_pairs.shape[0]:
             kv.kv_copy_blocks([kp], [vp_], self.d_pairs, self.NB, self.block_bytes)
-        kv.kv_reshape_and_cache(k_new, v_new, kp, vp_, self.d_slots)
+        kv.kv_append_tokens(self.d_tables, self.d_seq_idx, self.d_pos, k_new, v_new, kp, vp_,
+                            self.d_slots)
         if decode_events is not None:
             decode_events[0].record()
         kv.kv_paged_attention_decode(out, q, kp, vp_, self.d_tables, self.d_lens, scale,

@@ -85,19 +85,28 @@ def test_device_entry_points_validate_on_the_host(kv):
     assert call(Hq=7) == kv.KV_ERR_UNSUPPORTED
     assert call(Hq=64, Hkv=2) == kv.KV_ERR_UNSUPPORTED
     assert call(P=24) == kv.KV_ERR_INVALID
+    assert call(P=2048) == kv.KV_ERR_INVALID   # partitions hold at most 64 blocks
     assert call(dt=7) == kv.KV_ERR_UNSUPPORTED
     assert call() == kv.KV_ERR_INVALID          # null pointers
     assert call(S=0) == kv.KV_OK                # nothing to do
     assert lib.kv_reshape_and_cache(None, None, None, None, None, 1, 4, 2, 60, 16, kv.KV_F16, None) \
         == kv.KV_ERR_UNSUPPORTED                # 60*2 bytes is not a multiple of 16
     assert lib.kv_slot_mapping(None, 1, 1, None, None, 0, 16, None, None) == kv.KV_OK
+    assert lib.kv_append_tokens(None, 1, 1, None, None, 0, None, None, None, None, 4, 2, 64, 16,
+                                kv.KV_F16, None, None) == kv.KV_OK
+    assert lib.kv_append_tokens(None, 1, 1, None, None, 3, None, None, None, None, 4, 2, 64, 16,
+                                kv.KV_F16, None, None) == kv.KV_ERR_INVALID
+    assert lib.kv_append_tokens(None, 1, 1, None, None, 3, None, None, None, None, 4, 2, 64, 16,
+                                9, None, None) == kv.KV_ERR_UNSUPPORTED
     assert lib.kv_copy_blocks(None, None, 1, None, 1, 8, 24, None) == kv.KV_ERR_INVALID
 
 
 def test_workspace_size_formula(kv):
     assert kv.kv_paged_attention_workspace_bytes(8, 32, 8, 128, 512, 0) == 0
+    # fp32 partials: outputs [S][Hkv][parts][G][D], then (max, sum) [S][Hkv][parts][G][2]
     assert kv.kv_paged_attention_workspace_bytes(8, 32, 8, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
     assert kv.kv_paged_attention_workspace_bytes(4, 4, 2, 64, 40, 16) == 4 * 4 * 3 * 66 * 4
+    assert kv.kv_paged_attention_workspace_bytes(128, 64, 8, 128, 5000, 512) == 128 * 64 * 10 * 130 * 4
 
 
 # ---------------------------------------------------------------------------
@@ -261,3 +270,5 @@ def test_work_plan_lists_every_partition_longest_first(kv):
     assert sizes == sorted(sizes, reverse=True)
     with pytest.raises(kv.KVError):
         kv.kv_paged_attention_plan(lens, 24)
+    with pytest.raises(kv.KVError):
+        kv.kv_paged_attention_plan(lens, 2048)

@@ -79,6 +79,46 @@ def test_reshape_and_cache_bit_exact(dt, D):
     assert np.array_equal(bits(to_host(dv, dt)), bits(rv))
 
 
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f32", 64), ("f16", 128)])
+def test_append_tokens_bit_exact(dt, D):
+    """Slot mapping + cache write in one launch: slots equal the oracle's slot
+    formula, and the pools equal the oracle's scatter, bit for bit."""
+    kv = kvlib()
+    rng = np.random.default_rng(13)
+    rows, maxb, NB, Hkv = 29, 7, 64, 4
+    store = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16}[dt]
+    view = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dt]
+    nb = np.dtype(store).itemsize
+    # distinct physical blocks per table entry, with some holes (-1)
+    tables = rng.permutation(NB * 8)[: rows * maxb].reshape(rows, maxb).astype(np.int32) % NB
+    tables = np.where(rng.random((rows, maxb)) < 0.1, -1, tables).astype(np.int32)
+    # one token per row at distinct (row, position) pairs so slots never repeat
+    seq = np.arange(rows, dtype=np.int32)
+    pos = rng.integers(0, maxb * 16, size=rows).astype(np.int32)
+    pos[3], seq[4] = -1, rows + 5          # unmappable: slot -1, nothing written
+    ref_slots = np.full(rows, -1, np.int64)
+    okr = (seq >= 0) & (seq < rows)
+    ref_slots[okr] = oa.slot_mapping(tables, seq[okr], pos[okr])
+    live = ref_slots[ref_slots >= 0]
+    assert len(np.unique(live)) == len(live)
+    kp = rng.integers(0, 2 ** (8 * nb), size=(NB, Hkv, 16, D), dtype=np.uint64).astype(store)
+    vp = rng.integers(0, 2 ** (8 * nb), size=(NB, Hkv, 16, D), dtype=np.uint64).astype(store)
+    kn = rng.integers(0, 2 ** (8 * nb), size=(rows, Hkv, D), dtype=np.uint64).astype(store)
+    vn = rng.integers(0, 2 ** (8 * nb), size=(rows, Hkv, D), dtype=np.uint64).astype(store)
+    log(f"[gpu] append_tokens {dt} D={D} n={rows}")
+    dk, dv = to_dev(kp.view(view), dt), to_dev(vp.view(view), dt)
+    d_slots = torch.empty(rows, dtype=torch.int64, device="cuda")
+    kv.kv_append_tokens(torch.from_numpy(tables).cuda(), torch.from_numpy(seq).cuda(),
+                        torch.from_numpy(pos).cuda(), to_dev(kn.view(view), dt),
+                        to_dev(vn.view(view), dt), dk, dv, d_slots)
+    assert np.array_equal(d_slots.cpu().numpy(), ref_slots)
+    ok = ref_slots >= 0
+    rk, rv = kp.copy().view(view), vp.copy().view(view)
+    oa.reshape_and_cache(kn.view(view)[ok], vn.view(view)[ok], rk, rv, ref_slots[ok])
+    assert np.array_equal(bits(to_host(dk, dt)), bits(rk))
+    assert np.array_equal(bits(to_host(dv, dt)), bits(rv))
+
+
 def test_copy_blocks_bit_exact():
     kv = kvlib()
     rng = np.random.default_rng(12)
@@ -215,7 +255,7 @@ def gpu_decode(q, kp, vp, tab, lens, scale, dt, partition_size=0, max_ctx=None, 
     out = torch.full((S, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
     mc = int(lens.max()) if max_ctx is None else max_ctx
     wsb = kv.kv_paged_attention_workspace_bytes(S, Hq, kp.shape[1], D, mc, partition_size)
-    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
+    ws = torch.full((max(wsb, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda") if wsb else None
     items = None
     if plan:
         items = torch.from_numpy(kv.kv_paged_attention_plan(lens, partition_size)).cuda()
@@ -325,7 +365,7 @@ def test_split_and_unsplit_agree_and_runs_are_deterministic():
     q, kp, vp, tab, cl = random_case(rng, lens, G * Hkv, Hkv, D, dt)
     ref = oracle.decode_attention(q, kp, vp, tab, cl, 0.088, dt)
     outs = {}
-    for ps in (256, 512, 8192):
+    for ps in (256, 512, 1024):
         outs[ps] = gpu_decode(q, kp, vp, tab, cl, 0.088, dt, ps)
         check_attention(outs[ps].reshape(-1, D), ref.reshape(-1, D), dt, f"partition {ps}")
     again = gpu_decode(q, kp, vp, tab, cl, 0.088, dt, 512)
