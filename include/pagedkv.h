@@ -288,6 +288,29 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
                                     int32_t n_items, void* workspace, size_t ws_bytes,
                                     hipStream_t stream);
 
+/* One decode step with the cache write fused into the decode launch: for
+ * each sequence s with t = context_lens[s] >= 1, position t-1 holds the
+ * step's new token. Its K and V rows, k_new[s] and v_new[s]
+ * ([S][num_kv_heads][head_dim] of `dtype`, device), are written to slot
+ * block_tables[s][(t-1)/16]*16 + (t-1)%16 ([4], "How it works"; [3], "The
+ * allocation lifecycle": each decode step writes the new token's K,V into
+ * the last block), the slot is stored in slots[s] (device int64 [S]; -1
+ * when t <= 0, the sequence is invalid or a table entry is out of range, in
+ * which case nothing is written), and attention then runs exactly as
+ * kv_paged_attention_decode over positions 0..t-1, the new token included.
+ * On valid inputs, outputs, pools and slots are bit-identical to kv_slot_mapping +
+ * kv_reshape_and_cache + kv_paged_attention_decode on the same inputs. The
+ * block holding position t-1 must belong to s alone (run any copy-on-write
+ * copy first). Other arguments, checks and launches as for
+ * kv_paged_attention_decode; k_new and v_new must be 16-byte aligned. */
+kv_status kv_paged_attention_decode_append(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t S,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
+    int32_t max_context_len, const int32_t* work_items, int32_t n_items, void* workspace,
+    size_t ws_bytes, int64_t* slots, hipStream_t stream);
+
 /* Message describing the calling thread's last error ("" if none). */
 const char* kv_last_error(void);
 

@@ -78,6 +78,9 @@ _SIGS = {
     "kv_paged_attention_decode": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                             i32, f32, C.c_int, i32, i32, vp, i32, vp, C.c_size_t,
                                             vp]),
+    "kv_paged_attention_decode_append": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
+                                                   i32, i32, i32, i32, f32, C.c_int, i32, i32,
+                                                   vp, i32, vp, C.c_size_t, vp, vp]),
     "kv_last_error": (C.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -327,3 +330,32 @@ def kv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens
         None if work_items is None else _dev(work_items, "work_items", torch.int32),
         0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes, _stream(stream)),
         "kv_paged_attention_decode")
+
+
+def kv_paged_attention_decode_append(out, q, k_new, v_new, k_pool, v_pool, block_tables,
+                                     context_lens, scale: float, max_context_len: int, slots,
+                                     workspace=None, partition_size: int = 0, work_items=None,
+                                     stream=None) -> None:
+    """Decode step with the cache write fused in: k_new/v_new [S, Hkv, D] are written at
+    position context_lens[s]-1 of each sequence (slots int64 [S] receives the slots), then
+    attention as kv_paged_attention_decode."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_pool.shape
+    if D2 != D or tuple(out.shape) != (S, Hq, D) or block_tables.shape[0] != S \
+            or context_lens.numel() != S or q.dtype != k_pool.dtype or v_pool.shape != k_pool.shape \
+            or tuple(k_new.shape) != (S, Hkv, D) or k_new.shape != v_new.shape \
+            or k_new.dtype != k_pool.dtype or slots.numel() != S:
+        raise KVError(KV_ERR_INVALID, "kv_paged_attention_decode_append", "shape/dtype mismatch")
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                         workspace.numel() * workspace.element_size())
+    _check(lib.kv_paged_attention_decode_append(
+        _dev(out, "out", torch.float32), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, B, NB, float(scale),
+        dtype_code(q), partition_size, max_context_len,
+        None if work_items is None else _dev(work_items, "work_items", torch.int32),
+        0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
+        _dev(slots, "slots", torch.int64), _stream(stream)),
+        "kv_paged_attention_decode_append")

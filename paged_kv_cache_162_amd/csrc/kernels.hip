@@ -112,6 +112,13 @@ struct DecodeParams {
   const int32_t* items;  // optional work plan: [n_items][2] = (sequence, partition)
   float* ws_o;           // [S][Hkv][nparts][G][D]  partial outputs (unnormalised)
   float* ws_ml;          // [S][Hkv][nparts][G][2]  partial (max, sum) in base-2 units
+  // fused cache write (all NULL for a plain decode): the new token of each
+  // sequence, [S][Hkv][D], is written at its last position; slots [S]
+  const void* k_new;
+  const void* v_new;
+  void* k_pool_w;
+  void* v_pool_w;
+  int64_t* slots;
   int32_t max_blocks, S, Hq, Hkv, G, num_blocks, part_tokens, nparts, n_units;
   float scale_log2;
 };
@@ -159,6 +166,7 @@ __device__ __forceinline__ int unit_prologue(const DecodeParams& p, const WorkIt
       const float v = bad ? __builtin_nanf("") : 0.0f;
       float* dst = p.out + ((size_t)w.s * p.Hq + (size_t)w.h * p.G) * D;
       for (int i = lane; i < p.G * D; i += 64) dst[i] = v;
+      if (p.slots && w.h == 0 && lane == 0) p.slots[w.s] = -1;  // no new token to place
     }
     return 0;
   }
@@ -183,6 +191,28 @@ __device__ __forceinline__ int stage_entries(const DecodeParams& p, const int32_
 
 __device__ __forceinline__ int entry_of(int staged, int j) {
   return __builtin_amdgcn_readlane(staged, j);
+}
+
+// Fused cache write ([3], "The allocation lifecycle": each decode step
+// writes the new token's K,V into the last block). The unit holding the
+// sequence's last position ctx-1 - the last row in use of its last block -
+// owns that token's row for its KV head: it returns the row's slot
+// (table[(ctx-1)/16]*16 + (ctx-1)%16, [4] "How it works"), or -1 when the
+// unit is invalid, and the caller stores the row before loading any block.
+// No other unit reads the row.
+struct NewToken {
+  bool on;        // this unit places the new token
+  int row;        // row of the token in the unit's last block
+  int64_t slot;   // -1 if nothing is written (invalid unit)
+};
+__device__ __forceinline__ NewToken new_token(const DecodeParams& p, const WorkItem& w, int nps,
+                                              int ctx, int staged, int last, bool bad, int lane) {
+  NewToken t;
+  t.on = p.k_new != nullptr && w.part == nps - 1;
+  t.row = (ctx - 1) % kBlock;
+  t.slot = (t.on && !bad) ? (int64_t)entry_of(staged, last) * kBlock + t.row : -1;
+  if (t.on && p.slots && w.h == 0 && lane == 0) p.slots[w.s] = t.slot;
+  return t;
 }
 
 // Start of the unit's partial results: the G heads of (sequence, KV head,
@@ -224,10 +254,11 @@ __device__ __forceinline__ void store_result(const DecodeParams& p, const WorkIt
 //   M = max_k m_k,  L = sum_k l_k 2^(m_k - M),  out = sum_k 2^(m_k - M) o_k / L.
 // One workgroup per (sequence, KV head); sequences with one partition were
 // finished by the decode kernel and return at once. Thread t merges float4
-// chunk t of the group's G x D outputs, in partition order, so for each
-// partition the workgroup reads that partition's G x D partials as one
-// contiguous span and writes the group's outputs as one contiguous span. A
-// NaN partial sum (invalid table entry) makes the output NaN.
+// chunk t of the group's G x D outputs with a running (online) merge in
+// partition order, so for each partition the workgroup reads that
+// partition's G x D partials as one contiguous span and writes the group's
+// outputs as one contiguous span. A NaN partial sum (invalid table entry)
+// makes the output NaN.
 // ============================================================================
 constexpr int kMergeThreads = 256;
 
@@ -245,26 +276,26 @@ __global__ __launch_bounds__(kMergeThreads) void splitk_merge_kernel(DecodeParam
   for (int c = threadIdx.x; c < n_chunks; c += kMergeThreads) {
     const int g = c / (D / 4);
     const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + grp0 * p.G + g;
-    float M = neg_inf();
-    bool bad = false;
-    for (int k = 0; k < nps; ++k) {
-      const float2 v = ml[(size_t)k * p.G];
-      bad |= (v.y != v.y);
-      M = fmaxf(M, v.x);
-    }
-    float L = 0.f;
-    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
     const float* po = p.ws_o + grp0 * p.G * D + (size_t)c * 4;
+    // running merge in partition order; the loads of eight partitions are
+    // independent of the arithmetic and issue together
+    float M = neg_inf(), L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    bool bad = false;
 #pragma unroll 8
     for (int k = 0; k < nps; ++k) {
       const float2 v = ml[(size_t)k * p.G];
-      const float f = fast_exp2(v.x - M);
       const float4 o = *reinterpret_cast<const float4*>(po + (size_t)k * p.G * D);
-      L += v.y * f;
-      O.x += o.x * f;
-      O.y += o.y * f;
-      O.z += o.z * f;
-      O.w += o.w * f;
+      bad |= (v.y != v.y);
+      const float Mn = fmaxf(M, v.x);
+      const float a = fast_exp2(M - Mn);  // 0 while M is -inf
+      const float b = fast_exp2(v.x - Mn);
+      L = L * a + v.y * b;
+      O.x = O.x * a + o.x * b;
+      O.y = O.y * a + o.y * b;
+      O.z = O.z * a + o.z * b;
+      O.w = O.w * a + o.w * b;
+      M = Mn;
     }
     const float inv = 1.0f / L;
     float4 r = make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
@@ -306,6 +337,16 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + t0 / kBlock;
   bool bad = false;
   const int staged = stage_entries(p, row, nblk, lane, bad);
+  const NewToken nt = new_token(p, w, nps, ctx, staged, nblk - 1, bad, lane);
+  if (nt.on && nt.slot >= 0 && r == nt.row % TPI) {
+    // the lanes of row group nt.row % TPI load chunk c of the new token's
+    // rows with the last block; they store those chunks first, so program
+    // order within the lane makes that load return the new values
+    const size_t src = ((size_t)w.s * p.Hkv + w.h) * LPR + c;
+    const size_t dst = (((size_t)(nt.slot / kBlock) * p.Hkv + w.h) * kBlock + nt.row) * LPR + c;
+    static_cast<uint4*>(p.k_pool_w)[dst] = static_cast<const uint4*>(p.k_new)[src];
+    static_cast<uint4*>(p.v_pool_w)[dst] = static_cast<const uint4*>(p.v_new)[src];
+  }
 
   // query chunk of every head in the group, pre-scaled into base-2 logits
   float qf[GMAX][EPL];
@@ -344,7 +385,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     for (int i = 0; i < IPB; ++i) vu[i] = vbase[tile + (size_t)(r + TPI * i) * LPR + c];
   };
 
-  auto compute = [&](int jb, const uint4* ku, const uint4* vu) {
+  auto compute = [&](int jb, const uint4* ku, uint4* vu) {
     const int valid = t1 - (t0 + jb * kBlock);  // live tokens in this block (>= 1)
     const bool full = valid >= kBlock;
     float kf[IPB][EPL], vf[IPB][EPL];
@@ -591,6 +632,23 @@ void decode_mfma_kernel(DecodeParams p) {
   const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + t0 / kBlock;
   bool bad = false;
   const int staged = stage_entries(p, row, nblk, lane, bad);
+  const NewToken nt = new_token(p, w, nps, ctx, staged, last, bad, lane);
+  if (nt.on && nt.slot >= 0) {
+    // Each lane stores exactly the chunks of the new token's rows that it
+    // later loads with the last block (K: the lanes of column nt.row, chunks
+    // kc*4+grp; V: the lanes of row group nt.row/4, chunk col), so program
+    // order within the lane makes that load return the new values.
+    const size_t src = ((size_t)w.s * p.Hkv + w.h) * (D / 8);
+    const size_t dst = (((size_t)(nt.slot / kBlock) * p.Hkv + w.h) * kBlock + nt.row) * (D / 8);
+    if (col == nt.row) {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        static_cast<uint4*>(p.k_pool_w)[dst + kc * 4 + grp] =
+            static_cast<const uint4*>(p.k_new)[src + kc * 4 + grp];
+    }
+    if (grp == nt.row / 4)
+      static_cast<uint4*>(p.v_pool_w)[dst + col] = static_cast<const uint4*>(p.v_new)[src + col];
+  }
 
   // B operand of the score MFMA: Q^T, lane holds head `hd`, dims 32kc+8grp..+8
   const int hd = SPLITCOL ? (col & 7) : col;
@@ -626,7 +684,7 @@ void decode_mfma_kernel(DecodeParams p) {
     for (int jj = 0; jj < 4; ++jj) vu[jj] = vt[(4 * grp + jj) * 16 + col];
   };
 
-  auto compute = [&](int jb, const uint4* ku, uint4* vu) {
+  auto compute = [&](int jb, uint4* ku, uint4* vu) {
     f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) st = mfma_qk<DT>(ku[kc], qb[kc], st);
@@ -985,16 +1043,18 @@ size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_
   return (size_t)S * num_q_heads * nparts * (head_dim + 2) * sizeof(float);
 }
 
-kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_pool,
-                                    const void* v_pool, const int32_t* block_tables,
-                                    int32_t max_blocks, const int32_t* context_lens, int32_t S,
-                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                    int32_t block_size, int32_t num_blocks, float scale,
-                                    kv_dtype dtype, int32_t partition_size,
-                                    int32_t max_context_len, const int32_t* work_items,
-                                    int32_t n_items, void* workspace, size_t ws_bytes,
-                                    hipStream_t stream) {
-  pagedkv::clear_error();
+namespace {
+
+// Shared body of the decode entry points; k_new/v_new/slots are NULL for a
+// plain decode and set for the fused cache write.
+kv_status decode_impl(float* out, const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, int32_t max_blocks,
+                      const int32_t* context_lens, int32_t S, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
+                      int32_t max_context_len, const int32_t* work_items, int32_t n_items,
+                      void* workspace, size_t ws_bytes, const void* k_new, const void* v_new,
+                      int64_t* slots, hipStream_t stream) {
   if (pagedkv::dtype_bytes(dtype) == 0)
     return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: unknown dtype");
   if (S < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks < 0 || num_blocks <= 0 ||
@@ -1052,6 +1112,11 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
   prm.part_tokens = P;
   prm.nparts = (int32_t)nparts;
   prm.scale_log2 = scale * 1.4426950408889634f;
+  prm.k_new = k_new;
+  prm.v_new = v_new;
+  prm.k_pool_w = const_cast<void*>(k_pool);
+  prm.v_pool_w = const_cast<void*>(v_pool);
+  prm.slots = slots;
 
   kv_status st;
   const bool mfma = (dtype == KV_F16 || dtype == KV_BF16) && head_dim == 128 && G >= 2;
@@ -1068,12 +1133,12 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
     if (dtype == KV_F32)
       st = head_dim == 64 ? launch_valu<KV_F32, 64>(prm, gmax, stream)
                           : launch_valu<KV_F32, 128>(prm, gmax, stream);
-    else if (dtype == KV_F16)
+    else if (dtype == KV_F16)  // 16-bit head_dim 128 reaches here only with G == 1
       st = head_dim == 64 ? launch_valu<KV_F16, 64>(prm, gmax, stream)
-                          : launch_valu<KV_F16, 128>(prm, 1, stream);
+                          : launch_decode(decode_valu_kernel<KV_F16, 128, 1>, prm, stream);
     else
       st = head_dim == 64 ? launch_valu<KV_BF16, 64>(prm, gmax, stream)
-                          : launch_valu<KV_BF16, 128>(prm, 1, stream);
+                          : launch_decode(decode_valu_kernel<KV_BF16, 128, 1>, prm, stream);
   }
   if (st != KV_OK || nparts <= 1) return st;
   const dim3 mgrid((unsigned)((int64_t)S * num_kv_heads));
@@ -1082,6 +1147,44 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
   else
     hipLaunchKernelGGL(splitk_merge_kernel<64>, mgrid, dim3(kMergeThreads), 0, stream, prm);
   return launch_status("kv_paged_attention_decode (split-K merge)");
+}
+
+}  // namespace
+
+kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_pool,
+                                    const void* v_pool, const int32_t* block_tables,
+                                    int32_t max_blocks, const int32_t* context_lens, int32_t S,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t num_blocks, float scale,
+                                    kv_dtype dtype, int32_t partition_size,
+                                    int32_t max_context_len, const int32_t* work_items,
+                                    int32_t n_items, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream) {
+  pagedkv::clear_error();
+  return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     partition_size, max_context_len, work_items, n_items, workspace, ws_bytes,
+                     nullptr, nullptr, nullptr, stream);
+}
+
+kv_status kv_paged_attention_decode_append(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t S,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
+    int32_t max_context_len, const int32_t* work_items, int32_t n_items, void* workspace,
+    size_t ws_bytes, int64_t* slots, hipStream_t stream) {
+  pagedkv::clear_error();
+  if (S > 0) {
+    if (!k_new || !v_new || !slots)
+      return fail(KV_ERR_INVALID, "kv_paged_attention_decode_append: null pointer");
+    if (!aligned16(k_new) || !aligned16(v_new))
+      return fail(KV_ERR_INVALID, "kv_paged_attention_decode_append: k_new/v_new must be 16-byte aligned");
+  }
+  return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     partition_size, max_context_len, work_items, n_items, workspace, ws_bytes,
+                     k_new, v_new, slots, stream);
 }
 
 }  // extern "C"

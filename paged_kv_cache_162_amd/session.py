@@ -22,7 +22,7 @@ from . import binding as kv
 
 class DecodeSession:
     def __init__(self, *, k_pool, v_pool, num_q_heads: int, free_order: Optional[Sequence[int]] = None,
-                 partition_size: int = 0, use_plan: bool = True):
+                 partition_size: int = 0, use_plan: bool = True, fused: bool = True):
         import torch
         self.torch = torch
         NB, Hkv, B, D = k_pool.shape
@@ -31,6 +31,7 @@ class DecodeSession:
         self.dtype = kv.dtype_code(k_pool)
         self.partition_size = partition_size
         self.use_plan = use_plan
+        self.fused = fused
         self.pool = kv.kv_pool_create(NB, B, 1, Hkv, D, self.dtype)
         if free_order is not None:
             kv.kv_pool_set_free_order(self.pool, free_order)
@@ -118,22 +119,31 @@ class DecodeSession:
         return host_slots, pairs
 
     def step(self, q, k_new, v_new, out, scale: float, k_pool=None, v_pool=None,
-             decode_events=None) -> None:
+             decode_events=None, fused: Optional[bool] = None) -> None:
         """Device half of a decode step, all on the current stream:
-        copy-on-write copies, slot mapping + cache write (one launch), decode
-        attention (one launch).
-        `decode_events` = (start, end) torch events recorded around the
-        decode-attention call."""
+        copy-on-write copies (if any), then either the fused decode (cache
+        write + attention, one launch plus the split-K merge) or, with
+        fused=False, slot mapping + cache write (one launch) followed by the
+        decode. `decode_events` = (start, end) torch events recorded around
+        the call that runs attention."""
         kp = self.k_pool if k_pool is None else k_pool
         vp_ = self.v_pool if v_pool is None else v_pool
+        fused = self.fused if fused is None else fused
         if self.d_pairs.shape[0]:
             kv.kv_copy_blocks([kp], [vp_], self.d_pairs, self.NB, self.block_bytes)
-        kv.kv_append_tokens(self.d_tables, self.d_seq_idx, self.d_pos, k_new, v_new, kp, vp_,
-                            self.d_slots)
+        if not fused:
+            kv.kv_append_tokens(self.d_tables, self.d_seq_idx, self.d_pos, k_new, v_new, kp, vp_,
+                                self.d_slots)
         if decode_events is not None:
             decode_events[0].record()
-        kv.kv_paged_attention_decode(out, q, kp, vp_, self.d_tables, self.d_lens, scale,
-                                     self.max_context_len, self.workspace, self.partition_size,
-                                     self.d_items)
+        if fused:
+            kv.kv_paged_attention_decode_append(out, q, k_new, v_new, kp, vp_, self.d_tables,
+                                                self.d_lens, scale, self.max_context_len,
+                                                self.d_slots, self.workspace, self.partition_size,
+                                                self.d_items)
+        else:
+            kv.kv_paged_attention_decode(out, q, kp, vp_, self.d_tables, self.d_lens, scale,
+                                         self.max_context_len, self.workspace, self.partition_size,
+                                         self.d_items)
         if decode_events is not None:
             decode_events[1].record()

@@ -92,6 +92,12 @@ def test_device_entry_points_validate_on_the_host(kv):
     assert lib.kv_reshape_and_cache(None, None, None, None, None, 1, 4, 2, 60, 16, kv.KV_F16, None) \
         == kv.KV_ERR_UNSUPPORTED                # 60*2 bytes is not a multiple of 16
     assert lib.kv_slot_mapping(None, 1, 1, None, None, 0, 16, None, None) == kv.KV_OK
+    # fused decode + cache write: needs k_new, v_new and slots; nothing to do for S = 0
+    dec_app = lambda S, kn: lib.kv_paged_attention_decode_append(
+        None, None, kn, kn, None, None, None, 4, None, S, 8, 2, 128, 16, 8, 1.0, kv.KV_BF16, 0, 16,
+        None, 0, None, 0, None, None)
+    assert dec_app(1, None) == kv.KV_ERR_INVALID
+    assert dec_app(0, None) == kv.KV_OK
     assert lib.kv_append_tokens(None, 1, 1, None, None, 0, None, None, None, None, 4, 2, 64, 16,
                                 kv.KV_F16, None, None) == kv.KV_OK
     assert lib.kv_append_tokens(None, 1, 1, None, None, 3, None, None, None, None, 4, 2, 64, 16,

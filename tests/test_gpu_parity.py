@@ -222,6 +222,23 @@ def test_truncated_workloads_full_output():
     run_workload(2, S=3, full_pool_compare=False)
 
 
+@pytest.mark.parametrize("cfg,S", [(1, None), (2, 3), (3, 16), (6, None)])
+def test_fused_and_unfused_steps_are_bitwise_identical(cfg, S):
+    """The decode with the cache write fused in gives the same outputs, pools
+    and slots, bit for bit, as slot mapping + cache write + decode."""
+    case = Case(cfg, S=S)
+    res = {}
+    for fused in (True, False):
+        log(f"[gpu] workload {cfg} fused={fused}")
+        case.device_run(fused=fused)
+        res[fused] = (case.out_dev.cpu().numpy(), to_host(case.k_dev, case.dt),
+                      to_host(case.v_dev, case.dt), case.sess.d_slots.cpu().numpy())
+    a, b = res[True], res[False]
+    assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
+    assert np.array_equal(bits(a[1]), bits(b[1])) and np.array_equal(bits(a[2]), bits(b[2]))
+    assert np.array_equal(a[3], b[3]) and np.array_equal(a[3], case.step_slots)
+
+
 # ---------------------------------------------------------------------------
 # kernel coverage on random ragged shapes (every dtype / head_dim / group)
 # ---------------------------------------------------------------------------
@@ -281,6 +298,53 @@ def test_decode_shapes_against_oracle(dt, D, G):
         log(f"[gpu] decode {dt} D={D} G={G} partition={ps} plan={plan}")
         got = gpu_decode(q, kp, vp, tab, cl, scale, dt, ps, plan=plan)
         check_attention(got.reshape(-1, D), ref.reshape(-1, D), dt, f"{dt}/{D}/{G}/{ps}/{plan}")
+
+
+@pytest.mark.parametrize("dt,D,G", [("bf16", 128, 8), ("f16", 128, 2), ("bf16", 128, 16),
+                                    ("f32", 64, 4), ("f16", 128, 1), ("bf16", 64, 8)])
+def test_decode_append_against_oracle(dt, D, G):
+    """Fused cache write + decode on ragged lengths: slots and pools bit exact
+    against the oracle's slot formula and scatter, attention within tolerance
+    of the oracle run on the scattered pool. The new tokens' slots hold NaN
+    beforehand, so a read of the stale slot would show."""
+    kv = kvlib()
+    rng = np.random.default_rng(2000 + G + D)
+    lens = [1, 15, 16, 17, 33, 100, 511, 512, 513, 700, 0]
+    Hkv = 2
+    q, kp, vp, tab, cl = random_case(rng, lens, G * Hkv, Hkv, D, dt)
+    S = len(lens)
+    kn = round_to_dtype(rng.standard_normal((S, Hkv, D)).astype(np.float32), dt)
+    vn = round_to_dtype(rng.standard_normal((S, Hkv, D)).astype(np.float32), dt)
+    seq = np.arange(S, dtype=np.int32)
+    ok = cl > 0
+    ref_slots = np.full(S, -1, np.int64)
+    ref_slots[ok] = oa.slot_mapping(tab, seq[ok], cl[ok] - 1)
+    for pool in (kp, vp):  # stale content of the new slots
+        b = bits(pool)
+        b[ref_slots[ok] // 16, :, ref_slots[ok] % 16, :] = POISON[dt]
+    rk, rv = kp.copy(), vp.copy()
+    oa.reshape_and_cache(kn[ok], vn[ok], rk, rv, ref_slots[ok])
+    scale = float(np.float32(1 / np.sqrt(D)))
+    ref = oracle.decode_attention(q, rk, rv, tab, cl, scale, dt)
+    for ps, plan in ((0, True), (64, False)):
+        log(f"[gpu] decode_append {dt} D={D} G={G} partition={ps} plan={plan}")
+        dk, dv = to_dev(kp, dt), to_dev(vp, dt)
+        out = torch.full((S, G * Hkv, D), float("nan"), dtype=torch.float32, device="cuda")
+        slots = torch.full((S,), 7, dtype=torch.int64, device="cuda")
+        mc = int(cl.max())
+        wsb = kv.kv_paged_attention_workspace_bytes(S, G * Hkv, Hkv, D, mc, ps)
+        ws = torch.full((max(wsb, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda") if wsb else None
+        items = torch.from_numpy(kv.kv_paged_attention_plan(cl, ps)).cuda() if plan else None
+        kv.kv_paged_attention_decode_append(out, to_dev(q, dt), to_dev(kn, dt), to_dev(vn, dt), dk, dv,
+                                            torch.from_numpy(tab).cuda(), torch.from_numpy(cl).cuda(),
+                                            scale, mc, slots, ws, ps, items)
+        torch.cuda.synchronize()
+        assert np.array_equal(slots.cpu().numpy(), ref_slots)
+        assert np.array_equal(bits(to_host(dk, dt)), bits(rk))
+        assert np.array_equal(bits(to_host(dv, dt)), bits(rv))
+        got = out.cpu().numpy()
+        assert np.all(got[~ok] == 0.0)
+        check_attention(got[ok].reshape(-1, D), ref[ok].reshape(-1, D), dt, f"append {dt}/{D}/{G}/{ps}")
 
 
 def test_plan_and_padded_grid_are_bitwise_identical():
