@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas to rotate (0 = auto)")
     ap.add_argument("--no-plan", action="store_true", help="padded grid instead of the host work plan")
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate slot-mapping/cache-write launch instead of the fused decode step")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each replica's step in a HIP graph and time graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--pmc-traffic", default="",
@@ -211,7 +215,8 @@ def main():
           file=sys.stderr, flush=True)
     kp, vp = to_dev(w.k_pool, dt), to_dev(w.v_pool, dt)
     sess = DecodeSession(k_pool=kp, v_pool=vp, num_q_heads=sp.Hq, free_order=w.free_order,
-                         partition_size=args.partition, use_plan=not args.no_plan)
+                         partition_size=args.partition, use_plan=not args.no_plan,
+                         fused=not args.unfused)
     values = {}
     if w.tail_k is not None:
         values = {s: (to_dev(w.tail_k[s], dt), to_dev(w.tail_v[s], dt)) for s in range(sp.S)}
@@ -234,30 +239,58 @@ def main():
         a, b, qq, kk, vv = reps[k % R]
         sess.step(qq, kk, vv, out, sp.scale, k_pool=a, v_pool=b, decode_events=events)
 
+    graphs = None
+    if args.graph:
+        # one graph per replica; the step holds no memset nodes
+        for k in range(R):
+            one(k)
+        torch.cuda.synchronize()
+        graphs = []
+        cap_stream = torch.cuda.Stream()
+        with torch.cuda.stream(cap_stream):
+            for k in range(R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap_stream):
+                    one(k)
+                graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(k):
+        if graphs is not None:
+            graphs[k % R].replay()
+        else:
+            one(k)
+
     for k in range(args.warmup):
-        one(k)
+        run(k)
     torch.cuda.synchronize()
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # timed region: K whole steps back to back, nothing else on the stream
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for k in range(K):
-        one(k, ev[k])
+        run(k)
     t_end.record()
     torch.cuda.synchronize()
     step_ms = t_start.elapsed_time(t_end) / K
-    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    # per-call duration of the decode launch(es), events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for k in range(K):
+        one(k, ev[k])
+    torch.cuda.synchronize()
+    dec_ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
     dec_avg = float(dec_ms.mean())
 
     # warm number: same buffers every step
     for k in range(10):
-        one(0)
+        run(0)
     torch.cuda.synchronize()
     w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0.record()
     for k in range(K):
-        one(0)
+        run(0)
     w1.record()
     torch.cuda.synchronize()
     warm_ms = w0.elapsed_time(w1) / K
@@ -293,6 +326,7 @@ def main():
             "block_size": 16, "partition_tokens": args.partition or 512,
             "sum_context": int(lens.sum()), "max_context": int(lens.max()),
             "kv_bytes_per_step": kvb, "replicas_rotated": R, "parallelism": "single GPU",
+            "fused_cache_write": not args.unfused, "hip_graph": bool(args.graph),
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(sp.S / (step_ms * 1e-3), 1),
@@ -303,7 +337,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "kv_paged_attention_decode (partition kernel + split-K merge)",
+                     "kernel": ("kv_paged_attention_decode_append call: decode kernel + split-K merge"
+                                if not args.unfused else
+                                "kv_paged_attention_decode call: decode kernel + split-K merge"),
                      "alg_bytes_per_launch": alg},
     }
     if not args.no_cpu_baseline:

@@ -239,6 +239,34 @@ def test_fused_and_unfused_steps_are_bitwise_identical(cfg, S):
     assert np.array_equal(a[3], b[3]) and np.array_equal(a[3], case.step_slots)
 
 
+def test_graph_replay_matches_eager():
+    """The fused step captured in a HIP graph: every replay, with eager work
+    and synchronisations in between, reproduces the eager outputs, pools and
+    slots bit for bit (the captured step holds no memset nodes)."""
+    case = Case(3, S=10)
+    case.device_run()
+    sess, dt = case.sess, case.dt
+    eager = (case.out_dev.cpu().numpy().copy(), to_host(case.k_dev, dt).copy(),
+             case.sess.d_slots.cpu().numpy().copy())
+    out = torch.full_like(case.out_dev, float("nan"))
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            sess.step(case.q_dev, case.kn_dev, case.vn_dev, out, case.sp.scale)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        sess.d_slots.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"[gpu] graph replay {rep}")
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), eager[0].view(np.uint32))
+        assert np.array_equal(bits(to_host(case.k_dev, dt)), bits(eager[1]))
+        assert np.array_equal(sess.d_slots.cpu().numpy(), eager[2])
+
+
 # ---------------------------------------------------------------------------
 # kernel coverage on random ragged shapes (every dtype / head_dim / group)
 # ---------------------------------------------------------------------------
