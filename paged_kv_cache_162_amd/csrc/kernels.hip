@@ -189,6 +189,15 @@ __device__ __forceinline__ int stage_entries(const DecodeParams& p, const int32_
   return e;
 }
 
+// The same check on entries already loaded (lane i holds entry i of the
+// partition, or anything when i >= nblk).
+__device__ __forceinline__ int check_entries(const DecodeParams& p, int e, int nblk, int lane,
+                                             bool& bad) {
+  const bool out_of_pool = lane < nblk && (e < 0 || e >= p.num_blocks);
+  bad = __builtin_amdgcn_ballot_w64(out_of_pool) != 0;
+  return (out_of_pool || lane >= nblk) ? 0 : e;
+}
+
 __device__ __forceinline__ int entry_of(int staged, int j) {
   return __builtin_amdgcn_readlane(staged, j);
 }
@@ -622,34 +631,13 @@ void decode_mfma_kernel(DecodeParams p) {
   const int grp = lane >> 4;  // k-slot group
   const WorkItem w = unit_item(p, u);
   if (!w.ok) return;
+  // The loads that need only the unit go out together: the length, up to
+  // 64 table entries of the partition (bounded by the table width, so the
+  // length is not needed yet) and the queries.
   const int ctx = p.lens[w.s];
-  const int nps = unit_prologue<D>(p, w, ctx, lane);
-  if (nps == 0) return;
-  const int t0 = w.part * p.part_tokens;
-  const int t1 = min(ctx, t0 + p.part_tokens);
-  const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
-  const int last = nblk - 1;
-  const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + t0 / kBlock;
-  bool bad = false;
-  const int staged = stage_entries(p, row, nblk, lane, bad);
-  const NewToken nt = new_token(p, w, nps, ctx, staged, last, bad, lane);
-  if (nt.on && nt.slot >= 0) {
-    // Each lane stores exactly the chunks of the new token's rows that it
-    // later loads with the last block (K: the lanes of column nt.row, chunks
-    // kc*4+grp; V: the lanes of row group nt.row/4, chunk col), so program
-    // order within the lane makes that load return the new values.
-    const size_t src = ((size_t)w.s * p.Hkv + w.h) * (D / 8);
-    const size_t dst = (((size_t)(nt.slot / kBlock) * p.Hkv + w.h) * kBlock + nt.row) * (D / 8);
-    if (col == nt.row) {
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        static_cast<uint4*>(p.k_pool_w)[dst + kc * 4 + grp] =
-            static_cast<const uint4*>(p.k_new)[src + kc * 4 + grp];
-    }
-    if (grp == nt.row / 4)
-      static_cast<uint4*>(p.v_pool_w)[dst + col] = static_cast<const uint4*>(p.v_new)[src + col];
-  }
-
+  const int b0 = w.part * (p.part_tokens / kBlock);
+  int raw_entry = 0;
+  if (lane < p.max_blocks - b0) raw_entry = p.tables[(size_t)w.s * p.max_blocks + b0 + lane];
   // B operand of the score MFMA: Q^T, lane holds head `hd`, dims 32kc+8grp..+8
   const int hd = SPLITCOL ? (col & 7) : col;
   const bool live_head = hd < p.G;
@@ -664,6 +652,43 @@ void decode_mfma_kernel(DecodeParams p) {
       qb[kc] = live_head ? v : make_uint4(0, 0, 0, 0);
     }
   }
+  // With a fused cache write, the new token's K chunks kc*4+grp and V chunk
+  // col are fetched in the same batch (whether or not this unit turns out to
+  // hold the sequence's last position), so storing them costs no extra wait.
+  uint4 kn0 = make_uint4(0, 0, 0, 0), kn1 = kn0, kn2 = kn0, kn3 = kn0, vnew = kn0;
+  if (p.k_new) {
+    const uint4* kn = static_cast<const uint4*>(p.k_new) + ((size_t)w.s * p.Hkv + w.h) * (D / 8);
+    kn0 = kn[grp];
+    kn1 = kn[4 + grp];
+    kn2 = kn[8 + grp];
+    kn3 = kn[12 + grp];
+    vnew = (static_cast<const uint4*>(p.v_new) + ((size_t)w.s * p.Hkv + w.h) * (D / 8))[col];
+  }
+  const int nps = unit_prologue<D>(p, w, ctx, lane);
+  if (nps == 0) return;
+  const int t0 = w.part * p.part_tokens;
+  const int t1 = min(ctx, t0 + p.part_tokens);
+  const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
+  const int last = nblk - 1;
+  bool bad = false;
+  const int staged = check_entries(p, raw_entry, nblk, lane, bad);
+  const NewToken nt = new_token(p, w, nps, ctx, staged, last, bad, lane);
+  if (nt.on && nt.slot >= 0) {
+    // Each lane stores exactly the chunks of the new token's rows that it
+    // later loads with the last block (K: the lanes of column nt.row, chunks
+    // kc*4+grp; V: the lanes of row group nt.row/4, chunk col), so program
+    // order within the lane makes that load return the new values.
+    const size_t dst = (((size_t)(nt.slot / kBlock) * p.Hkv + w.h) * kBlock + nt.row) * (D / 8);
+    if (col == nt.row) {
+      uint4* kd = static_cast<uint4*>(p.k_pool_w) + dst + grp;
+      kd[0] = kn0;
+      kd[4] = kn1;
+      kd[8] = kn2;
+      kd[12] = kn3;
+    }
+    if (grp == nt.row / 4) static_cast<uint4*>(p.v_pool_w)[dst + col] = vnew;
+  }
+
   const bool residual_lane = SPLITCOL && col >= 8;
 
   f32x4 o[8];
