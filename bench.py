@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=3, help="workload number 1-6")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
+    ap.add_argument("--block-size", type=int, default=16, help="tokens per KV block (8, 16 or 32)")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas to rotate (0 = auto)")
     ap.add_argument("--no-plan", action="store_true", help="padded grid instead of the host work plan")
     ap.add_argument("--unfused", action="store_true",
@@ -155,10 +156,10 @@ def kv_bytes(lens, Hkv, D, eb):
     return int(np.sum(lens.astype(np.int64))) * Hkv * D * eb * 2
 
 
-def decode_alg_bytes(lens, S, Hq, Hkv, D, eb):
+def decode_alg_bytes(lens, S, Hq, Hkv, D, eb, B=16):
     """Algorithmic bytes of one decode-attention call: live K/V, queries, fp32
     outputs, live block-table entries, lengths."""
-    nb = int(np.sum((lens.astype(np.int64) + 15) // 16))
+    nb = int(np.sum((lens.astype(np.int64) + B - 1) // B))
     return kv_bytes(lens, Hkv, D, eb) + S * Hq * D * eb + S * Hq * D * 4 + nb * 4 + S * 4
 
 
@@ -169,7 +170,7 @@ def cpu_baseline(w, seconds):
     from threadpoolctl import threadpool_limits
     import oracle
     from oracle.block_manager import run_ops
-    bm = oracle.BlockManager(w.num_blocks, free_order=w.free_order)
+    bm = oracle.BlockManager(w.num_blocks, block_size=w.spec.block_size, free_order=w.free_order)
     h, _, _ = run_ops(bm, w.setup_ops + w.step_ops)
     tables, lens = bm.packed_tables([h[i] for i in range(w.S)])
     sp = w.spec
@@ -177,7 +178,8 @@ def cpu_baseline(w, seconds):
     with threadpool_limits(limits=1):
         while passes < 50 and (passes == 0 or t_total < seconds):
             t0 = time.perf_counter()
-            oracle.decode_attention(w.q, w.k_pool, w.v_pool, tables, lens, sp.scale, sp.dtype)
+            oracle.decode_attention(w.q, w.k_pool, w.v_pool, tables, lens, sp.scale, sp.dtype,
+                                    block_size=sp.block_size)
             t_total += time.perf_counter() - t0
             passes += 1
     per = t_total / passes
@@ -207,7 +209,7 @@ def main():
     import paged_kv_cache_162_amd as kv
     from paged_kv_cache_162_amd.session import DecodeSession
 
-    w = make_workload(args.workload)
+    w = make_workload(args.workload, block_size=args.block_size)
     sp = w.spec
     dt = sp.dtype
     print(f"[bench] workload {sp.name}: S={sp.S} Hq={sp.Hq} Hkv={sp.Hkv} D={sp.D} {dt} "
@@ -296,7 +298,7 @@ def main():
     warm_ms = w0.elapsed_time(w1) / K
 
     kvb = kv_bytes(lens, sp.Hkv, sp.D, sp.elem_bytes)
-    alg = decode_alg_bytes(lens, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes)
+    alg = decode_alg_bytes(lens, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes, args.block_size)
     value = kvb / (step_ms * 1e-3) / 1e9
     achieved = alg / (dec_avg * 1e-3) / 1e9
     traffic = None
@@ -323,7 +325,7 @@ def main():
         "config": {
             "workload": f"{sp.name}: {sp.description}",
             "sequences": sp.S, "q_heads": sp.Hq, "kv_heads": sp.Hkv, "head_dim": sp.D,
-            "block_size": 16, "partition_tokens": args.partition or 512,
+            "block_size": args.block_size, "partition_tokens": args.partition or 512,
             "sum_context": int(lens.sum()), "max_context": int(lens.max()),
             "kv_bytes_per_step": kvb, "replicas_rotated": R, "parallelism": "single GPU",
             "fused_cache_write": not args.unfused, "hip_graph": bool(args.graph),

@@ -31,9 +31,12 @@
  * - Token position p of a sequence lives in slot
  *   table[p / B] * B + p % B ([4], "How it works"); slot s is element
  *   [s / B][h][s % B][:] of a pool.
- * - Supported on the device: block_size 16, head_dim 64 or 128, num_q_heads
- *   a multiple of num_kv_heads, dtypes f32/f16/bf16. Anything else returns
- *   KV_ERR_UNSUPPORTED.
+ * - Supported by the decode kernels: block_size 8, 16 or 32 (16 is the
+ *   pages' default; [1] "Why 16 tokens per block specifically?" treats it as
+ *   a tuning knob), head_dim 64 or 128, num_q_heads a multiple of
+ *   num_kv_heads, dtypes f32/f16/bf16. Anything else returns
+ *   KV_ERR_UNSUPPORTED. Slot mapping, cache writes and block copies take any
+ *   block size.
  */
 #ifndef PAGEDKV_H_
 #define PAGEDKV_H_
@@ -251,7 +254,8 @@ size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_
  * context_lens: device int32 [S]
  * max_context_len: host upper bound on every context_lens[s]; it sizes the
  *               grid (number of partitions).
- * partition_size: tokens per work item (multiple of 16, 16..1024); 0 = 512.
+ * partition_size: tokens per work item: a multiple of 16 and of block_size,
+ *               at most 1024 tokens and 64 blocks; 0 = 512.
  *               Sequences longer than one partition are split and a second
  *               kernel merges the partial results with a log-sum-exp
  *               reduction ([2], "The Custom CUDA Kernel": per-piece partial

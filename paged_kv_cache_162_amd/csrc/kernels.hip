@@ -46,8 +46,9 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 
-constexpr int kBlock = 16;           // tokens per KV block (device kernels)
-constexpr int kMaxPartition = 1024;  // tokens: at most 64 blocks, one table entry per lane
+constexpr int kTile = 16;            // tokens per compute tile (MFMA rows / VALU block step)
+constexpr int kMaxPartition = 1024;  // tokens per partition
+constexpr int kMaxPartBlocks = 64;   // blocks per partition: one table entry per lane
 constexpr int kDefaultPartition = 512;
 constexpr int kStageStride = 132;  // floats per head row in LDS (128 + 4 against bank conflicts)
 #ifndef PAGEDKV_DECODE_RING
@@ -119,7 +120,7 @@ struct DecodeParams {
   void* k_pool_w;
   void* v_pool_w;
   int64_t* slots;
-  int32_t max_blocks, S, Hq, Hkv, G, num_blocks, part_tokens, nparts, n_units;
+  int32_t max_blocks, S, Hq, Hkv, G, num_blocks, block_size, part_tokens, nparts, n_units;
   float scale_log2;
 };
 
@@ -159,7 +160,7 @@ __device__ __forceinline__ WorkItem unit_item(const DecodeParams& p, int u) {
 template <int D>
 __device__ __forceinline__ int unit_prologue(const DecodeParams& p, const WorkItem& w, int ctx,
                                              int lane) {
-  const bool bad = ctx < 0 || (int64_t)ctx > (int64_t)p.max_blocks * kBlock ||
+  const bool bad = ctx < 0 || (int64_t)ctx > (int64_t)p.max_blocks * p.block_size ||
                    (int64_t)ctx > (int64_t)p.nparts * p.part_tokens;
   if (bad || ctx == 0) {
     if (w.part == 0) {
@@ -206,22 +207,44 @@ __device__ __forceinline__ int entry_of(int staged, int j) {
 // writes the new token's K,V into the last block). The unit holding the
 // sequence's last position ctx-1 - the last row in use of its last block -
 // owns that token's row for its KV head: it returns the row's slot
-// (table[(ctx-1)/16]*16 + (ctx-1)%16, [4] "How it works"), or -1 when the
+// (table[(ctx-1)/B]*B + (ctx-1)%B, [4] "How it works"), or -1 when the
 // unit is invalid, and the caller stores the row before loading any block.
 // No other unit reads the row.
 struct NewToken {
   bool on;        // this unit places the new token
-  int row;        // row of the token in the unit's last block
+  int row;        // row of the token in the unit's last 16-token tile
   int64_t slot;   // -1 if nothing is written (invalid unit)
 };
 __device__ __forceinline__ NewToken new_token(const DecodeParams& p, const WorkItem& w, int nps,
-                                              int ctx, int staged, int last, bool bad, int lane) {
+                                              int ctx, int t0, int staged, bool bad, int lane) {
   NewToken t;
   t.on = p.k_new != nullptr && w.part == nps - 1;
-  t.row = (ctx - 1) % kBlock;
-  t.slot = (t.on && !bad) ? (int64_t)entry_of(staged, last) * kBlock + t.row : -1;
+  t.row = (ctx - 1) % kTile;
+  const int blk = (ctx - 1 - t0) / p.block_size;  // partition block holding ctx-1
+  t.slot = (t.on && !bad) ? (int64_t)entry_of(staged, blk) * p.block_size + (ctx - 1) % p.block_size
+                          : -1;
   if (t.on && p.slots && w.h == 0 && lane == 0) p.slots[w.s] = t.slot;
   return t;
+}
+
+// Index, in units of `unit` elements per token row, of row r (0..15) of
+// 16-token tile j of a partition for KV head h. Blocks of 16 or 32 tokens
+// hold a whole tile (one table entry per tile, wave-uniform); blocks of 8
+// tokens hold half a tile, so rows 0..7 and 8..15 use consecutive entries.
+template <int BS>
+__device__ __forceinline__ size_t tile_row(const DecodeParams& p, int h, int staged, int j, int r,
+                                           int unit) {
+  int e, rb;
+  if constexpr (BS >= kTile) {
+    e = entry_of(staged, (kTile * j) / BS);
+    rb = (kTile * j) % BS + r;
+  } else {
+    const int e_lo = entry_of(staged, 2 * j);
+    const int e_hi = entry_of(staged, min(2 * j + 1, 63));
+    e = r < 8 ? e_lo : e_hi;
+    rb = r & 7;
+  }
+  return (((size_t)e * p.Hkv + h) * BS + rb) * unit;
 }
 
 // Start of the unit's partial results: the G heads of (sequence, KV head,
@@ -275,7 +298,7 @@ template <int D>
 __global__ __launch_bounds__(kMergeThreads) void splitk_merge_kernel(DecodeParams p) {
   const int s = blockIdx.x / p.Hkv, h = blockIdx.x % p.Hkv;
   const int ctx = p.lens[s];
-  if (ctx <= 0 || (int64_t)ctx > (int64_t)p.max_blocks * kBlock ||
+  if (ctx <= 0 || (int64_t)ctx > (int64_t)p.max_blocks * p.block_size ||
       (int64_t)ctx > (int64_t)p.nparts * p.part_tokens)
     return;  // written by the decode kernel
   const int nps = (ctx + p.part_tokens - 1) / p.part_tokens;
@@ -322,13 +345,13 @@ __global__ __launch_bounds__(kMergeThreads) void splitk_merge_kernel(DecodeParam
 // reductions. Each group of LPR lanes keeps its own online softmax over the
 // tokens it reads; the groups are merged with cross-lane shuffles at the end.
 // ============================================================================
-template <int DT, int D, int GMAX>
+template <int DT, int D, int GMAX, int BS>
 __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   constexpr int EB = DT == KV_F32 ? 4 : 2;
   constexpr int EPL = 16 / EB;           // elements per lane chunk
   constexpr int LPR = D * EB / 16;       // lanes per token row
   constexpr int TPI = 64 / LPR;          // rows per wave-wide load
-  constexpr int IPB = kBlock / TPI;      // loads per 16-token block
+  constexpr int IPB = kTile / TPI;       // loads per 16-token tile
   static_assert(LPR == 8 || LPR == 16 || LPR == 32, "unsupported row width");
 
   const int lane = threadIdx.x;
@@ -342,17 +365,18 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   if (nps == 0) return;
   const int t0 = w.part * p.part_tokens;
   const int t1 = min(ctx, t0 + p.part_tokens);
-  const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
-  const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + t0 / kBlock;
+  const int nblk = (t1 - t0 + kTile - 1) / kTile;        // 16-token tiles
+  const int nent = (t1 - t0 + BS - 1) / BS;              // table entries (blocks)
+  const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + t0 / BS;
   bool bad = false;
-  const int staged = stage_entries(p, row, nblk, lane, bad);
-  const NewToken nt = new_token(p, w, nps, ctx, staged, nblk - 1, bad, lane);
+  const int staged = stage_entries(p, row, nent, lane, bad);
+  const NewToken nt = new_token(p, w, nps, ctx, t0, staged, bad, lane);
   if (nt.on && nt.slot >= 0 && r == nt.row % TPI) {
     // the lanes of row group nt.row % TPI load chunk c of the new token's
-    // rows with the last block; they store those chunks first, so program
+    // rows with the last tile; they store those chunks first, so program
     // order within the lane makes that load return the new values
     const size_t src = ((size_t)w.s * p.Hkv + w.h) * LPR + c;
-    const size_t dst = (((size_t)(nt.slot / kBlock) * p.Hkv + w.h) * kBlock + nt.row) * LPR + c;
+    const size_t dst = tile_row<BS>(p, w.h, staged, nblk - 1, nt.row, LPR) + c;
     static_cast<uint4*>(p.k_pool_w)[dst] = static_cast<const uint4*>(p.k_new)[src];
     static_cast<uint4*>(p.v_pool_w)[dst] = static_cast<const uint4*>(p.v_new)[src];
   }
@@ -382,21 +406,21 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
   }
 
-  const size_t tile_u4 = (size_t)kBlock * LPR;  // uint4 per (block, head) tile
   const uint4* kbase = static_cast<const uint4*>(p.k_pool);
   const uint4* vbase = static_cast<const uint4*>(p.v_pool);
 
-  auto load = [&](int e, uint4* ku, uint4* vu) {
-    const size_t tile = ((size_t)e * p.Hkv + w.h) * tile_u4;
+  auto load = [&](int j, uint4* ku, uint4* vu) {
 #pragma unroll
-    for (int i = 0; i < IPB; ++i) ku[i] = kbase[tile + (size_t)(r + TPI * i) * LPR + c];
-#pragma unroll
-    for (int i = 0; i < IPB; ++i) vu[i] = vbase[tile + (size_t)(r + TPI * i) * LPR + c];
+    for (int i = 0; i < IPB; ++i) {
+      const size_t at = tile_row<BS>(p, w.h, staged, j, r + TPI * i, LPR) + c;
+      ku[i] = kbase[at];
+      vu[i] = vbase[at];
+    }
   };
 
   auto compute = [&](int jb, const uint4* ku, uint4* vu) {
-    const int valid = t1 - (t0 + jb * kBlock);  // live tokens in this block (>= 1)
-    const bool full = valid >= kBlock;
+    const int valid = t1 - (t0 + jb * kTile);  // live tokens in this tile (>= 1)
+    const bool full = valid >= kTile;
     float kf[IPB][EPL], vf[IPB][EPL];
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
@@ -453,16 +477,16 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   {
     uint4 ka[IPB], va[IPB], kb[IPB], vb[IPB];
     const int last = nblk - 1;
-    load(entry_of(staged, 0), ka, va);
+    load(0, ka, va);
     int jb = 0;
     for (; jb + 2 < nblk; jb += 2) {
-      load(entry_of(staged, jb + 1), kb, vb);
+      load(jb + 1, kb, vb);
       compute(jb, ka, va);
-      load(entry_of(staged, jb + 2), ka, va);
+      load(jb + 2, ka, va);
       compute(jb + 1, kb, vb);
     }
     if (jb + 1 < nblk) {
-      load(entry_of(staged, min(jb + 1, last)), kb, vb);
+      load(min(jb + 1, last), kb, vb);
       compute(jb, ka, va);
       compute(jb + 1, kb, vb);
     } else {
@@ -619,11 +643,11 @@ __device__ __forceinline__ float column_sum(float x) {
   return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
-template <int DT, bool SPLITCOL, int RING>
+template <int DT, bool SPLITCOL, int RING, int BS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_mfma_kernel(DecodeParams p) {
   constexpr int D = 128;
-  constexpr size_t kTileBytes = (size_t)kBlock * D * 2;  // 4 KB
+  constexpr int kRowU4 = D / 8;  // uint4 per 16-bit token row
   const int lane = threadIdx.x;
   const int u = blockIdx.x;
   if (u >= p.n_units) return;
@@ -635,7 +659,7 @@ void decode_mfma_kernel(DecodeParams p) {
   // 64 table entries of the partition (bounded by the table width, so the
   // length is not needed yet) and the queries.
   const int ctx = p.lens[w.s];
-  const int b0 = w.part * (p.part_tokens / kBlock);
+  const int b0 = w.part * (p.part_tokens / BS);
   int raw_entry = 0;
   if (lane < p.max_blocks - b0) raw_entry = p.tables[(size_t)w.s * p.max_blocks + b0 + lane];
   // B operand of the score MFMA: Q^T, lane holds head `hd`, dims 32kc+8grp..+8
@@ -668,17 +692,17 @@ void decode_mfma_kernel(DecodeParams p) {
   if (nps == 0) return;
   const int t0 = w.part * p.part_tokens;
   const int t1 = min(ctx, t0 + p.part_tokens);
-  const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
+  const int nblk = (t1 - t0 + kTile - 1) / kTile;  // 16-token tiles
   const int last = nblk - 1;
   bool bad = false;
-  const int staged = check_entries(p, raw_entry, nblk, lane, bad);
-  const NewToken nt = new_token(p, w, nps, ctx, staged, last, bad, lane);
+  const int staged = check_entries(p, raw_entry, (t1 - t0 + BS - 1) / BS, lane, bad);
+  const NewToken nt = new_token(p, w, nps, ctx, t0, staged, bad, lane);
   if (nt.on && nt.slot >= 0) {
     // Each lane stores exactly the chunks of the new token's rows that it
     // later loads with the last block (K: the lanes of column nt.row, chunks
     // kc*4+grp; V: the lanes of row group nt.row/4, chunk col), so program
     // order within the lane makes that load return the new values.
-    const size_t dst = (((size_t)(nt.slot / kBlock) * p.Hkv + w.h) * kBlock + nt.row) * (D / 8);
+    const size_t dst = tile_row<BS>(p, w.h, staged, last, nt.row, kRowU4);
     if (col == nt.row) {
       uint4* kd = static_cast<uint4*>(p.k_pool_w) + dst + grp;
       kd[0] = kn0;
@@ -700,13 +724,13 @@ void decode_mfma_kernel(DecodeParams p) {
   const char* vbase = static_cast<const char*>(p.v_pool);
 
   auto load = [&](int j, uint4* ku, uint4* vu) {
-    const size_t tile = ((size_t)entry_of(staged, j) * p.Hkv + w.h) * kTileBytes;
-    const uint4* kt = reinterpret_cast<const uint4*>(kbase + tile);
-    const uint4* vt = reinterpret_cast<const uint4*>(vbase + tile);
+    // K: row col of the tile; V: rows 4grp..4grp+3 (consecutive in one block)
+    const uint4* kt = reinterpret_cast<const uint4*>(kbase) + tile_row<BS>(p, w.h, staged, j, col, kRowU4);
+    const uint4* vt = reinterpret_cast<const uint4*>(vbase) + tile_row<BS>(p, w.h, staged, j, 4 * grp, kRowU4);
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) ku[kc] = kt[col * 16 + kc * 4 + grp];
+    for (int kc = 0; kc < 4; ++kc) ku[kc] = kt[kc * 4 + grp];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) vu[jj] = vt[(4 * grp + jj) * 16 + col];
+    for (int jj = 0; jj < 4; ++jj) vu[jj] = vt[jj * kRowU4 + col];
   };
 
   auto compute = [&](int jb, uint4* ku, uint4* vu) {
@@ -716,8 +740,8 @@ void decode_mfma_kernel(DecodeParams p) {
     float x[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = st[r] * p.scale_log2;
-    const int valid = t1 - (t0 + jb * kBlock);  // live tokens of the block (>= 1)
-    if (valid < kBlock) {
+    const int valid = t1 - (t0 + jb * kTile);  // live tokens of the tile (>= 1)
+    if (valid < kTile) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (4 * grp + r >= valid) {
@@ -937,16 +961,40 @@ kv_status launch_decode(Kernel kernel, const DecodeParams& prm, hipStream_t st) 
   return launch_status("kv_paged_attention_decode");
 }
 
-template <int DT, int D>
+template <int DT, int D, int BS>
 kv_status launch_valu(const DecodeParams& prm, int gmax, hipStream_t st) {
   switch (gmax) {
-    case 1: return launch_decode(decode_valu_kernel<DT, D, 1>, prm, st);
-    case 2: return launch_decode(decode_valu_kernel<DT, D, 2>, prm, st);
-    case 4: return launch_decode(decode_valu_kernel<DT, D, 4>, prm, st);
-    case 8: return launch_decode(decode_valu_kernel<DT, D, 8>, prm, st);
-    case 16: return launch_decode(decode_valu_kernel<DT, D, 16>, prm, st);
+    case 1: return launch_decode(decode_valu_kernel<DT, D, 1, BS>, prm, st);
+    case 2: return launch_decode(decode_valu_kernel<DT, D, 2, BS>, prm, st);
+    case 4: return launch_decode(decode_valu_kernel<DT, D, 4, BS>, prm, st);
+    case 8: return launch_decode(decode_valu_kernel<DT, D, 8, BS>, prm, st);
+    case 16: return launch_decode(decode_valu_kernel<DT, D, 16, BS>, prm, st);
     default: return fail(KV_ERR_UNSUPPORTED, "decode: group size");
   }
+}
+
+// The decode kernel for one block size: MFMA for grouped 16-bit heads of
+// dimension 128, vector ALUs otherwise.
+template <int BS>
+kv_status launch_decode_kernel(const DecodeParams& prm, kv_dtype dtype, int head_dim, int G,
+                               hipStream_t st) {
+  constexpr int R = kDecodeRing;
+  if ((dtype == KV_F16 || dtype == KV_BF16) && head_dim == 128 && G >= 2) {
+    if (G <= 8)
+      return dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16, true, R, BS>, prm, st)
+                              : launch_decode(decode_mfma_kernel<KV_F16, true, R, BS>, prm, st);
+    return dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16, false, R, BS>, prm, st)
+                            : launch_decode(decode_mfma_kernel<KV_F16, false, R, BS>, prm, st);
+  }
+  const int gmax = G == 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
+  if (dtype == KV_F32)
+    return head_dim == 64 ? launch_valu<KV_F32, 64, BS>(prm, gmax, st)
+                          : launch_valu<KV_F32, 128, BS>(prm, gmax, st);
+  if (dtype == KV_F16)  // 16-bit head_dim 128 reaches here only with G == 1
+    return head_dim == 64 ? launch_valu<KV_F16, 64, BS>(prm, gmax, st)
+                          : launch_decode(decode_valu_kernel<KV_F16, 128, 1, BS>, prm, st);
+  return head_dim == 64 ? launch_valu<KV_BF16, 64, BS>(prm, gmax, st)
+                        : launch_decode(decode_valu_kernel<KV_BF16, 128, 1, BS>, prm, st);
 }
 
 kv_status check_cache_write(const char* who, const void* k_new, const void* v_new,
@@ -1088,15 +1136,19 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
   if (num_q_heads % num_kv_heads != 0)
     return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: query heads %d not a multiple of KV heads %d",
                 num_q_heads, num_kv_heads);
-  if (block_size != kBlock)
-    return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: block_size %d (only 16)", block_size);
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: block_size %d (8, 16 or 32)",
+                block_size);
   if (head_dim != 64 && head_dim != 128)
     return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: head_dim %d (64 or 128)", head_dim);
   const int32_t G = num_q_heads / num_kv_heads;
   if (G > 16) return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: group size %d > 16", G);
   const int32_t P = effective_partition(partition_size);
-  if (P < kBlock || P > kMaxPartition || P % kBlock != 0)
-    return fail(KV_ERR_INVALID, "kv_paged_attention_decode: partition_size %d", partition_size);
+  if (P < kTile || P > kMaxPartition || P % kTile != 0 || P % block_size != 0 ||
+      P / block_size > kMaxPartBlocks)
+    return fail(KV_ERR_INVALID,
+                "kv_paged_attention_decode: partition_size %d (a multiple of 16 and of the block "
+                "size, at most 1024 tokens and 64 blocks)", partition_size);
   if (S == 0) return KV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(KV_ERR_INVALID, "kv_paged_attention_decode: null pointer");
@@ -1143,28 +1195,11 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
   prm.v_pool_w = const_cast<void*>(v_pool);
   prm.slots = slots;
 
-  kv_status st;
-  const bool mfma = (dtype == KV_F16 || dtype == KV_BF16) && head_dim == 128 && G >= 2;
-  if (mfma) {
-    constexpr int R = kDecodeRing;
-    if (G <= 8)
-      st = dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16, true, R>, prm, stream)
-                            : launch_decode(decode_mfma_kernel<KV_F16, true, R>, prm, stream);
-    else
-      st = dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16, false, R>, prm, stream)
-                            : launch_decode(decode_mfma_kernel<KV_F16, false, R>, prm, stream);
-  } else {
-    const int gmax = G == 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
-    if (dtype == KV_F32)
-      st = head_dim == 64 ? launch_valu<KV_F32, 64>(prm, gmax, stream)
-                          : launch_valu<KV_F32, 128>(prm, gmax, stream);
-    else if (dtype == KV_F16)  // 16-bit head_dim 128 reaches here only with G == 1
-      st = head_dim == 64 ? launch_valu<KV_F16, 64>(prm, gmax, stream)
-                          : launch_decode(decode_valu_kernel<KV_F16, 128, 1>, prm, stream);
-    else
-      st = head_dim == 64 ? launch_valu<KV_BF16, 64>(prm, gmax, stream)
-                          : launch_decode(decode_valu_kernel<KV_BF16, 128, 1>, prm, stream);
-  }
+  prm.block_size = block_size;
+  const kv_status st =
+      block_size == 8 ? launch_decode_kernel<8>(prm, dtype, head_dim, G, stream)
+      : block_size == 16 ? launch_decode_kernel<16>(prm, dtype, head_dim, G, stream)
+                         : launch_decode_kernel<32>(prm, dtype, head_dim, G, stream);
   if (st != KV_OK || nparts <= 1) return st;
   const dim3 mgrid((unsigned)((int64_t)S * num_kv_heads));
   if (head_dim == 128)

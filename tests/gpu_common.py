@@ -78,8 +78,8 @@ class Case:
     """One workload on both sides. `S` truncates workloads 2-4 for speed."""
 
     def __init__(self, cfg: int, S: Optional[int] = None, poison: bool = True,
-                 partition_size: int = 0, seed: Optional[int] = None):
-        self.w = w = make_workload(cfg, seed=seed, S=S)
+                 partition_size: int = 0, seed: Optional[int] = None, block_size: int = 16):
+        self.w = w = make_workload(cfg, seed=seed, S=S, block_size=block_size)
         self.sp = sp = w.spec
         self.dt = sp.dtype
         self.partition_size = partition_size
@@ -88,7 +88,8 @@ class Case:
         values = self._values()
         # dry run of the oracle block manager to learn which slots end up
         # live and which get written, so the shared input pool can be poisoned
-        dry = BlockManager(w.num_blocks, free_order=w.free_order)
+        B = self.B = sp.block_size
+        dry = BlockManager(w.num_blocks, block_size=B, free_order=w.free_order)
         h = {}
         written = []
         for is_step, ops in ((False, w.setup_ops), (True, w.step_ops)):
@@ -101,11 +102,11 @@ class Case:
                     slots, _ = dry.append(h[op[1]], op[2])
                     if is_step or (len(op) > 3 and op[3] == "values"):
                         written.extend(slots)
-        live = np.zeros((w.num_blocks, 16), bool)
+        live = np.zeros((w.num_blocks, B), bool)
         for s in range(sp.S):
             t = dry.table(h[s])
             for p in range(dry.length(h[s])):
-                live[t[p // 16], p % 16] = True
+                live[t[p // B], p % B] = True
         self.k_in, self.v_in = w.k_pool.copy(), w.v_pool.copy()
         if poison:
             dead = np.argwhere(~live)
@@ -114,7 +115,7 @@ class Case:
                 if len(dead):
                     poison_slots(pool, self.dt, dead[:, 0], dead[:, 1])
                 if len(wr):
-                    poison_slots(pool, self.dt, wr // 16, wr % 16)
+                    poison_slots(pool, self.dt, wr // B, wr % B)
         self._oracle_side(values)
 
     def _values(self) -> Dict[int, Tuple[np.ndarray, np.ndarray]]:
@@ -125,7 +126,7 @@ class Case:
 
     def _oracle_side(self, values):
         w = self.w
-        bm = BlockManager(w.num_blocks, free_order=w.free_order)
+        bm = BlockManager(w.num_blocks, block_size=self.B, free_order=w.free_order)
         kp, vp = self.k_in.copy(), self.v_in.copy()
         h = {}
         self.setup_pairs = []
@@ -140,21 +141,22 @@ class Case:
                     oa.copy_blocks([kp, vp], pairs)
                     self.setup_pairs.extend(pairs)
                 if len(op) > 3 and op[3] == "values":
-                    oa.reshape_and_cache(values[op[1]][0], values[op[1]][1], kp, vp, slots)
+                    oa.reshape_and_cache(values[op[1]][0], values[op[1]][1], kp, vp, slots,
+                                         block_size=self.B)
         step_slots = []
         for op in w.step_ops:
             slots, pairs = bm.append(h[op[1]], op[2])
             assert not pairs
             step_slots.extend(slots)
         self.step_slots = np.array(step_slots, dtype=np.int64)
-        oa.reshape_and_cache(w.k_new, w.v_new, kp, vp, self.step_slots)
+        oa.reshape_and_cache(w.k_new, w.v_new, kp, vp, self.step_slots, block_size=self.B)
         self.tables, self.lens = bm.packed_tables([h[s] for s in range(self.sp.S)])
         self.k_ref, self.v_ref = kp, vp
         self.bm, self.oh = bm, h
 
     def oracle_out(self, pairs: Optional[List[Tuple[int, int]]] = None) -> np.ndarray:
         return oracle.decode_attention(self.w.q, self.k_ref, self.v_ref, self.tables, self.lens,
-                                       self.sp.scale, self.dt, pairs=pairs)
+                                       self.sp.scale, self.dt, block_size=self.B, pairs=pairs)
 
     # -- device side ----------------------------------------------------------
     def device_run(self, partition_size: Optional[int] = None, fused: bool = True):

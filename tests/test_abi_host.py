@@ -80,7 +80,9 @@ def test_device_entry_points_validate_on_the_host(kv):
         return lib.kv_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["t"], a["mb"], a["lens"],
                                              a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"], a["scale"],
                                              a["dt"], a["P"], a["mc"], None, 0, a["ws"], a["wsb"], a["st"])
-    assert call(B=8) == kv.KV_ERR_UNSUPPORTED
+    assert call(B=12) == kv.KV_ERR_UNSUPPORTED
+    assert call(B=32, P=48) == kv.KV_ERR_INVALID   # partition not a multiple of the block
+    assert call(B=8, P=1024) == kv.KV_ERR_INVALID  # more than 64 blocks per partition
     assert call(D=96) == kv.KV_ERR_UNSUPPORTED
     assert call(Hq=7) == kv.KV_ERR_UNSUPPORTED
     assert call(Hq=64, Hkv=2) == kv.KV_ERR_UNSUPPORTED

@@ -148,8 +148,9 @@ def sample_pairs(case, n, rng):
     return sorted(pairs)
 
 
-def run_workload(cfg, S=None, full_pool_compare=True, n_sample=None, partition_size=0):
-    case = Case(cfg, S=S, partition_size=partition_size)
+def run_workload(cfg, S=None, full_pool_compare=True, n_sample=None, partition_size=0,
+                 block_size=16):
+    case = Case(cfg, S=S, partition_size=partition_size, block_size=block_size)
     cows, host_slots, step_pairs = case.device_run()
     sp = case.sp
     # allocator parity (C++ vs oracle model)
@@ -163,7 +164,7 @@ def run_workload(cfg, S=None, full_pool_compare=True, n_sample=None, partition_s
         assert np.array_equal(bits(to_host(case.k_dev, case.dt)), bits(case.k_ref))
         assert np.array_equal(bits(to_host(case.v_dev, case.dt)), bits(case.v_ref))
     else:
-        blocks = np.unique(np.concatenate([case.step_slots // 16,
+        blocks = np.unique(np.concatenate([case.step_slots // case.B,
                                            np.random.default_rng(3).integers(0, case.w.num_blocks, 64)]))
         idx = torch.from_numpy(blocks).cuda()
         assert np.array_equal(bits(to_host(case.k_dev[idx], case.dt)), bits(case.k_ref[blocks]))
@@ -270,8 +271,8 @@ def test_graph_replay_matches_eager():
 # ---------------------------------------------------------------------------
 # kernel coverage on random ragged shapes (every dtype / head_dim / group)
 # ---------------------------------------------------------------------------
-def random_case(rng, lens, Hq, Hkv, D, dt, num_blocks=None, poison=True):
-    nbs = [-(-t // 16) for t in lens]
+def random_case(rng, lens, Hq, Hkv, D, dt, num_blocks=None, poison=True, B=16):
+    nbs = [-(-t // B) for t in lens]
     NB = num_blocks or (sum(nbs) + 5)
     perm = rng.permutation(NB)
     tab = np.full((len(lens), max(nbs + [1])), -1, np.int32)
@@ -279,13 +280,13 @@ def random_case(rng, lens, Hq, Hkv, D, dt, num_blocks=None, poison=True):
     for s, nb in enumerate(nbs):
         tab[s, :nb] = perm[off:off + nb]
         off += nb
-    kp = round_to_dtype(rng.standard_normal((NB, Hkv, 16, D)).astype(np.float32), dt)
-    vp = round_to_dtype(rng.standard_normal((NB, Hkv, 16, D)).astype(np.float32), dt)
+    kp = round_to_dtype(rng.standard_normal((NB, Hkv, B, D)).astype(np.float32), dt)
+    vp = round_to_dtype(rng.standard_normal((NB, Hkv, B, D)).astype(np.float32), dt)
     if poison:
-        live = np.zeros((NB, 16), bool)
+        live = np.zeros((NB, B), bool)
         for s, t in enumerate(lens):
             for p in range(t):
-                live[tab[s, p // 16], p % 16] = True
+                live[tab[s, p // B], p % B] = True
         for pool in (kp, vp):
             b = bits(pool)
             dead = np.argwhere(~live)
@@ -373,6 +374,59 @@ def test_decode_append_against_oracle(dt, D, G):
         got = out.cpu().numpy()
         assert np.all(got[~ok] == 0.0)
         check_attention(got[ok].reshape(-1, D), ref[ok].reshape(-1, D), dt, f"append {dt}/{D}/{G}/{ps}")
+
+
+BLOCK_SHAPES = [(B, dt, D, G) for B in (8, 32)
+                for dt, D, G in (("bf16", 128, 8), ("f16", 128, 16), ("f32", 64, 2), ("bf16", 128, 1))]
+
+
+@pytest.mark.parametrize("B,dt,D,G", BLOCK_SHAPES)
+def test_block_size_variants_against_oracle(B, dt, D, G):
+    """Blocks of 8 and 32 tokens: plain decode, and decode with the fused
+    cache write, against the oracle run with the same block size."""
+    kv = kvlib()
+    rng = np.random.default_rng(3000 + B + G + D)
+    lens = [1, 7, 8, 9, 15, 16, 17, 33, 100, 255, 256, 257, 700]
+    Hkv = 2
+    q, kp, vp, tab, cl = random_case(rng, lens, G * Hkv, Hkv, D, dt, B=B)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    ref = oracle.decode_attention(q, kp, vp, tab, cl, scale, dt, block_size=B)
+    for ps, plan in ((0, True), (64, False), (256, True)):
+        log(f"[gpu] decode B={B} {dt} D={D} G={G} partition={ps} plan={plan}")
+        got = gpu_decode(q, kp, vp, tab, cl, scale, dt, ps, plan=plan)
+        check_attention(got.reshape(-1, D), ref.reshape(-1, D), dt, f"B={B} {dt}/{D}/{G}/{ps}")
+    # fused cache write of a new token at each sequence's last position
+    S = len(lens)
+    kn = round_to_dtype(rng.standard_normal((S, Hkv, D)).astype(np.float32), dt)
+    vn = round_to_dtype(rng.standard_normal((S, Hkv, D)).astype(np.float32), dt)
+    ref_slots = oa.slot_mapping(tab, np.arange(S), cl - 1, block_size=B)
+    for pool in (kp, vp):
+        bits(pool)[ref_slots // B, :, ref_slots % B, :] = POISON[dt]
+    rk, rv = kp.copy(), vp.copy()
+    oa.reshape_and_cache(kn, vn, rk, rv, ref_slots, block_size=B)
+    ref2 = oracle.decode_attention(q, rk, rv, tab, cl, scale, dt, block_size=B)
+    dk, dv = to_dev(kp, dt), to_dev(vp, dt)
+    out = torch.full((S, G * Hkv, D), float("nan"), dtype=torch.float32, device="cuda")
+    slots = torch.full((S,), 7, dtype=torch.int64, device="cuda")
+    mc = int(cl.max())
+    wsb = kv.kv_paged_attention_workspace_bytes(S, G * Hkv, Hkv, D, mc, 0)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
+    items = torch.from_numpy(kv.kv_paged_attention_plan(cl, 0)).cuda()
+    log(f"[gpu] decode_append B={B} {dt} D={D} G={G}")
+    kv.kv_paged_attention_decode_append(out, to_dev(q, dt), to_dev(kn, dt), to_dev(vn, dt), dk, dv,
+                                        torch.from_numpy(tab).cuda(), torch.from_numpy(cl).cuda(),
+                                        scale, mc, slots, ws, 0, items)
+    torch.cuda.synchronize()
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    assert np.array_equal(bits(to_host(dk, dt)), bits(rk)) and np.array_equal(bits(to_host(dv, dt)), bits(rv))
+    check_attention(out.cpu().numpy().reshape(-1, D), ref2.reshape(-1, D), dt, f"append B={B}")
+
+
+def test_block_size_workload_llama70b_b32():
+    """The 70B-shaped workload (truncated) in 32-token blocks, through the
+    session's fused step, against the oracle with the same block size."""
+    from gpu_common import Case as _Case  # noqa: F401
+    run_workload(3, S=12, block_size=32)
 
 
 def test_plan_and_padded_grid_are_bitwise_identical():

@@ -198,7 +198,7 @@ def _pool_blocks(sp: WorkloadSpec, lens: np.ndarray) -> int:
     if sp.cfg == 1:
         return 32
     if sp.cfg == 2:
-        return 8192
+        return 8192 * 16 // B  # the worst case, 64 sequences of 2048 tokens
     if sp.cfg == 3:
         need = int(sum(-(-int(t) // B) for t in lens))
         return int(math.ceil(1.1 * need))
@@ -213,7 +213,7 @@ def _pool_blocks(sp: WorkloadSpec, lens: np.ndarray) -> int:
 
 
 def make_workload(cfg: int, seed: Optional[int] = None, *, with_values: bool = True,
-                  S: Optional[int] = None) -> Workload:
+                  S: Optional[int] = None, block_size: int = 16) -> Workload:
     """Build workload `cfg` deterministically.
 
     `seed` defaults to 162000 + cfg. `with_values=False` skips the pool fill
@@ -222,6 +222,10 @@ def make_workload(cfg: int, seed: Optional[int] = None, *, with_values: bool = T
     the pool is then sized for that S with the same rule.
     """
     sp = SPECS[cfg]
+    if block_size != sp.block_size:
+        # the same workload in another block size: same lengths, queries and
+        # new tokens; the pool is sized by the same rule for the new block size
+        sp = dataclasses.replace(sp, block_size=block_size)
     if S is not None and S != sp.S:
         if cfg not in (2, 3, 4):
             raise ValueError("only workloads 2-4 may be truncated")
