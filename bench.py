@@ -60,6 +60,9 @@ def parse():
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --copy-calibration` into the traffic JSON and exit")
     ap.add_argument("--pmc-out", default="", help="where --pmc-parse writes its JSON")
+    ap.add_argument("--swap", action="store_true",
+                    help="measure swap-out / swap-in of one 4096-token sequence of an "
+                         "80-layer GQA model (8 KV heads, head_dim 128, bf16) instead")
     return ap.parse_args()
 
 
@@ -190,6 +193,68 @@ def cpu_baseline(w, seconds):
                       f"pass(es), BLAS limited to 1 thread"}
 
 
+def swap_bench(args, kv, torch):
+    """Swap bandwidth: one sequence of SWAP_TOKENS tokens of an 80-layer model
+    with 8 KV heads of 128 dims in bf16 (the per-layer shape of the 70B-class
+    GQA decode workload) goes to pinned host memory and back. The ceiling shown
+    beside it is a DMA copy of the same number of contiguous bytes."""
+    L, Hkv, B, D, eb = 80, 8, args.block_size, 128, 2
+    tokens = SWAP_TOKENS
+    nb = -(-tokens // B)
+    NB = 2 * nb
+    bb = Hkv * B * D * eb
+    kp = [torch.empty(NB * bb, dtype=torch.uint8, device="cuda") for _ in range(L)]
+    vp = [torch.empty(NB * bb, dtype=torch.uint8, device="cuda") for _ in range(L)]
+    for t in kp + vp:
+        t.random_(0, 256)
+    # scattered like a pool that has seen churn: every other block, shuffled
+    g = torch.Generator().manual_seed(162)
+    ids = (torch.randperm(NB, generator=g)[:nb].to(torch.int32)).cuda()
+    total = nb * L * 2 * bb
+    host = torch.empty(total, dtype=torch.uint8, pin_memory=True)
+    dev_flat = torch.empty(total, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3
+
+    reps = max(args.steps // 20, 3)
+    t_out = timed(lambda: kv.kv_swap_out_blocks(kp, vp, ids, NB, bb, host), reps)
+    t_in = timed(lambda: kv.kv_swap_in_blocks(kp, vp, ids, NB, bb, host), reps)
+    t_d2h = timed(lambda: host.copy_(dev_flat, non_blocking=True), reps)
+    t_h2d = timed(lambda: dev_flat.copy_(host, non_blocking=True), reps)
+    # the round trip is bit exact
+    kv.kv_swap_out_blocks(kp, vp, ids, NB, bb, host)
+    ref = [kp[0][i * bb:(i + 1) * bb].clone() for i in ids[:4].tolist()]
+    for t in kp[:1]:
+        t.zero_()
+    kv.kv_swap_in_blocks(kp, vp, ids, NB, bb, host)
+    torch.cuda.synchronize()
+    ok = all(torch.equal(r, kp[0][i * bb:(i + 1) * bb]) for r, i in zip(ref, ids[:4].tolist()))
+    gbs = lambda t: total / t / 1e9
+    print(json.dumps({
+        "metric": "swap_bandwidth", "unit": "GB/s", "higher_is_better": True,
+        "swap_out": round(gbs(t_out), 2), "swap_in": round(gbs(t_in), 2),
+        "dma_copy_d2h": round(gbs(t_d2h), 2), "dma_copy_h2d": round(gbs(t_h2d), 2),
+        "swap_out_ms": round(t_out * 1e3, 3), "swap_in_ms": round(t_in * 1e3, 3),
+        "bytes": total, "round_trip_bit_exact": ok, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"swap one {tokens}-token sequence, {L} layers x K,V, "
+                               f"{Hkv} KV heads x {D} dims, block {B}", "blocks": nb},
+    }))
+
+
+SWAP_TOKENS = 4096
+
+
 def main():
     args = parse()
     if args.pmc_parse:
@@ -208,6 +273,9 @@ def main():
         b.build()
     import paged_kv_cache_162_amd as kv
     from paged_kv_cache_162_amd.session import DecodeSession
+    if args.swap:
+        swap_bench(args, kv, torch)
+        return
 
     w = make_workload(args.workload, block_size=args.block_size)
     sp = w.spec

@@ -153,6 +153,27 @@ int32_t kv_seq_len(const kv_pool_t* pool, int64_t seq);
 kv_status kv_seq_pack_tables(const kv_pool_t* pool, int32_t n_seqs, const int64_t* seqs,
                              int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
 
+/* Swap a sequence out under memory pressure ([3], "The allocation
+ * lifecycle": preempt a sequence by moving its blocks to host memory; [1],
+ * "Preemption"): ids[0..*n) receive the sequence's current table (the blocks
+ * whose contents the caller copies to the host, e.g. with kv_swap_out_blocks,
+ * before any later write can reuse them), then each block loses one
+ * reference exactly as kv_seq_free does. The sequence keeps its length and
+ * is marked swapped out. If cap < the table length, returns KV_ERR_INVALID
+ * with *n set and nothing changed. KV_ERR_STATE if unknown or already
+ * swapped out. A swapped-out sequence cannot be appended to, forked, or
+ * packed / read by kv_seq_block_table (KV_ERR_STATE); it can be freed. */
+kv_status kv_seq_swap_out(kv_pool_t* pool, int64_t seq, int32_t cap, int32_t* ids, int32_t* n);
+/* Readmit a swapped-out sequence: takes ceil(len / block_size) free blocks
+ * (reference count 1, all or nothing: KV_ERR_OOM changes nothing) and
+ * returns them in logical order in ids[0..*n); the caller copies the saved
+ * contents into them (kv_swap_in_blocks). Blocks that were shared before
+ * the swap come back as private copies. KV_ERR_STATE if the sequence is
+ * unknown or not swapped out; KV_ERR_INVALID with *n set if cap is short. */
+kv_status kv_seq_swap_in(kv_pool_t* pool, int64_t seq, int32_t cap, int32_t* ids, int32_t* n);
+/* 1 if the sequence is swapped out, 0 if resident, -1 if unknown. */
+int32_t kv_seq_is_swapped(const kv_pool_t* pool, int64_t seq);
+
 /* ---------------------------------------------------------------------------
  * Device: slot mapping and cache writes.
  * ------------------------------------------------------------------------- */
@@ -208,6 +229,24 @@ kv_status kv_append_tokens(const int32_t* tables, int32_t num_rows, int32_t max_
 kv_status kv_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,
                          const int32_t* pairs, int32_t n, int32_t num_blocks,
                          size_t block_bytes, hipStream_t stream);
+
+/* Device half of a swap ([3], "The allocation lifecycle", memory
+ * pressure): copy whole blocks - every layer, K and V - between the pools and
+ * host memory. block_ids is a device int32 array of n physical IDs (entries
+ * outside [0, num_blocks) are skipped); k_pools and v_pools are HOST arrays
+ * of num_layers (<= 256) device pointers; block_bytes is one layer's bytes
+ * of one block in one pool (num_kv_heads * block_size * head_dim * element
+ * size, a multiple of 16). host_buffer must be pinned host memory
+ * (hipHostMalloc, torch pin_memory) of n * num_layers * 2 * block_bytes bytes,
+ * laid out [n][num_layers][K, V][block_bytes]; the kernel reads or writes it
+ * directly, so it must stay allocated until the stream has passed the copy.
+ * The copy is bit exact. KV_ERR_INVALID for unpinned or misaligned buffers. */
+kv_status kv_swap_out_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,
+                             const int32_t* block_ids, int32_t n, int32_t num_blocks,
+                             size_t block_bytes, void* host_buffer, hipStream_t stream);
+kv_status kv_swap_in_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,
+                            const int32_t* block_ids, int32_t n, int32_t num_blocks,
+                            size_t block_bytes, const void* host_buffer, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Device: paged decode attention ([1], "The PagedAttention kernel"; [2],

@@ -21,7 +21,8 @@ closed forms, invariants and brute force; none is "parity unpinned".
 from .attention import (  # noqa: F401
     widen, slot_of, slot_mapping, gather_sequence, decode_attention,
     decode_attention_blockwise, partial_attention, merge_partials,
-    decode_attention_split, reshape_and_cache, copy_blocks,
+    decode_attention_split, reshape_and_cache, copy_blocks, swap_out_blocks,
+    swap_in_blocks,
 )
 from .block_manager import BlockManager, KVError  # noqa: F401
 from .sizes import (  # noqa: F401

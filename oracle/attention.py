@@ -260,3 +260,42 @@ def copy_blocks(pools: List[np.ndarray], pairs: Sequence[Tuple[int, int]]) -> No
         b = _bits(pool)
         for src, dst in pairs:
             b[int(dst)] = b[int(src)]
+
+
+def swap_out_blocks(k_pools: List[np.ndarray], v_pools: List[np.ndarray],
+                    ids: Sequence[int]) -> np.ndarray:
+    """Host copy of whole blocks for a swap-out, as raw bytes laid out
+    [n][layer][K, V][block bytes] (one block's state for all layers together).
+
+    The device half of preemption by swapping ([3], "The allocation
+    lifecycle", memory pressure; [1], "Preemption"): the block contents move
+    to host memory unchanged. Entries outside the pool are left as zeros.
+    """
+    L = len(k_pools)
+    nb = k_pools[0].shape[0]
+    bb = k_pools[0][0].nbytes
+    host = np.zeros((len(ids), L, 2, bb), dtype=np.uint8)
+    for i, b in enumerate(ids):
+        if not (0 <= int(b) < nb):
+            continue
+        for layer in range(L):
+            host[i, layer, 0] = np.frombuffer(np.ascontiguousarray(k_pools[layer][int(b)]).tobytes(),
+                                              dtype=np.uint8)
+            host[i, layer, 1] = np.frombuffer(np.ascontiguousarray(v_pools[layer][int(b)]).tobytes(),
+                                              dtype=np.uint8)
+    return host
+
+
+def swap_in_blocks(k_pools: List[np.ndarray], v_pools: List[np.ndarray],
+                   ids: Sequence[int], host: np.ndarray) -> None:
+    """Inverse of swap_out_blocks: write host[i] back into block ids[i] of
+    every layer, in place (entries outside the pool are skipped)."""
+    nb = k_pools[0].shape[0]
+    for i, b in enumerate(ids):
+        if not (0 <= int(b) < nb):
+            continue
+        for layer, (kp, vp) in enumerate(zip(k_pools, v_pools)):
+            for pool, kv in ((kp, 0), (vp, 1)):
+                blk = pool[int(b)]
+                pool[int(b)] = np.frombuffer(host[i, layer, kv].tobytes(),
+                                             dtype=pool.dtype).reshape(blk.shape)

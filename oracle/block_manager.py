@@ -21,7 +21,11 @@ What the pages fix:
     block, drops the old block's count and redirects the writer ([2],
     "Copy-on-Write ..."); appending after a full shared block copies nothing
     ([1], "A small worked example", step 3);
-  * a finished sequence returns every block ([2], "Sequence Completion").
+  * a finished sequence returns every block ([2], "Sequence Completion");
+  * under memory pressure a sequence can be preempted by swapping its blocks
+    to host memory and bringing them back when it is readmitted ([3], "The
+    allocation lifecycle", memory pressure; [1], "Preemption"), all or
+    nothing per sequence ([3], "L3").
 
 Readings where the pages leave a choice open:
   * growth is lazy: a new block is taken just before writing position p when
@@ -35,7 +39,15 @@ Readings where the pages leave a choice open:
     it copies the whole block; it allocates the copy before any new block of
     the same append;
   * every operation is all-or-nothing: on failure nothing changes ([3], "L3",
-    preemption is all-or-nothing per sequence).
+    preemption is all-or-nothing per sequence);
+  * swapping out returns the sequence's current table (the blocks whose
+    contents go to host memory, in logical order) and then drops one
+    reference per block exactly as freeing does; the sequence keeps its
+    length. Swapping in takes ceil(length / B) fresh blocks (reference count
+    1, popped in logical order) that the contents are copied back into; a
+    block shared with another sequence before the swap comes back as a
+    private copy. A swapped-out sequence cannot be appended to, forked or
+    packed until it is swapped back in; it can be freed.
 """
 from __future__ import annotations
 
@@ -62,6 +74,7 @@ class BlockManager:
         self._set_stack(order)
         self.tables: Dict[int, List[int]] = {}
         self.lengths: Dict[int, int] = {}
+        self.swapped: set = set()
         self._next_seq = 0
 
     # -- pool ---------------------------------------------------------------
@@ -122,6 +135,8 @@ class BlockManager:
     def _seq(self, seq: int) -> List[int]:
         if seq not in self.tables:
             raise KVError("STATE", f"unknown sequence {seq}")
+        if seq in self.swapped:
+            raise KVError("STATE", f"sequence {seq} is swapped out")
         return self.tables[seq]
 
     def create(self) -> int:
@@ -176,16 +191,44 @@ class BlockManager:
         return slots, pairs
 
     def free_seq(self, seq: int) -> None:
-        table = self._seq(seq)
-        self.decref(table)
+        if seq in self.swapped:  # holds no blocks
+            self.swapped.discard(seq)
+        else:
+            self.decref(self._seq(seq))
         del self.tables[seq]
         del self.lengths[seq]
+
+    def swap_out(self, seq: int) -> List[int]:
+        """Preempt `seq`: return its table, then release its blocks."""
+        table = list(self._seq(seq))
+        self.decref(table)
+        self.tables[seq] = []
+        self.swapped.add(seq)
+        return table
+
+    def swap_in(self, seq: int) -> List[int]:
+        """Readmit `seq`: ceil(length / B) fresh blocks, all or nothing."""
+        if seq not in self.tables:
+            raise KVError("STATE", f"unknown sequence {seq}")
+        if seq not in self.swapped:
+            raise KVError("STATE", f"sequence {seq} is not swapped out")
+        need = -(-self.lengths[seq] // self.block_size)
+        ids = self.alloc(need)
+        self.tables[seq] = list(ids)
+        self.swapped.discard(seq)
+        return list(ids)
+
+    def is_swapped(self, seq: int) -> bool:
+        if seq not in self.tables:
+            raise KVError("STATE", f"unknown sequence {seq}")
+        return seq in self.swapped
 
     def table(self, seq: int) -> List[int]:
         return list(self._seq(seq))
 
     def length(self, seq: int) -> int:
-        self._seq(seq)
+        if seq not in self.lengths:
+            raise KVError("STATE", f"unknown sequence {seq}")
         return self.lengths[seq]
 
     # -- helpers for tests --------------------------------------------------

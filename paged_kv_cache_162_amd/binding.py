@@ -68,11 +68,18 @@ _SIGS = {
     "kv_seq_block_table": (C.c_int, [vp, i64, i32, P_i32, P_i32]),
     "kv_seq_len": (i32, [vp, i64]),
     "kv_seq_pack_tables": (C.c_int, [vp, i32, P_i64, i32, P_i32, P_i32]),
+    "kv_seq_swap_out": (C.c_int, [vp, i64, i32, P_i32, P_i32]),
+    "kv_seq_swap_in": (C.c_int, [vp, i64, i32, P_i32, P_i32]),
+    "kv_seq_is_swapped": (i32, [vp, i64]),
     "kv_slot_mapping": (C.c_int, [vp, i32, i32, vp, vp, i32, i32, vp, vp]),
     "kv_reshape_and_cache": (C.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, C.c_int, vp]),
     "kv_append_tokens": (C.c_int, [vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32,
                                    C.c_int, vp, vp]),
     "kv_copy_blocks": (C.c_int, [C.POINTER(vp), C.POINTER(vp), i32, vp, i32, i32, C.c_size_t, vp]),
+    "kv_swap_out_blocks": (C.c_int, [C.POINTER(vp), C.POINTER(vp), i32, vp, i32, i32, C.c_size_t,
+                                     vp, vp]),
+    "kv_swap_in_blocks": (C.c_int, [C.POINTER(vp), C.POINTER(vp), i32, vp, i32, i32, C.c_size_t,
+                                    vp, vp]),
     "kv_paged_attention_plan": (C.c_int, [P_i32, i32, i32, P_i32, i32, P_i32]),
     "kv_paged_attention_workspace_bytes": (C.c_size_t, [i32, i32, i32, i32, i32, i32]),
     "kv_paged_attention_decode": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
@@ -207,6 +214,29 @@ def kv_seq_pack_tables(pool: int, seqs: Sequence[int], max_blocks: int) -> Tuple
     return tables, lens
 
 
+def _seq_ids(fn, where: str, pool: int, seq: int) -> np.ndarray:
+    """Call a (pool, seq, cap, ids, n) entry point, sizing ids from *n."""
+    n = i32()
+    cap = max(kv_seq_len(pool, seq), 0) + 1  # ceil(len / B) <= len + 1 blocks
+    out = np.zeros(cap, dtype=np.int32)
+    _check(fn(pool, seq, cap, _p32(out), C.byref(n)), where)
+    return out[:n.value]
+
+
+def kv_seq_swap_out(pool: int, seq: int) -> np.ndarray:
+    """Release `seq`'s blocks for a swap; returns the table to copy out."""
+    return _seq_ids(lib.kv_seq_swap_out, "kv_seq_swap_out", pool, seq)
+
+
+def kv_seq_swap_in(pool: int, seq: int) -> np.ndarray:
+    """Give a swapped-out `seq` fresh blocks; returns them in logical order."""
+    return _seq_ids(lib.kv_seq_swap_in, "kv_seq_swap_in", pool, seq)
+
+
+def kv_seq_is_swapped(pool: int, seq: int) -> int:
+    return int(lib.kv_seq_is_swapped(pool, seq))
+
+
 # ---------------------------------------------------------------------------
 # device entry points (torch tensors on the GPU)
 # ---------------------------------------------------------------------------
@@ -287,6 +317,38 @@ def kv_copy_blocks(k_pools: List, v_pools: List, pairs, num_blocks: int, block_b
     vv = (vp * max(L, 1))(*[_dev(t, "v_pools") for t in v_pools])
     _check(lib.kv_copy_blocks(kp, vv, L, _dev(pairs, "pairs", torch.int32), pairs.shape[0],
                               num_blocks, block_bytes, _stream(stream)), "kv_copy_blocks")
+
+
+def _swap(fn, where: str, k_pools: List, v_pools: List, block_ids, num_blocks: int,
+          block_bytes: int, host, stream) -> None:
+    torch = _torch()
+    L = len(k_pools)
+    if len(v_pools) != L:
+        raise KVError(KV_ERR_INVALID, where, "k_pools and v_pools differ in length")
+    if host.is_cuda or not host.is_contiguous():
+        raise KVError(KV_ERR_INVALID, where, "host buffer must be a contiguous CPU tensor")
+    kp = (vp * max(L, 1))(*[_dev(t, "k_pools") for t in k_pools])
+    vv = (vp * max(L, 1))(*[_dev(t, "v_pools") for t in v_pools])
+    n = block_ids.shape[0]
+    if host.numel() * host.element_size() < n * L * 2 * block_bytes:
+        raise KVError(KV_ERR_INVALID, where, "host buffer too small")
+    _check(fn(kp, vv, L, _dev(block_ids, "block_ids", torch.int32), n, num_blocks, block_bytes,
+              host.data_ptr(), _stream(stream)), where)
+
+
+def kv_swap_out_blocks(k_pools: List, v_pools: List, block_ids, num_blocks: int,
+                       block_bytes: int, host, stream=None) -> None:
+    """Copy blocks (all layers, K and V) into pinned `host`
+    [n][layers][2][block_bytes]; block_ids: device int32 tensor [n]."""
+    _swap(lib.kv_swap_out_blocks, "kv_swap_out_blocks", k_pools, v_pools, block_ids,
+          num_blocks, block_bytes, host, stream)
+
+
+def kv_swap_in_blocks(k_pools: List, v_pools: List, block_ids, num_blocks: int,
+                      block_bytes: int, host, stream=None) -> None:
+    """Copy pinned `host` [n][layers][2][block_bytes] back into blocks."""
+    _swap(lib.kv_swap_in_blocks, "kv_swap_in_blocks", k_pools, v_pools, block_ids,
+          num_blocks, block_bytes, host, stream)
 
 
 def kv_paged_attention_plan(context_lens_host, partition_size: int = 0) -> np.ndarray:

@@ -14,7 +14,10 @@
 // O(1), [4] "How it works"). Reference counts live in a flat int32 array
 // indexed by block ID ([1], "Memory sharing"). Each sequence keeps its block
 // table as a vector. Every mutating call validates first and mutates after,
-// so a failing call changes nothing ([3], "L3": all-or-nothing).
+// so a failing call changes nothing ([3], "L3": all-or-nothing). A sequence
+// can be swapped out under memory pressure ([3], "The allocation lifecycle";
+// [1], "Preemption"): its blocks are released and it keeps only its length
+// until it is swapped back in.
 
 #include <algorithm>
 #include <cstdio>
@@ -33,6 +36,7 @@ struct kv_pool {
   struct Seq {
     std::vector<int32_t> blocks;
     int32_t len = 0;
+    bool swapped = false;  // blocks released to the pool, contents on the host
   };
   std::unordered_map<int64_t, Seq> seqs;
   int64_t next_seq = 0;
@@ -211,6 +215,8 @@ kv_status kv_seq_fork(kv_pool_t* p, int64_t parent, int64_t* child_out) {
   auto it = p->seqs.find(parent);
   if (it == p->seqs.end()) return fail(KV_ERR_STATE, "kv_seq_fork: unknown sequence %lld",
                                        (long long)parent);
+  if (it->second.swapped)
+    return fail(KV_ERR_STATE, "kv_seq_fork: sequence %lld is swapped out", (long long)parent);
   kv_pool::Seq child = it->second;  // copy before the map may rehash
   // every block must still be held (a raw kv_block_free may have dropped it)
   kv_status st = check_held(p, (int32_t)child.blocks.size(), child.blocks.data(), false,
@@ -235,6 +241,8 @@ kv_status kv_seq_append(kv_pool_t* p, int64_t seq, int32_t n_tokens, int64_t* sl
     return fail(KV_ERR_STATE, "kv_seq_append: unknown sequence %lld", (long long)seq);
   kv_pool::Seq& s = it->second;
   *n_cow = 0;
+  if (s.swapped)
+    return fail(KV_ERR_STATE, "kv_seq_append: sequence %lld is swapped out", (long long)seq);
   if (n_tokens == 0) return KV_OK;
   const int64_t B = p->cfg.block_size;
   const int64_t t = s.len;
@@ -280,7 +288,7 @@ kv_status kv_seq_free(kv_pool_t* p, int64_t seq) {
   auto it = p->seqs.find(seq);
   if (it == p->seqs.end())
     return fail(KV_ERR_STATE, "kv_seq_free: unknown sequence %lld", (long long)seq);
-  const std::vector<int32_t>& bl = it->second.blocks;
+  const std::vector<int32_t>& bl = it->second.blocks;  // empty when swapped out
   kv_status st = check_held(p, (int32_t)bl.size(), bl.data(), true, "kv_seq_free");
   if (st != KV_OK) return st;
   decref_unchecked(p, (int32_t)bl.size(), bl.data());
@@ -295,6 +303,8 @@ kv_status kv_seq_block_table(const kv_pool_t* p, int64_t seq, int32_t cap, int32
   auto it = p->seqs.find(seq);
   if (it == p->seqs.end())
     return fail(KV_ERR_STATE, "kv_seq_block_table: unknown sequence %lld", (long long)seq);
+  if (it->second.swapped)
+    return fail(KV_ERR_STATE, "kv_seq_block_table: sequence %lld is swapped out", (long long)seq);
   const std::vector<int32_t>& bl = it->second.blocks;
   *n = (int32_t)bl.size();
   if (cap < (int32_t)bl.size() || (!ids && !bl.empty()))
@@ -320,6 +330,9 @@ kv_status kv_seq_pack_tables(const kv_pool_t* p, int32_t n_seqs, const int64_t* 
     if (it == p->seqs.end())
       return fail(KV_ERR_STATE, "kv_seq_pack_tables: unknown sequence %lld",
                   (long long)seqs[i]);
+    if (it->second.swapped)
+      return fail(KV_ERR_STATE, "kv_seq_pack_tables: sequence %lld is swapped out",
+                  (long long)seqs[i]);
     if ((int32_t)it->second.blocks.size() > max_blocks)
       return fail(KV_ERR_INVALID, "kv_seq_pack_tables: sequence %lld needs %zu > %d entries",
                   (long long)seqs[i], it->second.blocks.size(), max_blocks);
@@ -332,6 +345,63 @@ kv_status kv_seq_pack_tables(const kv_pool_t* p, int32_t n_seqs, const int64_t* 
     lens_out[i] = s.len;
   }
   return KV_OK;
+}
+
+kv_status kv_seq_swap_out(kv_pool_t* p, int64_t seq, int32_t cap, int32_t* ids_out,
+                          int32_t* n) {
+  pagedkv::clear_error();
+  if (!p || !n) return fail(KV_ERR_INVALID, "kv_seq_swap_out: null argument");
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end())
+    return fail(KV_ERR_STATE, "kv_seq_swap_out: unknown sequence %lld", (long long)seq);
+  kv_pool::Seq& s = it->second;
+  if (s.swapped)
+    return fail(KV_ERR_STATE, "kv_seq_swap_out: sequence %lld is already swapped out",
+                (long long)seq);
+  *n = (int32_t)s.blocks.size();
+  if (cap < *n || (!ids_out && *n > 0))
+    return fail(KV_ERR_INVALID, "kv_seq_swap_out: capacity %d < %d", cap, *n);
+  kv_status st = check_held(p, *n, s.blocks.data(), true, "kv_seq_swap_out");
+  if (st != KV_OK) return st;
+  if (*n > 0) std::memcpy(ids_out, s.blocks.data(), (size_t)*n * sizeof(int32_t));
+  decref_unchecked(p, *n, s.blocks.data());
+  s.blocks.clear();
+  s.swapped = true;
+  return KV_OK;
+}
+
+kv_status kv_seq_swap_in(kv_pool_t* p, int64_t seq, int32_t cap, int32_t* ids_out, int32_t* n) {
+  pagedkv::clear_error();
+  if (!p || !n) return fail(KV_ERR_INVALID, "kv_seq_swap_in: null argument");
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end())
+    return fail(KV_ERR_STATE, "kv_seq_swap_in: unknown sequence %lld", (long long)seq);
+  kv_pool::Seq& s = it->second;
+  if (!s.swapped)
+    return fail(KV_ERR_STATE, "kv_seq_swap_in: sequence %lld is not swapped out", (long long)seq);
+  const int64_t need = ceil_div(s.len, p->cfg.block_size);
+  *n = (int32_t)need;
+  if (cap < need || (!ids_out && need > 0))
+    return fail(KV_ERR_INVALID, "kv_seq_swap_in: capacity %d < %lld", cap, (long long)need);
+  if (need > (int64_t)p->free_stack.size())
+    return fail(KV_ERR_OOM, "kv_seq_swap_in: need %lld blocks, %zu free", (long long)need,
+                p->free_stack.size());
+  s.blocks.resize(need);
+  for (int64_t i = 0; i < need; ++i) {
+    const int32_t b = p->free_stack.back();
+    p->free_stack.pop_back();
+    p->refcount[b] = 1;
+    s.blocks[i] = b;
+    ids_out[i] = b;
+  }
+  s.swapped = false;
+  return KV_OK;
+}
+
+int32_t kv_seq_is_swapped(const kv_pool_t* p, int64_t seq) {
+  if (!p) return -1;
+  auto it = p->seqs.find(seq);
+  return it == p->seqs.end() ? -1 : (it->second.swapped ? 1 : 0);
 }
 
 const char* kv_last_error(void) { return pagedkv::g_last_error.c_str(); }

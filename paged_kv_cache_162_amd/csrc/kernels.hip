@@ -940,6 +940,31 @@ __global__ void copy_blocks_kernel(CopyPools pools, const int32_t* __restrict__ 
   for (int64_t i = threadIdx.x; i < block_u4; i += blockDim.x) d[i] = s[i];
 }
 
+// ============================================================================
+// Swap of whole blocks between the pools and host memory ([3], "The
+// allocation lifecycle": under memory pressure a sequence's blocks are moved
+// to host memory and brought back when it is readmitted; [1], "Preemption").
+// Host layout [n][num_layers][2][block_bytes]: K then V of every layer, so
+// one block's state for all layers is contiguous. The host buffer is pinned
+// memory that the kernel reads or writes directly over the bus; blockIdx.x =
+// list entry, blockIdx.y = layer within this launch's chunk, blockIdx.z = K
+// (0) or V (1). Entries outside the pool are skipped.
+// ============================================================================
+__global__ void swap_blocks_kernel(CopyPools pools, const int32_t* __restrict__ ids,
+                                   int32_t num_blocks, int64_t block_u4, uint4* host,
+                                   int32_t num_layers, int32_t layer0, int32_t to_host) {
+  const int32_t e = ids[blockIdx.x];
+  if (e < 0 || e >= num_blocks) return;
+  uint4* pool = (blockIdx.z == 0 ? pools.k[blockIdx.y] : pools.v[blockIdx.y]) + (int64_t)e * block_u4;
+  uint4* h = host + (((int64_t)blockIdx.x * num_layers + layer0 + blockIdx.y) * 2 + blockIdx.z) *
+                        block_u4;
+  if (to_host) {
+    for (int64_t i = threadIdx.x; i < block_u4; i += blockDim.x) h[i] = pool[i];
+  } else {
+    for (int64_t i = threadIdx.x; i < block_u4; i += blockDim.x) pool[i] = h[i];
+  }
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 kv_status launch_status(const char* who) {
@@ -1101,6 +1126,67 @@ kv_status kv_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num
     if (st != KV_OK) return st;
   }
   return KV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+kv_status swap_blocks(const char* who, void* const* k_pools, void* const* v_pools,
+                      int32_t num_layers, const int32_t* block_ids, int32_t n,
+                      int32_t num_blocks, size_t block_bytes, const void* host_buffer,
+                      bool to_host, hipStream_t stream) {
+  if (n < 0 || num_layers < 0 || num_layers > 256 || num_blocks <= 0)
+    return fail(KV_ERR_INVALID, "%s: bad sizes", who);
+  if (block_bytes == 0 || block_bytes % 16 != 0)
+    return fail(KV_ERR_INVALID, "%s: block_bytes must be a positive multiple of 16", who);
+  if (n == 0 || num_layers == 0) return KV_OK;
+  if (!k_pools || !v_pools || !block_ids || !host_buffer)
+    return fail(KV_ERR_INVALID, "%s: null pointer", who);
+  if (!aligned16(host_buffer)) return fail(KV_ERR_INVALID, "%s: host buffer must be 16-byte aligned", who);
+  for (int32_t i = 0; i < num_layers; ++i)
+    if (!k_pools[i] || !v_pools[i] || !aligned16(k_pools[i]) || !aligned16(v_pools[i]))
+      return fail(KV_ERR_INVALID, "%s: layer %d pool null or misaligned", who, i);
+  void* dev_host = nullptr;
+  if (hipHostGetDevicePointer(&dev_host, const_cast<void*>(host_buffer), 0) != hipSuccess ||
+      !dev_host) {
+    (void)hipGetLastError();  // leave no sticky error behind
+    return fail(KV_ERR_INVALID, "%s: host buffer is not pinned host memory", who);
+  }
+  for (int32_t l0 = 0; l0 < num_layers; l0 += kCopyLayers) {
+    CopyPools cp{};
+    const int32_t nl = num_layers - l0 < kCopyLayers ? num_layers - l0 : kCopyLayers;
+    for (int32_t i = 0; i < nl; ++i) {
+      cp.k[i] = static_cast<uint4*>(k_pools[l0 + i]);
+      cp.v[i] = static_cast<uint4*>(v_pools[l0 + i]);
+    }
+    hipLaunchKernelGGL(swap_blocks_kernel, dim3(n, nl, 2), dim3(256), 0, stream, cp, block_ids,
+                       num_blocks, (int64_t)(block_bytes / 16), static_cast<uint4*>(dev_host),
+                       num_layers, l0, to_host ? 1 : 0);
+    kv_status st = launch_status(who);
+    if (st != KV_OK) return st;
+  }
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status kv_swap_out_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,
+                             const int32_t* block_ids, int32_t n, int32_t num_blocks,
+                             size_t block_bytes, void* host_buffer, hipStream_t stream) {
+  pagedkv::clear_error();
+  return swap_blocks("kv_swap_out_blocks", k_pools, v_pools, num_layers, block_ids, n,
+                     num_blocks, block_bytes, host_buffer, true, stream);
+}
+
+kv_status kv_swap_in_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,
+                            const int32_t* block_ids, int32_t n, int32_t num_blocks,
+                            size_t block_bytes, const void* host_buffer, hipStream_t stream) {
+  pagedkv::clear_error();
+  return swap_blocks("kv_swap_in_blocks", k_pools, v_pools, num_layers, block_ids, n,
+                     num_blocks, block_bytes, host_buffer, false, stream);
 }
 
 size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_t num_kv_heads,

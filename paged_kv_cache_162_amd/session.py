@@ -78,6 +78,47 @@ class DecodeSession:
                 raise ValueError(op)
         return cows
 
+    # -- preemption by swapping ([3], "The allocation lifecycle", memory
+    # pressure; [1], "Preemption") ------------------------------------------
+    def swap_out(self, s: int):
+        """Move sequence s's blocks to a new pinned host buffer and release
+        them to the pool. The copy is queued on the current stream; device
+        writes into the released blocks that later calls queue on the same
+        stream run after it. Returns the buffer ([blocks][K, V][block bytes])
+        that swap_in needs."""
+        torch = self.torch
+        ids = kv.kv_seq_swap_out(self.pool, self.handles[s])
+        host = torch.empty(max(len(ids), 1) * 2 * self.block_bytes, dtype=torch.uint8,
+                           pin_memory=True)
+        if len(ids):
+            d_ids = torch.from_numpy(ids).to(self.device)
+            kv.kv_swap_out_blocks([self.k_pool], [self.v_pool], d_ids, self.NB, self.block_bytes,
+                                  host)
+            self._keep_until_done(host, d_ids)
+        return host
+
+    def swap_in(self, s: int, host) -> np.ndarray:
+        """Readmit sequence s: take fresh blocks (all or nothing) and copy the
+        swap_out buffer into them on the current stream. Returns the blocks."""
+        torch = self.torch
+        ids = kv.kv_seq_swap_in(self.pool, self.handles[s])
+        if len(ids):
+            d_ids = torch.from_numpy(ids).to(self.device)
+            kv.kv_swap_in_blocks([self.k_pool], [self.v_pool], d_ids, self.NB, self.block_bytes,
+                                 host)
+            self._keep_until_done(host, d_ids)
+        return ids
+
+    def _keep_until_done(self, *tensors) -> None:
+        # the kernels use raw pointers, which torch's allocators do not track:
+        # hold the buffers until an event behind the copy has completed
+        pending = getattr(self, "_pending", [])
+        pending = [(e, t) for e, t in pending if not e.query()]
+        ev = self.torch.cuda.Event()
+        ev.record()
+        pending.append((ev, tensors))
+        self._pending = pending
+
     def tables(self, seqs: Sequence[int], max_blocks: Optional[int] = None):
         ids = [self.handles[s] for s in seqs]
         if max_blocks is None:

@@ -107,6 +107,11 @@ def test_device_entry_points_validate_on_the_host(kv):
     assert lib.kv_append_tokens(None, 1, 1, None, None, 3, None, None, None, None, 4, 2, 64, 16,
                                 9, None, None) == kv.KV_ERR_UNSUPPORTED
     assert lib.kv_copy_blocks(None, None, 1, None, 1, 8, 24, None) == kv.KV_ERR_INVALID
+    for fn in (lib.kv_swap_out_blocks, lib.kv_swap_in_blocks):
+        assert fn(None, None, 1, None, 0, 8, 4096, None, None) == kv.KV_OK    # nothing to do
+        assert fn(None, None, 1, None, 2, 8, 4096, None, None) == kv.KV_ERR_INVALID
+        assert fn(None, None, 1, None, 2, 8, 24, None, None) == kv.KV_ERR_INVALID  # not x16
+        assert fn(None, None, 1, None, 2, 0, 4096, None, None) == kv.KV_ERR_INVALID
 
 
 def test_workspace_size_formula(kv):
@@ -164,7 +169,8 @@ def test_workload_tables_match_oracle_exactly(kv, cfg):
 
 
 ops_strategy = st.lists(
-    st.tuples(st.sampled_from(["create", "append", "fork", "free", "alloc", "incref", "decref"]),
+    st.tuples(st.sampled_from(["create", "append", "fork", "free", "alloc", "incref", "decref",
+                               "swap_out", "swap_in"]),
               st.integers(0, 9), st.integers(0, 37)),
     min_size=1, max_size=80)
 
@@ -184,7 +190,7 @@ def test_random_operation_sequences_match_oracle(kv, ops, seed):
             oerr = cerr = None
             ores = cres = None
             try:
-                if kind == "create" or (not live and kind in ("append", "fork", "free")):
+                if kind == "create" or (not live and kind in ("append", "fork", "free", "swap_out", "swap_in")):
                     ores = bm.create()
                 elif kind == "append":
                     ores = bm.append(live[who % len(live)][0], n)
@@ -198,10 +204,14 @@ def test_random_operation_sequences_match_oracle(kv, ops, seed):
                     bm.incref([who % NB])
                 elif kind == "decref":
                     bm.decref([who % NB])
+                elif kind == "swap_out":
+                    ores = bm.swap_out(live[who % len(live)][0])
+                elif kind == "swap_in":
+                    ores = bm.swap_in(live[who % len(live)][0])
             except oracle.KVError as e:
                 oerr = e.code
             try:
-                if kind == "create" or (not live and kind in ("append", "fork", "free")):
+                if kind == "create" or (not live and kind in ("append", "fork", "free", "swap_out", "swap_in")):
                     cres = kv.kv_seq_create(p)
                 elif kind == "append":
                     s, pr = kv.kv_seq_append(p, live[who % len(live)][1], n)
@@ -216,11 +226,15 @@ def test_random_operation_sequences_match_oracle(kv, ops, seed):
                     kv.kv_block_incref(p, [who % NB])
                 elif kind == "decref":
                     kv.kv_block_free(p, [who % NB])
+                elif kind == "swap_out":
+                    cres = list(kv.kv_seq_swap_out(p, live[who % len(live)][1]))
+                elif kind == "swap_in":
+                    cres = list(kv.kv_seq_swap_in(p, live[who % len(live)][1]))
             except kv.KVError as e:
                 cerr = e.code
             assert oerr == cerr, (kind, oerr, cerr)
             if oerr is None:
-                if kind == "create" or (not live and kind in ("append", "fork", "free")):
+                if kind == "create" or (not live and kind in ("append", "fork", "free", "swap_out", "swap_in")):
                     live.append((ores, cres))
                 elif kind == "fork":
                     live.append((ores, cres))
@@ -228,14 +242,21 @@ def test_random_operation_sequences_match_oracle(kv, ops, seed):
                     live.pop(who % len(live))
                 elif kind == "append":
                     assert (ores[0], ores[1]) == (cres[0], cres[1])
-                elif kind == "alloc":
+                elif kind in ("alloc", "swap_out", "swap_in"):
                     assert ores == cres
-                    raw.extend(ores)
+                    if kind == "alloc":
+                        raw.extend(ores)
             assert [kv.kv_block_refcount(p, b) for b in range(NB)] == bm.refcount
             assert kv.kv_num_free_blocks(p) == bm.num_free()
             for oh, chh in live:
-                assert list(kv.kv_seq_block_table(p, chh)) == bm.table(oh)
+                assert kv.kv_seq_is_swapped(p, chh) == int(bm.is_swapped(oh))
                 assert kv.kv_seq_len(p, chh) == bm.length(oh)
+                if bm.is_swapped(oh):
+                    with pytest.raises(kv.KVError) as e:
+                        kv.kv_seq_block_table(p, chh)
+                    assert e.value.status == kv.KV_ERR_STATE
+                else:
+                    assert list(kv.kv_seq_block_table(p, chh)) == bm.table(oh)
     finally:
         kv.kv_pool_destroy(p)
 

@@ -438,3 +438,41 @@ def test_planted_scale_and_transpose_mistakes_are_caught():
     assert np.abs(no_scale - ref).max() > 1e-6
     swapped = oracle.decode_attention(q, vp, kp, tab, cl, 0.35, "f32")  # K and V exchanged
     assert np.abs(swapped - ref).max() > 1e-6
+
+
+def test_swap_blocks_layout_and_round_trip():
+    # host layout [n][layer][K, V][block bytes]: element (i, l, kv, h, r, d)
+    # of the host copy is element (h, r, d) of block ids[i] in that pool
+    rng = np.random.default_rng(3)
+    L, NB, Hkv, B, D = 2, 6, 2, 4, 8
+    kp = [rng.integers(0, 2 ** 16, size=(NB, Hkv, B, D)).astype(np.uint16) for _ in range(L)]
+    vp = [rng.integers(0, 2 ** 16, size=(NB, Hkv, B, D)).astype(np.uint16) for _ in range(L)]
+    ids = [4, 1, 9, 2]                       # 9 lies outside the pool
+    host = oa.swap_out_blocks(kp, vp, ids)
+    view = host.view(np.uint16).reshape(len(ids), L, 2, Hkv, B, D)
+    for i, b in enumerate(ids):
+        for l in range(L):
+            for h in range(Hkv):
+                for r in range(B):
+                    for d in range(D):
+                        if b >= NB:
+                            assert view[i, l, 0, h, r, d] == 0 and view[i, l, 1, h, r, d] == 0
+                        else:
+                            assert view[i, l, 0, h, r, d] == kp[l][b, h, r, d]
+                            assert view[i, l, 1, h, r, d] == vp[l][b, h, r, d]
+    # swapping out of blocks a and back into blocks b is a block copy a -> b
+    k2 = [x.copy() for x in kp]
+    v2 = [x.copy() for x in vp]
+    oa.swap_in_blocks(k2, v2, [0, 5, 3, 3], host)
+    k3 = [x.copy() for x in kp]
+    v3 = [x.copy() for x in vp]
+    oa.copy_blocks(k3 + v3, [(4, 0), (1, 5), (2, 3)])
+    # entry 2 (block 9) is skipped on the way out, so block 3 receives entry 3
+    for a, b in zip(k2 + v2, k3 + v3):
+        assert np.array_equal(a, b)
+    # round trip into the same blocks changes nothing
+    k4 = [x.copy() for x in kp]
+    v4 = [x.copy() for x in vp]
+    oa.swap_in_blocks(k4, v4, [4, 1, 2], host[[0, 1, 3]])
+    for a, b in zip(k4 + v4, kp + vp):
+        assert np.array_equal(a, b)

@@ -210,7 +210,7 @@ def test_waste_per_sequence_is_bounded(cfg):
 # properties under random operation sequences
 # ---------------------------------------------------------------------------
 ops_strategy = st.lists(
-    st.tuples(st.sampled_from(["create", "append", "fork", "free"]),
+    st.tuples(st.sampled_from(["create", "append", "fork", "free", "swap_out", "swap_in"]),
               st.integers(0, 7), st.integers(0, 40)),
     min_size=1, max_size=60)
 
@@ -239,18 +239,30 @@ def test_refcount_conservation(ops):
                 live.append(bm.fork(live[who % len(live)]))
             elif kind == "free":
                 bm.free_seq(live.pop(who % len(live)))
+            elif kind == "swap_out":
+                s = live[who % len(live)]
+                t, length = bm.table(s), bm.length(s)
+                assert bm.swap_out(s) == t and bm.length(s) == length
+            elif kind == "swap_in":
+                s = live[who % len(live)]
+                ids = bm.swap_in(s)
+                assert len(ids) == -(-bm.length(s) // B)
+                assert all(bm.refcount[b] == 1 for b in ids)
         except KVError as e:
-            assert e.code == "OOM"
-        # recount references from the tables
+            assert e.code == "OOM" or (e.code == "STATE" and kind != "create")
+        # recount references from the tables; swapped-out sequences hold none
         count = [0] * NB
         for s in live:
+            if bm.is_swapped(s):
+                continue
             for b in bm.table(s):
                 count[b] += 1
         assert count == bm.refcount
         assert sorted(bm.free) == [b for b in range(NB) if count[b] == 0]
         # the last block of a sequence that others share is never written in place
         for s in live:
-            assert bm.length(s) <= len(bm.table(s)) * B
+            if not bm.is_swapped(s):
+                assert bm.length(s) <= len(bm.table(s)) * B
 
 
 def test_errors_change_nothing():
@@ -272,3 +284,94 @@ def test_errors_change_nothing():
     with pytest.raises(KVError) as e:
         bm.set_free_order([0, 1, 2, 3])
     assert e.value.code == "STATE"
+
+
+# ---------------------------------------------------------------------------
+# swap out / swap in under memory pressure ([3], "The allocation lifecycle";
+# [1], "Preemption")
+# ---------------------------------------------------------------------------
+def _store(bm, seq, slots, tokens, mem):
+    for sl, tok in zip(slots, tokens):
+        mem[sl] = tok
+
+
+def _logical(bm, seq, mem):
+    B = bm.block_size
+    t = bm.table(seq)
+    return [mem.get(t[p // B] * B + p % B) for p in range(bm.length(seq))]
+
+
+def test_swap_round_trip_preserves_logical_contents():
+    # A token-addressed model of the pool: slot -> token value. Swapping a
+    # sequence out copies its blocks to "host" by table order, the freed blocks
+    # are reused by another request, and swapping back in scatters the host
+    # copy into the new blocks; the logical token sequence must be unchanged.
+    B = 4
+    bm = BlockManager(6, B)
+    mem = {}
+    a = bm.create()
+    slots, _ = bm.append(a, 10)                  # 3 blocks, last one half full
+    _store(bm, a, slots, [100 + i for i in range(10)], mem)
+    before = _logical(bm, a, mem)
+    table = bm.swap_out(a)
+    assert table == [0, 1, 2] and bm.num_free() == 6 and bm.is_swapped(a)
+    host = [[mem.get(b * B + r) for r in range(B)] for b in table]
+    # memory pressure: another request takes (and overwrites) the freed blocks
+    c = bm.create()
+    cs, _ = bm.append(c, 12)
+    assert bm.table(c) == [0, 1, 2]              # LIFO: the same blocks, in order
+    _store(bm, c, cs, [-1] * 12, mem)
+    ids = bm.swap_in(a)
+    assert ids == [3, 4, 5] and bm.table(a) == ids
+    for b, rows in zip(ids, host):
+        for r, tok in enumerate(rows):
+            mem[b * B + r] = tok
+    assert _logical(bm, a, mem) == before
+    # decode can continue: the next token lands in the half-full last block
+    s, pairs = bm.append(a, 1)
+    assert s == [5 * B + 2] and pairs == []
+
+
+def test_swap_of_a_forked_sequence_returns_private_blocks():
+    bm = BlockManager(8, 4)
+    p = bm.create()
+    bm.append(p, 6)                               # blocks 0, 1
+    c = bm.fork(p)
+    assert bm.refcount[:2] == [2, 2]
+    assert bm.swap_out(c) == [0, 1]
+    assert bm.refcount[:2] == [1, 1] and bm.num_free() == 6   # still held by the parent
+    ids = bm.swap_in(c)
+    assert ids == [2, 3] and bm.refcount[:4] == [1, 1, 1, 1]
+    # the child's half-full last block is private now: no copy-on-write
+    _, pairs = bm.append(c, 1)
+    assert pairs == []
+
+
+def test_swap_errors_change_nothing():
+    bm = BlockManager(3, 4)
+    a = bm.create()
+    bm.append(a, 8)                               # blocks 0, 1
+    bm.swap_out(a)
+    b = bm.create()
+    bm.append(b, 9)                               # takes all three blocks
+    with pytest.raises(KVError) as e:
+        bm.swap_in(a)
+    assert e.value.code == "OOM" and bm.is_swapped(a) and bm.num_free() == 0
+    for op in (lambda: bm.append(a, 1), lambda: bm.fork(a), lambda: bm.table(a),
+               lambda: bm.swap_out(a), lambda: bm.swap_in(b)):
+        with pytest.raises(KVError) as e:
+            op()
+        assert e.value.code == "STATE"
+    assert bm.length(a) == 8
+    bm.free_seq(a)                                # a swapped-out sequence can be dropped
+    with pytest.raises(KVError) as e:
+        bm.is_swapped(a)
+    assert e.value.code == "STATE"
+    bm.free_seq(b)
+    assert bm.num_free() == 3 and bm.refcount == [0, 0, 0]
+
+
+def test_swap_of_an_empty_sequence():
+    bm = BlockManager(2, 4)
+    a = bm.create()
+    assert bm.swap_out(a) == [] and bm.swap_in(a) == []
