@@ -13,7 +13,9 @@ define, in float64 numpy:
                        to pin the first;
   * block_manager.py - the host block manager (free list, refcounts, lazy
                        per-token growth, fork, copy-on-write, free);
-  * sizes.py         - the KV-cache size formula and block/waste counts.
+  * sizes.py         - the KV-cache size formula and block/waste counts;
+  * fp8.py           - the E4M3 code, per-tensor scales and the quantising
+                       cache write of an fp8 KV cache.
 
 Every function is pinned by tests under tests/ against values the pages print,
 closed forms, invariants and brute force; none is "parity unpinned".
@@ -25,6 +27,7 @@ from .attention import (  # noqa: F401
     swap_in_blocks,
 )
 from .block_manager import BlockManager, KVError  # noqa: F401
+from . import fp8  # noqa: F401
 from .sizes import (  # noqa: F401
     kv_cache_bytes, blocks_for_tokens, waste_slots, decode_call_bytes,
 )

@@ -23,8 +23,9 @@ Readings where the pages leave a step open:
   * grouped-query attention maps query head hq to KV head hq // (Hq // Hkv);
   * a sequence of length 0 attends to nothing and its output is 0.
 
-Storage dtypes arrive as numpy arrays: float32, float16, or uint16 holding
-bf16 bit patterns. They are widened exactly to float64 before any arithmetic.
+Storage dtypes arrive as numpy arrays: float32, float16, uint16 holding bf16
+bit patterns, or uint8 holding fp8 E4M3 codes (see oracle/fp8.py). They are
+widened exactly to float64 before any arithmetic.
 """
 from __future__ import annotations
 
@@ -44,6 +45,9 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
         return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     if dtype in ("f32", "f16"):
         return x.astype(np.float64)
+    if dtype == "e4m3":
+        from .fp8 import e4m3_decode
+        return e4m3_decode(x)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -100,7 +104,9 @@ def _kv_head(hq: int, Hq: int, Hkv: int) -> int:
 
 def decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale: float,
                      dtype: str, block_size: int = 16,
-                     pairs: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+                     pairs: Optional[Iterable[Tuple[int, int]]] = None,
+                     kv_dtype: Optional[str] = None, k_scale: float = 1.0,
+                     v_scale: float = 1.0) -> np.ndarray:
     """Decode attention over a paged cache, as the plain definition.
 
     [1] ("The PagedAttention kernel") states that walking the block table
@@ -110,7 +116,9 @@ def decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale: float
     w_j = exp(z_j - max z), z_j = scale * <q[s, hq], K[j]>, j < ctx.
 
     Returns float64 [S, Hq, D]. With `pairs`, only those (s, hq) entries are
-    computed and the rest stay NaN.
+    computed and the rest stay NaN. `kv_dtype` is the pools' storage type when
+    it differs from the query's (an fp8 cache, "e4m3"); the cache then holds
+    code value times `k_scale` (K) or `v_scale` (V).
     """
     q = widen(q, dtype)
     S, Hq, D = q.shape
@@ -127,8 +135,12 @@ def decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale: float
         if ctx == 0:
             out[s, heads] = 0.0
             continue
-        Kc = widen(gather_sequence(k_pool, block_tables[s], ctx, block_size), dtype)
-        Vc = widen(gather_sequence(v_pool, block_tables[s], ctx, block_size), dtype)
+        kd = kv_dtype or dtype
+        Kc = widen(gather_sequence(k_pool, block_tables[s], ctx, block_size), kd)
+        Vc = widen(gather_sequence(v_pool, block_tables[s], ctx, block_size), kd)
+        if kv_dtype is not None:
+            Kc = Kc * float(np.float32(k_scale))
+            Vc = Vc * float(np.float32(v_scale))
         for hq in heads:
             h = _kv_head(hq, Hq, Hkv)
             z = sc * (Kc[:, h, :] @ q[s, hq])

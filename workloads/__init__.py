@@ -22,6 +22,11 @@ Workload recipe (all seeded):
     with round-to-nearest-even; unused slots therefore hold finite data unless
     a test poisons them;
   * the query and the new token's K/V are N(0,1), rounded the same way;
+  * an fp8 cache (workload 7) holds random E4M3 codes instead: each byte has
+    a uniform sign bit, an exponent field uniform in 0..9 (field 0 gives the
+    subnormals and zero) and a uniform mantissa, i.e. magnitudes up to 7.5,
+    read with a per-pool scale of 1/4; the new token's K/V stay 16-bit
+    N(0,1) values (the cache write quantises them);
   * an operation script (create / append / fork) that builds the sequences.
 Heavy-tailed lengths follow the shape [2] describes for production traffic
 ("The Fragmentation Problem"): many short requests and a long tail. The
@@ -44,8 +49,8 @@ __all__ = [
 
 # Storage dtypes. bf16 is held as raw uint16 bit patterns on the host side
 # because numpy has no bfloat16 type.
-NP_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+NP_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "e4m3": np.uint8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
 
 
 def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -90,6 +95,13 @@ class WorkloadSpec:
     # tokens each sequence appends after the fork
     shared_prefix: int = 0
     tail: int = 0
+    # cache storage when it differs from `dtype` (the query's type): "e4m3",
+    # with one scale per pool
+    kv_dtype: str = ""
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    # default seed taken from this workload number (same lengths and queries)
+    seed_cfg: int = 0
     description: str = ""
 
     @property
@@ -104,6 +116,14 @@ class WorkloadSpec:
     @property
     def elem_bytes(self) -> int:
         return ELEM_BYTES[self.dtype]
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        return ELEM_BYTES[self.cache_dtype]
 
 
 SPECS = {
@@ -130,6 +150,11 @@ SPECS = {
                     description="as the prefix-share workload but forked inside "
                                 "a block (2056 shared tokens), so the first "
                                 "write of each fork copies the partial block"),
+    7: WorkloadSpec(7, "llama70b-gqa-fp8", S=128, Hq=64, Hkv=8, D=128, dtype="bf16",
+                    kv_dtype="e4m3", k_scale=0.25, v_scale=0.25, seed_cfg=3,
+                    description="the llama70b-gqa-bf16 workload (same lengths, "
+                                "queries and new tokens) over an fp8 E4M3 "
+                                "cache with per-pool scales"),
 }
 
 
@@ -177,12 +202,26 @@ def _normal(rng: np.random.Generator, shape, dtype: str, chunk=1 << 26) -> np.nd
     return out.reshape(shape)
 
 
+def _e4m3_codes(rng: np.random.Generator, shape, chunk=1 << 26) -> np.ndarray:
+    """Random E4M3 bytes: uniform sign, exponent field uniform in 0..9,
+    uniform mantissa (no NaN code can occur)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint8)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        sign = rng.integers(0, 2, e - s, dtype=np.uint8)
+        expo = rng.integers(0, 10, e - s, dtype=np.uint8)
+        mant = rng.integers(0, 8, e - s, dtype=np.uint8)
+        out[s:e] = (sign << 7) | (expo << 3) | mant
+    return out.reshape(shape)
+
+
 def _context_lengths(sp: WorkloadSpec, rng: np.random.Generator) -> np.ndarray:
     if sp.cfg == 1:
         return np.array([5, 16, 17, 40], dtype=np.int32)
     if sp.cfg == 2:
         return rng.integers(128, 2048, size=sp.S, endpoint=True).astype(np.int32)
-    if sp.cfg == 3:
+    if sp.cfg in (3, 7):
         x = np.exp(rng.normal(math.log(512.0), 0.86, size=sp.S))
         return np.clip(np.rint(x), 16, 8192).astype(np.int32)
     if sp.cfg == 4:
@@ -199,7 +238,7 @@ def _pool_blocks(sp: WorkloadSpec, lens: np.ndarray) -> int:
         return 32
     if sp.cfg == 2:
         return 8192 * 16 // B  # the worst case, 64 sequences of 2048 tokens
-    if sp.cfg == 3:
+    if sp.cfg in (3, 7):
         need = int(sum(-(-int(t) // B) for t in lens))
         return int(math.ceil(1.1 * need))
     if sp.cfg == 4:
@@ -227,10 +266,10 @@ def make_workload(cfg: int, seed: Optional[int] = None, *, with_values: bool = T
         # new tokens; the pool is sized by the same rule for the new block size
         sp = dataclasses.replace(sp, block_size=block_size)
     if S is not None and S != sp.S:
-        if cfg not in (2, 3, 4):
-            raise ValueError("only workloads 2-4 may be truncated")
+        if cfg not in (2, 3, 4, 7):
+            raise ValueError("only workloads 2-4 and 7 may be truncated")
         sp = dataclasses.replace(sp, S=S)
-    ss = np.random.SeedSequence(162_000 + cfg if seed is None else seed)
+    ss = np.random.SeedSequence(162_000 + (sp.seed_cfg or cfg) if seed is None else seed)
     r_len, r_perm, r_q, r_k, r_v, r_new = [np.random.default_rng(s) for s in ss.spawn(6)]
 
     lens = _context_lengths(sp, r_len)
@@ -259,8 +298,12 @@ def make_workload(cfg: int, seed: Optional[int] = None, *, with_values: bool = T
     Hkv, D, B = sp.Hkv, sp.D, sp.block_size
     if with_values:
         q = _normal(r_q, (sp.S, sp.Hq, D), sp.dtype)
-        k_pool = _normal(r_k, (NB, Hkv, B, D), sp.dtype)
-        v_pool = _normal(r_v, (NB, Hkv, B, D), sp.dtype)
+        if sp.kv_dtype == "e4m3":
+            k_pool = _e4m3_codes(r_k, (NB, Hkv, B, D))
+            v_pool = _e4m3_codes(r_v, (NB, Hkv, B, D))
+        else:
+            k_pool = _normal(r_k, (NB, Hkv, B, D), sp.dtype)
+            v_pool = _normal(r_v, (NB, Hkv, B, D), sp.dtype)
         k_new = _normal(r_new, (sp.S, Hkv, D), sp.dtype)
         v_new = _normal(r_new, (sp.S, Hkv, D), sp.dtype)
         tail_k = tail_v = None
@@ -269,7 +312,8 @@ def make_workload(cfg: int, seed: Optional[int] = None, *, with_values: bool = T
             tail_v = _normal(r_new, (sp.S, sp.tail, Hkv, D), sp.dtype)
     else:
         z = np.zeros(0, dtype=NP_STORAGE[sp.dtype])
-        q = k_pool = v_pool = k_new = v_new = z
+        q = k_new = v_new = z
+        k_pool = v_pool = np.zeros(0, dtype=NP_STORAGE[sp.cache_dtype])
         tail_k = tail_v = None
     return Workload(spec=sp, context_lens=lens.astype(np.int32), num_blocks=NB,
                     free_order=free_order, setup_ops=setup, step_ops=step,
