@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=3, help="workload number 1-6")
+    ap.add_argument("--workload", type=int, default=3, help="workload number 1-7")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--block-size", type=int, default=16, help="tokens per KV block (8, 16 or 32)")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas to rotate (0 = auto)")
@@ -159,11 +159,13 @@ def kv_bytes(lens, Hkv, D, eb):
     return int(np.sum(lens.astype(np.int64))) * Hkv * D * eb * 2
 
 
-def decode_alg_bytes(lens, S, Hq, Hkv, D, eb, B=16):
-    """Algorithmic bytes of one decode-attention call: live K/V, queries, fp32
-    outputs, live block-table entries, lengths."""
+def decode_alg_bytes(lens, S, Hq, Hkv, D, eb, B=16, kv_eb=None):
+    """Algorithmic bytes of one decode-attention call: live K/V (kv_eb bytes
+    per element, default eb), queries, fp32 outputs, live block-table entries,
+    lengths."""
     nb = int(np.sum((lens.astype(np.int64) + B - 1) // B))
-    return kv_bytes(lens, Hkv, D, eb) + S * Hq * D * eb + S * Hq * D * 4 + nb * 4 + S * 4
+    kv_eb = eb if kv_eb is None else kv_eb
+    return kv_bytes(lens, Hkv, D, kv_eb) + S * Hq * D * eb + S * Hq * D * 4 + nb * 4 + S * 4
 
 
 def cpu_baseline(w, seconds):
@@ -181,12 +183,17 @@ def cpu_baseline(w, seconds):
     with threadpool_limits(limits=1):
         while passes < 50 and (passes == 0 or t_total < seconds):
             t0 = time.perf_counter()
-            oracle.decode_attention(w.q, w.k_pool, w.v_pool, tables, lens, sp.scale, sp.dtype,
-                                    block_size=sp.block_size)
+            if sp.kv_dtype:
+                oracle.decode_attention(w.q, w.k_pool, w.v_pool, tables, lens, sp.scale, sp.dtype,
+                                        block_size=sp.block_size, kv_dtype=sp.kv_dtype,
+                                        k_scale=sp.k_scale, v_scale=sp.v_scale)
+            else:
+                oracle.decode_attention(w.q, w.k_pool, w.v_pool, tables, lens, sp.scale, sp.dtype,
+                                        block_size=sp.block_size)
             t_total += time.perf_counter() - t0
             passes += 1
     per = t_total / passes
-    kvb = kv_bytes(lens, sp.Hkv, sp.D, sp.elem_bytes)
+    kvb = kv_bytes(lens, sp.Hkv, sp.D, sp.kv_elem_bytes)
     return {"value": round(kvb / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seqs_per_s": round(sp.S / per, 2), "seconds_per_pass": round(per, 3),
             "sample": f"the whole workload ({sp.S} sequences x {sp.Hq} query heads), {passes} "
@@ -283,10 +290,10 @@ def main():
     print(f"[bench] workload {sp.name}: S={sp.S} Hq={sp.Hq} Hkv={sp.Hkv} D={sp.D} {dt} "
           f"blocks={w.num_blocks} sum_ctx={int(w.context_lens.sum())} max_ctx={int(w.context_lens.max())}",
           file=sys.stderr, flush=True)
-    kp, vp = to_dev(w.k_pool, dt), to_dev(w.v_pool, dt)
+    kp, vp = to_dev(w.k_pool, sp.cache_dtype), to_dev(w.v_pool, sp.cache_dtype)
     sess = DecodeSession(k_pool=kp, v_pool=vp, num_q_heads=sp.Hq, free_order=w.free_order,
                          partition_size=args.partition, use_plan=not args.no_plan,
-                         fused=not args.unfused)
+                         fused=not args.unfused, k_scale=sp.k_scale, v_scale=sp.v_scale)
     values = {}
     if w.tail_k is not None:
         values = {s: (to_dev(w.tail_k[s], dt), to_dev(w.tail_v[s], dt)) for s in range(sp.S)}
@@ -365,8 +372,9 @@ def main():
     torch.cuda.synchronize()
     warm_ms = w0.elapsed_time(w1) / K
 
-    kvb = kv_bytes(lens, sp.Hkv, sp.D, sp.elem_bytes)
-    alg = decode_alg_bytes(lens, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes, args.block_size)
+    kvb = kv_bytes(lens, sp.Hkv, sp.D, sp.kv_elem_bytes)
+    alg = decode_alg_bytes(lens, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes, args.block_size,
+                           sp.kv_elem_bytes)
     value = kvb / (step_ms * 1e-3) / 1e9
     achieved = alg / (dec_avg * 1e-3) / 1e9
     traffic = None
@@ -397,6 +405,7 @@ def main():
             "sum_context": int(lens.sum()), "max_context": int(lens.max()),
             "kv_bytes_per_step": kvb, "replicas_rotated": R, "parallelism": "single GPU",
             "fused_cache_write": not args.unfused, "hip_graph": bool(args.graph),
+            "kv_cache_dtype": sp.cache_dtype,
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(sp.S / (step_ms * 1e-3), 1),
@@ -407,9 +416,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": ("kv_paged_attention_decode_append call: decode kernel + split-K merge"
+                     "kernel": ("kv_paged_attention_decode_append%s call: decode kernel + split-K merge"
                                 if not args.unfused else
-                                "kv_paged_attention_decode call: decode kernel + split-K merge"),
+                                "kv_paged_attention_decode%s call: decode kernel + split-K merge")
+                               % ("_fp8" if sp.kv_dtype else ""),
                      "alg_bytes_per_launch": alg},
     }
     if not args.no_cpu_baseline:

@@ -59,7 +59,12 @@ typedef enum {
   KV_ERR_STATE = -5        /* wrong object state: unknown sequence, block not held */
 } kv_status;
 
-typedef enum { KV_F32 = 0, KV_F16 = 1, KV_BF16 = 2 } kv_dtype;
+/* KV_FP8_E4M3: one byte per element, the OCP E4M3 float (sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits, no infinities, 0x7F/0xFF NaN, largest
+ * magnitude 448). It describes a pool's storage only (kv_pool_create,
+ * kv_quantize_fp8 output); the _fp8 device entry points below read and write
+ * such pools, with the query / new-token type given separately. */
+typedef enum { KV_F32 = 0, KV_F16 = 1, KV_BF16 = 2, KV_FP8_E4M3 = 3 } kv_dtype;
 
 typedef struct {
   int32_t num_blocks;   /* physical blocks in the pool, > 0 */
@@ -353,6 +358,69 @@ kv_status kv_paged_attention_decode_append(
     int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
     int32_t max_context_len, const int32_t* work_items, int32_t n_items, void* workspace,
     size_t ws_bytes, int64_t* slots, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * fp8 KV cache ([1], "How does this relate to quantization?": K and V stored
+ * in 8 bits instead of 16 halve the bytes per element and compose with
+ * paging; [3], the bytes_per_element term of the KV-size formula).
+ *
+ * Scheme (the pages fix none): the pools hold KV_FP8_E4M3 codes, laid out as
+ * the 16-bit pools ([num_blocks][num_kv_heads][block_size][head_dim], one
+ * byte per element). Each pool has one fp32 scale: a stored code c stands for
+ * value(c) * scale. Writing x (f16 or bf16) stores the E4M3 code of
+ * fp32(x / scale) - the fp32 quotient rounded to nearest even, then rounded
+ * to the nearest E4M3 value with ties to the even code; magnitudes beyond 448
+ * (and infinities) saturate to +-448, NaN is stored as 0x7F. Scales must be
+ * finite and > 0 (else KV_ERR_INVALID).
+ * ------------------------------------------------------------------------- */
+
+/* As kv_reshape_and_cache, but k_new / v_new ([n][num_kv_heads][head_dim]
+ * of `dtype`, f16 or bf16) are stored quantised with k_scale / v_scale into
+ * fp8 pools. head_dim must be a multiple of 16; pools 8-byte aligned. */
+kv_status kv_reshape_and_cache_fp8(const void* k_new, const void* v_new, void* k_pool,
+                                   void* v_pool, const int64_t* slots, int32_t n,
+                                   int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, kv_dtype dtype, float k_scale,
+                                   float v_scale, hipStream_t stream);
+
+/* dst[i] = E4M3 code of src[i] / scale for n elements (a multiple of 8) of
+ * `dtype` (f16 or bf16); device pointers, src 16-byte and dst 8-byte
+ * aligned. The same rounding as the cache writes; e.g. to convert a 16-bit
+ * cache into an fp8 one. */
+kv_status kv_quantize_fp8(const void* src, void* dst, int64_t n, kv_dtype dtype, float scale,
+                          hipStream_t stream);
+
+/* kv_paged_attention_decode over fp8 pools: the attention of the cache
+ * values value(code) * k_scale (K) and value(code) * v_scale (V), i.e. the
+ * same definition on the dequantised cache. q is [S][num_q_heads][head_dim]
+ * of `dtype` (f16 or bf16); head_dim 128; group sizes 1..16; block sizes 8,
+ * 16, 32. Each code is widened exactly to the query's type and the MFMA path
+ * runs as for 16-bit pools; k_scale is folded into the score scale and
+ * v_scale into the output. Other arguments, checks and workspace as for
+ * kv_paged_attention_decode. */
+kv_status kv_paged_attention_decode_fp8(float* out, const void* q, const void* k_pool,
+                                        const void* v_pool, const int32_t* block_tables,
+                                        int32_t max_blocks, const int32_t* context_lens,
+                                        int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                        float scale, kv_dtype dtype, float k_scale,
+                                        float v_scale, int32_t partition_size,
+                                        int32_t max_context_len, const int32_t* work_items,
+                                        int32_t n_items, void* workspace, size_t ws_bytes,
+                                        hipStream_t stream);
+
+/* kv_paged_attention_decode_append over fp8 pools: the new token's K and V
+ * (of `dtype`) are quantised as kv_reshape_and_cache_fp8 does and written at
+ * position t-1, then attention runs as kv_paged_attention_decode_fp8. On
+ * valid inputs, outputs, pools and slots are bit-identical to kv_slot_mapping
+ * + kv_reshape_and_cache_fp8 + kv_paged_attention_decode_fp8. */
+kv_status kv_paged_attention_decode_append_fp8(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t S,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, float scale, kv_dtype dtype, float k_scale, float v_scale,
+    int32_t partition_size, int32_t max_context_len, const int32_t* work_items, int32_t n_items,
+    void* workspace, size_t ws_bytes, int64_t* slots, hipStream_t stream);
 
 /* Message describing the calling thread's last error ("" if none). */
 const char* kv_last_error(void);

@@ -19,9 +19,9 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 KV_OK, KV_ERR_INVALID, KV_ERR_OOM, KV_ERR_UNSUPPORTED, KV_ERR_HIP, KV_ERR_STATE = 0, -1, -2, -3, -4, -5
 STATUS_NAMES = {0: "OK", -1: "INVALID", -2: "OOM", -3: "UNSUPPORTED", -4: "HIP", -5: "STATE"}
-KV_F32, KV_F16, KV_BF16 = 0, 1, 2
-DTYPE_CODES = {"f32": KV_F32, "f16": KV_F16, "bf16": KV_BF16}
-ELEM_BYTES = {KV_F32: 4, KV_F16: 2, KV_BF16: 2}
+KV_F32, KV_F16, KV_BF16, KV_FP8_E4M3 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": KV_F32, "f16": KV_F16, "bf16": KV_BF16, "e4m3": KV_FP8_E4M3}
+ELEM_BYTES = {KV_F32: 4, KV_F16: 2, KV_BF16: 2, KV_FP8_E4M3: 1}
 
 
 class KVError(RuntimeError):
@@ -88,6 +88,16 @@ _SIGS = {
     "kv_paged_attention_decode_append": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
                                                    i32, i32, i32, i32, f32, C.c_int, i32, i32,
                                                    vp, i32, vp, C.c_size_t, vp, vp]),
+    "kv_reshape_and_cache_fp8": (C.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, C.c_int,
+                                           f32, f32, vp]),
+    "kv_quantize_fp8": (C.c_int, [vp, vp, i64, C.c_int, f32, vp]),
+    "kv_paged_attention_decode_fp8": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
+                                                i32, i32, f32, C.c_int, f32, f32, i32, i32, vp,
+                                                i32, vp, C.c_size_t, vp]),
+    "kv_paged_attention_decode_append_fp8": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32,
+                                                       i32, i32, i32, i32, i32, f32, C.c_int, f32,
+                                                       f32, i32, i32, vp, i32, vp, C.c_size_t, vp,
+                                                       vp]),
     "kv_last_error": (C.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -247,7 +257,8 @@ def _torch():
 
 def dtype_code(t) -> int:
     torch = _torch()
-    return {torch.float32: KV_F32, torch.float16: KV_F16, torch.bfloat16: KV_BF16}[t.dtype]
+    return {torch.float32: KV_F32, torch.float16: KV_F16, torch.bfloat16: KV_BF16,
+            torch.uint8: KV_FP8_E4M3}[t.dtype]
 
 
 def _dev(t, name: str, dtype=None):
@@ -421,3 +432,87 @@ def kv_paged_attention_decode_append(out, q, k_new, v_new, k_pool, v_pool, block
         0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
         _dev(slots, "slots", torch.int64), _stream(stream)),
         "kv_paged_attention_decode_append")
+
+
+# ---------------------------------------------------------------------------
+# fp8 (E4M3) cache: pools are uint8 tensors of codes, one scale per pool
+# ---------------------------------------------------------------------------
+def _fp8_pools(where, k_pool, v_pool):
+    torch = _torch()
+    if k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8 or v_pool.shape != k_pool.shape:
+        raise KVError(KV_ERR_INVALID, where, "fp8 pools must be matching uint8 tensors")
+    return k_pool.shape
+
+
+def kv_reshape_and_cache_fp8(k_new, v_new, k_pool, v_pool, slots, k_scale: float,
+                             v_scale: float, stream=None) -> None:
+    """k_new/v_new f16/bf16 [n, Hkv, D] -> uint8 pools [NB, Hkv, B, D], quantised."""
+    torch = _torch()
+    NB, Hkv, B, D = _fp8_pools("kv_reshape_and_cache_fp8", k_pool, v_pool)
+    if k_new.shape != v_new.shape or k_new.shape[1:] != (Hkv, D) or k_new.dtype != v_new.dtype:
+        raise KVError(KV_ERR_INVALID, "kv_reshape_and_cache_fp8", "shape/dtype mismatch")
+    _check(lib.kv_reshape_and_cache_fp8(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(slots, "slots", torch.int64), k_new.shape[0], NB, Hkv, D, B, dtype_code(k_new),
+        float(k_scale), float(v_scale), _stream(stream)), "kv_reshape_and_cache_fp8")
+
+
+def kv_quantize_fp8(src, dst, scale: float, stream=None) -> None:
+    """dst uint8 (same number of elements) = E4M3 codes of src (f16/bf16) / scale."""
+    torch = _torch()
+    if dst.dtype != torch.uint8 or dst.numel() != src.numel():
+        raise KVError(KV_ERR_INVALID, "kv_quantize_fp8", "dst must be uint8 with src's size")
+    _check(lib.kv_quantize_fp8(_dev(src, "src"), _dev(dst, "dst"), src.numel(), dtype_code(src),
+                               float(scale), _stream(stream)), "kv_quantize_fp8")
+
+
+def kv_paged_attention_decode_fp8(out, q, k_pool, v_pool, block_tables, context_lens,
+                                  scale: float, k_scale: float, v_scale: float,
+                                  max_context_len: int, workspace=None, partition_size: int = 0,
+                                  work_items=None, stream=None) -> None:
+    """kv_paged_attention_decode over uint8 E4M3 pools with per-pool scales; q f16/bf16."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = _fp8_pools("kv_paged_attention_decode_fp8", k_pool, v_pool)
+    if D2 != D or tuple(out.shape) != (S, Hq, D) or block_tables.shape[0] != S \
+            or context_lens.numel() != S:
+        raise KVError(KV_ERR_INVALID, "kv_paged_attention_decode_fp8", "shape mismatch")
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                         workspace.numel() * workspace.element_size())
+    _check(lib.kv_paged_attention_decode_fp8(
+        _dev(out, "out", torch.float32), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, B, NB, float(scale),
+        dtype_code(q), float(k_scale), float(v_scale), partition_size, max_context_len,
+        None if work_items is None else _dev(work_items, "work_items", torch.int32),
+        0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes, _stream(stream)),
+        "kv_paged_attention_decode_fp8")
+
+
+def kv_paged_attention_decode_append_fp8(out, q, k_new, v_new, k_pool, v_pool, block_tables,
+                                         context_lens, scale: float, k_scale: float,
+                                         v_scale: float, max_context_len: int, slots,
+                                         workspace=None, partition_size: int = 0,
+                                         work_items=None, stream=None) -> None:
+    """Fused decode step over uint8 E4M3 pools: the new token is quantised and written at
+    position context_lens[s]-1, then attention as kv_paged_attention_decode_fp8."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = _fp8_pools("kv_paged_attention_decode_append_fp8", k_pool, v_pool)
+    if D2 != D or tuple(out.shape) != (S, Hq, D) or block_tables.shape[0] != S \
+            or context_lens.numel() != S or tuple(k_new.shape) != (S, Hkv, D) \
+            or k_new.shape != v_new.shape or k_new.dtype != q.dtype or v_new.dtype != q.dtype \
+            or slots.numel() != S:
+        raise KVError(KV_ERR_INVALID, "kv_paged_attention_decode_append_fp8", "shape/dtype mismatch")
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                         workspace.numel() * workspace.element_size())
+    _check(lib.kv_paged_attention_decode_append_fp8(
+        _dev(out, "out", torch.float32), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, B, NB, float(scale),
+        dtype_code(q), float(k_scale), float(v_scale), partition_size, max_context_len,
+        None if work_items is None else _dev(work_items, "work_items", torch.int32),
+        0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
+        _dev(slots, "slots", torch.int64), _stream(stream)),
+        "kv_paged_attention_decode_append_fp8")

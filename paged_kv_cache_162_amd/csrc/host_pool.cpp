@@ -63,6 +63,7 @@ size_t dtype_bytes(kv_dtype dt) {
     case KV_F32: return 4;
     case KV_F16: return 2;
     case KV_BF16: return 2;
+    case KV_FP8_E4M3: return 1;
   }
   return 0;
 }

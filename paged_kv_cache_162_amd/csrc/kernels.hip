@@ -31,6 +31,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "../../include/pagedkv.h"
 #include "status.h"
@@ -55,6 +56,12 @@ constexpr int kStageStride = 132;  // floats per head row in LDS (128 + 4 agains
 #define PAGEDKV_DECODE_RING 3
 #endif
 constexpr int kDecodeRing = PAGEDKV_DECODE_RING;  // K/V blocks in flight per wave (MFMA decode)
+#ifndef PAGEDKV_DECODE_RING8
+#define PAGEDKV_DECODE_RING8 6
+#endif
+// fp8 cache: a tile holds half the bytes, so twice the tiles give the same
+// bytes in flight for the same registers
+constexpr int kDecodeRing8 = PAGEDKV_DECODE_RING8;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
@@ -121,7 +128,9 @@ struct DecodeParams {
   void* v_pool_w;
   int64_t* slots;
   int32_t max_blocks, S, Hq, Hkv, G, num_blocks, block_size, part_tokens, nparts, n_units;
-  float scale_log2;
+  float scale_log2;  // scale * log2(e), times the K scale for an fp8 cache
+  // fp8 cache: the per-pool scales (stored value = code value * scale)
+  float k_scale, v_scale;
 };
 
 // Wave u of the grid (one wave per workgroup) processes work unit u: one
@@ -643,11 +652,59 @@ __device__ __forceinline__ float column_sum(float x) {
   return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
-template <int DT, bool SPLITCOL, int RING, int BS>
+// ---- fp8 (OCP E4M3) cache ---------------------------------------------------
+// Four E4M3 codes (one dword, byte 0 first) as four 16-bit values of the
+// query's type, in the same order. Every E4M3 value is exact in f16 and bf16;
+// the gfx950 conversion takes a power-of-two scale, here 2^0.
+template <int DT>
+__device__ __forceinline__ uint2 e4m3x4_widen(uint32_t w) {
+  if constexpr (DT == KV_BF16)
+    return make_uint2(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)));
+  else
+    return make_uint2(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)));
+}
+template <int DT>
+__device__ __forceinline__ uint4 e4m3x8_widen(uint32_t a, uint32_t b) {
+  const uint2 lo = e4m3x4_widen<DT>(a), hi = e4m3x4_widen<DT>(b);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// The E4M3 code of x / scale: the quotient rounded to nearest even in fp32,
+// then to the nearest E4M3 value (ties to even); magnitudes past 448 and
+// infinities saturate to 448, NaN becomes 0x7F. The hardware conversion
+// rounds to nearest even; the clamp before it gives the saturation. It
+// writes every NaN as 0xFF, so the sign bit of a NaN byte is cleared after.
+__device__ __forceinline__ float e4m3_operand(float x, float scale) {
+  const float y = __fdiv_rn(x, scale);
+  return y != y ? y : fminf(fmaxf(y, -448.0f), 448.0f);
+}
+__device__ __forceinline__ uint32_t e4m3x4_pack(float a, float b, float c, float d, float scale) {
+  const float ya = e4m3_operand(a, scale), yb = e4m3_operand(b, scale);
+  const float yc = e4m3_operand(c, scale), yd = e4m3_operand(d, scale);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ya, yb, 0, false);
+  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(yc, yd, lo, true);
+  const uint32_t nan_sign = (ya != ya ? 0x80u : 0u) | (yb != yb ? 0x8000u : 0u) |
+                            (yc != yc ? 0x800000u : 0u) | (yd != yd ? 0x80000000u : 0u);
+  return w & ~nan_sign;
+}
+// Eight 16-bit values (one uint4) of type DT as eight E4M3 codes.
+template <int DT>
+__device__ __forceinline__ uint2 e4m3x8_from16(const uint4& u, float scale) {
+  float f[8];
+  unpack16<DT>(u, f);
+  return make_uint2(e4m3x4_pack(f[0], f[1], f[2], f[3], scale),
+                    e4m3x4_pack(f[4], f[5], f[6], f[7], scale));
+}
+
+template <int DT, bool SPLITCOL, int RING, int BS, bool KV8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_mfma_kernel(DecodeParams p) {
   constexpr int D = 128;
-  constexpr int kRowU4 = D / 8;  // uint4 per 16-bit token row
+  constexpr int kRowU4 = KV8 ? D / 16 : D / 8;  // uint4 per token row of the pools
   const int lane = threadIdx.x;
   const int u = blockIdx.x;
   if (u >= p.n_units) return;
@@ -663,6 +720,8 @@ void decode_mfma_kernel(DecodeParams p) {
   int raw_entry = 0;
   if (lane < p.max_blocks - b0) raw_entry = p.tables[(size_t)w.s * p.max_blocks + b0 + lane];
   // B operand of the score MFMA: Q^T, lane holds head `hd`, dims 32kc+8grp..+8
+  // (fp8 cache: dims 16grp+8kc.. for kc < 2 and 64+16grp+8(kc-2).. for kc >= 2,
+  // the order in which a lane's two 16-byte K loads hold them)
   const int hd = SPLITCOL ? (col & 7) : col;
   const bool live_head = hd < p.G;
   uint4 qb[4];
@@ -672,7 +731,7 @@ void decode_mfma_kernel(DecodeParams p) {
         (((size_t)w.s * p.Hq + (size_t)w.h * p.G + (live_head ? hd : 0)) * D) * 2);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const uint4 v = qp[kc * 4 + grp];
+      const uint4 v = qp[KV8 ? (kc >> 1) * 8 + 2 * grp + (kc & 1) : kc * 4 + grp];
       qb[kc] = live_head ? v : make_uint4(0, 0, 0, 0);
     }
   }
@@ -682,10 +741,17 @@ void decode_mfma_kernel(DecodeParams p) {
   uint4 kn0 = make_uint4(0, 0, 0, 0), kn1 = kn0, kn2 = kn0, kn3 = kn0, vnew = kn0;
   if (p.k_new) {
     const uint4* kn = static_cast<const uint4*>(p.k_new) + ((size_t)w.s * p.Hkv + w.h) * (D / 8);
-    kn0 = kn[grp];
-    kn1 = kn[4 + grp];
-    kn2 = kn[8 + grp];
-    kn3 = kn[12 + grp];
+    if constexpr (KV8) {  // the 16-bit chunks behind the lane's two fp8 K chunks
+      kn0 = kn[2 * grp];
+      kn1 = kn[2 * grp + 1];
+      kn2 = kn[8 + 2 * grp];
+      kn3 = kn[9 + 2 * grp];
+    } else {
+      kn0 = kn[grp];
+      kn1 = kn[4 + grp];
+      kn2 = kn[8 + grp];
+      kn3 = kn[12 + grp];
+    }
     vnew = (static_cast<const uint4*>(p.v_new) + ((size_t)w.s * p.Hkv + w.h) * (D / 8))[col];
   }
   const int nps = unit_prologue<D>(p, w, ctx, lane);
@@ -703,14 +769,27 @@ void decode_mfma_kernel(DecodeParams p) {
     // kc*4+grp; V: the lanes of row group nt.row/4, chunk col), so program
     // order within the lane makes that load return the new values.
     const size_t dst = tile_row<BS>(p, w.h, staged, last, nt.row, kRowU4);
-    if (col == nt.row) {
-      uint4* kd = static_cast<uint4*>(p.k_pool_w) + dst + grp;
-      kd[0] = kn0;
-      kd[4] = kn1;
-      kd[8] = kn2;
-      kd[12] = kn3;
+    if constexpr (KV8) {
+      // quantised: K chunks grp and 4+grp (16 codes each), V chunk col (8 codes)
+      if (col == nt.row) {
+        uint4* kd = static_cast<uint4*>(p.k_pool_w) + dst + grp;
+        const uint2 a = e4m3x8_from16<DT>(kn0, p.k_scale), b = e4m3x8_from16<DT>(kn1, p.k_scale);
+        const uint2 c = e4m3x8_from16<DT>(kn2, p.k_scale), d = e4m3x8_from16<DT>(kn3, p.k_scale);
+        kd[0] = make_uint4(a.x, a.y, b.x, b.y);
+        kd[4] = make_uint4(c.x, c.y, d.x, d.y);
+      }
+      if (grp == nt.row / 4)
+        static_cast<uint2*>(p.v_pool_w)[2 * dst + col] = e4m3x8_from16<DT>(vnew, p.v_scale);
+    } else {
+      if (col == nt.row) {
+        uint4* kd = static_cast<uint4*>(p.k_pool_w) + dst + grp;
+        kd[0] = kn0;
+        kd[4] = kn1;
+        kd[8] = kn2;
+        kd[12] = kn3;
+      }
+      if (grp == nt.row / 4) static_cast<uint4*>(p.v_pool_w)[dst + col] = vnew;
     }
-    if (grp == nt.row / 4) static_cast<uint4*>(p.v_pool_w)[dst + col] = vnew;
   }
 
   const bool residual_lane = SPLITCOL && col >= 8;
@@ -723,17 +802,31 @@ void decode_mfma_kernel(DecodeParams p) {
   const char* kbase = static_cast<const char*>(p.k_pool);
   const char* vbase = static_cast<const char*>(p.v_pool);
 
-  auto load = [&](int j, uint4* ku, uint4* vu) {
+  // Raw tile data held per lane: 16-bit cache 4 K + 4 V uint4; fp8 cache
+  // 2 K uint4 (16 codes each) + 4 V uint2 (8 codes each).
+  constexpr int kKU = KV8 ? 2 : 4;
+  typedef typename std::conditional<KV8, uint2, uint4>::type VRaw;
+  auto load = [&](int j, uint4* ku, VRaw* vu) {
     // K: row col of the tile; V: rows 4grp..4grp+3 (consecutive in one block)
     const uint4* kt = reinterpret_cast<const uint4*>(kbase) + tile_row<BS>(p, w.h, staged, j, col, kRowU4);
-    const uint4* vt = reinterpret_cast<const uint4*>(vbase) + tile_row<BS>(p, w.h, staged, j, 4 * grp, kRowU4);
+    if constexpr (KV8) {
+      const uint2* vt = reinterpret_cast<const uint2*>(vbase) +
+                        tile_row<BS>(p, w.h, staged, j, 4 * grp, 2 * kRowU4);
+      ku[0] = kt[grp];
+      ku[1] = kt[4 + grp];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) ku[kc] = kt[kc * 4 + grp];
+      for (int jj = 0; jj < 4; ++jj) vu[jj] = vt[jj * 2 * kRowU4 + col];
+    } else {
+      const uint4* vt = reinterpret_cast<const uint4*>(vbase) +
+                        tile_row<BS>(p, w.h, staged, j, 4 * grp, kRowU4);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) vu[jj] = vt[jj * kRowU4 + col];
+      for (int kc = 0; kc < 4; ++kc) ku[kc] = kt[kc * 4 + grp];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) vu[jj] = vt[jj * kRowU4 + col];
+    }
   };
 
-  auto compute = [&](int jb, uint4* ku, uint4* vu) {
+  auto compute16 = [&](int jb, uint4* ku, uint4* vu) {
     f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) st = mfma_qk<DT>(ku[kc], qb[kc], st);
@@ -781,6 +874,21 @@ void decode_mfma_kernel(DecodeParams p) {
       }
     }
   };
+  auto compute = [&](int jb, uint4* ku, VRaw* vu) {
+    if constexpr (KV8) {
+      // widen the codes to the query's 16-bit type (exact), then as above
+      uint4 k16[4], v16[4];
+      k16[0] = e4m3x8_widen<DT>(ku[0].x, ku[0].y);
+      k16[1] = e4m3x8_widen<DT>(ku[0].z, ku[0].w);
+      k16[2] = e4m3x8_widen<DT>(ku[1].x, ku[1].y);
+      k16[3] = e4m3x8_widen<DT>(ku[1].z, ku[1].w);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v16[r] = e4m3x8_widen<DT>(vu[r].x, vu[r].y);
+      compute16(jb, k16, v16);
+    } else {
+      compute16(jb, ku, vu);
+    }
+  };
 
   // Ring of RING blocks: while one block is computed the next RING-1 are in
   // flight. The prologue and the steady-state loop issue their loads
@@ -788,7 +896,8 @@ void decode_mfma_kernel(DecodeParams p) {
   // outstanding load at the join); the last blocks are drained with guarded
   // refills.
   {
-    uint4 kr[RING][4], vr[RING][4];
+    uint4 kr[RING][kKU];
+    VRaw vr[RING][4];
 #pragma unroll
     for (int s = 0; s < RING; ++s) load(min(s, last), kr[s], vr[s]);
     int j = 0;
@@ -823,8 +932,10 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ float stage[16 * kStageStride];
   const bool writer = SPLITCOL ? (col < 8 && live_head) : live_head;
   if (writer) {
-    // lane holds head hd, dims 32*grp + 8*r + n for r < 4, n < 8
-    const float inv = nps == 1 ? 1.0f / l : 1.0f;
+    // lane holds head hd, dims 32*grp + 8*r + n for r < 4, n < 8; an fp8
+    // cache's V scale multiplies the (partial) output
+    float inv = nps == 1 ? 1.0f / l : 1.0f;
+    if constexpr (KV8) inv *= p.v_scale;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -921,6 +1032,39 @@ __global__ void append_tokens_kernel(const int32_t* __restrict__ tables, int32_t
 }
 
 // ============================================================================
+// fp8 cache write: as reshape_and_cache, but each 16-bit value is stored as
+// the E4M3 code of value / scale (K and V pools have their own scales). One
+// thread turns 8 values (16 bytes in, 8 bytes out) of K and of V.
+// ============================================================================
+template <int DT>
+__global__ void reshape_and_cache_fp8_kernel(const uint4* __restrict__ k_new,
+                                             const uint4* __restrict__ v_new,
+                                             uint2* __restrict__ k_pool, uint2* __restrict__ v_pool,
+                                             const int64_t* __restrict__ slots, int32_t n,
+                                             int64_t num_slots, int32_t Hkv, int32_t row_c,
+                                             int32_t B, float k_scale, float v_scale) {
+  const int64_t per_token = (int64_t)Hkv * row_c;  // 8-value chunks per token
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)n * per_token) return;
+  const int64_t i = t / per_token, c = t % per_token;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t h = c / row_c, cc = c % row_c;
+  const int64_t dst = (((slot / B) * Hkv + h) * B + slot % B) * row_c + cc;
+  k_pool[dst] = e4m3x8_from16<DT>(k_new[t], k_scale);
+  v_pool[dst] = e4m3x8_from16<DT>(v_new[t], v_scale);
+}
+
+// Elementwise E4M3 codes of a 16-bit buffer (n a multiple of 8).
+template <int DT>
+__global__ void quantize_fp8_kernel(const uint4* __restrict__ src, uint2* __restrict__ dst,
+                                    int64_t n8, float scale) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = e4m3x8_from16<DT>(src[i], scale);
+}
+
+// ============================================================================
 // Block copy for copy-on-write ([2], "Copy-on-Write ..."): blockIdx.x = pair,
 // blockIdx.y = layer within this launch's chunk, blockIdx.z = 0 (K) / 1 (V).
 // ============================================================================
@@ -1006,10 +1150,12 @@ kv_status launch_decode_kernel(const DecodeParams& prm, kv_dtype dtype, int head
   constexpr int R = kDecodeRing;
   if ((dtype == KV_F16 || dtype == KV_BF16) && head_dim == 128 && G >= 2) {
     if (G <= 8)
-      return dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16, true, R, BS>, prm, st)
-                              : launch_decode(decode_mfma_kernel<KV_F16, true, R, BS>, prm, st);
-    return dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16, false, R, BS>, prm, st)
-                            : launch_decode(decode_mfma_kernel<KV_F16, false, R, BS>, prm, st);
+      return dtype == KV_BF16
+                 ? launch_decode(decode_mfma_kernel<KV_BF16, true, R, BS, false>, prm, st)
+                 : launch_decode(decode_mfma_kernel<KV_F16, true, R, BS, false>, prm, st);
+    return dtype == KV_BF16
+               ? launch_decode(decode_mfma_kernel<KV_BF16, false, R, BS, false>, prm, st)
+               : launch_decode(decode_mfma_kernel<KV_F16, false, R, BS, false>, prm, st);
   }
   const int gmax = G == 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
   if (dtype == KV_F32)
@@ -1020,6 +1166,19 @@ kv_status launch_decode_kernel(const DecodeParams& prm, kv_dtype dtype, int head
                           : launch_decode(decode_valu_kernel<KV_F16, 128, 1, BS>, prm, st);
   return head_dim == 64 ? launch_valu<KV_BF16, 64, BS>(prm, gmax, st)
                         : launch_decode(decode_valu_kernel<KV_BF16, 128, 1, BS>, prm, st);
+}
+
+// fp8 cache: the MFMA kernel for every group size (1..16), head_dim 128,
+// f16 or bf16 queries.
+template <int BS>
+kv_status launch_decode_kernel_fp8(const DecodeParams& prm, kv_dtype dtype, int G,
+                                   hipStream_t st) {
+  constexpr int R = kDecodeRing8;
+  if (G <= 8)
+    return dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16, true, R, BS, true>, prm, st)
+                            : launch_decode(decode_mfma_kernel<KV_F16, true, R, BS, true>, prm, st);
+  return dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16, false, R, BS, true>, prm, st)
+                          : launch_decode(decode_mfma_kernel<KV_F16, false, R, BS, true>, prm, st);
 }
 
 kv_status check_cache_write(const char* who, const void* k_new, const void* v_new,
@@ -1213,9 +1372,22 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
                       int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
                       int32_t max_context_len, const int32_t* work_items, int32_t n_items,
                       void* workspace, size_t ws_bytes, const void* k_new, const void* v_new,
-                      int64_t* slots, hipStream_t stream) {
+                      int64_t* slots, hipStream_t stream, bool kv8 = false,
+                      float k_scale = 1.0f, float v_scale = 1.0f) {
   if (pagedkv::dtype_bytes(dtype) == 0)
     return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: unknown dtype");
+  if (dtype == KV_FP8_E4M3)
+    return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: an fp8 cache goes through the "
+                                    "_fp8 entry points (dtype is the query's type)");
+  if (kv8) {
+    if (dtype != KV_F16 && dtype != KV_BF16)
+      return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode_fp8: queries must be f16 or bf16");
+    if (head_dim != 128)
+      return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode_fp8: head_dim %d (128)", head_dim);
+    if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !std::isfinite(k_scale) ||
+        !std::isfinite(v_scale))
+      return fail(KV_ERR_INVALID, "kv_paged_attention_decode_fp8: scales must be finite and > 0");
+  }
   if (S < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks < 0 || num_blocks <= 0 ||
       max_context_len < 0)
     return fail(KV_ERR_INVALID, "kv_paged_attention_decode: bad sizes");
@@ -1275,6 +1447,9 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
   prm.part_tokens = P;
   prm.nparts = (int32_t)nparts;
   prm.scale_log2 = scale * 1.4426950408889634f;
+  if (kv8) prm.scale_log2 *= k_scale;
+  prm.k_scale = k_scale;
+  prm.v_scale = v_scale;
   prm.k_new = k_new;
   prm.v_new = v_new;
   prm.k_pool_w = const_cast<void*>(k_pool);
@@ -1283,7 +1458,10 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
 
   prm.block_size = block_size;
   const kv_status st =
-      block_size == 8 ? launch_decode_kernel<8>(prm, dtype, head_dim, G, stream)
+      kv8 ? (block_size == 8    ? launch_decode_kernel_fp8<8>(prm, dtype, G, stream)
+             : block_size == 16 ? launch_decode_kernel_fp8<16>(prm, dtype, G, stream)
+                                : launch_decode_kernel_fp8<32>(prm, dtype, G, stream))
+      : block_size == 8  ? launch_decode_kernel<8>(prm, dtype, head_dim, G, stream)
       : block_size == 16 ? launch_decode_kernel<16>(prm, dtype, head_dim, G, stream)
                          : launch_decode_kernel<32>(prm, dtype, head_dim, G, stream);
   if (st != KV_OK || nparts <= 1) return st;
@@ -1331,6 +1509,93 @@ kv_status kv_paged_attention_decode_append(
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                      partition_size, max_context_len, work_items, n_items, workspace, ws_bytes,
                      k_new, v_new, slots, stream);
+}
+
+kv_status kv_paged_attention_decode_fp8(float* out, const void* q, const void* k_pool,
+                                        const void* v_pool, const int32_t* block_tables,
+                                        int32_t max_blocks, const int32_t* context_lens,
+                                        int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                        float scale, kv_dtype dtype, float k_scale,
+                                        float v_scale, int32_t partition_size,
+                                        int32_t max_context_len, const int32_t* work_items,
+                                        int32_t n_items, void* workspace, size_t ws_bytes,
+                                        hipStream_t stream) {
+  pagedkv::clear_error();
+  return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     partition_size, max_context_len, work_items, n_items, workspace, ws_bytes,
+                     nullptr, nullptr, nullptr, stream, true, k_scale, v_scale);
+}
+
+kv_status kv_paged_attention_decode_append_fp8(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t S,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, float scale, kv_dtype dtype, float k_scale, float v_scale,
+    int32_t partition_size, int32_t max_context_len, const int32_t* work_items, int32_t n_items,
+    void* workspace, size_t ws_bytes, int64_t* slots, hipStream_t stream) {
+  pagedkv::clear_error();
+  if (S > 0) {
+    if (!k_new || !v_new || !slots)
+      return fail(KV_ERR_INVALID, "kv_paged_attention_decode_append_fp8: null pointer");
+    if (!aligned16(k_new) || !aligned16(v_new))
+      return fail(KV_ERR_INVALID,
+                  "kv_paged_attention_decode_append_fp8: k_new/v_new must be 16-byte aligned");
+  }
+  return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     partition_size, max_context_len, work_items, n_items, workspace, ws_bytes,
+                     k_new, v_new, slots, stream, true, k_scale, v_scale);
+}
+
+kv_status kv_reshape_and_cache_fp8(const void* k_new, const void* v_new, void* k_pool,
+                                   void* v_pool, const int64_t* slots, int32_t n,
+                                   int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, kv_dtype dtype, float k_scale,
+                                   float v_scale, hipStream_t stream) {
+  pagedkv::clear_error();
+  const char* who = "kv_reshape_and_cache_fp8";
+  if (dtype != KV_F16 && dtype != KV_BF16)
+    return fail(KV_ERR_UNSUPPORTED, "%s: new tokens must be f16 or bf16", who);
+  if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(KV_ERR_INVALID, "%s: scales must be finite and > 0", who);
+  kv_status st = check_cache_write(who, k_new, v_new, k_pool, v_pool, n, num_blocks, num_kv_heads,
+                                   head_dim, block_size, KV_FP8_E4M3);
+  if (st != KV_OK || n == 0) return st;
+  if (!slots) return fail(KV_ERR_INVALID, "%s: null pointer", who);
+  const int32_t row_c = head_dim / 8;
+  const int64_t total = (int64_t)n * num_kv_heads * row_c;
+  const int64_t blocks = ceil_div64(total, 256);
+  if (blocks > INT32_MAX) return fail(KV_ERR_INVALID, "%s: too many tokens", who);
+  auto kern = dtype == KV_BF16 ? reshape_and_cache_fp8_kernel<KV_BF16>
+                               : reshape_and_cache_fp8_kernel<KV_F16>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                     static_cast<uint2*>(k_pool), static_cast<uint2*>(v_pool), slots, n,
+                     (int64_t)num_blocks * block_size, num_kv_heads, row_c, block_size, k_scale,
+                     v_scale);
+  return launch_status(who);
+}
+
+kv_status kv_quantize_fp8(const void* src, void* dst, int64_t n, kv_dtype dtype, float scale,
+                          hipStream_t stream) {
+  pagedkv::clear_error();
+  const char* who = "kv_quantize_fp8";
+  if (dtype != KV_F16 && dtype != KV_BF16)
+    return fail(KV_ERR_UNSUPPORTED, "%s: source must be f16 or bf16", who);
+  if (n < 0 || n % 8 != 0) return fail(KV_ERR_INVALID, "%s: n must be a multiple of 8", who);
+  if (!(scale > 0.0f) || !std::isfinite(scale))
+    return fail(KV_ERR_INVALID, "%s: scale must be finite and > 0", who);
+  if (n == 0) return KV_OK;
+  if (!src || !dst || !aligned16(src) || (reinterpret_cast<uintptr_t>(dst) & 7u))
+    return fail(KV_ERR_INVALID, "%s: null or misaligned pointer", who);
+  const int64_t n8 = n / 8;
+  const int64_t blocks = ceil_div64(n8, 256) < 65536 ? ceil_div64(n8, 256) : 65536;
+  auto kern = dtype == KV_BF16 ? quantize_fp8_kernel<KV_BF16> : quantize_fp8_kernel<KV_F16>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint4*>(src), static_cast<uint2*>(dst), n8, scale);
+  return launch_status(who);
 }
 
 }  // extern "C"

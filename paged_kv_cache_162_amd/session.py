@@ -10,6 +10,9 @@ separate so a benchmark can time the device part alone.
 
 Operation scripts are lists of tuples: ("create", s), ("fork", parent, child),
 ("append", s, n) where s are caller-chosen sequence numbers.
+
+Pools of dtype uint8 are an fp8 (E4M3) cache: every write quantises with the
+session's k_scale / v_scale and attention goes through the _fp8 entry points.
 """
 from __future__ import annotations
 
@@ -22,13 +25,16 @@ from . import binding as kv
 
 class DecodeSession:
     def __init__(self, *, k_pool, v_pool, num_q_heads: int, free_order: Optional[Sequence[int]] = None,
-                 partition_size: int = 0, use_plan: bool = True, fused: bool = True):
+                 partition_size: int = 0, use_plan: bool = True, fused: bool = True,
+                 k_scale: float = 1.0, v_scale: float = 1.0):
         import torch
         self.torch = torch
         NB, Hkv, B, D = k_pool.shape
         self.k_pool, self.v_pool = k_pool, v_pool
         self.NB, self.Hkv, self.B, self.D, self.Hq = NB, Hkv, B, D, num_q_heads
         self.dtype = kv.dtype_code(k_pool)
+        self.fp8 = self.dtype == kv.KV_FP8_E4M3
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
         self.partition_size = partition_size
         self.use_plan = use_plan
         self.fused = fused
@@ -73,7 +79,7 @@ class DecodeSession:
                 if len(op) > 3 and op[3] == "values":
                     k, v = values[s]
                     d_slots = torch.from_numpy(slots).to(self.device)
-                    kv.kv_reshape_and_cache(k, v, self.k_pool, self.v_pool, d_slots)
+                    self._write(k, v, self.k_pool, self.v_pool, d_slots)
             else:
                 raise ValueError(op)
         return cows
@@ -118,6 +124,12 @@ class DecodeSession:
         ev.record()
         pending.append((ev, tensors))
         self._pending = pending
+
+    def _write(self, k, v, kp, vp_, d_slots) -> None:
+        if self.fp8:
+            kv.kv_reshape_and_cache_fp8(k, v, kp, vp_, d_slots, self.k_scale, self.v_scale)
+        else:
+            kv.kv_reshape_and_cache(k, v, kp, vp_, d_slots)
 
     def tables(self, seqs: Sequence[int], max_blocks: Optional[int] = None):
         ids = [self.handles[s] for s in seqs]
@@ -173,11 +185,25 @@ class DecodeSession:
         if self.d_pairs.shape[0]:
             kv.kv_copy_blocks([kp], [vp_], self.d_pairs, self.NB, self.block_bytes)
         if not fused:
-            kv.kv_append_tokens(self.d_tables, self.d_seq_idx, self.d_pos, k_new, v_new, kp, vp_,
-                                self.d_slots)
+            if self.fp8:
+                kv.kv_slot_mapping(self.d_tables, self.d_seq_idx, self.d_pos, self.d_slots, self.B)
+                self._write(k_new, v_new, kp, vp_, self.d_slots)
+            else:
+                kv.kv_append_tokens(self.d_tables, self.d_seq_idx, self.d_pos, k_new, v_new, kp,
+                                    vp_, self.d_slots)
         if decode_events is not None:
             decode_events[0].record()
-        if fused:
+        if self.fp8:
+            if fused:
+                kv.kv_paged_attention_decode_append_fp8(
+                    out, q, k_new, v_new, kp, vp_, self.d_tables, self.d_lens, scale, self.k_scale,
+                    self.v_scale, self.max_context_len, self.d_slots, self.workspace,
+                    self.partition_size, self.d_items)
+            else:
+                kv.kv_paged_attention_decode_fp8(
+                    out, q, kp, vp_, self.d_tables, self.d_lens, scale, self.k_scale, self.v_scale,
+                    self.max_context_len, self.workspace, self.partition_size, self.d_items)
+        elif fused:
             kv.kv_paged_attention_decode_append(out, q, k_new, v_new, kp, vp_, self.d_tables,
                                                 self.d_lens, scale, self.max_context_len,
                                                 self.d_slots, self.workspace, self.partition_size,

@@ -301,3 +301,20 @@ def test_work_plan_lists_every_partition_longest_first(kv):
         kv.kv_paged_attention_plan(lens, 24)
     with pytest.raises(kv.KVError):
         kv.kv_paged_attention_plan(lens, 2048)
+
+
+def test_fp8_entry_points_validate_on_the_host(kv):
+    lib = kv.lib
+    call = lambda **k: lib.kv_paged_attention_decode_fp8(
+        None, None, None, None, None, 4, None, k.get("S", 1), 8, 2, k.get("D", 128), 16, 8, 1.0,
+        k.get("dt", kv.KV_BF16), k.get("ks", 1.0), k.get("vs", 1.0), 0, 16, None, 0, None, 0, None)
+    assert call(ks=0.0) == kv.KV_ERR_INVALID
+    assert call(vs=float("nan")) == kv.KV_ERR_INVALID
+    assert call(D=64) == kv.KV_ERR_UNSUPPORTED
+    assert call(dt=kv.KV_F32) == kv.KV_ERR_UNSUPPORTED
+    assert call() == kv.KV_ERR_INVALID            # null pointers
+    assert call(S=0) == kv.KV_OK
+    # the 16-bit entry point refuses an fp8 cache type
+    assert lib.kv_paged_attention_decode(None, None, None, None, None, 4, None, 1, 8, 2, 128, 16, 8,
+                                         1.0, kv.KV_FP8_E4M3, 0, 16, None, 0, None, 0, None) \
+        == kv.KV_ERR_UNSUPPORTED

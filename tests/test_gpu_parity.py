@@ -161,14 +161,14 @@ def run_workload(cfg, S=None, full_pool_compare=True, n_sample=None, partition_s
     # slot mapping kernel and scatter: bit exact
     assert np.array_equal(case.sess.d_slots.cpu().numpy(), case.step_slots)
     if full_pool_compare:
-        assert np.array_equal(bits(to_host(case.k_dev, case.dt)), bits(case.k_ref))
-        assert np.array_equal(bits(to_host(case.v_dev, case.dt)), bits(case.v_ref))
+        assert np.array_equal(bits(to_host(case.k_dev, case.kdt)), bits(case.k_ref))
+        assert np.array_equal(bits(to_host(case.v_dev, case.kdt)), bits(case.v_ref))
     else:
         blocks = np.unique(np.concatenate([case.step_slots // case.B,
                                            np.random.default_rng(3).integers(0, case.w.num_blocks, 64)]))
         idx = torch.from_numpy(blocks).cuda()
-        assert np.array_equal(bits(to_host(case.k_dev[idx], case.dt)), bits(case.k_ref[blocks]))
-        assert np.array_equal(bits(to_host(case.v_dev[idx], case.dt)), bits(case.v_ref[blocks]))
+        assert np.array_equal(bits(to_host(case.k_dev[idx], case.kdt)), bits(case.k_ref[blocks]))
+        assert np.array_equal(bits(to_host(case.v_dev[idx], case.kdt)), bits(case.v_ref[blocks]))
     got = case.out_dev.cpu().numpy()
     if n_sample is None:
         ref = case.oracle_out()
@@ -232,8 +232,8 @@ def test_fused_and_unfused_steps_are_bitwise_identical(cfg, S):
     for fused in (True, False):
         log(f"[gpu] workload {cfg} fused={fused}")
         case.device_run(fused=fused)
-        res[fused] = (case.out_dev.cpu().numpy(), to_host(case.k_dev, case.dt),
-                      to_host(case.v_dev, case.dt), case.sess.d_slots.cpu().numpy())
+        res[fused] = (case.out_dev.cpu().numpy(), to_host(case.k_dev, case.kdt),
+                      to_host(case.v_dev, case.kdt), case.sess.d_slots.cpu().numpy())
     a, b = res[True], res[False]
     assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
     assert np.array_equal(bits(a[1]), bits(b[1])) and np.array_equal(bits(a[2]), bits(b[2]))
@@ -247,7 +247,7 @@ def test_graph_replay_matches_eager():
     case = Case(3, S=10)
     case.device_run()
     sess, dt = case.sess, case.dt
-    eager = (case.out_dev.cpu().numpy().copy(), to_host(case.k_dev, dt).copy(),
+    eager = (case.out_dev.cpu().numpy().copy(), to_host(case.k_dev, case.kdt).copy(),
              case.sess.d_slots.cpu().numpy().copy())
     out = torch.full_like(case.out_dev, float("nan"))
     stream = torch.cuda.Stream()
@@ -264,7 +264,7 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         log(f"[gpu] graph replay {rep}")
         assert np.array_equal(out.cpu().numpy().view(np.uint32), eager[0].view(np.uint32))
-        assert np.array_equal(bits(to_host(case.k_dev, dt)), bits(eager[1]))
+        assert np.array_equal(bits(to_host(case.k_dev, case.kdt)), bits(eager[1]))
         assert np.array_equal(sess.d_slots.cpu().numpy(), eager[2])
 
 
