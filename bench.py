@@ -70,15 +70,17 @@ CAL_PAIRS = 4096            # block pairs copied by the calibration dispatch
 CAL_BLOCK_BYTES = 32768     # bytes per block and pool (K and V each)
 
 
+DECODE_SOURCES = ("decode.hip", "device_common.h")
+
+
 def kernel_source_digest():
-    """Digest of the device sources: measured traffic is only reported while
-    the kernels it was taken on are unchanged."""
+    """Digest of the sources the decode kernels are compiled from: measured
+    traffic is only reported while the kernels it was taken on are unchanged."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_162_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith(".hip"):
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in DECODE_SOURCES:
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 

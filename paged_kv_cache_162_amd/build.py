@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedkv.so")
 SOURCES = [os.path.join(CSRC, "host_pool.cpp"), os.path.join(CSRC, "plan.cpp"),
-           os.path.join(CSRC, "kernels.hip")]
+           os.path.join(CSRC, "cache.hip"), os.path.join(CSRC, "decode.hip")]
 ARCH = os.environ.get("PAGEDKV_ARCH", "gfx950")
 
 
