@@ -32,6 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
 
 
 def parse():
@@ -71,17 +72,23 @@ CAL_BLOCK_BYTES = 32768     # bytes per block and pool (K and V each)
 
 
 DECODE_SOURCES = ("decode.hip", "device_common.h")
+PREFILL_SOURCES = ("prefill.hip", "device_common.h")
 
 
-def kernel_source_digest():
-    """Digest of the sources the decode kernels are compiled from: measured
+def kernel_source_digest(sources=DECODE_SOURCES):
+    """Digest of the sources the measured kernels are compiled from: measured
     traffic is only reported while the kernels it was taken on are unchanged."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_162_amd", "csrc")
-    for name in DECODE_SOURCES:
+    for name in sources:
         h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
+
+
+def is_prefill(workload):
+    from workloads import spec
+    return spec(workload).chunk > 0
 
 
 def copy_calibration(kv, torch):
@@ -127,13 +134,15 @@ def pmc_parse(fetch_dir, write_dir, out_path, workload, partition):
     dispatch), each scaled by what the same counter reads for the calibration
     copy, whose true byte count is known."""
     cal_bytes = 2 * CAL_PAIRS * CAL_BLOCK_BYTES
+    prefill = is_prefill(workload)
     res = {"workload": workload, "partition": partition,
-           "kernel_source_digest": kernel_source_digest(), "calibration_bytes": cal_bytes}
+           "kernel_source_digest": kernel_source_digest(PREFILL_SOURCES if prefill else DECODE_SOURCES),
+           "calibration_bytes": cal_bytes}
     total = 0.0
     for tag, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = _counter_rows(d)
         cal, ncal = _mean_counter(rows, "copy_blocks_kernel", counter)
-        dec, ndec = _mean_counter(rows, "decode_", counter)
+        dec, ndec = _mean_counter(rows, "prefill_mfma" if prefill else "decode_", counter)
         mrg, nmrg = _mean_counter(rows, "splitk_merge", counter)
         if ncal == 0 or ndec == 0:
             raise SystemExit(f"{d}: calibration or decode dispatches missing")
@@ -200,6 +209,126 @@ def cpu_baseline(w, seconds):
             "seqs_per_s": round(sp.S / per, 2), "seconds_per_pass": round(per, 3),
             "sample": f"the whole workload ({sp.S} sequences x {sp.Hq} query heads), {passes} "
                       f"pass(es), BLAS limited to 1 thread"}
+
+
+def prefill_flops(lens, counts, Hq, D):
+    """Algorithmic flops of the chunked-prefill attention: every chunk row at
+    position p takes 2*D multiply-adds for each of its p+1 scores and as many
+    for the weighted sum of values, per query head (4*D*(p+1)*Hq flops)."""
+    total = 0
+    for L, C in zip(lens.tolist(), counts):
+        prev = L - C
+        total += 4 * Hq * D * (C * prev + C * (C + 1) // 2)
+    return total
+
+
+def prefill_bench(args, w, kv, torch):
+    """One step = the chunk's cache write + the causal attention of every chunk
+    row (`DecodeSession.prefill_step`), timed like the decode step."""
+    from paged_kv_cache_162_amd.session import DecodeSession
+    sp = w.spec
+    dt = sp.dtype
+    kp, vp = to_dev(w.k_pool, dt), to_dev(w.v_pool, dt)
+    sess = DecodeSession(k_pool=kp, v_pool=vp, num_q_heads=sp.Hq, free_order=w.free_order,
+                         use_plan=not args.no_plan)
+    sess.run_ops(w.setup_ops)
+    counts = [sp.chunk] * sp.S
+    sess.prepare_prefill(list(range(sp.S)), counts)
+    lens = sess.host_lens
+    q, kn, vn = to_dev(w.q, dt), to_dev(w.k_new, dt), to_dev(w.v_new, dt)
+    T = sp.S * sp.chunk
+    out = torch.empty((T, sp.Hq, sp.D), dtype=torch.float32, device="cuda")
+    pool_bytes = 2 * kp.numel() * kp.element_size()
+    R = args.replicas or max(1, int(np.ceil(1.0e9 / pool_bytes)))
+    reps = [(kp, vp, q, kn, vn)] + [(kp.clone(), vp.clone(), q.clone(), kn.clone(), vn.clone())
+                                    for _ in range(R - 1)]
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration(kv, torch)
+
+    def one(k, events=None):
+        a, b, qq, kk, vv = reps[k % R]
+        sess.prefill_step(qq, kk, vv, out, sp.scale, k_pool=a, v_pool=b, events=events)
+
+    for k in range(args.warmup):
+        one(k)
+    torch.cuda.synchronize()
+    K = args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for k in range(K):
+        one(k)
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / K
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for k in range(K):
+        one(k, ev[k])
+    torch.cuda.synchronize()
+    att_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    flops = prefill_flops(lens, counts, sp.Hq, sp.D)
+    tflops_step = flops / (step_ms * 1e-3) / 1e12
+    achieved = flops / (att_ms * 1e-3) / 1e12
+    traffic = None
+    tpath = args.pmc_traffic or os.path.join(ROOT, "profiles", f"decode_traffic_w{args.workload}.json")
+    if os.path.exists(tpath):
+        t = json.load(open(tpath))
+        if t.get("kernel_source_digest") == kernel_source_digest(PREFILL_SOURCES) and \
+                t.get("workload") == args.workload:
+            traffic = round(float(t["bytes_per_launch"]))
+    res = {
+        "metric": "chunked-prefill attention TFLOP/s and query tokens/s, 1 GPU",
+        "value": round(tflops_step, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dt, "data": "synthetic",
+        "config": {"workload": f"{sp.name}: {sp.description}", "sequences": sp.S,
+                   "chunk_tokens": sp.chunk, "q_heads": sp.Hq, "kv_heads": sp.Hkv,
+                   "head_dim": sp.D, "block_size": args.block_size,
+                   "sum_context": int(lens.sum()), "max_context": int(lens.max()),
+                   "flops_per_step": flops, "replicas_rotated": R, "parallelism": "single GPU"},
+        "query_tokens_per_s": round(T / (step_ms * 1e-3), 1),
+        "attention_ms": round(att_ms, 5),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "kv_paged_attention_prefill call: prefill_mfma_kernel",
+                     "alg_flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = prefill_cpu_baseline(w, lens, counts, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def prefill_cpu_baseline(w, lens, counts, seconds):
+    """The prefill oracle, untouched, on a bounded sample: the chunks of the
+    first sequences, rows added sequence by sequence until `seconds` pass."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from oracle.block_manager import run_ops
+    sp = w.spec
+    bm = oracle.BlockManager(w.num_blocks, block_size=sp.block_size, free_order=w.free_order)
+    h, slots_by_op, _ = run_ops(bm, w.setup_ops + w.step_ops)
+    tables, _ = bm.packed_tables([h[i] for i in range(w.S)])
+    qs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    done_flops, t_total, nseq = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        for s in range(w.S):
+            rows = range(int(qs[s]), int(qs[s + 1]))
+            t0 = time.perf_counter()
+            oracle.prefill_attention(w.q, qs, w.k_pool, w.v_pool, tables, lens, sp.scale, sp.dtype,
+                                     block_size=sp.block_size, rows=rows)
+            t_total += time.perf_counter() - t0
+            done_flops += prefill_flops(lens[s:s + 1], counts[s:s + 1], sp.Hq, sp.D)
+            nseq += 1
+            if t_total >= seconds:
+                break
+    return {"value": round(done_flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle", "seconds": round(t_total, 2),
+            "sample": f"the chunks of the first {nseq} of {w.S} sequences "
+                      f"({nseq * sp.chunk} query rows), BLAS limited to 1 thread"}
 
 
 def swap_bench(args, kv, torch):
@@ -288,6 +417,9 @@ def main():
 
     w = make_workload(args.workload, block_size=args.block_size)
     sp = w.spec
+    if sp.chunk:
+        prefill_bench(args, w, kv, torch)
+        return
     dt = sp.dtype
     print(f"[bench] workload {sp.name}: S={sp.S} Hq={sp.Hq} Hkv={sp.Hkv} D={sp.D} {dt} "
           f"blocks={w.num_blocks} sum_ctx={int(w.context_lens.sum())} max_ctx={int(w.context_lens.max())}",

@@ -422,6 +422,66 @@ kv_status kv_paged_attention_decode_append_fp8(
     int32_t partition_size, int32_t max_context_len, const int32_t* work_items, int32_t n_items,
     void* workspace, size_t ws_bytes, int64_t* slots, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Chunked prefill: several query tokens per sequence ([2] "The Successors -
+ * SGLang's RadixAttention and Prefix Sharing": a prompt fed in chunks of a
+ * fixed token count; [2] "Walking Through the Lifecycle", Prefill: the
+ * chunk's K/V are written into the sequence's blocks).
+ * ------------------------------------------------------------------------- */
+
+/* Query rows per work item of kv_paged_attention_prefill for this head
+ * configuration (0 if unsupported): 8 * (16 / G) for G = num_q_heads /
+ * num_kv_heads <= 16. */
+int32_t kv_paged_attention_prefill_rows_per_item(int32_t num_q_heads, int32_t num_kv_heads);
+
+/* Work plan for kv_paged_attention_prefill from host copies of query_start
+ * ([S + 1]) and context_lens ([S]): items_out receives n_items pairs
+ * (sequence, row block), one per block of rows_per_item rows of each
+ * sequence's chunk, the blocks whose last row sees the most keys first.
+ * If cap < n_items, returns KV_ERR_INVALID with *n_items set. */
+kv_status kv_paged_attention_prefill_plan(const int32_t* query_start_host,
+                                          const int32_t* context_lens_host, int32_t S,
+                                          int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t* items_out, int32_t cap, int32_t* n_items);
+
+/* Attention of each sequence's chunk of query tokens over its paged cache,
+ * causal within the chunk. The chunk's K and V must already be in the cache
+ * (kv_slot_mapping + kv_reshape_and_cache, or kv_append_tokens).
+ *
+ * q:            device [total_q][num_q_heads][head_dim] of `dtype` (f16 or
+ *               bf16); the rows of sequence s are query_start[s] ..
+ *               query_start[s+1]-1 (C_s rows, possibly 0).
+ * query_start:  device int32 [S + 1], non-decreasing, query_start[S] <= total_q.
+ * context_lens: device int32 [S]: L_s cached positions of s, the chunk's
+ *               included (L_s >= C_s).
+ * out:          device float [total_q][num_q_heads][head_dim]: row i of
+ *               sequence s (position p = L_s - C_s + i) gets
+ *               sum_{j<=p} softmax_j(scale * <q, K_s[j]>) V_s[j], K_s[j] and
+ *               V_s[j] read from slot(j) of KV head hq / (num_q_heads /
+ *               num_kv_heads). Rows of no sequence are not written.
+ * block_tables: device int32 [S][max_blocks]; k_pool / v_pool as for decode.
+ * work_items:   optional device int32 [n_items][2] from
+ *               kv_paged_attention_prefill_plan (grid = n_items *
+ *               num_kv_heads workgroups). NULL: the grid covers S *
+ *               num_kv_heads * ceil(max_query_len / rows_per_item)
+ *               workgroups, max_query_len >= every C_s (host value).
+ *
+ * head_dim 128, group sizes 1..16, block sizes 8, 16, 32. Device-side
+ * checks: a sequence with L_s < C_s or L_s > max_blocks * block_size gets
+ * NaN rows; a live table entry outside [0, num_blocks) gives NaN rows and no
+ * out-of-range read; a sequence whose query_start range is decreasing or
+ * leaves [0, total_q] is skipped. One workgroup of 4 wave64s per item; the
+ * library allocates nothing. */
+kv_status kv_paged_attention_prefill(float* out, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_tables,
+                                     int32_t max_blocks, const int32_t* context_lens,
+                                     const int32_t* query_start, int32_t S, int32_t total_q,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t num_blocks, float scale,
+                                     kv_dtype dtype, int32_t max_query_len,
+                                     const int32_t* work_items, int32_t n_items,
+                                     hipStream_t stream);
+
 /* Message describing the calling thread's last error ("" if none). */
 const char* kv_last_error(void);
 

@@ -10,7 +10,8 @@ define, in float64 numpy:
   * attention.py     - slot formula, cache scatter, block copy, and decode
                        attention (softmax(q K^T * scale) V) over a paged pool,
                        plus a second loop order and the split/merge form used
-                       to pin the first;
+                       to pin the first; attention of a chunk of query tokens
+                       (chunked prefill), causal within the chunk;
   * block_manager.py - the host block manager (free list, refcounts, lazy
                        per-token growth, fork, copy-on-write, free);
   * sizes.py         - the KV-cache size formula and block/waste counts;
@@ -24,7 +25,7 @@ from .attention import (  # noqa: F401
     widen, slot_of, slot_mapping, gather_sequence, decode_attention,
     decode_attention_blockwise, partial_attention, merge_partials,
     decode_attention_split, reshape_and_cache, copy_blocks, swap_out_blocks,
-    swap_in_blocks,
+    swap_in_blocks, prefill_attention,
 )
 from .block_manager import BlockManager, KVError  # noqa: F401
 from . import fp8  # noqa: F401

@@ -311,3 +311,50 @@ def swap_in_blocks(k_pools: List[np.ndarray], v_pools: List[np.ndarray],
                 blk = pool[int(b)]
                 pool[int(b)] = np.frombuffer(host[i, layer, kv].tobytes(),
                                              dtype=pool.dtype).reshape(blk.shape)
+
+
+def prefill_attention(q, q_start, k_pool, v_pool, block_tables, context_lens, scale: float,
+                      dtype: str, block_size: int = 16,
+                      rows: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Attention of a chunk of new query tokens per sequence over the paged
+    cache, causal within the chunk. Chunked prefill processes a prompt in
+    pieces of a fixed token count ([2] "The Successors - SGLang's
+    RadixAttention and Prefix Sharing"); the chunk's K/V are written into the
+    sequence's blocks first ([2] "Walking Through the Lifecycle", Prefill).
+
+    q is packed [T, Hq, D]; the tokens of sequence s are rows
+    q_start[s] .. q_start[s+1]-1, C_s of them, and context_lens[s] = L_s counts
+    every cached position of s including the chunk's own (already written).
+    Query row i of the chunk sits at position p = L_s - C_s + i and attends to
+    positions 0..p: out = sum_j w_j V[j] / sum_j w_j, w_j = exp(z_j - max z),
+    z_j = scale * <q, K[j]>. Returns float64 [T, Hq, D]; with `rows`, only
+    those query rows are computed and the rest stay NaN.
+    """
+    q = widen(q, dtype)
+    T, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    out = np.full((T, Hq, D), np.nan)
+    want = None if rows is None else set(int(r) for r in rows)
+    sc = float(np.float64(scale))
+    S = len(q_start) - 1
+    for s in range(S):
+        r0, r1 = int(q_start[s]), int(q_start[s + 1])
+        if r1 <= r0 or (want is not None and not any(r0 <= r < r1 for r in want)):
+            continue
+        L = int(context_lens[s])
+        C = r1 - r0
+        if C > L:
+            raise ValueError(f"sequence {s}: chunk of {C} tokens longer than its context {L}")
+        Kc = widen(gather_sequence(k_pool, block_tables[s], L, block_size), dtype)
+        Vc = widen(gather_sequence(v_pool, block_tables[s], L, block_size), dtype)
+        for i in range(C):
+            r = r0 + i
+            if want is not None and r not in want:
+                continue
+            p = L - C + i
+            for hq in range(Hq):
+                h = _kv_head(hq, Hq, Hkv)
+                z = sc * (Kc[:p + 1, h, :] @ q[r, hq])
+                w = np.exp(z - z.max())
+                out[r, hq] = (w @ Vc[:p + 1, h, :]) / w.sum()
+    return out

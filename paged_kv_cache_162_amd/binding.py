@@ -98,6 +98,10 @@ _SIGS = {
                                                        i32, i32, i32, i32, i32, f32, C.c_int, f32,
                                                        f32, i32, i32, vp, i32, vp, C.c_size_t, vp,
                                                        vp]),
+    "kv_paged_attention_prefill_rows_per_item": (i32, [i32, i32]),
+    "kv_paged_attention_prefill_plan": (C.c_int, [P_i32, P_i32, i32, i32, i32, P_i32, i32, P_i32]),
+    "kv_paged_attention_prefill": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32,
+                                             i32, i32, i32, f32, C.c_int, i32, vp, i32, vp]),
     "kv_last_error": (C.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -516,3 +520,52 @@ def kv_paged_attention_decode_append_fp8(out, q, k_new, v_new, k_pool, v_pool, b
         0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
         _dev(slots, "slots", torch.int64), _stream(stream)),
         "kv_paged_attention_decode_append_fp8")
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill: several query tokens per sequence, causal within the chunk
+# ---------------------------------------------------------------------------
+def kv_paged_attention_prefill_rows_per_item(num_q_heads: int, num_kv_heads: int) -> int:
+    return int(lib.kv_paged_attention_prefill_rows_per_item(num_q_heads, num_kv_heads))
+
+
+def kv_paged_attention_prefill_plan(query_start_host, context_lens_host, num_q_heads: int,
+                                    num_kv_heads: int) -> np.ndarray:
+    """Host work plan: int32 [n_items, 2] (sequence, row block), most keys first."""
+    qs = _i32_array(query_start_host)
+    lens = _i32_array(context_lens_host)
+    if len(qs) != len(lens) + 1:
+        raise KVError(KV_ERR_INVALID, "kv_paged_attention_prefill_plan", "query_start needs S + 1 entries")
+    n = i32()
+    st = lib.kv_paged_attention_prefill_plan(_p32(qs), _p32(lens), len(lens), num_q_heads,
+                                             num_kv_heads, None, 0, C.byref(n))
+    if st != KV_OK and n.value == 0:
+        _check(st, "kv_paged_attention_prefill_plan")
+    out = np.zeros((max(n.value, 1), 2), dtype=np.int32)
+    _check(lib.kv_paged_attention_prefill_plan(_p32(qs), _p32(lens), len(lens), num_q_heads,
+                                               num_kv_heads, _p32(out), out.shape[0], C.byref(n)),
+           "kv_paged_attention_prefill_plan")
+    return out[:n.value]
+
+
+def kv_paged_attention_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
+                               scale: float, max_query_len: int, work_items=None,
+                               stream=None) -> None:
+    """out fp32 [T, Hq, D]; q [T, Hq, D] f16/bf16; pools [NB, Hkv, B, D] of q's dtype;
+    tables int32 [S, max_blocks]; context_lens int32 [S]; query_start int32 [S + 1]."""
+    torch = _torch()
+    T, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_pool.shape
+    S = context_lens.numel()
+    if D2 != D or tuple(out.shape) != (T, Hq, D) or block_tables.shape[0] != S \
+            or query_start.numel() != S + 1 or q.dtype != k_pool.dtype \
+            or v_pool.shape != k_pool.shape:
+        raise KVError(KV_ERR_INVALID, "kv_paged_attention_prefill", "shape/dtype mismatch")
+    _check(lib.kv_paged_attention_prefill(
+        _dev(out, "out", torch.float32), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), _dev(query_start, "query_start", torch.int32),
+        S, T, Hq, Hkv, D, B, NB, float(scale), dtype_code(q), max_query_len,
+        None if work_items is None else _dev(work_items, "work_items", torch.int32),
+        0 if work_items is None else work_items.shape[0], _stream(stream)),
+        "kv_paged_attention_prefill")

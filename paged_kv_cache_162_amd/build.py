@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedkv.so")
 SOURCES = [os.path.join(CSRC, "host_pool.cpp"), os.path.join(CSRC, "plan.cpp"),
-           os.path.join(CSRC, "cache.hip"), os.path.join(CSRC, "decode.hip")]
+           os.path.join(CSRC, "cache.hip"), os.path.join(CSRC, "decode.hip"),
+           os.path.join(CSRC, "prefill.hip")]
 ARCH = os.environ.get("PAGEDKV_ARCH", "gfx950")
 
 

@@ -71,6 +71,101 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
+// ---- MFMA attention helpers (decode and prefill) ---------------------------
+// Lazy rescale slack of the online softmax, in base-2 units.
+constexpr float kRescaleSlack = 8.0f;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_qk(const uint4& a, const uint4& b, f32x4 c) {
+  if constexpr (DT == KV_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_pv(const uint2& a, const uint2& b, f32x4 c) {
+  if constexpr (DT == KV_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// Two fp32 values rounded (to nearest even) into one packed 16-bit pair, and
+// the two rounded values back as fp32.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (DT == KV_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+template <int DT>
+__device__ __forceinline__ void unpack2(uint32_t w, float& a, float& b) {
+  if constexpr (DT == KV_BF16) {
+    a = bf16lo(w);
+    b = bf16hi(w);
+  } else {
+    a = f16lo(w);
+    b = f16hi(w);
+  }
+}
+
+// Weights of 4 tokens as a B operand: the 16-bit high parts when
+// residual == 0, the 16-bit residuals x - high(x) when residual == 1.
+template <int DT>
+__device__ __forceinline__ uint2 weight_part(const float* x, float residual) {
+  uint32_t o[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t h = pack2<DT>(x[2 * i], x[2 * i + 1]);
+    float h0, h1;
+    unpack2<DT>(h, h0, h1);
+    o[i] = pack2<DT>(fmaf(-residual, h0, x[2 * i]), fmaf(-residual, h1, x[2 * i + 1]));
+  }
+  return make_uint2(o[0], o[1]);
+}
+
+// 16-bit element n (0..7) of the four V rows a lane holds, packed as an A
+// operand (row of token 4g in the low half of the first dword).
+__device__ __forceinline__ uint2 v_column(const uint4* v, int n) {
+  auto word = [](const uint4& u, int k) -> uint32_t {
+    return k == 0 ? u.x : (k == 1 ? u.y : (k == 2 ? u.z : u.w));
+  };
+  const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
+  const int k = n >> 1;
+  return make_uint2(__builtin_amdgcn_perm(word(v[1], k), word(v[0], k), sel),
+                    __builtin_amdgcn_perm(word(v[3], k), word(v[2], k), sel));
+}
+
+// Maximum and sum over the four lanes of an MFMA column (lanes l, l^16,
+// l^32, l^48), with the gfx950 row-swap instructions: permlane16_swap of x
+// with itself yields the values of rows (0,0,2,2) and (1,1,3,3), so
+// combining the two results reduces over row pairs; permlane32_swap does the
+// same for the two halves. The combination is symmetric, so every lane gets
+// the same value in the same order.
+__device__ __forceinline__ float column_max(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  u = __float_as_uint(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+  auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float column_sum(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  u = __float_as_uint(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+  auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+
 // ---- fp8 (OCP E4M3) cache ---------------------------------------------------
 // Four E4M3 codes (one dword, byte 0 first) as four 16-bit values of the
 // query's type, in the same order. Every E4M3 value is exact in f16 and bf16;

@@ -1,4 +1,4 @@
-// Host-side work plan for paged decode attention.
+// Host-side work plans for paged decode attention and chunked prefill.
 //
 // The decode kernel runs one workgroup per (sequence, KV head, context
 // partition). Built from the host's copy of the context lengths, the plan
@@ -50,6 +50,52 @@ extern "C" kv_status kv_paged_attention_plan(const int32_t* context_lens_host, i
   for (size_t i = 0; i < items.size(); ++i) {
     items_out[2 * i] = items[i].s;
     items_out[2 * i + 1] = items[i].p;
+  }
+  return KV_OK;
+}
+
+// Plan for the chunked-prefill kernel, which runs one workgroup per
+// (sequence, KV head, block of query rows): one item per block of
+// kv_paged_attention_prefill_rows_per_item rows of each sequence's chunk,
+// ordered by the number of keys the block's last row sees, most first, so
+// the longest workgroups start first. Blocks of an impossible sequence (chunk
+// longer than its context) come last; the kernel writes NaN for them.
+extern "C" kv_status kv_paged_attention_prefill_plan(const int32_t* query_start_host,
+                                                     const int32_t* context_lens_host, int32_t S,
+                                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                                     int32_t* items_out, int32_t cap,
+                                                     int32_t* n_items) {
+  pagedkv::clear_error();
+  if (!n_items || S < 0 || (S > 0 && (!query_start_host || !context_lens_host)))
+    return fail(KV_ERR_INVALID, "kv_paged_attention_prefill_plan: null argument or negative S");
+  const int32_t rpb = kv_paged_attention_prefill_rows_per_item(num_q_heads, num_kv_heads);
+  if (rpb <= 0)
+    return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_prefill_plan: heads %d / %d", num_q_heads,
+                num_kv_heads);
+  struct Item {
+    int32_t s, b;
+    int64_t keys;
+  };
+  std::vector<Item> items;
+  for (int32_t s = 0; s < S; ++s) {
+    const int64_t C = (int64_t)query_start_host[s + 1] - query_start_host[s];
+    if (C <= 0) continue;
+    const int64_t L = context_lens_host[s];
+    const int64_t nb = (C + rpb - 1) / rpb;
+    for (int64_t b = 0; b < nb; ++b) {
+      const int64_t keys = L < C ? -1 : (L - C) + std::min<int64_t>((b + 1) * rpb, C);
+      items.push_back({s, (int32_t)b, keys});
+    }
+  }
+  std::stable_sort(items.begin(), items.end(),
+                   [](const Item& a, const Item& b) { return a.keys > b.keys; });
+  *n_items = (int32_t)items.size();
+  if ((size_t)cap < items.size() || (!items_out && !items.empty()))
+    return fail(KV_ERR_INVALID, "kv_paged_attention_prefill_plan: capacity %d < %zu items", cap,
+                items.size());
+  for (size_t i = 0; i < items.size(); ++i) {
+    items_out[2 * i] = items[i].s;
+    items_out[2 * i + 1] = items[i].b;
   }
   return KV_OK;
 }

@@ -1,0 +1,386 @@
+// Device side of pagedkv for AMD CDNA4 (gfx950): attention of a chunk of new
+// query tokens per sequence over the paged cache, causal within the chunk
+// (chunked prefill).
+//
+// Pages cited in this file:
+//   [1] "PagedAttention - how vLLM stopped wasting 80% of your GPU memory"
+//       (shivam2003.com/posts/pagedattention.html)
+//   [2] "PagedAttention: How vLLM Borrowed Virtual Memory to Unlock GPU
+//       Serving at Scale" (fp4-site.pages.dev/system/pagedattention-vllm-deep-dive/)
+//   [4] "What is paged attention?" (netraruntime.com/learn/paged-attention)
+//
+// Chunked prefill feeds a prompt in pieces of a fixed token count ([2] "The
+// Successors - SGLang's RadixAttention and Prefix Sharing"); each piece's K
+// and V go into the sequence's blocks first ([2] "Walking Through the
+// Lifecycle", Prefill), then every query token of the piece attends to all
+// cached positions up to its own. Keys are reached through the block table
+// exactly as in decode ([4] "How it works"), so the result is the attention
+// of the contiguous cache ([1] "The PagedAttention kernel").
+//
+// Work split: one workgroup of four wave64s per (sequence, KV head, block of
+// query rows). The 16-key K/V tiles of the sequence are staged once per
+// workgroup in LDS (double buffered, loaded two tiles ahead) and shared by
+// the four waves. Each wave owns two 16-column MFMA tiles; a column is one
+// (query row, query head) pair of the KV head's group, so a group of G heads
+// gives 16 / G query rows per column tile. Per key tile a wave forms
+//   S^T[key][col] = K[key][:] . Q[col][:]         (4 x mfma 16x16x32 per column tile)
+//   O^T[d][col]  += V^T[d][key] . P^T[key][col]   (16 x mfma 16x16x16: the
+//                                                  weights as 16-bit high part
+//                                                  plus 16-bit residual)
+// with the causal rule key <= position(query) applied to the scores and an
+// online softmax per column (lazy rescale, as in decode).
+
+#include "device_common.h"
+
+using namespace pagedkv::dev;
+
+namespace {
+
+constexpr int kPfWaves = 4;        // waves per workgroup
+constexpr int kPfColTiles = 2;     // 16-column MFMA tiles per wave
+constexpr int kPfRowBytes = 272;   // LDS bytes per key row: 128 x 16-bit + 16 against bank conflicts
+constexpr int kPfSegment = 64;     // table entries staged at once (one per lane)
+constexpr int kPfKeys = 32;        // keys per LDS tile
+constexpr int kPfHeadDim = 128;
+
+struct PrefillParams {
+  float* out;              // [T][Hq][D] fp32
+  const void* q;           // [T][Hq][D]
+  const void* k_pool;      // [num_blocks][Hkv][B][D]
+  const void* v_pool;
+  const int32_t* tables;   // [S][max_blocks]
+  const int32_t* lens;     // [S] cached positions, the chunk included
+  const int32_t* q_start;  // [S + 1] first query row of each sequence
+  const int32_t* items;    // optional [n_items][2] = (sequence, query block)
+  int32_t T, S, Hq, Hkv, G, tpc, rows_per_block, max_blocks, num_blocks, n_units;
+  float scale_log2;
+};
+
+// Column tile of MFMA columns: query row of column c and whether it is live.
+struct ColTile {
+  int qrow;    // row of the chunk (0-based) this lane's column belongs to
+  int pos;     // its position in the sequence: keys up to pos are visible
+  bool live;
+};
+
+template <int DT, int BS>
+__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
+  constexpr int D = kPfHeadDim;
+  constexpr int kRowU4 = D / 8;  // uint4 per 16-bit key row
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+
+  int s, h, qblk;
+  if (p.items) {
+    const int it = blockIdx.x / p.Hkv;
+    h = blockIdx.x % p.Hkv;
+    s = p.items[2 * it];
+    qblk = p.items[2 * it + 1];
+  } else {
+    s = blockIdx.x % p.S;
+    h = (blockIdx.x / p.S) % p.Hkv;
+    qblk = blockIdx.x / (p.S * p.Hkv);
+  }
+  if (s < 0 || s >= p.S || qblk < 0) return;
+  const int r_begin = p.q_start[s], r_end = p.q_start[s + 1];
+  if (r_begin < 0 || r_end > p.T || r_end < r_begin) return;  // no row can be placed safely
+  const int C = r_end - r_begin;
+  const int row0 = qblk * p.rows_per_block;
+  if (row0 >= C) return;
+  const int rows = min(p.rows_per_block, C - row0);
+  const int L = p.lens[s];
+  const float nan = __builtin_nanf("");
+  if (L < C || (int64_t)L > (int64_t)p.max_blocks * BS) {
+    // impossible length: the block's rows get NaN
+    for (int i = tid; i < rows * p.G * (D / 4); i += blockDim.x) {
+      const int rr = i / (p.G * (D / 4)), rem = i % (p.G * (D / 4));
+      float* dst = p.out + ((size_t)(r_begin + row0 + rr) * p.Hq + (size_t)h * p.G) * D;
+      reinterpret_cast<float4*>(dst)[rem] = make_float4(nan, nan, nan, nan);
+    }
+    return;
+  }
+  const int prev = L - C;
+  const int nkeys = prev + row0 + rows;  // keys the block's last query sees
+  const int ntiles = (nkeys + kPfKeys - 1) / kPfKeys;
+  const int last = ntiles - 1;
+  const int nblk = (nkeys + BS - 1) / BS;  // table entries in use
+
+  // ---- columns and queries of this wave --------------------------------------
+  ColTile ct[kPfColTiles];
+  uint4 qb[kPfColTiles][4];
+  const int hd = col % p.G;
+#pragma unroll
+  for (int t = 0; t < kPfColTiles; ++t) {
+    const int qr = row0 + (wave * kPfColTiles + t) * p.tpc + col / p.G;
+    ct[t].live = col < p.tpc * p.G && qr < row0 + rows;
+    ct[t].qrow = qr;
+    // a dead column sees every key (finite softmax of zero scores), never stored
+    ct[t].pos = ct[t].live ? prev + qr : nkeys - 1;
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(p.q) +
+        (((size_t)r_begin + (ct[t].live ? qr : row0)) * p.Hq + (size_t)h * p.G +
+         (ct[t].live ? hd : 0)) * D * 2);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const uint4 v = qp[kc * 4 + grp];
+      qb[t][kc] = ct[t].live ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // ---- block table: 64 entries at a time, one per lane -----------------------
+  int staged = 0, seg = -1;
+  bool bad = false;
+  auto stage = [&](int sg) {
+    const int b = sg * kPfSegment + lane;
+    int e = 0;
+    if (b < p.max_blocks) e = p.tables[(size_t)s * p.max_blocks + b];
+    const bool need = b < nblk;
+    const bool oob = need && (e < 0 || e >= p.num_blocks);
+    bad = bad || __builtin_amdgcn_ballot_w64(oob) != 0;
+    staged = (oob || !need) ? 0 : e;  // out-of-pool and unused entries read block 0
+    seg = sg;
+  };
+  // uint4 index of key row r (0..31) of 32-key tile j. The block index is
+  // wave-uniform: a wave loads rows 4w..4w+3 and 16+4w..16+4w+3, and no
+  // group of four straddles two 8-token blocks
+  auto key_row = [&](int j, int r) -> size_t {
+    const int key = kPfKeys * j + r;
+    const int bi = key / BS, rb = key % BS;
+    const int sg = bi / kPfSegment;
+    if (sg != seg) stage(sg);
+    const int e = __builtin_amdgcn_readlane(staged, bi % kPfSegment);
+    return (((size_t)e * p.Hkv + h) * BS + rb) * kRowU4;
+  };
+
+  // ---- LDS tiles of 32 keys: [buffer][K, V][row] -----------------------------
+  __shared__ __align__(16) unsigned char lds[2][2][kPfKeys * kPfRowBytes];
+  const int lr = tid >> 4, lc = tid & 15;  // rows lr and lr + 16, 16-byte chunk lc
+  const uint4* kpool = static_cast<const uint4*>(p.k_pool);
+  const uint4* vpool = static_cast<const uint4*>(p.v_pool);
+  auto load = [&](int j, uint4* g) {
+    const size_t r0 = key_row(j, lr), r1 = key_row(j, lr + 16);
+    g[0] = kpool[r0 + lc];
+    g[1] = vpool[r0 + lc];
+    g[2] = kpool[r1 + lc];
+    g[3] = vpool[r1 + lc];
+  };
+  auto store = [&](int j, const uint4* g, int buf) {
+    // rows past the visible keys may hold anything: they are stored as zeros
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = lr + 16 * half;
+      const uint32_t mk = kPfKeys * j + row >= nkeys ? 0u : ~0u;
+      const uint4 kk = g[2 * half], vv = g[2 * half + 1];
+      *reinterpret_cast<uint4*>(&lds[buf][0][row * kPfRowBytes + lc * 16]) =
+          make_uint4(kk.x & mk, kk.y & mk, kk.z & mk, kk.w & mk);
+      *reinterpret_cast<uint4*>(&lds[buf][1][row * kPfRowBytes + lc * 16]) =
+          make_uint4(vv.x & mk, vv.y & mk, vv.z & mk, vv.w & mk);
+    }
+  };
+
+  f32x4 o[kPfColTiles][8];
+  float m[kPfColTiles], l[kPfColTiles];
+#pragma unroll
+  for (int t = 0; t < kPfColTiles; ++t) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[t] = neg_inf();
+    l[t] = 0.f;
+  }
+  const int first_pos = prev + row0;  // smallest position among the block's queries
+
+  // One 32-key tile. The score MFMAs run per 16-key half (lane: keys 4g..4g+3
+  // of each half); the value MFMA takes all 32 keys at once, its reduction
+  // index 8g+i standing for key 4g+i of the first half (i < 4) and key
+  // 16+4g+i-4 of the second, in both operands.
+  auto compute = [&](int j, int buf) {
+    // scores of every column tile first (K operands live), then the softmax,
+    // then the value products (V operands live): the two never overlap
+    float x[kPfColTiles][8];
+    {
+      uint4 ku[2][4];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+          ku[half][kc] = *reinterpret_cast<const uint4*>(
+              &lds[buf][0][(16 * half + col) * kPfRowBytes + (kc * 4 + grp) * 16]);
+#pragma unroll
+      for (int t = 0; t < kPfColTiles; ++t)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) st = mfma_qk<DT>(ku[half][kc], qb[t][kc], st);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[t][4 * half + r] = st[r] * p.scale_log2;
+        }
+    }
+    const bool causal = kPfKeys * j + kPfKeys - 1 > first_pos;  // some key hidden from some query
+    uint4 ph[kPfColTiles], pl[kPfColTiles];
+#pragma unroll
+    for (int t = 0; t < kPfColTiles; ++t) {
+      if (causal) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (kPfKeys * j + 16 * (i >> 2) + 4 * grp + (i & 3) > ct[t].pos) x[t][i] = neg_inf();
+      }
+      float lm = x[t][0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) lm = fmaxf(lm, x[t][i]);
+      if (__builtin_amdgcn_ballot_w64(lm > m[t] + kRescaleSlack) != 0) {
+        const float mn = fmaxf(m[t], column_max(lm));
+        const float alpha = fast_exp2(m[t] - mn);  // 0 while m is -inf
+        l[t] *= alpha;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) o[t][n] *= alpha;
+        m[t] = mn;
+      }
+      float pw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pw[i] = fast_exp2(x[t][i] - m[t]);  // 0 for hidden keys
+        l[t] += pw[i];
+      }
+      const uint2 h0 = weight_part<DT>(pw, 0.0f), h1 = weight_part<DT>(pw + 4, 0.0f);
+      const uint2 r0 = weight_part<DT>(pw, 1.0f), r1 = weight_part<DT>(pw + 4, 1.0f);
+      ph[t] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+      pl[t] = make_uint4(r0.x, r0.y, r1.x, r1.y);
+    }
+    uint4 vu[2][4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        vu[half][jj] = *reinterpret_cast<const uint4*>(
+            &lds[buf][1][(16 * half + 4 * grp + jj) * kPfRowBytes + col * 16]);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const uint2 a0 = v_column(vu[0], n), a1 = v_column(vu[1], n);
+      const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
+#pragma unroll
+      for (int t = 0; t < kPfColTiles; ++t) {
+        o[t][n] = mfma_qk<DT>(a, ph[t], o[t][n]);
+        o[t][n] = mfma_qk<DT>(a, pl[t], o[t][n]);
+      }
+    }
+  };
+
+  // ---- pipeline: tile j + 1 is in registers while tile j is computed from
+  // LDS buffer j % 2; loads and stores past the last tile repeat the last
+  // tile (in bounds, never computed).
+  uint4 g[4];
+  load(0, g);
+  store(0, g, 0);
+  load(min(1, last), g);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    compute(j, j & 1);
+    store(min(j + 1, last), g, (j + 1) & 1);
+    load(min(j + 2, last), g);
+    __syncthreads();
+  }
+
+  // ---- results: lane holds column col, dims 32grp + 8r + n (n < 8) -----------
+#pragma unroll
+  for (int t = 0; t < kPfColTiles; ++t) {
+    const float lt = column_sum(l[t]);
+    if (!ct[t].live) continue;
+    const float inv = 1.0f / lt;
+    float* dst = p.out + (((size_t)r_begin + ct[t].qrow) * p.Hq + (size_t)h * p.G + hd) * D +
+                 32 * grp;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float4 a = make_float4(o[t][0][r] * inv, o[t][1][r] * inv, o[t][2][r] * inv, o[t][3][r] * inv);
+      float4 b = make_float4(o[t][4][r] * inv, o[t][5][r] * inv, o[t][6][r] * inv, o[t][7][r] * inv);
+      if (bad) a = b = make_float4(nan, nan, nan, nan);
+      *reinterpret_cast<float4*>(dst + 8 * r) = a;
+      *reinterpret_cast<float4*>(dst + 8 * r + 4) = b;
+    }
+  }
+}
+
+int32_t rows_per_block(int32_t G) { return kPfWaves * kPfColTiles * (16 / G); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t kv_paged_attention_prefill_rows_per_item(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
+  const int32_t G = num_q_heads / num_kv_heads;
+  return G > 16 ? 0 : rows_per_block(G);
+}
+
+kv_status kv_paged_attention_prefill(float* out, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_tables,
+                                     int32_t max_blocks, const int32_t* context_lens,
+                                     const int32_t* query_start, int32_t S, int32_t total_q,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t num_blocks, float scale,
+                                     kv_dtype dtype, int32_t max_query_len,
+                                     const int32_t* work_items, int32_t n_items,
+                                     hipStream_t stream) {
+  pagedkv::clear_error();
+  const char* who = "kv_paged_attention_prefill";
+  if (dtype != KV_F16 && dtype != KV_BF16)
+    return fail(KV_ERR_UNSUPPORTED, "%s: dtype must be f16 or bf16", who);
+  if (S < 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks < 0 ||
+      num_blocks <= 0 || max_query_len < 0)
+    return fail(KV_ERR_INVALID, "%s: bad sizes", who);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(KV_ERR_UNSUPPORTED, "%s: query heads %d not a multiple of KV heads %d", who,
+                num_q_heads, num_kv_heads);
+  const int32_t G = num_q_heads / num_kv_heads;
+  if (G > 16) return fail(KV_ERR_UNSUPPORTED, "%s: group size %d > 16", who, G);
+  if (head_dim != kPfHeadDim)
+    return fail(KV_ERR_UNSUPPORTED, "%s: head_dim %d (128)", who, head_dim);
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(KV_ERR_UNSUPPORTED, "%s: block_size %d (8, 16 or 32)", who, block_size);
+  if (S == 0 || total_q == 0) return KV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
+    return fail(KV_ERR_INVALID, "%s: null pointer", who);
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(KV_ERR_INVALID, "%s: out/q/pools must be 16-byte aligned", who);
+  if (work_items && n_items <= 0)
+    return fail(KV_ERR_INVALID, "%s: work plan with %d items", who, n_items);
+  const int32_t rpb = rows_per_block(G);
+  const int64_t n_units = work_items ? (int64_t)n_items * num_kv_heads
+                                     : (int64_t)S * num_kv_heads * ceil_div64(max_query_len, rpb);
+  if (n_units > INT32_MAX) return fail(KV_ERR_INVALID, "%s: too many work units", who);
+  if (n_units == 0) return KV_OK;
+
+  PrefillParams prm;
+  prm.out = out;
+  prm.q = q;
+  prm.k_pool = k_pool;
+  prm.v_pool = v_pool;
+  prm.tables = block_tables;
+  prm.lens = context_lens;
+  prm.q_start = query_start;
+  prm.items = work_items;
+  prm.T = total_q;
+  prm.S = S;
+  prm.Hq = num_q_heads;
+  prm.Hkv = num_kv_heads;
+  prm.G = G;
+  prm.tpc = 16 / G;
+  prm.rows_per_block = rpb;
+  prm.max_blocks = max_blocks;
+  prm.num_blocks = num_blocks;
+  prm.n_units = (int32_t)n_units;
+  prm.scale_log2 = scale * 1.4426950408889634f;
+
+  auto kern = dtype == KV_BF16
+                  ? (block_size == 8    ? prefill_mfma_kernel<KV_BF16, 8>
+                     : block_size == 16 ? prefill_mfma_kernel<KV_BF16, 16>
+                                        : prefill_mfma_kernel<KV_BF16, 32>)
+                  : (block_size == 8    ? prefill_mfma_kernel<KV_F16, 8>
+                     : block_size == 16 ? prefill_mfma_kernel<KV_F16, 16>
+                                        : prefill_mfma_kernel<KV_F16, 32>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)n_units), dim3(kPfWaves * 64), 0, stream, prm);
+  return launch_status(who);
+}
+
+}  // extern "C"

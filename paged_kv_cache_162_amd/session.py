@@ -137,6 +137,57 @@ class DecodeSession:
             max_blocks = max(1, max(-(-kv.kv_seq_len(self.pool, h) // self.B) for h in ids))
         return kv.kv_seq_pack_tables(self.pool, ids, max_blocks)
 
+    # -- a chunked-prefill step ----------------------------------------------
+    def prepare_prefill(self, seqs: Sequence[int], counts: Sequence[int]):
+        """Host half of a chunked-prefill step: reserve counts[i] new positions
+        for sequence seqs[i] and upload the slots, tables, lengths, query row
+        ranges and the work plan. Returns the host-side slots and any
+        copy-on-write pairs."""
+        if self.fp8:
+            raise kv.KVError(kv.KV_ERR_UNSUPPORTED, "prepare_prefill", "fp8 pools")
+        torch = self.torch
+        dev = self.device
+        slots, pairs = [], []
+        for s, n in zip(seqs, counts):
+            sl, pair = kv.kv_seq_append(self.pool, self.handles[s], int(n))
+            slots.append(sl)
+            if pair is not None:
+                pairs.append(pair)
+        host_slots = np.concatenate(slots).astype(np.int64) if slots else np.zeros(0, np.int64)
+        tables, lens = self.tables(seqs)
+        q_start = np.concatenate([[0], np.cumsum(np.asarray(counts, np.int64))]).astype(np.int32)
+        self.seqs = list(seqs)
+        self.d_tables = torch.from_numpy(tables).to(dev)
+        self.d_lens = torch.from_numpy(lens).to(dev)
+        self.d_qstart = torch.from_numpy(q_start).to(dev)
+        self.d_slots = torch.from_numpy(host_slots).to(dev)
+        self.d_pairs = torch.tensor(pairs, dtype=torch.int32, device=dev).reshape(-1, 2)
+        self.max_query_len = int(max(counts)) if len(counts) else 0
+        self.host_tables, self.host_lens, self.host_qstart = tables, lens, q_start
+        self.d_items = None
+        if self.use_plan:
+            items = kv.kv_paged_attention_prefill_plan(q_start, lens, self.Hq, self.Hkv)
+            self.d_items = torch.from_numpy(items).to(dev) if len(items) else None
+        return host_slots, pairs
+
+    def prefill_step(self, q, k_new, v_new, out, scale: float, k_pool=None, v_pool=None,
+                     events=None) -> None:
+        """Device half of a chunked-prefill step on the current stream:
+        copy-on-write copies (if any), the chunk's K/V written into its slots,
+        then the causal attention of every chunk row. `events` = (start, end)
+        torch events recorded around the attention launch."""
+        kp = self.k_pool if k_pool is None else k_pool
+        vp_ = self.v_pool if v_pool is None else v_pool
+        if self.d_pairs.shape[0]:
+            kv.kv_copy_blocks([kp], [vp_], self.d_pairs, self.NB, self.block_bytes)
+        kv.kv_reshape_and_cache(k_new, v_new, kp, vp_, self.d_slots)
+        if events is not None:
+            events[0].record()
+        kv.kv_paged_attention_prefill(out, q, kp, vp_, self.d_tables, self.d_lens, self.d_qstart,
+                                      scale, self.max_query_len, self.d_items)
+        if events is not None:
+            events[1].record()
+
     # -- the decode step ----------------------------------------------------
     def prepare_step(self, seqs: Sequence[int]):
         """Host half of a decode step: reserve one new slot per sequence and

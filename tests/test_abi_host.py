@@ -318,3 +318,34 @@ def test_fp8_entry_points_validate_on_the_host(kv):
     assert lib.kv_paged_attention_decode(None, None, None, None, None, 4, None, 1, 8, 2, 128, 16, 8,
                                          1.0, kv.KV_FP8_E4M3, 0, 16, None, 0, None, 0, None) \
         == kv.KV_ERR_UNSUPPORTED
+
+
+def test_prefill_entry_points_validate_on_the_host(kv):
+    lib = kv.lib
+
+    def call(**k):
+        return lib.kv_paged_attention_prefill(
+            None, None, None, None, None, 4, None, None, k.get("S", 1), k.get("T", 4),
+            k.get("Hq", 8), k.get("Hkv", 2), k.get("D", 128), k.get("B", 16), 8, 1.0,
+            k.get("dt", kv.KV_BF16), 4, None, 0, None)
+    assert call(dt=kv.KV_F32) == kv.KV_ERR_UNSUPPORTED
+    assert call(dt=kv.KV_FP8_E4M3) == kv.KV_ERR_UNSUPPORTED
+    assert call(D=64) == kv.KV_ERR_UNSUPPORTED
+    assert call(Hq=64, Hkv=2) == kv.KV_ERR_UNSUPPORTED   # group of 32
+    assert call(Hq=7) == kv.KV_ERR_UNSUPPORTED
+    assert call(B=12) == kv.KV_ERR_UNSUPPORTED
+    assert call() == kv.KV_ERR_INVALID                   # null pointers
+    assert call(S=0) == kv.KV_OK and call(T=0) == kv.KV_OK
+    assert kv.kv_paged_attention_prefill_rows_per_item(64, 8) == 16
+    assert kv.kv_paged_attention_prefill_rows_per_item(32, 32) == 128
+    assert kv.kv_paged_attention_prefill_rows_per_item(64, 2) == 0
+
+
+def test_prefill_plan_orders_blocks_by_keys(kv):
+    # sequence 0: 3 rows over 10 keys; 1: empty chunk; 2: 37 rows over 50 keys
+    # (blocks of 16 rows see 29, 45 and 50 keys); 3: chunk longer than its context
+    items = kv.kv_paged_attention_prefill_plan([0, 3, 3, 40, 44], [10, 5, 50, 2], 64, 8)
+    assert items.tolist() == [[2, 2], [2, 1], [2, 0], [0, 0], [3, 0]]
+    assert len(kv.kv_paged_attention_prefill_plan([0, 0], [7], 64, 8)) == 0
+    with pytest.raises(kv.KVError):
+        kv.kv_paged_attention_prefill_plan([0, 3], [10], 64, 2)

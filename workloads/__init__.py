@@ -27,7 +27,10 @@ Workload recipe (all seeded):
     subnormals and zero) and a uniform mantissa, i.e. magnitudes up to 7.5,
     read with a per-pool scale of 1/4; the new token's K/V stay 16-bit
     N(0,1) values (the cache write quantises them);
-  * an operation script (create / append / fork) that builds the sequences.
+  * an operation script (create / append / fork) that builds the sequences;
+  * the chunked-prefill workload (8) gives every sequence a cached prefix
+    (lognormal like workload 3) and a chunk of new tokens: its queries are
+    [S * chunk, Hq, D] and its new K/V [S * chunk, Hkv, D], N(0,1) as above.
 Heavy-tailed lengths follow the shape [2] describes for production traffic
 ("The Fragmentation Problem"): many short requests and a long tail. The
 lognormal spread is taken from the eight-request sample of [3] ("A
@@ -102,6 +105,8 @@ class WorkloadSpec:
     v_scale: float = 1.0
     # default seed taken from this workload number (same lengths and queries)
     seed_cfg: int = 0
+    # chunked prefill: query tokens per sequence in the step (0 = decode, 1 token)
+    chunk: int = 0
     description: str = ""
 
     @property
@@ -150,6 +155,12 @@ SPECS = {
                     description="as the prefix-share workload but forked inside "
                                 "a block (2056 shared tokens), so the first "
                                 "write of each fork copies the partial block"),
+    8: WorkloadSpec(8, "llama70b-gqa-chunked-prefill-bf16", S=16, Hq=64, Hkv=8, D=128,
+                    dtype="bf16", chunk=256,
+                    description="16 sequences, each with a cached prefix of "
+                                "lognormal length (median 512, sigma 0.86) and "
+                                "a 256-token chunk attended causally; 64 query / "
+                                "8 KV heads, head_dim 128, bf16"),
     7: WorkloadSpec(7, "llama70b-gqa-fp8", S=128, Hq=64, Hkv=8, D=128, dtype="bf16",
                     kv_dtype="e4m3", k_scale=0.25, v_scale=0.25, seed_cfg=3,
                     description="the llama70b-gqa-bf16 workload (same lengths, "
@@ -224,6 +235,9 @@ def _context_lengths(sp: WorkloadSpec, rng: np.random.Generator) -> np.ndarray:
     if sp.cfg in (3, 7):
         x = np.exp(rng.normal(math.log(512.0), 0.86, size=sp.S))
         return np.clip(np.rint(x), 16, 8192).astype(np.int32)
+    if sp.cfg == 8:
+        x = np.exp(rng.normal(math.log(512.0), 0.86, size=sp.S))
+        return (np.clip(np.rint(x), 0, 8192 - sp.chunk) + sp.chunk).astype(np.int32)
     if sp.cfg == 4:
         return np.full(sp.S, 32768, dtype=np.int32)
     if sp.cfg in (5, 6):
@@ -238,7 +252,7 @@ def _pool_blocks(sp: WorkloadSpec, lens: np.ndarray) -> int:
         return 32
     if sp.cfg == 2:
         return 8192 * 16 // B  # the worst case, 64 sequences of 2048 tokens
-    if sp.cfg in (3, 7):
+    if sp.cfg in (3, 7, 8):
         need = int(sum(-(-int(t) // B) for t in lens))
         return int(math.ceil(1.1 * need))
     if sp.cfg == 4:
@@ -289,23 +303,26 @@ def make_workload(cfg: int, seed: Optional[int] = None, *, with_values: bool = T
             # tagged: these tokens' K/V are written from tail_k / tail_v
             setup.append(("append", s_, sp.tail, "values"))
     else:
+        step_n = sp.chunk or 1
         for s_ in range(sp.S):
             setup.append(("create", s_))
-            setup.append(("append", s_, int(lens[s_]) - 1))
+            if int(lens[s_]) > step_n:
+                setup.append(("append", s_, int(lens[s_]) - step_n))
     for s_ in range(sp.S):
-        step.append(("append", s_, 1))
+        step.append(("append", s_, sp.chunk or 1))
 
     Hkv, D, B = sp.Hkv, sp.D, sp.block_size
     if with_values:
-        q = _normal(r_q, (sp.S, sp.Hq, D), sp.dtype)
+        T = sp.S * (sp.chunk or 1)
+        q = _normal(r_q, (T, sp.Hq, D), sp.dtype) if sp.chunk else _normal(r_q, (sp.S, sp.Hq, D), sp.dtype)
         if sp.kv_dtype == "e4m3":
             k_pool = _e4m3_codes(r_k, (NB, Hkv, B, D))
             v_pool = _e4m3_codes(r_v, (NB, Hkv, B, D))
         else:
             k_pool = _normal(r_k, (NB, Hkv, B, D), sp.dtype)
             v_pool = _normal(r_v, (NB, Hkv, B, D), sp.dtype)
-        k_new = _normal(r_new, (sp.S, Hkv, D), sp.dtype)
-        v_new = _normal(r_new, (sp.S, Hkv, D), sp.dtype)
+        k_new = _normal(r_new, (T, Hkv, D), sp.dtype)
+        v_new = _normal(r_new, (T, Hkv, D), sp.dtype)
         tail_k = tail_v = None
         if sp.shared_prefix:
             tail_k = _normal(r_new, (sp.S, sp.tail, Hkv, D), sp.dtype)
