@@ -270,7 +270,7 @@ def prefill_bench(args, w, kv, torch):
     tflops_step = flops / (step_ms * 1e-3) / 1e12
     achieved = flops / (att_ms * 1e-3) / 1e12
     traffic = None
-    tpath = args.pmc_traffic or os.path.join(ROOT, "profiles", f"decode_traffic_w{args.workload}.json")
+    tpath = args.pmc_traffic or os.path.join(ROOT, "profiles", f"prefill_traffic_w{args.workload}.json")
     if os.path.exists(tpath):
         t = json.load(open(tpath))
         if t.get("kernel_source_digest") == kernel_source_digest(PREFILL_SOURCES) and \
@@ -396,7 +396,8 @@ SWAP_TOKENS = 4096
 def main():
     args = parse()
     if args.pmc_parse:
-        out = args.pmc_out or os.path.join(ROOT, "profiles", f"decode_traffic_w{args.workload}.json")
+        kind = "prefill" if is_prefill(args.workload) else "decode"
+        out = args.pmc_out or os.path.join(ROOT, "profiles", f"{kind}_traffic_w{args.workload}.json")
         pmc_parse(args.pmc_parse[0], args.pmc_parse[1], out, args.workload, args.partition or 512)
         return
     if args.gpus != 1:

@@ -64,7 +64,8 @@ struct ColTile {
 };
 
 template <int DT, int BS>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_mfma_kernel(PrefillParams p) {
   constexpr int D = kPfHeadDim;
   constexpr int kRowU4 = D / 8;  // uint4 per 16-bit key row
   const int tid = threadIdx.x;
@@ -194,9 +195,25 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   // of each half); the value MFMA takes all 32 keys at once, its reduction
   // index 8g+i standing for key 4g+i of the first half (i < 4) and key
   // 16+4g+i-4 of the second, in both operands.
+  // Weights of 8 keys as the value product's B operands: 16-bit high parts
+  // and 16-bit residuals w - high(w).
+  auto split_weights = [&](const float* w, uint4& hi, uint4& lo) {
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hw[i] = pack2<DT>(w[2 * i], w[2 * i + 1]);
+      float a, b;
+      unpack2<DT>(hw[i], a, b);
+      lw[i] = pack2<DT>(w[2 * i] - a, w[2 * i + 1] - b);
+    }
+    hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    lo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  };
+
   auto compute = [&](int j, int buf) {
-    // scores of every column tile first (K operands live), then the softmax,
-    // then the value products (V operands live): the two never overlap
+    // raw scores of every column tile first (K operands live); then per
+    // column tile the softmax and the value products, so the MFMAs of one
+    // tile can overlap the softmax of the next
     float x[kPfColTiles][8];
     {
       uint4 ku[2][4];
@@ -214,11 +231,18 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
 #pragma unroll
           for (int kc = 0; kc < 4; ++kc) st = mfma_qk<DT>(ku[half][kc], qb[t][kc], st);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[t][4 * half + r] = st[r] * p.scale_log2;
+          for (int r = 0; r < 4; ++r) x[t][4 * half + r] = st[r];
         }
     }
+    uint4 vu[2][4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        vu[half][jj] = *reinterpret_cast<const uint4*>(
+            &lds[buf][1][(16 * half + 4 * grp + jj) * kPfRowBytes + col * 16]);
     const bool causal = kPfKeys * j + kPfKeys - 1 > first_pos;  // some key hidden from some query
-    uint4 ph[kPfColTiles], pl[kPfColTiles];
+    const float sl = p.scale_log2;  // > 0, so the maximum commutes with the scaling
 #pragma unroll
     for (int t = 0; t < kPfColTiles; ++t) {
       if (causal) {
@@ -229,6 +253,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
       float lm = x[t][0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) lm = fmaxf(lm, x[t][i]);
+      lm *= sl;
       if (__builtin_amdgcn_ballot_w64(lm > m[t] + kRescaleSlack) != 0) {
         const float mn = fmaxf(m[t], column_max(lm));
         const float alpha = fast_exp2(m[t] - mn);  // 0 while m is -inf
@@ -238,47 +263,42 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
         m[t] = mn;
       }
       float pw[8];
+      const float nm = -m[t];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        pw[i] = fast_exp2(x[t][i] - m[t]);  // 0 for hidden keys
+        pw[i] = fast_exp2(fmaf(x[t][i], sl, nm));  // 0 for hidden keys
         l[t] += pw[i];
       }
-      const uint2 h0 = weight_part<DT>(pw, 0.0f), h1 = weight_part<DT>(pw + 4, 0.0f);
-      const uint2 r0 = weight_part<DT>(pw, 1.0f), r1 = weight_part<DT>(pw + 4, 1.0f);
-      ph[t] = make_uint4(h0.x, h0.y, h1.x, h1.y);
-      pl[t] = make_uint4(r0.x, r0.y, r1.x, r1.y);
-    }
-    uint4 vu[2][4];
+      uint4 ph, pl;
+      split_weights(pw, ph, pl);
 #pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        vu[half][jj] = *reinterpret_cast<const uint4*>(
-            &lds[buf][1][(16 * half + 4 * grp + jj) * kPfRowBytes + col * 16]);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const uint2 a0 = v_column(vu[0], n), a1 = v_column(vu[1], n);
-      const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
-#pragma unroll
-      for (int t = 0; t < kPfColTiles; ++t) {
-        o[t][n] = mfma_qk<DT>(a, ph[t], o[t][n]);
-        o[t][n] = mfma_qk<DT>(a, pl[t], o[t][n]);
+      for (int n = 0; n < 8; ++n) {
+        const uint2 a0 = v_column(vu[0], n), a1 = v_column(vu[1], n);
+        const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
+        o[t][n] = mfma_qk<DT>(a, ph, o[t][n]);
+        o[t][n] = mfma_qk<DT>(a, pl, o[t][n]);
       }
     }
   };
 
-  // ---- pipeline: tile j + 1 is in registers while tile j is computed from
-  // LDS buffer j % 2; loads and stores past the last tile repeat the last
-  // tile (in bounds, never computed).
-  uint4 g[4];
-  load(0, g);
-  store(0, g, 0);
-  load(min(1, last), g);
+  // ---- pipeline: tile t is loaded into register slot t % 2 two tiles ahead,
+  // stored into LDS buffer t % 2 and computed after a barrier; loads and
+  // stores past the last tile repeat the last tile (in bounds, never computed)
+  uint4 g0[4], g1[4];
+  load(0, g0);
+  store(0, g0, 0);
+  load(min(1, last), g1);
+  load(min(2, last), g0);
   __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    compute(j, j & 1);
-    store(min(j + 1, last), g, (j + 1) & 1);
-    load(min(j + 2, last), g);
+  for (int j = 0; j < ntiles; j += 2) {
+    compute(j, 0);
+    store(min(j + 1, last), g1, 1);
+    load(min(j + 3, last), g1);
+    __syncthreads();
+    if (j + 1 >= ntiles) break;
+    compute(j + 1, 1);
+    store(min(j + 2, last), g0, 0);
+    load(min(j + 4, last), g0);
     __syncthreads();
   }
 
