@@ -193,3 +193,32 @@ def test_fp8_fused_step_is_bit_identical_to_unfused():
         assert np.array_equal(bits(a) if a.dtype != np.int64 else a,
                               bits(b) if b.dtype != np.int64 else b)
 
+
+
+def test_fp8_graph_replay_matches_eager():
+    """The fused fp8 step captured in a HIP graph: every replay, with eager
+    work and synchronisations in between, reproduces the eager outputs, pools
+    and slots bit for bit."""
+    case = Case(7, S=10)
+    case.device_run()
+    sess = case.sess
+    eager = (case.out_dev.cpu().numpy().copy(), to_host(case.k_dev, "e4m3").copy(),
+             to_host(case.v_dev, "e4m3").copy(), sess.d_slots.cpu().numpy().copy())
+    out = torch.full_like(case.out_dev, float("nan"))
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            sess.step(case.q_dev, case.kn_dev, case.vn_dev, out, case.sp.scale)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        sess.d_slots.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"[gpu] fp8 graph replay {rep}")
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), eager[0].view(np.uint32))
+        assert np.array_equal(to_host(case.k_dev, "e4m3"), eager[1])
+        assert np.array_equal(to_host(case.v_dev, "e4m3"), eager[2])
+        assert np.array_equal(sess.d_slots.cpu().numpy(), eager[3])
