@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=3, help="workload number 1-7")
+    ap.add_argument("--workload", type=int, default=3, help="workload number 1-9")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--block-size", type=int, default=16, help="tokens per KV block (8, 16 or 32)")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas to rotate (0 = auto)")
@@ -228,9 +228,9 @@ def prefill_bench(args, w, kv, torch):
     from paged_kv_cache_162_amd.session import DecodeSession
     sp = w.spec
     dt = sp.dtype
-    kp, vp = to_dev(w.k_pool, dt), to_dev(w.v_pool, dt)
+    kp, vp = to_dev(w.k_pool, sp.cache_dtype), to_dev(w.v_pool, sp.cache_dtype)
     sess = DecodeSession(k_pool=kp, v_pool=vp, num_q_heads=sp.Hq, free_order=w.free_order,
-                         use_plan=not args.no_plan)
+                         use_plan=not args.no_plan, k_scale=sp.k_scale, v_scale=sp.v_scale)
     sess.run_ops(w.setup_ops)
     counts = [sp.chunk] * sp.S
     sess.prepare_prefill(list(range(sp.S)), counts)
@@ -288,13 +288,15 @@ def prefill_bench(args, w, kv, torch):
                    "chunk_tokens": sp.chunk, "q_heads": sp.Hq, "kv_heads": sp.Hkv,
                    "head_dim": sp.D, "block_size": args.block_size,
                    "sum_context": int(lens.sum()), "max_context": int(lens.max()),
-                   "flops_per_step": flops, "replicas_rotated": R, "parallelism": "single GPU"},
+                   "flops_per_step": flops, "replicas_rotated": R, "parallelism": "single GPU",
+                   "kv_cache_dtype": sp.cache_dtype},
         "query_tokens_per_s": round(T / (step_ms * 1e-3), 1),
         "attention_ms": round(att_ms, 5),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": "kv_paged_attention_prefill call: prefill_mfma_kernel",
+                     "kernel": "kv_paged_attention_prefill%s call: prefill_mfma_kernel"
+                               % ("_fp8" if sp.kv_dtype else ""),
                      "alg_flops_per_launch": flops},
     }
     if not args.no_cpu_baseline:
@@ -318,8 +320,14 @@ def prefill_cpu_baseline(w, lens, counts, seconds):
         for s in range(w.S):
             rows = range(int(qs[s]), int(qs[s + 1]))
             t0 = time.perf_counter()
-            oracle.prefill_attention(w.q, qs, w.k_pool, w.v_pool, tables, lens, sp.scale, sp.dtype,
-                                     block_size=sp.block_size, rows=rows)
+            if sp.kv_dtype:
+                oracle.prefill_attention(w.q, qs, w.k_pool, w.v_pool, tables, lens, sp.scale,
+                                         sp.dtype, block_size=sp.block_size, rows=rows,
+                                         kv_dtype=sp.kv_dtype, k_scale=sp.k_scale,
+                                         v_scale=sp.v_scale)
+            else:
+                oracle.prefill_attention(w.q, qs, w.k_pool, w.v_pool, tables, lens, sp.scale,
+                                         sp.dtype, block_size=sp.block_size, rows=rows)
             t_total += time.perf_counter() - t0
             done_flops += prefill_flops(lens[s:s + 1], counts[s:s + 1], sp.Hq, sp.D)
             nseq += 1

@@ -482,6 +482,24 @@ kv_status kv_paged_attention_prefill(float* out, const void* q, const void* k_po
                                      const int32_t* work_items, int32_t n_items,
                                      hipStream_t stream);
 
+/* kv_paged_attention_prefill over fp8 (KV_FP8_E4M3) pools with per-pool
+ * scales, the cache holding value(code) * k_scale / v_scale: each code is
+ * widened exactly to the query's type (`dtype`, f16 or bf16) as it is staged
+ * in LDS, k_scale is folded into the score scale and v_scale into the
+ * output. Write the chunk first with kv_reshape_and_cache_fp8. Arguments,
+ * checks and launches otherwise as for kv_paged_attention_prefill; scales
+ * must be finite and > 0 (else KV_ERR_INVALID). */
+kv_status kv_paged_attention_prefill_fp8(float* out, const void* q, const void* k_pool,
+                                         const void* v_pool, const int32_t* block_tables,
+                                         int32_t max_blocks, const int32_t* context_lens,
+                                         const int32_t* query_start, int32_t S, int32_t total_q,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                         float scale, kv_dtype dtype, float k_scale,
+                                         float v_scale, int32_t max_query_len,
+                                         const int32_t* work_items, int32_t n_items,
+                                         hipStream_t stream);
+
 /* Message describing the calling thread's last error ("" if none). */
 const char* kv_last_error(void);
 

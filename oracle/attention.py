@@ -315,7 +315,8 @@ def swap_in_blocks(k_pools: List[np.ndarray], v_pools: List[np.ndarray],
 
 def prefill_attention(q, q_start, k_pool, v_pool, block_tables, context_lens, scale: float,
                       dtype: str, block_size: int = 16,
-                      rows: Optional[Iterable[int]] = None) -> np.ndarray:
+                      rows: Optional[Iterable[int]] = None, kv_dtype: Optional[str] = None,
+                      k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Attention of a chunk of new query tokens per sequence over the paged
     cache, causal within the chunk. Chunked prefill processes a prompt in
     pieces of a fixed token count ([2] "The Successors - SGLang's
@@ -328,7 +329,8 @@ def prefill_attention(q, q_start, k_pool, v_pool, block_tables, context_lens, sc
     Query row i of the chunk sits at position p = L_s - C_s + i and attends to
     positions 0..p: out = sum_j w_j V[j] / sum_j w_j, w_j = exp(z_j - max z),
     z_j = scale * <q, K[j]>. Returns float64 [T, Hq, D]; with `rows`, only
-    those query rows are computed and the rest stay NaN.
+    those query rows are computed and the rest stay NaN. `kv_dtype` and the
+    scales describe an fp8 cache as in decode_attention.
     """
     q = widen(q, dtype)
     T, Hq, D = q.shape
@@ -345,8 +347,12 @@ def prefill_attention(q, q_start, k_pool, v_pool, block_tables, context_lens, sc
         C = r1 - r0
         if C > L:
             raise ValueError(f"sequence {s}: chunk of {C} tokens longer than its context {L}")
-        Kc = widen(gather_sequence(k_pool, block_tables[s], L, block_size), dtype)
-        Vc = widen(gather_sequence(v_pool, block_tables[s], L, block_size), dtype)
+        kd = kv_dtype or dtype
+        Kc = widen(gather_sequence(k_pool, block_tables[s], L, block_size), kd)
+        Vc = widen(gather_sequence(v_pool, block_tables[s], L, block_size), kd)
+        if kv_dtype is not None:
+            Kc = Kc * float(np.float32(k_scale))
+            Vc = Vc * float(np.float32(v_scale))
         for i in range(C):
             r = r0 + i
             if want is not None and r not in want:

@@ -102,6 +102,9 @@ _SIGS = {
     "kv_paged_attention_prefill_plan": (C.c_int, [P_i32, P_i32, i32, i32, i32, P_i32, i32, P_i32]),
     "kv_paged_attention_prefill": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32,
                                              i32, i32, i32, f32, C.c_int, i32, vp, i32, vp]),
+    "kv_paged_attention_prefill_fp8": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
+                                                 i32, i32, i32, i32, f32, C.c_int, f32, f32, i32,
+                                                 vp, i32, vp]),
     "kv_last_error": (C.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -569,3 +572,24 @@ def kv_paged_attention_prefill(out, q, k_pool, v_pool, block_tables, context_len
         None if work_items is None else _dev(work_items, "work_items", torch.int32),
         0 if work_items is None else work_items.shape[0], _stream(stream)),
         "kv_paged_attention_prefill")
+
+
+def kv_paged_attention_prefill_fp8(out, q, k_pool, v_pool, block_tables, context_lens,
+                                   query_start, scale: float, k_scale: float, v_scale: float,
+                                   max_query_len: int, work_items=None, stream=None) -> None:
+    """kv_paged_attention_prefill over uint8 E4M3 pools with per-pool scales; q f16/bf16."""
+    torch = _torch()
+    T, Hq, D = q.shape
+    NB, Hkv, B, D2 = _fp8_pools("kv_paged_attention_prefill_fp8", k_pool, v_pool)
+    S = context_lens.numel()
+    if D2 != D or tuple(out.shape) != (T, Hq, D) or block_tables.shape[0] != S \
+            or query_start.numel() != S + 1:
+        raise KVError(KV_ERR_INVALID, "kv_paged_attention_prefill_fp8", "shape mismatch")
+    _check(lib.kv_paged_attention_prefill_fp8(
+        _dev(out, "out", torch.float32), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), _dev(query_start, "query_start", torch.int32),
+        S, T, Hq, Hkv, D, B, NB, float(scale), dtype_code(q), float(k_scale), float(v_scale),
+        max_query_len, None if work_items is None else _dev(work_items, "work_items", torch.int32),
+        0 if work_items is None else work_items.shape[0], _stream(stream)),
+        "kv_paged_attention_prefill_fp8")

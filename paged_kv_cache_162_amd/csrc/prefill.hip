@@ -53,7 +53,8 @@ struct PrefillParams {
   const int32_t* q_start;  // [S + 1] first query row of each sequence
   const int32_t* items;    // optional [n_items][2] = (sequence, query block)
   int32_t T, S, Hq, Hkv, G, tpc, rows_per_block, max_blocks, num_blocks, n_units;
-  float scale_log2;
+  float scale_log2;  // scale * log2(e), times the K scale for an fp8 cache
+  float v_scale;     // fp8 cache: the V scale, applied to the output
 };
 
 // Column tile of MFMA columns: query row of column c and whether it is live.
@@ -63,11 +64,11 @@ struct ColTile {
   bool live;
 };
 
-template <int DT, int BS>
+template <int DT, int BS, bool KV8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_mfma_kernel(PrefillParams p) {
   constexpr int D = kPfHeadDim;
-  constexpr int kRowU4 = D / 8;  // uint4 per 16-bit key row
+  constexpr int kRowU4 = KV8 ? D / 16 : D / 8;  // uint4 per key row of the pools
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
@@ -143,8 +144,9 @@ void prefill_mfma_kernel(PrefillParams p) {
     seg = sg;
   };
   // uint4 index of key row r (0..31) of 32-key tile j. The block index is
-  // wave-uniform: a wave loads rows 4w..4w+3 and 16+4w..16+4w+3, and no
-  // group of four straddles two 8-token blocks
+  // wave-uniform: a wave loads rows 4w..4w+3 and 16+4w..16+4w+3 (16-bit
+  // pools) or 8w..8w+7 (fp8 pools), and no such group straddles two 8-token
+  // blocks
   auto key_row = [&](int j, int r) -> size_t {
     const int key = kPfKeys * j + r;
     const int bi = key / BS, rb = key % BS;
@@ -156,27 +158,46 @@ void prefill_mfma_kernel(PrefillParams p) {
 
   // ---- LDS tiles of 32 keys: [buffer][K, V][row] -----------------------------
   __shared__ __align__(16) unsigned char lds[2][2][kPfKeys * kPfRowBytes];
-  const int lr = tid >> 4, lc = tid & 15;  // rows lr and lr + 16, 16-byte chunk lc
+  // 16-bit pools: this thread moves rows lr and lr + 16, 16-byte chunk lc.
+  // fp8 pools: row r8, 16 codes from chunk c8, widened to two 16-bit chunks.
+  const int lr = tid >> 4, lc = tid & 15;
+  const int r8 = tid >> 3, c8 = tid & 7;
   const uint4* kpool = static_cast<const uint4*>(p.k_pool);
   const uint4* vpool = static_cast<const uint4*>(p.v_pool);
   auto load = [&](int j, uint4* g) {
-    const size_t r0 = key_row(j, lr), r1 = key_row(j, lr + 16);
-    g[0] = kpool[r0 + lc];
-    g[1] = vpool[r0 + lc];
-    g[2] = kpool[r1 + lc];
-    g[3] = vpool[r1 + lc];
+    if constexpr (KV8) {
+      const size_t r = key_row(j, r8);
+      g[0] = kpool[r + c8];
+      g[1] = vpool[r + c8];
+    } else {
+      const size_t r0 = key_row(j, lr), r1 = key_row(j, lr + 16);
+      g[0] = kpool[r0 + lc];
+      g[1] = vpool[r0 + lc];
+      g[2] = kpool[r1 + lc];
+      g[3] = vpool[r1 + lc];
+    }
+  };
+  auto put = [&](int buf, int kv, int row, int chunk, const uint4& u, uint32_t mk) {
+    *reinterpret_cast<uint4*>(&lds[buf][kv][row * kPfRowBytes + chunk * 16]) =
+        make_uint4(u.x & mk, u.y & mk, u.z & mk, u.w & mk);
   };
   auto store = [&](int j, const uint4* g, int buf) {
     // rows past the visible keys may hold anything: they are stored as zeros
+    if constexpr (KV8) {
+      const uint32_t mk = kPfKeys * j + r8 >= nkeys ? 0u : ~0u;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int row = lr + 16 * half;
-      const uint32_t mk = kPfKeys * j + row >= nkeys ? 0u : ~0u;
-      const uint4 kk = g[2 * half], vv = g[2 * half + 1];
-      *reinterpret_cast<uint4*>(&lds[buf][0][row * kPfRowBytes + lc * 16]) =
-          make_uint4(kk.x & mk, kk.y & mk, kk.z & mk, kk.w & mk);
-      *reinterpret_cast<uint4*>(&lds[buf][1][row * kPfRowBytes + lc * 16]) =
-          make_uint4(vv.x & mk, vv.y & mk, vv.z & mk, vv.w & mk);
+      for (int kv = 0; kv < 2; ++kv) {
+        put(buf, kv, r8, 2 * c8, e4m3x8_widen<DT>(g[kv].x, g[kv].y), mk);
+        put(buf, kv, r8, 2 * c8 + 1, e4m3x8_widen<DT>(g[kv].z, g[kv].w), mk);
+      }
+    } else {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int row = lr + 16 * half;
+        const uint32_t mk = kPfKeys * j + row >= nkeys ? 0u : ~0u;
+        put(buf, 0, row, lc, g[2 * half], mk);
+        put(buf, 1, row, lc, g[2 * half + 1], mk);
+      }
     }
   };
 
@@ -307,7 +328,7 @@ void prefill_mfma_kernel(PrefillParams p) {
   for (int t = 0; t < kPfColTiles; ++t) {
     const float lt = column_sum(l[t]);
     if (!ct[t].live) continue;
-    const float inv = 1.0f / lt;
+    const float inv = (KV8 ? p.v_scale : 1.0f) / lt;
     float* dst = p.out + (((size_t)r_begin + ct[t].qrow) * p.Hq + (size_t)h * p.G + hd) * D +
                  32 * grp;
 #pragma unroll
@@ -323,27 +344,25 @@ void prefill_mfma_kernel(PrefillParams p) {
 
 int32_t rows_per_block(int32_t G) { return kPfWaves * kPfColTiles * (16 / G); }
 
-}  // namespace
-
-extern "C" {
-
-int32_t kv_paged_attention_prefill_rows_per_item(int32_t num_q_heads, int32_t num_kv_heads) {
-  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
-  const int32_t G = num_q_heads / num_kv_heads;
-  return G > 16 ? 0 : rows_per_block(G);
+template <bool KV8>
+auto pick_kernel(kv_dtype dtype, int32_t block_size) -> decltype(&prefill_mfma_kernel<KV_BF16, 16, KV8>) {
+  if (dtype == KV_BF16)
+    return block_size == 8    ? prefill_mfma_kernel<KV_BF16, 8, KV8>
+           : block_size == 16 ? prefill_mfma_kernel<KV_BF16, 16, KV8>
+                              : prefill_mfma_kernel<KV_BF16, 32, KV8>;
+  return block_size == 8    ? prefill_mfma_kernel<KV_F16, 8, KV8>
+         : block_size == 16 ? prefill_mfma_kernel<KV_F16, 16, KV8>
+                            : prefill_mfma_kernel<KV_F16, 32, KV8>;
 }
 
-kv_status kv_paged_attention_prefill(float* out, const void* q, const void* k_pool,
-                                     const void* v_pool, const int32_t* block_tables,
-                                     int32_t max_blocks, const int32_t* context_lens,
-                                     const int32_t* query_start, int32_t S, int32_t total_q,
-                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                     int32_t block_size, int32_t num_blocks, float scale,
-                                     kv_dtype dtype, int32_t max_query_len,
-                                     const int32_t* work_items, int32_t n_items,
-                                     hipStream_t stream) {
-  pagedkv::clear_error();
-  const char* who = "kv_paged_attention_prefill";
+kv_status prefill_impl(const char* who, float* out, const void* q, const void* k_pool,
+                       const void* v_pool, const int32_t* block_tables, int32_t max_blocks,
+                       const int32_t* context_lens, const int32_t* query_start, int32_t S,
+                       int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                       kv_dtype dtype, int32_t max_query_len, const int32_t* work_items,
+                       int32_t n_items, hipStream_t stream, bool kv8, float k_scale,
+                       float v_scale) {
   if (dtype != KV_F16 && dtype != KV_BF16)
     return fail(KV_ERR_UNSUPPORTED, "%s: dtype must be f16 or bf16", who);
   if (S < 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks < 0 ||
@@ -358,6 +377,9 @@ kv_status kv_paged_attention_prefill(float* out, const void* q, const void* k_po
     return fail(KV_ERR_UNSUPPORTED, "%s: head_dim %d (128)", who, head_dim);
   if (block_size != 8 && block_size != 16 && block_size != 32)
     return fail(KV_ERR_UNSUPPORTED, "%s: block_size %d (8, 16 or 32)", who, block_size);
+  if (kv8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !std::isfinite(k_scale) ||
+              !std::isfinite(v_scale)))
+    return fail(KV_ERR_INVALID, "%s: scales must be finite and > 0", who);
   if (S == 0 || total_q == 0) return KV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
     return fail(KV_ERR_INVALID, "%s: null pointer", who);
@@ -390,17 +412,55 @@ kv_status kv_paged_attention_prefill(float* out, const void* q, const void* k_po
   prm.max_blocks = max_blocks;
   prm.num_blocks = num_blocks;
   prm.n_units = (int32_t)n_units;
-  prm.scale_log2 = scale * 1.4426950408889634f;
+  prm.scale_log2 = scale * 1.4426950408889634f * (kv8 ? k_scale : 1.0f);
+  prm.v_scale = v_scale;
 
-  auto kern = dtype == KV_BF16
-                  ? (block_size == 8    ? prefill_mfma_kernel<KV_BF16, 8>
-                     : block_size == 16 ? prefill_mfma_kernel<KV_BF16, 16>
-                                        : prefill_mfma_kernel<KV_BF16, 32>)
-                  : (block_size == 8    ? prefill_mfma_kernel<KV_F16, 8>
-                     : block_size == 16 ? prefill_mfma_kernel<KV_F16, 16>
-                                        : prefill_mfma_kernel<KV_F16, 32>);
+  auto kern = kv8 ? pick_kernel<true>(dtype, block_size) : pick_kernel<false>(dtype, block_size);
   hipLaunchKernelGGL(kern, dim3((unsigned)n_units), dim3(kPfWaves * 64), 0, stream, prm);
   return launch_status(who);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kv_paged_attention_prefill_rows_per_item(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
+  const int32_t G = num_q_heads / num_kv_heads;
+  return G > 16 ? 0 : rows_per_block(G);
+}
+
+kv_status kv_paged_attention_prefill(float* out, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_tables,
+                                     int32_t max_blocks, const int32_t* context_lens,
+                                     const int32_t* query_start, int32_t S, int32_t total_q,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t num_blocks, float scale,
+                                     kv_dtype dtype, int32_t max_query_len,
+                                     const int32_t* work_items, int32_t n_items,
+                                     hipStream_t stream) {
+  pagedkv::clear_error();
+  return prefill_impl("kv_paged_attention_prefill", out, q, k_pool, v_pool, block_tables,
+                      max_blocks, context_lens, query_start, S, total_q, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                      max_query_len, work_items, n_items, stream, false, 1.0f, 1.0f);
+}
+
+kv_status kv_paged_attention_prefill_fp8(float* out, const void* q, const void* k_pool,
+                                         const void* v_pool, const int32_t* block_tables,
+                                         int32_t max_blocks, const int32_t* context_lens,
+                                         const int32_t* query_start, int32_t S, int32_t total_q,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                         float scale, kv_dtype dtype, float k_scale,
+                                         float v_scale, int32_t max_query_len,
+                                         const int32_t* work_items, int32_t n_items,
+                                         hipStream_t stream) {
+  pagedkv::clear_error();
+  return prefill_impl("kv_paged_attention_prefill_fp8", out, q, k_pool, v_pool, block_tables,
+                      max_blocks, context_lens, query_start, S, total_q, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                      max_query_len, work_items, n_items, stream, true, k_scale, v_scale);
 }
 
 }  // extern "C"

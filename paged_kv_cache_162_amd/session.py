@@ -143,8 +143,6 @@ class DecodeSession:
         for sequence seqs[i] and upload the slots, tables, lengths, query row
         ranges and the work plan. Returns the host-side slots and any
         copy-on-write pairs."""
-        if self.fp8:
-            raise kv.KVError(kv.KV_ERR_UNSUPPORTED, "prepare_prefill", "fp8 pools")
         torch = self.torch
         dev = self.device
         slots, pairs = [], []
@@ -180,11 +178,16 @@ class DecodeSession:
         vp_ = self.v_pool if v_pool is None else v_pool
         if self.d_pairs.shape[0]:
             kv.kv_copy_blocks([kp], [vp_], self.d_pairs, self.NB, self.block_bytes)
-        kv.kv_reshape_and_cache(k_new, v_new, kp, vp_, self.d_slots)
+        self._write(k_new, v_new, kp, vp_, self.d_slots)
         if events is not None:
             events[0].record()
-        kv.kv_paged_attention_prefill(out, q, kp, vp_, self.d_tables, self.d_lens, self.d_qstart,
-                                      scale, self.max_query_len, self.d_items)
+        if self.fp8:
+            kv.kv_paged_attention_prefill_fp8(out, q, kp, vp_, self.d_tables, self.d_lens,
+                                              self.d_qstart, scale, self.k_scale, self.v_scale,
+                                              self.max_query_len, self.d_items)
+        else:
+            kv.kv_paged_attention_prefill(out, q, kp, vp_, self.d_tables, self.d_lens,
+                                          self.d_qstart, scale, self.max_query_len, self.d_items)
         if events is not None:
             events[1].record()
 

@@ -349,3 +349,19 @@ def test_prefill_plan_orders_blocks_by_keys(kv):
     assert len(kv.kv_paged_attention_prefill_plan([0, 0], [7], 64, 8)) == 0
     with pytest.raises(kv.KVError):
         kv.kv_paged_attention_prefill_plan([0, 3], [10], 64, 2)
+
+
+def test_prefill_fp8_entry_point_validates_on_the_host(kv):
+    lib = kv.lib
+
+    def call(**k):
+        return lib.kv_paged_attention_prefill_fp8(
+            None, None, None, None, None, 4, None, None, k.get("S", 1), 4, 8, 2, k.get("D", 128),
+            16, 8, 1.0, k.get("dt", kv.KV_BF16), k.get("ks", 1.0), k.get("vs", 1.0), 4, None, 0,
+            None)
+    assert call(ks=0.0) == kv.KV_ERR_INVALID
+    assert call(vs=float("inf")) == kv.KV_ERR_INVALID
+    assert call(D=64) == kv.KV_ERR_UNSUPPORTED
+    assert call(dt=kv.KV_F32) == kv.KV_ERR_UNSUPPORTED
+    assert call() == kv.KV_ERR_INVALID
+    assert call(S=0) == kv.KV_OK

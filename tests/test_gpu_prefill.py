@@ -199,3 +199,79 @@ def test_prefill_graph_replay_matches_eager():
         assert np.array_equal(bits(to_host(kd, dt)), bits(eager[1]))
         assert np.array_equal(bits(to_host(vd, dt)), bits(eager[2]))
     sess.close()
+
+
+FP8_SHAPES = [(dt, G, B) for dt in ("bf16", "f16") for G in (1, 8) for B in (8, 16, 32)]
+
+
+@pytest.mark.parametrize("dt,G,B", FP8_SHAPES)
+def test_prefill_fp8_cache_against_oracle(dt, G, B):
+    """The prefill kernel over an E4M3 cache: codes widened in LDS, K scale in
+    the scores, V scale on the output."""
+    kv = kvlib()
+    rng = np.random.default_rng(900 + FP8_SHAPES.index((dt, G, B)))
+    prev, chunk = [0, 5, 16, 100, 700, 33], [1, 16, 17, 40, 100, 0]
+    Hkv, D = 2, 128
+    q, qs, _, _, tab, lens = prefill_case(rng, prev, chunk, G * Hkv, Hkv, D, dt, B=B, poison=False)
+    NB = int(tab.max()) + 6
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    kp = rng.choice(finite, (NB, Hkv, B, D))
+    vp = rng.choice(finite, (NB, Hkv, B, D))
+    live = np.zeros((NB, B), bool)
+    for s, t in enumerate(lens):
+        for p in range(t):
+            live[tab[s, p // B], p % B] = True
+    dead = np.argwhere(~live)
+    for pool in (kp, vp):
+        pool[dead[:, 0], :, dead[:, 1], :] = POISON["e4m3"]
+    scale, ks, vs = float(np.float32(1 / np.sqrt(D))), 0.06, 0.02
+    ref = oracle.prefill_attention(q, qs, kp, vp, tab, lens, scale, dt, block_size=B,
+                                   kv_dtype="e4m3", k_scale=ks, v_scale=vs)
+    T, Hq = q.shape[0], q.shape[1]
+    for plan in (True, False):
+        out = torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+        items = None
+        if plan:
+            items = torch.from_numpy(kv.kv_paged_attention_prefill_plan(qs, lens, Hq, Hkv)).cuda()
+        log(f"[gpu] prefill fp8 {dt} G={G} B={B} plan={plan}")
+        kv.kv_paged_attention_prefill_fp8(out, to_dev(q, dt), to_dev(kp, "e4m3"), to_dev(vp, "e4m3"),
+                                          torch.from_numpy(tab).cuda(), torch.from_numpy(lens).cuda(),
+                                          torch.from_numpy(qs).cuda(), scale, ks, vs,
+                                          int(np.diff(qs).max()), items)
+        torch.cuda.synchronize()
+        check_attention(out.cpu().numpy().reshape(-1, D), ref.reshape(-1, D), dt,
+                        f"prefill fp8 {dt} G={G} B={B}")
+
+
+def test_prefill_fp8_session_step():
+    """A chunked-prefill step over an fp8 cache through the session: the
+    chunk is quantised into the pools (bit exact against the oracle's write)
+    and attended causally."""
+    from oracle import fp8 as ofp8
+    from paged_kv_cache_162_amd.session import DecodeSession
+    rng = np.random.default_rng(883)
+    dt, Hq, Hkv, D, NB = "bf16", 64, 8, 128, 96
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    kp = rng.choice(finite, (NB, Hkv, 16, D))
+    vp = rng.choice(finite, (NB, Hkv, 16, D))
+    kd, vd = to_dev(kp, "e4m3"), to_dev(vp, "e4m3")
+    sess = DecodeSession(k_pool=kd, v_pool=vd, num_q_heads=Hq, k_scale=0.25, v_scale=0.25)
+    ops = [("create", 0), ("append", 0, 300), ("create", 1), ("append", 1, 17), ("create", 2)]
+    sess.run_ops(ops)
+    counts = [64, 40, 33]
+    host_slots, _ = sess.prepare_prefill([0, 1, 2], counts)
+    T = sum(counts)
+    q = round_to_dtype(rng.standard_normal((T, Hq, D)).astype(np.float32), dt)
+    kn = round_to_dtype(rng.standard_normal((T, Hkv, D)).astype(np.float32), dt)
+    vn = round_to_dtype(rng.standard_normal((T, Hkv, D)).astype(np.float32), dt)
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    sess.prefill_step(to_dev(q, dt), to_dev(kn, dt), to_dev(vn, dt), out, 0.088)
+    torch.cuda.synchronize()
+    rk, rv = kp.copy(), vp.copy()
+    ofp8.reshape_and_cache_fp8(kn, vn, rk, rv, host_slots, dt, 0.25, 0.25)
+    assert np.array_equal(to_host(kd, "e4m3"), rk) and np.array_equal(to_host(vd, "e4m3"), rv)
+    qs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    ref = oracle.prefill_attention(q, qs, rk, rv, sess.host_tables, sess.host_lens, 0.088, dt,
+                                   kv_dtype="e4m3", k_scale=0.25, v_scale=0.25)
+    check_attention(out.cpu().numpy().reshape(-1, D), ref.reshape(-1, D), dt, "fp8 prefill step")
+    sess.close()

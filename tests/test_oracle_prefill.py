@@ -129,3 +129,30 @@ def test_rows_subset_and_empty_chunks():
     assert np.isnan(part[[0, 2, 3, 4]]).all()
     with pytest.raises(ValueError):
         oracle.prefill_attention(q, qs, kp, vp, tab, np.array([3, 9, 1], np.int32), 0.5, "f32")
+
+
+def test_fp8_cache_is_the_16bit_oracle_on_dequantised_values():
+    from oracle import fp8
+    from oracle import attention as oa
+    rng = np.random.default_rng(65)
+    prev, chunk = [9, 0, 30], [5, 12, 3]
+    Hq, Hkv, D = 4, 2, 8
+    _, qs, kp, vp, tab, lens, _, _ = paged_prefill_case(rng, prev, chunk, Hq, Hkv, D)
+    codes_k = rng.integers(0, 256, kp.shape).astype(np.uint8)
+    codes_v = rng.integers(0, 256, vp.shape).astype(np.uint8)
+    for c in (codes_k, codes_v):
+        c[(c & 0x7F) == 0x7F] = 0x30            # no NaN codes
+    q = rng.standard_normal((int(qs[-1]), Hq, D)).astype(np.float32)
+    got = oracle.prefill_attention(q, qs, codes_k, codes_v, tab, lens, 0.4, "f32",
+                                   kv_dtype="e4m3", k_scale=0.125, v_scale=3.0)
+    ref = oracle.prefill_attention(q, qs, fp8.dequantize(codes_k, 0.125),
+                                   fp8.dequantize(codes_v, 3.0), tab, lens, 0.4, "f32")
+    np.testing.assert_allclose(got, ref, rtol=0, atol=0)
+    # the decode oracle agrees on one-row chunks of the same cache
+    ones = np.arange(4, dtype=np.int32)
+    d = oracle.decode_attention(q[:3], codes_k, codes_v, tab, lens, 0.4, "f32",
+                                kv_dtype="e4m3", k_scale=0.125, v_scale=3.0)
+    p1 = oracle.prefill_attention(q[:3], ones, codes_k, codes_v, tab, lens, 0.4, "f32",
+                                  kv_dtype="e4m3", k_scale=0.125, v_scale=3.0)
+    assert np.array_equal(d, p1)
+    assert oa.widen(codes_k[0, 0, 0, :2], "e4m3").shape == (2,)

@@ -161,6 +161,12 @@ SPECS = {
                                 "lognormal length (median 512, sigma 0.86) and "
                                 "a 256-token chunk attended causally; 64 query / "
                                 "8 KV heads, head_dim 128, bf16"),
+    9: WorkloadSpec(9, "llama70b-gqa-chunked-prefill-fp8", S=16, Hq=64, Hkv=8, D=128,
+                    dtype="bf16", chunk=256, kv_dtype="e4m3", k_scale=0.25, v_scale=0.25,
+                    seed_cfg=8,
+                    description="the chunked-prefill workload (same prefixes, chunks "
+                                "and queries) over an fp8 E4M3 cache with per-pool "
+                                "scales"),
     7: WorkloadSpec(7, "llama70b-gqa-fp8", S=128, Hq=64, Hkv=8, D=128, dtype="bf16",
                     kv_dtype="e4m3", k_scale=0.25, v_scale=0.25, seed_cfg=3,
                     description="the llama70b-gqa-bf16 workload (same lengths, "
@@ -235,7 +241,7 @@ def _context_lengths(sp: WorkloadSpec, rng: np.random.Generator) -> np.ndarray:
     if sp.cfg in (3, 7):
         x = np.exp(rng.normal(math.log(512.0), 0.86, size=sp.S))
         return np.clip(np.rint(x), 16, 8192).astype(np.int32)
-    if sp.cfg == 8:
+    if sp.cfg in (8, 9):
         x = np.exp(rng.normal(math.log(512.0), 0.86, size=sp.S))
         return (np.clip(np.rint(x), 0, 8192 - sp.chunk) + sp.chunk).astype(np.int32)
     if sp.cfg == 4:
@@ -252,7 +258,7 @@ def _pool_blocks(sp: WorkloadSpec, lens: np.ndarray) -> int:
         return 32
     if sp.cfg == 2:
         return 8192 * 16 // B  # the worst case, 64 sequences of 2048 tokens
-    if sp.cfg in (3, 7, 8):
+    if sp.cfg in (3, 7, 8, 9):
         need = int(sum(-(-int(t) // B) for t in lens))
         return int(math.ceil(1.1 * need))
     if sp.cfg == 4:
