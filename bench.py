@@ -211,6 +211,25 @@ def cpu_baseline(w, seconds):
                       f"pass(es), BLAS limited to 1 thread"}
 
 
+MAX_CONTEXT = 8192  # longest context the workloads allow: a contiguous allocator reserves it
+
+
+def kv_memory(kv, sess, sp, w):
+    """Cache memory the host manager holds for the step's sequences: slots in
+    held blocks against the tokens they store (paged), and against a
+    contiguous reservation of MAX_CONTEXT tokens per sequence. Shared blocks
+    count once, so a shared prefix stores more logical tokens than it holds."""
+    held_blocks = w.num_blocks - kv.kv_num_free_blocks(sess.pool)
+    slots = held_blocks * sp.block_size
+    tokens = int(sess.host_lens.astype(np.int64).sum())
+    return {"blocks_held": int(held_blocks), "slots_held": int(slots), "tokens": tokens,
+            "paged_waste_pct": round(100.0 * (1 - min(tokens, slots) / slots), 2),
+            "contiguous_waste_pct": round(100.0 * (1 - tokens / (sp.S * MAX_CONTEXT)), 2),
+            "contiguous_reservation_tokens": MAX_CONTEXT,
+            "pages_context": "the pages report 60-80% of KV memory wasted by contiguous "
+                             "max-length reservation and under 4% with 16-token paging"}
+
+
 def prefill_flops(lens, counts, Hq, D):
     """Algorithmic flops of the chunked-prefill attention: every chunk row at
     position p takes 2*D multiply-adds for each of its p+1 scores and as many
@@ -442,6 +461,7 @@ def main():
         values = {s: (to_dev(w.tail_k[s], dt), to_dev(w.tail_v[s], dt)) for s in range(sp.S)}
     sess.run_ops(w.setup_ops, values)
     sess.prepare_step(list(range(sp.S)))
+    memory = kv_memory(kv, sess, sp, w)
     lens = sess.host_lens
     q, kn, vn = to_dev(w.q, dt), to_dev(w.k_new, dt), to_dev(w.v_new, dt)
     out = torch.empty((sp.S, sp.Hq, sp.D), dtype=torch.float32, device="cuda")
@@ -556,6 +576,7 @@ def main():
         "decode_kv_gbs": round(kvb / (dec_avg * 1e-3) / 1e9, 2),
         "warm_ms_per_step": round(warm_ms, 5),
         "warm_kv_gbs": round(kvb / (warm_ms * 1e-3) / 1e9, 2),
+        "kv_memory": memory,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
