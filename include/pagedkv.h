@@ -178,6 +178,9 @@ kv_status kv_seq_swap_out(kv_pool_t* pool, int64_t seq, int32_t cap, int32_t* id
 kv_status kv_seq_swap_in(kv_pool_t* pool, int64_t seq, int32_t cap, int32_t* ids, int32_t* n);
 /* 1 if the sequence is swapped out, 0 if resident, -1 if unknown. */
 int32_t kv_seq_is_swapped(const kv_pool_t* pool, int64_t seq);
+/* Number of blocks currently held by more than one reference (shared by
+ * forks or prefixes, [1] "Memory sharing"); -1 for a null pool. */
+int32_t kv_pool_shared_blocks(const kv_pool_t* pool);
 
 /* ---------------------------------------------------------------------------
  * Device: slot mapping and cache writes.
@@ -335,6 +338,21 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
                                     int32_t max_context_len, const int32_t* work_items,
                                     int32_t n_items, void* workspace, size_t ws_bytes,
                                     hipStream_t stream);
+
+/* How the decode kernels load K and V (all four decode entry points, for
+ * the calling host thread; default KV_LOADS_STREAM):
+ *   KV_LOADS_STREAM  loads carry the non-temporal hint: every block is read
+ *                    once per step, so nothing is kept in the caches for it.
+ *                    Fastest when no block is shared between the step's
+ *                    sequences (measured 10-15% over plain loads).
+ *   KV_LOADS_CACHED  plain loads: blocks shared by several sequences (a
+ *                    common prefix, [1] "Memory sharing") stay in the caches
+ *                    for their next reader.
+ * Results are identical under both. kv_pool_shared_blocks tells whether a
+ * pool currently holds shared blocks. */
+typedef enum { KV_LOADS_STREAM = 0, KV_LOADS_CACHED = 1 } kv_load_policy;
+kv_status kv_paged_attention_set_load_policy(kv_load_policy policy);
+kv_load_policy kv_paged_attention_load_policy(void);
 
 /* One decode step with the cache write fused into the decode launch: for
  * each sequence s with t = context_lens[s] >= 1, position t-1 holds the

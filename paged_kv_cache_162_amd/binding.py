@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 KV_OK, KV_ERR_INVALID, KV_ERR_OOM, KV_ERR_UNSUPPORTED, KV_ERR_HIP, KV_ERR_STATE = 0, -1, -2, -3, -4, -5
 STATUS_NAMES = {0: "OK", -1: "INVALID", -2: "OOM", -3: "UNSUPPORTED", -4: "HIP", -5: "STATE"}
 KV_F32, KV_F16, KV_BF16, KV_FP8_E4M3 = 0, 1, 2, 3
+KV_LOADS_STREAM, KV_LOADS_CACHED = 0, 1
 DTYPE_CODES = {"f32": KV_F32, "f16": KV_F16, "bf16": KV_BF16, "e4m3": KV_FP8_E4M3}
 ELEM_BYTES = {KV_F32: 4, KV_F16: 2, KV_BF16: 2, KV_FP8_E4M3: 1}
 
@@ -71,6 +72,7 @@ _SIGS = {
     "kv_seq_swap_out": (C.c_int, [vp, i64, i32, P_i32, P_i32]),
     "kv_seq_swap_in": (C.c_int, [vp, i64, i32, P_i32, P_i32]),
     "kv_seq_is_swapped": (i32, [vp, i64]),
+    "kv_pool_shared_blocks": (i32, [vp]),
     "kv_slot_mapping": (C.c_int, [vp, i32, i32, vp, vp, i32, i32, vp, vp]),
     "kv_reshape_and_cache": (C.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, C.c_int, vp]),
     "kv_append_tokens": (C.c_int, [vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32,
@@ -105,6 +107,8 @@ _SIGS = {
     "kv_paged_attention_prefill_fp8": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
                                                  i32, i32, i32, i32, f32, C.c_int, f32, f32, i32,
                                                  vp, i32, vp]),
+    "kv_paged_attention_set_load_policy": (C.c_int, [C.c_int]),
+    "kv_paged_attention_load_policy": (C.c_int, []),
     "kv_last_error": (C.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -252,6 +256,18 @@ def kv_seq_swap_in(pool: int, seq: int) -> np.ndarray:
 
 def kv_seq_is_swapped(pool: int, seq: int) -> int:
     return int(lib.kv_seq_is_swapped(pool, seq))
+
+
+def kv_pool_shared_blocks(pool: int) -> int:
+    return int(lib.kv_pool_shared_blocks(pool))
+
+
+def kv_paged_attention_set_load_policy(policy: int) -> None:
+    _check(lib.kv_paged_attention_set_load_policy(policy), "kv_paged_attention_set_load_policy")
+
+
+def kv_paged_attention_load_policy() -> int:
+    return int(lib.kv_paged_attention_load_policy())
 
 
 # ---------------------------------------------------------------------------

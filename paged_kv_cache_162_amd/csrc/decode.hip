@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kMergeThreads) void splitk_merge_kernel(DecodeParam
 // reductions. Each group of LPR lanes keeps its own online softmax over the
 // tokens it reads; the groups are merged with cross-lane shuffles at the end.
 // ============================================================================
-template <int DT, int D, int GMAX, int BS>
+template <int DT, int D, int GMAX, int BS, bool NT>
 __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   constexpr int EB = DT == KV_F32 ? 4 : 2;
   constexpr int EPL = 16 / EB;           // elements per lane chunk
@@ -363,8 +363,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
       const size_t at = tile_row<BS>(p, w.h, staged, j, r + TPI * i, LPR) + c;
-      ku[i] = kbase[at];
-      vu[i] = vbase[at];
+      ku[i] = load_kv<NT>(kbase + at);
+      vu[i] = load_kv<NT>(vbase + at);
     }
   };
 
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
 // (base-2 units), so most blocks skip the cross-lane max and the rescale of
 // the accumulators; weights stay below 2^kRescaleSlack, far from overflow.
 // ============================================================================
-template <int DT, bool SPLITCOL, int RING, int BS, bool KV8>
+template <int DT, bool SPLITCOL, int RING, int BS, bool KV8, bool NT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_mfma_kernel(DecodeParams p) {
   constexpr int D = 128;
@@ -613,17 +613,17 @@ void decode_mfma_kernel(DecodeParams p) {
     if constexpr (KV8) {
       const uint2* vt = reinterpret_cast<const uint2*>(vbase) +
                         tile_row<BS>(p, w.h, staged, j, 4 * grp, 2 * kRowU4);
-      ku[0] = kt[grp];
-      ku[1] = kt[4 + grp];
+      ku[0] = load_kv<NT>(kt + grp);
+      ku[1] = load_kv<NT>(kt + 4 + grp);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) vu[jj] = vt[jj * 2 * kRowU4 + col];
+      for (int jj = 0; jj < 4; ++jj) vu[jj] = load_kv<NT>(vt + jj * 2 * kRowU4 + col);
     } else {
       const uint4* vt = reinterpret_cast<const uint4*>(vbase) +
                         tile_row<BS>(p, w.h, staged, j, 4 * grp, kRowU4);
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) ku[kc] = kt[kc * 4 + grp];
+      for (int kc = 0; kc < 4; ++kc) ku[kc] = load_kv<NT>(kt + kc * 4 + grp);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) vu[jj] = vt[jj * kRowU4 + col];
+      for (int jj = 0; jj < 4; ++jj) vu[jj] = load_kv<NT>(vt + jj * kRowU4 + col);
     }
   };
 
@@ -771,56 +771,75 @@ kv_status launch_decode(Kernel kernel, const DecodeParams& prm, hipStream_t st) 
   return launch_status("kv_paged_attention_decode");
 }
 
-template <int DT, int D, int BS>
+template <int DT, int D, int BS, bool NT>
 kv_status launch_valu(const DecodeParams& prm, int gmax, hipStream_t st) {
   switch (gmax) {
-    case 1: return launch_decode(decode_valu_kernel<DT, D, 1, BS>, prm, st);
-    case 2: return launch_decode(decode_valu_kernel<DT, D, 2, BS>, prm, st);
-    case 4: return launch_decode(decode_valu_kernel<DT, D, 4, BS>, prm, st);
-    case 8: return launch_decode(decode_valu_kernel<DT, D, 8, BS>, prm, st);
-    case 16: return launch_decode(decode_valu_kernel<DT, D, 16, BS>, prm, st);
+    case 1: return launch_decode(decode_valu_kernel<DT, D, 1, BS, NT>, prm, st);
+    case 2: return launch_decode(decode_valu_kernel<DT, D, 2, BS, NT>, prm, st);
+    case 4: return launch_decode(decode_valu_kernel<DT, D, 4, BS, NT>, prm, st);
+    case 8: return launch_decode(decode_valu_kernel<DT, D, 8, BS, NT>, prm, st);
+    case 16: return launch_decode(decode_valu_kernel<DT, D, 16, BS, NT>, prm, st);
     default: return fail(KV_ERR_UNSUPPORTED, "decode: group size");
   }
 }
 
 // The decode kernel for one block size: MFMA for grouped 16-bit heads of
 // dimension 128, vector ALUs otherwise.
-template <int BS>
+template <int BS, bool NT>
 kv_status launch_decode_kernel(const DecodeParams& prm, kv_dtype dtype, int head_dim, int G,
                                hipStream_t st) {
   constexpr int R = kDecodeRing;
   if ((dtype == KV_F16 || dtype == KV_BF16) && head_dim == 128 && G >= 2) {
     if (G <= 8)
       return dtype == KV_BF16
-                 ? launch_decode(decode_mfma_kernel<KV_BF16, true, R, BS, false>, prm, st)
-                 : launch_decode(decode_mfma_kernel<KV_F16, true, R, BS, false>, prm, st);
+                 ? launch_decode(decode_mfma_kernel<KV_BF16, true, R, BS, false, NT>, prm, st)
+                 : launch_decode(decode_mfma_kernel<KV_F16, true, R, BS, false, NT>, prm, st);
     return dtype == KV_BF16
-               ? launch_decode(decode_mfma_kernel<KV_BF16, false, R, BS, false>, prm, st)
-               : launch_decode(decode_mfma_kernel<KV_F16, false, R, BS, false>, prm, st);
+               ? launch_decode(decode_mfma_kernel<KV_BF16, false, R, BS, false, NT>, prm, st)
+               : launch_decode(decode_mfma_kernel<KV_F16, false, R, BS, false, NT>, prm, st);
   }
   const int gmax = G == 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
   if (dtype == KV_F32)
-    return head_dim == 64 ? launch_valu<KV_F32, 64, BS>(prm, gmax, st)
-                          : launch_valu<KV_F32, 128, BS>(prm, gmax, st);
+    return head_dim == 64 ? launch_valu<KV_F32, 64, BS, NT>(prm, gmax, st)
+                          : launch_valu<KV_F32, 128, BS, NT>(prm, gmax, st);
   if (dtype == KV_F16)  // 16-bit head_dim 128 reaches here only with G == 1
-    return head_dim == 64 ? launch_valu<KV_F16, 64, BS>(prm, gmax, st)
-                          : launch_decode(decode_valu_kernel<KV_F16, 128, 1, BS>, prm, st);
-  return head_dim == 64 ? launch_valu<KV_BF16, 64, BS>(prm, gmax, st)
-                        : launch_decode(decode_valu_kernel<KV_BF16, 128, 1, BS>, prm, st);
+    return head_dim == 64 ? launch_valu<KV_F16, 64, BS, NT>(prm, gmax, st)
+                          : launch_decode(decode_valu_kernel<KV_F16, 128, 1, BS, NT>, prm, st);
+  return head_dim == 64 ? launch_valu<KV_BF16, 64, BS, NT>(prm, gmax, st)
+                        : launch_decode(decode_valu_kernel<KV_BF16, 128, 1, BS, NT>, prm, st);
 }
 
 // fp8 cache: the MFMA kernel for every group size (1..16), head_dim 128,
 // f16 or bf16 queries.
-template <int BS>
+template <int BS, bool NT>
 kv_status launch_decode_kernel_fp8(const DecodeParams& prm, kv_dtype dtype, int G,
                                    hipStream_t st) {
   constexpr int R = kDecodeRing8;
   if (G <= 8)
-    return dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16, true, R, BS, true>, prm, st)
-                            : launch_decode(decode_mfma_kernel<KV_F16, true, R, BS, true>, prm, st);
-  return dtype == KV_BF16 ? launch_decode(decode_mfma_kernel<KV_BF16, false, R, BS, true>, prm, st)
-                          : launch_decode(decode_mfma_kernel<KV_F16, false, R, BS, true>, prm, st);
+    return dtype == KV_BF16
+               ? launch_decode(decode_mfma_kernel<KV_BF16, true, R, BS, true, NT>, prm, st)
+               : launch_decode(decode_mfma_kernel<KV_F16, true, R, BS, true, NT>, prm, st);
+  return dtype == KV_BF16
+             ? launch_decode(decode_mfma_kernel<KV_BF16, false, R, BS, true, NT>, prm, st)
+             : launch_decode(decode_mfma_kernel<KV_F16, false, R, BS, true, NT>, prm, st);
 }
+
+// The decode kernel for a block size and load policy.
+template <bool NT>
+kv_status launch_for_block_size(const DecodeParams& prm, kv_dtype dtype, int head_dim, int G,
+                                bool kv8, hipStream_t stream) {
+  const int bs = prm.block_size;
+  if (kv8)
+    return bs == 8    ? launch_decode_kernel_fp8<8, NT>(prm, dtype, G, stream)
+           : bs == 16 ? launch_decode_kernel_fp8<16, NT>(prm, dtype, G, stream)
+                      : launch_decode_kernel_fp8<32, NT>(prm, dtype, G, stream);
+  return bs == 8    ? launch_decode_kernel<8, NT>(prm, dtype, head_dim, G, stream)
+         : bs == 16 ? launch_decode_kernel<16, NT>(prm, dtype, head_dim, G, stream)
+                    : launch_decode_kernel<32, NT>(prm, dtype, head_dim, G, stream);
+}
+
+// Load policy of the decode launches made by this host thread.
+thread_local kv_load_policy g_load_policy = KV_LOADS_STREAM;
 
 }  // namespace
 
@@ -935,13 +954,9 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
   prm.slots = slots;
 
   prm.block_size = block_size;
-  const kv_status st =
-      kv8 ? (block_size == 8    ? launch_decode_kernel_fp8<8>(prm, dtype, G, stream)
-             : block_size == 16 ? launch_decode_kernel_fp8<16>(prm, dtype, G, stream)
-                                : launch_decode_kernel_fp8<32>(prm, dtype, G, stream))
-      : block_size == 8  ? launch_decode_kernel<8>(prm, dtype, head_dim, G, stream)
-      : block_size == 16 ? launch_decode_kernel<16>(prm, dtype, head_dim, G, stream)
-                         : launch_decode_kernel<32>(prm, dtype, head_dim, G, stream);
+  const kv_status st = g_load_policy == KV_LOADS_CACHED
+                           ? launch_for_block_size<false>(prm, dtype, head_dim, G, kv8, stream)
+                           : launch_for_block_size<true>(prm, dtype, head_dim, G, kv8, stream);
   if (st != KV_OK || nparts <= 1) return st;
   const dim3 mgrid((unsigned)((int64_t)S * num_kv_heads));
   if (head_dim == 128)
@@ -1026,5 +1041,16 @@ kv_status kv_paged_attention_decode_append_fp8(
                      partition_size, max_context_len, work_items, n_items, workspace, ws_bytes,
                      k_new, v_new, slots, stream, true, k_scale, v_scale);
 }
+
+kv_status kv_paged_attention_set_load_policy(kv_load_policy policy) {
+  pagedkv::clear_error();
+  if (policy != KV_LOADS_STREAM && policy != KV_LOADS_CACHED)
+    return fail(KV_ERR_INVALID, "kv_paged_attention_set_load_policy: unknown policy %d",
+                (int)policy);
+  g_load_policy = policy;
+  return KV_OK;
+}
+
+kv_load_policy kv_paged_attention_load_policy(void) { return g_load_policy; }
 
 }  // extern "C"

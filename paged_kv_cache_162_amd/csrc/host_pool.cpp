@@ -399,6 +399,13 @@ kv_status kv_seq_swap_in(kv_pool_t* p, int64_t seq, int32_t cap, int32_t* ids_ou
   return KV_OK;
 }
 
+int32_t kv_pool_shared_blocks(const kv_pool_t* p) {
+  if (!p) return -1;
+  int32_t n = 0;
+  for (const int32_t r : p->refcount) n += r > 1 ? 1 : 0;
+  return n;
+}
+
 int32_t kv_seq_is_swapped(const kv_pool_t* p, int64_t seq) {
   if (!p) return -1;
   auto it = p->seqs.find(seq);

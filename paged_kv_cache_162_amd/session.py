@@ -223,6 +223,10 @@ class DecodeSession:
         if self.use_plan:
             items = kv.kv_paged_attention_plan(lens, self.partition_size)
             self.d_items = torch.from_numpy(items).to(dev)
+        # shared blocks are read by several sequences in the step: keep them
+        # in the caches; otherwise stream every block past them
+        self.load_policy = (kv.KV_LOADS_CACHED if kv.kv_pool_shared_blocks(self.pool) > 0
+                            else kv.KV_LOADS_STREAM)
         return host_slots, pairs
 
     def step(self, q, k_new, v_new, out, scale: float, k_pool=None, v_pool=None,
@@ -236,6 +240,7 @@ class DecodeSession:
         kp = self.k_pool if k_pool is None else k_pool
         vp_ = self.v_pool if v_pool is None else v_pool
         fused = self.fused if fused is None else fused
+        kv.kv_paged_attention_set_load_policy(self.load_policy)
         if self.d_pairs.shape[0]:
             kv.kv_copy_blocks([kp], [vp_], self.d_pairs, self.NB, self.block_bytes)
         if not fused:

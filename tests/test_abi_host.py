@@ -247,6 +247,7 @@ def test_random_operation_sequences_match_oracle(kv, ops, seed):
                     if kind == "alloc":
                         raw.extend(ores)
             assert [kv.kv_block_refcount(p, b) for b in range(NB)] == bm.refcount
+            assert kv.kv_pool_shared_blocks(p) == sum(r > 1 for r in bm.refcount)
             assert kv.kv_num_free_blocks(p) == bm.num_free()
             for oh, chh in live:
                 assert kv.kv_seq_is_swapped(p, chh) == int(bm.is_swapped(oh))
@@ -365,3 +366,14 @@ def test_prefill_fp8_entry_point_validates_on_the_host(kv):
     assert call(dt=kv.KV_F32) == kv.KV_ERR_UNSUPPORTED
     assert call() == kv.KV_ERR_INVALID
     assert call(S=0) == kv.KV_OK
+
+
+def test_load_policy_setting(kv):
+    assert kv.kv_paged_attention_load_policy() == kv.KV_LOADS_STREAM
+    kv.kv_paged_attention_set_load_policy(kv.KV_LOADS_CACHED)
+    assert kv.kv_paged_attention_load_policy() == kv.KV_LOADS_CACHED
+    with pytest.raises(kv.KVError):
+        kv.kv_paged_attention_set_load_policy(7)
+    assert kv.kv_paged_attention_load_policy() == kv.KV_LOADS_CACHED
+    kv.kv_paged_attention_set_load_policy(kv.KV_LOADS_STREAM)
+    assert kv.lib.kv_pool_shared_blocks(None) == -1

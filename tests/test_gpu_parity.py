@@ -543,3 +543,29 @@ def test_workspace_reuse_gives_identical_results():
     assert all(np.array_equal(outs[0].view(np.uint32), o.view(np.uint32)) for o in outs[1:])
     ref = oracle.decode_attention(q, kp, vp, tab, cl, 0.088, dt)
     check_attention(outs[0].reshape(-1, D), ref.reshape(-1, D), dt, "workspace reuse")
+
+
+@pytest.mark.parametrize("cfg,S", [(3, 12), (5, None), (2, 3)])
+def test_load_policies_give_identical_bits(cfg, S):
+    """Streaming (non-temporal) and cached K/V loads compute the same bits;
+    the session picks cached loads exactly when the pool holds shared blocks."""
+    kv = kvlib()
+    res = {}
+    for policy in (kv.KV_LOADS_STREAM, kv.KV_LOADS_CACHED):
+        case = Case(cfg, S=S)
+        case.device_run()        # the session's own choice
+        chosen = case.sess.load_policy
+        assert chosen == (kv.KV_LOADS_CACHED if cfg == 5 else kv.KV_LOADS_STREAM)
+        case.sess.load_policy = policy
+        out = torch.full_like(case.out_dev, float("nan"))
+        ws = case.sess.workspace
+        kv.kv_paged_attention_set_load_policy(policy)
+        kv.kv_paged_attention_decode(out, case.q_dev, case.k_dev, case.v_dev, case.sess.d_tables,
+                                     case.sess.d_lens, case.sp.scale, case.sess.max_context_len,
+                                     ws, 0, case.sess.d_items)
+        torch.cuda.synchronize()
+        res[policy] = out.cpu().numpy()
+        assert np.array_equal(res[policy].view(np.uint32), case.out_dev.cpu().numpy().view(np.uint32))
+        case.sess.close()
+    kv.kv_paged_attention_set_load_policy(kv.KV_LOADS_STREAM)
+    assert np.array_equal(res[0].view(np.uint32), res[1].view(np.uint32))
