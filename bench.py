@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=3, help="workload number 1-9")
-    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="partition tokens (0 = chosen per batch by kv_paged_attention_choose_partition)")
     ap.add_argument("--block-size", type=int, default=16, help="tokens per KV block (8, 16 or 32)")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas to rotate (0 = auto)")
     ap.add_argument("--no-plan", action="store_true", help="padded grid instead of the host work plan")
@@ -135,7 +136,7 @@ def pmc_parse(fetch_dir, write_dir, out_path, workload, partition):
     copy, whose true byte count is known."""
     cal_bytes = 2 * CAL_PAIRS * CAL_BLOCK_BYTES
     prefill = is_prefill(workload)
-    res = {"workload": workload, "partition": partition,
+    res = {"workload": workload, "partition_arg": partition,
            "kernel_source_digest": kernel_source_digest(PREFILL_SOURCES if prefill else DECODE_SOURCES),
            "calibration_bytes": cal_bytes}
     total = 0.0
@@ -425,7 +426,7 @@ def main():
     if args.pmc_parse:
         kind = "prefill" if is_prefill(args.workload) else "decode"
         out = args.pmc_out or os.path.join(ROOT, "profiles", f"{kind}_traffic_w{args.workload}.json")
-        pmc_parse(args.pmc_parse[0], args.pmc_parse[1], out, args.workload, args.partition or 512)
+        pmc_parse(args.pmc_parse[0], args.pmc_parse[1], out, args.workload, args.partition)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -545,7 +546,7 @@ def main():
     if os.path.exists(tpath):
         t = json.load(open(tpath))
         if t.get("kernel_source_digest") == kernel_source_digest() and \
-                t.get("workload") == args.workload and (args.partition or 512) == t.get("partition", 512):
+                t.get("workload") == args.workload and args.partition == t.get("partition_arg"):
             traffic = round(float(t["bytes_per_launch"]))
 
     res = {
@@ -564,7 +565,8 @@ def main():
         "config": {
             "workload": f"{sp.name}: {sp.description}",
             "sequences": sp.S, "q_heads": sp.Hq, "kv_heads": sp.Hkv, "head_dim": sp.D,
-            "block_size": args.block_size, "partition_tokens": args.partition or 512,
+            "block_size": args.block_size, "partition_tokens": sess.step_partition,
+            "partition_choice": "given" if args.partition else "chosen from the batch's lengths",
             "sum_context": int(lens.sum()), "max_context": int(lens.max()),
             "kv_bytes_per_step": kvb, "replicas_rotated": R, "parallelism": "single GPU",
             "fused_cache_write": not args.unfused, "hip_graph": bool(args.graph),

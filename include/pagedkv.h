@@ -339,6 +339,17 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
                                     int32_t n_items, void* workspace, size_t ws_bytes,
                                     hipStream_t stream);
 
+/* A partition size for a decode batch, from the host copy of its context
+ * lengths: the largest of 1024, 768 and 512 tokens that is valid for
+ * block_size and still gives at least min_units work units (num_kv_heads x
+ * the partitions of every sequence), else 512. Fewer, longer units start
+ * less work, write fewer partials and leave less to merge; min_units keeps
+ * the device covered (about 1500 measured best on MI355X: 3/4 of 256 CUs x
+ * 8 waves). Returns 512 for empty or invalid input. */
+int32_t kv_paged_attention_choose_partition(const int32_t* context_lens_host, int32_t S,
+                                            int32_t num_kv_heads, int32_t block_size,
+                                            int32_t min_units);
+
 /* How the decode kernels load K and V (all four decode entry points, for
  * the calling host thread; default KV_LOADS_STREAM):
  *   KV_LOADS_STREAM  loads carry the non-temporal hint: every block is read

@@ -107,6 +107,7 @@ _SIGS = {
     "kv_paged_attention_prefill_fp8": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
                                                  i32, i32, i32, i32, f32, C.c_int, f32, f32, i32,
                                                  vp, i32, vp]),
+    "kv_paged_attention_choose_partition": (i32, [P_i32, i32, i32, i32, i32]),
     "kv_paged_attention_set_load_policy": (C.c_int, [C.c_int]),
     "kv_paged_attention_load_policy": (C.c_int, []),
     "kv_last_error": (C.c_char_p, []),
@@ -268,6 +269,13 @@ def kv_paged_attention_set_load_policy(policy: int) -> None:
 
 def kv_paged_attention_load_policy() -> int:
     return int(lib.kv_paged_attention_load_policy())
+
+
+def kv_paged_attention_choose_partition(context_lens_host, num_kv_heads: int, block_size: int,
+                                        min_units: int) -> int:
+    lens = _i32_array(context_lens_host)
+    return int(lib.kv_paged_attention_choose_partition(_p32(lens), len(lens), num_kv_heads,
+                                                        block_size, min_units))
 
 
 # ---------------------------------------------------------------------------

@@ -99,3 +99,26 @@ extern "C" kv_status kv_paged_attention_prefill_plan(const int32_t* query_start_
   }
   return KV_OK;
 }
+
+// A partition size for a decode batch: the largest of 1024, 768 and 512
+// tokens (valid for the block size: at most 64 blocks per partition) whose
+// work units - KV heads times the partitions of every sequence - still
+// number at least min_units, else 512. Longer partitions mean fewer units to
+// start, fewer partial results and less merge work; min_units keeps enough
+// units to cover the device (measured on MI355X: about 3/4 of the 2048
+// waves it runs at once, 256 CUs x 8 waves).
+extern "C" int32_t kv_paged_attention_choose_partition(const int32_t* context_lens_host,
+                                                       int32_t S, int32_t num_kv_heads,
+                                                       int32_t block_size, int32_t min_units) {
+  if (S <= 0 || !context_lens_host || num_kv_heads <= 0 || block_size <= 0) return 512;
+  for (const int32_t P : {1024, 768}) {
+    if (P % block_size != 0 || P / block_size > 64) continue;
+    int64_t units = 0;
+    for (int32_t s = 0; s < S; ++s) {
+      const int64_t ctx = context_lens_host[s];
+      units += ctx > 0 ? (ctx + P - 1) / P : 1;
+    }
+    if (units * num_kv_heads >= min_units) return P;
+  }
+  return 512;
+}

@@ -22,6 +22,10 @@ import numpy as np
 
 from . import binding as kv
 
+# Work units below which a longer partition is not chosen: about 3/4 of the
+# 2048 waves an MI355X runs at once (256 CUs x 8 waves), measured best.
+AUTO_PARTITION_MIN_UNITS = 1500
+
 
 class DecodeSession:
     def __init__(self, *, k_pool, v_pool, num_q_heads: int, free_order: Optional[Sequence[int]] = None,
@@ -35,7 +39,10 @@ class DecodeSession:
         self.dtype = kv.dtype_code(k_pool)
         self.fp8 = self.dtype == kv.KV_FP8_E4M3
         self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        # 0: choose per step from the batch's lengths (the library's own
+        # default, 512 tokens, is what the entry points use for 0)
         self.partition_size = partition_size
+        self.min_units = AUTO_PARTITION_MIN_UNITS
         self.use_plan = use_plan
         self.fused = fused
         self.pool = kv.kv_pool_create(NB, B, 1, Hkv, D, self.dtype)
@@ -206,6 +213,8 @@ class DecodeSession:
                 pairs.append(pair)
         tables, lens = self.tables(seqs)
         dev = self.device
+        self.step_partition = self.partition_size or kv.kv_paged_attention_choose_partition(
+            lens, self.Hkv, self.B, self.min_units)
         self.seqs = list(seqs)
         self.d_tables = torch.from_numpy(tables).to(dev)
         self.d_lens = torch.from_numpy(lens).to(dev)
@@ -216,12 +225,12 @@ class DecodeSession:
         self.max_context_len = int(lens.max()) if len(lens) else 0
         S = len(seqs)
         ws = kv.kv_paged_attention_workspace_bytes(S, self.Hq, self.Hkv, self.D,
-                                                   self.max_context_len, self.partition_size)
+                                                   self.max_context_len, self.step_partition)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev) if ws else None
         self.host_tables, self.host_lens = tables, lens
         self.d_items = None
         if self.use_plan:
-            items = kv.kv_paged_attention_plan(lens, self.partition_size)
+            items = kv.kv_paged_attention_plan(lens, self.step_partition)
             self.d_items = torch.from_numpy(items).to(dev)
         # shared blocks are read by several sequences in the step: keep them
         # in the caches; otherwise stream every block past them
@@ -257,19 +266,19 @@ class DecodeSession:
                 kv.kv_paged_attention_decode_append_fp8(
                     out, q, k_new, v_new, kp, vp_, self.d_tables, self.d_lens, scale, self.k_scale,
                     self.v_scale, self.max_context_len, self.d_slots, self.workspace,
-                    self.partition_size, self.d_items)
+                    self.step_partition, self.d_items)
             else:
                 kv.kv_paged_attention_decode_fp8(
                     out, q, kp, vp_, self.d_tables, self.d_lens, scale, self.k_scale, self.v_scale,
-                    self.max_context_len, self.workspace, self.partition_size, self.d_items)
+                    self.max_context_len, self.workspace, self.step_partition, self.d_items)
         elif fused:
             kv.kv_paged_attention_decode_append(out, q, k_new, v_new, kp, vp_, self.d_tables,
                                                 self.d_lens, scale, self.max_context_len,
-                                                self.d_slots, self.workspace, self.partition_size,
+                                                self.d_slots, self.workspace, self.step_partition,
                                                 self.d_items)
         else:
             kv.kv_paged_attention_decode(out, q, kp, vp_, self.d_tables, self.d_lens, scale,
-                                         self.max_context_len, self.workspace, self.partition_size,
+                                         self.max_context_len, self.workspace, self.step_partition,
                                          self.d_items)
         if decode_events is not None:
             decode_events[1].record()

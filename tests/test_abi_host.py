@@ -377,3 +377,16 @@ def test_load_policy_setting(kv):
     assert kv.kv_paged_attention_load_policy() == kv.KV_LOADS_CACHED
     kv.kv_paged_attention_set_load_policy(kv.KV_LOADS_STREAM)
     assert kv.lib.kv_pool_shared_blocks(None) == -1
+
+
+def test_choose_partition(kv):
+    # 8 sequences of 32768 tokens, 8 KV heads: 1024-token partitions give 2048 units
+    lens = [32768] * 8
+    assert kv.kv_paged_attention_choose_partition(lens, 8, 16, 1500) == 1024
+    assert kv.kv_paged_attention_choose_partition(lens, 8, 16, 2049) == 768    # 2752 units
+    assert kv.kv_paged_attention_choose_partition(lens, 8, 16, 2753) == 512
+    assert kv.kv_paged_attention_choose_partition(lens, 8, 8, 1500) == 512     # 96 blocks > 64
+    assert kv.kv_paged_attention_choose_partition(lens, 8, 32, 1500) == 1024
+    assert kv.kv_paged_attention_choose_partition([], 8, 16, 1500) == 512
+    # a length of 0 still counts one unit (its output is written)
+    assert kv.kv_paged_attention_choose_partition([0] * 10, 2, 16, 20) == 1024
