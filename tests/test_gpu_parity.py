@@ -545,6 +545,87 @@ def test_workspace_reuse_gives_identical_results():
     check_attention(outs[0].reshape(-1, D), ref.reshape(-1, D), dt, "workspace reuse")
 
 
+def _split_case(seed):
+    rng = np.random.default_rng(seed)
+    dt, D, Hkv, G = "bf16", 128, 4, 4
+    lens = np.array([3000, 1, 513, 1024, 777, 2049], np.int32)
+    q, kp, vp, tab, cl = random_case(rng, list(lens), G * Hkv, Hkv, D, dt)
+    return dt, D, Hkv, G * Hkv, q, kp, vp, tab, cl
+
+
+def test_incomplete_plan_does_not_leak_into_the_next_call():
+    """A plan that leaves out a partition of a split sequence spoils only that
+    sequence's output (NaN here: the missing partials are the workspace's NaN
+    fill); the complete sequences of the call are right, and the next call on
+    the same workspace, with a full plan or none, is right everywhere."""
+    kv = kvlib()
+    dt, D, Hkv, Hq, q, kp, vp, tab, cl = _split_case(42)
+    S, P, mc = len(cl), 256, int(cl.max())
+    wsb = kv.kv_paged_attention_workspace_bytes(S, Hq, Hkv, D, mc, P)
+    ws = torch.full((wsb // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    args = (to_dev(q, dt), to_dev(kp, dt), to_dev(vp, dt), torch.from_numpy(tab).cuda(),
+            torch.from_numpy(cl).cuda())
+    plan = kv.kv_paged_attention_plan(cl, P)
+    # drop one partition of sequence 0 (12 partitions) and one of sequence 5
+    keep = np.ones(len(plan), bool)
+    keep[np.flatnonzero(plan[:, 0] == 0)[3]] = False
+    keep[np.flatnonzero(plan[:, 0] == 5)[0]] = False
+    partial_plan = torch.from_numpy(np.ascontiguousarray(plan[keep])).cuda()
+    out = torch.full((S, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    kv.kv_paged_attention_decode(out, *args, 0.088, mc, ws, P, partial_plan)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isnan(got[0]).all() and np.isnan(got[5]).all()   # merged with NaN partials
+    ref = oracle.decode_attention(q, kp, vp, tab, cl, 0.088, dt)
+    check_attention(got[1:5].reshape(-1, D), ref[1:5].reshape(-1, D), dt, "complete groups")
+    for items in (torch.from_numpy(plan).cuda(), None):
+        out.fill_(float("nan"))
+        kv.kv_paged_attention_decode(out, *args, 0.088, mc, ws, P, items)
+        torch.cuda.synchronize()
+        check_attention(out.cpu().numpy().reshape(-1, D), ref.reshape(-1, D), dt,
+                        f"after an incomplete plan ({'plan' if items is not None else 'grid'})")
+
+
+def test_graph_replays_and_eager_calls_share_a_workspace():
+    """A captured split-K decode (decode and merge kernels) replayed with
+    eager calls on the same workspace in between: every replay and every
+    eager call gives the same bits."""
+    kv = kvlib()
+    dt, D, Hkv, Hq, q, kp, vp, tab, cl = _split_case(43)
+    S, P, mc = len(cl), 512, int(cl.max())
+    wsb = kv.kv_paged_attention_workspace_bytes(S, Hq, Hkv, D, mc, P)
+    ws = torch.full((wsb // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    args = (to_dev(q, dt), to_dev(kp, dt), to_dev(vp, dt), torch.from_numpy(tab).cuda(),
+            torch.from_numpy(cl).cuda())
+    items = torch.from_numpy(kv.kv_paged_attention_plan(cl, P)).cuda()
+    eager = torch.full((S, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    kv.kv_paged_attention_decode(eager, *args, 0.088, mc, ws, P, items)
+    torch.cuda.synchronize()
+    want = eager.cpu().numpy()
+    ref = oracle.decode_attention(q, kp, vp, tab, cl, 0.088, dt)
+    check_attention(want.reshape(-1, D), ref.reshape(-1, D), dt, "eager")
+    out = torch.full_like(eager, float("nan"))
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            kv.kv_paged_attention_decode(out, *args, 0.088, mc, ws, P, items,
+                                         stream=stream.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"[gpu] decode graph replay {rep}")
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+        if rep % 2 == 0:
+            eager.fill_(float("nan"))
+            kv.kv_paged_attention_decode(eager, *args, 0.088, mc, ws, P, items)
+            torch.cuda.synchronize()
+            assert np.array_equal(eager.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
 @pytest.mark.parametrize("cfg,S", [(3, 12), (5, None), (2, 3)])
 def test_load_policies_give_identical_bits(cfg, S):
     """Streaming (non-temporal) and cached K/V loads compute the same bits;
