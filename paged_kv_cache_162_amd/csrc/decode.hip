@@ -44,10 +44,11 @@ constexpr int kStageStride = 132;  // floats per head row in LDS (128 + 4 agains
 #endif
 constexpr int kDecodeRing = PAGEDKV_DECODE_RING;  // K/V blocks in flight per wave (MFMA decode)
 #ifndef PAGEDKV_DECODE_RING8
-#define PAGEDKV_DECODE_RING8 6
+#define PAGEDKV_DECODE_RING8 4
 #endif
-// fp8 cache: a tile holds half the bytes, so twice the tiles give the same
-// bytes in flight for the same registers
+// fp8 cache: a raw tile holds half the bytes, but its widened copy costs
+// registers; four tiles in flight keep the kernel at three waves per SIMD
+// (164 VGPRs), which measured faster than six tiles at two waves
 constexpr int kDecodeRing8 = PAGEDKV_DECODE_RING8;
 
 // ---- shared decode parameters ----------------------------------------------
