@@ -504,6 +504,51 @@ def test_shared_prefix_bitwise_equals_duplicated():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("P", [0, 16])
+def test_many_short_sequences(P):
+    """3,000 sequences of 1..40 tokens: a grid of 6,000+ single-wave units
+    (no merge at the default partition), and at the smallest partition (16
+    tokens) up to 3 partitions per sequence merged in 6,000 groups."""
+    rng = np.random.default_rng(78)
+    dt, D, Hkv, G = "bf16", 128, 2, 4
+    lens = list(rng.integers(1, 41, 3000))
+    q, kp, vp, tab, cl = random_case(rng, lens, G * Hkv, Hkv, D, dt)
+    ref = oracle.decode_attention(q, kp, vp, tab, cl, 0.09, dt)
+    for plan in (False, True):
+        got = gpu_decode(q, kp, vp, tab, cl, 0.09, dt, P, plan=plan)
+        log(f"[gpu] many short P={P} plan={plan}",
+            check_attention(got.reshape(-1, D), ref.reshape(-1, D), dt, f"3000 short, P={P}"))
+
+
+_LONG = {}
+
+
+def _long_case():
+    """One 131,071-token sequence beside a 1-token one (oracle computed once)."""
+    if not _LONG:
+        rng = np.random.default_rng(77)
+        dt, D, Hkv, G = "bf16", 128, 1, 8
+        q, kp, vp, tab, cl = random_case(rng, [131071, 1], G * Hkv, Hkv, D, dt, poison=False)
+        ref = oracle.decode_attention(q, kp, vp, tab, cl, 1 / np.sqrt(D), dt)
+        _LONG.update(case=(q, kp, vp, tab, cl), ref=ref, dt=dt, D=D)
+    return _LONG
+
+
+@pytest.mark.parametrize("P", [512, 1024])
+def test_one_very_long_sequence(P):
+    """256 (or 128) partitions merged in one group, a table far longer than
+    the 64 entries a unit stages, and a tail partition of 511 (1,023) tokens;
+    the 1-token sequence beside it is checked on its own scale."""
+    c = _long_case()
+    q, kp, vp, tab, cl = c["case"]
+    dt, D, ref = c["dt"], c["D"], c["ref"]
+    got = gpu_decode(q, kp, vp, tab, cl, 1 / np.sqrt(D), dt, P, plan=True)
+    for s in range(2):
+        log(f"[gpu] long sequence P={P} seq {s}",
+            check_attention(got[s].reshape(-1, D), ref[s].reshape(-1, D), dt,
+                            f"sequence {s} ({cl[s]} tokens), partition {P}"))
+
+
 def test_split_and_unsplit_agree_and_runs_are_deterministic():
     rng = np.random.default_rng(33)
     dt, D, Hkv, G = "bf16", 128, 2, 4
