@@ -429,8 +429,9 @@ def main():
         pmc_parse(args.pmc_parse[0], args.pmc_parse[1], out, args.workload, args.partition)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(the design for sharding is described in DESIGN.md)"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1 "
+                                   "(the kernels work on one GPU's share of the batch; "
+                                   "sharding across GPUs is not implemented)"}))
         sys.exit(2)
     import torch
     from workloads import make_workload
