@@ -107,6 +107,29 @@ def copy_calibration(kv, torch):
     del k, v
 
 
+def copy_bandwidth(kv, torch, reps=10):
+    """Bytes read plus written per second by kv_copy_blocks on the calibration
+    buffers (256 MiB read and 256 MiB written per call): a measured ceiling for
+    HBM traffic on this GPU, reported beside the 8 TB/s peak."""
+    nb = 2 * CAL_PAIRS
+    k = torch.zeros(nb * CAL_BLOCK_BYTES, dtype=torch.uint8, device="cuda")
+    v = torch.zeros_like(k)
+    pairs = torch.stack([torch.arange(CAL_PAIRS, dtype=torch.int32),
+                         torch.arange(CAL_PAIRS, 2 * CAL_PAIRS, dtype=torch.int32)], 1).cuda()
+    for _ in range(3):
+        kv.kv_copy_blocks([k], [v], pairs, nb, CAL_BLOCK_BYTES)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        kv.kv_copy_blocks([k], [v], pairs, nb, CAL_BLOCK_BYTES)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del k, v
+    return 2 * 2 * CAL_PAIRS * CAL_BLOCK_BYTES / (ms * 1e-3) / 1e9
+
+
 def _counter_rows(d):
     import csv
     import glob
@@ -537,6 +560,19 @@ def main():
     torch.cuda.synchronize()
     warm_ms = w0.elapsed_time(w1) / K
 
+    # the step's cache write on its own (the unfused path: slot mapping and
+    # write of the S new tokens), events per call
+    cw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for k in range(K):
+        a, b, qq, kk, vv = reps[k % R]
+        cw[k][0].record()
+        sess.write_step_tokens(kk, vv, a, b)
+        cw[k][1].record()
+    torch.cuda.synchronize()
+    cache_write_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in cw]))
+    copy_gbs = copy_bandwidth(kv, torch)
+
     kvb = kv_bytes(lens, sp.Hkv, sp.D, sp.kv_elem_bytes)
     alg = decode_alg_bytes(lens, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes, args.block_size,
                            sp.kv_elem_bytes)
@@ -576,7 +612,10 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(sp.S / (step_ms * 1e-3), 1),
         "decode_ms": round(dec_avg, 5),
+        "decode_ms_median": round(float(np.median(dec_ms)), 5),
         "decode_kv_gbs": round(kvb / (dec_avg * 1e-3) / 1e9, 2),
+        "cache_write_ms": round(cache_write_ms, 5),
+        "copy_gbs": round(copy_gbs, 1),
         "warm_ms_per_step": round(warm_ms, 5),
         "warm_kv_gbs": round(kvb / (warm_ms * 1e-3) / 1e9, 2),
         "kv_memory": memory,

@@ -238,6 +238,19 @@ class DecodeSession:
                             else kv.KV_LOADS_STREAM)
         return host_slots, pairs
 
+    def write_step_tokens(self, k_new, v_new, k_pool=None, v_pool=None) -> None:
+        """The unfused cache write of the step on its own: slot mapping of
+        every new token and the write of its K/V rows (one launch for a
+        16-bit cache, two for fp8), on the current stream."""
+        kp = self.k_pool if k_pool is None else k_pool
+        vp_ = self.v_pool if v_pool is None else v_pool
+        if self.fp8:
+            kv.kv_slot_mapping(self.d_tables, self.d_seq_idx, self.d_pos, self.d_slots, self.B)
+            self._write(k_new, v_new, kp, vp_, self.d_slots)
+        else:
+            kv.kv_append_tokens(self.d_tables, self.d_seq_idx, self.d_pos, k_new, v_new, kp, vp_,
+                                self.d_slots)
+
     def step(self, q, k_new, v_new, out, scale: float, k_pool=None, v_pool=None,
              decode_events=None, fused: Optional[bool] = None) -> None:
         """Device half of a decode step, all on the current stream:
@@ -253,12 +266,7 @@ class DecodeSession:
         if self.d_pairs.shape[0]:
             kv.kv_copy_blocks([kp], [vp_], self.d_pairs, self.NB, self.block_bytes)
         if not fused:
-            if self.fp8:
-                kv.kv_slot_mapping(self.d_tables, self.d_seq_idx, self.d_pos, self.d_slots, self.B)
-                self._write(k_new, v_new, kp, vp_, self.d_slots)
-            else:
-                kv.kv_append_tokens(self.d_tables, self.d_seq_idx, self.d_pos, k_new, v_new, kp,
-                                    vp_, self.d_slots)
+            self.write_step_tokens(k_new, v_new, kp, vp_)
         if decode_events is not None:
             decode_events[0].record()
         if self.fp8:
