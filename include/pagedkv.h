@@ -302,7 +302,7 @@ size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_
  * max_context_len: host upper bound on every context_lens[s]; it sizes the
  *               grid (number of partitions).
  * partition_size: tokens per work item: a multiple of 16 and of block_size,
- *               at most 1024 tokens and 64 blocks; 0 = 512.
+ *               at most 1024 tokens; 0 = 512.
  *               Sequences longer than one partition are split and a second
  *               kernel merges the partial results with a log-sum-exp
  *               reduction ([2], "The Custom CUDA Kernel": per-piece partial
@@ -340,7 +340,7 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
                                     hipStream_t stream);
 
 /* A partition size for a decode batch, from the host copy of its context
- * lengths: the largest of 1024, 768 and 512 tokens that is valid for
+ * lengths: the largest of 1024, 768 and 512 tokens that is a multiple of
  * block_size and still gives at least min_units work units (num_kv_heads x
  * the partitions of every sequence), else 512. Fewer, longer units start
  * less work, write fewer partials and leave less to merge; min_units keeps

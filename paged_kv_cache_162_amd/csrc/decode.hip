@@ -36,7 +36,9 @@ namespace {
 
 constexpr int kTile = 16;            // tokens per compute tile (MFMA rows / VALU block step)
 constexpr int kMaxPartition = 1024;  // tokens per partition
-constexpr int kMaxPartBlocks = 64;   // blocks per partition: one table entry per lane
+// a partition's tiles fit one wave's lanes, so its table entries do too (one
+// per lane, or two with 8-token blocks)
+static_assert(kMaxPartition / kTile <= 64, "partition larger than a wave's table staging");
 constexpr int kDefaultPartition = 512;
 constexpr int kStageStride = 132;  // floats per head row in LDS (128 + 4 against bank conflicts)
 #ifndef PAGEDKV_DECODE_RING
@@ -126,32 +128,58 @@ __device__ __forceinline__ int unit_prologue(const DecodeParams& p, const WorkIt
   return w.part < nps ? nps : 0;
 }
 
-// Stage the unit's table entries ([2], "The Custom CUDA Kernel": the kernel
-// resolves logical blocks through the block table): lane i receives the
-// physical ID of the partition's block i (i < nblk <= 64). An ID outside the
+// A partition's table entries, held by the wave that reads them ([2], "The
+// Custom CUDA Kernel": the kernel resolves logical blocks through the block
+// table). With blocks of 16 or 32 tokens lane i holds entry i (a partition of
+// at most 64 tiles has at most 64 entries); with 8-token blocks lane i holds
+// entries 2i and 2i+1, so a partition of 64 tiles (128 entries) still fits.
+// Any entry j is then read by every lane with readlane. An ID outside the
 // pool marks the unit invalid and is replaced by block 0, so no load leaves
-// the pool. Entry j is later read by every lane with readlane.
-__device__ __forceinline__ int stage_entries(const DecodeParams& p, const int32_t* row, int nblk,
-                                             int lane, bool& bad) {
-  int e = 0;
-  if (lane < nblk) e = row[lane];
-  const bool out_of_pool = lane < nblk && (e < 0 || e >= p.num_blocks);
-  if (out_of_pool) e = 0;
-  bad = __builtin_amdgcn_ballot_w64(out_of_pool) != 0;
+// the pool; entries past the partition's end read as block 0.
+struct Entries {
+  int lo, hi;  // entry lane * K (and lane * K + 1 when K = 2)
+};
+template <int BS>
+constexpr int entries_per_lane() {
+  return BS < kTile ? 2 : 1;
+}
+
+// Replace out-of-pool and unused entries (index >= nent) by block 0 and
+// report whether any used entry is outside the pool.
+template <int BS>
+__device__ __forceinline__ Entries check_entries(const DecodeParams& p, Entries raw, int nent,
+                                                 int lane, bool& bad) {
+  constexpr int K = entries_per_lane<BS>();
+  const int i0 = lane * K;
+  const bool bad0 = i0 < nent && (raw.lo < 0 || raw.lo >= p.num_blocks);
+  const bool bad1 = K == 2 && i0 + 1 < nent && (raw.hi < 0 || raw.hi >= p.num_blocks);
+  bad = __builtin_amdgcn_ballot_w64(bad0 || bad1) != 0;
+  Entries e;
+  e.lo = (bad0 || i0 >= nent) ? 0 : raw.lo;
+  e.hi = (K == 1 || bad1 || i0 + 1 >= nent) ? 0 : raw.hi;
   return e;
 }
 
-// The same check on entries already loaded (lane i holds entry i of the
-// partition, or anything when i >= nblk).
-__device__ __forceinline__ int check_entries(const DecodeParams& p, int e, int nblk, int lane,
-                                             bool& bad) {
-  const bool out_of_pool = lane < nblk && (e < 0 || e >= p.num_blocks);
-  bad = __builtin_amdgcn_ballot_w64(out_of_pool) != 0;
-  return (out_of_pool || lane >= nblk) ? 0 : e;
+// Load the partition's entries from its table row (row[0] = the partition's
+// first block; at most `avail` entries exist in the row) and check them.
+template <int BS>
+__device__ __forceinline__ Entries stage_entries(const DecodeParams& p, const int32_t* row,
+                                                 int avail, int nent, int lane, bool& bad) {
+  constexpr int K = entries_per_lane<BS>();
+  Entries raw{0, 0};
+  if (lane * K < avail) raw.lo = row[lane * K];
+  if (K == 2 && lane * K + 1 < avail) raw.hi = row[lane * K + 1];
+  return check_entries<BS>(p, raw, nent, lane, bad);
 }
 
-__device__ __forceinline__ int entry_of(int staged, int j) {
-  return __builtin_amdgcn_readlane(staged, j);
+// Entry e (wave-uniform) of the partition.
+template <int BS>
+__device__ __forceinline__ int entry_at(const Entries& st, int e) {
+  if constexpr (BS < kTile)
+    return (e & 1) ? __builtin_amdgcn_readlane(st.hi, e >> 1)
+                   : __builtin_amdgcn_readlane(st.lo, e >> 1);
+  else
+    return __builtin_amdgcn_readlane(st.lo, e);
 }
 
 // Fused cache write ([3], "The allocation lifecycle": each decode step
@@ -166,13 +194,15 @@ struct NewToken {
   int row;        // row of the token in the unit's last 16-token tile
   int64_t slot;   // -1 if nothing is written (invalid unit)
 };
+template <int BS>
 __device__ __forceinline__ NewToken new_token(const DecodeParams& p, const WorkItem& w, int nps,
-                                              int ctx, int t0, int staged, bool bad, int lane) {
+                                              int ctx, int t0, const Entries& staged, bool bad,
+                                              int lane) {
   NewToken t;
   t.on = p.k_new != nullptr && w.part == nps - 1;
   t.row = (ctx - 1) % kTile;
   const int blk = (ctx - 1 - t0) / p.block_size;  // partition block holding ctx-1
-  t.slot = (t.on && !bad) ? (int64_t)entry_of(staged, blk) * p.block_size + (ctx - 1) % p.block_size
+  t.slot = (t.on && !bad) ? (int64_t)entry_at<BS>(staged, blk) * p.block_size + (ctx - 1) % p.block_size
                           : -1;
   if (t.on && p.slots && w.h == 0 && lane == 0) p.slots[w.s] = t.slot;
   return t;
@@ -183,15 +213,16 @@ __device__ __forceinline__ NewToken new_token(const DecodeParams& p, const WorkI
 // hold a whole tile (one table entry per tile, wave-uniform); blocks of 8
 // tokens hold half a tile, so rows 0..7 and 8..15 use consecutive entries.
 template <int BS>
-__device__ __forceinline__ size_t tile_row(const DecodeParams& p, int h, int staged, int j, int r,
-                                           int unit) {
+__device__ __forceinline__ size_t tile_row(const DecodeParams& p, int h, const Entries& staged,
+                                           int j, int r, int unit) {
   int e, rb;
   if constexpr (BS >= kTile) {
-    e = entry_of(staged, (kTile * j) / BS);
+    e = entry_at<BS>(staged, (kTile * j) / BS);
     rb = (kTile * j) % BS + r;
   } else {
-    const int e_lo = entry_of(staged, 2 * j);
-    const int e_hi = entry_of(staged, min(2 * j + 1, 63));
+    // entries 2j and 2j+1: both held by lane j
+    const int e_lo = __builtin_amdgcn_readlane(staged.lo, j);
+    const int e_hi = __builtin_amdgcn_readlane(staged.hi, j);
     e = r < 8 ? e_lo : e_hi;
     rb = r & 7;
   }
@@ -320,8 +351,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   const int nent = (t1 - t0 + BS - 1) / BS;              // table entries (blocks)
   const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + t0 / BS;
   bool bad = false;
-  const int staged = stage_entries(p, row, nent, lane, bad);
-  const NewToken nt = new_token(p, w, nps, ctx, t0, staged, bad, lane);
+  const Entries staged = stage_entries<BS>(p, row, p.max_blocks - t0 / BS, nent, lane, bad);
+  const NewToken nt = new_token<BS>(p, w, nps, ctx, t0, staged, bad, lane);
   if (nt.on && nt.slot >= 0 && r == nt.row % TPI) {
     // the lanes of row group nt.row % TPI load chunk c of the new token's
     // rows with the last tile; they store those chunks first, so program
@@ -514,13 +545,18 @@ void decode_mfma_kernel(DecodeParams p) {
   const int grp = lane >> 4;  // k-slot group
   const WorkItem w = unit_item(p, u);
   if (!w.ok) return;
-  // The loads that need only the unit go out together: the length, up to
-  // 64 table entries of the partition (bounded by the table width, so the
-  // length is not needed yet) and the queries.
+  // The loads that need only the unit go out together: the length, the
+  // partition's table entries (bounded by the table width, so the length is
+  // not needed yet) and the queries.
   const int ctx = p.lens[w.s];
   const int b0 = w.part * (p.part_tokens / BS);
-  int raw_entry = 0;
-  if (lane < p.max_blocks - b0) raw_entry = p.tables[(size_t)w.s * p.max_blocks + b0 + lane];
+  Entries raw_entry{0, 0};
+  {
+    constexpr int K = entries_per_lane<BS>();
+    const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + b0;
+    if (lane * K < p.max_blocks - b0) raw_entry.lo = row[lane * K];
+    if (K == 2 && lane * K + 1 < p.max_blocks - b0) raw_entry.hi = row[lane * K + 1];
+  }
   // B operand of the score MFMA: Q^T, lane holds head `hd`, dims 32kc+8grp..+8
   // (fp8 cache: dims 16grp+8kc.. for kc < 2 and 64+16grp+8(kc-2).. for kc >= 2,
   // the order in which a lane's two 16-byte K loads hold them)
@@ -563,8 +599,8 @@ void decode_mfma_kernel(DecodeParams p) {
   const int nblk = (t1 - t0 + kTile - 1) / kTile;  // 16-token tiles
   const int last = nblk - 1;
   bool bad = false;
-  const int staged = check_entries(p, raw_entry, (t1 - t0 + BS - 1) / BS, lane, bad);
-  const NewToken nt = new_token(p, w, nps, ctx, t0, staged, bad, lane);
+  const Entries staged = check_entries<BS>(p, raw_entry, (t1 - t0 + BS - 1) / BS, lane, bad);
+  const NewToken nt = new_token<BS>(p, w, nps, ctx, t0, staged, bad, lane);
   if (nt.on && nt.slot >= 0) {
     // Each lane stores exactly the chunks of the new token's rows that it
     // later loads with the last block (K: the lanes of column nt.row, chunks
@@ -900,11 +936,10 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
   const int32_t G = num_q_heads / num_kv_heads;
   if (G > 16) return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: group size %d > 16", G);
   const int32_t P = effective_partition(partition_size);
-  if (P < kTile || P > kMaxPartition || P % kTile != 0 || P % block_size != 0 ||
-      P / block_size > kMaxPartBlocks)
+  if (P < kTile || P > kMaxPartition || P % kTile != 0 || P % block_size != 0)
     return fail(KV_ERR_INVALID,
                 "kv_paged_attention_decode: partition_size %d (a multiple of 16 and of the block "
-                "size, at most 1024 tokens and 64 blocks)", partition_size);
+                "size, at most 1024 tokens)", partition_size);
   if (S == 0) return KV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(KV_ERR_INVALID, "kv_paged_attention_decode: null pointer");

@@ -101,7 +101,7 @@ extern "C" kv_status kv_paged_attention_prefill_plan(const int32_t* query_start_
 }
 
 // A partition size for a decode batch: the largest of 1024, 768 and 512
-// tokens (valid for the block size: at most 64 blocks per partition) whose
+// tokens (a multiple of the block size) whose
 // work units - KV heads times the partitions of every sequence - still
 // number at least min_units, else 512. Longer partitions mean fewer units to
 // start, fewer partial results and less merge work; min_units keeps enough
@@ -112,7 +112,7 @@ extern "C" int32_t kv_paged_attention_choose_partition(const int32_t* context_le
                                                        int32_t block_size, int32_t min_units) {
   if (S <= 0 || !context_lens_host || num_kv_heads <= 0 || block_size <= 0) return 512;
   for (const int32_t P : {1024, 768}) {
-    if (P % block_size != 0 || P / block_size > 64) continue;
+    if (P % block_size != 0) continue;
     int64_t units = 0;
     for (int32_t s = 0; s < S; ++s) {
       const int64_t ctx = context_lens_host[s];

@@ -82,12 +82,13 @@ def test_device_entry_points_validate_on_the_host(kv):
                                              a["dt"], a["P"], a["mc"], None, 0, a["ws"], a["wsb"], a["st"])
     assert call(B=12) == kv.KV_ERR_UNSUPPORTED
     assert call(B=32, P=48) == kv.KV_ERR_INVALID   # partition not a multiple of the block
-    assert call(B=8, P=1024) == kv.KV_ERR_INVALID  # more than 64 blocks per partition
+    assert call(B=8, P=24) == kv.KV_ERR_INVALID    # not a multiple of the 16-token tile
     assert call(D=96) == kv.KV_ERR_UNSUPPORTED
     assert call(Hq=7) == kv.KV_ERR_UNSUPPORTED
     assert call(Hq=64, Hkv=2) == kv.KV_ERR_UNSUPPORTED
     assert call(P=24) == kv.KV_ERR_INVALID
-    assert call(P=2048) == kv.KV_ERR_INVALID   # partitions hold at most 64 blocks
+    assert call(P=2048) == kv.KV_ERR_INVALID   # partitions hold at most 1024 tokens
+    assert call(B=8, P=1024, S=0) == kv.KV_OK  # 128 entries of 8-token blocks are accepted
     assert call(dt=7) == kv.KV_ERR_UNSUPPORTED
     assert call() == kv.KV_ERR_INVALID          # null pointers
     assert call(S=0) == kv.KV_OK                # nothing to do
@@ -385,7 +386,7 @@ def test_choose_partition(kv):
     assert kv.kv_paged_attention_choose_partition(lens, 8, 16, 1500) == 1024
     assert kv.kv_paged_attention_choose_partition(lens, 8, 16, 2049) == 768    # 2752 units
     assert kv.kv_paged_attention_choose_partition(lens, 8, 16, 2753) == 512
-    assert kv.kv_paged_attention_choose_partition(lens, 8, 8, 1500) == 512     # 96 blocks > 64
+    assert kv.kv_paged_attention_choose_partition(lens, 8, 8, 1500) == 1024    # 8-token blocks too
     assert kv.kv_paged_attention_choose_partition(lens, 8, 32, 1500) == 1024
     assert kv.kv_paged_attention_choose_partition([], 8, 16, 1500) == 512
     # a length of 0 still counts one unit (its output is written)

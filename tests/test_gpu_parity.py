@@ -391,7 +391,7 @@ def test_block_size_variants_against_oracle(B, dt, D, G):
     q, kp, vp, tab, cl = random_case(rng, lens, G * Hkv, Hkv, D, dt, B=B)
     scale = float(np.float32(1 / np.sqrt(D)))
     ref = oracle.decode_attention(q, kp, vp, tab, cl, scale, dt, block_size=B)
-    for ps, plan in ((0, True), (64, False), (256, True)):
+    for ps, plan in ((0, True), (64, False), (256, True), (1024, True), (768, False)):
         log(f"[gpu] decode B={B} {dt} D={D} G={G} partition={ps} plan={plan}")
         got = gpu_decode(q, kp, vp, tab, cl, scale, dt, ps, plan=plan)
         check_attention(got.reshape(-1, D), ref.reshape(-1, D), dt, f"B={B} {dt}/{D}/{G}/{ps}")
@@ -405,21 +405,25 @@ def test_block_size_variants_against_oracle(B, dt, D, G):
     rk, rv = kp.copy(), vp.copy()
     oa.reshape_and_cache(kn, vn, rk, rv, ref_slots, block_size=B)
     ref2 = oracle.decode_attention(q, rk, rv, tab, cl, scale, dt, block_size=B)
-    dk, dv = to_dev(kp, dt), to_dev(vp, dt)
-    out = torch.full((S, G * Hkv, D), float("nan"), dtype=torch.float32, device="cuda")
-    slots = torch.full((S,), 7, dtype=torch.int64, device="cuda")
     mc = int(cl.max())
-    wsb = kv.kv_paged_attention_workspace_bytes(S, G * Hkv, Hkv, D, mc, 0)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
-    items = torch.from_numpy(kv.kv_paged_attention_plan(cl, 0)).cuda()
-    log(f"[gpu] decode_append B={B} {dt} D={D} G={G}")
-    kv.kv_paged_attention_decode_append(out, to_dev(q, dt), to_dev(kn, dt), to_dev(vn, dt), dk, dv,
-                                        torch.from_numpy(tab).cuda(), torch.from_numpy(cl).cuda(),
-                                        scale, mc, slots, ws, 0, items)
-    torch.cuda.synchronize()
-    assert np.array_equal(slots.cpu().numpy(), ref_slots)
-    assert np.array_equal(bits(to_host(dk, dt)), bits(rk)) and np.array_equal(bits(to_host(dv, dt)), bits(rv))
-    check_attention(out.cpu().numpy().reshape(-1, D), ref2.reshape(-1, D), dt, f"append B={B}")
+    for ps in (0, 1024):  # 1024 tokens: the 700-token sequence's new row is entry 87 (B=8)
+        dk, dv = to_dev(kp, dt), to_dev(vp, dt)
+        out = torch.full((S, G * Hkv, D), float("nan"), dtype=torch.float32, device="cuda")
+        slots = torch.full((S,), 7, dtype=torch.int64, device="cuda")
+        wsb = kv.kv_paged_attention_workspace_bytes(S, G * Hkv, Hkv, D, mc, ps)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
+        items = torch.from_numpy(kv.kv_paged_attention_plan(cl, ps)).cuda()
+        log(f"[gpu] decode_append B={B} {dt} D={D} G={G} partition={ps}")
+        kv.kv_paged_attention_decode_append(out, to_dev(q, dt), to_dev(kn, dt), to_dev(vn, dt), dk,
+                                            dv, torch.from_numpy(tab).cuda(),
+                                            torch.from_numpy(cl).cuda(), scale, mc, slots, ws, ps,
+                                            items)
+        torch.cuda.synchronize()
+        assert np.array_equal(slots.cpu().numpy(), ref_slots)
+        assert np.array_equal(bits(to_host(dk, dt)), bits(rk))
+        assert np.array_equal(bits(to_host(dv, dt)), bits(rv))
+        check_attention(out.cpu().numpy().reshape(-1, D), ref2.reshape(-1, D), dt,
+                        f"append B={B} partition {ps}")
 
 
 def test_block_size_workload_llama70b_b32():
