@@ -388,6 +388,48 @@ kv_status kv_paged_attention_decode_append(
     int32_t max_context_len, const int32_t* work_items, int32_t n_items, void* workspace,
     size_t ws_bytes, int64_t* slots, hipStream_t stream);
 
+/* The decode step of kv_paged_attention_decode_append for a batch whose
+ * sequences all share their first shared_tokens positions ([1] "Memory
+ * sharing": the same physical blocks, reached through the same first
+ * shared_tokens / block_size table entries). Attention over the shared
+ * positions is computed once for all S queries - the shared blocks are read
+ * once, not once per sequence - with the chunked-prefill kernel (no causal
+ * mask: every query sees every shared position); attention over each
+ * sequence's own positions shared_tokens..t-1 runs in the decode kernels,
+ * with the new token written as in kv_paged_attention_decode_append; the
+ * two are combined with their softmax denominators into the attention over
+ * positions 0..t-1 (the same value as kv_paged_attention_decode_append, up
+ * to rounding order). Three launches (four when a tail spans several
+ * partitions).
+ *
+ * shared_tokens: > 0, a multiple of block_size; the shared blocks are read
+ *               through row 0 of block_tables. A sequence normally has
+ *               context_lens[s] >= shared_tokens + 1 (its tail holds at
+ *               least the new token); one of exactly shared_tokens gets the
+ *               attention over the shared positions and no write (slots[s]
+ *               = -1); a shorter one gets NaN.
+ * max_tail_len: host bound on context_lens[s] - shared_tokens; it sizes
+ *               the tail grid and the workspace (kv_paged_attention_
+ *               workspace_bytes with max_context_len = max_tail_len).
+ * work_items:   optional plan from kv_paged_attention_plan over the tail
+ *               lengths context_lens[s] - shared_tokens.
+ * aux:          device scratch of kv_paged_attention_shared_aux_bytes(S,
+ *               num_q_heads, head_dim) bytes, 16-byte aligned: the prefix's
+ *               outputs and both softmax denominators. Needs no
+ *               initialisation.
+ * dtype f16 or bf16, head_dim 128, group size at most 16 (the prefill
+ * kernel's limits: KV_ERR_UNSUPPORTED otherwise); other
+ * arguments and checks as for kv_paged_attention_decode_append. */
+size_t kv_paged_attention_shared_aux_bytes(int32_t S, int32_t num_q_heads, int32_t head_dim);
+kv_status kv_paged_attention_decode_append_shared(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t S,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
+    int32_t shared_tokens, int32_t max_tail_len, const int32_t* work_items, int32_t n_items,
+    void* workspace, size_t ws_bytes, float* aux, size_t aux_bytes, int64_t* slots,
+    hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * fp8 KV cache ([1], "How does this relate to quantization?": K and V stored
  * in 8 bits instead of 16 halve the bytes per element and compose with

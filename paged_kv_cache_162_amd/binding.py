@@ -90,6 +90,11 @@ _SIGS = {
     "kv_paged_attention_decode_append": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
                                                    i32, i32, i32, i32, f32, C.c_int, i32, i32,
                                                    vp, i32, vp, C.c_size_t, vp, vp]),
+    "kv_paged_attention_shared_aux_bytes": (C.c_size_t, [i32, i32, i32]),
+    "kv_paged_attention_decode_append_shared": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32,
+                                                          i32, i32, i32, i32, i32, f32, C.c_int,
+                                                          i32, i32, i32, vp, i32, vp, C.c_size_t,
+                                                          vp, C.c_size_t, vp, vp]),
     "kv_reshape_and_cache_fp8": (C.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, C.c_int,
                                            f32, f32, vp]),
     "kv_quantize_fp8": (C.c_int, [vp, vp, i64, C.c_int, f32, vp]),
@@ -463,6 +468,43 @@ def kv_paged_attention_decode_append(out, q, k_new, v_new, k_pool, v_pool, block
         0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
         _dev(slots, "slots", torch.int64), _stream(stream)),
         "kv_paged_attention_decode_append")
+
+
+def kv_paged_attention_shared_aux_bytes(S: int, num_q_heads: int, head_dim: int) -> int:
+    return int(lib.kv_paged_attention_shared_aux_bytes(S, num_q_heads, head_dim))
+
+
+def kv_paged_attention_decode_append_shared(out, q, k_new, v_new, k_pool, v_pool, block_tables,
+                                            context_lens, scale: float, shared_tokens: int,
+                                            max_tail_len: int, slots, aux, workspace=None,
+                                            partition_size: int = 0, work_items=None,
+                                            stream=None) -> None:
+    """kv_paged_attention_decode_append for sequences sharing their first shared_tokens
+    positions: attention over the shared positions computed once for all queries, the tails
+    per sequence; aux: device tensor of kv_paged_attention_shared_aux_bytes bytes; work_items
+    and workspace are for the tails (lengths context_lens - shared_tokens)."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_pool.shape
+    if D2 != D or tuple(out.shape) != (S, Hq, D) or block_tables.shape[0] != S \
+            or context_lens.numel() != S or q.dtype != k_pool.dtype or v_pool.shape != k_pool.shape \
+            or tuple(k_new.shape) != (S, Hkv, D) or k_new.shape != v_new.shape \
+            or k_new.dtype != k_pool.dtype or slots.numel() != S:
+        raise KVError(KV_ERR_INVALID, "kv_paged_attention_decode_append_shared",
+                      "shape/dtype mismatch")
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                         workspace.numel() * workspace.element_size())
+    _check(lib.kv_paged_attention_decode_append_shared(
+        _dev(out, "out", torch.float32), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, B, NB, float(scale),
+        dtype_code(q), partition_size, shared_tokens, max_tail_len,
+        None if work_items is None else _dev(work_items, "work_items", torch.int32),
+        0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
+        _dev(aux, "aux"), aux.numel() * aux.element_size(), _dev(slots, "slots", torch.int64),
+        _stream(stream)),
+        "kv_paged_attention_decode_append_shared")
 
 
 # ---------------------------------------------------------------------------

@@ -71,6 +71,14 @@ struct DecodeParams {
   void* k_pool_w;
   void* v_pool_w;
   int64_t* slots;
+  // Tail mode: the first skip_tokens positions of every sequence (whole
+  // blocks, shared by all of them) are left out - the kernel attends to
+  // positions [skip_tokens, lens[s]) and reads the tables from entry
+  // skip_tokens / block_size on; 0 otherwise.
+  int32_t skip_tokens;
+  // optional [S][Hq]: log2 of each output's softmax denominator (base-2
+  // units, the scores' running max included); -inf for an empty sequence
+  float* lse;
   int32_t max_blocks, S, Hq, Hkv, G, num_blocks, block_size, part_tokens, nparts, n_units;
   float scale_log2;  // scale * log2(e), times the K scale for an fp8 cache
   // fp8 cache: the per-pool scales (stored value = code value * scale)
@@ -113,7 +121,8 @@ __device__ __forceinline__ WorkItem unit_item(const DecodeParams& p, int u) {
 template <int D>
 __device__ __forceinline__ int unit_prologue(const DecodeParams& p, const WorkItem& w, int ctx,
                                              int lane) {
-  const bool bad = ctx < 0 || (int64_t)ctx > (int64_t)p.max_blocks * p.block_size ||
+  const bool bad = ctx < 0 ||
+                   (int64_t)ctx + p.skip_tokens > (int64_t)p.max_blocks * p.block_size ||
                    (int64_t)ctx > (int64_t)p.nparts * p.part_tokens;
   if (bad || ctx == 0) {
     if (w.part == 0) {
@@ -121,6 +130,8 @@ __device__ __forceinline__ int unit_prologue(const DecodeParams& p, const WorkIt
       float* dst = p.out + ((size_t)w.s * p.Hq + (size_t)w.h * p.G) * D;
       for (int i = lane; i < p.G * D; i += 64) dst[i] = v;
       if (p.slots && w.h == 0 && lane == 0) p.slots[w.s] = -1;  // no new token to place
+      if (p.lse && lane < p.G)
+        p.lse[(size_t)w.s * p.Hq + (size_t)w.h * p.G + lane] = bad ? __builtin_nanf("") : neg_inf();
     }
     return 0;
   }
@@ -251,6 +262,8 @@ __device__ __forceinline__ void store_result(const DecodeParams& p, const WorkIt
       if (bad) v = make_float4(nan, nan, nan, nan);
       *reinterpret_cast<float4*>(dst + i) = v;
     }
+    if (p.lse && write_ml)
+      p.lse[(size_t)w.s * p.Hq + (size_t)w.h * p.G + g] = bad ? nan : m + log2f(l);
   } else {
     const size_t grp = partial_group(p, w);
     float* dst = p.ws_o + (grp * p.G + g) * D + d0;
@@ -279,8 +292,8 @@ constexpr int kMergeThreads = 256;
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void splitk_merge_kernel(DecodeParams p) {
   const int s = blockIdx.x / p.Hkv, h = blockIdx.x % p.Hkv;
-  const int ctx = p.lens[s];
-  if (ctx <= 0 || (int64_t)ctx > (int64_t)p.max_blocks * p.block_size ||
+  const int ctx = p.lens[s] - p.skip_tokens;
+  if (ctx <= 0 || (int64_t)ctx + p.skip_tokens > (int64_t)p.max_blocks * p.block_size ||
       (int64_t)ctx > (int64_t)p.nparts * p.part_tokens)
     return;  // written by the decode kernel
   const int nps = (ctx + p.part_tokens - 1) / p.part_tokens;
@@ -315,6 +328,8 @@ __global__ __launch_bounds__(kMergeThreads) void splitk_merge_kernel(DecodeParam
     float4 r = make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
     if (bad) r = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                              __builtin_nanf(""));
+    if (p.lse && c % (D / 4) == 0)
+      p.lse[(size_t)s * p.Hq + (size_t)h * p.G + g] = bad ? __builtin_nanf("") : M + log2f(L);
     *reinterpret_cast<float4*>(p.out + ((size_t)s * p.Hq + (size_t)h * p.G) * D + (size_t)c * 4) = r;
   }
 }
@@ -342,16 +357,17 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   const int r = lane / LPR, c = lane % LPR;
   const WorkItem w = unit_item(p, u);
   if (!w.ok) return;
-  const int ctx = p.lens[w.s];
+  const int ctx = p.lens[w.s] - p.skip_tokens;
   const int nps = unit_prologue<D>(p, w, ctx, lane);
   if (nps == 0) return;
   const int t0 = w.part * p.part_tokens;
   const int t1 = min(ctx, t0 + p.part_tokens);
   const int nblk = (t1 - t0 + kTile - 1) / kTile;        // 16-token tiles
   const int nent = (t1 - t0 + BS - 1) / BS;              // table entries (blocks)
-  const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + t0 / BS;
+  const int e0 = (p.skip_tokens + t0) / BS;              // the partition's first entry
+  const int32_t* row = p.tables + (size_t)w.s * p.max_blocks + e0;
   bool bad = false;
-  const Entries staged = stage_entries<BS>(p, row, p.max_blocks - t0 / BS, nent, lane, bad);
+  const Entries staged = stage_entries<BS>(p, row, p.max_blocks - e0, nent, lane, bad);
   const NewToken nt = new_token<BS>(p, w, nps, ctx, t0, staged, bad, lane);
   if (nt.on && nt.slot >= 0 && r == nt.row % TPI) {
     // the lanes of row group nt.row % TPI load chunk c of the new token's
@@ -548,8 +564,8 @@ void decode_mfma_kernel(DecodeParams p) {
   // The loads that need only the unit go out together: the length, the
   // partition's table entries (bounded by the table width, so the length is
   // not needed yet) and the queries.
-  const int ctx = p.lens[w.s];
-  const int b0 = w.part * (p.part_tokens / BS);
+  const int ctx = p.lens[w.s] - p.skip_tokens;
+  const int b0 = (p.skip_tokens + w.part * p.part_tokens) / BS;  // the partition's first entry
   Entries raw_entry{0, 0};
   {
     constexpr int K = entries_per_lane<BS>();
@@ -795,6 +811,34 @@ void decode_mfma_kernel(DecodeParams p) {
   if (nps > 1 && writer && grp == 0)
     *reinterpret_cast<float2*>(p.ws_ml + (pg * p.G + hd) * 2) =
         bad ? make_float2(nan, nan) : make_float2(m, l);
+  if (p.lse && nps == 1 && writer && grp == 0)
+    p.lse[(size_t)w.s * p.Hq + (size_t)w.h * p.G + hd] = bad ? nan : m + log2f(l);
+}
+
+// Attention over a sequence's shared prefix and over its own tail, each
+// normalised with its own softmax denominator 2^lse, combined into the
+// attention over the whole context:
+//   out = (o_a 2^(lse_a - M) + o_b 2^(lse_b - M)) / (2^(lse_a - M) + 2^(lse_b - M)),
+// M = max(lse_a, lse_b); an empty tail has lse_b = -inf and weight 0. o_b is
+// read from and the result written to `out`. Thread t handles float4 t.
+__global__ __launch_bounds__(256) void combine_kernel(float* out, const float* o_a,
+                                                      const float* lse_a, const float* lse_b,
+                                                      int64_t n4, int D) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const int64_t row = i / (D / 4);  // (sequence, query head)
+  const float la = lse_a[row], lb = lse_b[row];
+  const float M = fmaxf(la, lb);
+  const float wa = fast_exp2(la - M), wb = fast_exp2(lb - M);
+  const float inv = 1.0f / (wa + wb);
+  const float4 a = reinterpret_cast<const float4*>(o_a)[i];
+  float4* po = reinterpret_cast<float4*>(out) + i;
+  const float4 b = *po;
+  float4 r = make_float4((a.x * wa + b.x * wb) * inv, (a.y * wa + b.y * wb) * inv,
+                         (a.z * wa + b.z * wb) * inv, (a.w * wa + b.w * wb) * inv);
+  if (la != la || lb != lb) r = make_float4(__builtin_nanf(""), __builtin_nanf(""),
+                                            __builtin_nanf(""), __builtin_nanf(""));
+  *po = r;
 }
 
 int32_t effective_partition(int32_t partition_size) {
@@ -907,7 +951,8 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
                       int32_t max_context_len, const int32_t* work_items, int32_t n_items,
                       void* workspace, size_t ws_bytes, const void* k_new, const void* v_new,
                       int64_t* slots, hipStream_t stream, bool kv8 = false,
-                      float k_scale = 1.0f, float v_scale = 1.0f) {
+                      float k_scale = 1.0f, float v_scale = 1.0f, int32_t skip_tokens = 0,
+                      float* lse = nullptr) {
   if (pagedkv::dtype_bytes(dtype) == 0)
     return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: unknown dtype");
   if (dtype == KV_FP8_E4M3)
@@ -958,7 +1003,7 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
   if (n_units > INT32_MAX)
     return fail(KV_ERR_INVALID, "kv_paged_attention_decode: too many work units");
 
-  DecodeParams prm;
+  DecodeParams prm = {};  // skip_tokens 0, no lse unless set below
   prm.out = out;
   prm.q = q;
   prm.k_pool = k_pool;
@@ -988,6 +1033,8 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
   prm.k_pool_w = const_cast<void*>(k_pool);
   prm.v_pool_w = const_cast<void*>(v_pool);
   prm.slots = slots;
+  prm.skip_tokens = skip_tokens;
+  prm.lse = lse;
 
   prm.block_size = block_size;
   const kv_status st = g_load_policy == KV_LOADS_CACHED
@@ -1038,6 +1085,62 @@ kv_status kv_paged_attention_decode_append(
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                      partition_size, max_context_len, work_items, n_items, workspace, ws_bytes,
                      k_new, v_new, slots, stream);
+}
+
+size_t kv_paged_attention_shared_aux_bytes(int32_t S, int32_t num_q_heads, int32_t head_dim) {
+  if (S < 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  // prefix outputs, then the prefix's and the tails' softmax denominators
+  return (size_t)S * num_q_heads * (head_dim + 2) * sizeof(float);
+}
+
+kv_status kv_paged_attention_decode_append_shared(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t S,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
+    int32_t shared_tokens, int32_t max_tail_len, const int32_t* work_items, int32_t n_items,
+    void* workspace, size_t ws_bytes, float* aux, size_t aux_bytes, int64_t* slots,
+    hipStream_t stream) {
+  pagedkv::clear_error();
+  const char* who = "kv_paged_attention_decode_append_shared";
+  if (dtype != KV_F16 && dtype != KV_BF16)
+    return fail(KV_ERR_UNSUPPORTED, "%s: dtype must be f16 or bf16", who);
+  if (head_dim != 128) return fail(KV_ERR_UNSUPPORTED, "%s: head_dim %d (128)", who, head_dim);
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(KV_ERR_UNSUPPORTED, "%s: block_size %d (8, 16 or 32)", who, block_size);
+  if (shared_tokens <= 0 || shared_tokens % block_size != 0 ||
+      shared_tokens / block_size > max_blocks)
+    return fail(KV_ERR_INVALID, "%s: shared_tokens %d (whole blocks within the table)", who,
+                shared_tokens);
+  if (num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 && num_q_heads / num_kv_heads > 16)
+    return fail(KV_ERR_UNSUPPORTED, "%s: group size %d > 16", who, num_q_heads / num_kv_heads);
+  if (S < 0) return fail(KV_ERR_INVALID, "%s: bad sizes", who);
+  if (S == 0) return KV_OK;
+  if (!k_new || !v_new || !slots || !aux)
+    return fail(KV_ERR_INVALID, "%s: null pointer", who);
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(aux))
+    return fail(KV_ERR_INVALID, "%s: k_new/v_new/aux must be 16-byte aligned", who);
+  if (num_q_heads > 0 && aux_bytes < kv_paged_attention_shared_aux_bytes(S, num_q_heads, head_dim))
+    return fail(KV_ERR_INVALID, "%s: aux of %zu bytes needed (got %zu)", who,
+                kv_paged_attention_shared_aux_bytes(S, num_q_heads, head_dim), aux_bytes);
+  float* o_a = aux;
+  float* lse_a = aux + (size_t)S * num_q_heads * head_dim;
+  float* lse_b = lse_a + (size_t)S * num_q_heads;
+  // the tails (checks every other argument), then the prefix, then the combination
+  kv_status st = decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
+                             num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                             dtype, partition_size, max_tail_len, work_items, n_items, workspace,
+                             ws_bytes, k_new, v_new, slots, stream, false, 1.0f, 1.0f,
+                             shared_tokens, lse_b);
+  if (st != KV_OK) return st;
+  st = pagedkv::shared_prefix_attention(o_a, lse_a, q, k_pool, v_pool, block_tables, max_blocks,
+                                        S, num_q_heads, num_kv_heads, block_size, num_blocks,
+                                        scale, dtype, shared_tokens, stream);
+  if (st != KV_OK) return st;
+  const int64_t n4 = (int64_t)S * num_q_heads * head_dim / 4;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                     out, o_a, lse_a, lse_b, n4, head_dim);
+  return launch_status(who);
 }
 
 kv_status kv_paged_attention_decode_fp8(float* out, const void* q, const void* k_pool,

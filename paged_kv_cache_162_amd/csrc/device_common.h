@@ -257,4 +257,18 @@ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace dev
 }  // namespace pagedkv
 
+namespace pagedkv {
+// Attention of S decode queries over the first shared_len positions of table
+// row 0, which every sequence of the call shares (the prefill kernel's
+// shared-prefix mode): normalised outputs to o [S][Hq][D], log2 of the
+// softmax denominators (base-2 units) to lse [S][Hq]. Defined with the
+// prefill kernel; the caller checks the arguments.
+kv_status shared_prefix_attention(float* o, float* lse, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* table_row0,
+                                  int32_t max_blocks, int32_t S, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t block_size, int32_t num_blocks,
+                                  float scale, kv_dtype dtype, int32_t shared_len,
+                                  hipStream_t stream);
+}  // namespace pagedkv
+
 #endif  // PAGEDKV_DEVICE_COMMON_H_

@@ -55,6 +55,11 @@ struct PrefillParams {
   int32_t T, S, Hq, Hkv, G, tpc, rows_per_block, max_blocks, num_blocks, n_units;
   float scale_log2;  // scale * log2(e), times the K scale for an fp8 cache
   float v_scale;     // fp8 cache: the V scale, applied to the output
+  // Shared-prefix mode (shared_len > 0): every query row (T of them) attends,
+  // without a causal mask, to the first shared_len positions of table row 0,
+  // which all the rows' sequences share; q_start, lens and items are unused.
+  int32_t shared_len;
+  float* lse;  // optional [T][Hq]: log2 of the softmax denominator, base-2 units
 };
 
 // Column tile of MFMA columns: query row of column c and whether it is live.
@@ -73,8 +78,13 @@ void prefill_mfma_kernel(PrefillParams p) {
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
 
+  const bool shared = p.shared_len > 0;
   int s, h, qblk;
-  if (p.items) {
+  if (shared) {
+    s = 0;
+    h = blockIdx.x % p.Hkv;
+    qblk = blockIdx.x / p.Hkv;
+  } else if (p.items) {
     const int it = blockIdx.x / p.Hkv;
     h = blockIdx.x % p.Hkv;
     s = p.items[2 * it];
@@ -85,15 +95,15 @@ void prefill_mfma_kernel(PrefillParams p) {
     qblk = blockIdx.x / (p.S * p.Hkv);
   }
   if (s < 0 || s >= p.S || qblk < 0) return;
-  const int r_begin = p.q_start[s], r_end = p.q_start[s + 1];
+  const int r_begin = shared ? 0 : p.q_start[s], r_end = shared ? p.T : p.q_start[s + 1];
   if (r_begin < 0 || r_end > p.T || r_end < r_begin) return;  // no row can be placed safely
   const int C = r_end - r_begin;
   const int row0 = qblk * p.rows_per_block;
   if (row0 >= C) return;
   const int rows = min(p.rows_per_block, C - row0);
-  const int L = p.lens[s];
+  const int L = shared ? p.shared_len : p.lens[s];
   const float nan = __builtin_nanf("");
-  if (L < C || (int64_t)L > (int64_t)p.max_blocks * BS) {
+  if ((!shared && L < C) || (int64_t)L > (int64_t)p.max_blocks * BS) {
     // impossible length: the block's rows get NaN
     for (int i = tid; i < rows * p.G * (D / 4); i += blockDim.x) {
       const int rr = i / (p.G * (D / 4)), rem = i % (p.G * (D / 4));
@@ -103,7 +113,7 @@ void prefill_mfma_kernel(PrefillParams p) {
     return;
   }
   const int prev = L - C;
-  const int nkeys = prev + row0 + rows;  // keys the block's last query sees
+  const int nkeys = shared ? L : prev + row0 + rows;  // keys the block's last query sees
   const int ntiles = (nkeys + kPfKeys - 1) / kPfKeys;
   const int last = ntiles - 1;
   const int nblk = (nkeys + BS - 1) / BS;  // table entries in use
@@ -118,7 +128,7 @@ void prefill_mfma_kernel(PrefillParams p) {
     ct[t].live = col < p.tpc * p.G && qr < row0 + rows;
     ct[t].qrow = qr;
     // a dead column sees every key (finite softmax of zero scores), never stored
-    ct[t].pos = ct[t].live ? prev + qr : nkeys - 1;
+    ct[t].pos = ct[t].live && !shared ? prev + qr : nkeys - 1;
     const uint4* qp = reinterpret_cast<const uint4*>(
         static_cast<const char*>(p.q) +
         (((size_t)r_begin + (ct[t].live ? qr : row0)) * p.Hq + (size_t)h * p.G +
@@ -210,7 +220,9 @@ void prefill_mfma_kernel(PrefillParams p) {
     m[t] = neg_inf();
     l[t] = 0.f;
   }
-  const int first_pos = prev + row0;  // smallest position among the block's queries
+  // smallest position among the block's queries (shared mode: every row
+  // sees all nkeys keys)
+  const int first_pos = shared ? nkeys - 1 : prev + row0;
 
   // One 32-key tile. The score MFMAs run per 16-key half (lane: keys 4g..4g+3
   // of each half); the value MFMA takes all 32 keys at once, its reduction
@@ -328,6 +340,8 @@ void prefill_mfma_kernel(PrefillParams p) {
   for (int t = 0; t < kPfColTiles; ++t) {
     const float lt = column_sum(l[t]);
     if (!ct[t].live) continue;
+    if (p.lse && grp == 0)
+      p.lse[((size_t)r_begin + ct[t].qrow) * p.Hq + (size_t)h * p.G + hd] = bad ? nan : m[t] + log2f(lt);
     const float inv = (KV8 ? p.v_scale : 1.0f) / lt;
     float* dst = p.out + (((size_t)r_begin + ct[t].qrow) * p.Hq + (size_t)h * p.G + hd) * D +
                  32 * grp;
@@ -393,7 +407,7 @@ kv_status prefill_impl(const char* who, float* out, const void* q, const void* k
   if (n_units > INT32_MAX) return fail(KV_ERR_INVALID, "%s: too many work units", who);
   if (n_units == 0) return KV_OK;
 
-  PrefillParams prm;
+  PrefillParams prm = {};  // shared_len 0, no lse: the chunked-prefill mode
   prm.out = out;
   prm.q = q;
   prm.k_pool = k_pool;
@@ -421,6 +435,47 @@ kv_status prefill_impl(const char* who, float* out, const void* q, const void* k
 }
 
 }  // namespace
+
+namespace pagedkv {
+
+// Attention of S query rows (one decode query per sequence) over the first
+// shared_len positions of table row 0, which every sequence shares: the
+// normalised outputs go to o [S][Hq][D], log2 of the softmax denominators
+// (base-2 units) to lse [S][Hq]. Arguments are checked by the caller.
+kv_status shared_prefix_attention(float* o, float* lse, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* table_row0,
+                                  int32_t max_blocks, int32_t S, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t block_size, int32_t num_blocks,
+                                  float scale, kv_dtype dtype, int32_t shared_len,
+                                  hipStream_t stream) {
+  const int32_t G = num_q_heads / num_kv_heads;
+  const int32_t rpb = rows_per_block(G);
+  PrefillParams prm = {};
+  prm.out = o;
+  prm.q = q;
+  prm.k_pool = k_pool;
+  prm.v_pool = v_pool;
+  prm.tables = table_row0;
+  prm.T = S;
+  prm.S = 1;
+  prm.Hq = num_q_heads;
+  prm.Hkv = num_kv_heads;
+  prm.G = G;
+  prm.tpc = 16 / G;
+  prm.rows_per_block = rpb;
+  prm.max_blocks = max_blocks;
+  prm.num_blocks = num_blocks;
+  prm.n_units = (int32_t)(ceil_div64(S, rpb) * num_kv_heads);
+  prm.scale_log2 = scale * 1.4426950408889634f;
+  prm.v_scale = 1.0f;
+  prm.shared_len = shared_len;
+  prm.lse = lse;
+  hipLaunchKernelGGL(pick_kernel<false>(dtype, block_size), dim3((unsigned)prm.n_units),
+                     dim3(kPfWaves * 64), 0, stream, prm);
+  return launch_status("kv_paged_attention_decode_append_shared (shared prefix)");
+}
+
+}  // namespace pagedkv
 
 extern "C" {
 

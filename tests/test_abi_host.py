@@ -115,6 +115,24 @@ def test_device_entry_points_validate_on_the_host(kv):
         assert fn(None, None, 1, None, 2, 0, 4096, None, None) == kv.KV_ERR_INVALID
 
 
+def test_shared_prefix_entry_validation(kv):
+    # prefix outputs [S][Hq][D], then two softmax denominators [S][Hq]
+    assert kv.kv_paged_attention_shared_aux_bytes(32, 32, 128) == 32 * 32 * 130 * 4
+    assert kv.kv_paged_attention_shared_aux_bytes(0, 32, 128) == 0
+    call = lambda shared, S=2, D=128, B=16, dt=kv.KV_BF16: \
+        kv.lib.kv_paged_attention_decode_append_shared(
+            None, None, None, None, None, None, None, 4, None, S, 8, 2, D, B, 8, 1.0, dt, 0,
+            shared, 16, None, 0, None, 0, None, 0, None, None)
+    assert call(24) == kv.KV_ERR_INVALID          # not whole blocks
+    assert call(0) == kv.KV_ERR_INVALID           # nothing shared
+    assert call(80) == kv.KV_ERR_INVALID          # more blocks than the table holds
+    assert call(32) == kv.KV_ERR_INVALID          # null pointers
+    assert call(32, S=0) == kv.KV_OK              # nothing to do
+    assert call(32, D=64) == kv.KV_ERR_UNSUPPORTED
+    assert call(32, B=64) == kv.KV_ERR_UNSUPPORTED
+    assert call(32, dt=kv.KV_F32) == kv.KV_ERR_UNSUPPORTED
+
+
 def test_workspace_size_formula(kv):
     assert kv.kv_paged_attention_workspace_bytes(8, 32, 8, 128, 512, 0) == 0
     # fp32 partials: outputs [S][Hkv][parts][G][D], then (max, sum) [S][Hkv][parts][G][2]
