@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--block-size", type=int, default=16, help="tokens per KV block (8, 16 or 32)")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas to rotate (0 = auto)")
     ap.add_argument("--no-plan", action="store_true", help="padded grid instead of the host work plan")
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="decode a common prefix per sequence instead of once per batch")
     ap.add_argument("--unfused", action="store_true",
                     help="separate slot-mapping/cache-write launch instead of the fused decode step")
     ap.add_argument("--graph", action="store_true",
@@ -74,6 +76,8 @@ CAL_BLOCK_BYTES = 32768     # bytes per block and pool (K and V each)
 
 DECODE_SOURCES = ("decode.hip", "device_common.h")
 PREFILL_SOURCES = ("prefill.hip", "device_common.h")
+# a shared-prefix decode step runs the prefill kernel too
+SHARED_DECODE_SOURCES = ("decode.hip", "prefill.hip", "device_common.h")
 
 
 def kernel_source_digest(sources=DECODE_SOURCES):
@@ -156,26 +160,33 @@ def _mean_counter(rows, kernel_substr, counter):
 def pmc_parse(fetch_dir, write_dir, out_path, workload, partition):
     """HBM bytes per decode call from FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the calibration
-    copy, whose true byte count is known."""
+    copy, whose true byte count is known. A shared-prefix decode call adds its
+    prefix attention (prefill kernel) and combine kernel."""
     cal_bytes = 2 * CAL_PAIRS * CAL_BLOCK_BYTES
     prefill = is_prefill(workload)
-    res = {"workload": workload, "partition_arg": partition,
-           "kernel_source_digest": kernel_source_digest(PREFILL_SOURCES if prefill else DECODE_SOURCES),
-           "calibration_bytes": cal_bytes}
+    res = {"workload": workload, "partition_arg": partition, "calibration_bytes": cal_bytes}
     total = 0.0
+    shared = False
     for tag, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = _counter_rows(d)
         cal, ncal = _mean_counter(rows, "copy_blocks_kernel", counter)
         dec, ndec = _mean_counter(rows, "prefill_mfma" if prefill else "decode_", counter)
         mrg, nmrg = _mean_counter(rows, "splitk_merge", counter)
+        pre, npre = (0.0, 0) if prefill else _mean_counter(rows, "prefill_mfma", counter)
+        cmb, ncmb = _mean_counter(rows, "combine_kernel", counter)
         if ncal == 0 or ndec == 0:
             raise SystemExit(f"{d}: calibration or decode dispatches missing")
+        shared = shared or npre > 0
         factor = cal_bytes / (cal * 1024.0)
-        per_call = (dec + (mrg if nmrg else 0.0)) * 1024.0 * factor
+        per_call = (dec + (mrg if nmrg else 0.0) + (pre if npre else 0.0)
+                    + (cmb if ncmb else 0.0)) * 1024.0 * factor
         res[tag] = {"counter": counter, "calibration_kib": cal, "factor": factor,
                     "decode_kib": dec, "merge_kib": mrg if nmrg else None,
+                    "prefix_kib": pre if npre else None, "combine_kib": cmb if ncmb else None,
                     "decode_dispatches": ndec, "bytes_per_call": per_call}
         total += per_call
+    res["kernel_source_digest"] = kernel_source_digest(
+        PREFILL_SOURCES if prefill else SHARED_DECODE_SOURCES if shared else DECODE_SOURCES)
     res["bytes_per_launch"] = total
     with open(out_path, "w") as fh:
         json.dump(res, fh, indent=1)
@@ -480,12 +491,14 @@ def main():
     kp, vp = to_dev(w.k_pool, sp.cache_dtype), to_dev(w.v_pool, sp.cache_dtype)
     sess = DecodeSession(k_pool=kp, v_pool=vp, num_q_heads=sp.Hq, free_order=w.free_order,
                          partition_size=args.partition, use_plan=not args.no_plan,
-                         fused=not args.unfused, k_scale=sp.k_scale, v_scale=sp.v_scale)
+                         fused=not args.unfused, k_scale=sp.k_scale, v_scale=sp.v_scale,
+                         shared_prefix=not args.no_shared_prefix)
     values = {}
     if w.tail_k is not None:
         values = {s: (to_dev(w.tail_k[s], dt), to_dev(w.tail_v[s], dt)) for s in range(sp.S)}
     sess.run_ops(w.setup_ops, values)
     sess.prepare_step(list(range(sp.S)))
+    shared = sess.shared_tokens
     memory = kv_memory(kv, sess, sp, w)
     lens = sess.host_lens
     q, kn, vn = to_dev(w.q, dt), to_dev(w.k_new, dt), to_dev(w.v_new, dt)
@@ -574,15 +587,23 @@ def main():
     copy_gbs = copy_bandwidth(kv, torch)
 
     kvb = kv_bytes(lens, sp.Hkv, sp.D, sp.kv_elem_bytes)
-    alg = decode_alg_bytes(lens, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes, args.block_size,
-                           sp.kv_elem_bytes)
+    if shared:
+        # the common prefix is read once for the batch, its table entries once
+        alg = (decode_alg_bytes(lens - shared, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes,
+                                args.block_size, sp.kv_elem_bytes)
+               + kv_bytes(np.array([shared]), sp.Hkv, sp.D, sp.kv_elem_bytes)
+               + shared // args.block_size * 4)
+    else:
+        alg = decode_alg_bytes(lens, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes, args.block_size,
+                               sp.kv_elem_bytes)
     value = kvb / (step_ms * 1e-3) / 1e9
     achieved = alg / (dec_avg * 1e-3) / 1e9
     traffic = None
     tpath = args.pmc_traffic or os.path.join(ROOT, "profiles", f"decode_traffic_w{args.workload}.json")
     if os.path.exists(tpath):
         t = json.load(open(tpath))
-        if t.get("kernel_source_digest") == kernel_source_digest() and \
+        sources = SHARED_DECODE_SOURCES if shared else DECODE_SOURCES
+        if t.get("kernel_source_digest") == kernel_source_digest(sources) and \
                 t.get("workload") == args.workload and args.partition == t.get("partition_arg"):
             traffic = round(float(t["bytes_per_launch"]))
 
@@ -607,7 +628,7 @@ def main():
             "sum_context": int(lens.sum()), "max_context": int(lens.max()),
             "kv_bytes_per_step": kvb, "replicas_rotated": R, "parallelism": "single GPU",
             "fused_cache_write": not args.unfused, "hip_graph": bool(args.graph),
-            "kv_cache_dtype": sp.cache_dtype,
+            "kv_cache_dtype": sp.cache_dtype, "shared_prefix_tokens": shared,
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(sp.S / (step_ms * 1e-3), 1),
@@ -622,10 +643,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": ("kv_paged_attention_decode_append%s call: decode kernel + split-K merge"
-                                if not args.unfused else
-                                "kv_paged_attention_decode%s call: decode kernel + split-K merge")
-                               % ("_fp8" if sp.kv_dtype else ""),
+                     "kernel": ("kv_paged_attention_decode_append_shared call: tail decode "
+                                "(+ split-K merge), prefix attention once, combine" if shared else
+                                ("kv_paged_attention_decode_append%s call: decode kernel + split-K merge"
+                                 if not args.unfused else
+                                 "kv_paged_attention_decode%s call: decode kernel + split-K merge")
+                                % ("_fp8" if sp.kv_dtype else "")),
                      "alg_bytes_per_launch": alg},
     }
     if not args.no_cpu_baseline:

@@ -394,13 +394,14 @@ kv_status kv_paged_attention_decode_append(
  * shared_tokens / block_size table entries). Attention over the shared
  * positions is computed once for all S queries - the shared blocks are read
  * once, not once per sequence - with the chunked-prefill kernel (no causal
- * mask: every query sees every shared position); attention over each
+ * mask: every query sees every shared position), the positions cut into
+ * ranges of at least 128 that run in parallel; attention over each
  * sequence's own positions shared_tokens..t-1 runs in the decode kernels,
  * with the new token written as in kv_paged_attention_decode_append; the
- * two are combined with their softmax denominators into the attention over
- * positions 0..t-1 (the same value as kv_paged_attention_decode_append, up
- * to rounding order). Three launches (four when a tail spans several
- * partitions).
+ * partial results are combined with their softmax denominators into the
+ * attention over positions 0..t-1 (the same value as
+ * kv_paged_attention_decode_append, up to rounding order). Three launches
+ * (four when a tail spans several partitions).
  *
  * shared_tokens: > 0, a multiple of block_size; the shared blocks are read
  *               through row 0 of block_tables. A sequence normally has
@@ -414,13 +415,16 @@ kv_status kv_paged_attention_decode_append(
  * work_items:   optional plan from kv_paged_attention_plan over the tail
  *               lengths context_lens[s] - shared_tokens.
  * aux:          device scratch of kv_paged_attention_shared_aux_bytes(S,
- *               num_q_heads, head_dim) bytes, 16-byte aligned: the prefix's
- *               outputs and both softmax denominators. Needs no
- *               initialisation.
+ *               num_q_heads, num_kv_heads, head_dim, shared_tokens) bytes,
+ *               16-byte aligned: each prefix range's outputs and softmax
+ *               denominators, and the tails' denominators. Needs no
+ *               initialisation; 0 from the size function means invalid
+ *               sizes.
  * dtype f16 or bf16, head_dim 128, group size at most 16 (the prefill
  * kernel's limits: KV_ERR_UNSUPPORTED otherwise); other
  * arguments and checks as for kv_paged_attention_decode_append. */
-size_t kv_paged_attention_shared_aux_bytes(int32_t S, int32_t num_q_heads, int32_t head_dim);
+size_t kv_paged_attention_shared_aux_bytes(int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t shared_tokens);
 kv_status kv_paged_attention_decode_append_shared(
     float* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
     const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t S,

@@ -90,7 +90,7 @@ _SIGS = {
     "kv_paged_attention_decode_append": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
                                                    i32, i32, i32, i32, f32, C.c_int, i32, i32,
                                                    vp, i32, vp, C.c_size_t, vp, vp]),
-    "kv_paged_attention_shared_aux_bytes": (C.c_size_t, [i32, i32, i32]),
+    "kv_paged_attention_shared_aux_bytes": (C.c_size_t, [i32, i32, i32, i32, i32]),
     "kv_paged_attention_decode_append_shared": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32,
                                                           i32, i32, i32, i32, i32, f32, C.c_int,
                                                           i32, i32, i32, vp, i32, vp, C.c_size_t,
@@ -470,8 +470,10 @@ def kv_paged_attention_decode_append(out, q, k_new, v_new, k_pool, v_pool, block
         "kv_paged_attention_decode_append")
 
 
-def kv_paged_attention_shared_aux_bytes(S: int, num_q_heads: int, head_dim: int) -> int:
-    return int(lib.kv_paged_attention_shared_aux_bytes(S, num_q_heads, head_dim))
+def kv_paged_attention_shared_aux_bytes(S: int, num_q_heads: int, num_kv_heads: int,
+                                        head_dim: int, shared_tokens: int) -> int:
+    return int(lib.kv_paged_attention_shared_aux_bytes(S, num_q_heads, num_kv_heads, head_dim,
+                                                       shared_tokens))
 
 
 def kv_paged_attention_decode_append_shared(out, q, k_new, v_new, k_pool, v_pool, block_tables,

@@ -815,29 +815,58 @@ void decode_mfma_kernel(DecodeParams p) {
     p.lse[(size_t)w.s * p.Hq + (size_t)w.h * p.G + hd] = bad ? nan : m + log2f(l);
 }
 
-// Attention over a sequence's shared prefix and over its own tail, each
-// normalised with its own softmax denominator 2^lse, combined into the
-// attention over the whole context:
-//   out = (o_a 2^(lse_a - M) + o_b 2^(lse_b - M)) / (2^(lse_a - M) + 2^(lse_b - M)),
-// M = max(lse_a, lse_b); an empty tail has lse_b = -inf and weight 0. o_b is
-// read from and the result written to `out`. Thread t handles float4 t.
+// Attention over the key ranges of a sequence's shared prefix and over its
+// own tail, each normalised with its own softmax denominator 2^lse, combined
+// into the attention over the whole context:
+//   out = sum_k o_k 2^(lse_k - M) / sum_k 2^(lse_k - M),  M = max_k lse_k,
+// k over the prefix ranges and the tail; an empty tail has lse = -inf and
+// weight 0. Range k's outputs are o_a + k*n4 float4s, its denominators
+// lse_a + k*rows; the tail's outputs are read from and the result written to
+// `out`. Thread t handles float4 t; every range's loads are issued before
+// any is used. A NaN denominator (an invalid sequence or table) makes the
+// row NaN.
 __global__ __launch_bounds__(256) void combine_kernel(float* out, const float* o_a,
                                                       const float* lse_a, const float* lse_b,
-                                                      int64_t n4, int D) {
+                                                      int64_t n4, int D, int parts) {
+  constexpr int K = pagedkv::kMaxSharedParts;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   const int64_t row = i / (D / 4);  // (sequence, query head)
-  const float la = lse_a[row], lb = lse_b[row];
-  const float M = fmaxf(la, lb);
-  const float wa = fast_exp2(la - M), wb = fast_exp2(lb - M);
-  const float inv = 1.0f / (wa + wb);
-  const float4 a = reinterpret_cast<const float4*>(o_a)[i];
+  const int64_t rows = n4 / (D / 4);
+  float la[K];
+  float4 a[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    la[k] = k < parts ? lse_a[k * rows + row] : neg_inf();
+    a[k] = k < parts ? reinterpret_cast<const float4*>(o_a)[k * n4 + i]
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float4* po = reinterpret_cast<float4*>(out) + i;
   const float4 b = *po;
-  float4 r = make_float4((a.x * wa + b.x * wb) * inv, (a.y * wa + b.y * wb) * inv,
-                         (a.z * wa + b.z * wb) * inv, (a.w * wa + b.w * wb) * inv);
-  if (la != la || lb != lb) r = make_float4(__builtin_nanf(""), __builtin_nanf(""),
-                                            __builtin_nanf(""), __builtin_nanf(""));
+  const float lb = lse_b[row];
+  float M = lb;
+  bool nan = lb != lb;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    nan = nan || la[k] != la[k];
+    M = fmaxf(M, la[k]);
+  }
+  const float wb = fast_exp2(lb - M);
+  float4 acc = make_float4(b.x * wb, b.y * wb, b.z * wb, b.w * wb);
+  float den = wb;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const float w = fast_exp2(la[k] - M);  // 0 for the unused ranges
+    acc.x += a[k].x * w;
+    acc.y += a[k].y * w;
+    acc.z += a[k].z * w;
+    acc.w += a[k].w * w;
+    den += w;
+  }
+  const float inv = 1.0f / den;
+  float4 r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (nan) r = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                           __builtin_nanf(""));
   *po = r;
 }
 
@@ -1087,10 +1116,14 @@ kv_status kv_paged_attention_decode_append(
                      k_new, v_new, slots, stream);
 }
 
-size_t kv_paged_attention_shared_aux_bytes(int32_t S, int32_t num_q_heads, int32_t head_dim) {
-  if (S < 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  // prefix outputs, then the prefix's and the tails' softmax denominators
-  return (size_t)S * num_q_heads * (head_dim + 2) * sizeof(float);
+size_t kv_paged_attention_shared_aux_bytes(int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t shared_tokens) {
+  int32_t part_keys = 0;
+  const int32_t parts =
+      pagedkv::shared_prefix_parts(S, num_q_heads, num_kv_heads, shared_tokens, &part_keys);
+  if (parts <= 0 || head_dim <= 0) return 0;
+  // per prefix range its outputs and denominators, then the tails' denominators
+  return ((size_t)parts * (head_dim + 1) + 1) * S * num_q_heads * sizeof(float);
 }
 
 kv_status kv_paged_attention_decode_append_shared(
@@ -1120,12 +1153,17 @@ kv_status kv_paged_attention_decode_append_shared(
     return fail(KV_ERR_INVALID, "%s: null pointer", who);
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(aux))
     return fail(KV_ERR_INVALID, "%s: k_new/v_new/aux must be 16-byte aligned", who);
-  if (num_q_heads > 0 && aux_bytes < kv_paged_attention_shared_aux_bytes(S, num_q_heads, head_dim))
-    return fail(KV_ERR_INVALID, "%s: aux of %zu bytes needed (got %zu)", who,
-                kv_paged_attention_shared_aux_bytes(S, num_q_heads, head_dim), aux_bytes);
+  int32_t part_keys = 0;
+  const int32_t parts =
+      pagedkv::shared_prefix_parts(S, num_q_heads, num_kv_heads, shared_tokens, &part_keys);
+  if (parts <= 0) return fail(KV_ERR_INVALID, "%s: bad head counts", who);
+  const size_t need =
+      kv_paged_attention_shared_aux_bytes(S, num_q_heads, num_kv_heads, head_dim, shared_tokens);
+  if (aux_bytes < need)
+    return fail(KV_ERR_INVALID, "%s: aux of %zu bytes needed (got %zu)", who, need, aux_bytes);
   float* o_a = aux;
-  float* lse_a = aux + (size_t)S * num_q_heads * head_dim;
-  float* lse_b = lse_a + (size_t)S * num_q_heads;
+  float* lse_a = aux + (size_t)parts * S * num_q_heads * head_dim;
+  float* lse_b = lse_a + (size_t)parts * S * num_q_heads;
   // the tails (checks every other argument), then the prefix, then the combination
   kv_status st = decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
@@ -1139,7 +1177,7 @@ kv_status kv_paged_attention_decode_append_shared(
   if (st != KV_OK) return st;
   const int64_t n4 = (int64_t)S * num_q_heads * head_dim / 4;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                     out, o_a, lse_a, lse_b, n4, head_dim);
+                     out, o_a, lse_a, lse_b, n4, head_dim, parts);
   return launch_status(who);
 }
 

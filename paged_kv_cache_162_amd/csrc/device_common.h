@@ -258,11 +258,20 @@ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace pagedkv
 
 namespace pagedkv {
+// At most this many key ranges of a shared prefix (the combining kernel holds
+// one value per range in registers).
+constexpr int kMaxSharedParts = 16;
+// Key ranges the shared-prefix attention cuts shared_len positions into:
+// returns their number (0 for invalid sizes) and sets *part_keys to the
+// positions per range (a multiple of 32).
+int32_t shared_prefix_parts(int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t shared_len, int32_t* part_keys);
 // Attention of S decode queries over the first shared_len positions of table
 // row 0, which every sequence of the call shares (the prefill kernel's
-// shared-prefix mode): normalised outputs to o [S][Hq][D], log2 of the
-// softmax denominators (base-2 units) to lse [S][Hq]. Defined with the
-// prefill kernel; the caller checks the arguments.
+// shared-prefix mode), one launch over the ranges of shared_prefix_parts:
+// range k's normalised outputs to o + k*S*Hq*D, log2 of its softmax
+// denominators (base-2 units) to lse + k*S*Hq. Defined with the prefill
+// kernel; the caller checks the arguments.
 kv_status shared_prefix_attention(float* o, float* lse, const void* q, const void* k_pool,
                                   const void* v_pool, const int32_t* table_row0,
                                   int32_t max_blocks, int32_t S, int32_t num_q_heads,

@@ -58,7 +58,10 @@ struct PrefillParams {
   // Shared-prefix mode (shared_len > 0): every query row (T of them) attends,
   // without a causal mask, to the first shared_len positions of table row 0,
   // which all the rows' sequences share; q_start, lens and items are unused.
-  int32_t shared_len;
+  // The positions are cut into key_parts ranges of part_keys (a multiple of
+  // the 32-key tile); range k's normalised outputs go to out + k*T*Hq*D and
+  // its denominators to lse + k*T*Hq.
+  int32_t shared_len, key_parts, part_keys;
   float* lse;  // optional [T][Hq]: log2 of the softmax denominator, base-2 units
 };
 
@@ -79,11 +82,13 @@ void prefill_mfma_kernel(PrefillParams p) {
   const int col = lane & 15, grp = lane >> 4;
 
   const bool shared = p.shared_len > 0;
-  int s, h, qblk;
+  int s, h, qblk, kpart = 0;
   if (shared) {
     s = 0;
     h = blockIdx.x % p.Hkv;
-    qblk = blockIdx.x / p.Hkv;
+    const int nq = (p.T + p.rows_per_block - 1) / p.rows_per_block;
+    qblk = (blockIdx.x / p.Hkv) % nq;
+    kpart = blockIdx.x / (p.Hkv * nq);
   } else if (p.items) {
     const int it = blockIdx.x / p.Hkv;
     h = blockIdx.x % p.Hkv;
@@ -101,13 +106,19 @@ void prefill_mfma_kernel(PrefillParams p) {
   const int row0 = qblk * p.rows_per_block;
   if (row0 >= C) return;
   const int rows = min(p.rows_per_block, C - row0);
-  const int L = shared ? p.shared_len : p.lens[s];
+  // keys [k_begin, L) of the sequence: all of them, or one range of the
+  // shared prefix
+  const int k_begin = kpart * p.part_keys;
+  const int L = shared ? min(p.shared_len, k_begin + p.part_keys) : p.lens[s];
+  if (k_begin >= L) return;
+  float* const out = shared ? p.out + (size_t)kpart * p.T * p.Hq * D : p.out;
+  float* const lse = p.lse && shared ? p.lse + (size_t)kpart * p.T * p.Hq : p.lse;
   const float nan = __builtin_nanf("");
   if ((!shared && L < C) || (int64_t)L > (int64_t)p.max_blocks * BS) {
     // impossible length: the block's rows get NaN
     for (int i = tid; i < rows * p.G * (D / 4); i += blockDim.x) {
       const int rr = i / (p.G * (D / 4)), rem = i % (p.G * (D / 4));
-      float* dst = p.out + ((size_t)(r_begin + row0 + rr) * p.Hq + (size_t)h * p.G) * D;
+      float* dst = out + ((size_t)(r_begin + row0 + rr) * p.Hq + (size_t)h * p.G) * D;
       reinterpret_cast<float4*>(dst)[rem] = make_float4(nan, nan, nan, nan);
     }
     return;
@@ -116,6 +127,7 @@ void prefill_mfma_kernel(PrefillParams p) {
   const int nkeys = shared ? L : prev + row0 + rows;  // keys the block's last query sees
   const int ntiles = (nkeys + kPfKeys - 1) / kPfKeys;
   const int last = ntiles - 1;
+  const int j0 = k_begin / kPfKeys;  // first tile (k_begin is a multiple of the tile)
   const int nblk = (nkeys + BS - 1) / BS;  // table entries in use
 
   // ---- columns and queries of this wave --------------------------------------
@@ -318,12 +330,12 @@ void prefill_mfma_kernel(PrefillParams p) {
   // stored into LDS buffer t % 2 and computed after a barrier; loads and
   // stores past the last tile repeat the last tile (in bounds, never computed)
   uint4 g0[4], g1[4];
-  load(0, g0);
-  store(0, g0, 0);
-  load(min(1, last), g1);
-  load(min(2, last), g0);
+  load(j0, g0);
+  store(j0, g0, 0);
+  load(min(j0 + 1, last), g1);
+  load(min(j0 + 2, last), g0);
   __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
+  for (int j = j0; j < ntiles; j += 2) {
     compute(j, 0);
     store(min(j + 1, last), g1, 1);
     load(min(j + 3, last), g1);
@@ -340,10 +352,10 @@ void prefill_mfma_kernel(PrefillParams p) {
   for (int t = 0; t < kPfColTiles; ++t) {
     const float lt = column_sum(l[t]);
     if (!ct[t].live) continue;
-    if (p.lse && grp == 0)
-      p.lse[((size_t)r_begin + ct[t].qrow) * p.Hq + (size_t)h * p.G + hd] = bad ? nan : m[t] + log2f(lt);
+    if (lse && grp == 0)
+      lse[((size_t)r_begin + ct[t].qrow) * p.Hq + (size_t)h * p.G + hd] = bad ? nan : m[t] + log2f(lt);
     const float inv = (KV8 ? p.v_scale : 1.0f) / lt;
-    float* dst = p.out + (((size_t)r_begin + ct[t].qrow) * p.Hq + (size_t)h * p.G + hd) * D +
+    float* dst = out + (((size_t)r_begin + ct[t].qrow) * p.Hq + (size_t)h * p.G + hd) * D +
                  32 * grp;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -438,10 +450,35 @@ kv_status prefill_impl(const char* who, float* out, const void* q, const void* k
 
 namespace pagedkv {
 
+#ifndef PAGEDKV_SHARED_MIN_TILES
+#define PAGEDKV_SHARED_MIN_TILES 4
+#endif
+
+// Key ranges of a shared prefix: enough workgroups to give each CU about two
+// (the kernel's occupancy), but no range under PAGEDKV_SHARED_MIN_TILES tiles,
+// since every range adds S*Hq*(D+1) floats of partial results to write and
+// merge; at most kMaxSharedParts ranges.
+int32_t shared_prefix_parts(int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t shared_len, int32_t* part_keys) {
+  *part_keys = 0;
+  if (S <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || shared_len <= 0)
+    return 0;
+  const int32_t G = num_q_heads / num_kv_heads;
+  if (G > 16) return 0;
+  const int64_t units = ceil_div64(S, rows_per_block(G)) * num_kv_heads;
+  const int64_t tiles = ceil_div64(shared_len, kPfKeys);
+  int64_t parts = std::min<int64_t>(ceil_div64(512, units), kMaxSharedParts);
+  parts = std::max<int64_t>(1, std::min<int64_t>(parts, tiles / PAGEDKV_SHARED_MIN_TILES));
+  const int64_t per = ceil_div64(tiles, parts);
+  *part_keys = (int32_t)(per * kPfKeys);
+  return (int32_t)ceil_div64(tiles, per);
+}
+
 // Attention of S query rows (one decode query per sequence) over the first
-// shared_len positions of table row 0, which every sequence shares: the
-// normalised outputs go to o [S][Hq][D], log2 of the softmax denominators
-// (base-2 units) to lse [S][Hq]. Arguments are checked by the caller.
+// shared_len positions of table row 0, which every sequence shares, cut into
+// the key ranges of shared_prefix_parts: range k's normalised outputs go to
+// o + k*S*Hq*D, log2 of its softmax denominators (base-2 units) to
+// lse + k*S*Hq. Arguments are checked by the caller.
 kv_status shared_prefix_attention(float* o, float* lse, const void* q, const void* k_pool,
                                   const void* v_pool, const int32_t* table_row0,
                                   int32_t max_blocks, int32_t S, int32_t num_q_heads,
@@ -450,6 +487,9 @@ kv_status shared_prefix_attention(float* o, float* lse, const void* q, const voi
                                   hipStream_t stream) {
   const int32_t G = num_q_heads / num_kv_heads;
   const int32_t rpb = rows_per_block(G);
+  int32_t part_keys = 0;
+  const int32_t parts = shared_prefix_parts(S, num_q_heads, num_kv_heads, shared_len, &part_keys);
+  if (parts <= 0) return fail(KV_ERR_INVALID, "shared prefix: bad sizes");
   PrefillParams prm = {};
   prm.out = o;
   prm.q = q;
@@ -465,10 +505,12 @@ kv_status shared_prefix_attention(float* o, float* lse, const void* q, const voi
   prm.rows_per_block = rpb;
   prm.max_blocks = max_blocks;
   prm.num_blocks = num_blocks;
-  prm.n_units = (int32_t)(ceil_div64(S, rpb) * num_kv_heads);
+  prm.n_units = (int32_t)(ceil_div64(S, rpb) * num_kv_heads * parts);
   prm.scale_log2 = scale * 1.4426950408889634f;
   prm.v_scale = 1.0f;
   prm.shared_len = shared_len;
+  prm.key_parts = parts;
+  prm.part_keys = part_keys;
   prm.lse = lse;
   hipLaunchKernelGGL(pick_kernel<false>(dtype, block_size), dim3((unsigned)prm.n_units),
                      dim3(kPfWaves * 64), 0, stream, prm);

@@ -26,11 +26,17 @@ from . import binding as kv
 # 2048 waves an MI355X runs at once (256 CUs x 8 waves), measured best.
 AUTO_PARTITION_MIN_UNITS = 1500
 
+# A decode step takes the shared-prefix entry point when every sequence of the
+# batch (at least this many) reaches at least this many positions through the
+# same leading blocks: below that the prefix is cheap to read per sequence.
+SHARED_PREFIX_MIN_SEQS = 4
+SHARED_PREFIX_MIN_TOKENS = 256
+
 
 class DecodeSession:
     def __init__(self, *, k_pool, v_pool, num_q_heads: int, free_order: Optional[Sequence[int]] = None,
                  partition_size: int = 0, use_plan: bool = True, fused: bool = True,
-                 k_scale: float = 1.0, v_scale: float = 1.0):
+                 k_scale: float = 1.0, v_scale: float = 1.0, shared_prefix: bool = True):
         import torch
         self.torch = torch
         NB, Hkv, B, D = k_pool.shape
@@ -45,6 +51,9 @@ class DecodeSession:
         self.min_units = AUTO_PARTITION_MIN_UNITS
         self.use_plan = use_plan
         self.fused = fused
+        # decode steps over a common prefix read it once (fused 16-bit steps only)
+        self.shared_prefix = shared_prefix
+        self.shared_tokens = 0
         self.pool = kv.kv_pool_create(NB, B, 1, Hkv, D, self.dtype)
         if free_order is not None:
             kv.kv_pool_set_free_order(self.pool, free_order)
@@ -213,8 +222,14 @@ class DecodeSession:
                 pairs.append(pair)
         tables, lens = self.tables(seqs)
         dev = self.device
+        S = len(seqs)
+        self.shared_tokens = self._common_prefix_tokens(tables, lens)
+        # the decode kernels see the tails of a shared-prefix step, else everything
+        dlens = lens - self.shared_tokens
+        # (short tails measured fastest with the same 512-token floor as
+        # whole sequences: smaller partitions add a merge launch)
         self.step_partition = self.partition_size or kv.kv_paged_attention_choose_partition(
-            lens, self.Hkv, self.B, self.min_units)
+            dlens, self.Hkv, self.B, self.min_units)
         self.seqs = list(seqs)
         self.d_tables = torch.from_numpy(tables).to(dev)
         self.d_lens = torch.from_numpy(lens).to(dev)
@@ -223,20 +238,44 @@ class DecodeSession:
         self.d_slots = torch.empty(len(seqs), dtype=torch.int64, device=dev)
         self.d_pairs = torch.tensor(pairs, dtype=torch.int32, device=dev).reshape(-1, 2)
         self.max_context_len = int(lens.max()) if len(lens) else 0
-        S = len(seqs)
+        self.max_decode_len = int(dlens.max()) if len(dlens) else 0
         ws = kv.kv_paged_attention_workspace_bytes(S, self.Hq, self.Hkv, self.D,
-                                                   self.max_context_len, self.step_partition)
+                                                   self.max_decode_len, self.step_partition)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev) if ws else None
+        self.aux = None
+        if self.shared_tokens:
+            aux = kv.kv_paged_attention_shared_aux_bytes(S, self.Hq, self.Hkv, self.D,
+                                                         self.shared_tokens)
+            self.aux = torch.empty(aux // 4, dtype=torch.float32, device=dev)
         self.host_tables, self.host_lens = tables, lens
         self.d_items = None
         if self.use_plan:
-            items = kv.kv_paged_attention_plan(lens, self.step_partition)
+            items = kv.kv_paged_attention_plan(dlens, self.step_partition)
             self.d_items = torch.from_numpy(items).to(dev)
-        # shared blocks are read by several sequences in the step: keep them
-        # in the caches; otherwise stream every block past them
-        self.load_policy = (kv.KV_LOADS_CACHED if kv.kv_pool_shared_blocks(self.pool) > 0
+        # blocks the decode kernels read for several sequences in the step
+        # stay in the caches; otherwise every block streams past them (the
+        # shared prefix of a shared-prefix step is read once, elsewhere)
+        common = self.shared_tokens // self.B
+        self.load_policy = (kv.KV_LOADS_CACHED if kv.kv_pool_shared_blocks(self.pool) > common
                             else kv.KV_LOADS_STREAM)
         return host_slots, pairs
+
+    def _common_prefix_tokens(self, tables, lens) -> int:
+        """Positions every sequence of the step reaches through the same
+        leading table entries (the same physical blocks), in whole blocks and
+        short of each sequence's last position; 0 when the shared-prefix step
+        does not apply (disabled, unfused, fp8, head_dim other than 128,
+        group above 16, too few sequences or too short a prefix)."""
+        S = len(lens)
+        if (not self.shared_prefix or not self.fused or self.fp8 or self.D != 128
+                or self.Hq // self.Hkv > 16 or S < SHARED_PREFIX_MIN_SEQS):
+            return 0
+        kmax = min(int(lens.min()) - 1, tables.shape[1] * self.B) // self.B
+        if kmax * self.B < SHARED_PREFIX_MIN_TOKENS:
+            return 0
+        same = np.all(tables[:, :kmax] == tables[:1, :kmax], axis=0)
+        k = kmax if same.all() else int(np.argmin(same))
+        return k * self.B if k * self.B >= SHARED_PREFIX_MIN_TOKENS else 0
 
     def write_step_tokens(self, k_new, v_new, k_pool=None, v_pool=None) -> None:
         """The unfused cache write of the step on its own: slot mapping of
@@ -255,13 +294,17 @@ class DecodeSession:
              decode_events=None, fused: Optional[bool] = None) -> None:
         """Device half of a decode step, all on the current stream:
         copy-on-write copies (if any), then either the fused decode (cache
-        write + attention, one launch plus the split-K merge) or, with
-        fused=False, slot mapping + cache write (one launch) followed by the
-        decode. `decode_events` = (start, end) torch events recorded around
+        write + attention, one launch plus the split-K merge; for a step over
+        a common prefix, the shared-prefix decode: tails, prefix once, and
+        their combination) or, with fused=False, slot mapping + cache write
+        (one launch) followed by the decode. `decode_events` = (start, end) torch events recorded around
         the call that runs attention."""
         kp = self.k_pool if k_pool is None else k_pool
         vp_ = self.v_pool if v_pool is None else v_pool
         fused = self.fused if fused is None else fused
+        if self.shared_tokens and not fused:
+            raise ValueError("this step was prepared for the shared-prefix decode, which fuses "
+                             "the cache write; create the session with shared_prefix=False")
         kv.kv_paged_attention_set_load_policy(self.load_policy)
         if self.d_pairs.shape[0]:
             kv.kv_copy_blocks([kp], [vp_], self.d_pairs, self.NB, self.block_bytes)
@@ -279,6 +322,11 @@ class DecodeSession:
                 kv.kv_paged_attention_decode_fp8(
                     out, q, kp, vp_, self.d_tables, self.d_lens, scale, self.k_scale, self.v_scale,
                     self.max_context_len, self.workspace, self.step_partition, self.d_items)
+        elif self.shared_tokens:
+            kv.kv_paged_attention_decode_append_shared(
+                out, q, k_new, v_new, kp, vp_, self.d_tables, self.d_lens, scale,
+                self.shared_tokens, self.max_decode_len, self.d_slots, self.aux, self.workspace,
+                self.step_partition, self.d_items)
         elif fused:
             kv.kv_paged_attention_decode_append(out, q, k_new, v_new, kp, vp_, self.d_tables,
                                                 self.d_lens, scale, self.max_context_len,

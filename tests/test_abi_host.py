@@ -116,9 +116,18 @@ def test_device_entry_points_validate_on_the_host(kv):
 
 
 def test_shared_prefix_entry_validation(kv):
-    # prefix outputs [S][Hq][D], then two softmax denominators [S][Hq]
-    assert kv.kv_paged_attention_shared_aux_bytes(32, 32, 128) == 32 * 32 * 130 * 4
-    assert kv.kv_paged_attention_shared_aux_bytes(0, 32, 128) == 0
+    # per prefix range outputs [S][Hq][D] and denominators [S][Hq], then the tails'
+    # denominators [S][Hq]. 32 sequences of group 4 fill one 32-row block per KV head:
+    # 8 blocks, so 64 ranges are wanted; at most 16, at least 4 tiles (128 positions) each
+    aux = kv.kv_paged_attention_shared_aux_bytes
+    assert aux(32, 32, 8, 128, 2048) == (16 * 129 + 1) * 32 * 32 * 4      # 16 ranges of 128
+    assert aux(32, 32, 8, 128, 8192) == (16 * 129 + 1) * 32 * 32 * 4      # 16 ranges of 512
+    assert aux(32, 32, 8, 128, 256) == (2 * 129 + 1) * 32 * 32 * 4        # 2 ranges of 128
+    assert aux(32, 32, 8, 128, 96) == (1 * 129 + 1) * 32 * 32 * 4         # one range
+    assert aux(512, 64, 8, 128, 65536) == (2 * 129 + 1) * 512 * 64 * 4    # 256 blocks already
+    assert aux(0, 32, 8, 128, 2048) == 0
+    assert aux(32, 32, 8, 128, 0) == 0
+    assert aux(32, 64, 2, 128, 2048) == 0                                # group 32
     call = lambda shared, S=2, D=128, B=16, dt=kv.KV_BF16: \
         kv.lib.kv_paged_attention_decode_append_shared(
             None, None, None, None, None, None, None, 4, None, S, 8, 2, D, B, 8, 1.0, dt, 0,

@@ -207,14 +207,16 @@ def test_workload_longctx_splitk_bf16():
 
 def test_workload_prefix_share_bf16():
     case = run_workload(5, n_sample=64)
-    # 128 shared prefix blocks with reference count 32
+    # 128 shared prefix blocks with reference count 32, read once by the shared-prefix step
     t0 = case.tables[0][:128]
     assert all((case.tables[s][:128] == t0).all() for s in range(case.sp.S))
+    assert case.sess.shared_tokens == 2048
 
 
 def test_workload_prefix_cow_bf16():
     case = run_workload(6, n_sample=64)
     assert len(case.setup_pairs) == 31
+    assert case.sess.shared_tokens == 2048   # the forked partial block is not common
 
 
 def test_truncated_workloads_full_output():
@@ -231,7 +233,7 @@ def test_fused_and_unfused_steps_are_bitwise_identical(cfg, S):
     res = {}
     for fused in (True, False):
         log(f"[gpu] workload {cfg} fused={fused}")
-        case.device_run(fused=fused)
+        case.device_run(fused=fused, shared_prefix=False)
         res[fused] = (case.out_dev.cpu().numpy(), to_host(case.k_dev, case.kdt),
                       to_host(case.v_dev, case.kdt), case.sess.d_slots.cpu().numpy())
     a, b = res[True], res[False]
@@ -683,7 +685,7 @@ def test_load_policies_give_identical_bits(cfg, S):
     res = {}
     for policy in (kv.KV_LOADS_STREAM, kv.KV_LOADS_CACHED):
         case = Case(cfg, S=S)
-        case.device_run()        # the session's own choice
+        case.device_run(shared_prefix=False)        # the session's own choice
         chosen = case.sess.load_policy
         assert chosen == (kv.KV_LOADS_CACHED if cfg == 5 else kv.KV_LOADS_STREAM)
         case.sess.load_policy = policy

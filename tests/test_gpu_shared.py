@@ -62,7 +62,8 @@ def test_shared_prefix_step_against_oracle(dt, G, B, P, plan):
     kv = kvlib()
     rng = np.random.default_rng(9000 + G + B + P + plan)
     D, Hkv, S = 128, 2, 37
-    shared_blocks = 640 // B
+    # 664 / 656 / 640 shared positions: 5 ranges of 128, the last one ragged for 8 and 16
+    shared_blocks = {8: 83, 16: 41, 32: 20}[B]
     tails = list(rng.integers(1, 300, S))
     tails[0], tails[1], tails[2] = 1, 2, 700       # new token only; tiny; several partitions
     q, kp, vp, tab, cl = shared_case(rng, S, shared_blocks, tails, G * Hkv, Hkv, D, dt, B)
@@ -81,7 +82,7 @@ def test_shared_prefix_step_against_oracle(dt, G, B, P, plan):
     mt = int(tail_lens.max())
     wsb = kv.kv_paged_attention_workspace_bytes(S, G * Hkv, Hkv, D, mt, P)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
-    aux = torch.full((kv.kv_paged_attention_shared_aux_bytes(S, G * Hkv, D) // 4,), float("nan"),
+    aux = torch.full((kv.kv_paged_attention_shared_aux_bytes(S, G * Hkv, Hkv, D, shared) // 4,), float("nan"),
                      dtype=torch.float32, device="cuda")
     items = torch.from_numpy(kv.kv_paged_attention_plan(tail_lens, P)).cuda() if plan else None
     dk, dv = to_dev(kp, dt), to_dev(vp, dt)
@@ -125,7 +126,7 @@ def test_shared_prefix_edge_lengths():
     mt = int(max(cl_run - shared))
     wsb = kv.kv_paged_attention_workspace_bytes(S, G * Hkv, Hkv, D, mt, 0)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
-    aux = torch.empty(kv.kv_paged_attention_shared_aux_bytes(S, G * Hkv, D) // 4,
+    aux = torch.empty(kv.kv_paged_attention_shared_aux_bytes(S, G * Hkv, Hkv, D, shared) // 4,
                       dtype=torch.float32, device="cuda")
     dk, dv = to_dev(kp, dt), to_dev(vp, dt)
     out = torch.full((S, G * Hkv, D), 3.0, dtype=torch.float32, device="cuda")
@@ -142,3 +143,29 @@ def test_shared_prefix_edge_lengths():
     check_attention(got[ok].reshape(-1, D), ref.reshape(-1, D), dt, "valid rows")
     check_attention(got[1].reshape(-1, D), ref1.reshape(-1, D), dt, "prefix only")
     assert np.array_equal(bits(to_host(dk, dt)), bits(rk))
+
+
+@pytest.mark.parametrize("cfg,B", [(5, 16), (6, 16), (5, 8), (5, 32)])
+def test_session_shared_step_matches_plain_step(cfg, B):
+    """The session's shared-prefix step and its plain fused step on the prefix-sharing
+    workloads: identical slots and pools, outputs within the attention tolerance of each other
+    and of the oracle."""
+    from gpu_common import Case
+    res = {}
+    for shared in (True, False):
+        case = Case(cfg, block_size=B)
+        log(f"[gpu] session workload {cfg} B={B} shared_prefix={shared}")
+        case.device_run(shared_prefix=shared)
+        assert (case.sess.shared_tokens > 0) == shared
+        res[shared] = (case.out_dev.cpu().numpy(), to_host(case.k_dev, case.kdt),
+                       to_host(case.v_dev, case.kdt), case.sess.d_slots.cpu().numpy())
+        case.sess.close()
+    a, b = res[True], res[False]
+    assert np.array_equal(a[3], b[3]) and np.array_equal(a[3], case.step_slots)
+    assert np.array_equal(bits(a[1]), bits(b[1])) and np.array_equal(bits(a[2]), bits(b[2]))
+    D = case.sp.D
+    check_attention(a[0].reshape(-1, D), b[0].reshape(-1, D), case.dt, "shared vs plain step")
+    pairs = [(s, h) for s in range(0, case.sp.S, 5) for h in (0, case.sp.Hq - 1)]
+    ref = case.oracle_out(pairs)
+    check_attention(np.stack([a[0][s, h] for s, h in pairs]),
+                    np.stack([ref[s, h] for s, h in pairs]), case.dt, "shared step vs oracle")
