@@ -169,3 +169,37 @@ def test_session_shared_step_matches_plain_step(cfg, B):
     ref = case.oracle_out(pairs)
     check_attention(np.stack([a[0][s, h] for s, h in pairs]),
                     np.stack([ref[s, h] for s, h in pairs]), case.dt, "shared step vs oracle")
+
+
+def test_shared_step_graph_replay_matches_eager():
+    """The session's shared-prefix step captured in a HIP graph (three launches, no memset
+    nodes): every replay, with the outputs, slots and scratch poisoned in between by eager work,
+    reproduces the eager step bit for bit."""
+    from gpu_common import Case
+    case = Case(5)
+    case.device_run()
+    sess = case.sess
+    assert sess.shared_tokens == 2048
+    eager = (case.out_dev.cpu().numpy().copy(), to_host(case.k_dev, case.kdt).copy(),
+             sess.d_slots.cpu().numpy().copy())
+    out = torch.full_like(case.out_dev, float("nan"))
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            sess.step(case.q_dev, case.kn_dev, case.vn_dev, out, case.sp.scale)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        sess.d_slots.fill_(-7)
+        sess.aux.fill_(float("nan"))
+        if sess.workspace is not None:
+            sess.workspace.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"[gpu] shared step graph replay {rep}")
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), eager[0].view(np.uint32))
+        assert np.array_equal(bits(to_host(case.k_dev, case.kdt)), bits(eager[1]))
+        assert np.array_equal(sess.d_slots.cpu().numpy(), eager[2])
+    sess.close()
