@@ -398,10 +398,12 @@ kv_status kv_paged_attention_decode_append(
  * ranges of at least 128 that run in parallel; attention over each
  * sequence's own positions shared_tokens..t-1 runs in the decode kernels,
  * with the new token written as in kv_paged_attention_decode_append; the
- * partial results are combined with their softmax denominators into the
- * attention over positions 0..t-1 (the same value as
- * kv_paged_attention_decode_append, up to rounding order). Three launches
- * (four when a tail spans several partitions).
+ * prefix pass runs first, and the kernel that writes each tail's output (the
+ * decode kernel, or the split-K merge for a tail spanning several
+ * partitions) combines it with the prefix ranges through their softmax
+ * denominators into the attention over positions 0..t-1 (the same value as
+ * kv_paged_attention_decode_append, up to rounding order). Two launches
+ * (three when a tail spans several partitions).
  *
  * shared_tokens: > 0, a multiple of block_size; the shared blocks are read
  *               through row 0 of block_tables. A sequence normally has
@@ -417,9 +419,8 @@ kv_status kv_paged_attention_decode_append(
  * aux:          device scratch of kv_paged_attention_shared_aux_bytes(S,
  *               num_q_heads, num_kv_heads, head_dim, shared_tokens) bytes,
  *               16-byte aligned: each prefix range's outputs and softmax
- *               denominators, and the tails' denominators. Needs no
- *               initialisation; 0 from the size function means invalid
- *               sizes.
+ *               denominators. Needs no initialisation; 0 from the size
+ *               function means invalid sizes.
  * dtype f16 or bf16, head_dim 128, group size at most 16 (the prefill
  * kernel's limits: KV_ERR_UNSUPPORTED otherwise); other
  * arguments and checks as for kv_paged_attention_decode_append. */

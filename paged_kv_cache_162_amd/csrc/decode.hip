@@ -76,9 +76,13 @@ struct DecodeParams {
   // positions [skip_tokens, lens[s]) and reads the tables from entry
   // skip_tokens / block_size on; 0 otherwise.
   int32_t skip_tokens;
-  // optional [S][Hq]: log2 of each output's softmax denominator (base-2
-  // units, the scores' running max included); -inf for an empty sequence
-  float* lse;
+  // Shared-prefix step: the prefix ranges' normalised outputs
+  // [pre_parts][S][Hq][D] and log2 of their softmax denominators
+  // [pre_parts][S][Hq], folded into each output by the kernel that writes it
+  // (pre_parts 0 otherwise).
+  const float* pre_o;
+  const float* pre_lse;
+  int32_t pre_parts;
   int32_t max_blocks, S, Hq, Hkv, G, num_blocks, block_size, part_tokens, nparts, n_units;
   float scale_log2;  // scale * log2(e), times the K scale for an fp8 cache
   // fp8 cache: the per-pool scales (stored value = code value * scale)
@@ -113,12 +117,58 @@ __device__ __forceinline__ WorkItem unit_item(const DecodeParams& p, int u) {
   return w;
 }
 
+// Shared-prefix step: the attention of output row `row` (sequence, query
+// head) over the sequence's tail - v, float4 c4 of the normalised output,
+// with lb = log2 of its softmax denominator, -inf for an empty tail - and
+// over the prefix ranges, combined into the attention over the whole
+// context:
+//   out = sum_k o_k 2^(lse_k - M) / sum_k 2^(lse_k - M),  M = max_k lse_k,
+// k over the ranges and the tail (softmax over a union of key sets). Every
+// range's loads are issued before any is used; a NaN denominator (invalid
+// sequence or table) gives NaN.
+__device__ __forceinline__ float4 with_prefix(const DecodeParams& p, size_t row, int c4, int d4,
+                                              float4 v, float lb) {
+  constexpr int K = pagedkv::kMaxSharedParts;
+  const size_t rows = (size_t)p.S * p.Hq;
+  const float4* po = reinterpret_cast<const float4*>(p.pre_o);
+  float la[K];
+  float4 a[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    la[k] = k < p.pre_parts ? p.pre_lse[k * rows + row] : neg_inf();
+    a[k] = k < p.pre_parts ? po[(k * rows + row) * d4 + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float M = lb;
+  bool nan = lb != lb;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    nan = nan || la[k] != la[k];
+    M = fmaxf(M, la[k]);
+  }
+  const float wb = fast_exp2(lb - M);  // 0 for an empty tail
+  float4 acc = make_float4(v.x * wb, v.y * wb, v.z * wb, v.w * wb);
+  float den = wb;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const float w = fast_exp2(la[k] - M);  // 0 for the unused ranges
+    acc.x += a[k].x * w;
+    acc.y += a[k].y * w;
+    acc.z += a[k].z * w;
+    acc.w += a[k].w * w;
+    den += w;
+  }
+  const float inv = 1.0f / den;
+  const float nanf = __builtin_nanf("");
+  return nan ? make_float4(nanf, nanf, nanf, nanf)
+             : make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
 // Sequence-level checks (one wave). Returns the number of partitions of the
 // sequence when this unit has tokens to process, else 0. The output of an
 // empty or invalid sequence is written here by its partition-0 unit: zeros,
 // or NaN for a length that is negative or exceeds the table or
 // max_context_len.
-template <int D>
+template <int D, bool PRE>
 __device__ __forceinline__ int unit_prologue(const DecodeParams& p, const WorkItem& w, int ctx,
                                              int lane) {
   const bool bad = ctx < 0 ||
@@ -127,11 +177,15 @@ __device__ __forceinline__ int unit_prologue(const DecodeParams& p, const WorkIt
   if (bad || ctx == 0) {
     if (w.part == 0) {
       const float v = bad ? __builtin_nanf("") : 0.0f;
-      float* dst = p.out + ((size_t)w.s * p.Hq + (size_t)w.h * p.G) * D;
-      for (int i = lane; i < p.G * D; i += 64) dst[i] = v;
+      const size_t row0 = (size_t)w.s * p.Hq + (size_t)w.h * p.G;
+      float4* dst = reinterpret_cast<float4*>(p.out + row0 * D);
+      for (int c = lane; c < p.G * (D / 4); c += 64) {
+        float4 r = make_float4(v, v, v, v);
+        // an empty tail: the prefix alone
+        if constexpr (PRE) r = with_prefix(p, row0 + c / (D / 4), c % (D / 4), D / 4, r, bad ? v : neg_inf());
+        dst[c] = r;
+      }
       if (p.slots && w.h == 0 && lane == 0) p.slots[w.s] = -1;  // no new token to place
-      if (p.lse && lane < p.G)
-        p.lse[(size_t)w.s * p.Hq + (size_t)w.h * p.G + lane] = bad ? __builtin_nanf("") : neg_inf();
     }
     return 0;
   }
@@ -250,20 +304,21 @@ __device__ __forceinline__ size_t partial_group(const DecodeParams& p, const Wor
 // d0: the final output o / l for a single-partition sequence, else the
 // partial o and, from the lane with write_ml, the pair (m, l). An invalid
 // unit stores NaN.
+template <bool PRE>
 __device__ __forceinline__ void store_result(const DecodeParams& p, const WorkItem& w, int nps,
                                              int g, int d0, const float* o, int n, float m,
                                              float l, bool write_ml, bool bad, int D) {
   const float nan = __builtin_nanf("");
   if (nps == 1) {
-    float* dst = p.out + ((size_t)w.s * p.Hq + (size_t)w.h * p.G + g) * D + d0;
+    const size_t row = (size_t)w.s * p.Hq + (size_t)w.h * p.G + g;
+    float* dst = p.out + row * D + d0;
     const float inv = 1.0f / l;
     for (int i = 0; i < n; i += 4) {
       float4 v = make_float4(o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv);
       if (bad) v = make_float4(nan, nan, nan, nan);
+      if constexpr (PRE) v = with_prefix(p, row, (d0 + i) / 4, D / 4, v, bad ? nan : m + log2f(l));
       *reinterpret_cast<float4*>(dst + i) = v;
     }
-    if (p.lse && write_ml)
-      p.lse[(size_t)w.s * p.Hq + (size_t)w.h * p.G + g] = bad ? nan : m + log2f(l);
   } else {
     const size_t grp = partial_group(p, w);
     float* dst = p.ws_o + (grp * p.G + g) * D + d0;
@@ -289,7 +344,7 @@ __device__ __forceinline__ void store_result(const DecodeParams& p, const WorkIt
 // ============================================================================
 constexpr int kMergeThreads = 256;
 
-template <int D>
+template <int D, bool PRE>
 __global__ __launch_bounds__(kMergeThreads) void splitk_merge_kernel(DecodeParams p) {
   const int s = blockIdx.x / p.Hkv, h = blockIdx.x % p.Hkv;
   const int ctx = p.lens[s] - p.skip_tokens;
@@ -328,8 +383,9 @@ __global__ __launch_bounds__(kMergeThreads) void splitk_merge_kernel(DecodeParam
     float4 r = make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
     if (bad) r = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                              __builtin_nanf(""));
-    if (p.lse && c % (D / 4) == 0)
-      p.lse[(size_t)s * p.Hq + (size_t)h * p.G + g] = bad ? __builtin_nanf("") : M + log2f(L);
+    if constexpr (PRE)
+      r = with_prefix(p, (size_t)s * p.Hq + (size_t)h * p.G + g, c % (D / 4), D / 4, r,
+                      bad ? __builtin_nanf("") : M + log2f(L));
     *reinterpret_cast<float4*>(p.out + ((size_t)s * p.Hq + (size_t)h * p.G) * D + (size_t)c * 4) = r;
   }
 }
@@ -342,7 +398,7 @@ __global__ __launch_bounds__(kMergeThreads) void splitk_merge_kernel(DecodeParam
 // reductions. Each group of LPR lanes keeps its own online softmax over the
 // tokens it reads; the groups are merged with cross-lane shuffles at the end.
 // ============================================================================
-template <int DT, int D, int GMAX, int BS, bool NT>
+template <int DT, int D, int GMAX, int BS, bool NT, bool PRE = false>
 __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   constexpr int EB = DT == KV_F32 ? 4 : 2;
   constexpr int EPL = 16 / EB;           // elements per lane chunk
@@ -358,7 +414,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   const WorkItem w = unit_item(p, u);
   if (!w.ok) return;
   const int ctx = p.lens[w.s] - p.skip_tokens;
-  const int nps = unit_prologue<D>(p, w, ctx, lane);
+  const int nps = unit_prologue<D, PRE>(p, w, ctx, lane);
   if (nps == 0) return;
   const int t0 = w.part * p.part_tokens;
   const int t1 = min(ctx, t0 + p.part_tokens);
@@ -516,7 +572,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
 #pragma unroll
     for (int g = 0; g < GMAX; ++g)
       if (g < p.G)
-        store_result(p, w, nps, g, c * EPL, acc[g], EPL, m[g], l[g], c == 0, bad, D);
+        store_result<PRE>(p, w, nps, g, c * EPL, acc[g], EPL, m[g], l[g], c == 0, bad, D);
   }
 }
 
@@ -549,7 +605,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
 // (base-2 units), so most blocks skip the cross-lane max and the rescale of
 // the accumulators; weights stay below 2^kRescaleSlack, far from overflow.
 // ============================================================================
-template <int DT, bool SPLITCOL, int RING, int BS, bool KV8, bool NT>
+template <int DT, bool SPLITCOL, int RING, int BS, bool KV8, bool NT, bool PRE = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_mfma_kernel(DecodeParams p) {
   constexpr int D = 128;
@@ -608,7 +664,7 @@ void decode_mfma_kernel(DecodeParams p) {
     }
     vnew = (static_cast<const uint4*>(p.v_new) + ((size_t)w.s * p.Hkv + w.h) * (D / 8))[col];
   }
-  const int nps = unit_prologue<D>(p, w, ctx, lane);
+  const int nps = unit_prologue<D, PRE>(p, w, ctx, lane);
   if (nps == 0) return;
   const int t0 = w.part * p.part_tokens;
   const int t1 = min(ctx, t0 + p.part_tokens);
@@ -784,8 +840,11 @@ void decode_mfma_kernel(DecodeParams p) {
   // 1 KB spans: in the accumulator layout neighbouring lanes hold different
   // heads, 512 bytes apart in memory.
   __shared__ float stage[16 * kStageStride];
+  __shared__ float stage_lse[16];  // shared-prefix step: log2 denominators per head
   const bool writer = SPLITCOL ? (col < 8 && live_head) : live_head;
   if (writer) {
+    if constexpr (PRE)
+      if (nps == 1 && grp == 0) stage_lse[hd] = m + log2f(l);
     // lane holds head hd, dims 32*grp + 8*r + n for r < 4, n < 8; an fp8
     // cache's V scale multiplies the (partial) output
     float inv = nps == 1 ? 1.0f / l : 1.0f;
@@ -803,71 +862,19 @@ void decode_mfma_kernel(DecodeParams p) {
   float* dst = nps == 1 ? p.out + ((size_t)w.s * p.Hq + (size_t)w.h * p.G) * D
                         : p.ws_o + pg * p.G * D;
   const float nan = __builtin_nanf("");
+  const size_t row0 = (size_t)w.s * p.Hq + (size_t)w.h * p.G;
   for (int c = lane; c < p.G * (D / 4); c += 64) {
     float4 v = *reinterpret_cast<const float4*>(&stage[(c >> 5) * kStageStride + 4 * (c & 31)]);
     if (bad && nps == 1) v = make_float4(nan, nan, nan, nan);
+    if constexpr (PRE)
+      if (nps == 1)
+        v = with_prefix(p, row0 + c / (D / 4), c % (D / 4), D / 4, v,
+                        bad ? nan : stage_lse[c / (D / 4)]);
     *reinterpret_cast<float4*>(dst + (size_t)c * 4) = v;
   }
   if (nps > 1 && writer && grp == 0)
     *reinterpret_cast<float2*>(p.ws_ml + (pg * p.G + hd) * 2) =
         bad ? make_float2(nan, nan) : make_float2(m, l);
-  if (p.lse && nps == 1 && writer && grp == 0)
-    p.lse[(size_t)w.s * p.Hq + (size_t)w.h * p.G + hd] = bad ? nan : m + log2f(l);
-}
-
-// Attention over the key ranges of a sequence's shared prefix and over its
-// own tail, each normalised with its own softmax denominator 2^lse, combined
-// into the attention over the whole context:
-//   out = sum_k o_k 2^(lse_k - M) / sum_k 2^(lse_k - M),  M = max_k lse_k,
-// k over the prefix ranges and the tail; an empty tail has lse = -inf and
-// weight 0. Range k's outputs are o_a + k*n4 float4s, its denominators
-// lse_a + k*rows; the tail's outputs are read from and the result written to
-// `out`. Thread t handles float4 t; every range's loads are issued before
-// any is used. A NaN denominator (an invalid sequence or table) makes the
-// row NaN.
-__global__ __launch_bounds__(256) void combine_kernel(float* out, const float* o_a,
-                                                      const float* lse_a, const float* lse_b,
-                                                      int64_t n4, int D, int parts) {
-  constexpr int K = pagedkv::kMaxSharedParts;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  const int64_t row = i / (D / 4);  // (sequence, query head)
-  const int64_t rows = n4 / (D / 4);
-  float la[K];
-  float4 a[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    la[k] = k < parts ? lse_a[k * rows + row] : neg_inf();
-    a[k] = k < parts ? reinterpret_cast<const float4*>(o_a)[k * n4 + i]
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  float4* po = reinterpret_cast<float4*>(out) + i;
-  const float4 b = *po;
-  const float lb = lse_b[row];
-  float M = lb;
-  bool nan = lb != lb;
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    nan = nan || la[k] != la[k];
-    M = fmaxf(M, la[k]);
-  }
-  const float wb = fast_exp2(lb - M);
-  float4 acc = make_float4(b.x * wb, b.y * wb, b.z * wb, b.w * wb);
-  float den = wb;
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const float w = fast_exp2(la[k] - M);  // 0 for the unused ranges
-    acc.x += a[k].x * w;
-    acc.y += a[k].y * w;
-    acc.z += a[k].z * w;
-    acc.w += a[k].w * w;
-    den += w;
-  }
-  const float inv = 1.0f / den;
-  float4 r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  if (nan) r = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
-                           __builtin_nanf(""));
-  *po = r;
 }
 
 int32_t effective_partition(int32_t partition_size) {
@@ -899,6 +906,21 @@ template <int BS, bool NT>
 kv_status launch_decode_kernel(const DecodeParams& prm, kv_dtype dtype, int head_dim, int G,
                                hipStream_t st) {
   constexpr int R = kDecodeRing;
+  if (prm.pre_parts) {
+    // the shared-prefix step's tails (16-bit, head_dim 128): the variants that
+    // fold the prefix ranges into the outputs
+    if (G == 1)
+      return dtype == KV_BF16
+                 ? launch_decode(decode_valu_kernel<KV_BF16, 128, 1, BS, NT, true>, prm, st)
+                 : launch_decode(decode_valu_kernel<KV_F16, 128, 1, BS, NT, true>, prm, st);
+    if (G <= 8)
+      return dtype == KV_BF16
+                 ? launch_decode(decode_mfma_kernel<KV_BF16, true, R, BS, false, NT, true>, prm, st)
+                 : launch_decode(decode_mfma_kernel<KV_F16, true, R, BS, false, NT, true>, prm, st);
+    return dtype == KV_BF16
+               ? launch_decode(decode_mfma_kernel<KV_BF16, false, R, BS, false, NT, true>, prm, st)
+               : launch_decode(decode_mfma_kernel<KV_F16, false, R, BS, false, NT, true>, prm, st);
+  }
   if ((dtype == KV_F16 || dtype == KV_BF16) && head_dim == 128 && G >= 2) {
     if (G <= 8)
       return dtype == KV_BF16
@@ -972,6 +994,16 @@ namespace {
 
 // Shared body of the decode entry points; k_new/v_new/slots are NULL for a
 // plain decode and set for the fused cache write.
+// The shared-prefix step's prefix pass ([1] "Memory sharing": positions every
+// sequence reaches through the same blocks): attention of all S queries over
+// the first `tokens` positions, in `parts` key ranges (outputs o, log2
+// denominators lse); the decode kernels then cover each sequence's tail.
+struct SharedPrefix {
+  int32_t tokens, parts;
+  float* o;
+  float* lse;
+};
+
 kv_status decode_impl(float* out, const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* block_tables, int32_t max_blocks,
                       const int32_t* context_lens, int32_t S, int32_t num_q_heads,
@@ -980,8 +1012,8 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
                       int32_t max_context_len, const int32_t* work_items, int32_t n_items,
                       void* workspace, size_t ws_bytes, const void* k_new, const void* v_new,
                       int64_t* slots, hipStream_t stream, bool kv8 = false,
-                      float k_scale = 1.0f, float v_scale = 1.0f, int32_t skip_tokens = 0,
-                      float* lse = nullptr) {
+                      float k_scale = 1.0f, float v_scale = 1.0f,
+                      const SharedPrefix* pre = nullptr) {
   if (pagedkv::dtype_bytes(dtype) == 0)
     return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: unknown dtype");
   if (dtype == KV_FP8_E4M3)
@@ -1032,7 +1064,7 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
   if (n_units > INT32_MAX)
     return fail(KV_ERR_INVALID, "kv_paged_attention_decode: too many work units");
 
-  DecodeParams prm = {};  // skip_tokens 0, no lse unless set below
+  DecodeParams prm = {};  // skip_tokens 0, no prefix unless set below
   prm.out = out;
   prm.q = q;
   prm.k_pool = k_pool;
@@ -1062,19 +1094,29 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
   prm.k_pool_w = const_cast<void*>(k_pool);
   prm.v_pool_w = const_cast<void*>(v_pool);
   prm.slots = slots;
-  prm.skip_tokens = skip_tokens;
-  prm.lse = lse;
-
   prm.block_size = block_size;
+  if (pre) {
+    // the prefix pass first: the decode kernels fold its results into the outputs
+    const kv_status ps = pagedkv::shared_prefix_attention(
+        pre->o, pre->lse, q, k_pool, v_pool, block_tables, max_blocks, S, num_q_heads,
+        num_kv_heads, block_size, num_blocks, scale, dtype, pre->tokens, stream);
+    if (ps != KV_OK) return ps;
+    prm.skip_tokens = pre->tokens;
+    prm.pre_o = pre->o;
+    prm.pre_lse = pre->lse;
+    prm.pre_parts = pre->parts;
+  }
   const kv_status st = g_load_policy == KV_LOADS_CACHED
                            ? launch_for_block_size<false>(prm, dtype, head_dim, G, kv8, stream)
                            : launch_for_block_size<true>(prm, dtype, head_dim, G, kv8, stream);
   if (st != KV_OK || nparts <= 1) return st;
   const dim3 mgrid((unsigned)((int64_t)S * num_kv_heads));
-  if (head_dim == 128)
-    hipLaunchKernelGGL(splitk_merge_kernel<128>, mgrid, dim3(kMergeThreads), 0, stream, prm);
+  if (pre)
+    hipLaunchKernelGGL((splitk_merge_kernel<128, true>), mgrid, dim3(kMergeThreads), 0, stream, prm);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((splitk_merge_kernel<128, false>), mgrid, dim3(kMergeThreads), 0, stream, prm);
   else
-    hipLaunchKernelGGL(splitk_merge_kernel<64>, mgrid, dim3(kMergeThreads), 0, stream, prm);
+    hipLaunchKernelGGL((splitk_merge_kernel<64, false>), mgrid, dim3(kMergeThreads), 0, stream, prm);
   return launch_status("kv_paged_attention_decode (split-K merge)");
 }
 
@@ -1122,8 +1164,8 @@ size_t kv_paged_attention_shared_aux_bytes(int32_t S, int32_t num_q_heads, int32
   const int32_t parts =
       pagedkv::shared_prefix_parts(S, num_q_heads, num_kv_heads, shared_tokens, &part_keys);
   if (parts <= 0 || head_dim <= 0) return 0;
-  // per prefix range its outputs and denominators, then the tails' denominators
-  return ((size_t)parts * (head_dim + 1) + 1) * S * num_q_heads * sizeof(float);
+  // per prefix range its outputs, then per range its denominators
+  return (size_t)parts * (head_dim + 1) * S * num_q_heads * sizeof(float);
 }
 
 kv_status kv_paged_attention_decode_append_shared(
@@ -1161,24 +1203,13 @@ kv_status kv_paged_attention_decode_append_shared(
       kv_paged_attention_shared_aux_bytes(S, num_q_heads, num_kv_heads, head_dim, shared_tokens);
   if (aux_bytes < need)
     return fail(KV_ERR_INVALID, "%s: aux of %zu bytes needed (got %zu)", who, need, aux_bytes);
-  float* o_a = aux;
-  float* lse_a = aux + (size_t)parts * S * num_q_heads * head_dim;
-  float* lse_b = lse_a + (size_t)parts * S * num_q_heads;
-  // the tails (checks every other argument), then the prefix, then the combination
-  kv_status st = decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
-                             num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
-                             dtype, partition_size, max_tail_len, work_items, n_items, workspace,
-                             ws_bytes, k_new, v_new, slots, stream, false, 1.0f, 1.0f,
-                             shared_tokens, lse_b);
-  if (st != KV_OK) return st;
-  st = pagedkv::shared_prefix_attention(o_a, lse_a, q, k_pool, v_pool, block_tables, max_blocks,
-                                        S, num_q_heads, num_kv_heads, block_size, num_blocks,
-                                        scale, dtype, shared_tokens, stream);
-  if (st != KV_OK) return st;
-  const int64_t n4 = (int64_t)S * num_q_heads * head_dim / 4;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                     out, o_a, lse_a, lse_b, n4, head_dim, parts);
-  return launch_status(who);
+  const SharedPrefix pre = {shared_tokens, parts, aux,
+                            aux + (size_t)parts * S * num_q_heads * head_dim};
+  // checks every other argument, then the prefix pass, then the tails
+  return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     partition_size, max_tail_len, work_items, n_items, workspace, ws_bytes, k_new,
+                     v_new, slots, stream, false, 1.0f, 1.0f, &pre);
 }
 
 kv_status kv_paged_attention_decode_fp8(float* out, const void* q, const void* k_pool,

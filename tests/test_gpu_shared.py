@@ -53,8 +53,11 @@ def shared_case(rng, S, shared_blocks, tails, Hq, Hkv, D, dt, B=16):
     return q, kp, vp, tab, np.array(lens, np.int32)
 
 
+# (dtype, group, block size, partition, plan): group 1 takes the vector-ALU decode kernel, the
+# others the MFMA kernel; a partition below the 700-token tail makes the merge kernel combine
 CASES = [("bf16", 8, 16, 0, True), ("bf16", 8, 16, 256, False), ("f16", 4, 16, 128, True),
-         ("bf16", 16, 16, 0, True), ("bf16", 8, 8, 0, True), ("bf16", 4, 32, 64, True)]
+         ("bf16", 16, 16, 0, True), ("bf16", 8, 8, 0, True), ("bf16", 4, 32, 64, True),
+         ("bf16", 1, 16, 0, True), ("f16", 1, 8, 128, False), ("f16", 2, 16, 0, False)]
 
 
 @pytest.mark.parametrize("dt,G,B,P,plan", CASES)
