@@ -13,6 +13,13 @@ Operation scripts are lists of tuples: ("create", s), ("fork", parent, child),
 
 Pools of dtype uint8 are an fp8 (E4M3) cache: every write quantises with the
 session's k_scale / v_scale and attention goes through the _fp8 entry points.
+
+When every sequence of a decode step reaches its first positions through the
+same blocks (a shared prefix: "PagedAttention - how vLLM stopped wasting 80% of
+your GPU memory", "Memory sharing"), the step
+goes through kv_paged_attention_decode_append_shared, which reads those blocks
+once for the batch instead of once per sequence (shared_prefix=False turns
+this off).
 """
 from __future__ import annotations
 
