@@ -161,7 +161,7 @@ def pmc_parse(fetch_dir, write_dir, out_path, workload, partition):
     """HBM bytes per decode call from FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the calibration
     copy, whose true byte count is known. A shared-prefix decode call adds its
-    prefix attention (prefill kernel) and combine kernel."""
+    prefix attention (prefill kernel)."""
     cal_bytes = 2 * CAL_PAIRS * CAL_BLOCK_BYTES
     prefill = is_prefill(workload)
     res = {"workload": workload, "partition_arg": partition, "calibration_bytes": cal_bytes}
@@ -173,16 +173,14 @@ def pmc_parse(fetch_dir, write_dir, out_path, workload, partition):
         dec, ndec = _mean_counter(rows, "prefill_mfma" if prefill else "decode_", counter)
         mrg, nmrg = _mean_counter(rows, "splitk_merge", counter)
         pre, npre = (0.0, 0) if prefill else _mean_counter(rows, "prefill_mfma", counter)
-        cmb, ncmb = _mean_counter(rows, "combine_kernel", counter)
         if ncal == 0 or ndec == 0:
             raise SystemExit(f"{d}: calibration or decode dispatches missing")
         shared = shared or npre > 0
         factor = cal_bytes / (cal * 1024.0)
-        per_call = (dec + (mrg if nmrg else 0.0) + (pre if npre else 0.0)
-                    + (cmb if ncmb else 0.0)) * 1024.0 * factor
+        per_call = (dec + (mrg if nmrg else 0.0) + (pre if npre else 0.0)) * 1024.0 * factor
         res[tag] = {"counter": counter, "calibration_kib": cal, "factor": factor,
                     "decode_kib": dec, "merge_kib": mrg if nmrg else None,
-                    "prefix_kib": pre if npre else None, "combine_kib": cmb if ncmb else None,
+                    "prefix_kib": pre if npre else None,
                     "decode_dispatches": ndec, "bytes_per_call": per_call}
         total += per_call
     res["kernel_source_digest"] = kernel_source_digest(
@@ -643,8 +641,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": ("kv_paged_attention_decode_append_shared call: tail decode "
-                                "(+ split-K merge), prefix attention once, combine" if shared else
+                     "kernel": ("kv_paged_attention_decode_append_shared call: prefix attention "
+                                "once, then the tails' decode (+ split-K merge) folding it in"
+                                if shared else
                                 ("kv_paged_attention_decode_append%s call: decode kernel + split-K merge"
                                  if not args.unfused else
                                  "kv_paged_attention_decode%s call: decode kernel + split-K merge")
