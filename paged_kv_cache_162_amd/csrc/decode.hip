@@ -45,6 +45,12 @@ constexpr int kStageStride = 132;  // floats per head row in LDS (128 + 4 agains
 #define PAGEDKV_DECODE_RING 3
 #endif
 constexpr int kDecodeRing = PAGEDKV_DECODE_RING;  // K/V blocks in flight per wave (MFMA decode)
+#ifndef PAGEDKV_DECODE_RING_PRE
+#define PAGEDKV_DECODE_RING_PRE 4
+#endif
+// the shared-prefix step's tail units: short tails give few waves per SIMD,
+// so a deeper ring pays (207 VGPRs, two waves per SIMD)
+constexpr int kDecodeRingPre = PAGEDKV_DECODE_RING_PRE;
 #ifndef PAGEDKV_DECODE_RING8
 #define PAGEDKV_DECODE_RING8 4
 #endif
@@ -913,13 +919,14 @@ kv_status launch_decode_kernel(const DecodeParams& prm, kv_dtype dtype, int head
       return dtype == KV_BF16
                  ? launch_decode(decode_valu_kernel<KV_BF16, 128, 1, BS, NT, true>, prm, st)
                  : launch_decode(decode_valu_kernel<KV_F16, 128, 1, BS, NT, true>, prm, st);
+    constexpr int RP = kDecodeRingPre;
     if (G <= 8)
       return dtype == KV_BF16
-                 ? launch_decode(decode_mfma_kernel<KV_BF16, true, R, BS, false, NT, true>, prm, st)
-                 : launch_decode(decode_mfma_kernel<KV_F16, true, R, BS, false, NT, true>, prm, st);
+                 ? launch_decode(decode_mfma_kernel<KV_BF16, true, RP, BS, false, NT, true>, prm, st)
+                 : launch_decode(decode_mfma_kernel<KV_F16, true, RP, BS, false, NT, true>, prm, st);
     return dtype == KV_BF16
-               ? launch_decode(decode_mfma_kernel<KV_BF16, false, R, BS, false, NT, true>, prm, st)
-               : launch_decode(decode_mfma_kernel<KV_F16, false, R, BS, false, NT, true>, prm, st);
+               ? launch_decode(decode_mfma_kernel<KV_BF16, false, RP, BS, false, NT, true>, prm, st)
+               : launch_decode(decode_mfma_kernel<KV_F16, false, RP, BS, false, NT, true>, prm, st);
   }
   if ((dtype == KV_F16 || dtype == KV_BF16) && head_dim == 128 && G >= 2) {
     if (G <= 8)
