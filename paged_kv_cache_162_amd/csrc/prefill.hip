@@ -37,7 +37,11 @@ using namespace pagedkv::dev;
 namespace {
 
 constexpr int kPfWaves = 4;        // waves per workgroup
-constexpr int kPfColTiles = 2;     // 16-column MFMA tiles per wave
+constexpr int kPfColTiles = 2;     // 16-column MFMA tiles per wave (chunked prefill)
+// The shared-prefix pass has few query rows (one per sequence) and short key
+// ranges: one column tile per wave doubles its workgroups and halves each
+// one's work per key tile, which measured faster there.
+constexpr int kShColTiles = 1;
 constexpr int kPfRowBytes = 272;   // LDS bytes per key row: 128 x 16-bit + 16 against bank conflicts
 constexpr int kPfSegment = 64;     // table entries staged at once (one per lane)
 constexpr int kPfKeys = 32;        // keys per LDS tile
@@ -72,7 +76,7 @@ struct ColTile {
   bool live;
 };
 
-template <int DT, int BS, bool KV8>
+template <int DT, int BS, bool KV8, int CT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_mfma_kernel(PrefillParams p) {
   constexpr int D = kPfHeadDim;
@@ -131,12 +135,12 @@ void prefill_mfma_kernel(PrefillParams p) {
   const int nblk = (nkeys + BS - 1) / BS;  // table entries in use
 
   // ---- columns and queries of this wave --------------------------------------
-  ColTile ct[kPfColTiles];
-  uint4 qb[kPfColTiles][4];
+  ColTile ct[CT];
+  uint4 qb[CT][4];
   const int hd = col % p.G;
 #pragma unroll
-  for (int t = 0; t < kPfColTiles; ++t) {
-    const int qr = row0 + (wave * kPfColTiles + t) * p.tpc + col / p.G;
+  for (int t = 0; t < CT; ++t) {
+    const int qr = row0 + (wave * CT + t) * p.tpc + col / p.G;
     ct[t].live = col < p.tpc * p.G && qr < row0 + rows;
     ct[t].qrow = qr;
     // a dead column sees every key (finite softmax of zero scores), never stored
@@ -223,10 +227,10 @@ void prefill_mfma_kernel(PrefillParams p) {
     }
   };
 
-  f32x4 o[kPfColTiles][8];
-  float m[kPfColTiles], l[kPfColTiles];
+  f32x4 o[CT][8];
+  float m[CT], l[CT];
 #pragma unroll
-  for (int t = 0; t < kPfColTiles; ++t) {
+  for (int t = 0; t < CT; ++t) {
 #pragma unroll
     for (int n = 0; n < 8; ++n) o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[t] = neg_inf();
@@ -259,7 +263,7 @@ void prefill_mfma_kernel(PrefillParams p) {
     // raw scores of every column tile first (K operands live); then per
     // column tile the softmax and the value products, so the MFMAs of one
     // tile can overlap the softmax of the next
-    float x[kPfColTiles][8];
+    float x[CT][8];
     {
       uint4 ku[2][4];
 #pragma unroll
@@ -269,7 +273,7 @@ void prefill_mfma_kernel(PrefillParams p) {
           ku[half][kc] = *reinterpret_cast<const uint4*>(
               &lds[buf][0][(16 * half + col) * kPfRowBytes + (kc * 4 + grp) * 16]);
 #pragma unroll
-      for (int t = 0; t < kPfColTiles; ++t)
+      for (int t = 0; t < CT; ++t)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -289,7 +293,7 @@ void prefill_mfma_kernel(PrefillParams p) {
     const bool causal = kPfKeys * j + kPfKeys - 1 > first_pos;  // some key hidden from some query
     const float sl = p.scale_log2;  // > 0, so the maximum commutes with the scaling
 #pragma unroll
-    for (int t = 0; t < kPfColTiles; ++t) {
+    for (int t = 0; t < CT; ++t) {
       if (causal) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -349,7 +353,7 @@ void prefill_mfma_kernel(PrefillParams p) {
 
   // ---- results: lane holds column col, dims 32grp + 8r + n (n < 8) -----------
 #pragma unroll
-  for (int t = 0; t < kPfColTiles; ++t) {
+  for (int t = 0; t < CT; ++t) {
     const float lt = column_sum(l[t]);
     if (!ct[t].live) continue;
     if (lse && grp == 0)
@@ -368,17 +372,20 @@ void prefill_mfma_kernel(PrefillParams p) {
   }
 }
 
-int32_t rows_per_block(int32_t G) { return kPfWaves * kPfColTiles * (16 / G); }
+int32_t rows_per_block(int32_t G, int32_t col_tiles = kPfColTiles) {
+  return kPfWaves * col_tiles * (16 / G);
+}
 
-template <bool KV8>
-auto pick_kernel(kv_dtype dtype, int32_t block_size) -> decltype(&prefill_mfma_kernel<KV_BF16, 16, KV8>) {
+template <bool KV8, int CT = kPfColTiles>
+auto pick_kernel(kv_dtype dtype, int32_t block_size)
+    -> decltype(&prefill_mfma_kernel<KV_BF16, 16, KV8, CT>) {
   if (dtype == KV_BF16)
-    return block_size == 8    ? prefill_mfma_kernel<KV_BF16, 8, KV8>
-           : block_size == 16 ? prefill_mfma_kernel<KV_BF16, 16, KV8>
-                              : prefill_mfma_kernel<KV_BF16, 32, KV8>;
-  return block_size == 8    ? prefill_mfma_kernel<KV_F16, 8, KV8>
-         : block_size == 16 ? prefill_mfma_kernel<KV_F16, 16, KV8>
-                            : prefill_mfma_kernel<KV_F16, 32, KV8>;
+    return block_size == 8    ? prefill_mfma_kernel<KV_BF16, 8, KV8, CT>
+           : block_size == 16 ? prefill_mfma_kernel<KV_BF16, 16, KV8, CT>
+                              : prefill_mfma_kernel<KV_BF16, 32, KV8, CT>;
+  return block_size == 8    ? prefill_mfma_kernel<KV_F16, 8, KV8, CT>
+         : block_size == 16 ? prefill_mfma_kernel<KV_F16, 16, KV8, CT>
+                            : prefill_mfma_kernel<KV_F16, 32, KV8, CT>;
 }
 
 kv_status prefill_impl(const char* who, float* out, const void* q, const void* k_pool,
@@ -465,7 +472,7 @@ int32_t shared_prefix_parts(int32_t S, int32_t num_q_heads, int32_t num_kv_heads
     return 0;
   const int32_t G = num_q_heads / num_kv_heads;
   if (G > 16) return 0;
-  const int64_t units = ceil_div64(S, rows_per_block(G)) * num_kv_heads;
+  const int64_t units = ceil_div64(S, rows_per_block(G, kShColTiles)) * num_kv_heads;
   const int64_t tiles = ceil_div64(shared_len, kPfKeys);
   int64_t parts = std::min<int64_t>(ceil_div64(512, units), kMaxSharedParts);
   parts = std::max<int64_t>(1, std::min<int64_t>(parts, tiles / PAGEDKV_SHARED_MIN_TILES));
@@ -486,7 +493,7 @@ kv_status shared_prefix_attention(float* o, float* lse, const void* q, const voi
                                   float scale, kv_dtype dtype, int32_t shared_len,
                                   hipStream_t stream) {
   const int32_t G = num_q_heads / num_kv_heads;
-  const int32_t rpb = rows_per_block(G);
+  const int32_t rpb = rows_per_block(G, kShColTiles);
   int32_t part_keys = 0;
   const int32_t parts = shared_prefix_parts(S, num_q_heads, num_kv_heads, shared_len, &part_keys);
   if (parts <= 0) return fail(KV_ERR_INVALID, "shared prefix: bad sizes");
@@ -512,7 +519,7 @@ kv_status shared_prefix_attention(float* o, float* lse, const void* q, const voi
   prm.key_parts = parts;
   prm.part_keys = part_keys;
   prm.lse = lse;
-  hipLaunchKernelGGL(pick_kernel<false>(dtype, block_size), dim3((unsigned)prm.n_units),
+  hipLaunchKernelGGL((pick_kernel<false, kShColTiles>(dtype, block_size)), dim3((unsigned)prm.n_units),
                      dim3(kPfWaves * 64), 0, stream, prm);
   return launch_status("kv_paged_attention_decode_append_shared (shared prefix)");
 }

@@ -117,14 +117,14 @@ def test_device_entry_points_validate_on_the_host(kv):
 
 def test_shared_prefix_entry_validation(kv):
     # per prefix range outputs [S][Hq][D] and denominators [S][Hq]. 32 sequences of group 4
-    # fill one 32-row block per KV head: 8 blocks, so 64 ranges are wanted; at most 16, at
+    # fill two 16-row blocks per KV head: 16 blocks, so 32 ranges are wanted; at most 16, at
     # least 4 tiles (128 positions) each
     aux = kv.kv_paged_attention_shared_aux_bytes
     assert aux(32, 32, 8, 128, 2048) == 16 * 129 * 32 * 32 * 4      # 16 ranges of 128
     assert aux(32, 32, 8, 128, 8192) == 16 * 129 * 32 * 32 * 4      # 16 ranges of 512
     assert aux(32, 32, 8, 128, 256) == 2 * 129 * 32 * 32 * 4        # 2 ranges of 128
     assert aux(32, 32, 8, 128, 96) == 1 * 129 * 32 * 32 * 4         # one range
-    assert aux(512, 64, 8, 128, 65536) == 2 * 129 * 512 * 64 * 4    # 256 blocks already
+    assert aux(512, 64, 8, 128, 65536) == 1 * 129 * 512 * 64 * 4    # 512 blocks already
     assert aux(0, 32, 8, 128, 2048) == 0
     assert aux(32, 32, 8, 128, 0) == 0
     assert aux(32, 64, 2, 128, 2048) == 0                                # group 32
