@@ -9,12 +9,12 @@ from workloads import make_workload
 torch = pytest.importorskip("torch")
 
 
-def prepared(cfg, B=16, S=None, **kw):
+def prepared(cfg, B=16, S=None, fp8=False, **kw):
     import paged_kv_cache_162_amd.binding as kv
     from paged_kv_cache_162_amd.session import DecodeSession
     w = make_workload(cfg, block_size=B, S=S)
     sp = w.spec
-    dt = torch.bfloat16 if sp.dtype == "bf16" else torch.float16
+    dt = torch.uint8 if fp8 else torch.bfloat16 if sp.dtype == "bf16" else torch.float16
     pool = torch.empty((w.num_blocks, sp.Hkv, B, sp.D), dtype=dt)
     sess = DecodeSession(k_pool=pool, v_pool=pool, num_q_heads=sp.Hq, free_order=w.free_order, **kw)
     for op in w.setup_ops:  # the host half of the operation script (no K/V values)
@@ -50,7 +50,7 @@ def test_common_prefix_is_found(cfg, B):
 
 
 @pytest.mark.parametrize("cfg,S,kw", [(3, 16, {}), (5, None, {"shared_prefix": False}),
-                                      (5, None, {"fused": False})])
+                                      (5, None, {"fused": False}), (5, None, {"fp8": True})])
 def test_plain_step_when_nothing_or_nothing_usable_is_shared(cfg, S, kw):
     kv, w, sess = prepared(cfg, S=S, **kw)
     assert sess.shared_tokens == 0 and sess.aux is None
