@@ -57,7 +57,8 @@ def shared_case(rng, S, shared_blocks, tails, Hq, Hkv, D, dt, B=16):
 # others the MFMA kernel; a partition below the 700-token tail makes the merge kernel combine
 CASES = [("bf16", 8, 16, 0, True), ("bf16", 8, 16, 256, False), ("f16", 4, 16, 128, True),
          ("bf16", 16, 16, 0, True), ("bf16", 8, 8, 0, True), ("bf16", 4, 32, 64, True),
-         ("bf16", 1, 16, 0, True), ("f16", 1, 8, 128, False), ("f16", 2, 16, 0, False)]
+         ("bf16", 1, 16, 0, True), ("f16", 1, 8, 128, False), ("f16", 2, 16, 0, False),
+         ("bf16", 6, 16, 0, True), ("f16", 3, 32, 128, False)]
 
 
 @pytest.mark.parametrize("dt,G,B,P,plan", CASES)
