@@ -34,10 +34,40 @@ from . import binding as kv
 AUTO_PARTITION_MIN_UNITS = 1500
 
 # A decode step takes the shared-prefix entry point when every sequence of the
-# batch (at least this many) reaches at least this many positions through the
-# same leading blocks: below that the prefix is cheap to read per sequence.
+# batch reaches the same leading blocks and reading them once saves more than
+# the extra launch and the shorter tails cost. Measured on an MI355X (32/8
+# heads, bf16, batches of 4-128 sequences, prefixes of 256-4096 positions,
+# tails of 64 and 512): the step was faster exactly where the batch re-reads
+# at least 65,536 prefix positions (sequences x shared positions) and the
+# prefix is at least 3.5 times the mean tail (the new token included);
+# elsewhere the plain step was as fast or faster.
 SHARED_PREFIX_MIN_SEQS = 4
 SHARED_PREFIX_MIN_TOKENS = 256
+SHARED_PREFIX_MIN_READS = 65536
+SHARED_PREFIX_TAIL_RATIO = 3.5
+
+
+def common_prefix_tokens(tables, lens, block_size: int) -> int:
+    """Positions every sequence reaches through the same leading table entries
+    (the same physical blocks), in whole blocks and short of each sequence's
+    last position (the new token's block is never shared)."""
+    if len(lens) == 0:
+        return 0
+    kmax = min(int(lens.min()) - 1, tables.shape[1] * block_size) // block_size
+    if kmax <= 0:
+        return 0
+    same = np.all(tables[:, :kmax] == tables[:1, :kmax], axis=0)
+    k = kmax if same.all() else int(np.argmin(same))
+    return k * block_size
+
+
+def shared_step_pays(S: int, shared: int, lens) -> bool:
+    """Whether the shared-prefix step is expected to beat the plain step for a
+    batch of S sequences sharing `shared` positions (the measured rule above)."""
+    if S < SHARED_PREFIX_MIN_SEQS or shared < SHARED_PREFIX_MIN_TOKENS:
+        return False
+    tail_mean = float(np.mean(np.asarray(lens, np.int64) - shared))
+    return S * shared >= SHARED_PREFIX_MIN_READS and shared >= SHARED_PREFIX_TAIL_RATIO * tail_mean
 
 
 class DecodeSession:
@@ -268,21 +298,15 @@ class DecodeSession:
         return host_slots, pairs
 
     def _common_prefix_tokens(self, tables, lens) -> int:
-        """Positions every sequence of the step reaches through the same
-        leading table entries (the same physical blocks), in whole blocks and
-        short of each sequence's last position; 0 when the shared-prefix step
-        does not apply (disabled, unfused, fp8, head_dim other than 128,
-        group above 16, too few sequences or too short a prefix)."""
-        S = len(lens)
+        """Positions the step's shared-prefix entry point treats as common: the
+        batch's common prefix (common_prefix_tokens), or 0 when that step does
+        not apply (disabled, unfused, fp8, head_dim other than 128, group
+        above 16) or is not expected to pay (shared_step_pays)."""
         if (not self.shared_prefix or not self.fused or self.fp8 or self.D != 128
-                or self.Hq // self.Hkv > 16 or S < SHARED_PREFIX_MIN_SEQS):
+                or self.Hq // self.Hkv > 16):
             return 0
-        kmax = min(int(lens.min()) - 1, tables.shape[1] * self.B) // self.B
-        if kmax * self.B < SHARED_PREFIX_MIN_TOKENS:
-            return 0
-        same = np.all(tables[:, :kmax] == tables[:1, :kmax], axis=0)
-        k = kmax if same.all() else int(np.argmin(same))
-        return k * self.B if k * self.B >= SHARED_PREFIX_MIN_TOKENS else 0
+        shared = common_prefix_tokens(tables, lens, self.B)
+        return shared if shared_step_pays(len(lens), shared, lens) else 0
 
     def write_step_tokens(self, k_new, v_new, k_pool=None, v_pool=None) -> None:
         """The unfused cache write of the step on its own: slot mapping of
