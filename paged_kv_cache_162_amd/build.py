@@ -1,23 +1,29 @@
 """Build libpagedkv.so in-tree with hipcc for gfx950.
 
 The library is one shared object: the host block manager (plain C++) and the
-HIP kernels with their C entry points. Packed-FP32 instruction selection is
-turned off for the device code.
+HIP kernels with their C entry points. Each source is compiled to an object
+of its own (in parallel; every device file carries its own code object), then
+the objects are linked. Packed-FP32 instruction selection is turned off for
+the device code.
 """
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedkv.so")
+OBJDIR = os.path.join(HERE, "_build")
 SOURCES = [os.path.join(CSRC, "host_pool.cpp"), os.path.join(CSRC, "plan.cpp"),
            os.path.join(CSRC, "cache.hip"), os.path.join(CSRC, "decode.hip"),
            os.path.join(CSRC, "prefill.hip")]
 ARCH = os.environ.get("PAGEDKV_ARCH", "gfx950")
+# the host pass warns that it does not know the packed-fp32 feature
+_NOISE = "is not a recognized feature for this target"
 
 
 def hipcc() -> str:
@@ -25,25 +31,45 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into paged_kv_cache_162_amd/libpagedkv.so."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-function",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-o", tmp] + SOURCES
+def _flags() -> list:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+            "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include")]
+
+
+def _run(cmd: list, verbose: bool) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    # the host pass warns that it does not know the packed-fp32 feature
-    noise = "is not a recognized feature for this target"
-    msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l]
+    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if _NOISE not in l)
     if res.returncode != 0:
-        sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    if verbose and msgs:
-        print("\n".join(msgs))
-    os.replace(tmp, LIB)
+        sys.stderr.write(msgs + "\n")
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}: {cmd[-1]}")
+    return msgs
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link paged_kv_cache_162_amd/libpagedkv.so."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    tag = "%d" % os.getpid()
+    objs = [os.path.join(OBJDIR, os.path.basename(s) + "." + tag + ".o") for s in SOURCES]
+    cmds = [[hipcc()] + _flags() + ["-c", "-o", o, s] for s, o in zip(SOURCES, objs)]
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    try:
+        with ThreadPoolExecutor(jobs) as ex:
+            outs = list(ex.map(lambda c: _run(c, verbose), cmds))
+        tmp = LIB + ".tmp" + tag
+        outs.append(_run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs,
+                         verbose))
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
+    if verbose:
+        text = "\n".join(m for m in outs if m)
+        if text:
+            print(text)
     return LIB
 
 
