@@ -263,18 +263,25 @@ kv_status kv_swap_in_blocks(void* const* k_pools, void* const* v_pools, int32_t 
 
 /* Work plan for kv_paged_attention_decode, built on the host from the host
  * copy of the context lengths (the block manager has them): the list of
- * (sequence, partition) items that hold tokens, longest first - every full
- * partition, then partial last partitions by decreasing length, then one
- * item for each sequence of length <= 0 (so its output is still written).
+ * (sequence, partition) items that hold tokens, and one item for each
+ * sequence of length <= 0 (so its output is still written), every item once.
+ * Order: longest first, laid out for the device's workgroup placement.
+ * Item i becomes workgroups i*num_kv_heads .. i*num_kv_heads + num_kv_heads - 1,
+ * which the hardware deals to compute units in turn, so items i and i + T,
+ * T = num_cus / gcd(num_kv_heads, num_cus), share compute units; the sorted
+ * items go out in rows of T with every other row reversed, which evens out
+ * the K/V bytes each compute unit streams. num_kv_heads or num_cus <= 0:
+ * plain longest-first order. num_cus is the device's compute-unit count
+ * (hipDeviceAttributeMultiprocessorCount, 256 on MI355X).
  * items_out: host int32 [cap][2] receiving (sequence, partition) pairs;
  * *n_items receives the item count, which is at most
  * S * ceil(max_len / partition) (KV_ERR_INVALID with *n_items set if cap is
  * smaller). partition_size as for the decode (0 = 512). The caller copies
  * the items to the device and passes them to the decode with the same
- * lengths and partition size. */
+ * lengths, partition size and KV head count. */
 kv_status kv_paged_attention_plan(const int32_t* context_lens_host, int32_t S,
-                                  int32_t partition_size, int32_t* items_out, int32_t cap,
-                                  int32_t* n_items);
+                                  int32_t partition_size, int32_t num_kv_heads, int32_t num_cus,
+                                  int32_t* items_out, int32_t cap, int32_t* n_items);
 
 /* Workspace bytes kv_paged_attention_decode needs for these sizes: 0 when
  * max_context_len <= the partition size (every sequence finishes in one

@@ -37,6 +37,11 @@ def _load() -> C.CDLL:
         raise ImportError(
             f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
             "or `python paged_kv_cache_162_amd/build.py`")
+    # torch first: its wheel carries its own HIP runtime under the same soname
+    # (libamdhip64.so.7), and the library must bind to the runtime that owns
+    # the tensors it is handed. Loaded the other way round, the first kernel
+    # launch finds no device.
+    import torch  # noqa: F401
     return C.CDLL(LIB_PATH)
 
 
@@ -82,7 +87,7 @@ _SIGS = {
                                      vp, vp]),
     "kv_swap_in_blocks": (C.c_int, [C.POINTER(vp), C.POINTER(vp), i32, vp, i32, i32, C.c_size_t,
                                     vp, vp]),
-    "kv_paged_attention_plan": (C.c_int, [P_i32, i32, i32, P_i32, i32, P_i32]),
+    "kv_paged_attention_plan": (C.c_int, [P_i32, i32, i32, i32, i32, P_i32, i32, P_i32]),
     "kv_paged_attention_workspace_bytes": (C.c_size_t, [i32, i32, i32, i32, i32, i32]),
     "kv_paged_attention_decode": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                             i32, f32, C.c_int, i32, i32, vp, i32, vp, C.c_size_t,
@@ -398,16 +403,21 @@ def kv_swap_in_blocks(k_pools: List, v_pools: List, block_ids, num_blocks: int,
           num_blocks, block_bytes, host, stream)
 
 
-def kv_paged_attention_plan(context_lens_host, partition_size: int = 0) -> np.ndarray:
-    """Host work plan: int32 [n_items, 2] (sequence, partition), longest first."""
+def kv_paged_attention_plan(context_lens_host, partition_size: int = 0, num_kv_heads: int = 0,
+                            num_cus: int = 0) -> np.ndarray:
+    """Host work plan: int32 [n_items, 2] (sequence, partition), longest first,
+    laid out for the workgroup placement of a device with num_cus compute units
+    (0 = plain longest-first order)."""
     lens = _i32_array(context_lens_host)
     n = i32()
-    st = lib.kv_paged_attention_plan(_p32(lens), len(lens), partition_size, None, 0, C.byref(n))
+    st = lib.kv_paged_attention_plan(_p32(lens), len(lens), partition_size, num_kv_heads,
+                                     num_cus, None, 0, C.byref(n))
     if st != KV_OK and n.value == 0:
         _check(st, "kv_paged_attention_plan")
     out = np.zeros((max(n.value, 1), 2), dtype=np.int32)
-    _check(lib.kv_paged_attention_plan(_p32(lens), len(lens), partition_size, _p32(out),
-                                       out.shape[0], C.byref(n)), "kv_paged_attention_plan")
+    _check(lib.kv_paged_attention_plan(_p32(lens), len(lens), partition_size, num_kv_heads,
+                                       num_cus, _p32(out), out.shape[0], C.byref(n)),
+           "kv_paged_attention_plan")
     return out[:n.value]
 
 

@@ -9,7 +9,7 @@ whole cache. The host part (`prepare_step`) and the device part (`step`) are
 separate so a benchmark can time the device part alone.
 
 Operation scripts are lists of tuples: ("create", s), ("fork", parent, child),
-("append", s, n) where s are caller-chosen sequence numbers.
+("append", s, n), ("free", s) where s are caller-chosen sequence numbers.
 
 Pools of dtype uint8 are an fp8 (E4M3) cache: every write quantises with the
 session's k_scale / v_scale and attention goes through the _fp8 entry points.
@@ -32,6 +32,7 @@ from . import binding as kv
 # Work units below which a longer partition is not chosen: about 3/4 of the
 # 2048 waves an MI355X runs at once (256 CUs x 8 waves), measured best.
 AUTO_PARTITION_MIN_UNITS = 1500
+MI355X_CUS = 256
 
 # A decode step takes the shared-prefix entry point when every sequence of the
 # batch reaches the same leading blocks and reading them once saves more than
@@ -73,7 +74,8 @@ def shared_step_pays(S: int, shared: int, lens) -> bool:
 class DecodeSession:
     def __init__(self, *, k_pool, v_pool, num_q_heads: int, free_order: Optional[Sequence[int]] = None,
                  partition_size: int = 0, use_plan: bool = True, fused: bool = True,
-                 k_scale: float = 1.0, v_scale: float = 1.0, shared_prefix: bool = True):
+                 k_scale: float = 1.0, v_scale: float = 1.0, shared_prefix: bool = True,
+                 num_cus: Optional[int] = None):
         import torch
         self.torch = torch
         NB, Hkv, B, D = k_pool.shape
@@ -97,6 +99,12 @@ class DecodeSession:
         self.handles: Dict[int, int] = {}
         self.block_bytes = Hkv * B * D * k_pool.element_size()
         self.device = k_pool.device
+        # compute units the decode plan lays its work out for (host-only
+        # sessions on CPU tensors plan for an MI355X's 256)
+        if num_cus is None:
+            num_cus = (torch.cuda.get_device_properties(self.device).multi_processor_count
+                       if self.device.type == "cuda" else MI355X_CUS)
+        self.num_cus = int(num_cus)
 
     def close(self) -> None:
         if self.pool:
@@ -122,6 +130,8 @@ class DecodeSession:
                 self.handles[op[1]] = kv.kv_seq_create(self.pool)
             elif op[0] == "fork":
                 self.handles[op[2]] = kv.kv_seq_fork(self.pool, self.handles[op[1]])
+            elif op[0] == "free":
+                kv.kv_seq_free(self.pool, self.handles.pop(op[1]))
             elif op[0] == "append":
                 s, n = op[1], op[2]
                 slots, pair = kv.kv_seq_append(self.pool, self.handles[s], n)
@@ -287,7 +297,7 @@ class DecodeSession:
         self.host_tables, self.host_lens = tables, lens
         self.d_items = None
         if self.use_plan:
-            items = kv.kv_paged_attention_plan(dlens, self.step_partition)
+            items = kv.kv_paged_attention_plan(dlens, self.step_partition, self.Hkv, self.num_cus)
             self.d_items = torch.from_numpy(items).to(dev)
         # blocks the decode kernels read for several sequences in the step
         # stay in the caches; otherwise every block streams past them (the

@@ -5,6 +5,7 @@ exactly (block IDs, slots, copy-on-write pairs, refcounts, free counts).
 No GPU work is launched here: device entry points are only called with
 arguments that host-side validation rejects before any HIP call.
 """
+import math
 import os
 import re
 
@@ -315,21 +316,56 @@ def test_worked_trace_through_the_c_abi(kv):
         kv.kv_pool_destroy(p)
 
 
-def test_work_plan_lists_every_partition_longest_first(kv):
+def _plan_sizes(lens, items, P):
+    return [-1 if lens[s] <= 0 else min(P, lens[s] - P * p) for s, p in items]
+
+
+def test_work_plan_lists_every_partition_once(kv):
     lens = [0, 40, 1030, 512, 513, -3, 16]
-    items = kv.kv_paged_attention_plan(lens, 512)
-    got = sorted(map(tuple, items))
     want = sorted([(0, 0), (1, 0), (2, 0), (2, 1), (2, 2), (3, 0), (4, 0), (4, 1), (5, 0), (6, 0)])
-    assert got == want
-    sizes = []
-    for s, p in items:
-        t = lens[s]
-        sizes.append(-1 if t <= 0 else min(512, t - 512 * p))
+    # no placement model: longest first
+    items = kv.kv_paged_attention_plan(lens, 512)
+    assert sorted(map(tuple, items)) == want
+    sizes = _plan_sizes(lens, items, 512)
     assert sizes == sorted(sizes, reverse=True)
+    # placement model: the longest-first list in rows of T = num_cus / gcd(heads, num_cus),
+    # every other row reversed
+    for hkv, cus in ((2, 8), (3, 8), (8, 256), (5, 4)):
+        T = cus // math.gcd(hkv, cus)
+        items = kv.kv_paged_attention_plan(lens, 512, hkv, cus)
+        assert sorted(map(tuple, items)) == want
+        base = sorted(_plan_sizes(lens, items, 512), reverse=True)
+        rows = [base[r:r + T] for r in range(0, len(base), T)]
+        assert _plan_sizes(lens, items, 512) == sum(
+            (row[::-1] if k % 2 else row for k, row in enumerate(rows)), [])
     with pytest.raises(kv.KVError):
         kv.kv_paged_attention_plan(lens, 24)
     with pytest.raises(kv.KVError):
         kv.kv_paged_attention_plan(lens, 2048)
+
+
+def test_work_plan_evens_out_compute_unit_loads(kv):
+    """On the 70B-shaped lengths, workgroup w = item * Hkv + head going to compute
+    unit w % 256: the placement-aware order leaves the most loaded unit with less
+    than longest-first order does, and close to the mean."""
+    from workloads import make_workload
+    w = make_workload(3)
+    lens = w.context_lens.astype(np.int32)
+    hkv, cus, P = w.spec.Hkv, 256, 768
+
+    def loads(items):
+        cu = np.zeros(cus)
+        sz = _plan_sizes(lens, items, P)
+        for i, n in enumerate(sz):
+            for h in range(hkv):
+                cu[(i * hkv + h) % cus] += max(n, 0)
+        return cu
+
+    plain = loads(kv.kv_paged_attention_plan(lens, P))
+    placed = loads(kv.kv_paged_attention_plan(lens, P, hkv, cus))
+    assert plain.sum() == placed.sum() == lens.sum() * hkv
+    assert placed.max() < plain.max()
+    assert placed.max() <= 1.1 * placed.mean()
 
 
 def test_fp8_entry_points_validate_on_the_host(kv):

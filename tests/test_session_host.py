@@ -40,7 +40,7 @@ def test_common_prefix_is_found(cfg, B):
     # tails of 257 take the partition chooser's smallest, 512 tokens (one partition each)
     assert sess.step_partition == kv.kv_paged_attention_choose_partition(
         tails, sp.Hkv, B, 1500) == 512
-    items = kv.kv_paged_attention_plan(tails, 512)
+    items = kv.kv_paged_attention_plan(tails, 512, sp.Hkv, 256)
     assert np.array_equal(sess.d_items.numpy(), items)
     assert sess.aux.numel() * 4 == kv.kv_paged_attention_shared_aux_bytes(
         sp.S, sp.Hq, sp.Hkv, sp.D, 2048)
