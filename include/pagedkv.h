@@ -296,6 +296,20 @@ size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_
                                           int32_t head_dim, int32_t max_context_len,
                                           int32_t partition_size);
 
+/* How the decode kernels load K and V (the load_policy argument of every
+ * decode entry point):
+ *   KV_LOADS_STREAM  loads carry the non-temporal hint: every block is read
+ *                    once per step, so nothing is kept in the caches for it.
+ *                    Fastest when no block is shared between the step's
+ *                    sequences (measured 10-15% over plain loads).
+ *   KV_LOADS_CACHED  plain loads: blocks shared by several sequences (a
+ *                    common prefix, [1] "Memory sharing") stay in the caches
+ *                    for their next reader.
+ * Results are identical under both; kv_paged_attention_choose_load_policy
+ * picks one for a step from the pool's sharing. Any other value is
+ * KV_ERR_INVALID. */
+typedef enum { KV_LOADS_STREAM = 0, KV_LOADS_CACHED = 1 } kv_load_policy;
+
 /* out[s][hq][:] = sum_j softmax_j(scale * <q[s][hq], K_s[j]>) V_s[j] over the
  * first context_lens[s] positions of sequence s, where K_s[j] and V_s[j] are
  * read from slot(j) of KV head hq / (num_q_heads / num_kv_heads) - exactly
@@ -324,6 +338,7 @@ size_t kv_paged_attention_workspace_bytes(int32_t S, int32_t num_q_heads, int32_
  * workspace:    device scratch of at least
  *               kv_paged_attention_workspace_bytes(...) bytes (may be NULL
  *               when that is 0).
+ * load_policy:  how K and V are loaded (kv_load_policy above).
  *
  * Per-sequence device-side checks (no fault, no error code): a sequence with
  * context_lens[s] == 0 gets an all-zero output. A sequence whose length is
@@ -344,7 +359,7 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
                                     kv_dtype dtype, int32_t partition_size,
                                     int32_t max_context_len, const int32_t* work_items,
                                     int32_t n_items, void* workspace, size_t ws_bytes,
-                                    hipStream_t stream);
+                                    kv_load_policy load_policy, hipStream_t stream);
 
 /* A partition size for a decode batch, from the host copy of its context
  * lengths: the largest of 1024, 768 and 512 tokens that is a multiple of
@@ -357,20 +372,45 @@ int32_t kv_paged_attention_choose_partition(const int32_t* context_lens_host, in
                                             int32_t num_kv_heads, int32_t block_size,
                                             int32_t min_units);
 
-/* How the decode kernels load K and V (all four decode entry points, for
- * the calling host thread; default KV_LOADS_STREAM):
- *   KV_LOADS_STREAM  loads carry the non-temporal hint: every block is read
- *                    once per step, so nothing is kept in the caches for it.
- *                    Fastest when no block is shared between the step's
- *                    sequences (measured 10-15% over plain loads).
- *   KV_LOADS_CACHED  plain loads: blocks shared by several sequences (a
- *                    common prefix, [1] "Memory sharing") stay in the caches
- *                    for their next reader.
- * Results are identical under both. kv_pool_shared_blocks tells whether a
- * pool currently holds shared blocks. */
-typedef enum { KV_LOADS_STREAM = 0, KV_LOADS_CACHED = 1 } kv_load_policy;
-kv_status kv_paged_attention_set_load_policy(kv_load_policy policy);
-kv_load_policy kv_paged_attention_load_policy(void);
+/* Positions that all S sequences reach through the same leading table
+ * entries, i.e. the same physical blocks ([1] "Memory sharing"), counted in
+ * whole blocks and short of every sequence's last position (the block that
+ * takes the step's new token never counts): k * block_size for the largest k
+ * with tables[s][i] == tables[0][i] for every s and i < k and
+ * k * block_size < context_lens[s] for every s. Host arrays: tables
+ * [S][max_blocks] int32, context_lens [S]. 0 for S == 0 or invalid sizes. */
+int32_t kv_paged_attention_common_prefix(const int32_t* tables_host, int32_t S,
+                                         int32_t max_blocks, const int32_t* context_lens_host,
+                                         int32_t block_size);
+
+/* Shared positions for kv_paged_attention_decode_append_shared, or 0 when a
+ * decode step over these sequences should take the plain step: the common
+ * prefix above, where that entry point supports the step (dtype f16 or
+ * bf16, head_dim 128, group size at most 16) and reading the prefix once per
+ * batch is expected to be faster than once per sequence. The rule comes from
+ * shared/plain step times measured on MI355X (32 query / 8 KV heads, bf16,
+ * 4-128 sequences, 256-4096 shared positions, tails of 64 and 512; a point
+ * counts as faster at a time ratio of 0.97 or less): at least 4 sequences
+ * and 256 shared positions, sequences x shared positions >= 49,152, and
+ * shared positions >= 3.5 x the mean tail (positions past the prefix, new
+ * token included). Every measured point with 32,768 prefix reads or fewer
+ * was not faster and every one with 65,536 or more that met the tail
+ * condition was; the threshold sits between. */
+int32_t kv_paged_attention_choose_shared_prefix(const int32_t* tables_host, int32_t S,
+                                                int32_t max_blocks,
+                                                const int32_t* context_lens_host,
+                                                int32_t block_size, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim,
+                                                kv_dtype dtype);
+
+/* Load policy for a decode step over pool: KV_LOADS_CACHED when the pool
+ * holds shared blocks besides the shared_tokens / block_size prefix blocks
+ * a shared-prefix step reads once by itself (those others are read by
+ * several of the step's sequences and should stay in the caches), else
+ * KV_LOADS_STREAM. shared_tokens 0 for a plain step. A null pool gives
+ * KV_LOADS_STREAM. */
+kv_load_policy kv_paged_attention_choose_load_policy(const kv_pool_t* pool,
+                                                     int32_t shared_tokens);
 
 /* One decode step with the cache write fused into the decode launch: for
  * each sequence s with t = context_lens[s] >= 1, position t-1 holds the
@@ -393,7 +433,7 @@ kv_status kv_paged_attention_decode_append(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
     int32_t max_context_len, const int32_t* work_items, int32_t n_items, void* workspace,
-    size_t ws_bytes, int64_t* slots, hipStream_t stream);
+    size_t ws_bytes, int64_t* slots, kv_load_policy load_policy, hipStream_t stream);
 
 /* The decode step of kv_paged_attention_decode_append for a batch whose
  * sequences all share their first shared_tokens positions ([1] "Memory
@@ -440,7 +480,7 @@ kv_status kv_paged_attention_decode_append_shared(
     int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
     int32_t shared_tokens, int32_t max_tail_len, const int32_t* work_items, int32_t n_items,
     void* workspace, size_t ws_bytes, float* aux, size_t aux_bytes, int64_t* slots,
-    hipStream_t stream);
+    kv_load_policy load_policy, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * fp8 KV cache ([1], "How does this relate to quantization?": K and V stored
@@ -490,7 +530,7 @@ kv_status kv_paged_attention_decode_fp8(float* out, const void* q, const void* k
                                         float v_scale, int32_t partition_size,
                                         int32_t max_context_len, const int32_t* work_items,
                                         int32_t n_items, void* workspace, size_t ws_bytes,
-                                        hipStream_t stream);
+                                        kv_load_policy load_policy, hipStream_t stream);
 
 /* kv_paged_attention_decode_append over fp8 pools: the new token's K and V
  * (of `dtype`) are quantised as kv_reshape_and_cache_fp8 does and written at
@@ -503,7 +543,8 @@ kv_status kv_paged_attention_decode_append_fp8(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     int32_t num_blocks, float scale, kv_dtype dtype, float k_scale, float v_scale,
     int32_t partition_size, int32_t max_context_len, const int32_t* work_items, int32_t n_items,
-    void* workspace, size_t ws_bytes, int64_t* slots, hipStream_t stream);
+    void* workspace, size_t ws_bytes, int64_t* slots, kv_load_policy load_policy,
+    hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Chunked prefill: several query tokens per sequence ([2] "The Successors -

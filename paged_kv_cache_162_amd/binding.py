@@ -91,25 +91,25 @@ _SIGS = {
     "kv_paged_attention_workspace_bytes": (C.c_size_t, [i32, i32, i32, i32, i32, i32]),
     "kv_paged_attention_decode": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                             i32, f32, C.c_int, i32, i32, vp, i32, vp, C.c_size_t,
-                                            vp]),
+                                            C.c_int, vp]),
     "kv_paged_attention_decode_append": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
                                                    i32, i32, i32, i32, f32, C.c_int, i32, i32,
-                                                   vp, i32, vp, C.c_size_t, vp, vp]),
+                                                   vp, i32, vp, C.c_size_t, vp, C.c_int, vp]),
     "kv_paged_attention_shared_aux_bytes": (C.c_size_t, [i32, i32, i32, i32, i32]),
     "kv_paged_attention_decode_append_shared": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32,
                                                           i32, i32, i32, i32, i32, f32, C.c_int,
                                                           i32, i32, i32, vp, i32, vp, C.c_size_t,
-                                                          vp, C.c_size_t, vp, vp]),
+                                                          vp, C.c_size_t, vp, C.c_int, vp]),
     "kv_reshape_and_cache_fp8": (C.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, C.c_int,
                                            f32, f32, vp]),
     "kv_quantize_fp8": (C.c_int, [vp, vp, i64, C.c_int, f32, vp]),
     "kv_paged_attention_decode_fp8": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
                                                 i32, i32, f32, C.c_int, f32, f32, i32, i32, vp,
-                                                i32, vp, C.c_size_t, vp]),
+                                                i32, vp, C.c_size_t, C.c_int, vp]),
     "kv_paged_attention_decode_append_fp8": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32,
                                                        i32, i32, i32, i32, i32, f32, C.c_int, f32,
                                                        f32, i32, i32, vp, i32, vp, C.c_size_t, vp,
-                                                       vp]),
+                                                       C.c_int, vp]),
     "kv_paged_attention_prefill_rows_per_item": (i32, [i32, i32]),
     "kv_paged_attention_prefill_plan": (C.c_int, [P_i32, P_i32, i32, i32, i32, P_i32, i32, P_i32]),
     "kv_paged_attention_prefill": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32,
@@ -118,8 +118,10 @@ _SIGS = {
                                                  i32, i32, i32, i32, f32, C.c_int, f32, f32, i32,
                                                  vp, i32, vp]),
     "kv_paged_attention_choose_partition": (i32, [P_i32, i32, i32, i32, i32]),
-    "kv_paged_attention_set_load_policy": (C.c_int, [C.c_int]),
-    "kv_paged_attention_load_policy": (C.c_int, []),
+    "kv_paged_attention_common_prefix": (i32, [P_i32, i32, i32, P_i32, i32]),
+    "kv_paged_attention_choose_shared_prefix": (i32, [P_i32, i32, i32, P_i32, i32, i32, i32, i32,
+                                                      C.c_int]),
+    "kv_paged_attention_choose_load_policy": (C.c_int, [vp, i32]),
     "kv_last_error": (C.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -273,19 +275,35 @@ def kv_pool_shared_blocks(pool: int) -> int:
     return int(lib.kv_pool_shared_blocks(pool))
 
 
-def kv_paged_attention_set_load_policy(policy: int) -> None:
-    _check(lib.kv_paged_attention_set_load_policy(policy), "kv_paged_attention_set_load_policy")
-
-
-def kv_paged_attention_load_policy() -> int:
-    return int(lib.kv_paged_attention_load_policy())
-
-
 def kv_paged_attention_choose_partition(context_lens_host, num_kv_heads: int, block_size: int,
                                         min_units: int) -> int:
     lens = _i32_array(context_lens_host)
     return int(lib.kv_paged_attention_choose_partition(_p32(lens), len(lens), num_kv_heads,
                                                         block_size, min_units))
+
+
+def kv_paged_attention_common_prefix(tables_host, context_lens_host, block_size: int) -> int:
+    """Positions every sequence reaches through the same leading blocks (whole blocks,
+    short of each sequence's last position)."""
+    tab = np.ascontiguousarray(tables_host, dtype=np.int32)
+    lens = _i32_array(context_lens_host)
+    return int(lib.kv_paged_attention_common_prefix(_p32(tab), tab.shape[0], tab.shape[1],
+                                                    _p32(lens), block_size))
+
+
+def kv_paged_attention_choose_shared_prefix(tables_host, context_lens_host, block_size: int,
+                                            num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                            dtype: int) -> int:
+    """Shared positions for the shared-prefix step, or 0 for the plain step."""
+    tab = np.ascontiguousarray(tables_host, dtype=np.int32)
+    lens = _i32_array(context_lens_host)
+    return int(lib.kv_paged_attention_choose_shared_prefix(
+        _p32(tab), tab.shape[0], tab.shape[1], _p32(lens), block_size, num_q_heads, num_kv_heads,
+        head_dim, dtype))
+
+
+def kv_paged_attention_choose_load_policy(pool: int, shared_tokens: int) -> int:
+    return int(lib.kv_paged_attention_choose_load_policy(pool, shared_tokens))
 
 
 # ---------------------------------------------------------------------------
@@ -429,7 +447,8 @@ def kv_paged_attention_workspace_bytes(S: int, num_q_heads: int, num_kv_heads: i
 
 def kv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale: float,
                               max_context_len: int, workspace=None, partition_size: int = 0,
-                              work_items=None, stream=None) -> None:
+                              work_items=None, load_policy: int = KV_LOADS_STREAM,
+                              stream=None) -> None:
     """out fp32 [S, Hq, D]; q [S, Hq, D]; pools [NB, Hkv, B, D]; tables int32 [S, max_blocks];
     context_lens int32 [S]; workspace: uint8/any device tensor or None; work_items: device
     int32 [n, 2] from kv_paged_attention_plan or None."""
@@ -447,14 +466,15 @@ def kv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens
         _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, B, NB, float(scale),
         dtype_code(q), partition_size, max_context_len,
         None if work_items is None else _dev(work_items, "work_items", torch.int32),
-        0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes, _stream(stream)),
+        0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
+        int(load_policy), _stream(stream)),
         "kv_paged_attention_decode")
 
 
 def kv_paged_attention_decode_append(out, q, k_new, v_new, k_pool, v_pool, block_tables,
                                      context_lens, scale: float, max_context_len: int, slots,
                                      workspace=None, partition_size: int = 0, work_items=None,
-                                     stream=None) -> None:
+                                     load_policy: int = KV_LOADS_STREAM, stream=None) -> None:
     """Decode step with the cache write fused in: k_new/v_new [S, Hkv, D] are written at
     position context_lens[s]-1 of each sequence (slots int64 [S] receives the slots), then
     attention as kv_paged_attention_decode."""
@@ -476,7 +496,7 @@ def kv_paged_attention_decode_append(out, q, k_new, v_new, k_pool, v_pool, block
         dtype_code(q), partition_size, max_context_len,
         None if work_items is None else _dev(work_items, "work_items", torch.int32),
         0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
-        _dev(slots, "slots", torch.int64), _stream(stream)),
+        _dev(slots, "slots", torch.int64), int(load_policy), _stream(stream)),
         "kv_paged_attention_decode_append")
 
 
@@ -490,6 +510,7 @@ def kv_paged_attention_decode_append_shared(out, q, k_new, v_new, k_pool, v_pool
                                             context_lens, scale: float, shared_tokens: int,
                                             max_tail_len: int, slots, aux, workspace=None,
                                             partition_size: int = 0, work_items=None,
+                                            load_policy: int = KV_LOADS_STREAM,
                                             stream=None) -> None:
     """kv_paged_attention_decode_append for sequences sharing their first shared_tokens
     positions: attention over the shared positions computed once for all queries, the tails
@@ -515,7 +536,7 @@ def kv_paged_attention_decode_append_shared(out, q, k_new, v_new, k_pool, v_pool
         None if work_items is None else _dev(work_items, "work_items", torch.int32),
         0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
         _dev(aux, "aux"), aux.numel() * aux.element_size(), _dev(slots, "slots", torch.int64),
-        _stream(stream)),
+        int(load_policy), _stream(stream)),
         "kv_paged_attention_decode_append_shared")
 
 
@@ -554,7 +575,8 @@ def kv_quantize_fp8(src, dst, scale: float, stream=None) -> None:
 def kv_paged_attention_decode_fp8(out, q, k_pool, v_pool, block_tables, context_lens,
                                   scale: float, k_scale: float, v_scale: float,
                                   max_context_len: int, workspace=None, partition_size: int = 0,
-                                  work_items=None, stream=None) -> None:
+                                  work_items=None, load_policy: int = KV_LOADS_STREAM,
+                                  stream=None) -> None:
     """kv_paged_attention_decode over uint8 E4M3 pools with per-pool scales; q f16/bf16."""
     torch = _torch()
     S, Hq, D = q.shape
@@ -570,7 +592,8 @@ def kv_paged_attention_decode_fp8(out, q, k_pool, v_pool, block_tables, context_
         _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, B, NB, float(scale),
         dtype_code(q), float(k_scale), float(v_scale), partition_size, max_context_len,
         None if work_items is None else _dev(work_items, "work_items", torch.int32),
-        0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes, _stream(stream)),
+        0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
+        int(load_policy), _stream(stream)),
         "kv_paged_attention_decode_fp8")
 
 
@@ -578,7 +601,8 @@ def kv_paged_attention_decode_append_fp8(out, q, k_new, v_new, k_pool, v_pool, b
                                          context_lens, scale: float, k_scale: float,
                                          v_scale: float, max_context_len: int, slots,
                                          workspace=None, partition_size: int = 0,
-                                         work_items=None, stream=None) -> None:
+                                         work_items=None, load_policy: int = KV_LOADS_STREAM,
+                                         stream=None) -> None:
     """Fused decode step over uint8 E4M3 pools: the new token is quantised and written at
     position context_lens[s]-1, then attention as kv_paged_attention_decode_fp8."""
     torch = _torch()
@@ -599,7 +623,7 @@ def kv_paged_attention_decode_append_fp8(out, q, k_new, v_new, k_pool, v_pool, b
         dtype_code(q), float(k_scale), float(v_scale), partition_size, max_context_len,
         None if work_items is None else _dev(work_items, "work_items", torch.int32),
         0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
-        _dev(slots, "slots", torch.int64), _stream(stream)),
+        _dev(slots, "slots", torch.int64), int(load_policy), _stream(stream)),
         "kv_paged_attention_decode_append_fp8")
 
 

@@ -977,9 +977,6 @@ kv_status launch_for_block_size(const DecodeParams& prm, kv_dtype dtype, int hea
                     : launch_decode_kernel<32, NT>(prm, dtype, head_dim, G, stream);
 }
 
-// Load policy of the decode launches made by this host thread.
-thread_local kv_load_policy g_load_policy = KV_LOADS_STREAM;
-
 }  // namespace
 
 extern "C" {
@@ -1018,11 +1015,15 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
                       int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
                       int32_t max_context_len, const int32_t* work_items, int32_t n_items,
                       void* workspace, size_t ws_bytes, const void* k_new, const void* v_new,
-                      int64_t* slots, hipStream_t stream, bool kv8 = false,
+                      int64_t* slots, kv_load_policy load_policy, hipStream_t stream,
+                      bool kv8 = false,
                       float k_scale = 1.0f, float v_scale = 1.0f,
                       const SharedPrefix* pre = nullptr) {
   if (pagedkv::dtype_bytes(dtype) == 0)
     return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: unknown dtype");
+  if (load_policy != KV_LOADS_STREAM && load_policy != KV_LOADS_CACHED)
+    return fail(KV_ERR_INVALID, "kv_paged_attention_decode: unknown load policy %d",
+                (int)load_policy);
   if (dtype == KV_FP8_E4M3)
     return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode: an fp8 cache goes through the "
                                     "_fp8 entry points (dtype is the query's type)");
@@ -1113,7 +1114,7 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
     prm.pre_lse = pre->lse;
     prm.pre_parts = pre->parts;
   }
-  const kv_status st = g_load_policy == KV_LOADS_CACHED
+  const kv_status st = load_policy == KV_LOADS_CACHED
                            ? launch_for_block_size<false>(prm, dtype, head_dim, G, kv8, stream)
                            : launch_for_block_size<true>(prm, dtype, head_dim, G, kv8, stream);
   if (st != KV_OK || nparts <= 1) return st;
@@ -1137,12 +1138,12 @@ kv_status kv_paged_attention_decode(float* out, const void* q, const void* k_poo
                                     kv_dtype dtype, int32_t partition_size,
                                     int32_t max_context_len, const int32_t* work_items,
                                     int32_t n_items, void* workspace, size_t ws_bytes,
-                                    hipStream_t stream) {
+                                    kv_load_policy load_policy, hipStream_t stream) {
   pagedkv::clear_error();
   return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                      partition_size, max_context_len, work_items, n_items, workspace, ws_bytes,
-                     nullptr, nullptr, nullptr, stream);
+                     nullptr, nullptr, nullptr, load_policy, stream);
 }
 
 kv_status kv_paged_attention_decode_append(
@@ -1151,7 +1152,7 @@ kv_status kv_paged_attention_decode_append(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
     int32_t max_context_len, const int32_t* work_items, int32_t n_items, void* workspace,
-    size_t ws_bytes, int64_t* slots, hipStream_t stream) {
+    size_t ws_bytes, int64_t* slots, kv_load_policy load_policy, hipStream_t stream) {
   pagedkv::clear_error();
   if (S > 0) {
     if (!k_new || !v_new || !slots)
@@ -1162,7 +1163,7 @@ kv_status kv_paged_attention_decode_append(
   return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                      partition_size, max_context_len, work_items, n_items, workspace, ws_bytes,
-                     k_new, v_new, slots, stream);
+                     k_new, v_new, slots, load_policy, stream);
 }
 
 size_t kv_paged_attention_shared_aux_bytes(int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
@@ -1182,7 +1183,7 @@ kv_status kv_paged_attention_decode_append_shared(
     int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
     int32_t shared_tokens, int32_t max_tail_len, const int32_t* work_items, int32_t n_items,
     void* workspace, size_t ws_bytes, float* aux, size_t aux_bytes, int64_t* slots,
-    hipStream_t stream) {
+    kv_load_policy load_policy, hipStream_t stream) {
   pagedkv::clear_error();
   const char* who = "kv_paged_attention_decode_append_shared";
   if (dtype != KV_F16 && dtype != KV_BF16)
@@ -1216,7 +1217,7 @@ kv_status kv_paged_attention_decode_append_shared(
   return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                      partition_size, max_tail_len, work_items, n_items, workspace, ws_bytes, k_new,
-                     v_new, slots, stream, false, 1.0f, 1.0f, &pre);
+                     v_new, slots, load_policy, stream, false, 1.0f, 1.0f, &pre);
 }
 
 kv_status kv_paged_attention_decode_fp8(float* out, const void* q, const void* k_pool,
@@ -1228,12 +1229,12 @@ kv_status kv_paged_attention_decode_fp8(float* out, const void* q, const void* k
                                         float v_scale, int32_t partition_size,
                                         int32_t max_context_len, const int32_t* work_items,
                                         int32_t n_items, void* workspace, size_t ws_bytes,
-                                        hipStream_t stream) {
+                                        kv_load_policy load_policy, hipStream_t stream) {
   pagedkv::clear_error();
   return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                      partition_size, max_context_len, work_items, n_items, workspace, ws_bytes,
-                     nullptr, nullptr, nullptr, stream, true, k_scale, v_scale);
+                     nullptr, nullptr, nullptr, load_policy, stream, true, k_scale, v_scale);
 }
 
 kv_status kv_paged_attention_decode_append_fp8(
@@ -1242,7 +1243,8 @@ kv_status kv_paged_attention_decode_append_fp8(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     int32_t num_blocks, float scale, kv_dtype dtype, float k_scale, float v_scale,
     int32_t partition_size, int32_t max_context_len, const int32_t* work_items, int32_t n_items,
-    void* workspace, size_t ws_bytes, int64_t* slots, hipStream_t stream) {
+    void* workspace, size_t ws_bytes, int64_t* slots, kv_load_policy load_policy,
+    hipStream_t stream) {
   pagedkv::clear_error();
   if (S > 0) {
     if (!k_new || !v_new || !slots)
@@ -1254,18 +1256,7 @@ kv_status kv_paged_attention_decode_append_fp8(
   return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                      partition_size, max_context_len, work_items, n_items, workspace, ws_bytes,
-                     k_new, v_new, slots, stream, true, k_scale, v_scale);
+                     k_new, v_new, slots, load_policy, stream, true, k_scale, v_scale);
 }
-
-kv_status kv_paged_attention_set_load_policy(kv_load_policy policy) {
-  pagedkv::clear_error();
-  if (policy != KV_LOADS_STREAM && policy != KV_LOADS_CACHED)
-    return fail(KV_ERR_INVALID, "kv_paged_attention_set_load_policy: unknown policy %d",
-                (int)policy);
-  g_load_policy = policy;
-  return KV_OK;
-}
-
-kv_load_policy kv_paged_attention_load_policy(void) { return g_load_policy; }
 
 }  // extern "C"

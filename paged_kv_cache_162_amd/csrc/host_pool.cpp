@@ -406,6 +406,15 @@ int32_t kv_pool_shared_blocks(const kv_pool_t* p) {
   return n;
 }
 
+// Blocks a step's sequences share, other than the prefix a shared-prefix
+// step reads once, are read by several sequences in one launch: keep them in
+// the caches.
+kv_load_policy kv_paged_attention_choose_load_policy(const kv_pool_t* p, int32_t shared_tokens) {
+  if (!p) return KV_LOADS_STREAM;
+  const int32_t common = shared_tokens > 0 ? shared_tokens / p->cfg.block_size : 0;
+  return kv_pool_shared_blocks(p) > common ? KV_LOADS_CACHED : KV_LOADS_STREAM;
+}
+
 int32_t kv_seq_is_swapped(const kv_pool_t* p, int64_t seq) {
   if (!p) return -1;
   auto it = p->seqs.find(seq);

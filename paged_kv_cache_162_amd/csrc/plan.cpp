@@ -145,3 +145,51 @@ extern "C" int32_t kv_paged_attention_choose_partition(const int32_t* context_le
   }
   return 512;
 }
+
+// ---- step policies --------------------------------------------------------
+// How many leading positions a decode batch shares, and whether the
+// shared-prefix step should read them once for the batch. The thresholds are
+// measurements on MI355X, stated in the header. (The load-policy choice needs
+// the pool's reference counts and sits with the block manager.)
+
+namespace {
+constexpr int32_t kSharedMinSeqs = 4;
+constexpr int32_t kSharedMinTokens = 256;
+constexpr int64_t kSharedMinReads = 49152;  // sequences x shared positions
+constexpr double kSharedTailRatio = 3.5;    // shared positions / mean tail
+}  // namespace
+
+extern "C" int32_t kv_paged_attention_common_prefix(const int32_t* tables_host, int32_t S,
+                                                    int32_t max_blocks,
+                                                    const int32_t* context_lens_host,
+                                                    int32_t block_size) {
+  if (S <= 0 || !tables_host || !context_lens_host || max_blocks <= 0 || block_size <= 0)
+    return 0;
+  int64_t min_len = context_lens_host[0];
+  for (int32_t s = 1; s < S; ++s) min_len = std::min<int64_t>(min_len, context_lens_host[s]);
+  // blocks wholly before every sequence's last position, within the table
+  const int64_t kmax = std::min<int64_t>(min_len - 1, (int64_t)max_blocks * block_size) / block_size;
+  int64_t k = 0;
+  for (; k < kmax; ++k) {
+    const int32_t id = tables_host[k];
+    bool same = true;
+    for (int32_t s = 1; s < S && same; ++s) same = tables_host[(size_t)s * max_blocks + k] == id;
+    if (!same) break;
+  }
+  return (int32_t)(k * block_size);
+}
+
+extern "C" int32_t kv_paged_attention_choose_shared_prefix(
+    const int32_t* tables_host, int32_t S, int32_t max_blocks, const int32_t* context_lens_host,
+    int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    kv_dtype dtype) {
+  if ((dtype != KV_F16 && dtype != KV_BF16) || head_dim != 128 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 16 || S < kSharedMinSeqs)
+    return 0;
+  const int32_t shared =
+      kv_paged_attention_common_prefix(tables_host, S, max_blocks, context_lens_host, block_size);
+  if (shared < kSharedMinTokens || (int64_t)S * shared < kSharedMinReads) return 0;
+  double tail_sum = 0.0;
+  for (int32_t s = 0; s < S; ++s) tail_sum += (double)context_lens_host[s] - shared;
+  return shared >= kSharedTailRatio * (tail_sum / S) ? shared : 0;
+}

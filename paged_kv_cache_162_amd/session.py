@@ -34,43 +34,6 @@ from . import binding as kv
 AUTO_PARTITION_MIN_UNITS = 1500
 MI355X_CUS = 256
 
-# A decode step takes the shared-prefix entry point when every sequence of the
-# batch reaches the same leading blocks and reading them once saves more than
-# the extra launch and the shorter tails cost. Measured on an MI355X (32/8
-# heads, bf16, batches of 4-128 sequences, prefixes of 256-4096 positions,
-# tails of 64 and 512): the step was faster exactly where the batch re-reads
-# at least 65,536 prefix positions (sequences x shared positions) and the
-# prefix is at least 3.5 times the mean tail (the new token included);
-# elsewhere the plain step was as fast or faster.
-SHARED_PREFIX_MIN_SEQS = 4
-SHARED_PREFIX_MIN_TOKENS = 256
-SHARED_PREFIX_MIN_READS = 65536
-SHARED_PREFIX_TAIL_RATIO = 3.5
-
-
-def common_prefix_tokens(tables, lens, block_size: int) -> int:
-    """Positions every sequence reaches through the same leading table entries
-    (the same physical blocks), in whole blocks and short of each sequence's
-    last position (the new token's block is never shared)."""
-    if len(lens) == 0:
-        return 0
-    kmax = min(int(lens.min()) - 1, tables.shape[1] * block_size) // block_size
-    if kmax <= 0:
-        return 0
-    same = np.all(tables[:, :kmax] == tables[:1, :kmax], axis=0)
-    k = kmax if same.all() else int(np.argmin(same))
-    return k * block_size
-
-
-def shared_step_pays(S: int, shared: int, lens) -> bool:
-    """Whether the shared-prefix step is expected to beat the plain step for a
-    batch of S sequences sharing `shared` positions (the measured rule above)."""
-    if S < SHARED_PREFIX_MIN_SEQS or shared < SHARED_PREFIX_MIN_TOKENS:
-        return False
-    tail_mean = float(np.mean(np.asarray(lens, np.int64) - shared))
-    return S * shared >= SHARED_PREFIX_MIN_READS and shared >= SHARED_PREFIX_TAIL_RATIO * tail_mean
-
-
 class DecodeSession:
     def __init__(self, *, k_pool, v_pool, num_q_heads: int, free_order: Optional[Sequence[int]] = None,
                  partition_size: int = 0, use_plan: bool = True, fused: bool = True,
@@ -302,21 +265,19 @@ class DecodeSession:
         # blocks the decode kernels read for several sequences in the step
         # stay in the caches; otherwise every block streams past them (the
         # shared prefix of a shared-prefix step is read once, elsewhere)
-        common = self.shared_tokens // self.B
-        self.load_policy = (kv.KV_LOADS_CACHED if kv.kv_pool_shared_blocks(self.pool) > common
-                            else kv.KV_LOADS_STREAM)
+        self.load_policy = kv.kv_paged_attention_choose_load_policy(self.pool, self.shared_tokens)
         return host_slots, pairs
 
     def _common_prefix_tokens(self, tables, lens) -> int:
         """Positions the step's shared-prefix entry point treats as common: the
-        batch's common prefix (common_prefix_tokens), or 0 when that step does
-        not apply (disabled, unfused, fp8, head_dim other than 128, group
-        above 16) or is not expected to pay (shared_step_pays)."""
-        if (not self.shared_prefix or not self.fused or self.fp8 or self.D != 128
-                or self.Hq // self.Hkv > 16):
+        library's choice for the batch (kv_paged_attention_choose_shared_prefix:
+        the common leading blocks where that step applies and is expected to
+        pay), or 0 when the session runs plain steps (shared_prefix=False) or
+        unfused steps, which the shared-prefix entry point does not offer."""
+        if not self.shared_prefix or not self.fused:
             return 0
-        shared = common_prefix_tokens(tables, lens, self.B)
-        return shared if shared_step_pays(len(lens), shared, lens) else 0
+        return kv.kv_paged_attention_choose_shared_prefix(tables, lens, self.B, self.Hq, self.Hkv,
+                                                          self.D, self.dtype)
 
     def write_step_tokens(self, k_new, v_new, k_pool=None, v_pool=None) -> None:
         """The unfused cache write of the step on its own: slot mapping of
@@ -346,7 +307,6 @@ class DecodeSession:
         if self.shared_tokens and not fused:
             raise ValueError("this step was prepared for the shared-prefix decode, which fuses "
                              "the cache write; create the session with shared_prefix=False")
-        kv.kv_paged_attention_set_load_policy(self.load_policy)
         if self.d_pairs.shape[0]:
             kv.kv_copy_blocks([kp], [vp_], self.d_pairs, self.NB, self.block_bytes)
         if not fused:
@@ -358,24 +318,25 @@ class DecodeSession:
                 kv.kv_paged_attention_decode_append_fp8(
                     out, q, k_new, v_new, kp, vp_, self.d_tables, self.d_lens, scale, self.k_scale,
                     self.v_scale, self.max_context_len, self.d_slots, self.workspace,
-                    self.step_partition, self.d_items)
+                    self.step_partition, self.d_items, load_policy=self.load_policy)
             else:
                 kv.kv_paged_attention_decode_fp8(
                     out, q, kp, vp_, self.d_tables, self.d_lens, scale, self.k_scale, self.v_scale,
-                    self.max_context_len, self.workspace, self.step_partition, self.d_items)
+                    self.max_context_len, self.workspace, self.step_partition, self.d_items,
+                    load_policy=self.load_policy)
         elif self.shared_tokens:
             kv.kv_paged_attention_decode_append_shared(
                 out, q, k_new, v_new, kp, vp_, self.d_tables, self.d_lens, scale,
                 self.shared_tokens, self.max_decode_len, self.d_slots, self.aux, self.workspace,
-                self.step_partition, self.d_items)
+                self.step_partition, self.d_items, load_policy=self.load_policy)
         elif fused:
             kv.kv_paged_attention_decode_append(out, q, k_new, v_new, kp, vp_, self.d_tables,
                                                 self.d_lens, scale, self.max_context_len,
                                                 self.d_slots, self.workspace, self.step_partition,
-                                                self.d_items)
+                                                self.d_items, load_policy=self.load_policy)
         else:
             kv.kv_paged_attention_decode(out, q, kp, vp_, self.d_tables, self.d_lens, scale,
                                          self.max_context_len, self.workspace, self.step_partition,
-                                         self.d_items)
+                                         self.d_items, load_policy=self.load_policy)
         if decode_events is not None:
             decode_events[1].record()

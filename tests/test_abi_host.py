@@ -74,13 +74,15 @@ def test_device_entry_points_validate_on_the_host(kv):
     lib = kv.lib
     # unsupported block size / head_dim / group; rejected before any launch
     args = dict(out=None, q=None, k=None, v=None, t=None, mb=4, lens=None, S=1, Hq=8, Hkv=2,
-                D=128, B=16, NB=8, scale=1.0, dt=kv.KV_BF16, P=0, mc=16, ws=None, wsb=0, st=None)
+                D=128, B=16, NB=8, scale=1.0, dt=kv.KV_BF16, P=0, mc=16, ws=None, wsb=0,
+                pol=kv.KV_LOADS_STREAM, st=None)
 
     def call(**kw):
         a = dict(args, **kw)
         return lib.kv_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["t"], a["mb"], a["lens"],
                                              a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"], a["scale"],
-                                             a["dt"], a["P"], a["mc"], None, 0, a["ws"], a["wsb"], a["st"])
+                                             a["dt"], a["P"], a["mc"], None, 0, a["ws"], a["wsb"],
+                                             a["pol"], a["st"])
     assert call(B=12) == kv.KV_ERR_UNSUPPORTED
     assert call(B=32, P=48) == kv.KV_ERR_INVALID   # partition not a multiple of the block
     assert call(B=8, P=24) == kv.KV_ERR_INVALID    # not a multiple of the 16-token tile
@@ -91,6 +93,7 @@ def test_device_entry_points_validate_on_the_host(kv):
     assert call(P=2048) == kv.KV_ERR_INVALID   # partitions hold at most 1024 tokens
     assert call(B=8, P=1024, S=0) == kv.KV_OK  # 128 entries of 8-token blocks are accepted
     assert call(dt=7) == kv.KV_ERR_UNSUPPORTED
+    assert call(pol=2) == kv.KV_ERR_INVALID     # unknown load policy
     assert call() == kv.KV_ERR_INVALID          # null pointers
     assert call(S=0) == kv.KV_OK                # nothing to do
     assert lib.kv_reshape_and_cache(None, None, None, None, None, 1, 4, 2, 60, 16, kv.KV_F16, None) \
@@ -99,7 +102,7 @@ def test_device_entry_points_validate_on_the_host(kv):
     # fused decode + cache write: needs k_new, v_new and slots; nothing to do for S = 0
     dec_app = lambda S, kn: lib.kv_paged_attention_decode_append(
         None, None, kn, kn, None, None, None, 4, None, S, 8, 2, 128, 16, 8, 1.0, kv.KV_BF16, 0, 16,
-        None, 0, None, 0, None, None)
+        None, 0, None, 0, None, kv.KV_LOADS_STREAM, None)
     assert dec_app(1, None) == kv.KV_ERR_INVALID
     assert dec_app(0, None) == kv.KV_OK
     assert lib.kv_append_tokens(None, 1, 1, None, None, 0, None, None, None, None, 4, 2, 64, 16,
@@ -132,7 +135,7 @@ def test_shared_prefix_entry_validation(kv):
     call = lambda shared, S=2, D=128, B=16, dt=kv.KV_BF16: \
         kv.lib.kv_paged_attention_decode_append_shared(
             None, None, None, None, None, None, None, 4, None, S, 8, 2, D, B, 8, 1.0, dt, 0,
-            shared, 16, None, 0, None, 0, None, 0, None, None)
+            shared, 16, None, 0, None, 0, None, 0, None, kv.KV_LOADS_CACHED, None)
     assert call(24) == kv.KV_ERR_INVALID          # not whole blocks
     assert call(0) == kv.KV_ERR_INVALID           # nothing shared
     assert call(80) == kv.KV_ERR_INVALID          # more blocks than the table holds
@@ -372,17 +375,19 @@ def test_fp8_entry_points_validate_on_the_host(kv):
     lib = kv.lib
     call = lambda **k: lib.kv_paged_attention_decode_fp8(
         None, None, None, None, None, 4, None, k.get("S", 1), 8, 2, k.get("D", 128), 16, 8, 1.0,
-        k.get("dt", kv.KV_BF16), k.get("ks", 1.0), k.get("vs", 1.0), 0, 16, None, 0, None, 0, None)
+        k.get("dt", kv.KV_BF16), k.get("ks", 1.0), k.get("vs", 1.0), 0, 16, None, 0, None, 0,
+        k.get("pol", kv.KV_LOADS_STREAM), None)
     assert call(ks=0.0) == kv.KV_ERR_INVALID
     assert call(vs=float("nan")) == kv.KV_ERR_INVALID
     assert call(D=64) == kv.KV_ERR_UNSUPPORTED
     assert call(dt=kv.KV_F32) == kv.KV_ERR_UNSUPPORTED
     assert call() == kv.KV_ERR_INVALID            # null pointers
     assert call(S=0) == kv.KV_OK
+    assert call(pol=-1) == kv.KV_ERR_INVALID
     # the 16-bit entry point refuses an fp8 cache type
     assert lib.kv_paged_attention_decode(None, None, None, None, None, 4, None, 1, 8, 2, 128, 16, 8,
-                                         1.0, kv.KV_FP8_E4M3, 0, 16, None, 0, None, 0, None) \
-        == kv.KV_ERR_UNSUPPORTED
+                                         1.0, kv.KV_FP8_E4M3, 0, 16, None, 0, None, 0,
+                                         kv.KV_LOADS_STREAM, None) == kv.KV_ERR_UNSUPPORTED
 
 
 def test_prefill_entry_points_validate_on_the_host(kv):
@@ -432,15 +437,23 @@ def test_prefill_fp8_entry_point_validates_on_the_host(kv):
     assert call(S=0) == kv.KV_OK
 
 
-def test_load_policy_setting(kv):
-    assert kv.kv_paged_attention_load_policy() == kv.KV_LOADS_STREAM
-    kv.kv_paged_attention_set_load_policy(kv.KV_LOADS_CACHED)
-    assert kv.kv_paged_attention_load_policy() == kv.KV_LOADS_CACHED
-    with pytest.raises(kv.KVError):
-        kv.kv_paged_attention_set_load_policy(7)
-    assert kv.kv_paged_attention_load_policy() == kv.KV_LOADS_CACHED
-    kv.kv_paged_attention_set_load_policy(kv.KV_LOADS_STREAM)
+def test_load_policy_choice(kv):
+    """Cached loads exactly when the pool holds shared blocks beyond the prefix a
+    shared-prefix step reads once by itself."""
     assert kv.lib.kv_pool_shared_blocks(None) == -1
+    assert kv.kv_paged_attention_choose_load_policy(0, 0) == kv.KV_LOADS_STREAM
+    p = kv.kv_pool_create(32, 16, 1, 2, 64, kv.KV_BF16)
+    try:
+        a = kv.kv_seq_create(p)
+        kv.kv_seq_append(p, a, 40)                  # 3 blocks, private
+        assert kv.kv_paged_attention_choose_load_policy(p, 0) == kv.KV_LOADS_STREAM
+        kv.kv_seq_fork(p, a)                        # 3 blocks shared
+        assert kv.kv_paged_attention_choose_load_policy(p, 0) == kv.KV_LOADS_CACHED
+        # a shared-prefix step reading 2 of them once still leaves one shared block
+        assert kv.kv_paged_attention_choose_load_policy(p, 32) == kv.KV_LOADS_CACHED
+        assert kv.kv_paged_attention_choose_load_policy(p, 48) == kv.KV_LOADS_STREAM
+    finally:
+        kv.kv_pool_destroy(p)
 
 
 def test_choose_partition(kv):

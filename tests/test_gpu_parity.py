@@ -680,16 +680,14 @@ def test_load_policies_give_identical_bits(cfg, S):
         case.device_run(shared_prefix=False)        # the session's own choice
         chosen = case.sess.load_policy
         assert chosen == (kv.KV_LOADS_CACHED if cfg == 5 else kv.KV_LOADS_STREAM)
-        case.sess.load_policy = policy
         out = torch.full_like(case.out_dev, float("nan"))
         ws = case.sess.workspace
-        kv.kv_paged_attention_set_load_policy(policy)
         kv.kv_paged_attention_decode(out, case.q_dev, case.k_dev, case.v_dev, case.sess.d_tables,
                                      case.sess.d_lens, case.sp.scale, case.sess.max_context_len,
-                                     ws, 0, case.sess.d_items)
+                                     ws, case.sess.step_partition, case.sess.d_items,
+                                     load_policy=policy)
         torch.cuda.synchronize()
         res[policy] = out.cpu().numpy()
         assert np.array_equal(res[policy].view(np.uint32), case.out_dev.cpu().numpy().view(np.uint32))
         case.sess.close()
-    kv.kv_paged_attention_set_load_policy(kv.KV_LOADS_STREAM)
     assert np.array_equal(res[0].view(np.uint32), res[1].view(np.uint32))

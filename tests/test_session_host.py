@@ -62,8 +62,11 @@ def test_plain_step_when_nothing_or_nothing_usable_is_shared(cfg, S, kw):
 
 def test_common_prefix_rule():
     """Whole common leading blocks, each sequence's last position left in its tail."""
-    from paged_kv_cache_162_amd.session import common_prefix_tokens as f
     kv, w, sess = prepared(5)
+
+    def f(tab, lens, B):
+        return kv.kv_paged_attention_common_prefix(tab, lens, B)
+
     tab, lens = sess.host_tables.copy(), sess.host_lens.copy()
     assert f(tab, lens, 16) == 2048
     assert f(tab[:3], lens[:3], 16) == 2048
@@ -83,7 +86,11 @@ def test_common_prefix_rule():
 
 
 # (sequences, shared positions, tail, shared step faster) as measured on an MI355X for
-# 32/8 heads in bf16: ratios of shared to plain step time from 0.29 to 1.67
+# 32/8 heads in bf16: ratios of shared to plain step time from 0.29 to 1.67. "Faster" means a
+# ratio of 0.97 or less (run-to-run spread is 1-2%): (32, 1024, 64) measured 0.98 and
+# (128, 1024, 512) 0.99, so both count as not faster. Every point with at most 32,768 prefix
+# reads (sequences x shared positions) was not faster; the library's threshold, 49,152, sits
+# between that and the 65,536 of the prefix-sharing workload (32 x 2048).
 MEASURED = [(4, 4096, 64, False), (8, 4096, 512, False), (16, 2048, 64, False),
             (16, 4096, 64, True), (16, 4096, 512, True), (32, 1024, 64, False),
             (32, 2048, 64, True), (32, 2048, 512, True), (32, 2048, 257, True),
@@ -93,8 +100,34 @@ MEASURED = [(4, 4096, 64, False), (8, 4096, 512, False), (16, 2048, 64, False),
             (32, 4096, 512, True), (64, 2048, 64, True), (128, 1024, 512, False)]
 
 
+def _shared_batch(S, shared, tail, B=16):
+    """Tables of S sequences with `shared` common leading positions and a private tail of
+    tail + 1 positions each (the new token included)."""
+    nb = -(-(shared + tail + 1) // B)
+    tab = np.empty((S, nb), np.int32)
+    tab[:, :shared // B] = np.arange(shared // B)
+    priv = nb - shared // B
+    tab[:, shared // B:] = shared // B + np.arange(S * priv).reshape(S, priv)
+    return tab, np.full(S, shared + tail + 1, np.int32)
+
+
 @pytest.mark.parametrize("S,shared,tail,faster", MEASURED)
 def test_shared_step_rule_matches_measurements(S, shared, tail, faster):
-    from paged_kv_cache_162_amd.session import shared_step_pays
-    lens = np.full(S, shared + tail + 1, np.int32)
-    assert shared_step_pays(S, shared, lens) == faster
+    import paged_kv_cache_162_amd.binding as kv
+    tab, lens = _shared_batch(S, shared, tail)
+    got = kv.kv_paged_attention_choose_shared_prefix(tab, lens, 16, 32, 8, 128, kv.KV_BF16)
+    assert got == (shared if faster else 0)
+
+
+def test_shared_step_only_where_the_entry_point_applies():
+    import paged_kv_cache_162_amd.binding as kv
+    tab, lens = _shared_batch(32, 2048, 257)
+    choose = lambda **k: kv.kv_paged_attention_choose_shared_prefix(
+        tab, lens, 16, k.get("Hq", 32), k.get("Hkv", 8), k.get("D", 128), k.get("dt", kv.KV_BF16))
+    assert choose() == choose(dt=kv.KV_F16) == 2048
+    assert choose(dt=kv.KV_FP8_E4M3) == choose(dt=kv.KV_F32) == 0
+    assert choose(D=64) == 0 and choose(Hq=64, Hkv=2) == 0 and choose(Hq=30) == 0
+    assert choose(Hq=128, Hkv=8) == 2048     # group 16, the prefill kernel's largest
+    # three sequences are too few, and a prefix read once per batch by them does not pay
+    assert kv.kv_paged_attention_choose_shared_prefix(tab[:3], lens[:3], 16, 32, 8, 128,
+                                                      kv.KV_BF16) == 0
