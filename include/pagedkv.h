@@ -435,6 +435,34 @@ kv_status kv_paged_attention_decode_append(
     int32_t max_context_len, const int32_t* work_items, int32_t n_items, void* workspace,
     size_t ws_bytes, int64_t* slots, kv_load_policy load_policy, hipStream_t stream);
 
+/* Bytes of the library's own split-K buffer used by
+ * kv_paged_attention_decode_append_noalloc, on each GPU: 32 MiB. */
+#define KV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* kv_paged_attention_decode_append without a workspace argument, for callers
+ * that cannot allocate device memory: code under stream or graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. The split-K partials
+ * go to a device buffer of KV_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on, from the first call there until the process ends
+ * (the call looks up its address once per device; it calls no hipMalloc,
+ * hipFree or other allocating routine). Arguments, checks, launches and
+ * results are those of kv_paged_attention_decode_append: bit-identical
+ * outputs, pools and slots for the same inputs. Sizes whose workspace
+ * (kv_paged_attention_workspace_bytes) exceeds KV_NOALLOC_SCRATCH_BYTES get
+ * KV_ERR_INVALID before anything is launched; e.g. 128 sequences x 64 query
+ * heads with 768-token partitions fit contexts up to 5,376 tokens. Every call
+ * on one GPU shares that GPU's buffer: calls that may overlap on one GPU
+ * (different streams, no ordering between them) race and must not be made;
+ * calls in one stream are ordered. The buffer needs no clearing between
+ * calls (each call writes every partial it reads). */
+kv_status kv_paged_attention_decode_append_noalloc(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t S,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
+    int32_t max_context_len, const int32_t* work_items, int32_t n_items, int64_t* slots,
+    kv_load_policy load_policy, hipStream_t stream);
+
 /* The decode step of kv_paged_attention_decode_append for a batch whose
  * sequences all share their first shared_tokens positions ([1] "Memory
  * sharing": the same physical blocks, reached through the same first

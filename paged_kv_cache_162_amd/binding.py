@@ -95,6 +95,10 @@ _SIGS = {
     "kv_paged_attention_decode_append": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
                                                    i32, i32, i32, i32, f32, C.c_int, i32, i32,
                                                    vp, i32, vp, C.c_size_t, vp, C.c_int, vp]),
+    "kv_paged_attention_decode_append_noalloc": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                                           i32, i32, i32, i32, i32, i32, f32,
+                                                           C.c_int, i32, i32, vp, i32, vp,
+                                                           C.c_int, vp]),
     "kv_paged_attention_shared_aux_bytes": (C.c_size_t, [i32, i32, i32, i32, i32]),
     "kv_paged_attention_decode_append_shared": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32,
                                                           i32, i32, i32, i32, i32, f32, C.c_int,
@@ -498,6 +502,37 @@ def kv_paged_attention_decode_append(out, q, k_new, v_new, k_pool, v_pool, block
         0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
         _dev(slots, "slots", torch.int64), int(load_policy), _stream(stream)),
         "kv_paged_attention_decode_append")
+
+
+KV_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def kv_paged_attention_decode_append_noalloc(out, q, k_new, v_new, k_pool, v_pool, block_tables,
+                                             context_lens, scale: float, max_context_len: int,
+                                             slots, partition_size: int = 0, work_items=None,
+                                             load_policy: int = KV_LOADS_STREAM,
+                                             stream=None) -> None:
+    """kv_paged_attention_decode_append with the split-K partials in the library's own
+    per-GPU buffer (KV_NOALLOC_SCRATCH_BYTES) instead of a caller workspace."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_pool.shape
+    if D2 != D or tuple(out.shape) != (S, Hq, D) or block_tables.shape[0] != S \
+            or context_lens.numel() != S or q.dtype != k_pool.dtype or v_pool.shape != k_pool.shape \
+            or tuple(k_new.shape) != (S, Hkv, D) or k_new.shape != v_new.shape \
+            or k_new.dtype != k_pool.dtype or slots.numel() != S:
+        raise KVError(KV_ERR_INVALID, "kv_paged_attention_decode_append_noalloc",
+                      "shape/dtype mismatch")
+    _check(lib.kv_paged_attention_decode_append_noalloc(
+        _dev(out, "out", torch.float32), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, B, NB, float(scale),
+        dtype_code(q), partition_size, max_context_len,
+        None if work_items is None else _dev(work_items, "work_items", torch.int32),
+        0 if work_items is None else work_items.shape[0], _dev(slots, "slots", torch.int64),
+        int(load_policy), _stream(stream)),
+        "kv_paged_attention_decode_append_noalloc")
 
 
 def kv_paged_attention_shared_aux_bytes(S: int, num_q_heads: int, num_kv_heads: int,

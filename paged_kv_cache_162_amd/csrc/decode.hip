@@ -28,6 +28,8 @@
 // Softmax runs in base 2: scores are multiplied by scale*log2(e) and
 // exponentiated with v_exp_f32; the result is the same softmax.
 
+#include <mutex>
+
 #include "device_common.h"
 
 using namespace pagedkv::dev;
@@ -977,6 +979,38 @@ kv_status launch_for_block_size(const DecodeParams& prm, kv_dtype dtype, int hea
                     : launch_decode_kernel<32, NT>(prm, dtype, head_dim, G, stream);
 }
 
+// ---- the split-K partials of kv_paged_attention_decode_append_noalloc -------
+// Callers that cannot allocate device memory get the library's own buffer: a
+// file-scope device array, one copy per GPU, held until the process ends.
+// Host code never passes the array's name to a kernel (in host code it stands
+// for a host-side shadow, not the device memory); it asks the runtime for the
+// array's address on the current device once and keeps it per device.
+constexpr size_t kNoAllocScratchBytes = KV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+kv_status scratch_on_current_device(void** out, const char* who) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KV_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KV_ERR_UNSUPPORTED, "%s: device %d (at most %d devices)", who, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(KV_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", who, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1164,6 +1198,36 @@ kv_status kv_paged_attention_decode_append(
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                      partition_size, max_context_len, work_items, n_items, workspace, ws_bytes,
                      k_new, v_new, slots, load_policy, stream);
+}
+
+kv_status kv_paged_attention_decode_append_noalloc(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t S,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
+    int32_t max_context_len, const int32_t* work_items, int32_t n_items, int64_t* slots,
+    kv_load_policy load_policy, hipStream_t stream) {
+  pagedkv::clear_error();
+  const char* who = "kv_paged_attention_decode_append_noalloc";
+  const size_t need = kv_paged_attention_workspace_bytes(S, num_q_heads, num_kv_heads, head_dim,
+                                                         max_context_len, partition_size);
+  if (need > kNoAllocScratchBytes)
+    return fail(KV_ERR_INVALID,
+                "%s: these sizes need %zu bytes of split-K partials and the built-in buffer "
+                "holds %zu; use kv_paged_attention_decode_append with a workspace",
+                who, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0 && S > 0) {
+    const kv_status st = scratch_on_current_device(&ws, who);
+    if (st != KV_OK) return st;
+  }
+  // the decode writes every partial before the merge reads it: nothing to clear
+  return kv_paged_attention_decode_append(out, q, k_new, v_new, k_pool, v_pool, block_tables,
+                                          max_blocks, context_lens, S, num_q_heads, num_kv_heads,
+                                          head_dim, block_size, num_blocks, scale, dtype,
+                                          partition_size, max_context_len, work_items, n_items,
+                                          ws, ws ? kNoAllocScratchBytes : 0, slots, load_policy,
+                                          stream);
 }
 
 size_t kv_paged_attention_shared_aux_bytes(int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
