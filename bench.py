@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="capture each replica's step in a HIP graph and time graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only the chosen workload (the default run also times workloads "
+                         "1, 2, 4 and 5 and reports them under per_config)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--pmc-traffic", default="",
                     help="JSON file with the measured HBM traffic per decode call "
@@ -111,27 +114,27 @@ def copy_calibration(kv, torch):
     del k, v
 
 
-def copy_bandwidth(kv, torch, reps=10):
-    """Bytes read plus written per second by kv_copy_blocks on the calibration
-    buffers (256 MiB read and 256 MiB written per call): a measured ceiling for
-    HBM traffic on this GPU, reported beside the 8 TB/s peak."""
-    nb = 2 * CAL_PAIRS
-    k = torch.zeros(nb * CAL_BLOCK_BYTES, dtype=torch.uint8, device="cuda")
-    v = torch.zeros_like(k)
-    pairs = torch.stack([torch.arange(CAL_PAIRS, dtype=torch.int32),
-                         torch.arange(CAL_PAIRS, 2 * CAL_PAIRS, dtype=torch.int32)], 1).cuda()
+def hbm_read_ceiling(kv, torch, reps=20):
+    """Measured HBM read ceiling: kv_hbm_read_probe (non-temporal 16-byte loads,
+    the decode kernels' K/V load policy) streaming a 1 GiB buffer, far past the
+    256 MB last-level cache; bytes read per second."""
+    nbytes = 1 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.random_(0, 256)
+    wg = 8192
+    sink = torch.empty(wg, dtype=torch.int32, device="cuda")
     for _ in range(3):
-        kv.kv_copy_blocks([k], [v], pairs, nb, CAL_BLOCK_BYTES)
+        kv.kv_hbm_read_probe(buf, sink, wg)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
-        kv.kv_copy_blocks([k], [v], pairs, nb, CAL_BLOCK_BYTES)
+        kv.kv_hbm_read_probe(buf, sink, wg)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    del k, v
-    return 2 * 2 * CAL_PAIRS * CAL_BLOCK_BYTES / (ms * 1e-3) / 1e9
+    del buf, sink
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def _counter_rows(d):
@@ -212,36 +215,83 @@ def decode_alg_bytes(lens, S, Hq, Hkv, D, eb, B=16, kv_eb=None):
     return kv_bytes(lens, Hkv, D, kv_eb) + S * Hq * D * eb + S * Hq * D * 4 + nb * 4 + S * 4
 
 
-def cpu_baseline(w, seconds):
-    """The oracle, untouched, timed on this host on the same workload: the
-    whole decode (gather through the block table + fp64 attention) over all
-    sequences, repeated until `seconds` have elapsed (at most 50 passes)."""
+# The oracle baseline runs in worker processes started fresh (spawn: they never
+# touch the GPU); each builds the workload and the oracle's block tables once.
+_ORACLE = {}
+
+
+def _oracle_worker_init(cfg, block_size):
+    # one BLAS thread per worker (the parent's limit does not reach a spawned child)
     from threadpoolctl import threadpool_limits
+    _ORACLE["blas"] = threadpool_limits(limits=1)
     import oracle
     from oracle.block_manager import run_ops
-    bm = oracle.BlockManager(w.num_blocks, block_size=w.spec.block_size, free_order=w.free_order)
+    from workloads import make_workload
+    w = make_workload(cfg, block_size=block_size)
+    bm = oracle.BlockManager(w.num_blocks, block_size=block_size, free_order=w.free_order)
     h, _, _ = run_ops(bm, w.setup_ops + w.step_ops)
     tables, lens = bm.packed_tables([h[i] for i in range(w.S)])
+    _ORACLE.update(w=w, tables=tables, lens=lens)
+
+
+def _oracle_worker_run(seqs):
+    """The oracle, untouched, for every query head of the sequences `seqs`."""
+    import oracle
+    w, sp = _ORACLE["w"], _ORACLE["w"].spec
+    pairs = [(s, h) for s in seqs for h in range(sp.Hq)]
+    kw = dict(kv_dtype=sp.kv_dtype, k_scale=sp.k_scale, v_scale=sp.v_scale) if sp.kv_dtype else {}
+    t0 = time.perf_counter()
+    oracle.decode_attention(w.q, w.k_pool, w.v_pool, _ORACLE["tables"], _ORACLE["lens"], sp.scale,
+                            sp.dtype, block_size=sp.block_size, pairs=pairs, **kw)
+    return time.perf_counter() - t0
+
+
+def host_cores():
+    """Cores this process may run on, capped at the 16-core share a one-GPU machine gives."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_baseline(w, seconds):
+    """The oracle, untouched, on this host's cores: the whole decode (gather
+    through the block table + fp64 attention) of every sequence, split over one
+    worker process per core (sequences dealt out longest first to the least
+    loaded worker), passes repeated until `seconds` have elapsed (at most 50)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    from threadpoolctl import threadpool_limits
     sp = w.spec
+    cores = host_cores()
+    lens = w.context_lens.astype(np.int64)
+    chunks, load = [[] for _ in range(cores)], np.zeros(cores)
+    for s in np.argsort(-lens, kind="stable"):
+        c = int(np.argmin(load))
+        chunks[c].append(int(s))
+        load[c] += lens[s] + 1
+    chunks = [c for c in chunks if c]
     passes, t_total = 0, 0.0
+    # one BLAS thread per process: the workers are the parallelism
     with threadpool_limits(limits=1):
-        while passes < 50 and (passes == 0 or t_total < seconds):
-            t0 = time.perf_counter()
-            if sp.kv_dtype:
-                oracle.decode_attention(w.q, w.k_pool, w.v_pool, tables, lens, sp.scale, sp.dtype,
-                                        block_size=sp.block_size, kv_dtype=sp.kv_dtype,
-                                        k_scale=sp.k_scale, v_scale=sp.v_scale)
-            else:
-                oracle.decode_attention(w.q, w.k_pool, w.v_pool, tables, lens, sp.scale, sp.dtype,
-                                        block_size=sp.block_size)
-            t_total += time.perf_counter() - t0
-            passes += 1
+        # a worker that dies raises here instead of hanging the pool
+        with ProcessPoolExecutor(len(chunks), mp_context=mp.get_context("spawn"),
+                                 initializer=_oracle_worker_init,
+                                 initargs=(sp_cfg(w), sp.block_size)) as pool:
+            list(pool.map(_oracle_worker_run, [[c[0]] for c in chunks]))  # warm the workers
+            while passes < 50 and (passes == 0 or t_total < seconds):
+                t0 = time.perf_counter()
+                list(pool.map(_oracle_worker_run, chunks))
+                t_total += time.perf_counter() - t0
+                passes += 1
     per = t_total / passes
     kvb = kv_bytes(lens, sp.Hkv, sp.D, sp.kv_elem_bytes)
-    return {"value": round(kvb / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seqs_per_s": round(sp.S / per, 2), "seconds_per_pass": round(per, 3),
-            "sample": f"the whole workload ({sp.S} sequences x {sp.Hq} query heads), {passes} "
-                      f"pass(es), BLAS limited to 1 thread"}
+    return {"value": round(kvb / per / 1e9, 4), "unit": "GB/s", "cores": len(chunks),
+            "kind": "oracle", "seqs_per_s": round(sp.S / per, 2), "seconds_per_pass": round(per, 3),
+            "sample": f"the whole workload ({sp.S} sequences x {sp.Hq} query heads) per pass, "
+                      f"{passes} pass(es), sequences split over {len(chunks)} worker processes "
+                      f"with one BLAS thread each"}
+
+
+def sp_cfg(w):
+    return w.spec.cfg
 
 
 MAX_CONTEXT = 8192  # longest context the workloads allow: a contiguous allocator reserves it
@@ -453,44 +503,31 @@ def swap_bench(args, kv, torch):
 SWAP_TOKENS = 4096
 
 
-def main():
-    args = parse()
-    if args.pmc_parse:
-        kind = "prefill" if is_prefill(args.workload) else "decode"
-        out = args.pmc_out or os.path.join(ROOT, "profiles", f"{kind}_traffic_w{args.workload}.json")
-        pmc_parse(args.pmc_parse[0], args.pmc_parse[1], out, args.workload, args.partition)
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1 "
-                                   "(the kernels work on one GPU's share of the batch; "
-                                   "sharding across GPUs is not implemented)"}))
-        sys.exit(2)
-    import torch
-    from workloads import make_workload
-    lib_path = os.path.join(ROOT, "paged_kv_cache_162_amd", "libpagedkv.so")
-    if not os.path.exists(lib_path):
-        from paged_kv_cache_162_amd import build as b
-        b.build()
-    import paged_kv_cache_162_amd as kv
-    from paged_kv_cache_162_amd.session import DecodeSession
-    if args.swap:
-        swap_bench(args, kv, torch)
-        return
+TRAFFIC_NOTE = ("HBM bytes per decode call from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of "
+                "this kernel source, scaled by the counters' reading for a copy of known size "
+                "(profiles/decode_traffic_w{w}.json); null when the kernels changed since")
+# workloads timed beside the default one, each with its own bench line's numbers
+PER_CONFIG = (1, 2, 4, 5)
 
-    w = make_workload(args.workload, block_size=args.block_size)
+
+def run_decode(args, cfg, kv, torch, steps, warmup, primary):
+    """Time the decode step on workload `cfg`: K steps back to back over rotating pool
+    replicas (inputs resident in HBM), per-call event timing of the attention launches,
+    and, for the primary workload, the warm, cache-write and ceiling measurements.
+    Returns the numbers of the bench line."""
+    from paged_kv_cache_162_amd.session import DecodeSession
+    from workloads import make_workload
+    w = make_workload(cfg, block_size=args.block_size)
     sp = w.spec
-    if sp.chunk:
-        prefill_bench(args, w, kv, torch)
-        return
     dt = sp.dtype
     print(f"[bench] workload {sp.name}: S={sp.S} Hq={sp.Hq} Hkv={sp.Hkv} D={sp.D} {dt} "
           f"blocks={w.num_blocks} sum_ctx={int(w.context_lens.sum())} max_ctx={int(w.context_lens.max())}",
           file=sys.stderr, flush=True)
     kp, vp = to_dev(w.k_pool, sp.cache_dtype), to_dev(w.v_pool, sp.cache_dtype)
     sess = DecodeSession(k_pool=kp, v_pool=vp, num_q_heads=sp.Hq, free_order=w.free_order,
-                         partition_size=args.partition, use_plan=not args.no_plan,
-                         fused=not args.unfused, k_scale=sp.k_scale, v_scale=sp.v_scale,
-                         shared_prefix=not args.no_shared_prefix)
+                         partition_size=args.partition if primary else 0,
+                         use_plan=not args.no_plan, fused=not args.unfused, k_scale=sp.k_scale,
+                         v_scale=sp.v_scale, shared_prefix=not args.no_shared_prefix)
     values = {}
     if w.tail_k is not None:
         values = {s: (to_dev(w.tail_k[s], dt), to_dev(w.tail_v[s], dt)) for s in range(sp.S)}
@@ -503,12 +540,12 @@ def main():
     out = torch.empty((sp.S, sp.Hq, sp.D), dtype=torch.float32, device="cuda")
 
     pool_bytes = 2 * kp.numel() * kp.element_size()
-    R = args.replicas or max(1, int(np.ceil(1.0e9 / pool_bytes)))
+    R = (args.replicas if primary else 0) or max(1, int(np.ceil(1.0e9 / pool_bytes)))
     reps = [(kp, vp, q, kn, vn)]
     for _ in range(R - 1):
         reps.append((kp.clone(), vp.clone(), q.clone(), kn.clone(), vn.clone()))
     torch.cuda.synchronize()
-    if args.copy_calibration:
+    if primary and args.copy_calibration:
         copy_calibration(kv, torch)
 
     def one(k, events=None):
@@ -516,7 +553,7 @@ def main():
         sess.step(qq, kk, vv, out, sp.scale, k_pool=a, v_pool=b, decode_events=events)
 
     graphs = None
-    if args.graph:
+    if primary and args.graph:
         # one graph per replica; the step holds no memset nodes
         for k in range(R):
             one(k)
@@ -537,10 +574,10 @@ def main():
         else:
             one(k)
 
-    for k in range(args.warmup):
+    for k in range(warmup):
         run(k)
     torch.cuda.synchronize()
-    K = args.steps
+    K = steps
     # timed region: K whole steps back to back, nothing else on the stream
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -551,13 +588,45 @@ def main():
     torch.cuda.synchronize()
     step_ms = t_start.elapsed_time(t_end) / K
 
-    # per-call duration of the decode launch(es), events on the launch stream
+    # per-call duration of the attention launch(es), events on the launch stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for k in range(K):
         one(k, ev[k])
     torch.cuda.synchronize()
     dec_ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
     dec_avg = float(dec_ms.mean())
+
+    kvb = kv_bytes(lens, sp.Hkv, sp.D, sp.kv_elem_bytes)
+    if shared:
+        # the common prefix is read once for the batch, its table entries once
+        alg = (decode_alg_bytes(lens - shared, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes,
+                                args.block_size, sp.kv_elem_bytes)
+               + kv_bytes(np.array([shared]), sp.Hkv, sp.D, sp.kv_elem_bytes)
+               + shared // args.block_size * 4)
+        kv_read = kv_bytes(lens - shared, sp.Hkv, sp.D, sp.kv_elem_bytes) + \
+            kv_bytes(np.array([shared]), sp.Hkv, sp.D, sp.kv_elem_bytes)
+    else:
+        alg = decode_alg_bytes(lens, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes, args.block_size,
+                               sp.kv_elem_bytes)
+        kv_read = kvb
+    value = kvb / (step_ms * 1e-3) / 1e9
+    res = {
+        "workload": f"{sp.name}: {sp.description}", "ms_per_step": round(step_ms, 5),
+        "kv_gbs": round(value, 2),
+        # bytes the step actually reads: a shared prefix counts once
+        "pct_hbm_peak": round(100 * kv_read / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(sp.S / (step_ms * 1e-3), 1),
+        "decode_ms": round(dec_avg, 5), "decode_ms_median": round(float(np.median(dec_ms)), 5),
+        "partition_tokens": sess.step_partition, "shared_prefix_tokens": shared,
+        "steps": K, "warmup": warmup, "replicas_rotated": R,
+        "roofline_frac": round(alg / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    if shared:
+        res["logical_kv_gbs"] = round(value, 2)
+        res["read_kv_gbs"] = round(kv_read / (step_ms * 1e-3) / 1e9, 2)
+    if not primary:
+        sess.close()
+        return res
 
     # warm number: same buffers every step
     for k in range(10):
@@ -582,65 +651,29 @@ def main():
         cw[k][1].record()
     torch.cuda.synchronize()
     cache_write_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in cw]))
-    copy_gbs = copy_bandwidth(kv, torch)
+    del reps
+    torch.cuda.empty_cache()
+    read_gbs = hbm_read_ceiling(kv, torch)
 
-    kvb = kv_bytes(lens, sp.Hkv, sp.D, sp.kv_elem_bytes)
-    if shared:
-        # the common prefix is read once for the batch, its table entries once
-        alg = (decode_alg_bytes(lens - shared, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes,
-                                args.block_size, sp.kv_elem_bytes)
-               + kv_bytes(np.array([shared]), sp.Hkv, sp.D, sp.kv_elem_bytes)
-               + shared // args.block_size * 4)
-    else:
-        alg = decode_alg_bytes(lens, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes, args.block_size,
-                               sp.kv_elem_bytes)
-    value = kvb / (step_ms * 1e-3) / 1e9
-    achieved = alg / (dec_avg * 1e-3) / 1e9
     traffic = None
-    tpath = args.pmc_traffic or os.path.join(ROOT, "profiles", f"decode_traffic_w{args.workload}.json")
+    tpath = args.pmc_traffic or os.path.join(ROOT, "profiles", f"decode_traffic_w{cfg}.json")
     if os.path.exists(tpath):
         t = json.load(open(tpath))
         sources = SHARED_DECODE_SOURCES if shared else DECODE_SOURCES
         if t.get("kernel_source_digest") == kernel_source_digest(sources) and \
-                t.get("workload") == args.workload and args.partition == t.get("partition_arg"):
+                t.get("workload") == cfg and args.partition == t.get("partition_arg"):
             traffic = round(float(t["bytes_per_launch"]))
-
-    res = {
-        "metric": "paged decode attention KV GB/s (% of HBM peak) and seqs/s per config, 1 GPU",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dt,
-        "data": "synthetic",
-        "config": {
-            "workload": f"{sp.name}: {sp.description}",
-            "sequences": sp.S, "q_heads": sp.Hq, "kv_heads": sp.Hkv, "head_dim": sp.D,
-            "block_size": args.block_size, "partition_tokens": sess.step_partition,
-            "partition_choice": "given" if args.partition else "chosen from the batch's lengths",
-            "sum_context": int(lens.sum()), "max_context": int(lens.max()),
-            "kv_bytes_per_step": kvb, "replicas_rotated": R, "parallelism": "single GPU",
-            "fused_cache_write": not args.unfused, "hip_graph": bool(args.graph),
-            "kv_cache_dtype": sp.cache_dtype, "shared_prefix_tokens": shared,
-        },
-        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "seqs_per_s": round(sp.S / (step_ms * 1e-3), 1),
-        "decode_ms": round(dec_avg, 5),
-        "decode_ms_median": round(float(np.median(dec_ms)), 5),
-        "decode_kv_gbs": round(kvb / (dec_avg * 1e-3) / 1e9, 2),
+    achieved = alg / (dec_avg * 1e-3) / 1e9
+    res.update({
+        "sp": sp, "w": w, "value": value, "kvb": kvb, "memory": memory,
+        "warm_ms_per_step": round(warm_ms, 5), "warm_kv_gbs": round(kvb / (warm_ms * 1e-3) / 1e9, 2),
         "cache_write_ms": round(cache_write_ms, 5),
-        "copy_gbs": round(copy_gbs, 1),
-        "warm_ms_per_step": round(warm_ms, 5),
-        "warm_kv_gbs": round(kvb / (warm_ms * 1e-3) / 1e9, 2),
-        "kv_memory": memory,
+        "decode_kv_gbs": round(kvb / (dec_avg * 1e-3) / 1e9, 2),
+        "stream_read_gbs": round(read_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
+                     "traffic_source": TRAFFIC_NOTE.format(w=cfg),
                      "kernel": ("kv_paged_attention_decode_append_shared call: prefix attention "
                                 "once, then the tails' decode (+ split-K merge) folding it in"
                                 if shared else
@@ -649,7 +682,91 @@ def main():
                                  "kv_paged_attention_decode%s call: decode kernel + split-K merge")
                                 % ("_fp8" if sp.kv_dtype else "")),
                      "alg_bytes_per_launch": alg},
+    })
+    sess.close()
+    return res
+
+
+def main():
+    args = parse()
+    if args.pmc_parse:
+        kind = "prefill" if is_prefill(args.workload) else "decode"
+        out = args.pmc_out or os.path.join(ROOT, "profiles", f"{kind}_traffic_w{args.workload}.json")
+        pmc_parse(args.pmc_parse[0], args.pmc_parse[1], out, args.workload, args.partition)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1 "
+                                   "(the kernels work on one GPU's share of the batch; "
+                                   "sharding across GPUs is not implemented)"}))
+        sys.exit(2)
+    import torch
+    from workloads import make_workload
+    lib_path = os.path.join(ROOT, "paged_kv_cache_162_amd", "libpagedkv.so")
+    if not os.path.exists(lib_path):
+        from paged_kv_cache_162_amd import build as b
+        b.build()
+    import paged_kv_cache_162_amd as kv
+    if args.swap:
+        swap_bench(args, kv, torch)
+        return
+    if is_prefill(args.workload):
+        prefill_bench(args, make_workload(args.workload, block_size=args.block_size), kv, torch)
+        return
+
+    r = run_decode(args, args.workload, kv, torch, args.steps, args.warmup, primary=True)
+    sp, w = r.pop("sp"), r.pop("w")
+    res = {
+        "metric": "paged decode attention KV GB/s (% of HBM peak) and seqs/s per config, 1 GPU",
+        "value": round(r["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sp.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": r["workload"],
+            "sequences": sp.S, "q_heads": sp.Hq, "kv_heads": sp.Hkv, "head_dim": sp.D,
+            "block_size": args.block_size, "partition_tokens": r["partition_tokens"],
+            "partition_choice": "given" if args.partition else "chosen from the batch's lengths",
+            "sum_context": int(w.context_lens.sum()),
+            "max_context": int(w.context_lens.max()),
+            "kv_bytes_per_step": r["kvb"], "replicas_rotated": r["replicas_rotated"],
+            "parallelism": "single GPU", "fused_cache_write": not args.unfused,
+            "hip_graph": bool(args.graph), "kv_cache_dtype": sp.cache_dtype,
+            "shared_prefix_tokens": r["shared_prefix_tokens"],
+        },
+        "pct_hbm_peak": r["pct_hbm_peak"],
+        "seqs_per_s": r["seqs_per_s"],
+        "decode_ms": r["decode_ms"],
+        "decode_ms_median": r["decode_ms_median"],
+        "decode_kv_gbs": r["decode_kv_gbs"],
+        "cache_write_ms": r["cache_write_ms"],
+        "stream_read_gbs": r["stream_read_gbs"],
+        "warm_ms_per_step": r["warm_ms_per_step"],
+        "warm_kv_gbs": r["warm_kv_gbs"],
+        "kv_memory": r["memory"],
+        "roofline": r["roofline"],
     }
+    if "logical_kv_gbs" in r:
+        res["logical_kv_gbs"], res["read_kv_gbs"] = r["logical_kv_gbs"], r["read_kv_gbs"]
+    if not args.no_per_config and args.workload == 3 and not (args.partition or args.graph
+                                                              or args.unfused or args.no_plan):
+        per = {"3": {k: r[k] for k in ("workload", "ms_per_step", "kv_gbs", "pct_hbm_peak",
+                                          "seqs_per_s", "partition_tokens", "decode_ms",
+                                          "roofline_frac", "steps")}}
+        for cfg in PER_CONFIG:
+            torch.cuda.empty_cache()
+            pr = run_decode(args, cfg, kv, torch, min(args.steps, 100), min(args.warmup, 10),
+                            primary=False)
+            per[str(cfg)] = pr
+            print(f"[bench] workload {cfg}: {pr['ms_per_step'] * 1e3:.1f} us per step, "
+                  f"{pr['pct_hbm_peak']}% of HBM peak", file=sys.stderr, flush=True)
+        res["per_config"] = per
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -256,6 +256,16 @@ kv_status kv_swap_in_blocks(void* const* k_pools, void* const* v_pools, int32_t 
                             const int32_t* block_ids, int32_t n, int32_t num_blocks,
                             size_t block_bytes, const void* host_buffer, hipStream_t stream);
 
+/* Measurement utility, not a step of the method: reads `bytes` (a multiple of
+ * 16) of device memory at src (16-byte aligned) with the decode kernels'
+ * non-temporal 16-byte loads, `workgroups` workgroups of 256 threads striding
+ * over the buffer, and writes one checksum word per workgroup to sink (device
+ * uint32 [workgroups]). Its bytes per second over a buffer far larger than
+ * the last-level cache are the HBM read rate a streaming kernel reaches on the
+ * device, the ceiling beside the published peak. */
+kv_status kv_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                            hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Device: paged decode attention ([1], "The PagedAttention kernel"; [2],
  * "The Custom CUDA Kernel"; [3], "The kernel change").

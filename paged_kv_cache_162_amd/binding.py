@@ -126,6 +126,7 @@ _SIGS = {
     "kv_paged_attention_choose_shared_prefix": (i32, [P_i32, i32, i32, P_i32, i32, i32, i32, i32,
                                                       C.c_int]),
     "kv_paged_attention_choose_load_policy": (C.c_int, [vp, i32]),
+    "kv_hbm_read_probe": (C.c_int, [vp, C.c_size_t, vp, i32, vp]),
     "kv_last_error": (C.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -423,6 +424,13 @@ def kv_swap_in_blocks(k_pools: List, v_pools: List, block_ids, num_blocks: int,
     """Copy pinned `host` [n][layers][2][block_bytes] back into blocks."""
     _swap(lib.kv_swap_in_blocks, "kv_swap_in_blocks", k_pools, v_pools, block_ids,
           num_blocks, block_bytes, host, stream)
+
+
+def kv_hbm_read_probe(src, sink, workgroups: int, stream=None) -> None:
+    """Stream-read every byte of device tensor src; sink: device uint32/int32 [workgroups]."""
+    _check(lib.kv_hbm_read_probe(_dev(src, "src"), src.numel() * src.element_size(),
+                                 _dev(sink, "sink"), workgroups, _stream(stream)),
+           "kv_hbm_read_probe")
 
 
 def kv_paged_attention_plan(context_lens_host, partition_size: int = 0, num_kv_heads: int = 0,

@@ -222,6 +222,22 @@ kv_status swap_blocks(const char* who, void* const* k_pools, void* const* v_pool
 
 }  // namespace
 
+// HBM read ceiling for the measurements: every workgroup streams 16-byte
+// chunks of the buffer with non-temporal loads (the decode kernels' K/V load
+// policy) in a grid-stride loop and folds them into one word per thread, and
+// thread 0 stores its word per workgroup so the loads are not dead code.
+constexpr int kProbeThreads = 256;
+__global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const uint4* __restrict__ src,
+                                                                       int64_t n16, uint32_t* sink) {
+  uint32_t acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x; i < n16; i += stride) {
+    const uint4 v = load_kv<true>(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (threadIdx.x == 0) sink[blockIdx.x] = acc;
+}
+
 extern "C" {
 
 kv_status kv_slot_mapping(const int32_t* tables, int32_t num_rows, int32_t max_blocks,
@@ -371,6 +387,19 @@ kv_status kv_quantize_fp8(const void* src, void* dst, int64_t n, kv_dtype dtype,
   auto kern = dtype == KV_BF16 ? quantize_fp8_kernel<KV_BF16> : quantize_fp8_kernel<KV_F16>;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<const uint4*>(src), static_cast<uint2*>(dst), n8, scale);
+  return launch_status(who);
+}
+
+kv_status kv_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                            hipStream_t stream) {
+  pagedkv::clear_error();
+  const char* who = "kv_hbm_read_probe";
+  if (bytes % 16 != 0 || workgroups <= 0)
+    return fail(KV_ERR_INVALID, "%s: bytes a multiple of 16, workgroups > 0", who);
+  if (bytes == 0) return KV_OK;
+  if (!src || !sink || !aligned16(src)) return fail(KV_ERR_INVALID, "%s: null or misaligned", who);
+  hipLaunchKernelGGL(hbm_read_probe_kernel, dim3((unsigned)workgroups), dim3(kProbeThreads), 0,
+                     stream, static_cast<const uint4*>(src), (int64_t)(bytes / 16), sink);
   return launch_status(who);
 }
 
