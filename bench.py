@@ -77,10 +77,10 @@ CAL_PAIRS = 4096            # block pairs copied by the calibration dispatch
 CAL_BLOCK_BYTES = 32768     # bytes per block and pool (K and V each)
 
 
-DECODE_SOURCES = ("decode.hip", "device_common.h")
+DECODE_SOURCES = ("decode.hip", "decode_kernels.h", "decode_variants.hip", "device_common.h")
 PREFILL_SOURCES = ("prefill.hip", "device_common.h")
 # a shared-prefix decode step runs the prefill kernel too
-SHARED_DECODE_SOURCES = ("decode.hip", "prefill.hip", "device_common.h")
+SHARED_DECODE_SOURCES = DECODE_SOURCES + ("prefill.hip",)
 
 
 def kernel_source_digest(sources=DECODE_SOURCES):

@@ -18,9 +18,12 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedkv.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = [os.path.join(CSRC, "host_pool.cpp"), os.path.join(CSRC, "plan.cpp"),
-           os.path.join(CSRC, "cache.hip"), os.path.join(CSRC, "decode.hip"),
-           os.path.join(CSRC, "prefill.hip")]
+# (source, extra flags, object tag): decode_variants.hip is compiled once per
+# block size and K/V load policy, so the decode kernels build in parallel
+SOURCES = ([(os.path.join(CSRC, f), [], f) for f in
+            ("host_pool.cpp", "plan.cpp", "cache.hip", "decode.hip", "prefill.hip")] +
+           [(os.path.join(CSRC, "decode_variants.hip"), [f"-DPAGEDKV_BS={bs}", f"-DPAGEDKV_NT={nt}"],
+             f"decode_variants_b{bs}_nt{nt}") for bs in (8, 16, 32) for nt in (0, 1)])
 ARCH = os.environ.get("PAGEDKV_ARCH", "gfx950")
 # the host pass warns that it does not know the packed-fp32 feature
 _NOISE = "is not a recognized feature for this target"
@@ -44,7 +47,7 @@ def _run(cmd: list, verbose: bool) -> str:
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if _NOISE not in l)
     if res.returncode != 0:
         sys.stderr.write(msgs + "\n")
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}: {cmd[-1]}")
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}: {' '.join(cmd[-4:])}")
     return msgs
 
 
@@ -52,8 +55,9 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link paged_kv_cache_162_amd/libpagedkv.so."""
     os.makedirs(OBJDIR, exist_ok=True)
     tag = "%d" % os.getpid()
-    objs = [os.path.join(OBJDIR, os.path.basename(s) + "." + tag + ".o") for s in SOURCES]
-    cmds = [[hipcc()] + _flags() + ["-c", "-o", o, s] for s, o in zip(SOURCES, objs)]
+    objs = [os.path.join(OBJDIR, name + "." + tag + ".o") for _, _, name in SOURCES]
+    cmds = [[hipcc()] + _flags() + extra + ["-c", "-o", o, src]
+            for (src, extra, _), o in zip(SOURCES, objs)]
     jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     try:
         with ThreadPoolExecutor(jobs) as ex:
