@@ -279,8 +279,9 @@ kv_status kv_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int32
  * Item i becomes workgroups i*num_kv_heads .. i*num_kv_heads + num_kv_heads - 1,
  * which the hardware deals to compute units in turn, so items i and i + T,
  * T = num_cus / gcd(num_kv_heads, num_cus), share compute units; the sorted
- * items go out in rows of T with every other row reversed, which evens out
- * the K/V bytes each compute unit streams. num_kv_heads or num_cus <= 0:
+ * items go out in rows with every other row reversed, which evens out the
+ * K/V bytes each compute unit streams: rows of 2T when num_kv_heads divides
+ * num_cus, of T otherwise (the lengths that measured fastest). num_kv_heads or num_cus <= 0:
  * plain longest-first order. num_cus is the device's compute-unit count
  * (hipDeviceAttributeMultiprocessorCount, 256 on MI355X).
  * items_out: host int32 [cap][2] receiving (sequence, partition) pairs;

@@ -332,9 +332,9 @@ def test_work_plan_lists_every_partition_once(kv):
     sizes = _plan_sizes(lens, items, 512)
     assert sizes == sorted(sizes, reverse=True)
     # placement model: the longest-first list in rows of T = num_cus / gcd(heads, num_cus),
-    # every other row reversed
-    for hkv, cus in ((2, 8), (3, 8), (8, 256), (5, 4)):
-        T = cus // math.gcd(hkv, cus)
+    # twice that when the heads divide num_cus, every other row reversed
+    for hkv, cus in ((2, 8), (3, 8), (8, 256), (5, 4), (2, 2), (40, 256)):
+        T = cus // math.gcd(hkv, cus) * (2 if cus % hkv == 0 else 1)
         items = kv.kv_paged_attention_plan(lens, 512, hkv, cus)
         assert sorted(map(tuple, items)) == want
         base = sorted(_plan_sizes(lens, items, 512), reverse=True)
