@@ -555,10 +555,11 @@ kv_status kv_quantize_fp8(const void* src, void* dst, int64_t n, kv_dtype dtype,
 /* kv_paged_attention_decode over fp8 pools: the attention of the cache
  * values value(code) * k_scale (K) and value(code) * v_scale (V), i.e. the
  * same definition on the dequantised cache. q is [S][num_q_heads][head_dim]
- * of `dtype` (f16 or bf16); head_dim 128; group sizes 1..16; block sizes 8,
- * 16, 32. Each code is widened exactly to the query's type and the MFMA path
- * runs as for 16-bit pools; k_scale is folded into the score scale and
- * v_scale into the output. Other arguments, checks and workspace as for
+ * of `dtype` (f16 or bf16); head_dim 64 or 128; group sizes 1..16; block
+ * sizes 8, 16, 32. Each code is widened exactly to the query's type; at
+ * head_dim 128 the MFMA path runs as for 16-bit pools, at head_dim 64 the
+ * vector-ALU path. k_scale is folded into the score scale and v_scale into
+ * the output. Other arguments, checks and workspace as for
  * kv_paged_attention_decode. */
 kv_status kv_paged_attention_decode_fp8(float* out, const void* q, const void* k_pool,
                                         const void* v_pool, const int32_t* block_tables,

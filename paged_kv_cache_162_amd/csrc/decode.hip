@@ -55,9 +55,9 @@ kv_status launch_for_block_size(const DecodeParams& prm, kv_dtype dtype, int hea
                                 bool kv8, hipStream_t stream) {
   const int bs = prm.block_size;
   if (kv8)
-    return bs == 8    ? launch_decode_kernel_fp8<8, NT>(prm, dtype, G, stream)
-           : bs == 16 ? launch_decode_kernel_fp8<16, NT>(prm, dtype, G, stream)
-                      : launch_decode_kernel_fp8<32, NT>(prm, dtype, G, stream);
+    return bs == 8    ? launch_decode_kernel_fp8<8, NT>(prm, dtype, head_dim, G, stream)
+           : bs == 16 ? launch_decode_kernel_fp8<16, NT>(prm, dtype, head_dim, G, stream)
+                      : launch_decode_kernel_fp8<32, NT>(prm, dtype, head_dim, G, stream);
   return bs == 8    ? launch_decode_kernel<8, NT>(prm, dtype, head_dim, G, stream)
          : bs == 16 ? launch_decode_kernel<16, NT>(prm, dtype, head_dim, G, stream)
                     : launch_decode_kernel<32, NT>(prm, dtype, head_dim, G, stream);
@@ -148,8 +148,9 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
   if (kv8) {
     if (dtype != KV_F16 && dtype != KV_BF16)
       return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode_fp8: queries must be f16 or bf16");
-    if (head_dim != 128)
-      return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode_fp8: head_dim %d (128)", head_dim);
+    if (head_dim != 64 && head_dim != 128)
+      return fail(KV_ERR_UNSUPPORTED, "kv_paged_attention_decode_fp8: head_dim %d (64 or 128)",
+                  head_dim);
     if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !std::isfinite(k_scale) ||
         !std::isfinite(v_scale))
       return fail(KV_ERR_INVALID, "kv_paged_attention_decode_fp8: scales must be finite and > 0");

@@ -409,8 +409,11 @@ __global__ __launch_bounds__(kMergeThreads) void splitk_merge_kernel(DecodeParam
 // 16-token block takes IPB loads. Dot products are finished with DPP row
 // reductions. Each group of LPR lanes keeps its own online softmax over the
 // tokens it reads; the groups are merged with cross-lane shuffles at the end.
+// With an fp8 cache (KV8; DT is then the query's 16-bit type) a lane loads the
+// 8 codes of the same 8 elements (8 bytes) and widens them exactly to DT; the
+// K scale is folded into the score scale and the V scale into the result.
 // ============================================================================
-template <int DT, int D, int GMAX, int BS, bool NT, bool PRE = false>
+template <int DT, int D, int GMAX, int BS, bool NT, bool PRE = false, bool KV8 = false>
 __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   constexpr int EB = DT == KV_F32 ? 4 : 2;
   constexpr int EPL = 16 / EB;           // elements per lane chunk
@@ -418,6 +421,10 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   constexpr int TPI = 64 / LPR;          // rows per wave-wide load
   constexpr int IPB = kTile / TPI;       // loads per 16-token tile
   static_assert(LPR == 8 || LPR == 16 || LPR == 32, "unsupported row width");
+  static_assert(!KV8 || (DT != KV_F32 && !PRE), "fp8 cache: 16-bit queries, plain step");
+  // a lane's chunk of a pool row: 16 bytes of 16-bit/fp32 elements, or the
+  // 8 codes of the same 8 elements
+  typedef typename std::conditional<KV8, uint2, uint4>::type Raw;
 
   const int lane = threadIdx.x;
   const int u = blockIdx.x;
@@ -443,8 +450,15 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     // order within the lane makes that load return the new values
     const size_t src = ((size_t)w.s * p.Hkv + w.h) * LPR + c;
     const size_t dst = tile_row<BS>(p, w.h, staged, nblk - 1, nt.row, LPR) + c;
-    static_cast<uint4*>(p.k_pool_w)[dst] = static_cast<const uint4*>(p.k_new)[src];
-    static_cast<uint4*>(p.v_pool_w)[dst] = static_cast<const uint4*>(p.v_new)[src];
+    const uint4 kn = static_cast<const uint4*>(p.k_new)[src];
+    const uint4 vn = static_cast<const uint4*>(p.v_new)[src];
+    if constexpr (KV8) {  // quantised: the 8 codes of the lane's 8 elements
+      static_cast<uint2*>(p.k_pool_w)[dst] = e4m3x8_from16<DT>(kn, p.k_scale);
+      static_cast<uint2*>(p.v_pool_w)[dst] = e4m3x8_from16<DT>(vn, p.v_scale);
+    } else {
+      static_cast<uint4*>(p.k_pool_w)[dst] = kn;
+      static_cast<uint4*>(p.v_pool_w)[dst] = vn;
+    }
   }
 
   // query chunk of every head in the group, pre-scaled into base-2 logits
@@ -472,10 +486,10 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
   }
 
-  const uint4* kbase = static_cast<const uint4*>(p.k_pool);
-  const uint4* vbase = static_cast<const uint4*>(p.v_pool);
+  const Raw* kbase = static_cast<const Raw*>(p.k_pool);
+  const Raw* vbase = static_cast<const Raw*>(p.v_pool);
 
-  auto load = [&](int j, uint4* ku, uint4* vu) {
+  auto load = [&](int j, Raw* ku, Raw* vu) {
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
       const size_t at = tile_row<BS>(p, w.h, staged, j, r + TPI * i, LPR) + c;
@@ -484,14 +498,19 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     }
   };
 
-  auto compute = [&](int jb, const uint4* ku, uint4* vu) {
+  auto compute = [&](int jb, const Raw* ku, const Raw* vu) {
     const int valid = t1 - (t0 + jb * kTile);  // live tokens in this tile (>= 1)
     const bool full = valid >= kTile;
     float kf[IPB][EPL], vf[IPB][EPL];
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
-      unpack16<DT>(ku[i], kf[i]);
-      unpack16<DT>(vu[i], vf[i]);
+      if constexpr (KV8) {
+        unpack16<DT>(e4m3x8_widen<DT>(ku[i].x, ku[i].y), kf[i]);
+        unpack16<DT>(e4m3x8_widen<DT>(vu[i].x, vu[i].y), vf[i]);
+      } else {
+        unpack16<DT>(ku[i], kf[i]);
+        unpack16<DT>(vu[i], vf[i]);
+      }
     }
     if (!full) {
 #pragma unroll
@@ -541,7 +560,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   // unconditionally (a load under a branch makes the compiler wait for every
   // outstanding load at the join); the last one or two blocks are peeled.
   {
-    uint4 ka[IPB], va[IPB], kb[IPB], vb[IPB];
+    Raw ka[IPB], va[IPB], kb[IPB], vb[IPB];
     const int last = nblk - 1;
     load(0, ka, va);
     int jb = 0;
@@ -583,8 +602,13 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   if (r == 0) {
 #pragma unroll
     for (int g = 0; g < GMAX; ++g)
-      if (g < p.G)
+      if (g < p.G) {
+        if constexpr (KV8) {  // the V scale multiplies the (partial) output
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[g][e] *= p.v_scale;
+        }
         store_result<PRE>(p, w, nps, g, c * EPL, acc[g], EPL, m[g], l[g], c == 0, bad, D);
+      }
   }
 }
 
@@ -900,17 +924,19 @@ kv_status launch_decode(Kernel kernel, const DecodeParams& prm, hipStream_t st) 
   return launch_status("kv_paged_attention_decode");
 }
 
-template <int DT, int D, int BS, bool NT>
+template <int DT, int D, int BS, bool NT, bool KV8 = false>
 kv_status launch_valu(const DecodeParams& prm, int gmax, hipStream_t st) {
   switch (gmax) {
-    case 1: return launch_decode(decode_valu_kernel<DT, D, 1, BS, NT>, prm, st);
-    case 2: return launch_decode(decode_valu_kernel<DT, D, 2, BS, NT>, prm, st);
-    case 4: return launch_decode(decode_valu_kernel<DT, D, 4, BS, NT>, prm, st);
-    case 8: return launch_decode(decode_valu_kernel<DT, D, 8, BS, NT>, prm, st);
-    case 16: return launch_decode(decode_valu_kernel<DT, D, 16, BS, NT>, prm, st);
+    case 1: return launch_decode(decode_valu_kernel<DT, D, 1, BS, NT, false, KV8>, prm, st);
+    case 2: return launch_decode(decode_valu_kernel<DT, D, 2, BS, NT, false, KV8>, prm, st);
+    case 4: return launch_decode(decode_valu_kernel<DT, D, 4, BS, NT, false, KV8>, prm, st);
+    case 8: return launch_decode(decode_valu_kernel<DT, D, 8, BS, NT, false, KV8>, prm, st);
+    case 16: return launch_decode(decode_valu_kernel<DT, D, 16, BS, NT, false, KV8>, prm, st);
     default: return fail(KV_ERR_UNSUPPORTED, "decode: group size");
   }
 }
+
+inline int group_bucket(int G) { return G == 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16; }
 
 // The decode kernel for one block size: MFMA for grouped 16-bit heads of
 // dimension 128, vector ALUs otherwise.
@@ -943,7 +969,7 @@ kv_status launch_decode_kernel(const DecodeParams& prm, kv_dtype dtype, int head
                ? launch_decode(decode_mfma_kernel<KV_BF16, false, R, BS, false, NT>, prm, st)
                : launch_decode(decode_mfma_kernel<KV_F16, false, R, BS, false, NT>, prm, st);
   }
-  const int gmax = G == 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
+  const int gmax = group_bucket(G);
   if (dtype == KV_F32)
     return head_dim == 64 ? launch_valu<KV_F32, 64, BS, NT>(prm, gmax, st)
                           : launch_valu<KV_F32, 128, BS, NT>(prm, gmax, st);
@@ -954,12 +980,15 @@ kv_status launch_decode_kernel(const DecodeParams& prm, kv_dtype dtype, int head
                         : launch_decode(decode_valu_kernel<KV_BF16, 128, 1, BS, NT>, prm, st);
 }
 
-// fp8 cache: the MFMA kernel for every group size (1..16), head_dim 128,
-// f16 or bf16 queries.
+// fp8 cache, f16 or bf16 queries: the MFMA kernel for every group size
+// (1..16) at head_dim 128, the vector-ALU kernel at head_dim 64.
 template <int BS, bool NT>
-kv_status launch_decode_kernel_fp8(const DecodeParams& prm, kv_dtype dtype, int G,
+kv_status launch_decode_kernel_fp8(const DecodeParams& prm, kv_dtype dtype, int head_dim, int G,
                                    hipStream_t st) {
   constexpr int R = kDecodeRing8;
+  if (head_dim == 64)
+    return dtype == KV_BF16 ? launch_valu<KV_BF16, 64, BS, NT, true>(prm, group_bucket(G), st)
+                            : launch_valu<KV_F16, 64, BS, NT, true>(prm, group_bucket(G), st);
   if (G <= 8)
     return dtype == KV_BF16
                ? launch_decode(decode_mfma_kernel<KV_BF16, true, R, BS, true, NT>, prm, st)
@@ -975,7 +1004,7 @@ kv_status launch_decode_kernel_fp8(const DecodeParams& prm, kv_dtype dtype, int 
   EXTERN template kv_status launch_decode_kernel<BS, NT>(const DecodeParams&, kv_dtype, int, \
                                                          int, hipStream_t);              \
   EXTERN template kv_status launch_decode_kernel_fp8<BS, NT>(const DecodeParams&, kv_dtype, \
-                                                             int, hipStream_t);
+                                                             int, int, hipStream_t);
 
 }  // namespace decode
 }  // namespace pagedkv

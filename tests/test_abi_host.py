@@ -379,7 +379,8 @@ def test_fp8_entry_points_validate_on_the_host(kv):
         k.get("pol", kv.KV_LOADS_STREAM), None)
     assert call(ks=0.0) == kv.KV_ERR_INVALID
     assert call(vs=float("nan")) == kv.KV_ERR_INVALID
-    assert call(D=64) == kv.KV_ERR_UNSUPPORTED
+    assert call(D=96) == kv.KV_ERR_UNSUPPORTED
+    assert call(D=64) == kv.KV_ERR_INVALID        # supported: the null pointers are what fails
     assert call(dt=kv.KV_F32) == kv.KV_ERR_UNSUPPORTED
     assert call() == kv.KV_ERR_INVALID            # null pointers
     assert call(S=0) == kv.KV_OK

@@ -116,22 +116,65 @@ def gpu_decode_fp8(q, kp, vp, tab, lens, scale, ks, vs, dt, partition_size=0, pl
     return out.cpu().numpy()
 
 
-SHAPES = [(dt, G, B) for dt in ("bf16", "f16") for G in (1, 2, 4, 8, 16) for B in (8, 16, 32)]
+SHAPES = [(dt, G, B, D) for D in (128, 64) for dt in ("bf16", "f16") for G in (1, 2, 4, 8, 16)
+          for B in (8, 16, 32)]
 
 
-@pytest.mark.parametrize("dt,G,B", SHAPES)
-def test_decode_fp8_against_oracle(dt, G, B):
-    rng = np.random.default_rng(700 + SHAPES.index((dt, G, B)))
+@pytest.mark.parametrize("dt,G,B,D", SHAPES)
+def test_decode_fp8_against_oracle(dt, G, B, D):
+    """Head dimension 128 runs the MFMA kernel, 64 the vector-ALU kernel."""
+    rng = np.random.default_rng(700 + SHAPES.index((dt, G, B, D)))
     lens = [1, 15, 16, 17, 33, 100, 511, 512, 513, 700]
-    Hkv, D = 2, 128
+    Hkv = 2
     q, kp, vp, tab, cl = fp8_case(rng, lens, G * Hkv, Hkv, D, dt, B=B)
     scale, ks, vs = float(np.float32(1 / np.sqrt(D))), 0.07, 0.013
     ref = oracle.decode_attention(q, kp, vp, tab, cl, scale, dt, block_size=B, kv_dtype="e4m3",
                                   k_scale=ks, v_scale=vs)
     for ps, plan in ((0, True), (0, False), (64, True), (32, False)):
-        log(f"[gpu] decode fp8 {dt} G={G} B={B} partition={ps} plan={plan}")
+        log(f"[gpu] decode fp8 {dt} G={G} B={B} D={D} partition={ps} plan={plan}")
         got = gpu_decode_fp8(q, kp, vp, tab, cl, scale, ks, vs, dt, ps, plan=plan)
-        check_attention(got.reshape(-1, D), ref.reshape(-1, D), dt, f"fp8 {dt} G={G} B={B} ps={ps}")
+        check_attention(got.reshape(-1, D), ref.reshape(-1, D), dt,
+                        f"fp8 {dt} G={G} B={B} D={D} ps={ps}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_decode_append_fp8_against_oracle(D, G):
+    """The fused step over fp8 pools: each sequence's new token is quantised
+    into its last position (pools and slots bit exact against the oracle's
+    write), then attention over the updated cache within tolerance."""
+    kv = kvlib()
+    rng = np.random.default_rng(790 + D + G)
+    dt, Hkv, B = "bf16", 2, 16
+    lens = [1, 16, 17, 40, 512, 513, 1500]
+    q, kp, vp, tab, cl = fp8_case(rng, lens, G * Hkv, Hkv, D, dt, B=B)
+    kn = round_to_dtype(rng.standard_normal((len(lens), Hkv, D)).astype(np.float32) * 2, dt)
+    vn = round_to_dtype(rng.standard_normal((len(lens), Hkv, D)).astype(np.float32) * 2, dt)
+    scale, ks, vs = float(np.float32(1 / np.sqrt(D))), 0.03, 0.011
+    slots = oracle.slot_mapping(tab, np.arange(len(lens)), cl - 1, B)
+    rk, rv = kp.copy(), vp.copy()
+    ofp8.reshape_and_cache_fp8(kn, vn, rk, rv, slots, dt, ks, vs, block_size=B)
+    ref = oracle.decode_attention(q, rk, rv, tab, cl, scale, dt, block_size=B, kv_dtype="e4m3",
+                                  k_scale=ks, v_scale=vs)
+    for ps in (0, 64):
+        log(f"[gpu] decode append fp8 D={D} G={G} partition={ps}")
+        dk, dv = to_dev(kp, "e4m3"), to_dev(vp, "e4m3")
+        S, Hq = q.shape[:2]
+        out = torch.full((S, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+        d_slots = torch.full((S,), -7, dtype=torch.int64, device="cuda")
+        mc = int(cl.max())
+        wsb = kv.kv_paged_attention_workspace_bytes(S, Hq, Hkv, D, mc, ps)
+        ws = torch.full((max(wsb, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        kv.kv_paged_attention_decode_append_fp8(
+            out, to_dev(q, dt), to_dev(kn, dt), to_dev(vn, dt), dk, dv,
+            torch.from_numpy(tab).cuda(), torch.from_numpy(cl).cuda(), scale, ks, vs, mc,
+            d_slots, ws if wsb else None, ps)
+        torch.cuda.synchronize()
+        assert np.array_equal(d_slots.cpu().numpy(), slots)
+        assert np.array_equal(dk.cpu().numpy(), rk)
+        assert np.array_equal(dv.cpu().numpy(), rv)
+        check_attention(out.cpu().numpy().reshape(-1, D), ref.reshape(-1, D), dt,
+                        f"fp8 append D={D} G={G} ps={ps}")
 
 
 def test_decode_fp8_long_context_split():
