@@ -79,8 +79,8 @@ CAL_BLOCK_BYTES = 32768     # bytes per block and pool (K and V each)
 
 DECODE_SOURCES = ("decode.hip", "decode_kernels.h", "decode_variants.hip", "device_common.h")
 PREFILL_SOURCES = ("prefill.hip", "device_common.h")
-# a shared-prefix decode step runs the prefill kernel too
-SHARED_DECODE_SOURCES = DECODE_SOURCES + ("prefill.hip",)
+# a shared-prefix decode step runs the shared-prefix kernel too
+SHARED_DECODE_SOURCES = DECODE_SOURCES + ("shared_prefix.hip",)
 
 
 def kernel_source_digest(sources=DECODE_SOURCES):
@@ -164,7 +164,7 @@ def pmc_parse(fetch_dir, write_dir, out_path, workload, partition):
     """HBM bytes per decode call from FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the calibration
     copy, whose true byte count is known. A shared-prefix decode call adds its
-    prefix attention (prefill kernel)."""
+    prefix attention (shared_prefix_kernel)."""
     cal_bytes = 2 * CAL_PAIRS * CAL_BLOCK_BYTES
     prefill = is_prefill(workload)
     res = {"workload": workload, "partition_arg": partition, "calibration_bytes": cal_bytes}
@@ -175,7 +175,7 @@ def pmc_parse(fetch_dir, write_dir, out_path, workload, partition):
         cal, ncal = _mean_counter(rows, "copy_blocks_kernel", counter)
         dec, ndec = _mean_counter(rows, "prefill_mfma" if prefill else "decode_", counter)
         mrg, nmrg = _mean_counter(rows, "splitk_merge", counter)
-        pre, npre = (0.0, 0) if prefill else _mean_counter(rows, "prefill_mfma", counter)
+        pre, npre = (0.0, 0) if prefill else _mean_counter(rows, "shared_prefix_kernel", counter)
         if ncal == 0 or ndec == 0:
             raise SystemExit(f"{d}: calibration or decode dispatches missing")
         shared = shared or npre > 0

@@ -397,8 +397,10 @@ int32_t kv_paged_attention_common_prefix(const int32_t* tables_host, int32_t S,
 /* Shared positions for kv_paged_attention_decode_append_shared, or 0 when a
  * decode step over these sequences should take the plain step: the common
  * prefix above, where that entry point supports the step (dtype f16 or
- * bf16, head_dim 128, group size at most 16) and reading the prefix once per
- * batch is expected to be faster than once per sequence. The rule comes from
+ * bf16, head_dim 128, group size at most 16; a common prefix longer than
+ * KV_SHARED_PREFIX_MAX_TOKENS is cut to it, the rest left to the tails) and
+ * reading the prefix once per batch is expected to be faster than once per
+ * sequence. The rule comes from
  * shared/plain step times measured on MI355X (32 query / 8 KV heads, bf16,
  * 4-128 sequences, 256-4096 shared positions, tails of 64 and 512; a point
  * counts as faster at a time ratio of 0.97 or less): at least 4 sequences
@@ -479,10 +481,11 @@ kv_status kv_paged_attention_decode_append_noalloc(
  * sharing": the same physical blocks, reached through the same first
  * shared_tokens / block_size table entries). Attention over the shared
  * positions is computed once for all S queries - the shared blocks are read
- * once, not once per sequence - with the chunked-prefill kernel (no causal
- * mask: every query sees every shared position), the positions cut into
- * ranges of at least 128 that run in parallel; attention over each
- * sequence's own positions shared_tokens..t-1 runs in the decode kernels,
+ * once, not once per sequence - by a kernel whose workgroups each take 16
+ * (sequence, query head) columns of one KV head and one range of the shared
+ * positions, split into slices of at least 64 over up to 8 waves and merged
+ * in LDS, so each range leaves one partial result per column; attention over
+ * each sequence's own positions shared_tokens..t-1 runs in the decode kernels,
  * with the new token written as in kv_paged_attention_decode_append; the
  * prefix pass runs first, and the kernel that writes each tail's output (the
  * decode kernel, or the split-K merge for a tail spanning several
@@ -491,8 +494,10 @@ kv_status kv_paged_attention_decode_append_noalloc(
  * kv_paged_attention_decode_append, up to rounding order). Two launches
  * (three when a tail spans several partitions).
  *
- * shared_tokens: > 0, a multiple of block_size; the shared blocks are read
- *               through row 0 of block_tables. A sequence normally has
+ * shared_tokens: > 0, a multiple of block_size, at most
+ *               KV_SHARED_PREFIX_MAX_TOKENS (KV_ERR_UNSUPPORTED beyond);
+ *               the shared blocks are read through row 0 of block_tables.
+ *               A sequence normally has
  *               context_lens[s] >= shared_tokens + 1 (its tail holds at
  *               least the new token); one of exactly shared_tokens gets the
  *               attention over the shared positions and no write (slots[s]
@@ -507,9 +512,10 @@ kv_status kv_paged_attention_decode_append_noalloc(
  *               16-byte aligned: each prefix range's outputs and softmax
  *               denominators. Needs no initialisation; 0 from the size
  *               function means invalid sizes.
- * dtype f16 or bf16, head_dim 128, group size at most 16 (the prefill
- * kernel's limits: KV_ERR_UNSUPPORTED otherwise); other
- * arguments and checks as for kv_paged_attention_decode_append. */
+ * dtype f16 or bf16, head_dim 128, group size at most 16 (KV_ERR_UNSUPPORTED
+ * otherwise); other arguments and checks as for
+ * kv_paged_attention_decode_append. */
+#define KV_SHARED_PREFIX_MAX_TOKENS 131072 /* 16 ranges x 8 slices x 1,024 */
 size_t kv_paged_attention_shared_aux_bytes(int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
                                           int32_t head_dim, int32_t shared_tokens);
 kv_status kv_paged_attention_decode_append_shared(

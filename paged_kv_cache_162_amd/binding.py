@@ -543,6 +543,9 @@ def kv_paged_attention_decode_append_noalloc(out, q, k_new, v_new, k_pool, v_poo
         "kv_paged_attention_decode_append_noalloc")
 
 
+KV_SHARED_PREFIX_MAX_TOKENS = 131072
+
+
 def kv_paged_attention_shared_aux_bytes(S: int, num_q_heads: int, num_kv_heads: int,
                                         head_dim: int, shared_tokens: int) -> int:
     return int(lib.kv_paged_attention_shared_aux_bytes(S, num_q_heads, num_kv_heads, head_dim,

@@ -21,7 +21,8 @@ OBJDIR = os.path.join(HERE, "_build")
 # (source, extra flags, object tag): decode_variants.hip is compiled once per
 # block size and K/V load policy, so the decode kernels build in parallel
 SOURCES = ([(os.path.join(CSRC, f), [], f) for f in
-            ("host_pool.cpp", "plan.cpp", "cache.hip", "decode.hip", "prefill.hip")] +
+            ("host_pool.cpp", "plan.cpp", "cache.hip", "decode.hip", "prefill.hip",
+             "shared_prefix.hip")] +
            [(os.path.join(CSRC, "decode_variants.hip"), [f"-DPAGEDKV_BS={bs}", f"-DPAGEDKV_NT={nt}"],
              f"decode_variants_b{bs}_nt{nt}") for bs in (8, 16, 32) for nt in (0, 1)])
 ARCH = os.environ.get("PAGEDKV_ARCH", "gfx950")

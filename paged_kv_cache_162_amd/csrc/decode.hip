@@ -344,6 +344,9 @@ kv_status kv_paged_attention_decode_append_shared(
       shared_tokens / block_size > max_blocks)
     return fail(KV_ERR_INVALID, "%s: shared_tokens %d (whole blocks within the table)", who,
                 shared_tokens);
+  if (shared_tokens > KV_SHARED_PREFIX_MAX_TOKENS)
+    return fail(KV_ERR_UNSUPPORTED, "%s: shared_tokens %d (at most %d)", who, shared_tokens,
+                KV_SHARED_PREFIX_MAX_TOKENS);
   if (num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 && num_q_heads / num_kv_heads > 16)
     return fail(KV_ERR_UNSUPPORTED, "%s: group size %d > 16", who, num_q_heads / num_kv_heads);
   if (S < 0) return fail(KV_ERR_INVALID, "%s: bad sizes", who);

@@ -489,10 +489,14 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   const Raw* kbase = static_cast<const Raw*>(p.k_pool);
   const Raw* vbase = static_cast<const Raw*>(p.v_pool);
 
+  // rows past the tile's live tokens read the last live row instead (their
+  // values are masked), so the unused rows of a sequence's last block are
+  // never fetched
   auto load = [&](int j, Raw* ku, Raw* vu) {
+    const int lim = t1 - (t0 + j * kTile) - 1;  // last live row of tile j
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
-      const size_t at = tile_row<BS>(p, w.h, staged, j, r + TPI * i, LPR) + c;
+      const size_t at = tile_row<BS>(p, w.h, staged, j, min(r + TPI * i, lim), LPR) + c;
       ku[i] = load_kv<NT>(kbase + at);
       vu[i] = load_kv<NT>(vbase + at);
     }
@@ -753,18 +757,23 @@ void decode_mfma_kernel(DecodeParams p) {
   constexpr int kKU = KV8 ? 2 : 4;
   typedef typename std::conditional<KV8, uint2, uint4>::type VRaw;
   auto load = [&](int j, uint4* ku, VRaw* vu) {
-    // K: row col of the tile; V: rows 4grp..4grp+3 (consecutive in one block)
-    const uint4* kt = reinterpret_cast<const uint4*>(kbase) + tile_row<BS>(p, w.h, staged, j, col, kRowU4);
+    // K: row col of the tile; V: rows 4grp..4grp+3 (consecutive in one block).
+    // Rows past the tile's live tokens read the last live row (K) or row
+    // group (V) instead - their values are masked - so the unused rows of a
+    // sequence's last block are never fetched.
+    const int lim = t1 - (t0 + j * kTile) - 1;  // last live row of tile j
+    const int kr = min(col, lim), vg = min(grp, lim >> 2);
+    const uint4* kt = reinterpret_cast<const uint4*>(kbase) + tile_row<BS>(p, w.h, staged, j, kr, kRowU4);
     if constexpr (KV8) {
       const uint2* vt = reinterpret_cast<const uint2*>(vbase) +
-                        tile_row<BS>(p, w.h, staged, j, 4 * grp, 2 * kRowU4);
+                        tile_row<BS>(p, w.h, staged, j, 4 * vg, 2 * kRowU4);
       ku[0] = load_kv<NT>(kt + grp);
       ku[1] = load_kv<NT>(kt + 4 + grp);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) vu[jj] = load_kv<NT>(vt + jj * 2 * kRowU4 + col);
     } else {
       const uint4* vt = reinterpret_cast<const uint4*>(vbase) +
-                        tile_row<BS>(p, w.h, staged, j, 4 * grp, kRowU4);
+                        tile_row<BS>(p, w.h, staged, j, 4 * vg, kRowU4);
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) ku[kc] = load_kv<NT>(kt + kc * 4 + grp);
 #pragma unroll

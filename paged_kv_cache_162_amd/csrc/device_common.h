@@ -267,11 +267,10 @@ constexpr int kMaxSharedParts = 16;
 int32_t shared_prefix_parts(int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t shared_len, int32_t* part_keys);
 // Attention of S decode queries over the first shared_len positions of table
-// row 0, which every sequence of the call shares (the prefill kernel's
-// shared-prefix mode), one launch over the ranges of shared_prefix_parts:
-// range k's normalised outputs to o + k*S*Hq*D, log2 of its softmax
-// denominators (base-2 units) to lse + k*S*Hq. Defined with the prefill
-// kernel; the caller checks the arguments.
+// row 0, which every sequence of the call shares, one launch over the ranges
+// of shared_prefix_parts: range k's normalised outputs to o + k*S*Hq*D, log2
+// of its softmax denominators (base-2 units) to lse + k*S*Hq. Defined in
+// shared_prefix.hip; the caller checks the arguments.
 kv_status shared_prefix_attention(float* o, float* lse, const void* q, const void* k_pool,
                                   const void* v_pool, const int32_t* table_row0,
                                   int32_t max_blocks, int32_t S, int32_t num_q_heads,

@@ -191,8 +191,10 @@ extern "C" int32_t kv_paged_attention_choose_shared_prefix(
   if ((dtype != KV_F16 && dtype != KV_BF16) || head_dim != 128 || num_kv_heads <= 0 ||
       num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 16 || S < kSharedMinSeqs)
     return 0;
-  const int32_t shared =
+  int32_t shared =
       kv_paged_attention_common_prefix(tables_host, S, max_blocks, context_lens_host, block_size);
+  if (shared > KV_SHARED_PREFIX_MAX_TOKENS)  // whole blocks: every block size divides the limit
+    shared = KV_SHARED_PREFIX_MAX_TOKENS;
   if (shared < kSharedMinTokens || (int64_t)S * shared < kSharedMinReads) return 0;
   double tail_sum = 0.0;
   for (int32_t s = 0; s < S; ++s) tail_sum += (double)context_lens_host[s] - shared;

@@ -37,11 +37,7 @@ using namespace pagedkv::dev;
 namespace {
 
 constexpr int kPfWaves = 4;        // waves per workgroup
-constexpr int kPfColTiles = 2;     // 16-column MFMA tiles per wave (chunked prefill)
-// The shared-prefix pass has few query rows (one per sequence) and short key
-// ranges: one column tile per wave doubles its workgroups and halves each
-// one's work per key tile, which measured faster there.
-constexpr int kShColTiles = 1;
+constexpr int kPfColTiles = 2;     // 16-column MFMA tiles per wave
 constexpr int kPfRowBytes = 272;   // LDS bytes per key row: 128 x 16-bit + 16 against bank conflicts
 constexpr int kPfSegment = 64;     // table entries staged at once (one per lane)
 constexpr int kPfKeys = 32;        // keys per LDS tile
@@ -59,14 +55,6 @@ struct PrefillParams {
   int32_t T, S, Hq, Hkv, G, tpc, rows_per_block, max_blocks, num_blocks, n_units;
   float scale_log2;  // scale * log2(e), times the K scale for an fp8 cache
   float v_scale;     // fp8 cache: the V scale, applied to the output
-  // Shared-prefix mode (shared_len > 0): every query row (T of them) attends,
-  // without a causal mask, to the first shared_len positions of table row 0,
-  // which all the rows' sequences share; q_start, lens and items are unused.
-  // The positions are cut into key_parts ranges of part_keys (a multiple of
-  // the 32-key tile); range k's normalised outputs go to out + k*T*Hq*D and
-  // its denominators to lse + k*T*Hq.
-  int32_t shared_len, key_parts, part_keys;
-  float* lse;  // optional [T][Hq]: log2 of the softmax denominator, base-2 units
 };
 
 // Column tile of MFMA columns: query row of column c and whether it is live.
@@ -85,15 +73,8 @@ void prefill_mfma_kernel(PrefillParams p) {
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
 
-  const bool shared = p.shared_len > 0;
-  int s, h, qblk, kpart = 0;
-  if (shared) {
-    s = 0;
-    h = blockIdx.x % p.Hkv;
-    const int nq = (p.T + p.rows_per_block - 1) / p.rows_per_block;
-    qblk = (blockIdx.x / p.Hkv) % nq;
-    kpart = blockIdx.x / (p.Hkv * nq);
-  } else if (p.items) {
+  int s, h, qblk;
+  if (p.items) {
     const int it = blockIdx.x / p.Hkv;
     h = blockIdx.x % p.Hkv;
     s = p.items[2 * it];
@@ -104,21 +85,16 @@ void prefill_mfma_kernel(PrefillParams p) {
     qblk = blockIdx.x / (p.S * p.Hkv);
   }
   if (s < 0 || s >= p.S || qblk < 0) return;
-  const int r_begin = shared ? 0 : p.q_start[s], r_end = shared ? p.T : p.q_start[s + 1];
+  const int r_begin = p.q_start[s], r_end = p.q_start[s + 1];
   if (r_begin < 0 || r_end > p.T || r_end < r_begin) return;  // no row can be placed safely
   const int C = r_end - r_begin;
   const int row0 = qblk * p.rows_per_block;
   if (row0 >= C) return;
   const int rows = min(p.rows_per_block, C - row0);
-  // keys [k_begin, L) of the sequence: all of them, or one range of the
-  // shared prefix
-  const int k_begin = kpart * p.part_keys;
-  const int L = shared ? min(p.shared_len, k_begin + p.part_keys) : p.lens[s];
-  if (k_begin >= L) return;
-  float* const out = shared ? p.out + (size_t)kpart * p.T * p.Hq * D : p.out;
-  float* const lse = p.lse && shared ? p.lse + (size_t)kpart * p.T * p.Hq : p.lse;
+  const int L = p.lens[s];
+  float* const out = p.out;
   const float nan = __builtin_nanf("");
-  if ((!shared && L < C) || (int64_t)L > (int64_t)p.max_blocks * BS) {
+  if (L < C || (int64_t)L > (int64_t)p.max_blocks * BS) {
     // impossible length: the block's rows get NaN
     for (int i = tid; i < rows * p.G * (D / 4); i += blockDim.x) {
       const int rr = i / (p.G * (D / 4)), rem = i % (p.G * (D / 4));
@@ -128,10 +104,9 @@ void prefill_mfma_kernel(PrefillParams p) {
     return;
   }
   const int prev = L - C;
-  const int nkeys = shared ? L : prev + row0 + rows;  // keys the block's last query sees
+  const int nkeys = prev + row0 + rows;  // keys the block's last query sees
   const int ntiles = (nkeys + kPfKeys - 1) / kPfKeys;
   const int last = ntiles - 1;
-  const int j0 = k_begin / kPfKeys;  // first tile (k_begin is a multiple of the tile)
   const int nblk = (nkeys + BS - 1) / BS;  // table entries in use
 
   // ---- columns and queries of this wave --------------------------------------
@@ -144,7 +119,7 @@ void prefill_mfma_kernel(PrefillParams p) {
     ct[t].live = col < p.tpc * p.G && qr < row0 + rows;
     ct[t].qrow = qr;
     // a dead column sees every key (finite softmax of zero scores), never stored
-    ct[t].pos = ct[t].live && !shared ? prev + qr : nkeys - 1;
+    ct[t].pos = ct[t].live ? prev + qr : nkeys - 1;
     const uint4* qp = reinterpret_cast<const uint4*>(
         static_cast<const char*>(p.q) +
         (((size_t)r_begin + (ct[t].live ? qr : row0)) * p.Hq + (size_t)h * p.G +
@@ -236,9 +211,8 @@ void prefill_mfma_kernel(PrefillParams p) {
     m[t] = neg_inf();
     l[t] = 0.f;
   }
-  // smallest position among the block's queries (shared mode: every row
-  // sees all nkeys keys)
-  const int first_pos = shared ? nkeys - 1 : prev + row0;
+  // smallest position among the block's queries
+  const int first_pos = prev + row0;
 
   // One 32-key tile. The score MFMAs run per 16-key half (lane: keys 4g..4g+3
   // of each half); the value MFMA takes all 32 keys at once, its reduction
@@ -334,12 +308,12 @@ void prefill_mfma_kernel(PrefillParams p) {
   // stored into LDS buffer t % 2 and computed after a barrier; loads and
   // stores past the last tile repeat the last tile (in bounds, never computed)
   uint4 g0[4], g1[4];
-  load(j0, g0);
-  store(j0, g0, 0);
-  load(min(j0 + 1, last), g1);
-  load(min(j0 + 2, last), g0);
+  load(0, g0);
+  store(0, g0, 0);
+  load(min(1, last), g1);
+  load(min(2, last), g0);
   __syncthreads();
-  for (int j = j0; j < ntiles; j += 2) {
+  for (int j = 0; j < ntiles; j += 2) {
     compute(j, 0);
     store(min(j + 1, last), g1, 1);
     load(min(j + 3, last), g1);
@@ -356,8 +330,6 @@ void prefill_mfma_kernel(PrefillParams p) {
   for (int t = 0; t < CT; ++t) {
     const float lt = column_sum(l[t]);
     if (!ct[t].live) continue;
-    if (lse && grp == 0)
-      lse[((size_t)r_begin + ct[t].qrow) * p.Hq + (size_t)h * p.G + hd] = bad ? nan : m[t] + log2f(lt);
     const float inv = (KV8 ? p.v_scale : 1.0f) / lt;
     float* dst = out + (((size_t)r_begin + ct[t].qrow) * p.Hq + (size_t)h * p.G + hd) * D +
                  32 * grp;
@@ -454,77 +426,6 @@ kv_status prefill_impl(const char* who, float* out, const void* q, const void* k
 }
 
 }  // namespace
-
-namespace pagedkv {
-
-#ifndef PAGEDKV_SHARED_MIN_TILES
-#define PAGEDKV_SHARED_MIN_TILES 4
-#endif
-
-// Key ranges of a shared prefix: enough workgroups to give each CU about two
-// (the kernel's occupancy), but no range under PAGEDKV_SHARED_MIN_TILES tiles,
-// since every range adds S*Hq*(D+1) floats of partial results to write and
-// merge; at most kMaxSharedParts ranges.
-int32_t shared_prefix_parts(int32_t S, int32_t num_q_heads, int32_t num_kv_heads,
-                            int32_t shared_len, int32_t* part_keys) {
-  *part_keys = 0;
-  if (S <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || shared_len <= 0)
-    return 0;
-  const int32_t G = num_q_heads / num_kv_heads;
-  if (G > 16) return 0;
-  const int64_t units = ceil_div64(S, rows_per_block(G, kShColTiles)) * num_kv_heads;
-  const int64_t tiles = ceil_div64(shared_len, kPfKeys);
-  int64_t parts = std::min<int64_t>(ceil_div64(512, units), kMaxSharedParts);
-  parts = std::max<int64_t>(1, std::min<int64_t>(parts, tiles / PAGEDKV_SHARED_MIN_TILES));
-  const int64_t per = ceil_div64(tiles, parts);
-  *part_keys = (int32_t)(per * kPfKeys);
-  return (int32_t)ceil_div64(tiles, per);
-}
-
-// Attention of S query rows (one decode query per sequence) over the first
-// shared_len positions of table row 0, which every sequence shares, cut into
-// the key ranges of shared_prefix_parts: range k's normalised outputs go to
-// o + k*S*Hq*D, log2 of its softmax denominators (base-2 units) to
-// lse + k*S*Hq. Arguments are checked by the caller.
-kv_status shared_prefix_attention(float* o, float* lse, const void* q, const void* k_pool,
-                                  const void* v_pool, const int32_t* table_row0,
-                                  int32_t max_blocks, int32_t S, int32_t num_q_heads,
-                                  int32_t num_kv_heads, int32_t block_size, int32_t num_blocks,
-                                  float scale, kv_dtype dtype, int32_t shared_len,
-                                  hipStream_t stream) {
-  const int32_t G = num_q_heads / num_kv_heads;
-  const int32_t rpb = rows_per_block(G, kShColTiles);
-  int32_t part_keys = 0;
-  const int32_t parts = shared_prefix_parts(S, num_q_heads, num_kv_heads, shared_len, &part_keys);
-  if (parts <= 0) return fail(KV_ERR_INVALID, "shared prefix: bad sizes");
-  PrefillParams prm = {};
-  prm.out = o;
-  prm.q = q;
-  prm.k_pool = k_pool;
-  prm.v_pool = v_pool;
-  prm.tables = table_row0;
-  prm.T = S;
-  prm.S = 1;
-  prm.Hq = num_q_heads;
-  prm.Hkv = num_kv_heads;
-  prm.G = G;
-  prm.tpc = 16 / G;
-  prm.rows_per_block = rpb;
-  prm.max_blocks = max_blocks;
-  prm.num_blocks = num_blocks;
-  prm.n_units = (int32_t)(ceil_div64(S, rpb) * num_kv_heads * parts);
-  prm.scale_log2 = scale * 1.4426950408889634f;
-  prm.v_scale = 1.0f;
-  prm.shared_len = shared_len;
-  prm.key_parts = parts;
-  prm.part_keys = part_keys;
-  prm.lse = lse;
-  hipLaunchKernelGGL((pick_kernel<false, kShColTiles>(dtype, block_size)), dim3((unsigned)prm.n_units),
-                     dim3(kPfWaves * 64), 0, stream, prm);
-  return launch_status("kv_paged_attention_decode_append_shared (shared prefix)");
-}
-
-}  // namespace pagedkv
 
 extern "C" {
 

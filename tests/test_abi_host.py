@@ -120,15 +120,19 @@ def test_device_entry_points_validate_on_the_host(kv):
 
 
 def test_shared_prefix_entry_validation(kv):
-    # per prefix range outputs [S][Hq][D] and denominators [S][Hq]. 32 sequences of group 4
-    # fill two 16-row blocks per KV head: 16 blocks, so 32 ranges are wanted; at most 16, at
-    # least 4 tiles (128 positions) each
+    # per prefix range outputs [S][Hq][D] and denominators [S][Hq]. A range is up to 8
+    # slices (one wave each) of 64..1024 positions, slices sized for about 2,048 waves over
+    # the grid (16-column tiles x KV heads x slices), at most 16 ranges. 32 sequences of
+    # group 4 make 8 column tiles per KV head
     aux = kv.kv_paged_attention_shared_aux_bytes
-    assert aux(32, 32, 8, 128, 2048) == 16 * 129 * 32 * 32 * 4      # 16 ranges of 128
-    assert aux(32, 32, 8, 128, 8192) == 16 * 129 * 32 * 32 * 4      # 16 ranges of 512
-    assert aux(32, 32, 8, 128, 256) == 2 * 129 * 32 * 32 * 4        # 2 ranges of 128
-    assert aux(32, 32, 8, 128, 96) == 1 * 129 * 32 * 32 * 4         # one range
-    assert aux(512, 64, 8, 128, 65536) == 1 * 129 * 512 * 64 * 4    # 512 blocks already
+    assert aux(32, 32, 8, 128, 2048) == 4 * 129 * 32 * 32 * 4       # 32 slices of 64
+    assert aux(32, 32, 8, 128, 8192) == 4 * 129 * 32 * 32 * 4       # 32 slices of 256
+    assert aux(32, 32, 8, 128, 256) == 1 * 129 * 32 * 32 * 4        # 4 slices of 64
+    assert aux(32, 32, 8, 128, 96) == 1 * 129 * 32 * 32 * 4         # 2 slices
+    assert aux(512, 64, 8, 128, 65536) == 8 * 129 * 512 * 64 * 4    # 64 slices of 1024
+    assert aux(1, 1, 1, 128, 131072) == 16 * 129 * 1 * 1 * 4        # the limit: 16 x 8 x 1024
+    assert kv.KV_SHARED_PREFIX_MAX_TOKENS == 131072
+    assert aux(1, 1, 1, 128, 131072 + 32) == 0
     assert aux(0, 32, 8, 128, 2048) == 0
     assert aux(32, 32, 8, 128, 0) == 0
     assert aux(32, 64, 2, 128, 2048) == 0                                # group 32
@@ -138,6 +142,10 @@ def test_shared_prefix_entry_validation(kv):
             shared, 16, None, 0, None, 0, None, 0, None, kv.KV_LOADS_CACHED, None)
     assert call(24) == kv.KV_ERR_INVALID          # not whole blocks
     assert call(0) == kv.KV_ERR_INVALID           # nothing shared
+    assert kv.lib.kv_paged_attention_decode_append_shared(
+        None, None, None, None, None, None, None, 131072 // 16 + 1, None, 2, 8, 2, 128, 16, 8,
+        1.0, kv.KV_BF16, 0, 131072 + 16, 16, None, 0, None, 0, None, 0, None, kv.KV_LOADS_CACHED,
+        None) == kv.KV_ERR_UNSUPPORTED           # beyond the shared-prefix limit
     assert call(80) == kv.KV_ERR_INVALID          # more blocks than the table holds
     assert call(32) == kv.KV_ERR_INVALID          # null pointers
     assert call(32, S=0) == kv.KV_OK              # nothing to do
