@@ -400,15 +400,13 @@ int32_t kv_paged_attention_common_prefix(const int32_t* tables_host, int32_t S,
  * bf16, head_dim 128, group size at most 16; a common prefix longer than
  * KV_SHARED_PREFIX_MAX_TOKENS is cut to it, the rest left to the tails) and
  * reading the prefix once per batch is expected to be faster than once per
- * sequence. The rule comes from
- * shared/plain step times measured on MI355X (32 query / 8 KV heads, bf16,
- * 4-128 sequences, 256-4096 shared positions, tails of 64 and 512; a point
- * counts as faster at a time ratio of 0.97 or less): at least 4 sequences
- * and 256 shared positions, sequences x shared positions >= 49,152, and
- * shared positions >= 3.5 x the mean tail (positions past the prefix, new
- * token included). Every measured point with 32,768 prefix reads or fewer
- * was not faster and every one with 65,536 or more that met the tail
- * condition was; the threshold sits between. */
+ * sequence. The rule comes from shared/plain step times measured on MI355X
+ * (32 query / 8 KV heads, bf16, 4-128 sequences, 256-4096 shared positions,
+ * tails of 64 and 512 positions; a point counts as faster at a time ratio of
+ * 0.97 or less): at least 4 sequences and 256 shared positions, and
+ * sequences x shared positions >= 49,152. Every measured point with 65,536
+ * prefix reads or more was faster (ratios 0.34-0.89, whatever the tail), and
+ * of those with 32,768 or fewer one was (0.88); the threshold sits between. */
 int32_t kv_paged_attention_choose_shared_prefix(const int32_t* tables_host, int32_t S,
                                                 int32_t max_blocks,
                                                 const int32_t* context_lens_host,

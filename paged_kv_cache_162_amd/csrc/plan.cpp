@@ -161,7 +161,6 @@ namespace {
 constexpr int32_t kSharedMinSeqs = 4;
 constexpr int32_t kSharedMinTokens = 256;
 constexpr int64_t kSharedMinReads = 49152;  // sequences x shared positions
-constexpr double kSharedTailRatio = 3.5;    // shared positions / mean tail
 }  // namespace
 
 extern "C" int32_t kv_paged_attention_common_prefix(const int32_t* tables_host, int32_t S,
@@ -195,8 +194,5 @@ extern "C" int32_t kv_paged_attention_choose_shared_prefix(
       kv_paged_attention_common_prefix(tables_host, S, max_blocks, context_lens_host, block_size);
   if (shared > KV_SHARED_PREFIX_MAX_TOKENS)  // whole blocks: every block size divides the limit
     shared = KV_SHARED_PREFIX_MAX_TOKENS;
-  if (shared < kSharedMinTokens || (int64_t)S * shared < kSharedMinReads) return 0;
-  double tail_sum = 0.0;
-  for (int32_t s = 0; s < S; ++s) tail_sum += (double)context_lens_host[s] - shared;
-  return shared >= kSharedTailRatio * (tail_sum / S) ? shared : 0;
+  return (shared < kSharedMinTokens || (int64_t)S * shared < kSharedMinReads) ? 0 : shared;
 }

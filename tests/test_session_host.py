@@ -85,19 +85,33 @@ def test_common_prefix_rule():
     sess.close()
 
 
-# (sequences, shared positions, tail, shared step faster) as measured on an MI355X for
-# 32/8 heads in bf16: ratios of shared to plain step time from 0.29 to 1.67. "Faster" means a
-# ratio of 0.97 or less (run-to-run spread is 1-2%): (32, 1024, 64) measured 0.98 and
-# (128, 1024, 512) 0.99, so both count as not faster. Every point with at most 32,768 prefix
-# reads (sequences x shared positions) was not faster; the library's threshold, 49,152, sits
-# between that and the 65,536 of the prefix-sharing workload (32 x 2048).
-MEASURED = [(4, 4096, 64, False), (8, 4096, 512, False), (16, 2048, 64, False),
-            (16, 4096, 64, True), (16, 4096, 512, True), (32, 1024, 64, False),
-            (32, 2048, 64, True), (32, 2048, 512, True), (32, 2048, 257, True),
-            (64, 512, 64, False), (64, 1024, 64, True), (64, 1024, 512, False),
-            (64, 2048, 512, True), (128, 256, 64, False), (128, 512, 64, True),
-            (128, 512, 512, False), (128, 2048, 512, True), (128, 4096, 64, True),
-            (32, 4096, 512, True), (64, 2048, 64, True), (128, 1024, 512, False)]
+# (sequences, shared positions, tail, shared / plain step time) as measured on an MI355X
+# for 32/8 heads in bf16 (each time the better of two 100-step runs over pools rotated past
+# the caches). "Faster" means a ratio of 0.97 or less (run-to-run spread is 1-2%): (16, 2048,
+# 64) measured 0.997 and (32, 1024, 512) 0.995, so both count as not faster. Every point with
+# 65,536 or more prefix reads (sequences x shared positions) was faster, whatever the tail;
+# of those with 32,768 or fewer only (128, 256, 512) was. The library's threshold, 49,152,
+# sits between; it leaves that one point to the plain step.
+MEASURED = [(4, 256, 64, 1.257), (4, 256, 512, 1.450), (4, 512, 64, 1.082), (4, 512, 512, 1.652),
+            (4, 1024, 64, 1.105), (4, 1024, 512, 1.681), (4, 2048, 64, 1.082),
+            (4, 2048, 512, 1.614), (4, 4096, 64, 1.091), (4, 4096, 512, 1.594),
+            (8, 256, 64, 1.275), (8, 256, 512, 1.513), (8, 512, 64, 1.106), (8, 512, 512, 1.622),
+            (8, 1024, 64, 1.085), (8, 1024, 512, 1.677), (8, 2048, 64, 1.080),
+            (8, 2048, 512, 1.565), (8, 4096, 64, 1.023), (8, 4096, 512, 1.233),
+            (16, 256, 64, 1.346), (16, 256, 512, 1.500), (16, 512, 64, 1.127),
+            (16, 512, 512, 1.591), (16, 1024, 64, 1.086), (16, 1024, 512, 1.515),
+            (16, 2048, 64, 0.997), (16, 2048, 512, 1.168), (16, 4096, 64, 0.689),
+            (16, 4096, 512, 0.759), (32, 256, 64, 1.290), (32, 256, 512, 1.208),
+            (32, 512, 64, 1.094), (32, 512, 512, 1.230), (32, 1024, 64, 1.046),
+            (32, 1024, 512, 0.995), (32, 2048, 64, 0.693), (32, 2048, 512, 0.747),
+            (32, 4096, 64, 0.493), (32, 4096, 512, 0.599), (64, 256, 64, 1.370),
+            (64, 256, 512, 1.089), (64, 512, 64, 1.046), (64, 512, 512, 1.057),
+            (64, 1024, 64, 0.733), (64, 1024, 512, 0.893), (64, 2048, 64, 0.542),
+            (64, 2048, 512, 0.702), (64, 4096, 64, 0.408), (64, 4096, 512, 0.541),
+            (128, 256, 64, 1.099), (128, 256, 512, 0.876), (128, 512, 64, 0.766),
+            (128, 512, 512, 0.808), (128, 1024, 64, 0.575), (128, 1024, 512, 0.834),
+            (128, 2048, 64, 0.429), (128, 2048, 512, 0.612), (128, 4096, 64, 0.343),
+            (128, 4096, 512, 0.469)]
 
 
 def _shared_batch(S, shared, tail, B=16):
@@ -111,12 +125,20 @@ def _shared_batch(S, shared, tail, B=16):
     return tab, np.full(S, shared + tail + 1, np.int32)
 
 
-@pytest.mark.parametrize("S,shared,tail,faster", MEASURED)
-def test_shared_step_rule_matches_measurements(S, shared, tail, faster):
+# the one measured point that was faster but is left to the plain step (32,768 prefix reads)
+CONSERVATIVE = {(128, 256, 512)}
+
+
+@pytest.mark.parametrize("S,shared,tail,ratio", MEASURED)
+def test_shared_step_rule_matches_measurements(S, shared, tail, ratio):
     import paged_kv_cache_162_amd.binding as kv
     tab, lens = _shared_batch(S, shared, tail)
     got = kv.kv_paged_attention_choose_shared_prefix(tab, lens, 16, 32, 8, 128, kv.KV_BF16)
-    assert got == (shared if faster else 0)
+    faster = ratio <= 0.97
+    if (S, shared, tail) in CONSERVATIVE:
+        assert faster and got == 0
+    else:
+        assert got == (shared if faster else 0)
 
 
 def test_shared_step_only_where_the_entry_point_applies():
