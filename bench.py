@@ -160,6 +160,17 @@ def _mean_counter(rows, kernel_substr, counter):
     return (sum(per.values()) / len(per), len(per)) if per else (0.0, 0)
 
 
+def _max_counter(rows, kernel_substr, counter):
+    """Largest per-dispatch value of one counter for kernels whose name
+    contains kernel_substr (values summed per dispatch first)."""
+    per = {}
+    for r in rows:
+        if kernel_substr in r["Kernel_Name"] and r["Counter_Name"].startswith(counter):
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return (max(per.values()), len(per)) if per else (0.0, 0)
+
+
 def pmc_parse(fetch_dir, write_dir, out_path, workload, partition):
     """HBM bytes per decode call from FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the calibration
@@ -172,7 +183,9 @@ def pmc_parse(fetch_dir, write_dir, out_path, workload, partition):
     shared = False
     for tag, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = _counter_rows(d)
-        cal, ncal = _mean_counter(rows, "copy_blocks_kernel", counter)
+        # the calibration copy is the largest copy_blocks dispatch: a step's own
+        # copy-on-write copies run the same kernel on a few blocks
+        cal, ncal = _max_counter(rows, "copy_blocks_kernel", counter)
         dec, ndec = _mean_counter(rows, "prefill_mfma" if prefill else "decode_", counter)
         mrg, nmrg = _mean_counter(rows, "splitk_merge", counter)
         pre, npre = (0.0, 0) if prefill else _mean_counter(rows, "shared_prefix_kernel", counter)
