@@ -61,15 +61,10 @@ CASES = [("bf16", 8, 16, 0, True), ("bf16", 8, 16, 256, False), ("f16", 4, 16, 1
          ("bf16", 6, 16, 0, True), ("f16", 3, 32, 128, False)]
 
 
-@pytest.mark.parametrize("dt,G,B,P,plan", CASES)
-def test_shared_prefix_step_against_oracle(dt, G, B, P, plan):
+def run_shared_case(rng, dt, G, B, P, plan, S, Hkv, shared_blocks, tails, D=128):
+    """One fused shared-prefix step against the oracle: slots, both pools bit for bit, the
+    output within the 16-bit tolerance."""
     kv = kvlib()
-    rng = np.random.default_rng(9000 + G + B + P + plan)
-    D, Hkv, S = 128, 2, 37
-    # 664 / 656 / 640 shared positions: 5 ranges of 128, the last one ragged for 8 and 16
-    shared_blocks = {8: 83, 16: 41, 32: 20}[B]
-    tails = list(rng.integers(1, 300, S))
-    tails[0], tails[1], tails[2] = 1, 2, 700       # new token only; tiny; several partitions
     q, kp, vp, tab, cl = shared_case(rng, S, shared_blocks, tails, G * Hkv, Hkv, D, dt, B)
     shared = shared_blocks * B
     scale = float(np.float32(1 / np.sqrt(D)))
@@ -92,7 +87,7 @@ def test_shared_prefix_step_against_oracle(dt, G, B, P, plan):
     dk, dv = to_dev(kp, dt), to_dev(vp, dt)
     out = torch.full((S, G * Hkv, D), float("nan"), dtype=torch.float32, device="cuda")
     slots = torch.full((S,), 7, dtype=torch.int64, device="cuda")
-    log(f"[gpu] shared prefix {dt} G={G} B={B} P={P} plan={plan}")
+    log(f"[gpu] shared prefix {dt} S={S} G={G} Hkv={Hkv} B={B} shared={shared} P={P} plan={plan}")
     kv.kv_paged_attention_decode_append_shared(out, to_dev(q, dt), to_dev(kn, dt), to_dev(vn, dt),
                                                dk, dv, torch.from_numpy(tab).cuda(),
                                                torch.from_numpy(cl).cuda(), scale, shared, mt,
@@ -102,7 +97,35 @@ def test_shared_prefix_step_against_oracle(dt, G, B, P, plan):
     assert np.array_equal(bits(to_host(dk, dt)), bits(rk))
     assert np.array_equal(bits(to_host(dv, dt)), bits(rv))
     log(check_attention(out.cpu().numpy().reshape(-1, D), ref.reshape(-1, D), dt,
-                        f"shared {dt} G={G} B={B} P={P}"))
+                        f"shared {dt} S={S} G={G} B={B} shared={shared} P={P}"))
+
+
+@pytest.mark.parametrize("dt,G,B,P,plan", CASES)
+def test_shared_prefix_step_against_oracle(dt, G, B, P, plan):
+    rng = np.random.default_rng(9000 + G + B + P + plan)
+    S = 37
+    # 664 / 656 / 640 shared positions: two ranges of 8 slices of 64 positions, the second
+    # holding 2-3 slices (the last one ragged) and 5-6 waves without keys
+    shared_blocks = {8: 83, 16: 41, 32: 20}[B]
+    tails = list(rng.integers(1, 300, S))
+    tails[0], tails[1], tails[2] = 1, 2, 700       # new token only; tiny; several partitions
+    run_shared_case(rng, dt, G, B, P, plan, S, 2, shared_blocks, tails)
+
+
+# Shapes of the prefix pass's plan: (sequences, group, KV heads, block size, shared blocks).
+# 64 x 4 / 8 heads: 16 column tiles per head, 2 ranges of 8 slices of 128; 32 x 4 / 8 heads
+# over 8,192 positions: slices of 256, 4 ranges; 2 x 1 / 1 head over 131,072 positions (the
+# limit): 16 ranges of 8 slices of 1,024; 3 x 16 / 1 head over 104 positions of 8-token
+# blocks: one range of 2 slices, the second 40 positions (a half tile)
+PLANS = [(64, 4, 8, 16, 128), (32, 4, 8, 16, 512), (2, 1, 1, 32, 4096), (3, 16, 1, 8, 13)]
+
+
+@pytest.mark.parametrize("S,G,Hkv,B,shared_blocks", PLANS)
+def test_shared_prefix_plans(S, G, Hkv, B, shared_blocks):
+    rng = np.random.default_rng(9200 + S + G + shared_blocks)
+    tails = list(rng.integers(1, 90, S))
+    tails[0] = 1
+    run_shared_case(rng, "bf16", G, B, 0, True, S, Hkv, shared_blocks, tails)
 
 
 def test_shared_prefix_edge_lengths():
