@@ -35,28 +35,13 @@ namespace pagedkv {
 namespace decode {
 namespace {
 
-#ifndef PAGEDKV_SH_WAVES
-#define PAGEDKV_SH_WAVES 8
-#endif
-#ifndef PAGEDKV_SH_RING
-#define PAGEDKV_SH_RING 2
-#endif
-#ifndef PAGEDKV_SH_MIN_TILES
-#define PAGEDKV_SH_MIN_TILES 2
-#endif
-#ifndef PAGEDKV_SH_TARGET_WAVES
-#define PAGEDKV_SH_TARGET_WAVES 2048
-#endif
-#ifndef PAGEDKV_SH_HEAD_FAST
-#define PAGEDKV_SH_HEAD_FAST 1
-#endif
-constexpr int kShMaxWaves = PAGEDKV_SH_WAVES;  // waves per workgroup
-constexpr int kShRing = PAGEDKV_SH_RING;       // 16-key K/V tiles in flight per wave
+constexpr int kShMaxWaves = 8;        // waves per workgroup (slices per range)
+constexpr int kShRing = 2;            // 16-key K/V tiles in flight per wave
+constexpr int kShMinTiles = 2;        // 32-position tiles per slice, at least
+constexpr int kShTargetWaves = 2048;  // waves the plan aims at over the grid
 constexpr int kShMaxWaveKeys = 1024;  // a wave's table entries fit its lanes
-#if PAGEDKV_SH_WAVES == 8
 static_assert(KV_SHARED_PREFIX_MAX_TOKENS == kMaxSharedParts * kShMaxWaves * kShMaxWaveKeys,
               "the entry point's documented limit is the plan's");
-#endif
 
 struct SharedParams {
   float* o;              // [ranges][S][Hq][D] normalised outputs of each range
@@ -77,13 +62,8 @@ __global__ __launch_bounds__(64 * kShMaxWaves) void shared_prefix_kernel(SharedP
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nwaves = (int)(blockDim.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
-#if PAGEDKV_SH_HEAD_FAST
   const int h = blockIdx.x % p.Hkv;
   const int ctile = (blockIdx.x / p.Hkv) % p.col_tiles;
-#else
-  const int ctile = blockIdx.x % p.col_tiles;
-  const int h = (blockIdx.x / p.col_tiles) % p.Hkv;
-#endif
   const int range = blockIdx.x / (p.Hkv * p.col_tiles);
   if (range >= p.ranges) return;  // the whole workgroup
   // keys [k0, k0 + nk) of this wave: its slice of the range
@@ -280,9 +260,8 @@ SharedPlan plan_shared(int32_t S, int32_t num_q_heads, int32_t num_kv_heads, int
   const int64_t col_tiles = ceil_div64((int64_t)S * G, 16);
   const int64_t t32 = ceil_div64(shared_len, 32);
   const int64_t max_per = kShMaxWaveKeys / 32;
-  int64_t per = std::max<int64_t>(PAGEDKV_SH_MIN_TILES,
-                                  ceil_div64(t32 * col_tiles * num_kv_heads,
-                                             PAGEDKV_SH_TARGET_WAVES));
+  int64_t per = std::max<int64_t>(kShMinTiles,
+                                  ceil_div64(t32 * col_tiles * num_kv_heads, kShTargetWaves));
   per = std::min(per, max_per);
   const int64_t wpp = ceil_div64(t32, per);  // slices per (column tile, head)
   const int64_t waves = std::min<int64_t>(kShMaxWaves, wpp);
