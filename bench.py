@@ -628,6 +628,15 @@ def run_decode(args, cfg, kv, torch, steps, warmup, primary):
         alg = decode_alg_bytes(lens, sp.S, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes, args.block_size,
                                sp.kv_elem_bytes)
         kv_read = kvb
+        # a plain step over blocks the batch shares (--no-shared-prefix) reads
+        # them once per sequence, mostly from the caches; HBM need hold them once
+        common = kv.kv_paged_attention_common_prefix(sess.host_tables, lens, args.block_size)
+        if common:
+            dup = (sp.S - 1) * (kv_bytes(np.array([common]), sp.Hkv, sp.D, sp.kv_elem_bytes)
+                                + common // args.block_size * 4)
+            alg -= dup
+            kv_read = kv_bytes(lens - common, sp.Hkv, sp.D, sp.kv_elem_bytes) + \
+                kv_bytes(np.array([common]), sp.Hkv, sp.D, sp.kv_elem_bytes)
     value = kvb / (step_ms * 1e-3) / 1e9
     res = {
         "workload": f"{sp.name}: {sp.description}", "ms_per_step": round(step_ms, 5),
