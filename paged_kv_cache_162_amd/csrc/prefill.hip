@@ -18,17 +18,22 @@
 // of the contiguous cache ([1] "The PagedAttention kernel").
 //
 // Work split: one workgroup of four wave64s per (sequence, KV head, block of
-// query rows). The 16-key K/V tiles of the sequence are staged once per
+// query rows). The 32-key K/V tiles of the sequence are staged once per
 // workgroup in LDS (double buffered, loaded two tiles ahead) and shared by
 // the four waves. Each wave owns two 16-column MFMA tiles; a column is one
 // (query row, query head) pair of the KV head's group, so a group of G heads
-// gives 16 / G query rows per column tile. Per key tile a wave forms
-//   S^T[key][col] = K[key][:] . Q[col][:]         (4 x mfma 16x16x32 per column tile)
-//   O^T[d][col]  += V^T[d][key] . P^T[key][col]   (16 x mfma 16x16x16: the
-//                                                  weights as 16-bit high part
-//                                                  plus 16-bit residual)
+// gives 16 / G query rows per column tile. Per key tile and column tile a
+// wave forms
+//   S^T[key][col] = K[key][:] . Q[col][:]         (8 x mfma 16x16x32: two
+//                                                  16-key halves x 4 dim slices)
+//   O^T[d][col]  += V^T[d][key] . P^T[key][col]   (16 x mfma 16x16x32: 8 dim
+//                                                  slices x the weights as
+//                                                  16-bit high part plus
+//                                                  16-bit residual)
 // with the causal rule key <= position(query) applied to the scores and an
-// online softmax per column (lazy rescale, as in decode).
+// online softmax per column (lazy rescale, as in decode). The V^T operands
+// come straight from the key-major LDS tile through gfx950's transposing
+// LDS read.
 
 #include "device_common.h"
 
@@ -63,6 +68,15 @@ struct ColTile {
   int pos;     // its position in the sequence: keys up to pos are visible
   bool live;
 };
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16). Within each group of 16
+// lanes, the four 16-bit values that lane r names at its address form row r
+// of a 16 x 4 matrix M; lane i receives M[4k + i/4][i%4] for k = 0..3, element
+// k in the k-th 16-bit slot (lowest first).
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
 
 template <int DT, int BS, bool KV8, int CT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -162,6 +176,8 @@ void prefill_mfma_kernel(PrefillParams p) {
   // 16-bit pools: this thread moves rows lr and lr + 16, 16-byte chunk lc.
   // fp8 pools: row r8, 16 codes from chunk c8, widened to two 16-bit chunks.
   const int lr = tid >> 4, lc = tid & 15;
+  // transposing V reads: key row 4grp + (col >> 2), dims 4 (col & 3)..+3
+  const int vt_off = (4 * grp + (col >> 2)) * kPfRowBytes + 8 * (col & 3);
   const int r8 = tid >> 3, c8 = tid & 7;
   const uint4* kpool = static_cast<const uint4*>(p.k_pool);
   const uint4* vpool = static_cast<const uint4*>(p.v_pool);
@@ -257,15 +273,23 @@ void prefill_mfma_kernel(PrefillParams p) {
           for (int r = 0; r < 4; ++r) x[t][4 * half + r] = st[r];
         }
     }
-    uint4 vu[2][4];
+    // V operands: one transposing LDS read per 4 keys gives lane (i, g) dim
+    // 16n + i of keys 4g..4g+3 (16 + 4g.. for the second read); the source
+    // lane 4k + a of each 16-lane group names key row 4g + k, dims 16n + 4a..+3
+    uint4 va[8];
 #pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        vu[half][jj] = *reinterpret_cast<const uint4*>(
-            &lds[buf][1][(16 * half + 4 * grp + jj) * kPfRowBytes + col * 16]);
+    for (int n = 0; n < 8; ++n) {
+      const uint2 lo = lds_read_tr16(&lds[buf][1][vt_off + 32 * n]);
+      const uint2 hi = lds_read_tr16(&lds[buf][1][vt_off + 32 * n + 16 * kPfRowBytes]);
+      va[n] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
     const bool causal = kPfKeys * j + kPfKeys - 1 > first_pos;  // some key hidden from some query
     const float sl = p.scale_log2;  // > 0, so the maximum commutes with the scaling
+    // maxima of every column tile first, and one rescale branch for all of
+    // them, so the exponentials of one tile and the value products of
+    // another sit in one straight-line block the scheduler can interleave
+    float lm[CT];
+    bool grow = false;
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
       if (causal) {
@@ -273,18 +297,25 @@ void prefill_mfma_kernel(PrefillParams p) {
         for (int i = 0; i < 8; ++i)
           if (kPfKeys * j + 16 * (i >> 2) + 4 * grp + (i & 3) > ct[t].pos) x[t][i] = neg_inf();
       }
-      float lm = x[t][0];
+      lm[t] = x[t][0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) lm = fmaxf(lm, x[t][i]);
-      lm *= sl;
-      if (__builtin_amdgcn_ballot_w64(lm > m[t] + kRescaleSlack) != 0) {
-        const float mn = fmaxf(m[t], column_max(lm));
+      for (int i = 1; i < 8; ++i) lm[t] = fmaxf(lm[t], x[t][i]);
+      lm[t] *= sl;
+      grow = grow || lm[t] > m[t] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+        const float mn = fmaxf(m[t], column_max(lm[t]));
         const float alpha = fast_exp2(m[t] - mn);  // 0 while m is -inf
         l[t] *= alpha;
 #pragma unroll
         for (int n = 0; n < 8; ++n) o[t][n] *= alpha;
         m[t] = mn;
       }
+    }
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
       float pw[8];
       const float nm = -m[t];
 #pragma unroll
@@ -296,12 +327,19 @@ void prefill_mfma_kernel(PrefillParams p) {
       split_weights(pw, ph, pl);
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const uint2 a0 = v_column(vu[0], n), a1 = v_column(vu[1], n);
-        const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
-        o[t][n] = mfma_qk<DT>(a, ph, o[t][n]);
-        o[t][n] = mfma_qk<DT>(a, pl, o[t][n]);
+        o[t][n] = mfma_qk<DT>(va[n], ph, o[t][n]);
+        o[t][n] = mfma_qk<DT>(va[n], pl, o[t][n]);
       }
     }
+#ifdef PF_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x002, 70, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+#endif
   };
 
   // ---- pipeline: tile t is loaded into register slot t % 2 two tiles ahead,
@@ -325,21 +363,19 @@ void prefill_mfma_kernel(PrefillParams p) {
     __syncthreads();
   }
 
-  // ---- results: lane holds column col, dims 32grp + 8r + n (n < 8) -----------
+  // ---- results: lane holds column col, dims 16n + 4grp + r (r < 4) -----------
 #pragma unroll
   for (int t = 0; t < CT; ++t) {
     const float lt = column_sum(l[t]);
     if (!ct[t].live) continue;
     const float inv = (KV8 ? p.v_scale : 1.0f) / lt;
     float* dst = out + (((size_t)r_begin + ct[t].qrow) * p.Hq + (size_t)h * p.G + hd) * D +
-                 32 * grp;
+                 4 * grp;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float4 a = make_float4(o[t][0][r] * inv, o[t][1][r] * inv, o[t][2][r] * inv, o[t][3][r] * inv);
-      float4 b = make_float4(o[t][4][r] * inv, o[t][5][r] * inv, o[t][6][r] * inv, o[t][7][r] * inv);
-      if (bad) a = b = make_float4(nan, nan, nan, nan);
-      *reinterpret_cast<float4*>(dst + 8 * r) = a;
-      *reinterpret_cast<float4*>(dst + 8 * r + 4) = b;
+    for (int n = 0; n < 8; ++n) {
+      float4 a = make_float4(o[t][n][0] * inv, o[t][n][1] * inv, o[t][n][2] * inv, o[t][n][3] * inv);
+      if (bad) a = make_float4(nan, nan, nan, nan);
+      *reinterpret_cast<float4*>(dst + 16 * n) = a;
     }
   }
 }
