@@ -331,15 +331,6 @@ void prefill_mfma_kernel(PrefillParams p) {
         o[t][n] = mfma_qk<DT>(va[n], pl, o[t][n]);
       }
     }
-#ifdef PF_SCHED
-    __builtin_amdgcn_sched_group_barrier(0x002, 70, 0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-#endif
   };
 
   // ---- pipeline: tile t is loaded into register slot t % 2 two tiles ahead,
