@@ -158,12 +158,16 @@ void prefill_mfma_kernel(PrefillParams p) {
     staged = (oob || !need) ? 0 : e;  // out-of-pool and unused entries read block 0
     seg = sg;
   };
-  // uint4 index of key row r (0..31) of 32-key tile j. The block index is
-  // wave-uniform: a wave loads rows 4w..4w+3 and 16+4w..16+4w+3 (16-bit
-  // pools) or 8w..8w+7 (fp8 pools), and no such group straddles two 8-token
-  // blocks
-  auto key_row = [&](int j, int r) -> size_t {
-    const int key = kPfKeys * j + r;
+  // A wave stages a group of consecutive rows of each tile: rows 4w..4w+3
+  // and 16+4w..16+4w+3 (16-bit pools) or 8w..8w+7 (fp8 pools). Such a group
+  // never straddles two blocks (8 tokens at least), so its block, table entry
+  // and first row are wave-uniform and computed once per group on the scalar
+  // unit; a lane adds a fixed offset (row within the group, 16-byte chunk).
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  constexpr int kGroupRows = KV8 ? 8 : 4;
+  // uint4 index of the first row of the group starting at row r0 of tile j
+  auto group_row = [&](int j, int r0) -> size_t {
+    const int key = kPfKeys * j + r0;
     const int bi = key / BS, rb = key % BS;
     const int sg = bi / kPfSegment;
     if (sg != seg) stage(sg);
@@ -173,48 +177,62 @@ void prefill_mfma_kernel(PrefillParams p) {
 
   // ---- LDS tiles of 32 keys: [buffer][K, V][row] -----------------------------
   __shared__ __align__(16) unsigned char lds[2][2][kPfKeys * kPfRowBytes];
-  // 16-bit pools: this thread moves rows lr and lr + 16, 16-byte chunk lc.
-  // fp8 pools: row r8, 16 codes from chunk c8, widened to two 16-bit chunks.
-  const int lr = tid >> 4, lc = tid & 15;
+  // 16-bit pools: this lane moves rows gr and gr + 16 of the tile, 16-byte
+  // chunk lc. fp8 pools: row gr, 16 codes from chunk lc, widened to two
+  // 16-bit chunks.
+  const int lc = KV8 ? (lane & 7) : (lane & 15);
+  const int gr = kGroupRows * wv + (KV8 ? lane >> 3 : lane >> 4);  // tile row
+  const int lane_u4 = (gr - kGroupRows * wv) * kRowU4 + lc;         // within the group
   // transposing V reads: key row 4grp + (col >> 2), dims 4 (col & 3)..+3
   const int vt_off = (4 * grp + (col >> 2)) * kPfRowBytes + 8 * (col & 3);
-  const int r8 = tid >> 3, c8 = tid & 7;
   const uint4* kpool = static_cast<const uint4*>(p.k_pool);
   const uint4* vpool = static_cast<const uint4*>(p.v_pool);
   auto load = [&](int j, uint4* g) {
     if constexpr (KV8) {
-      const size_t r = key_row(j, r8);
-      g[0] = kpool[r + c8];
-      g[1] = vpool[r + c8];
+      const size_t r = group_row(j, kGroupRows * wv);
+      g[0] = (kpool + r)[lane_u4];
+      g[1] = (vpool + r)[lane_u4];
     } else {
-      const size_t r0 = key_row(j, lr), r1 = key_row(j, lr + 16);
-      g[0] = kpool[r0 + lc];
-      g[1] = vpool[r0 + lc];
-      g[2] = kpool[r1 + lc];
-      g[3] = vpool[r1 + lc];
+      const size_t r0 = group_row(j, kGroupRows * wv), r1 = group_row(j, 16 + kGroupRows * wv);
+      g[0] = (kpool + r0)[lane_u4];
+      g[1] = (vpool + r0)[lane_u4];
+      g[2] = (kpool + r1)[lane_u4];
+      g[3] = (vpool + r1)[lane_u4];
     }
   };
-  auto put = [&](int buf, int kv, int row, int chunk, const uint4& u, uint32_t mk) {
-    *reinterpret_cast<uint4*>(&lds[buf][kv][row * kPfRowBytes + chunk * 16]) =
-        make_uint4(u.x & mk, u.y & mk, u.z & mk, u.w & mk);
+  auto put = [&](int buf, int kv, int row, int chunk, const uint4& u) {
+    *reinterpret_cast<uint4*>(&lds[buf][kv][row * kPfRowBytes + chunk * 16]) = u;
+  };
+  auto zero_past = [&](int j, int row, uint4 u) {
+    return kPfKeys * j + row >= nkeys ? make_uint4(0, 0, 0, 0) : u;
   };
   auto store = [&](int j, const uint4* g, int buf) {
-    // rows past the visible keys may hold anything: they are stored as zeros
+    // Rows past the visible keys may hold anything. Their scores are replaced
+    // by -inf (a select, so even NaN keys drop out), but their zero weights
+    // would still meet the values in the product: V rows there are stored as
+    // zeros. Only a tail tile has such rows.
+    const bool tail = kPfKeys * j + kPfKeys > nkeys;
     if constexpr (KV8) {
-      const uint32_t mk = kPfKeys * j + r8 >= nkeys ? 0u : ~0u;
-#pragma unroll
-      for (int kv = 0; kv < 2; ++kv) {
-        put(buf, kv, r8, 2 * c8, e4m3x8_widen<DT>(g[kv].x, g[kv].y), mk);
-        put(buf, kv, r8, 2 * c8 + 1, e4m3x8_widen<DT>(g[kv].z, g[kv].w), mk);
+      const uint4 k0 = e4m3x8_widen<DT>(g[0].x, g[0].y), k1 = e4m3x8_widen<DT>(g[0].z, g[0].w);
+      uint4 v0 = e4m3x8_widen<DT>(g[1].x, g[1].y), v1 = e4m3x8_widen<DT>(g[1].z, g[1].w);
+      if (tail) {
+        v0 = zero_past(j, gr, v0);
+        v1 = zero_past(j, gr, v1);
       }
+      put(buf, 0, gr, 2 * lc, k0);
+      put(buf, 0, gr, 2 * lc + 1, k1);
+      put(buf, 1, gr, 2 * lc, v0);
+      put(buf, 1, gr, 2 * lc + 1, v1);
     } else {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int row = lr + 16 * half;
-        const uint32_t mk = kPfKeys * j + row >= nkeys ? 0u : ~0u;
-        put(buf, 0, row, lc, g[2 * half], mk);
-        put(buf, 1, row, lc, g[2 * half + 1], mk);
+      uint4 v0 = g[1], v1 = g[3];
+      if (tail) {
+        v0 = zero_past(j, gr, v0);
+        v1 = zero_past(j, gr + 16, v1);
       }
+      put(buf, 0, gr, lc, g[0]);
+      put(buf, 1, gr, lc, v0);
+      put(buf, 0, gr + 16, lc, g[2]);
+      put(buf, 1, gr + 16, lc, v1);
     }
   };
 
