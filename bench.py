@@ -419,39 +419,81 @@ def prefill_bench(args, w, kv, torch):
     print(json.dumps(res), flush=True)
 
 
-def prefill_cpu_baseline(w, lens, counts, seconds):
-    """The prefill oracle, untouched, on a bounded sample: the chunks of the
-    first sequences, rows added sequence by sequence until `seconds` pass."""
+def _prefill_worker_init(cfg, block_size, lens, qs):
+    # one BLAS thread per worker, as for the decode baseline
     from threadpoolctl import threadpool_limits
+    _ORACLE["blas"] = threadpool_limits(limits=1)
     import oracle
     from oracle.block_manager import run_ops
-    sp = w.spec
-    bm = oracle.BlockManager(w.num_blocks, block_size=sp.block_size, free_order=w.free_order)
-    h, slots_by_op, _ = run_ops(bm, w.setup_ops + w.step_ops)
+    from workloads import make_workload
+    w = make_workload(cfg, block_size=block_size)
+    bm = oracle.BlockManager(w.num_blocks, block_size=block_size, free_order=w.free_order)
+    h, _, _ = run_ops(bm, w.setup_ops + w.step_ops)
     tables, _ = bm.packed_tables([h[i] for i in range(w.S)])
-    qs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    done_flops, t_total, nseq = 0, 0.0, 0
+    _ORACLE.update(w=w, tables=tables, lens=np.asarray(lens, dtype=np.int32),
+                   qs=np.asarray(qs, dtype=np.int32))
+
+
+def _prefill_worker_run(units):
+    """The prefill oracle, untouched, for the chunk rows [r0, r1) of each unit."""
+    import oracle
+    w, sp = _ORACLE["w"], _ORACLE["w"].spec
+    kw = dict(kv_dtype=sp.kv_dtype, k_scale=sp.k_scale, v_scale=sp.v_scale) if sp.kv_dtype else {}
+    t0 = time.perf_counter()
+    for r0, r1 in units:
+        oracle.prefill_attention(w.q, _ORACLE["qs"], w.k_pool, w.v_pool, _ORACLE["tables"],
+                                 _ORACLE["lens"], sp.scale, sp.dtype, block_size=sp.block_size,
+                                 rows=range(r0, r1), **kw)
+    return time.perf_counter() - t0
+
+
+def prefill_cpu_baseline(w, lens, counts, seconds):
+    """The prefill oracle, untouched, on this host's cores: every chunk row of
+    the step, in one oracle call per piece of a sequence's chunk - about one
+    piece per 512 positions of context, since the oracle's cost per row grows
+    with the context and each call also widens the whole query array - the
+    pieces dealt out costliest first to one worker process per core, passes
+    repeated until `seconds` have elapsed (at most 20)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    from threadpoolctl import threadpool_limits
+    sp = w.spec
+    qs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    units, cost = [], []
+    for s in range(w.S):
+        prev, c = int(lens[s]) - int(counts[s]), int(counts[s])
+        k = max(1, min(c, int(round(int(lens[s]) / 512))))
+        for i in range(k):
+            r0, r1 = c * i // k, c * (i + 1) // k
+            if r1 > r0:
+                units.append((int(qs[s]) + r0, int(qs[s]) + r1))
+                cost.append(int(lens[s]) * (r1 - r0))
+    cores = host_cores()
+    chunks, load = [[] for _ in range(cores)], np.zeros(cores)
+    for u in np.argsort(-np.asarray(cost), kind="stable"):
+        c = int(np.argmin(load))
+        chunks[c].append(units[u])
+        load[c] += cost[u]
+    chunks = [c for c in chunks if c]
+    passes, t_total = 0, 0.0
     with threadpool_limits(limits=1):
-        for s in range(w.S):
-            rows = range(int(qs[s]), int(qs[s + 1]))
-            t0 = time.perf_counter()
-            if sp.kv_dtype:
-                oracle.prefill_attention(w.q, qs, w.k_pool, w.v_pool, tables, lens, sp.scale,
-                                         sp.dtype, block_size=sp.block_size, rows=rows,
-                                         kv_dtype=sp.kv_dtype, k_scale=sp.k_scale,
-                                         v_scale=sp.v_scale)
-            else:
-                oracle.prefill_attention(w.q, qs, w.k_pool, w.v_pool, tables, lens, sp.scale,
-                                         sp.dtype, block_size=sp.block_size, rows=rows)
-            t_total += time.perf_counter() - t0
-            done_flops += prefill_flops(lens[s:s + 1], counts[s:s + 1], sp.Hq, sp.D)
-            nseq += 1
-            if t_total >= seconds:
-                break
-    return {"value": round(done_flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-            "kind": "oracle", "seconds": round(t_total, 2),
-            "sample": f"the chunks of the first {nseq} of {w.S} sequences "
-                      f"({nseq * sp.chunk} query rows), BLAS limited to 1 thread"}
+        with ProcessPoolExecutor(len(chunks), mp_context=mp.get_context("spawn"),
+                                 initializer=_prefill_worker_init,
+                                 initargs=(sp_cfg(w), sp.block_size, [int(x) for x in lens],
+                                           [int(x) for x in qs])) as pool:
+            list(pool.map(_prefill_worker_run, [[c[0]] for c in chunks]))  # warm the workers
+            while passes < 20 and (passes == 0 or t_total < seconds):
+                t0 = time.perf_counter()
+                list(pool.map(_prefill_worker_run, chunks))
+                t_total += time.perf_counter() - t0
+                passes += 1
+    per = t_total / passes
+    flops = prefill_flops(lens, counts, sp.Hq, sp.D)
+    return {"value": round(flops / per / 1e12, 6), "unit": "TFLOP/s", "cores": len(chunks),
+            "kind": "oracle", "seconds_per_pass": round(per, 3), "passes": passes,
+            "sample": f"every chunk row of the step ({int(sum(counts))} rows of {w.S} sequences, "
+                      f"{len(units)} oracle calls over {len(chunks)} worker processes, one "
+                      f"BLAS thread each), {passes} pass(es)"}
 
 
 def swap_bench(args, kv, torch):
