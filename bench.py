@@ -40,11 +40,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=3, help="workload number 1-9")
+    ap.add_argument("--workload", type=int, default=3, help="workload number 1-10")
     ap.add_argument("--partition", type=int, default=0,
                     help="partition tokens (0 = chosen per batch by kv_paged_attention_choose_partition)")
     ap.add_argument("--block-size", type=int, default=16, help="tokens per KV block (8, 16 or 32)")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas to rotate (0 = auto)")
+    ap.add_argument("--prefill-splits", type=int, default=0,
+                    help="key runs per prefill block (0 = chosen per step by "
+                         "kv_paged_attention_prefill_choose_splits)")
     ap.add_argument("--no-plan", action="store_true", help="padded grid instead of the host work plan")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="decode a common prefix per sequence instead of once per batch")
@@ -345,7 +348,8 @@ def prefill_bench(args, w, kv, torch):
     dt = sp.dtype
     kp, vp = to_dev(w.k_pool, sp.cache_dtype), to_dev(w.v_pool, sp.cache_dtype)
     sess = DecodeSession(k_pool=kp, v_pool=vp, num_q_heads=sp.Hq, free_order=w.free_order,
-                         use_plan=not args.no_plan, k_scale=sp.k_scale, v_scale=sp.v_scale)
+                         use_plan=not args.no_plan, k_scale=sp.k_scale, v_scale=sp.v_scale,
+                         prefill_splits=args.prefill_splits or None)
     sess.run_ops(w.setup_ops)
     counts = [sp.chunk] * sp.S
     sess.prepare_prefill(list(range(sp.S)), counts)
@@ -404,13 +408,15 @@ def prefill_bench(args, w, kv, torch):
                    "head_dim": sp.D, "block_size": args.block_size,
                    "sum_context": int(lens.sum()), "max_context": int(lens.max()),
                    "flops_per_step": flops, "replicas_rotated": R, "parallelism": "single GPU",
-                   "kv_cache_dtype": sp.cache_dtype},
+                   "kv_cache_dtype": sp.cache_dtype, "key_runs_per_block": sess.step_splits},
         "query_tokens_per_s": round(T / (step_ms * 1e-3), 1),
         "attention_ms": round(att_ms, 5),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": "kv_paged_attention_prefill%s call: prefill_mfma_kernel"
+                     "kernel": ("kv_paged_attention_prefill_split%s call: prefill_mfma_kernel "
+                                "+ prefill_merge_kernel" if sess.step_splits > 1 else
+                                "kv_paged_attention_prefill%s call: prefill_mfma_kernel")
                                % ("_fp8" if sp.kv_dtype else ""),
                      "alg_flops_per_launch": flops},
     }

@@ -668,6 +668,63 @@ kv_status kv_paged_attention_prefill_fp8(float* out, const void* q, const void* 
                                          const int32_t* work_items, int32_t n_items,
                                          hipStream_t stream);
 
+/* Key split for chunks that are short against their cached prefix
+ * ([2] "The Custom CUDA Kernel": the partition-and-reduce of long contexts,
+ * here over a block of query rows). A block's visible keys, in tiles of 32,
+ * are cut into `splits` runs of equal length; each run is one workgroup per
+ * KV head, which writes its rows' unnormalised sums and (max, weight sum) to
+ * a workspace, and a second launch combines the runs with the online-softmax
+ * rescale. Results match the unsplit call up to rounding order. */
+#define KV_PREFILL_MAX_SPLITS 64
+
+/* Number of key runs for a prefill launch from host copies of query_start
+ * ([S + 1]) and context_lens ([S]): 1 when the plan's work units (items x
+ * num_kv_heads) already number min_units, else the smallest count that
+ * reaches min_units, capped so that the longest item keeps at least 16
+ * tiles (512 keys) per run and at KV_PREFILL_MAX_SPLITS. 1 for invalid
+ * arguments. */
+int32_t kv_paged_attention_prefill_choose_splits(const int32_t* query_start_host,
+                                                 const int32_t* context_lens_host, int32_t S,
+                                                 int32_t num_q_heads, int32_t num_kv_heads,
+                                                 int32_t min_units);
+
+/* Workspace bytes kv_paged_attention_prefill_split needs: splits * total_q
+ * * num_q_heads * (head_dim + 2) floats, 0 when splits <= 1 or a size is not
+ * positive. The workspace needs no initialisation; calls that run
+ * concurrently need separate workspaces. */
+size_t kv_paged_attention_prefill_workspace_bytes(int32_t total_q, int32_t num_q_heads,
+                                                 int32_t head_dim, int32_t splits);
+
+/* kv_paged_attention_prefill with each block's keys cut into `splits` runs
+ * (1..KV_PREFILL_MAX_SPLITS; 1 is the unsplit call and needs no workspace):
+ * grid = items * num_kv_heads * splits workgroups, then one merge workgroup
+ * per item and KV head, both on `stream`. workspace: device, 16-byte
+ * aligned, at least kv_paged_attention_prefill_workspace_bytes(total_q,
+ * num_q_heads, head_dim, splits) bytes, else KV_ERR_INVALID. Output, checks
+ * and NaN rules as for kv_paged_attention_prefill (a NaN run makes its rows
+ * NaN). */
+kv_status kv_paged_attention_prefill_split(float* out, const void* q, const void* k_pool,
+                                           const void* v_pool, const int32_t* block_tables,
+                                           int32_t max_blocks, const int32_t* context_lens,
+                                           const int32_t* query_start, int32_t S, int32_t total_q,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t num_blocks, float scale, kv_dtype dtype,
+                                           int32_t max_query_len, const int32_t* work_items,
+                                           int32_t n_items, int32_t splits, void* workspace,
+                                           size_t ws_bytes, hipStream_t stream);
+
+/* kv_paged_attention_prefill_split over fp8 pools, scales as for
+ * kv_paged_attention_prefill_fp8. */
+kv_status kv_paged_attention_prefill_split_fp8(
+    float* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+    const int32_t* query_start, int32_t S, int32_t total_q, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    kv_dtype dtype, float k_scale, float v_scale, int32_t max_query_len,
+    const int32_t* work_items, int32_t n_items, int32_t splits, void* workspace, size_t ws_bytes,
+    hipStream_t stream);
+
 /* Message describing the calling thread's last error ("" if none). */
 const char* kv_last_error(void);
 

@@ -121,6 +121,15 @@ _SIGS = {
     "kv_paged_attention_prefill_fp8": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
                                                  i32, i32, i32, i32, f32, C.c_int, f32, f32, i32,
                                                  vp, i32, vp]),
+    "kv_paged_attention_prefill_choose_splits": (i32, [P_i32, P_i32, i32, i32, i32, i32]),
+    "kv_paged_attention_prefill_workspace_bytes": (C.c_size_t, [i32, i32, i32, i32]),
+    "kv_paged_attention_prefill_split": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
+                                                   i32, i32, i32, i32, f32, C.c_int, i32, vp, i32,
+                                                   i32, vp, C.c_size_t, vp]),
+    "kv_paged_attention_prefill_split_fp8": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32,
+                                                       i32, i32, i32, i32, i32, f32, C.c_int, f32,
+                                                       f32, i32, vp, i32, i32, vp, C.c_size_t,
+                                                       vp]),
     "kv_paged_attention_choose_partition": (i32, [P_i32, i32, i32, i32, i32]),
     "kv_paged_attention_common_prefix": (i32, [P_i32, i32, i32, P_i32, i32]),
     "kv_paged_attention_choose_shared_prefix": (i32, [P_i32, i32, i32, P_i32, i32, i32, i32, i32,
@@ -720,6 +729,76 @@ def kv_paged_attention_prefill(out, q, k_pool, v_pool, block_tables, context_len
         None if work_items is None else _dev(work_items, "work_items", torch.int32),
         0 if work_items is None else work_items.shape[0], _stream(stream)),
         "kv_paged_attention_prefill")
+
+
+KV_PREFILL_MAX_SPLITS = 64
+
+
+def kv_paged_attention_prefill_choose_splits(query_start_host, context_lens_host, num_q_heads: int,
+                                             num_kv_heads: int, min_units: int) -> int:
+    """Key runs per block for a prefill launch (1 = no split)."""
+    qs = _i32_array(query_start_host)
+    lens = _i32_array(context_lens_host)
+    if qs.size != lens.size + 1:
+        raise KVError(KV_ERR_INVALID, "kv_paged_attention_prefill_choose_splits",
+                      "query_start needs S + 1 entries")
+    return int(lib.kv_paged_attention_prefill_choose_splits(_p32(qs), _p32(lens), len(lens),
+                                                            num_q_heads, num_kv_heads, min_units))
+
+
+def kv_paged_attention_prefill_workspace_bytes(total_q: int, num_q_heads: int, head_dim: int,
+                                               splits: int) -> int:
+    return int(lib.kv_paged_attention_prefill_workspace_bytes(total_q, num_q_heads, head_dim,
+                                                              splits))
+
+
+def kv_paged_attention_prefill_split(out, q, k_pool, v_pool, block_tables, context_lens,
+                                     query_start, scale: float, max_query_len: int, splits: int,
+                                     workspace, work_items=None, stream=None) -> None:
+    """kv_paged_attention_prefill with each block's keys cut into `splits` runs; workspace:
+    a device tensor of at least kv_paged_attention_prefill_workspace_bytes bytes."""
+    torch = _torch()
+    T, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_pool.shape
+    S = context_lens.numel()
+    if D2 != D or tuple(out.shape) != (T, Hq, D) or block_tables.shape[0] != S \
+            or query_start.numel() != S + 1 or q.dtype != k_pool.dtype \
+            or v_pool.shape != k_pool.shape:
+        raise KVError(KV_ERR_INVALID, "kv_paged_attention_prefill_split", "shape/dtype mismatch")
+    ws, ws_bytes = (0, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                     workspace.numel() * workspace.element_size())
+    _check(lib.kv_paged_attention_prefill_split(
+        _dev(out, "out", torch.float32), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), _dev(query_start, "query_start", torch.int32),
+        S, T, Hq, Hkv, D, B, NB, float(scale), dtype_code(q), max_query_len,
+        None if work_items is None else _dev(work_items, "work_items", torch.int32),
+        0 if work_items is None else work_items.shape[0], int(splits), ws, ws_bytes,
+        _stream(stream)), "kv_paged_attention_prefill_split")
+
+
+def kv_paged_attention_prefill_split_fp8(out, q, k_pool, v_pool, block_tables, context_lens,
+                                         query_start, scale: float, k_scale: float, v_scale: float,
+                                         max_query_len: int, splits: int, workspace,
+                                         work_items=None, stream=None) -> None:
+    """kv_paged_attention_prefill_split over uint8 E4M3 pools with per-pool scales."""
+    torch = _torch()
+    T, Hq, D = q.shape
+    NB, Hkv, B, D2 = _fp8_pools("kv_paged_attention_prefill_split_fp8", k_pool, v_pool)
+    S = context_lens.numel()
+    if D2 != D or tuple(out.shape) != (T, Hq, D) or block_tables.shape[0] != S \
+            or query_start.numel() != S + 1:
+        raise KVError(KV_ERR_INVALID, "kv_paged_attention_prefill_split_fp8", "shape mismatch")
+    ws, ws_bytes = (0, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                     workspace.numel() * workspace.element_size())
+    _check(lib.kv_paged_attention_prefill_split_fp8(
+        _dev(out, "out", torch.float32), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), _dev(query_start, "query_start", torch.int32),
+        S, T, Hq, Hkv, D, B, NB, float(scale), dtype_code(q), float(k_scale), float(v_scale),
+        max_query_len, None if work_items is None else _dev(work_items, "work_items", torch.int32),
+        0 if work_items is None else work_items.shape[0], int(splits), ws, ws_bytes,
+        _stream(stream)), "kv_paged_attention_prefill_split_fp8")
 
 
 def kv_paged_attention_prefill_fp8(out, q, k_pool, v_pool, block_tables, context_lens,

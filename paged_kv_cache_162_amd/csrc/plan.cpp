@@ -128,6 +128,34 @@ extern "C" kv_status kv_paged_attention_prefill_plan(const int32_t* query_start_
   return KV_OK;
 }
 
+// Key runs for a prefill launch (kv_paged_attention_prefill_split): none
+// while the plan's units cover min_units; else as many as reach it, each run
+// keeping at least kPrefillMinRunTiles tiles of the longest item.
+constexpr int64_t kPrefillMinRunTiles = 16;  // 512 keys
+
+extern "C" int32_t kv_paged_attention_prefill_choose_splits(const int32_t* query_start_host,
+                                                            const int32_t* context_lens_host,
+                                                            int32_t S, int32_t num_q_heads,
+                                                            int32_t num_kv_heads,
+                                                            int32_t min_units) {
+  const int32_t rpb = kv_paged_attention_prefill_rows_per_item(num_q_heads, num_kv_heads);
+  if (rpb <= 0 || S <= 0 || !query_start_host || !context_lens_host || min_units <= 0) return 1;
+  int64_t items = 0, max_tiles = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    const int64_t C = (int64_t)query_start_host[s + 1] - query_start_host[s];
+    const int64_t L = context_lens_host[s];
+    if (C <= 0 || L < C) continue;
+    items += (C + rpb - 1) / rpb;
+    max_tiles = std::max<int64_t>(max_tiles, (L + 31) / 32);  // the last block sees every key
+  }
+  const int64_t units = items * num_kv_heads;
+  if (units == 0 || units >= min_units) return 1;
+  int64_t splits = (min_units + units - 1) / units;
+  splits = std::min<int64_t>(splits, max_tiles / kPrefillMinRunTiles);
+  splits = std::min<int64_t>(splits, KV_PREFILL_MAX_SPLITS);
+  return (int32_t)std::max<int64_t>(1, splits);
+}
+
 // A partition size for a decode batch: the largest of 1024, 768 and 512
 // tokens (a multiple of the block size) whose
 // work units - KV heads times the partitions of every sequence - still

@@ -57,10 +57,43 @@ struct PrefillParams {
   const int32_t* lens;     // [S] cached positions, the chunk included
   const int32_t* q_start;  // [S + 1] first query row of each sequence
   const int32_t* items;    // optional [n_items][2] = (sequence, query block)
-  int32_t T, S, Hq, Hkv, G, tpc, rows_per_block, max_blocks, num_blocks, n_units;
+  int32_t T, S, Hq, Hkv, G, tpc, rows_per_block, max_blocks, num_blocks, n_units, block_size;
   float scale_log2;  // scale * log2(e), times the K scale for an fp8 cache
   float v_scale;     // fp8 cache: the V scale, applied to the output
+  // key split: each block's keys in `splits` runs of whole tiles, one
+  // workgroup each, whose unnormalised results go to the workspace:
+  int32_t splits;  // 1: no split, the kernel writes `out` itself
+  float* ws_o;     // [splits][T][Hq][D] fp32, sum of weight x value (V scale applied)
+  float* ws_ml;    // [splits][T][Hq][2] fp32: running max (log2 units) and weight sum
 };
+
+// Work unit b: (sequence, query block, KV head, key run). The KV head varies
+// fastest, so a head's units share one XCD's L2, then the key run, then the
+// plan's item (or, without a plan, the sequence, then the query block).
+struct PfUnit {
+  int s, qblk, h, run;
+};
+__device__ __forceinline__ PfUnit pf_unit(const PrefillParams& p, int b, int splits) {
+  PfUnit u;
+  u.h = b % p.Hkv;
+  const int rest = b / p.Hkv;
+  u.run = rest % splits;
+  const int it = rest / splits;
+  if (p.items) {
+    u.s = p.items[2 * it];
+    u.qblk = p.items[2 * it + 1];
+  } else {
+    u.s = it % p.S;
+    u.qblk = it / p.S;
+  }
+  return u;
+}
+
+// Tiles per key run of a block with ntiles tiles: runs of equal length, so
+// the last ones may be shorter or empty.
+__device__ __forceinline__ int pf_run_tiles(int ntiles, int splits) {
+  return (ntiles + splits - 1) / splits;
+}
 
 // Column tile of MFMA columns: query row of column c and whether it is live.
 struct ColTile {
@@ -87,17 +120,8 @@ void prefill_mfma_kernel(PrefillParams p) {
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
 
-  int s, h, qblk;
-  if (p.items) {
-    const int it = blockIdx.x / p.Hkv;
-    h = blockIdx.x % p.Hkv;
-    s = p.items[2 * it];
-    qblk = p.items[2 * it + 1];
-  } else {
-    s = blockIdx.x % p.S;
-    h = (blockIdx.x / p.S) % p.Hkv;
-    qblk = blockIdx.x / (p.S * p.Hkv);
-  }
+  const PfUnit un = pf_unit(p, blockIdx.x, p.splits);
+  const int s = un.s, h = un.h, qblk = un.qblk;
   if (s < 0 || s >= p.S || qblk < 0) return;
   const int r_begin = p.q_start[s], r_end = p.q_start[s + 1];
   if (r_begin < 0 || r_end > p.T || r_end < r_begin) return;  // no row can be placed safely
@@ -120,7 +144,12 @@ void prefill_mfma_kernel(PrefillParams p) {
   const int prev = L - C;
   const int nkeys = prev + row0 + rows;  // keys the block's last query sees
   const int ntiles = (nkeys + kPfKeys - 1) / kPfKeys;
-  const int last = ntiles - 1;
+  // this unit's run of tiles [jb, last]; an empty run (a short block split as
+  // finely as the longest) has nothing to add and writes nothing
+  const int tpr = pf_run_tiles(ntiles, p.splits);
+  const int jb = un.run * tpr;
+  const int last = min(ntiles, jb + tpr) - 1;
+  if (jb > last) return;
   const int nblk = (nkeys + BS - 1) / BS;  // table entries in use
 
   // ---- columns and queries of this wave --------------------------------------
@@ -242,7 +271,10 @@ void prefill_mfma_kernel(PrefillParams p) {
   for (int t = 0; t < CT; ++t) {
 #pragma unroll
     for (int n = 0; n < 8; ++n) o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[t] = neg_inf();
+    // the lowest finite value, not -inf: a column none of whose keys in a
+    // run is visible (a later run of a split block) then gets weights
+    // exp2(-inf - m) = 0 rather than NaN, and rescale factors exp2(m - new) 0
+    m[t] = -3.402823466e38f;
     l[t] = 0.f;
   }
   // smallest position among the block's queries
@@ -325,7 +357,7 @@ void prefill_mfma_kernel(PrefillParams p) {
 #pragma unroll
       for (int t = 0; t < CT; ++t) {
         const float mn = fmaxf(m[t], column_max(lm[t]));
-        const float alpha = fast_exp2(m[t] - mn);  // 0 while m is -inf
+        const float alpha = fast_exp2(m[t] - mn);  // 0 while m is the initial value
         l[t] *= alpha;
 #pragma unroll
         for (int n = 0; n < 8; ++n) o[t][n] *= alpha;
@@ -355,17 +387,17 @@ void prefill_mfma_kernel(PrefillParams p) {
   // stored into LDS buffer t % 2 and computed after a barrier; loads and
   // stores past the last tile repeat the last tile (in bounds, never computed)
   uint4 g0[4], g1[4];
-  load(0, g0);
-  store(0, g0, 0);
-  load(min(1, last), g1);
-  load(min(2, last), g0);
+  load(jb, g0);
+  store(jb, g0, 0);
+  load(min(jb + 1, last), g1);
+  load(min(jb + 2, last), g0);
   __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
+  for (int j = jb; j <= last; j += 2) {
     compute(j, 0);
     store(min(j + 1, last), g1, 1);
     load(min(j + 3, last), g1);
     __syncthreads();
-    if (j + 1 >= ntiles) break;
+    if (j + 1 > last) break;
     compute(j + 1, 1);
     store(min(j + 2, last), g0, 0);
     load(min(j + 4, last), g0);
@@ -373,19 +405,89 @@ void prefill_mfma_kernel(PrefillParams p) {
   }
 
   // ---- results: lane holds column col, dims 16n + 4grp + r (r < 4) -----------
+  // Unsplit: the normalised output. Split: the run's unnormalised sum and its
+  // (max, weight sum), combined by prefill_merge_kernel.
+  const bool split = p.splits > 1;
 #pragma unroll
   for (int t = 0; t < CT; ++t) {
     const float lt = column_sum(l[t]);
     if (!ct[t].live) continue;
-    const float inv = (KV8 ? p.v_scale : 1.0f) / lt;
-    float* dst = out + (((size_t)r_begin + ct[t].qrow) * p.Hq + (size_t)h * p.G + hd) * D +
-                 4 * grp;
+    const float vs = KV8 ? p.v_scale : 1.0f;
+    const float inv = split ? vs : vs / lt;
+    const size_t orow = ((size_t)(split ? un.run : 0) * p.T + r_begin + ct[t].qrow) * p.Hq +
+                        (size_t)h * p.G + hd;
+    float* dst = (split ? p.ws_o : out) + orow * D + 4 * grp;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       float4 a = make_float4(o[t][n][0] * inv, o[t][n][1] * inv, o[t][n][2] * inv, o[t][n][3] * inv);
       if (bad) a = make_float4(nan, nan, nan, nan);
       *reinterpret_cast<float4*>(dst + 16 * n) = a;
     }
+    if (split && grp == 0)
+      *reinterpret_cast<float2*>(p.ws_ml + 2 * orow) =
+          bad ? make_float2(nan, nan) : make_float2(m[t], lt);
+  }
+}
+
+// Combines the key runs of a split launch: for each (query row, head) of a
+// block, out = sum_r 2^(m_r - M) o_r / sum_r 2^(m_r - M) l_r with M = max_r m_r
+// over the block's non-empty runs (the online-softmax rescale of the pages'
+// partition-and-reduce, [2] "The Custom CUDA Kernel"). A NaN partial (an
+// out-of-pool table entry) makes the row NaN. One workgroup per (plan item,
+// query row of its block, KV head), a thread per (head of the group, 4
+// dims); rows of a sequence with an impossible length were written (NaN) by
+// the attention kernel and are left alone.
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
+  constexpr int D = kPfHeadDim;
+  const int rr = blockIdx.x % p.rows_per_block;  // row within the block
+  const PfUnit un = pf_unit(p, blockIdx.x / p.rows_per_block, 1);
+  const int s = un.s, h = un.h, qblk = un.qblk;
+  if (s < 0 || s >= p.S || qblk < 0) return;
+  const int r_begin = p.q_start[s], r_end = p.q_start[s + 1];
+  if (r_begin < 0 || r_end > p.T || r_end < r_begin) return;
+  const int C = r_end - r_begin;
+  const int row0 = qblk * p.rows_per_block;
+  if (row0 + rr >= C) return;
+  const int rows = min(p.rows_per_block, C - row0);
+  const int L = p.lens[s];
+  if (L < C || (int64_t)L > (int64_t)p.max_blocks * p.block_size) return;
+  const int nkeys = L - C + row0 + rows;
+  const int ntiles = (nkeys + kPfKeys - 1) / kPfKeys;
+  const int tpr = pf_run_tiles(ntiles, p.splits);
+  const int runs = (ntiles + tpr - 1) / tpr;  // non-empty runs
+  const size_t plane = (size_t)p.T * p.Hq;     // rows of one run in the workspace
+  const float2* ml = reinterpret_cast<const float2*>(p.ws_ml);
+  for (int i = threadIdx.x; i < p.G * (D / 4); i += blockDim.x) {
+    const int g = i / (D / 4), c4 = i % (D / 4);
+    const size_t orow = ((size_t)r_begin + row0 + rr) * p.Hq + (size_t)h * p.G + g;
+    bool nan_seen = false;
+    float M = -3.402823466e38f;
+#pragma unroll 8
+    for (int r = 0; r < runs; ++r) {
+      const float mr = ml[r * plane + orow].x;
+      nan_seen = nan_seen || __builtin_isnan(mr);
+      M = fmaxf(M, mr);
+    }
+    float Lsum = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int r = 0; r < runs; ++r) {
+      const float2 mlr = ml[r * plane + orow];
+      const float w = exp2f(mlr.x - M);
+      const float4 v = reinterpret_cast<const float4*>(p.ws_o + (r * plane + orow) * D)[c4];
+      Lsum += w * mlr.y;
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+      acc.z += w * v.z;
+      acc.w += w * v.w;
+    }
+    const float inv = 1.0f / Lsum;
+    float4 res = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (nan_seen) {
+      const float nanv = __builtin_nanf("");
+      res = make_float4(nanv, nanv, nanv, nanv);
+    }
+    reinterpret_cast<float4*>(p.out + orow * D)[c4] = res;
   }
 }
 
@@ -412,7 +514,8 @@ kv_status prefill_impl(const char* who, float* out, const void* q, const void* k
                        int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                        kv_dtype dtype, int32_t max_query_len, const int32_t* work_items,
                        int32_t n_items, hipStream_t stream, bool kv8, float k_scale,
-                       float v_scale) {
+                       float v_scale, int32_t splits = 1, void* workspace = nullptr,
+                       size_t ws_bytes = 0) {
   if (dtype != KV_F16 && dtype != KV_BF16)
     return fail(KV_ERR_UNSUPPORTED, "%s: dtype must be f16 or bf16", who);
   if (S < 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks < 0 ||
@@ -437,10 +540,20 @@ kv_status prefill_impl(const char* who, float* out, const void* q, const void* k
     return fail(KV_ERR_INVALID, "%s: out/q/pools must be 16-byte aligned", who);
   if (work_items && n_items <= 0)
     return fail(KV_ERR_INVALID, "%s: work plan with %d items", who, n_items);
+  if (splits < 1 || splits > KV_PREFILL_MAX_SPLITS)
+    return fail(KV_ERR_INVALID, "%s: %d key splits (1..%d)", who, splits, KV_PREFILL_MAX_SPLITS);
+  if (splits > 1) {
+    const size_t need = kv_paged_attention_prefill_workspace_bytes(total_q, num_q_heads, head_dim,
+                                                                   splits);
+    if (!workspace || ws_bytes < need || !aligned16(workspace))
+      return fail(KV_ERR_INVALID, "%s: workspace of %zu bytes needed (got %zu)", who, need,
+                  workspace ? ws_bytes : (size_t)0);
+  }
   const int32_t rpb = rows_per_block(G);
   const int64_t n_units = work_items ? (int64_t)n_items * num_kv_heads
                                      : (int64_t)S * num_kv_heads * ceil_div64(max_query_len, rpb);
-  if (n_units > INT32_MAX) return fail(KV_ERR_INVALID, "%s: too many work units", who);
+  if (n_units * std::max<int64_t>(splits, rpb) > INT32_MAX)
+    return fail(KV_ERR_INVALID, "%s: too many work units", who);
   if (n_units == 0) return KV_OK;
 
   PrefillParams prm = {};  // shared_len 0, no lse: the chunked-prefill mode
@@ -464,9 +577,19 @@ kv_status prefill_impl(const char* who, float* out, const void* q, const void* k
   prm.n_units = (int32_t)n_units;
   prm.scale_log2 = scale * 1.4426950408889634f * (kv8 ? k_scale : 1.0f);
   prm.v_scale = v_scale;
+  prm.block_size = block_size;
+  prm.splits = splits;
+  if (splits > 1) {
+    prm.ws_o = static_cast<float*>(workspace);
+    prm.ws_ml = prm.ws_o + (size_t)splits * total_q * num_q_heads * head_dim;
+  }
 
   auto kern = kv8 ? pick_kernel<true>(dtype, block_size) : pick_kernel<false>(dtype, block_size);
-  hipLaunchKernelGGL(kern, dim3((unsigned)n_units), dim3(kPfWaves * 64), 0, stream, prm);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(n_units * splits)), dim3(kPfWaves * 64), 0, stream,
+                     prm);
+  if (splits > 1)
+    hipLaunchKernelGGL(prefill_merge_kernel, dim3((unsigned)(n_units * rpb)), dim3(256), 0, stream,
+                       prm);
   return launch_status(who);
 }
 
@@ -494,6 +617,47 @@ kv_status kv_paged_attention_prefill(float* out, const void* q, const void* k_po
                       max_blocks, context_lens, query_start, S, total_q, num_q_heads,
                       num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                       max_query_len, work_items, n_items, stream, false, 1.0f, 1.0f);
+}
+
+size_t kv_paged_attention_prefill_workspace_bytes(int32_t total_q, int32_t num_q_heads,
+                                                 int32_t head_dim, int32_t splits) {
+  if (total_q <= 0 || num_q_heads <= 0 || head_dim <= 0 || splits <= 1) return 0;
+  // per run and row: head_dim sums, then (max, weight sum), for every query head
+  return (size_t)splits * total_q * num_q_heads * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+kv_status kv_paged_attention_prefill_split(float* out, const void* q, const void* k_pool,
+                                           const void* v_pool, const int32_t* block_tables,
+                                           int32_t max_blocks, const int32_t* context_lens,
+                                           const int32_t* query_start, int32_t S, int32_t total_q,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t num_blocks, float scale, kv_dtype dtype,
+                                           int32_t max_query_len, const int32_t* work_items,
+                                           int32_t n_items, int32_t splits, void* workspace,
+                                           size_t ws_bytes, hipStream_t stream) {
+  pagedkv::clear_error();
+  return prefill_impl("kv_paged_attention_prefill_split", out, q, k_pool, v_pool, block_tables,
+                      max_blocks, context_lens, query_start, S, total_q, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                      max_query_len, work_items, n_items, stream, false, 1.0f, 1.0f, splits,
+                      workspace, ws_bytes);
+}
+
+kv_status kv_paged_attention_prefill_split_fp8(
+    float* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+    const int32_t* query_start, int32_t S, int32_t total_q, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    kv_dtype dtype, float k_scale, float v_scale, int32_t max_query_len,
+    const int32_t* work_items, int32_t n_items, int32_t splits, void* workspace, size_t ws_bytes,
+    hipStream_t stream) {
+  pagedkv::clear_error();
+  return prefill_impl("kv_paged_attention_prefill_split_fp8", out, q, k_pool, v_pool,
+                      block_tables, max_blocks, context_lens, query_start, S, total_q,
+                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                      max_query_len, work_items, n_items, stream, true, k_scale, v_scale, splits,
+                      workspace, ws_bytes);
 }
 
 kv_status kv_paged_attention_prefill_fp8(float* out, const void* q, const void* k_pool,

@@ -33,12 +33,15 @@ from . import binding as kv
 # 2048 waves an MI355X runs at once (256 CUs x 8 waves), measured best.
 AUTO_PARTITION_MIN_UNITS = 1500
 MI355X_CUS = 256
+# Prefill workgroups (4 waves each) per compute unit below which a chunk's
+# keys are split into runs: two fill a CU at the kernel's register use.
+PREFILL_UNITS_PER_CU = 2
 
 class DecodeSession:
     def __init__(self, *, k_pool, v_pool, num_q_heads: int, free_order: Optional[Sequence[int]] = None,
                  partition_size: int = 0, use_plan: bool = True, fused: bool = True,
                  k_scale: float = 1.0, v_scale: float = 1.0, shared_prefix: bool = True,
-                 num_cus: Optional[int] = None):
+                 num_cus: Optional[int] = None, prefill_splits: Optional[int] = None):
         import torch
         self.torch = torch
         NB, Hkv, B, D = k_pool.shape
@@ -68,6 +71,11 @@ class DecodeSession:
             num_cus = (torch.cuda.get_device_properties(self.device).multi_processor_count
                        if self.device.type == "cuda" else MI355X_CUS)
         self.num_cus = int(num_cus)
+        # key runs per prefill block: None chooses per step
+        # (kv_paged_attention_prefill_choose_splits), else a fixed count
+        self.prefill_splits = prefill_splits
+        self.step_splits = 1
+        self.d_prefill_ws = None
 
     def close(self) -> None:
         if self.pool:
@@ -192,6 +200,12 @@ class DecodeSession:
         if self.use_plan:
             items = kv.kv_paged_attention_prefill_plan(q_start, lens, self.Hq, self.Hkv)
             self.d_items = torch.from_numpy(items).to(dev) if len(items) else None
+        self.step_splits = self.prefill_splits or kv.kv_paged_attention_prefill_choose_splits(
+            q_start, lens, self.Hq, self.Hkv, PREFILL_UNITS_PER_CU * self.num_cus)
+        need = kv.kv_paged_attention_prefill_workspace_bytes(int(q_start[-1]), self.Hq, self.D,
+                                                             self.step_splits)
+        if need and (self.d_prefill_ws is None or self.d_prefill_ws.numel() < need):
+            self.d_prefill_ws = torch.empty(need, dtype=torch.uint8, device=dev)
         return host_slots, pairs
 
     def prefill_step(self, q, k_new, v_new, out, scale: float, k_pool=None, v_pool=None,
@@ -207,7 +221,18 @@ class DecodeSession:
         self._write(k_new, v_new, kp, vp_, self.d_slots)
         if events is not None:
             events[0].record()
-        if self.fp8:
+        if self.step_splits > 1 and self.fp8:
+            kv.kv_paged_attention_prefill_split_fp8(out, q, kp, vp_, self.d_tables, self.d_lens,
+                                                    self.d_qstart, scale, self.k_scale,
+                                                    self.v_scale, self.max_query_len,
+                                                    self.step_splits, self.d_prefill_ws,
+                                                    self.d_items)
+        elif self.step_splits > 1:
+            kv.kv_paged_attention_prefill_split(out, q, kp, vp_, self.d_tables, self.d_lens,
+                                                self.d_qstart, scale, self.max_query_len,
+                                                self.step_splits, self.d_prefill_ws,
+                                                self.d_items)
+        elif self.fp8:
             kv.kv_paged_attention_prefill_fp8(out, q, kp, vp_, self.d_tables, self.d_lens,
                                               self.d_qstart, scale, self.k_scale, self.v_scale,
                                               self.max_query_len, self.d_items)

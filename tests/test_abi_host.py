@@ -446,6 +446,52 @@ def test_prefill_fp8_entry_point_validates_on_the_host(kv):
     assert call(S=0) == kv.KV_OK
 
 
+def test_prefill_split_entry_points_validate_on_the_host(kv):
+    lib = kv.lib
+    need = kv.kv_paged_attention_prefill_workspace_bytes(4, 8, 128, 4)
+    assert need == 4 * 4 * 8 * 130 * 4
+    assert kv.kv_paged_attention_prefill_workspace_bytes(4, 8, 128, 1) == 0
+    assert kv.kv_paged_attention_prefill_workspace_bytes(0, 8, 128, 4) == 0
+
+    def call(fp8=False, **k):
+        head = (None, None, None, None, None, 4, None, None, k.get("S", 1), 4, 8, 2, 128, 16, 8,
+                1.0, kv.KV_BF16)
+        scales = (k.get("ks", 1.0), 1.0) if fp8 else ()
+        tail = (4, None, 0, k.get("splits", 4), k.get("ws", None), k.get("ws_bytes", 0), None)
+        f = lib.kv_paged_attention_prefill_split_fp8 if fp8 else lib.kv_paged_attention_prefill_split
+        return f(*head, *scales, *tail)
+    for fp8 in (False, True):
+        assert call(fp8, splits=0) == kv.KV_ERR_INVALID
+        assert call(fp8, splits=kv.KV_PREFILL_MAX_SPLITS + 1) == kv.KV_ERR_INVALID
+        assert call(fp8) == kv.KV_ERR_INVALID                      # no workspace
+        assert call(fp8, ws=16, ws_bytes=need - 1) == kv.KV_ERR_INVALID
+        assert call(fp8, ws=8, ws_bytes=need) == kv.KV_ERR_INVALID  # misaligned
+        assert call(fp8, ws=16, ws_bytes=need) == kv.KV_ERR_INVALID  # null tensors
+        assert call(fp8, S=0) == kv.KV_OK
+        assert call(fp8, splits=1) == kv.KV_ERR_INVALID           # unsplit: null tensors
+    assert call(True, ks=0.0) == kv.KV_ERR_INVALID
+
+
+def test_prefill_split_choice(kv):
+    """No split while the plan's units (row blocks x KV heads) cover min_units;
+    else enough runs to reach it, each keeping 16 tiles of the longest block."""
+    ch = kv.kv_paged_attention_prefill_choose_splits
+    # 16 sequences x 256 rows (64/8 heads: 16-row blocks) = 2,048 units: no split
+    assert ch(list(range(0, 257 * 16, 256))[:17], [1024] * 16, 64, 8, 512) == 1
+    # one 16-row block over 32,768 keys: 8 units, 64 runs of 16 tiles
+    assert ch([0, 16], [32768], 64, 8, 512) == 64
+    # the same over 4,096 keys: 128 tiles allow 8 runs
+    assert ch([0, 16], [4096], 64, 8, 512) == 8
+    # 64 rows (4 blocks, 32 units) over 16,384 keys: 16 runs reach 512
+    assert ch([0, 64], [16384], 64, 8, 512) == 16
+    # a short context is never split
+    assert ch([0, 16], [300], 64, 8, 512) == 1
+    # invalid input: no split
+    assert ch([0, 16], [8], 64, 8, 512) == 1          # chunk longer than its context
+    assert ch([0, 16], [32768], 64, 2, 512) == 1      # group of 32
+    assert ch([0, 16], [32768], 64, 8, 0) == 1
+
+
 def test_load_policy_choice(kv):
     """Cached loads exactly when the pool holds shared blocks beyond the prefix a
     shared-prefix step reads once by itself."""

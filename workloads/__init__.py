@@ -167,6 +167,11 @@ SPECS = {
                     description="the chunked-prefill workload (same prefixes, chunks "
                                 "and queries) over an fp8 E4M3 cache with per-pool "
                                 "scales"),
+    10: WorkloadSpec(10, "llama70b-gqa-longprefix-prefill-bf16", S=4, Hq=64, Hkv=8, D=128,
+                     dtype="bf16", chunk=16,
+                     description="4 sequences, each with a 32752-token cached prefix "
+                                 "and a 16-token chunk attended causally (context "
+                                 "32768); 64 query / 8 KV heads, head_dim 128, bf16"),
     7: WorkloadSpec(7, "llama70b-gqa-fp8", S=128, Hq=64, Hkv=8, D=128, dtype="bf16",
                     kv_dtype="e4m3", k_scale=0.25, v_scale=0.25, seed_cfg=3,
                     description="the llama70b-gqa-bf16 workload (same lengths, "
@@ -244,7 +249,7 @@ def _context_lengths(sp: WorkloadSpec, rng: np.random.Generator) -> np.ndarray:
     if sp.cfg in (8, 9):
         x = np.exp(rng.normal(math.log(512.0), 0.86, size=sp.S))
         return (np.clip(np.rint(x), 0, 8192 - sp.chunk) + sp.chunk).astype(np.int32)
-    if sp.cfg == 4:
+    if sp.cfg in (4, 10):
         return np.full(sp.S, 32768, dtype=np.int32)
     if sp.cfg in (5, 6):
         return np.full(sp.S, sp.shared_prefix + sp.tail + 1, dtype=np.int32)
@@ -258,7 +263,7 @@ def _pool_blocks(sp: WorkloadSpec, lens: np.ndarray) -> int:
         return 32
     if sp.cfg == 2:
         return 8192 * 16 // B  # the worst case, 64 sequences of 2048 tokens
-    if sp.cfg in (3, 7, 8, 9):
+    if sp.cfg in (3, 7, 8, 9, 10):
         need = int(sum(-(-int(t) // B) for t in lens))
         return int(math.ceil(1.1 * need))
     if sp.cfg == 4:
