@@ -178,7 +178,8 @@ def pmc_parse(fetch_dir, write_dir, out_path, workload, partition):
     """HBM bytes per decode call from FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the calibration
     copy, whose true byte count is known. A shared-prefix decode call adds its
-    prefix attention (shared_prefix_kernel)."""
+    prefix attention (shared_prefix_kernel); a split call its merge launch
+    (splitk_merge_kernel, or prefill_merge_kernel for a prefill with key runs)."""
     cal_bytes = 2 * CAL_PAIRS * CAL_BLOCK_BYTES
     prefill = is_prefill(workload)
     res = {"workload": workload, "partition_arg": partition, "calibration_bytes": cal_bytes}
@@ -190,7 +191,7 @@ def pmc_parse(fetch_dir, write_dir, out_path, workload, partition):
         # copy-on-write copies run the same kernel on a few blocks
         cal, ncal = _max_counter(rows, "copy_blocks_kernel", counter)
         dec, ndec = _mean_counter(rows, "prefill_mfma" if prefill else "decode_", counter)
-        mrg, nmrg = _mean_counter(rows, "splitk_merge", counter)
+        mrg, nmrg = _mean_counter(rows, "prefill_merge" if prefill else "splitk_merge", counter)
         pre, npre = (0.0, 0) if prefill else _mean_counter(rows, "shared_prefix_kernel", counter)
         if ncal == 0 or ndec == 0:
             raise SystemExit(f"{d}: calibration or decode dispatches missing")
@@ -340,6 +341,19 @@ def prefill_flops(lens, counts, Hq, D):
     return total
 
 
+def prefill_alg_bytes(lens, counts, Hq, Hkv, D, eb, kv_eb, B=16):
+    """Algorithmic bytes of one chunked-prefill attention call: every cached
+    position's K and V once per sequence (kv_eb bytes per element), the
+    queries, the fp32 outputs, the live block-table entries, the lengths and
+    the chunk offsets."""
+    lens = np.asarray(lens, dtype=np.int64)
+    T = int(sum(counts))
+    nb = int(np.sum((lens + B - 1) // B))
+    S = len(lens)
+    return (kv_bytes(lens, Hkv, D, kv_eb) + T * Hq * D * eb + T * Hq * D * 4 + nb * 4
+            + S * 4 + (S + 1) * 4)
+
+
 def prefill_bench(args, w, kv, torch):
     """One step = the chunk's cache write + the causal attention of every chunk
     row (`DecodeSession.prefill_step`), timed like the decode step."""
@@ -387,7 +401,16 @@ def prefill_bench(args, w, kv, torch):
     att_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
     flops = prefill_flops(lens, counts, sp.Hq, sp.D)
     tflops_step = flops / (step_ms * 1e-3) / 1e12
-    achieved = flops / (att_ms * 1e-3) / 1e12
+    alg_bytes = prefill_alg_bytes(lens, counts, sp.Hq, sp.Hkv, sp.D, sp.elem_bytes,
+                                  sp.kv_elem_bytes, args.block_size)
+    # the bound is whichever floor is higher: the algorithmic flops at the
+    # dense bf16 matrix peak or the algorithmic bytes at the HBM peak (short
+    # chunks over long prefixes do few flops per K/V byte)
+    hbm_bound = alg_bytes / (HBM_PEAK_GBS * 1e9) > flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if hbm_bound:
+        achieved, peak, unit = alg_bytes / (att_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = flops / (att_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
     traffic = None
     tpath = args.pmc_traffic or os.path.join(ROOT, "profiles", f"prefill_traffic_w{args.workload}.json")
     if os.path.exists(tpath):
@@ -411,14 +434,14 @@ def prefill_bench(args, w, kv, torch):
                    "kv_cache_dtype": sp.cache_dtype, "key_runs_per_block": sess.step_splits},
         "query_tokens_per_s": round(T / (step_ms * 1e-3), 1),
         "attention_ms": round(att_ms, 5),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic,
                      "kernel": ("kv_paged_attention_prefill_split%s call: prefill_mfma_kernel "
                                 "+ prefill_merge_kernel" if sess.step_splits > 1 else
                                 "kv_paged_attention_prefill%s call: prefill_mfma_kernel")
                                % ("_fp8" if sp.kv_dtype else ""),
-                     "alg_flops_per_launch": flops},
+                     "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = prefill_cpu_baseline(w, lens, counts, args.cpu_seconds)
