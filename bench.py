@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=3, help="workload number 1-10")
+    ap.add_argument("--workload", type=int, default=3, help="workload number 1-11")
     ap.add_argument("--partition", type=int, default=0,
                     help="partition tokens (0 = chosen per batch by kv_paged_attention_choose_partition)")
     ap.add_argument("--block-size", type=int, default=16, help="tokens per KV block (8, 16 or 32)")
@@ -776,11 +776,11 @@ def run_decode(args, cfg, kv, torch, steps, warmup, primary):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "traffic_source": TRAFFIC_NOTE.format(w=cfg),
-                     "kernel": ("kv_paged_attention_decode_append_shared call: prefix attention "
-                                "once, then the tails' decode (+ split-K merge) folding it in"
-                                if shared else
-                                ("kv_paged_attention_decode_append%s call: decode kernel + split-K merge"
-                                 if not args.unfused else
+                     "kernel": (("kv_paged_attention_decode_append_shared%s call: prefix "
+                                 "attention once, then the tails' decode (+ split-K merge) "
+                                 "folding it in" if shared else
+                                 "kv_paged_attention_decode_append%s call: decode kernel + "
+                                 "split-K merge" if not args.unfused else
                                  "kv_paged_attention_decode%s call: decode kernel + split-K merge")
                                 % ("_fp8" if sp.kv_dtype else "")),
                      "alg_bytes_per_launch": alg},

@@ -394,19 +394,24 @@ int32_t kv_paged_attention_common_prefix(const int32_t* tables_host, int32_t S,
                                          int32_t max_blocks, const int32_t* context_lens_host,
                                          int32_t block_size);
 
-/* Shared positions for kv_paged_attention_decode_append_shared, or 0 when a
- * decode step over these sequences should take the plain step: the common
- * prefix above, where that entry point supports the step (dtype f16 or
- * bf16, head_dim 128, group size at most 16; a common prefix longer than
- * KV_SHARED_PREFIX_MAX_TOKENS is cut to it, the rest left to the tails) and
- * reading the prefix once per batch is expected to be faster than once per
- * sequence. The rule comes from shared/plain step times measured on MI355X
- * (32 query / 8 KV heads, bf16, 4-128 sequences, 256-4096 shared positions,
- * tails of 64 and 512 positions; a point counts as faster at a time ratio of
- * 0.97 or less): at least 4 sequences and 256 shared positions, and
- * sequences x shared positions >= 49,152. Every measured point with 65,536
- * prefix reads or more was faster (ratios 0.34-0.89, whatever the tail), and
- * of those with 32,768 or fewer one was (0.88); the threshold sits between. */
+/* Shared positions for kv_paged_attention_decode_append_shared (dtype f16
+ * or bf16: the pools' type) or kv_paged_attention_decode_append_shared_fp8
+ * (dtype KV_FP8_E4M3: an fp8 cache), or 0 when a decode step over these
+ * sequences should take the plain step: the common prefix above, where those
+ * entry points support the step (head_dim 128, group size at most 16; a
+ * common prefix longer than KV_SHARED_PREFIX_MAX_TOKENS is cut to it, the
+ * rest left to the tails) and reading the prefix once per batch is expected
+ * to be faster than once per sequence. The rule comes from shared/plain step
+ * times measured on MI355X (32 query / 8 KV heads, bf16 queries, 4-128
+ * sequences, 256-4096 shared positions, tails of 64 and 512 positions; a
+ * point counts as faster at a time ratio of 0.97 or less): at least 4
+ * sequences and 256 shared positions, and sequences x shared positions >=
+ * 49,152 (16-bit cache) or >= 98,304 (fp8 cache, half the bytes saved per
+ * read). 16-bit: every measured point with 65,536 prefix reads or more was
+ * faster (ratios 0.34-0.89, whatever the tail), and of those with 32,768 or
+ * fewer one was (0.88). fp8: every point with 131,072 reads or more was
+ * faster (0.42-0.94), 3 of the 8 at 65,536, none below. Each threshold sits
+ * between. */
 int32_t kv_paged_attention_choose_shared_prefix(const int32_t* tables_host, int32_t S,
                                                 int32_t max_blocks,
                                                 const int32_t* context_lens_host,
@@ -589,6 +594,27 @@ kv_status kv_paged_attention_decode_append_fp8(
     int32_t partition_size, int32_t max_context_len, const int32_t* work_items, int32_t n_items,
     void* workspace, size_t ws_bytes, int64_t* slots, kv_load_policy load_policy,
     hipStream_t stream);
+
+/* kv_paged_attention_decode_append_shared over fp8 pools ([1] "Memory
+ * sharing" with the cache of "How does this relate to quantization?"): the
+ * shared positions are read once for the batch and each sequence's tail by
+ * the fp8 decode kernels, the codes widened exactly to the query's type, the
+ * K scale folded into the scores and the V scale into every output before the
+ * prefix ranges and the tail are combined; the new token is written as
+ * kv_paged_attention_decode_append_fp8 writes it. The result is the
+ * attention over positions 0..t-1 of the dequantised cache (that of
+ * kv_paged_attention_decode_append_fp8 up to rounding order). Arguments,
+ * checks and scratch as for kv_paged_attention_decode_append_shared, with
+ * k_scale and v_scale as for kv_paged_attention_decode_append_fp8 (finite
+ * and > 0, else KV_ERR_INVALID); dtype is the query's type (f16 or bf16). */
+kv_status kv_paged_attention_decode_append_shared_fp8(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t S,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, float scale, kv_dtype dtype, float k_scale, float v_scale,
+    int32_t partition_size, int32_t shared_tokens, int32_t max_tail_len,
+    const int32_t* work_items, int32_t n_items, void* workspace, size_t ws_bytes, float* aux,
+    size_t aux_bytes, int64_t* slots, kv_load_policy load_policy, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Chunked prefill: several query tokens per sequence ([2] "The Successors -

@@ -114,6 +114,11 @@ _SIGS = {
                                                        i32, i32, i32, i32, i32, f32, C.c_int, f32,
                                                        f32, i32, i32, vp, i32, vp, C.c_size_t, vp,
                                                        C.c_int, vp]),
+    "kv_paged_attention_decode_append_shared_fp8": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                                              i32, i32, i32, i32, i32, i32, f32,
+                                                              C.c_int, f32, f32, i32, i32, i32, vp,
+                                                              i32, vp, C.c_size_t, vp, C.c_size_t,
+                                                              vp, C.c_int, vp]),
     "kv_paged_attention_prefill_rows_per_item": (i32, [i32, i32]),
     "kv_paged_attention_prefill_plan": (C.c_int, [P_i32, P_i32, i32, i32, i32, P_i32, i32, P_i32]),
     "kv_paged_attention_prefill": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32,
@@ -680,6 +685,40 @@ def kv_paged_attention_decode_append_fp8(out, q, k_new, v_new, k_pool, v_pool, b
         0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
         _dev(slots, "slots", torch.int64), int(load_policy), _stream(stream)),
         "kv_paged_attention_decode_append_fp8")
+
+
+def kv_paged_attention_decode_append_shared_fp8(out, q, k_new, v_new, k_pool, v_pool,
+                                                block_tables, context_lens, scale: float,
+                                                k_scale: float, v_scale: float,
+                                                shared_tokens: int, max_tail_len: int, slots, aux,
+                                                workspace=None, partition_size: int = 0,
+                                                work_items=None,
+                                                load_policy: int = KV_LOADS_STREAM,
+                                                stream=None) -> None:
+    """kv_paged_attention_decode_append_shared over uint8 E4M3 pools with per-pool scales;
+    q, k_new, v_new f16/bf16."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = _fp8_pools("kv_paged_attention_decode_append_shared_fp8", k_pool, v_pool)
+    if D2 != D or tuple(out.shape) != (S, Hq, D) or block_tables.shape[0] != S \
+            or context_lens.numel() != S or tuple(k_new.shape) != (S, Hkv, D) \
+            or k_new.shape != v_new.shape or k_new.dtype != q.dtype or v_new.dtype != q.dtype \
+            or slots.numel() != S:
+        raise KVError(KV_ERR_INVALID, "kv_paged_attention_decode_append_shared_fp8",
+                      "shape/dtype mismatch")
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                         workspace.numel() * workspace.element_size())
+    _check(lib.kv_paged_attention_decode_append_shared_fp8(
+        _dev(out, "out", torch.float32), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, B, NB, float(scale),
+        dtype_code(q), float(k_scale), float(v_scale), partition_size, shared_tokens,
+        max_tail_len, None if work_items is None else _dev(work_items, "work_items", torch.int32),
+        0 if work_items is None else work_items.shape[0], ws_ptr or None, ws_bytes,
+        _dev(aux, "aux"), aux.numel() * aux.element_size(), _dev(slots, "slots", torch.int64),
+        int(load_policy), _stream(stream)),
+        "kv_paged_attention_decode_append_shared_fp8")
 
 
 # ---------------------------------------------------------------------------

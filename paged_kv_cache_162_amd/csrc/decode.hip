@@ -226,7 +226,8 @@ kv_status decode_impl(float* out, const void* q, const void* k_pool, const void*
     // the prefix pass first: the decode kernels fold its results into the outputs
     const kv_status ps = pagedkv::shared_prefix_attention(
         pre->o, pre->lse, q, k_pool, v_pool, block_tables, max_blocks, S, num_q_heads,
-        num_kv_heads, block_size, num_blocks, scale, dtype, pre->tokens, stream);
+        num_kv_heads, block_size, num_blocks, scale, dtype, pre->tokens, kv8, k_scale, v_scale,
+        stream);
     if (ps != KV_OK) return ps;
     prm.skip_tokens = pre->tokens;
     prm.pre_o = pre->o;
@@ -325,16 +326,19 @@ size_t kv_paged_attention_shared_aux_bytes(int32_t S, int32_t num_q_heads, int32
   return (size_t)parts * (head_dim + 1) * S * num_q_heads * sizeof(float);
 }
 
-kv_status kv_paged_attention_decode_append_shared(
-    float* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
-    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t S,
-    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-    int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
-    int32_t shared_tokens, int32_t max_tail_len, const int32_t* work_items, int32_t n_items,
-    void* workspace, size_t ws_bytes, float* aux, size_t aux_bytes, int64_t* slots,
-    kv_load_policy load_policy, hipStream_t stream) {
-  pagedkv::clear_error();
-  const char* who = "kv_paged_attention_decode_append_shared";
+namespace {
+
+// Both shared-prefix entry points: checks, then decode_impl with the prefix.
+kv_status shared_impl(const char* who, float* out, const void* q, const void* k_new,
+                      const void* v_new, void* k_pool, void* v_pool, const int32_t* block_tables,
+                      int32_t max_blocks, const int32_t* context_lens, int32_t S,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, float scale, kv_dtype dtype,
+                      int32_t partition_size, int32_t shared_tokens, int32_t max_tail_len,
+                      const int32_t* work_items, int32_t n_items, void* workspace,
+                      size_t ws_bytes, float* aux, size_t aux_bytes, int64_t* slots,
+                      kv_load_policy load_policy, hipStream_t stream, bool kv8, float k_scale,
+                      float v_scale) {
   if (dtype != KV_F16 && dtype != KV_BF16)
     return fail(KV_ERR_UNSUPPORTED, "%s: dtype must be f16 or bf16", who);
   if (head_dim != 128) return fail(KV_ERR_UNSUPPORTED, "%s: head_dim %d (128)", who, head_dim);
@@ -349,6 +353,9 @@ kv_status kv_paged_attention_decode_append_shared(
                 KV_SHARED_PREFIX_MAX_TOKENS);
   if (num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 && num_q_heads / num_kv_heads > 16)
     return fail(KV_ERR_UNSUPPORTED, "%s: group size %d > 16", who, num_q_heads / num_kv_heads);
+  if (kv8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !std::isfinite(k_scale) ||
+              !std::isfinite(v_scale)))
+    return fail(KV_ERR_INVALID, "%s: scales must be finite and > 0", who);
   if (S < 0) return fail(KV_ERR_INVALID, "%s: bad sizes", who);
   if (S == 0) return KV_OK;
   if (!k_new || !v_new || !slots || !aux)
@@ -369,7 +376,41 @@ kv_status kv_paged_attention_decode_append_shared(
   return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, S,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                      partition_size, max_tail_len, work_items, n_items, workspace, ws_bytes, k_new,
-                     v_new, slots, load_policy, stream, false, 1.0f, 1.0f, &pre);
+                     v_new, slots, load_policy, stream, kv8, k_scale, v_scale, &pre);
+}
+
+}  // namespace
+
+kv_status kv_paged_attention_decode_append_shared(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t S,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, float scale, kv_dtype dtype, int32_t partition_size,
+    int32_t shared_tokens, int32_t max_tail_len, const int32_t* work_items, int32_t n_items,
+    void* workspace, size_t ws_bytes, float* aux, size_t aux_bytes, int64_t* slots,
+    kv_load_policy load_policy, hipStream_t stream) {
+  pagedkv::clear_error();
+  return shared_impl("kv_paged_attention_decode_append_shared", out, q, k_new, v_new, k_pool,
+                     v_pool, block_tables, max_blocks, context_lens, S, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, dtype, partition_size,
+                     shared_tokens, max_tail_len, work_items, n_items, workspace, ws_bytes, aux,
+                     aux_bytes, slots, load_policy, stream, false, 1.0f, 1.0f);
+}
+
+kv_status kv_paged_attention_decode_append_shared_fp8(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t S,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, float scale, kv_dtype dtype, float k_scale, float v_scale,
+    int32_t partition_size, int32_t shared_tokens, int32_t max_tail_len,
+    const int32_t* work_items, int32_t n_items, void* workspace, size_t ws_bytes, float* aux,
+    size_t aux_bytes, int64_t* slots, kv_load_policy load_policy, hipStream_t stream) {
+  pagedkv::clear_error();
+  return shared_impl("kv_paged_attention_decode_append_shared_fp8", out, q, k_new, v_new, k_pool,
+                     v_pool, block_tables, max_blocks, context_lens, S, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, dtype, partition_size,
+                     shared_tokens, max_tail_len, work_items, n_items, workspace, ws_bytes, aux,
+                     aux_bytes, slots, load_policy, stream, true, k_scale, v_scale);
 }
 
 kv_status kv_paged_attention_decode_fp8(float* out, const void* q, const void* k_pool,

@@ -990,11 +990,22 @@ kv_status launch_decode_kernel(const DecodeParams& prm, kv_dtype dtype, int head
 }
 
 // fp8 cache, f16 or bf16 queries: the MFMA kernel for every group size
-// (1..16) at head_dim 128, the vector-ALU kernel at head_dim 64.
+// (1..16) at head_dim 128, the vector-ALU kernel at head_dim 64; the
+// shared-prefix step's tails (head_dim 128) take the MFMA variants that fold
+// the prefix ranges into the outputs.
 template <int BS, bool NT>
 kv_status launch_decode_kernel_fp8(const DecodeParams& prm, kv_dtype dtype, int head_dim, int G,
                                    hipStream_t st) {
   constexpr int R = kDecodeRing8;
+  if (prm.pre_parts) {
+    if (G <= 8)
+      return dtype == KV_BF16
+                 ? launch_decode(decode_mfma_kernel<KV_BF16, true, R, BS, true, NT, true>, prm, st)
+                 : launch_decode(decode_mfma_kernel<KV_F16, true, R, BS, true, NT, true>, prm, st);
+    return dtype == KV_BF16
+               ? launch_decode(decode_mfma_kernel<KV_BF16, false, R, BS, true, NT, true>, prm, st)
+               : launch_decode(decode_mfma_kernel<KV_F16, false, R, BS, true, NT, true>, prm, st);
+  }
   if (head_dim == 64)
     return dtype == KV_BF16 ? launch_valu<KV_BF16, 64, BS, NT, true>(prm, group_bucket(G), st)
                             : launch_valu<KV_F16, 64, BS, NT, true>(prm, group_bucket(G), st);

@@ -269,14 +269,16 @@ int32_t shared_prefix_parts(int32_t S, int32_t num_q_heads, int32_t num_kv_heads
 // Attention of S decode queries over the first shared_len positions of table
 // row 0, which every sequence of the call shares, one launch over the ranges
 // of shared_prefix_parts: range k's normalised outputs to o + k*S*Hq*D, log2
-// of its softmax denominators (base-2 units) to lse + k*S*Hq. Defined in
+// of its softmax denominators (base-2 units) to lse + k*S*Hq. With kv8 the
+// pools hold E4M3 codes: the K scale multiplies the scores (and so enters the
+// denominators' units) and the V scale the outputs. Defined in
 // shared_prefix.hip; the caller checks the arguments.
 kv_status shared_prefix_attention(float* o, float* lse, const void* q, const void* k_pool,
                                   const void* v_pool, const int32_t* table_row0,
                                   int32_t max_blocks, int32_t S, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t block_size, int32_t num_blocks,
-                                  float scale, kv_dtype dtype, int32_t shared_len,
-                                  hipStream_t stream);
+                                  float scale, kv_dtype dtype, int32_t shared_len, bool kv8,
+                                  float k_scale, float v_scale, hipStream_t stream);
 }  // namespace pagedkv
 
 #endif  // PAGEDKV_DEVICE_COMMON_H_

@@ -189,6 +189,9 @@ namespace {
 constexpr int32_t kSharedMinSeqs = 4;
 constexpr int32_t kSharedMinTokens = 256;
 constexpr int64_t kSharedMinReads = 49152;  // sequences x shared positions
+// an fp8 cache saves half the bytes per position read once instead of per
+// sequence, so the prefix must be read about twice as often to pay
+constexpr int64_t kSharedMinReadsFp8 = 98304;
 }  // namespace
 
 extern "C" int32_t kv_paged_attention_common_prefix(const int32_t* tables_host, int32_t S,
@@ -215,12 +218,14 @@ extern "C" int32_t kv_paged_attention_choose_shared_prefix(
     const int32_t* tables_host, int32_t S, int32_t max_blocks, const int32_t* context_lens_host,
     int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     kv_dtype dtype) {
-  if ((dtype != KV_F16 && dtype != KV_BF16) || head_dim != 128 || num_kv_heads <= 0 ||
-      num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 16 || S < kSharedMinSeqs)
+  if ((dtype != KV_F16 && dtype != KV_BF16 && dtype != KV_FP8_E4M3) || head_dim != 128 ||
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 16 ||
+      S < kSharedMinSeqs)
     return 0;
   int32_t shared =
       kv_paged_attention_common_prefix(tables_host, S, max_blocks, context_lens_host, block_size);
   if (shared > KV_SHARED_PREFIX_MAX_TOKENS)  // whole blocks: every block size divides the limit
     shared = KV_SHARED_PREFIX_MAX_TOKENS;
-  return (shared < kSharedMinTokens || (int64_t)S * shared < kSharedMinReads) ? 0 : shared;
+  const int64_t min_reads = dtype == KV_FP8_E4M3 ? kSharedMinReadsFp8 : kSharedMinReads;
+  return (shared < kSharedMinTokens || (int64_t)S * shared < min_reads) ? 0 : shared;
 }

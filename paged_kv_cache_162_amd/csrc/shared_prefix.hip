@@ -19,7 +19,9 @@
 // all of a workgroup's waves hold the same 16 columns and each streams its
 // own contiguous slice of the range's keys, with the decode kernel's register
 // layouts (K straight into the score MFMA's A operand, V regrouped with
-// v_perm, weights as a 16-bit high part plus residual). At the end the W
+// v_perm, weights as a 16-bit high part plus residual; an fp8 cache's codes
+// are widened exactly to the query's 16-bit type as they arrive, the K scale
+// folded into the scores and the V scale into the outputs). At the end the W
 // (max, sum, output) states of each column are merged through LDS into one
 // normalised output and log2 denominator per column and range. A range
 // covers W slices, so the pass writes few partial results (four ranges on a
@@ -52,13 +54,14 @@ struct SharedParams {
   const int32_t* table;  // row 0 of the block tables: the shared blocks first
   int32_t shared_len, ranges, range_keys, wave_keys, col_tiles;
   int32_t S, Hq, Hkv, G, num_blocks;
-  float scale_log2;      // scale * log2(e)
+  float scale_log2;      // scale * log2(e), times the K scale for an fp8 cache
+  float v_scale;         // fp8 cache: multiplies the outputs (1 otherwise)
 };
 
-template <int DT, int BS>
+template <int DT, int BS, bool KV8>
 __global__ __launch_bounds__(64 * kShMaxWaves) void shared_prefix_kernel(SharedParams p) {
   constexpr int D = 128;
-  constexpr int kRowU4 = D / 8;  // uint4 per token row of the pools
+  constexpr int kRowU4 = KV8 ? D / 16 : D / 8;  // uint4 per token row of the pools
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nwaves = (int)(blockDim.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
@@ -72,7 +75,9 @@ __global__ __launch_bounds__(64 * kShMaxWaves) void shared_prefix_kernel(SharedP
   const int nk = max(0, min(kr1, k0 + p.wave_keys) - k0);
 
   // the lane's column and its query: B operand of the score MFMA, dims
-  // 32kc + 8grp .. +8 (dead columns of the last tile get zeros, never stored)
+  // 32kc + 8grp .. +8 (fp8 cache: dims 16grp + 8kc .. for kc < 2 and
+  // 64 + 16grp + 8(kc - 2) .. for kc >= 2, the order of the lane's two
+  // 16-byte K code loads); dead columns of the last tile get zeros, never stored
   const int cidx = ctile * 16 + col;
   const bool live = cidx < p.S * p.G;
   const size_t orow = live ? (size_t)(cidx / p.G) * p.Hq + (size_t)h * p.G + cidx % p.G : 0;
@@ -81,7 +86,7 @@ __global__ __launch_bounds__(64 * kShMaxWaves) void shared_prefix_kernel(SharedP
     const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const char*>(p.q) + orow * D * 2);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const uint4 v = qp[kc * 4 + grp];
+      const uint4 v = qp[KV8 ? (kc >> 1) * 8 + 2 * grp + (kc & 1) : kc * 4 + grp];
       qb[kc] = live ? v : make_uint4(0, 0, 0, 0);
     }
   }
@@ -100,22 +105,34 @@ __global__ __launch_bounds__(64 * kShMaxWaves) void shared_prefix_kernel(SharedP
   for (int n = 0; n < 8; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = neg_inf(), l = 0.f;
   const uint4* kbase = static_cast<const uint4*>(p.k_pool);
-  const uint4* vbase = static_cast<const uint4*>(p.v_pool);
   const int nblk = (nk + kTile - 1) / kTile;  // 16-key tiles
   const int last = nblk - 1;
 
-  // K: row col of the tile, chunks kc*4+grp; V: rows 4grp..4grp+3, chunk col.
-  // Rows past the slice read its last row or row group instead (masked).
-  auto load = [&](int j, uint4* ku, uint4* vu) {
+  // K: row col of the tile, chunks kc*4+grp (fp8: the 16-code chunks grp and
+  // 4+grp); V: rows 4grp..4grp+3, chunk col (fp8: its 8 codes). Rows past the
+  // slice read its last row or row group instead (masked).
+  constexpr int kKU = KV8 ? 2 : 4;
+  typedef typename std::conditional<KV8, uint2, uint4>::type VRaw;
+  auto load = [&](int j, uint4* ku, VRaw* vu) {
     const int lim = nk - j * kTile - 1;  // last row of tile j in the slice
     const uint4* kt = kbase + tile_row<BS>(dp, h, staged, j, min(col, lim), kRowU4);
-    const uint4* vt = vbase + tile_row<BS>(dp, h, staged, j, 4 * min(grp, lim >> 2), kRowU4);
+    if constexpr (KV8) {
+      const uint2* vt = static_cast<const uint2*>(p.v_pool) +
+                        tile_row<BS>(dp, h, staged, j, 4 * min(grp, lim >> 2), 2 * kRowU4);
+      ku[0] = kt[grp];
+      ku[1] = kt[4 + grp];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) ku[kc] = kt[kc * 4 + grp];
+      for (int jj = 0; jj < 4; ++jj) vu[jj] = vt[jj * 2 * kRowU4 + col];
+    } else {
+      const uint4* vt = static_cast<const uint4*>(p.v_pool) +
+                        tile_row<BS>(dp, h, staged, j, 4 * min(grp, lim >> 2), kRowU4);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) vu[jj] = vt[jj * kRowU4 + col];
+      for (int kc = 0; kc < 4; ++kc) ku[kc] = kt[kc * 4 + grp];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) vu[jj] = vt[jj * kRowU4 + col];
+    }
   };
-  auto compute = [&](int jb, const uint4* ku, uint4* vu) {
+  auto compute16 = [&](int jb, const uint4* ku, uint4* vu) {
     f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) st = mfma_qk<DT>(ku[kc], qb[kc], st);
@@ -155,11 +172,27 @@ __global__ __launch_bounds__(64 * kShMaxWaves) void shared_prefix_kernel(SharedP
       o[n] = mfma_pv<DT>(a, pl, o[n]);
     }
   };
+  auto compute = [&](int jb, const uint4* ku, VRaw* vu) {
+    if constexpr (KV8) {
+      // the codes widened to the query's 16-bit type (exact), then as above
+      uint4 k16[4], v16[4];
+      k16[0] = e4m3x8_widen<DT>(ku[0].x, ku[0].y);
+      k16[1] = e4m3x8_widen<DT>(ku[0].z, ku[0].w);
+      k16[2] = e4m3x8_widen<DT>(ku[1].x, ku[1].y);
+      k16[3] = e4m3x8_widen<DT>(ku[1].z, ku[1].w);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v16[r] = e4m3x8_widen<DT>(vu[r].x, vu[r].y);
+      compute16(jb, k16, v16);
+    } else {
+      compute16(jb, ku, vu);
+    }
+  };
 
   // ring of kShRing tiles, as in the decode kernel: unconditional loads in
   // the steady state, guarded refills while draining
   if (nblk > 0) {
-    uint4 kr[kShRing][4], vr[kShRing][4];
+    uint4 kr[kShRing][kKU];
+    VRaw vr[kShRing][4];
 #pragma unroll
     for (int s = 0; s < kShRing; ++s) load(min(s, last), kr[s], vr[s]);
     int j = 0;
@@ -201,7 +234,8 @@ __global__ __launch_bounds__(64 * kShMaxWaves) void shared_prefix_kernel(SharedP
   }
   float L = 0.f;
   for (int w = 0; w < nwaves; ++w) L += sh_l[w][col] * fast_exp2(sh_m[w][col] - M);
-  const float a = fast_exp2(m - M) / L;
+  float a = fast_exp2(m - M) / L;
+  if constexpr (KV8) a *= p.v_scale;
   // lane holds column col, dims 32grp + 8r + n for r < 4, n < 8
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -275,11 +309,11 @@ SharedPlan plan_shared(int32_t S, int32_t num_q_heads, int32_t num_kv_heads, int
   return sp;
 }
 
-template <int DT>
+template <int DT, bool KV8>
 auto pick_shared_kernel(int32_t block_size) {
-  return block_size == 8 ? shared_prefix_kernel<DT, 8>
-         : block_size == 16 ? shared_prefix_kernel<DT, 16>
-                            : shared_prefix_kernel<DT, 32>;
+  return block_size == 8 ? shared_prefix_kernel<DT, 8, KV8>
+         : block_size == 16 ? shared_prefix_kernel<DT, 16, KV8>
+                            : shared_prefix_kernel<DT, 32, KV8>;
 }
 
 }  // namespace
@@ -296,8 +330,8 @@ kv_status shared_prefix_attention(float* o, float* lse, const void* q, const voi
                                   const void* v_pool, const int32_t* table_row0,
                                   int32_t max_blocks, int32_t S, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t block_size, int32_t num_blocks,
-                                  float scale, kv_dtype dtype, int32_t shared_len,
-                                  hipStream_t stream) {
+                                  float scale, kv_dtype dtype, int32_t shared_len, bool kv8,
+                                  float k_scale, float v_scale, hipStream_t stream) {
   using namespace decode;
   const SharedPlan sp = plan_shared(S, num_q_heads, num_kv_heads, shared_len);
   if (sp.ranges <= 0) return fail(KV_ERR_INVALID, "shared prefix: bad sizes");
@@ -320,11 +354,14 @@ kv_status shared_prefix_attention(float* o, float* lse, const void* q, const voi
   prm.Hkv = num_kv_heads;
   prm.G = num_q_heads / num_kv_heads;
   prm.num_blocks = num_blocks;
-  prm.scale_log2 = scale * 1.4426950408889634f;
+  prm.scale_log2 = scale * 1.4426950408889634f * (kv8 ? k_scale : 1.0f);
+  prm.v_scale = kv8 ? v_scale : 1.0f;
   const int64_t groups = (int64_t)sp.ranges * sp.col_tiles * num_kv_heads;
   if (groups > INT32_MAX) return fail(KV_ERR_INVALID, "shared prefix: too many workgroups");
-  auto kern = dtype == KV_BF16 ? pick_shared_kernel<KV_BF16>(block_size)
-                               : pick_shared_kernel<KV_F16>(block_size);
+  auto kern = kv8 ? (dtype == KV_BF16 ? pick_shared_kernel<KV_BF16, true>(block_size)
+                                     : pick_shared_kernel<KV_F16, true>(block_size))
+                  : (dtype == KV_BF16 ? pick_shared_kernel<KV_BF16, false>(block_size)
+                                      : pick_shared_kernel<KV_F16, false>(block_size));
   hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(64 * sp.waves), 0, stream, prm);
   return launch_status("kv_paged_attention_decode_append_shared (shared prefix)");
 }

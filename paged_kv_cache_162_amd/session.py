@@ -338,7 +338,12 @@ class DecodeSession:
             self.write_step_tokens(k_new, v_new, kp, vp_)
         if decode_events is not None:
             decode_events[0].record()
-        if self.fp8:
+        if self.fp8 and self.shared_tokens:
+            kv.kv_paged_attention_decode_append_shared_fp8(
+                out, q, k_new, v_new, kp, vp_, self.d_tables, self.d_lens, scale, self.k_scale,
+                self.v_scale, self.shared_tokens, self.max_decode_len, self.d_slots, self.aux,
+                self.workspace, self.step_partition, self.d_items, load_policy=self.load_policy)
+        elif self.fp8:
             if fused:
                 kv.kv_paged_attention_decode_append_fp8(
                     out, q, k_new, v_new, kp, vp_, self.d_tables, self.d_lens, scale, self.k_scale,

@@ -522,3 +522,24 @@ def test_choose_partition(kv):
     assert kv.kv_paged_attention_choose_partition([], 8, 16, 1500) == 512
     # a length of 0 still counts one unit (its output is written)
     assert kv.kv_paged_attention_choose_partition([0] * 10, 2, 16, 20) == 1024
+
+
+def test_shared_fp8_entry_point_validates_on_the_host(kv):
+    lib = kv.lib
+
+    def call(**k):
+        return lib.kv_paged_attention_decode_append_shared_fp8(
+            None, None, None, None, None, None, None, 8, None, k.get("S", 2), 8, 2,
+            k.get("D", 128), k.get("B", 16), 8, 1.0, k.get("dt", kv.KV_BF16), k.get("ks", 1.0),
+            k.get("vs", 1.0), 0, k.get("shared", 32), 16, None, 0, None, 0, None,
+            k.get("aux", 0), None, kv.KV_LOADS_STREAM, None)
+    assert call(ks=0.0) == kv.KV_ERR_INVALID
+    assert call(vs=float("inf")) == kv.KV_ERR_INVALID
+    assert call(D=64) == kv.KV_ERR_UNSUPPORTED
+    assert call(dt=kv.KV_F32) == kv.KV_ERR_UNSUPPORTED
+    assert call(dt=kv.KV_FP8_E4M3) == kv.KV_ERR_UNSUPPORTED   # dtype is the query's type
+    assert call(B=12) == kv.KV_ERR_UNSUPPORTED
+    assert call(shared=24) == kv.KV_ERR_INVALID               # not whole blocks
+    assert call(shared=2 * kv.KV_SHARED_PREFIX_MAX_TOKENS) == kv.KV_ERR_INVALID  # past the table
+    assert call() == kv.KV_ERR_INVALID                        # null pointers
+    assert call(S=0) == kv.KV_OK

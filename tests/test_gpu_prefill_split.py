@@ -226,3 +226,52 @@ def test_prefill_split_long_prefix_workload_through_the_session():
     ref = oracle.prefill_attention(w.q, qs, kp, vp, tables, lens, sp.scale, dt, rows=rows)
     check_attention(got[rows].reshape(-1, sp.D), ref[rows].reshape(-1, sp.D), dt, sp.name)
     sess.close()
+
+
+def test_prefill_split_graph_replay_matches_eager():
+    """The split prefill step (cache write, key runs, merge) captured in a HIP
+    graph: with the output and the workspace refilled with NaN bytes before
+    every replay, each replay reproduces the eager output and pools bit for
+    bit, and the eager output matches the oracle."""
+    from paged_kv_cache_162_amd.session import DecodeSession
+    rng = np.random.default_rng(1400)
+    dt, Hq, Hkv, D, B, NB = "bf16", 32, 8, 128, 16, 400
+    kp = round_to_dtype(rng.standard_normal((NB, Hkv, B, D)).astype(np.float32), dt)
+    vp = round_to_dtype(rng.standard_normal((NB, Hkv, B, D)).astype(np.float32), dt)
+    kd, vd = to_dev(kp, dt), to_dev(vp, dt)
+    sess = DecodeSession(k_pool=kd, v_pool=vd, num_q_heads=Hq, prefill_splits=5)
+    sess.run_ops([("create", 0), ("append", 0, 3000), ("create", 1), ("append", 1, 200),
+                  ("create", 2)])
+    counts = [16, 9, 24]
+    sess.prepare_prefill([0, 1, 2], counts)
+    assert sess.step_splits == 5
+    T = sum(counts)
+    q = round_to_dtype(rng.standard_normal((T, Hq, D)).astype(np.float32), dt)
+    kn = to_dev(round_to_dtype(rng.standard_normal((T, Hkv, D)).astype(np.float32), dt), dt)
+    vn = to_dev(round_to_dtype(rng.standard_normal((T, Hkv, D)).astype(np.float32), dt), dt)
+    qd = to_dev(q, dt)
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    sess.d_prefill_ws.fill_(0xFF)
+    sess.prefill_step(qd, kn, vn, out, 0.088)
+    torch.cuda.synchronize()
+    eager = (out.cpu().numpy().copy(), to_host(kd, dt).copy(), to_host(vd, dt).copy())
+    ref = oracle.prefill_attention(q, sess.host_qstart, eager[1], eager[2], sess.host_tables,
+                                   sess.host_lens, 0.088, dt, block_size=B)
+    check_attention(eager[0].reshape(-1, D), ref.reshape(-1, D), dt, "prefill split eager")
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            sess.prefill_step(qd, kn, vn, out, 0.088)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        sess.d_prefill_ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"[gpu] prefill split graph replay {rep}")
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), eager[0].view(np.uint32))
+        assert np.array_equal(to_host(kd, dt).view(np.uint16), eager[1].view(np.uint16))
+        assert np.array_equal(to_host(vd, dt).view(np.uint16), eager[2].view(np.uint16))
+    sess.close()

@@ -129,6 +129,46 @@ def _shared_batch(S, shared, tail, B=16):
 CONSERVATIVE = {(128, 256, 512)}
 
 
+# The same grid over an fp8 (E4M3) cache with bf16 queries (scales 1/4), shared / plain
+# step time, one box: every point with 131,072 or more prefix reads was faster; of the 8
+# points at 65,536 reads, 3 were ((16, 4096, 64), (32, 2048, 64), (128, 512, 512)); none
+# below. The library's fp8 threshold, 98,304, sits between and leaves those 3 to the plain
+# step.
+MEASURED_FP8 = [(4, 256, 64, 1.250), (4, 256, 512, 1.486), (4, 512, 64, 1.056),
+                (4, 512, 512, 1.547), (4, 1024, 64, 1.044), (4, 1024, 512, 1.586),
+                (4, 2048, 64, 1.025), (4, 2048, 512, 1.539), (4, 4096, 64, 1.032),
+                (4, 4096, 512, 1.520), (8, 256, 64, 1.265), (8, 256, 512, 1.499),
+                (8, 512, 64, 1.055), (8, 512, 512, 1.562), (8, 1024, 64, 1.025),
+                (8, 1024, 512, 1.560), (8, 2048, 64, 1.008), (8, 2048, 512, 1.481),
+                (8, 4096, 64, 0.983), (8, 4096, 512, 1.486), (16, 256, 64, 1.297),
+                (16, 256, 512, 1.463), (16, 512, 64, 1.052), (16, 512, 512, 1.497),
+                (16, 1024, 64, 1.018), (16, 1024, 512, 1.476), (16, 2048, 64, 0.980),
+                (16, 2048, 512, 1.450), (16, 4096, 64, 0.944), (16, 4096, 512, 1.083),
+                (32, 256, 64, 1.300), (32, 256, 512, 1.410), (32, 512, 64, 1.047),
+                (32, 512, 512, 1.433), (32, 1024, 64, 1.012), (32, 1024, 512, 1.398),
+                (32, 2048, 64, 0.927), (32, 2048, 512, 1.003), (32, 4096, 64, 0.608),
+                (32, 4096, 512, 0.771), (64, 256, 64, 1.293), (64, 256, 512, 1.215),
+                (64, 512, 64, 1.034), (64, 512, 512, 1.186), (64, 1024, 64, 0.980),
+                (64, 1024, 512, 1.019), (64, 2048, 64, 0.746), (64, 2048, 512, 0.863),
+                (64, 4096, 64, 0.531), (64, 4096, 512, 0.633), (128, 256, 64, 1.307),
+                (128, 256, 512, 0.993), (128, 512, 64, 0.985), (128, 512, 512, 0.942),
+                (128, 1024, 64, 0.759), (128, 1024, 512, 0.941), (128, 2048, 64, 0.539),
+                (128, 2048, 512, 0.704), (128, 4096, 64, 0.416), (128, 4096, 512, 0.525)]
+CONSERVATIVE_FP8 = {(16, 4096, 64), (32, 2048, 64), (128, 512, 512)}
+
+
+@pytest.mark.parametrize("S,shared,tail,ratio", MEASURED_FP8)
+def test_shared_step_rule_matches_fp8_measurements(S, shared, tail, ratio):
+    import paged_kv_cache_162_amd.binding as kv
+    tab, lens = _shared_batch(S, shared, tail)
+    got = kv.kv_paged_attention_choose_shared_prefix(tab, lens, 16, 32, 8, 128, kv.KV_FP8_E4M3)
+    faster = ratio <= 0.97
+    if (S, shared, tail) in CONSERVATIVE_FP8:
+        assert faster and got == 0
+    else:
+        assert got == (shared if faster else 0)
+
+
 @pytest.mark.parametrize("S,shared,tail,ratio", MEASURED)
 def test_shared_step_rule_matches_measurements(S, shared, tail, ratio):
     import paged_kv_cache_162_amd.binding as kv
@@ -147,7 +187,12 @@ def test_shared_step_only_where_the_entry_point_applies():
     choose = lambda **k: kv.kv_paged_attention_choose_shared_prefix(
         tab, lens, 16, k.get("Hq", 32), k.get("Hkv", 8), k.get("D", 128), k.get("dt", kv.KV_BF16))
     assert choose() == choose(dt=kv.KV_F16) == 2048
-    assert choose(dt=kv.KV_FP8_E4M3) == choose(dt=kv.KV_F32) == 0
+    assert choose(dt=kv.KV_F32) == 0
+    # an fp8 cache needs twice the prefix reads: 32 x 2048 is too few, 64 x 2048 enough
+    assert choose(dt=kv.KV_FP8_E4M3) == 0
+    tab64, lens64 = _shared_batch(64, 2048, 257)
+    assert kv.kv_paged_attention_choose_shared_prefix(tab64, lens64, 16, 32, 8, 128,
+                                                      kv.KV_FP8_E4M3) == 2048
     assert choose(D=64) == 0 and choose(Hq=64, Hkv=2) == 0 and choose(Hq=30) == 0
     assert choose(Hq=128, Hkv=8) == 2048     # group 16, the prefill kernel's largest
     # three sequences are too few, and a prefix read once per batch by them does not pay

@@ -172,6 +172,12 @@ SPECS = {
                      description="4 sequences, each with a 32752-token cached prefix "
                                  "and a 16-token chunk attended causally (context "
                                  "32768); 64 query / 8 KV heads, head_dim 128, bf16"),
+    11: WorkloadSpec(11, "prefix-share-long-fp8", S=64, Hq=32, Hkv=8, D=128, dtype="bf16",
+                     kv_dtype="e4m3", k_scale=0.25, v_scale=0.25, shared_prefix=4096, tail=256,
+                     description="64 sequences sharing a 4096-token prefix, 256 own tail "
+                                 "tokens each, one decode token; 32 query / 8 KV heads, "
+                                 "head_dim 128, bf16 queries over an fp8 E4M3 cache with "
+                                 "per-pool scales"),
     7: WorkloadSpec(7, "llama70b-gqa-fp8", S=128, Hq=64, Hkv=8, D=128, dtype="bf16",
                     kv_dtype="e4m3", k_scale=0.25, v_scale=0.25, seed_cfg=3,
                     description="the llama70b-gqa-bf16 workload (same lengths, "
@@ -251,7 +257,7 @@ def _context_lengths(sp: WorkloadSpec, rng: np.random.Generator) -> np.ndarray:
         return (np.clip(np.rint(x), 0, 8192 - sp.chunk) + sp.chunk).astype(np.int32)
     if sp.cfg in (4, 10):
         return np.full(sp.S, 32768, dtype=np.int32)
-    if sp.cfg in (5, 6):
+    if sp.cfg in (5, 6, 11):
         return np.full(sp.S, sp.shared_prefix + sp.tail + 1, dtype=np.int32)
     raise ValueError(sp.cfg)
 
@@ -268,7 +274,7 @@ def _pool_blocks(sp: WorkloadSpec, lens: np.ndarray) -> int:
         return int(math.ceil(1.1 * need))
     if sp.cfg == 4:
         return int(sp.S * (32768 // B))
-    if sp.cfg in (5, 6):
+    if sp.cfg in (5, 6, 11):
         # shared prefix once plus every sequence's own blocks, +10%
         pre = -(-sp.shared_prefix // B)
         own = -(-(sp.shared_prefix + sp.tail + 1) // B) - sp.shared_prefix // B
