@@ -53,6 +53,7 @@ SIGS = {
     "kv_paged_attention_choose_shared_prefix": (i32, [P_i32, i32, i32, P_i32, i32, i32, i32, i32,
                                                       C.c_int]),
     "kv_paged_attention_choose_load_policy": (C.c_int, [vp, i32]),
+    "kv_paged_attention_prefill_choose_splits": (i32, [P_i32, P_i32, i32, i32, i32, i32]),
 }
 STATUS = {0: None, -1: "INVALID", -2: "OOM", -3: "UNSUPPORTED", -5: "STATE"}
 
@@ -201,6 +202,10 @@ def planners(lib, rounds, rng):
         items = np.zeros((max(n.value, 1), 2), np.int32)
         assert lib.kv_paged_attention_prefill_plan(p32(qs), p32(plen), S, 64, 8, p32(items),
                                                    n.value, C.byref(n)) == 0
+        hq = int(rng.choice([8, 32, 64, 128]))
+        splits = lib.kv_paged_attention_prefill_choose_splits(p32(qs), p32(plen), S, hq, 8,
+                                                              int(rng.choice([0, 64, 512])))
+        assert 1 <= splits <= 64
         assert lib.kv_paged_attention_choose_partition(p32(lens), S, hkv, 16, 1500) in (512, 768,
                                                                                         1024)
         if S:
@@ -209,8 +214,10 @@ def planners(lib, rounds, rng):
             tab[:, :width // 2] = tab[0, :width // 2]
             sh = lib.kv_paged_attention_common_prefix(p32(tab), S, width, p32(lens), 16)
             assert 0 <= sh <= width * 16 and sh % 16 == 0
-            lib.kv_paged_attention_choose_shared_prefix(p32(tab), S, width, p32(lens), 16, 32, 8,
-                                                        128, 2)
+            for dt in (2, 3):   # bf16 and an fp8 cache
+                got = lib.kv_paged_attention_choose_shared_prefix(p32(tab), S, width, p32(lens),
+                                                                  16, 32, 8, 128, dt)
+                assert got == 0 or (got == sh and got >= 256)
 
 
 if __name__ == "__main__":

@@ -100,9 +100,14 @@ def test_prefill_split_against_oracle(dt, G, B, splits):
                         f"prefill split {dt} G={G} B={B} splits={splits}")
 
 
-def test_prefill_split_fp8_cache_against_oracle():
-    rng = np.random.default_rng(1100)
-    dt, G, B, Hkv, D = "bf16", 8, 16, 2, 128
+FP8_SPLIT_SHAPES = [("bf16", 8, 16, True), ("f16", 1, 8, False), ("bf16", 16, 32, True),
+                    ("f16", 4, 16, False), ("bf16", 3, 8, True)]
+
+
+@pytest.mark.parametrize("dt,G,B,plan", FP8_SPLIT_SHAPES)
+def test_prefill_split_fp8_cache_against_oracle(dt, G, B, plan):
+    rng = np.random.default_rng(1100 + FP8_SPLIT_SHAPES.index((dt, G, B, plan)))
+    Hkv, D = 2, 128
     q, qs, _, _, tab, lens = prefill_case(rng, PREV, CHUNK, G * Hkv, Hkv, D, dt, B=B,
                                           poison=False)
     NB = int(tab.max()) + 6
@@ -120,9 +125,11 @@ def test_prefill_split_fp8_cache_against_oracle():
     ref = oracle.prefill_attention(q, qs, kp, vp, tab, lens, scale, dt, block_size=B,
                                    kv_dtype="e4m3", k_scale=ks, v_scale=vs)
     for splits in (3, 16):
-        log(f"[gpu] prefill split fp8 splits={splits}")
-        got = gpu_prefill_split(q, qs, kp, vp, tab, lens, scale, dt, splits, fp8=(ks, vs))
-        check_attention(got.reshape(-1, D), ref.reshape(-1, D), dt, f"prefill split fp8 {splits}")
+        log(f"[gpu] prefill split fp8 {dt} G={G} B={B} plan={plan} splits={splits}")
+        got = gpu_prefill_split(q, qs, kp, vp, tab, lens, scale, dt, splits, plan=plan,
+                                fp8=(ks, vs))
+        check_attention(got.reshape(-1, D), ref.reshape(-1, D), dt,
+                        f"prefill split fp8 {dt} G={G} B={B} splits={splits}")
 
 
 def test_prefill_split_invalid_sequences_give_nan_rows_only():
