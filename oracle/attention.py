@@ -240,8 +240,9 @@ def decode_attention_split(q, k_pool, v_pool, block_tables, context_lens, scale:
 
 
 def _bits(a: np.ndarray) -> np.ndarray:
-    """View any 2- or 4-byte array as unsigned integers (raw bit copies)."""
-    return a.view({2: np.uint16, 4: np.uint32}[a.dtype.itemsize])
+    """View any 1-, 2- or 4-byte array as unsigned integers (raw bit copies;
+    1-byte elements are the codes of an fp8 cache)."""
+    return a.view({1: np.uint8, 2: np.uint16, 4: np.uint32}[a.dtype.itemsize])
 
 
 def reshape_and_cache(k_new, v_new, k_pool, v_pool, slots, block_size: int = 16) -> None:

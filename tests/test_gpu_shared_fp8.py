@@ -204,3 +204,38 @@ def test_session_shared_fp8_step_matches_plain_step(B):
     ref = case.oracle_out()
     log(check_attention(a[0].reshape(-1, D), ref.reshape(-1, D), case.dt,
                         "shared fp8 step vs oracle"))
+
+
+def test_shared_fp8_step_graph_replay_matches_eager():
+    """The fp8 shared-prefix step captured in a HIP graph (no memset nodes): every replay,
+    with the outputs, slots and scratch poisoned in between by eager work, reproduces the
+    eager step bit for bit (outputs, both pools, slots)."""
+    from gpu_common import Case
+    case = Case(11)
+    case.device_run()
+    sess = case.sess
+    assert sess.shared_tokens == 4096
+    eager = (case.out_dev.cpu().numpy().copy(), to_host(case.k_dev, "e4m3").copy(),
+             to_host(case.v_dev, "e4m3").copy(), sess.d_slots.cpu().numpy().copy())
+    out = torch.full_like(case.out_dev, float("nan"))
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            sess.step(case.q_dev, case.kn_dev, case.vn_dev, out, case.sp.scale)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        sess.d_slots.fill_(-7)
+        sess.aux.fill_(float("nan"))
+        if sess.workspace is not None:
+            sess.workspace.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"[gpu] shared fp8 step graph replay {rep}")
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), eager[0].view(np.uint32))
+        assert np.array_equal(to_host(case.k_dev, "e4m3"), eager[1])
+        assert np.array_equal(to_host(case.v_dev, "e4m3"), eager[2])
+        assert np.array_equal(sess.d_slots.cpu().numpy(), eager[3])
+    sess.close()

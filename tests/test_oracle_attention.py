@@ -193,6 +193,19 @@ def test_copy_blocks_bits():
     assert np.array_equal(b[3], b[0]) and np.array_equal(b[2], b[1])
 
 
+def test_copy_blocks_fp8_codes():
+    """A block of an fp8 cache is copied byte for byte, NaN codes included; the
+    other blocks are untouched."""
+    rng = np.random.default_rng(3)
+    a = rng.integers(0, 256, (5, 2, B, 8), dtype=np.uint8)
+    a[1, 0, 0, 0] = 0x7F                      # an E4M3 NaN code travels as a byte
+    before = a.copy()
+    oa.copy_blocks([a], [(1, 4), (0, 2)])
+    assert np.array_equal(a[4], before[1]) and np.array_equal(a[2], before[0])
+    assert a[4, 0, 0, 0] == 0x7F
+    assert np.array_equal(a[[0, 1, 3]], before[[0, 1, 3]])
+
+
 # ---------------------------------------------------------------------------
 # attention: brute force and a library routine
 # ---------------------------------------------------------------------------
