@@ -38,8 +38,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # 500 warm-up steps bring the clocks to their steady state before the
+    # 2,000 timed ones (about 130 ms at the 70B-shaped decode step)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", type=int, default=3, help="workload number 1-11")
     ap.add_argument("--partition", type=int, default=0,
                     help="partition tokens (0 = chosen per batch by kv_paged_attention_choose_partition)")
@@ -559,7 +561,7 @@ def swap_bench(args, kv, torch):
         e1.synchronize()
         return e0.elapsed_time(e1) / reps / 1e3
 
-    reps = max(args.steps // 20, 3)
+    reps = max(min(args.steps // 20, 10), 3)
     t_out = timed(lambda: kv.kv_swap_out_blocks(kp, vp, ids, NB, bb, host), reps)
     t_in = timed(lambda: kv.kv_swap_in_blocks(kp, vp, ids, NB, bb, host), reps)
     t_d2h = timed(lambda: host.copy_(dev_flat, non_blocking=True), reps)
@@ -865,7 +867,7 @@ def main():
                                           "decode_ms", "roofline_frac", "steps")}}
         for cfg in PER_CONFIG:
             torch.cuda.empty_cache()
-            pr = run_decode(args, cfg, kv, torch, min(args.steps, 100), min(args.warmup, 10),
+            pr = run_decode(args, cfg, kv, torch, min(args.steps, 500), min(args.warmup, 100),
                             primary=False)
             per[str(cfg)] = pr
             print(f"[bench] workload {cfg}: {pr['ms_per_step'] * 1e3:.1f} us per step, "
