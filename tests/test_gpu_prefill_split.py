@@ -282,3 +282,29 @@ def test_prefill_split_graph_replay_matches_eager():
         assert np.array_equal(to_host(kd, dt).view(np.uint16), eager[1].view(np.uint16))
         assert np.array_equal(to_host(vd, dt).view(np.uint16), eager[2].view(np.uint16))
     sess.close()
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_prefill_split_random_shapes(case):
+    """Seeded random shapes: group size, block size, run count, query type,
+    cached prefixes (zero included) and chunk lengths (empty and one-row
+    chunks included), with and without the plan; every row against the oracle."""
+    rng = np.random.default_rng(1500 + case)
+    G = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    B = int(rng.choice([8, 16, 32]))
+    dt = str(rng.choice(["bf16", "f16"]))
+    splits = int(rng.integers(2, 65))
+    S = int(rng.integers(1, 7))
+    prev = [int(x) for x in rng.choice([0, 1, 15, 16, 17, 300, 1500, 2600], S)]
+    chunk = [int(x) for x in rng.choice([0, 1, 2, 16, 33, 70], S)]
+    if sum(chunk) == 0:
+        chunk[0] = 5
+    Hkv, D = int(rng.choice([1, 2])), 128
+    q, qs, kp, vp, tab, lens = prefill_case(rng, prev, chunk, G * Hkv, Hkv, D, dt, B=B)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    ref = oracle.prefill_attention(q, qs, kp, vp, tab, lens, scale, dt, block_size=B)
+    for plan in (True, False):
+        log(f"[gpu] prefill split random {case}: {dt} G={G} Hkv={Hkv} B={B} splits={splits} "
+            f"prev={prev} chunk={chunk} plan={plan}")
+        got = gpu_prefill_split(q, qs, kp, vp, tab, lens, scale, dt, splits, plan=plan)
+        check_attention(got.reshape(-1, D), ref.reshape(-1, D), dt, f"prefill split random {case}")
