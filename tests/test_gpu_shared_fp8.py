@@ -239,3 +239,33 @@ def test_shared_fp8_step_graph_replay_matches_eager():
         assert np.array_equal(to_host(case.v_dev, "e4m3"), eager[2])
         assert np.array_equal(sess.d_slots.cpu().numpy(), eager[3])
     sess.close()
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_shared_prefix_fp8_random_shapes(case):
+    """Seeded random shapes of the fp8 shared step: group size, block size, sequences, shared
+    length, tail lengths, partition size, plan and scales; slots and pools bit exact, every
+    output within tolerance."""
+    rng = np.random.default_rng(9800 + case)
+    G = int(rng.choice([1, 2, 4, 5, 8, 16]))
+    B = int(rng.choice([8, 16, 32]))
+    dt = str(rng.choice(["bf16", "f16"]))
+    S = int(rng.integers(2, 40))
+    Hkv = int(rng.choice([1, 2, 4]))
+    shared_blocks = int(rng.integers(1, 1600 // B))
+    tails = [int(t) for t in rng.integers(1, 400, S)]
+    P = int(rng.choice([0, 64, 128, 256]))
+    plan = bool(rng.integers(0, 2))
+    ks, vs = float(rng.uniform(0.01, 1.0)), float(rng.uniform(0.01, 1.0))
+    (out, slots, dk, dv), (q, kp, vp, tab, cl, kn, vn, scale) = run_shared_fp8(
+        rng, dt, G, B, P, plan, S, Hkv, shared_blocks, tails, ks, vs)
+    ref_slots = oa.slot_mapping(tab, np.arange(S), cl - 1, block_size=B)
+    rk, rv = kp.copy(), vp.copy()
+    ofp8.reshape_and_cache_fp8(kn, vn, rk, rv, ref_slots, dt, ks, vs, block_size=B)
+    ref = oracle.decode_attention(q, rk, rv, tab, cl, scale, dt, block_size=B, kv_dtype="e4m3",
+                                  k_scale=ks, v_scale=vs)
+    assert np.array_equal(slots, ref_slots)
+    assert np.array_equal(dk, rk) and np.array_equal(dv, rv)
+    check_attention(out.reshape(-1, 128), ref.reshape(-1, 128), dt,
+                    f"shared fp8 random {case}: {dt} G={G} Hkv={Hkv} B={B} S={S} "
+                    f"shared={shared_blocks * B} P={P} plan={plan}")
