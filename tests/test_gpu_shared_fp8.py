@@ -269,3 +269,51 @@ def test_shared_prefix_fp8_random_shapes(case):
     check_attention(out.reshape(-1, 128), ref.reshape(-1, 128), dt,
                     f"shared fp8 random {case}: {dt} G={G} Hkv={Hkv} B={B} S={S} "
                     f"shared={shared_blocks * B} P={P} plan={plan}")
+
+
+@pytest.mark.parametrize("where", ["prefix", "tail"])
+def test_shared_fp8_step_invalid_table_entry(where):
+    """Over an fp8 cache as over a 16-bit one: an out-of-pool block ID in the shared part of
+    row 0's table makes every output NaN; one in a sequence's tail makes only that sequence
+    NaN, the other outputs matching the oracle (no load leaves the pool)."""
+    kv = kvlib()
+    rng = np.random.default_rng(9900)
+    dt, D, Hkv, G, B = "bf16", 128, 2, 8, 16
+    S, shared_blocks = 6, 20
+    tails = [40, 3, 77, 16, 1, 130]
+    q, kp, vp, tab, cl = shared_case_fp8(rng, S, shared_blocks, tails, G * Hkv, Hkv, D, dt, B)
+    shared = shared_blocks * B
+    scale, ks, vs = 0.088, 0.06, 0.03
+    kn = round_to_dtype(rng.standard_normal((S, Hkv, D)).astype(np.float32), dt)
+    vn = round_to_dtype(rng.standard_normal((S, Hkv, D)).astype(np.float32), dt)
+    bad_tab = tab.copy()
+    victim = 2
+    if where == "prefix":
+        bad_tab[0, 7] = kp.shape[0] + 5          # only row 0's copy is read for the prefix
+    else:
+        bad_tab[victim, shared_blocks + 2] = -3  # a tail block of sequence 2
+    ref_slots = oa.slot_mapping(tab, np.arange(S), cl - 1, block_size=B)
+    rk, rv = kp.copy(), vp.copy()
+    ofp8.reshape_and_cache_fp8(kn, vn, rk, rv, ref_slots, dt, ks, vs, block_size=B)
+    ref = oracle.decode_attention(q, rk, rv, tab, cl, scale, dt, block_size=B, kv_dtype="e4m3",
+                                  k_scale=ks, v_scale=vs)
+    mt = int(max(cl - shared))
+    wsb = kv.kv_paged_attention_workspace_bytes(S, G * Hkv, Hkv, D, mt, 0)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
+    aux = torch.empty(kv.kv_paged_attention_shared_aux_bytes(S, G * Hkv, Hkv, D, shared) // 4,
+                      dtype=torch.float32, device="cuda")
+    out = torch.full((S, G * Hkv, D), 3.0, dtype=torch.float32, device="cuda")
+    slots = torch.full((S,), 7, dtype=torch.int64, device="cuda")
+    log(f"[gpu] shared fp8 step, invalid entry in the {where}")
+    kv.kv_paged_attention_decode_append_shared_fp8(
+        out, to_dev(q, dt), to_dev(kn, dt), to_dev(vn, dt), to_dev(kp, "e4m3"),
+        to_dev(vp, "e4m3"), torch.from_numpy(bad_tab).cuda(), torch.from_numpy(cl).cuda(), scale,
+        ks, vs, shared, mt, slots, aux, ws, 0, None)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    if where == "prefix":
+        assert np.isnan(got).all()
+    else:
+        ok = [s for s in range(S) if s != victim]
+        assert np.isnan(got[victim]).all()
+        check_attention(got[ok].reshape(-1, D), ref[ok].reshape(-1, D), dt, "other sequences")
